@@ -1,0 +1,180 @@
+/*
+ * qgalore.h — C ABI of the MI355X (gfx950) Q-GaLore optimizer-step library.
+ *
+ * The method (AIMech curated page "Q-GaLore (Quantized GaLore with INT4 Projection and
+ * Layer-Adaptive Low-Rank Gradients)"; paper Section 3.2 for the update rule, Section 3.1 /
+ * Equation (5) for the subspace test): for each linear layer with weight W (m x n) and
+ * gradient G (m x n), a rank-r projection P (m x r) stored in INT4 projects the gradient,
+ * R = P^T G; Adam runs on R with first and second moments M, V (r x n) stored in INT8; the
+ * Adam update N is back-projected, U = alpha * P N, and added into the INT8 weights with
+ * unbiased stochastic rounding. A layer's projection is refreshed from an SVD at an
+ * interval that doubles whenever the subspace similarity
+ *     CosSim(P_t, P_prev) = (1/r) * sum_i sigma_i(P_t^T P_prev)
+ * exceeds gamma (default 0.4).
+ *
+ * Number formats (fixed by this library; the pages leave them open):
+ *   G        bf16, m x n row-major (bit patterns as uint16).
+ *   W_q      int8, m x n row-major, codes in [-127, 127].
+ *   W_scale  fp32, one scale per group of 256 consecutive flat elements of W
+ *            (ceil(m*n/256) entries). Read-only during a step.
+ *   P_q      INT4, m x r row-major, two codes per byte (flat element 2k in the low nibble
+ *            of byte k, 2k+1 in the high nibble, two's complement, codes in [-7, 7]);
+ *            ceil(m*r/2) bytes.
+ *   P_scale  fp32, ceil(m*r/256) group scales of P.
+ *   M_q, V_q int8, r x n row-major; M_scale, V_scale fp32, ceil(r*n/256) group scales.
+ *            All four are rewritten in place by every step (absmax requantization).
+ * Group quantization everywhere is symmetric absmax over 256 flat elements:
+ *   s = absmax/qmax, q = clamp(round_half_even(x * (1/s)), -qmax, qmax), s = 0 -> q = 0.
+ *
+ * Arithmetic of one step (every fp32 operation rounded to nearest-even, no contraction):
+ *   P~  = bf16(q_P * s_P)                      (dequantized projection, bf16 operand)
+ *   R   = P~^T G                               (fp32 accumulation on bf16 MFMA)
+ *   m1  = b1*(q_M*s_M) + (1-b1)*R ;  v1 = b2*(q_V*s_V) + (1-b2)*(R*R)
+ *   N   = -(lr * (m1/(1-b1^t))) / (sqrt(v1/(1-b2^t)) + eps) ;  N~ = bf16(N)
+ *   M, V <- absmax INT8 requantization of m1, v1 (the update uses the fresh fp32 values)
+ *   U   = alpha * (P~ N~)                      (fp32 accumulation on bf16 MFMA)
+ *   d   = (W_q + U * (1/s_W)) + u ;  W_q <- clamp(floor(d), -127, 127)  (d finite;
+ *         otherwise W_q is left unchanged)
+ *   u   = 16-bit uniform in [0,1) from Philox4x32-10 (Salmon et al., SC'11):
+ *         key = (seed & 0xffffffff, seed >> 32), counter = (j >> 3, i, t, layer_id),
+ *         word (j >> 1) & 3, low half for even j and high half for odd j, times 2^-16.
+ *
+ * Conventions for every entry point below:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library keeps no tensor
+ *     state. Inputs are read-only unless stated. No two pointers may alias.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Step entry points are
+ *     asynchronous on that stream.
+ *   - Errors are returned as qg_status; nothing is thrown or aborted across the ABI.
+ *     Arguments are validated before any HIP call. HIP failures return QG_ERR_HIP and
+ *     qgalore_last_error() (thread-local) holds the text.
+ *   - Base pointers of G, W_q, M_q, V_q, R_out, U_out and workspaces must be 16-byte
+ *     aligned; scale arrays and P_q 4-byte aligned (QG_ERR_ALIGN otherwise).
+ */
+#ifndef QGALORE_H
+#define QGALORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QG_OK = 0,
+  QG_ERR_NULL = 1,       /* a required pointer is NULL */
+  QG_ERR_SHAPE = 2,      /* m, n, r out of range (need 1 <= r <= m, m, n, r < 2^31) */
+  QG_ERR_ALIGN = 3,      /* a base pointer breaks the alignment rule above */
+  QG_ERR_WORKSPACE = 4,  /* workspace smaller than the size query returns */
+  QG_ERR_ARG = 5,        /* step out of [1, 2^32), non-finite or out-of-range hyperparameter */
+  QG_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+  QG_ERR_NO_DEVICE = 7   /* no HIP device is present */
+} qg_status;
+
+/* Per-layer description for qgalore_step. */
+typedef struct {
+  int64_t m, n, r;          /* W, G: m x n; P: m x r; M, V: r x n */
+  uint32_t layer_id;        /* Philox counter word 3: unique per layer within a model */
+  float lr, beta1, beta2, eps, alpha;   /* Adam (0 <= beta < 1, eps >= 0) and the update scale */
+  float *M_scale, *V_scale; /* fp32[ceil(r*n/256)], read and rewritten in place */
+  float *R_out;             /* optional fp32 r x n: the projected gradient R (NULL = skip) */
+  float *U_out;             /* optional fp32 m x n: the back-projected update U (NULL = skip) */
+  void *workspace;          /* caller-owned device scratch, >= qgalore_workspace_bytes() */
+  size_t workspace_bytes;
+  void *stream;             /* hipStream_t */
+} qg_layer_desc;
+
+/* Device scratch one qgalore_step call needs for an m x n layer of rank r. */
+size_t qgalore_workspace_bytes(int64_t m, int64_t n, int64_t r);
+
+/* One Q-GaLore optimizer step for one layer (AIMech Q-GaLore page, mechanism claim "INT4
+ * projection and INT8 stochastic rounding", paper Section 3.2). Updates W_q, M_q, V_q and
+ * the desc's M_scale, V_scale in place; `step` is the 1-based Adam step t (1 <= t < 2^32);
+ * `seed` keys the stochastic rounding. Asynchronous on desc->stream. Concurrent calls on
+ * one device must use distinct workspaces. */
+qg_status qgalore_step(const qg_layer_desc *desc, const uint16_t *G, int8_t *W_q,
+                       const float *W_scale, const uint8_t *P_q, const float *P_scale,
+                       int8_t *M_q, int8_t *V_q, int64_t step, uint64_t seed);
+
+/* ------------------------------------------------------------------------------------
+ * Grouped step: one launch per kernel over a whole set of layers (the per-layer step of
+ * the same page, applied to every linear layer of a model at once).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  qg_layer_desc desc;       /* workspace / workspace_bytes / stream are ignored here */
+  const uint16_t *G;
+  int8_t *W_q;
+  const float *W_scale;
+  const uint8_t *P_q;
+  const float *P_scale;
+  int8_t *M_q;
+  int8_t *V_q;
+} qg_layer;
+
+typedef struct qg_plan qg_plan;
+
+/* Validates every layer and uploads a layer table to the current device (the only
+ * allocation: a small table, freed by qgalore_plan_destroy). All layers must share beta1
+ * and beta2. The tensors named by `layers` must stay valid while the plan is used. */
+qg_status qgalore_plan_create(const qg_layer *layers, int32_t count, qg_plan **out);
+/* Device scratch a qgalore_plan_step call needs. */
+size_t qgalore_plan_workspace_bytes(const qg_plan *plan);
+/* One optimizer step over every layer of the plan, asynchronous on `stream`. */
+qg_status qgalore_plan_step(qg_plan *plan, int64_t step, uint64_t seed, void *workspace,
+                            size_t workspace_bytes, void *stream);
+qg_status qgalore_plan_destroy(qg_plan *plan);
+
+/* ------------------------------------------------------------------------------------
+ * Subspace similarity (AIMech Q-GaLore page, mechanism claim "layer-adaptive subspace
+ * cosine schedule", paper Section 3.1, Equation (5)).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t m, r;             /* P is m x r */
+  const uint8_t *q;         /* INT4 codes, layout as P_q above */
+  const float *scale;       /* ceil(m*r/256) group scales */
+} qg_proj;
+
+size_t qgalore_cossim_workspace_bytes(int64_t m, int64_t r);
+/* CosSim of two stored projections (each dequantized and rounded to bf16 as the step uses
+ * it): C = P~_new^T P~_old, then (1/r) * nuclear norm of C, computed with a Newton-Schulz
+ * polar iteration in fp32. Writes one fp32 to `out_dev` (device), asynchronously. */
+qg_status qgalore_cossim_async(const qg_proj *P_new, const qg_proj *P_old, void *workspace,
+                               size_t workspace_bytes, void *stream, float *out_dev);
+/* Same, then synchronizes `stream` and stores the value in *out_host. */
+qg_status qgalore_cossim(const qg_proj *P_new, const qg_proj *P_old, void *workspace,
+                         size_t workspace_bytes, void *stream, float *out_host);
+
+/* INT4 group quantization of an fp32 m x r projection (the format of P_q/P_scale above;
+ * used when a refresh installs a new projection). Asynchronous on `stream`. */
+qg_status qgalore_quantize_proj(const float *P, int64_t m, int64_t r, uint8_t *P_q,
+                                float *P_scale, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Per-layer refresh schedule (host only; same page and claim as CosSim). A refresh falls
+ * due when t >= next_refresh. At each refresh after the first, a similarity above gamma
+ * doubles the interval; the next refresh is then t + interval.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t delta;            /* current refresh interval */
+  int64_t next_refresh;     /* step of the next refresh */
+  int64_t count;            /* refreshes (SVDs) done so far */
+  float gamma;              /* similarity threshold */
+  float last_cossim;        /* similarity seen at the last refresh (NaN before the second) */
+} qg_sched;
+
+qg_status qgalore_sched_init(qg_sched *s, int64_t delta0, float gamma);
+/* 1 when a refresh is due at step t, else 0 (-1 for a NULL schedule). */
+int32_t qgalore_sched_due(const qg_sched *s, int64_t t);
+/* Records a refresh at step t with similarity `cossim` (ignored at the first refresh).
+ * *doubled (optional) is set to 1 when the interval doubled. */
+qg_status qgalore_sched_refresh(qg_sched *s, int64_t t, float cossim, int32_t *doubled);
+
+/* ------------------------------------------------------------------------------------ */
+const char *qgalore_status_str(qg_status s);
+const char *qgalore_last_error(void);   /* thread-local text of the last QG_ERR_HIP */
+const char *qgalore_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGALORE_H */

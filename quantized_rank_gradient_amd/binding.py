@@ -1,0 +1,326 @@
+"""Python binding of libqgalore.so (ctypes): argument marshalling only.
+
+Every step of the optimizer runs in the library's gfx950 kernels; this module checks dtypes,
+shapes and devices of torch tensors, passes their device pointers and the current HIP stream
+across the C ABI, and turns status codes into exceptions. There is no fallback: if the
+library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgalore.so")
+
+GROUP = 256
+
+c_int64, c_uint32, c_int32, c_float, c_void_p, c_size_t, c_uint64 = (
+    ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+    ctypes.c_size_t, ctypes.c_uint64)
+
+STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN",
+          4: "QG_ERR_WORKSPACE", 5: "QG_ERR_ARG", 6: "QG_ERR_HIP", 7: "QG_ERR_NO_DEVICE"}
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("m", c_int64), ("n", c_int64), ("r", c_int64), ("layer_id", c_uint32),
+                ("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("alpha", c_float), ("M_scale", c_void_p), ("V_scale", c_void_p),
+                ("R_out", c_void_p), ("U_out", c_void_p), ("workspace", c_void_p),
+                ("workspace_bytes", c_size_t), ("stream", c_void_p)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("desc", LayerDesc), ("G", c_void_p), ("W_q", c_void_p), ("W_scale", c_void_p),
+                ("P_q", c_void_p), ("P_scale", c_void_p), ("M_q", c_void_p), ("V_q", c_void_p)]
+
+
+class Proj(ctypes.Structure):
+    _fields_ = [("m", c_int64), ("r", c_int64), ("q", c_void_p), ("scale", c_void_p)]
+
+
+class Sched(ctypes.Structure):
+    _fields_ = [("delta", c_int64), ("next_refresh", c_int64), ("count", c_int64),
+                ("gamma", c_float), ("last_cossim", c_float)]
+
+
+EXPORTS = {
+    "qgalore_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
+    "qgalore_step": (c_int32, [ctypes.POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_int64, c_uint64]),
+    "qgalore_plan_create": (c_int32, [ctypes.POINTER(Layer), c_int32, ctypes.POINTER(c_void_p)]),
+    "qgalore_plan_workspace_bytes": (c_size_t, [c_void_p]),
+    "qgalore_plan_step": (c_int32, [c_void_p, c_int64, c_uint64, c_void_p, c_size_t, c_void_p]),
+    "qgalore_plan_destroy": (c_int32, [c_void_p]),
+    "qgalore_cossim_workspace_bytes": (c_size_t, [c_int64, c_int64]),
+    "qgalore_cossim_async": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p,
+                                       c_size_t, c_void_p, c_void_p]),
+    "qgalore_cossim": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p, c_size_t,
+                                 c_void_p, ctypes.POINTER(c_float)]),
+    "qgalore_quantize_proj": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "qgalore_sched_init": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float]),
+    "qgalore_sched_due": (c_int32, [ctypes.POINTER(Sched), c_int64]),
+    "qgalore_sched_refresh": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float,
+                                        ctypes.POINTER(c_int32)]),
+    "qgalore_status_str": (ctypes.c_char_p, [c_int32]),
+    "qgalore_last_error": (ctypes.c_char_p, []),
+    "qgalore_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgalore.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python quantized_rank_gradient_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class QgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        L = lib()
+        text = L.qgalore_status_str(status).decode()
+        if status == 6:
+            text += ": " + L.qgalore_last_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QgError(status, where)
+
+
+def n_groups(numel: int) -> int:
+    return -(-int(numel) // GROUP)
+
+
+def _ptr(t, dtype, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclasses.dataclass
+class LayerTensors:
+    """One linear layer's optimizer state on the GPU (see include/qgalore.h for layouts)."""
+    layer_id: int
+    G: torch.Tensor          # bf16 m x n
+    Wq: torch.Tensor         # int8 m x n
+    Ws: torch.Tensor         # fp32 [groups(m*n)]
+    Pq: torch.Tensor         # uint8 [ceil(m*r/2)]
+    Ps: torch.Tensor         # fp32 [groups(m*r)]
+    Mq: torch.Tensor         # int8 r x n
+    Ms: torch.Tensor         # fp32 [groups(r*n)]
+    Vq: torch.Tensor         # int8 r x n
+    Vs: torch.Tensor         # fp32 [groups(r*n)]
+    r: int
+
+    @property
+    def m(self) -> int:
+        return int(self.Wq.shape[0])
+
+    @property
+    def n(self) -> int:
+        return int(self.Wq.shape[1])
+
+
+def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None):
+    m, n, r = L.m, L.n, L.r
+    d.m, d.n, d.r = m, n, r
+    d.layer_id = L.layer_id
+    d.lr, d.beta1, d.beta2 = hp.get("lr", 1e-3), hp.get("beta1", 0.9), hp.get("beta2", 0.999)
+    d.eps, d.alpha = hp.get("eps", 1e-8), hp.get("alpha", 0.25)
+    d.M_scale = _ptr(L.Ms, torch.float32, (n_groups(r * n),), "Ms")
+    d.V_scale = _ptr(L.Vs, torch.float32, (n_groups(r * n),), "Vs")
+    d.R_out = _ptr(R_out, torch.float32, (r, n), "R_out")
+    d.U_out = _ptr(U_out, torch.float32, (m, n), "U_out")
+    ptrs = dict(G=_ptr(L.G, torch.bfloat16, (m, n), "G"),
+                W_q=_ptr(L.Wq, torch.int8, (m, n), "Wq"),
+                W_scale=_ptr(L.Ws, torch.float32, (n_groups(m * n),), "Ws"),
+                P_q=_ptr(L.Pq, torch.uint8, ((m * r + 1) // 2,), "Pq"),
+                P_scale=_ptr(L.Ps, torch.float32, (n_groups(m * r),), "Ps"),
+                M_q=_ptr(L.Mq, torch.int8, (r, n), "Mq"),
+                V_q=_ptr(L.Vq, torch.int8, (r, n), "Vq"))
+    return ptrs
+
+
+def workspace_bytes(m: int, n: int, r: int) -> int:
+    return int(lib().qgalore_workspace_bytes(m, n, r))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def step(L: LayerTensors, t: int, seed: int, hp: dict | None = None, workspace=None,
+         R_out=None, U_out=None, stream=None) -> None:
+    """One optimizer step of one layer (asynchronous on the current stream)."""
+    hp = hp or {}
+    d = LayerDesc()
+    ptrs = _fill_desc(d, L, hp, R_out, U_out)
+    need = workspace_bytes(L.m, L.n, L.r)
+    if workspace is None:
+        workspace = alloc_workspace(need, L.Wq.device)
+    d.workspace = _ptr(workspace, torch.uint8, None, "workspace")
+    d.workspace_bytes = workspace.numel()
+    d.stream = _stream(stream)
+    _check(lib().qgalore_step(ctypes.byref(d), ptrs["G"], ptrs["W_q"], ptrs["W_scale"],
+                              ptrs["P_q"], ptrs["P_scale"], ptrs["M_q"], ptrs["V_q"], int(t),
+                              int(seed) & (2 ** 64 - 1)), "qgalore_step")
+
+
+class Plan:
+    """A grouped step over many layers: one launch per kernel for the whole set."""
+
+    def __init__(self, layers: list, hp: dict | None = None, per_layer_hp: list | None = None,
+                 R_out: list | None = None, U_out: list | None = None):
+        hp = hp or {}
+        arr = (Layer * len(layers))()
+        self._keep = list(layers) + list(R_out or []) + list(U_out or [])
+        for k, L in enumerate(layers):
+            h = per_layer_hp[k] if per_layer_hp else hp
+            ptrs = _fill_desc(arr[k].desc, L, h, R_out[k] if R_out else None,
+                              U_out[k] if U_out else None)
+            for name, val in ptrs.items():
+                setattr(arr[k], name, val)
+        handle = c_void_p()
+        _check(lib().qgalore_plan_create(arr, len(layers), ctypes.byref(handle)),
+               "qgalore_plan_create")
+        self._h = handle
+        self.workspace_bytes = int(lib().qgalore_plan_workspace_bytes(handle))
+        self.workspace = None
+
+    def step(self, t: int, seed: int, workspace=None, stream=None) -> None:
+        if workspace is None:
+            if self.workspace is None:
+                self.workspace = alloc_workspace(self.workspace_bytes, self._keep[0].Wq.device)
+            workspace = self.workspace
+        _check(lib().qgalore_plan_step(self._h, int(t), int(seed) & (2 ** 64 - 1),
+                                       _ptr(workspace, torch.uint8, None, "workspace"),
+                                       workspace.numel(), _stream(stream)), "qgalore_plan_step")
+
+    def close(self) -> None:
+        if self._h:
+            _check(lib().qgalore_plan_destroy(self._h), "qgalore_plan_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _proj(Pq, Ps, m, r) -> Proj:
+    p = Proj()
+    p.m, p.r = m, r
+    p.q = _ptr(Pq, torch.uint8, ((m * r + 1) // 2,), "P_q")
+    p.scale = _ptr(Ps, torch.float32, (n_groups(m * r),), "P_scale")
+    return p
+
+
+def cossim_workspace_bytes(m: int, r: int) -> int:
+    return int(lib().qgalore_cossim_workspace_bytes(m, r))
+
+
+def cossim_async(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, out: torch.Tensor,
+                 workspace=None, stream=None) -> None:
+    """CosSim of two stored INT4 projections into out[0] (device fp32), asynchronously."""
+    a, b = _proj(Pq_new, Ps_new, m, r), _proj(Pq_old, Ps_old, m, r)
+    if workspace is None:
+        workspace = alloc_workspace(cossim_workspace_bytes(m, r), Pq_new.device)
+    _check(lib().qgalore_cossim_async(ctypes.byref(a), ctypes.byref(b),
+                                      _ptr(workspace, torch.uint8, None, "workspace"),
+                                      workspace.numel(), _stream(stream),
+                                      _ptr(out, torch.float32, None, "out")),
+           "qgalore_cossim_async")
+
+
+def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, workspace=None, stream=None) -> float:
+    a, b = _proj(Pq_new, Ps_new, m, r), _proj(Pq_old, Ps_old, m, r)
+    if workspace is None:
+        workspace = alloc_workspace(cossim_workspace_bytes(m, r), Pq_new.device)
+    out = c_float()
+    _check(lib().qgalore_cossim(ctypes.byref(a), ctypes.byref(b),
+                                _ptr(workspace, torch.uint8, None, "workspace"),
+                                workspace.numel(), _stream(stream), ctypes.byref(out)),
+           "qgalore_cossim")
+    return float(out.value)
+
+
+def quantize_proj(P: torch.Tensor, stream=None):
+    """INT4 group quantization of an fp32 m x r projection -> (P_q uint8, P_scale fp32)."""
+    m, r = P.shape
+    Pq = torch.empty((m * r + 1) // 2, dtype=torch.uint8, device=P.device)
+    Ps = torch.empty(n_groups(m * r), dtype=torch.float32, device=P.device)
+    _check(lib().qgalore_quantize_proj(_ptr(P, torch.float32, (m, r), "P"), m, r, Pq.data_ptr(),
+                                       Ps.data_ptr(), _stream(stream)), "qgalore_quantize_proj")
+    return Pq, Ps
+
+
+class Schedule:
+    """Per-layer refresh bookkeeping (host-side, in the library)."""
+
+    def __init__(self, delta0: int, gamma: float = 0.4):
+        self._s = Sched()
+        _check(lib().qgalore_sched_init(ctypes.byref(self._s), int(delta0), float(gamma)),
+               "qgalore_sched_init")
+
+    def due(self, t: int) -> bool:
+        return bool(lib().qgalore_sched_due(ctypes.byref(self._s), int(t)))
+
+    def refresh(self, t: int, cs: float | None) -> bool:
+        doubled = c_int32(0)
+        _check(lib().qgalore_sched_refresh(ctypes.byref(self._s), int(t),
+                                           float("nan") if cs is None else float(cs),
+                                           ctypes.byref(doubled)), "qgalore_sched_refresh")
+        return bool(doubled.value)
+
+    @property
+    def delta(self) -> int:
+        return int(self._s.delta)
+
+    @property
+    def next_refresh(self) -> int:
+        return int(self._s.next_refresh)
+
+    @property
+    def count(self) -> int:
+        return int(self._s.count)
+
+    @property
+    def last_cossim(self) -> float:
+        v = float(self._s.last_cossim)
+        return v if not math.isnan(v) else float("nan")

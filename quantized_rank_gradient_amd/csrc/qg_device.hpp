@@ -1,0 +1,156 @@
+// Device-side types and helpers shared by the Q-GaLore gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kGroup = 256;     // flat elements per quantization group
+constexpr int kThreads = 256;   // threads per workgroup in every step kernel (4 wave64)
+
+// Everything one layer's kernels need. In a grouped launch the host uploads one of these per
+// layer; a single-layer launch passes it by value in the kernel arguments.
+struct LayerDev {
+  const uint16_t* G;   // bf16 m x n
+  int8_t* Wq;          // int8 m x n
+  const float* Ws;     // W group scales
+  const uint8_t* Pq;   // INT4 m x r
+  const float* Ps;     // P group scales
+  int8_t* Mq;          // int8 r x n
+  float* Ms;
+  int8_t* Vq;          // int8 r x n
+  float* Vs;
+  int64_t off_r;       // workspace byte offset: split x rpitch fp32 partial sums of R
+  int64_t off_n;       // workspace byte offset: bf16 r x n update N~
+  float* R_out;        // optional
+  float* U_out;        // optional
+  int64_t m, n, r;
+  int64_t rpitch;      // elements between split slabs of Rpart
+  uint32_t layer_id;
+  int32_t split;       // K-splits of the projection
+  int32_t kslab;       // rows of G per split (multiple of the K tile)
+  int32_t p_tiles_i;   // projection tiles along r
+  int32_t p_tiles_j;   // projection tiles along n
+  int32_t b_tiles_j;   // back-projection tiles along n
+  int32_t wg_base[3];  // first workgroup of this layer in the projection / Adam /
+                       // back-projection launch of a grouped step
+  float lr, eps, alpha;
+};
+
+struct StepArgs {
+  LayerDev one;              // the layer of a single-layer launch (table == nullptr)
+  char* ws;                  // workspace base
+  const LayerDev* table;     // grouped launch: per-layer descriptors
+  const int32_t* wg_layer;   // grouped launch: workgroup -> layer index for this kernel
+  float beta1, beta2, c1, c2, bc1, bc2;
+  uint32_t step, seed_lo, seed_hi;
+};
+
+enum { KPROJ = 0, KADAM = 1, KBACK = 2 };
+
+__device__ __forceinline__ LayerDev fetch_layer(const StepArgs& a, int kernel, int& local) {
+  if (a.table == nullptr) {
+    local = blockIdx.x;
+    return a.one;
+  }
+  const int li = a.wg_layer[blockIdx.x];
+  LayerDev L = a.table[li];
+  local = blockIdx.x - L.wg_base[kernel];
+  return L;
+}
+
+// --------------------------------------------------------------- global accesses ---
+// Loads and stores through an explicit global-address-space pointer, so that pointers that
+// come out of a layer descriptor still compile to global_* (not flat_*) instructions.
+// (The host compilation pass of this file never executes device code; it only needs the
+// functions to parse, so it takes the plain pointer.)
+template <class T>
+__device__ __forceinline__ T gload(const T* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(const __attribute__((address_space(1))) T*)(p);
+#else
+  return *p;
+#endif
+}
+template <class T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  *(__attribute__((address_space(1))) T*)(p) = v;
+#else
+  *p = v;
+#endif
+}
+
+// ---------------------------------------------------------------- numeric helpers ---
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Correctly rounded fp32 square root: the hardware estimate is within one ulp; the exact
+// residuals x - s_lo*s and x - s_hi*s (one rounding each in an fma) tell which of the
+// neighbours is nearest. A midpoint can never be an exact square root of an fp32 value,
+// so no tie occurs.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  float s = __builtin_sqrtf(x);
+  if (!(x > 0.0f) || !__builtin_isfinite(x)) return s;
+  const float s_lo = __uint_as_float(__float_as_uint(s) - 1u);
+  const float s_hi = __uint_as_float(__float_as_uint(s) + 1u);
+  const float r_lo = __builtin_fmaf(-s_lo, s, x);
+  const float r_hi = __builtin_fmaf(-s_hi, s, x);
+  if (r_lo <= 0.0f) s = s_lo;
+  if (r_hi > 0.0f) s = s_hi;
+  return s;
+}
+
+__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
+__device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
+__device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
+
+__device__ __forceinline__ float recip_or_zero(float s) {
+  return s == 0.0f ? 0.0f : div_rn(1.0f, s);
+}
+
+// Sign-extend nibble k (0..7) of a 32-bit word holding 8 packed INT4 codes.
+__device__ __forceinline__ int nibble(uint32_t w, int k) {
+  return ((int)(w << (28 - 4 * k))) >> 28;
+}
+
+// ---------------------------------------------------------------- Philox4x32-10 ---
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11),
+// Section 3: each round multiplies words 0 and 2 by the round multipliers and mixes the
+// 64-bit products' halves with words 1, 3 and the key; the key advances by the Weyl
+// constants between rounds. Ten rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// ---------------------------------------------------------------- wave reductions ---
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace qg

@@ -1,0 +1,484 @@
+// gfx950 kernels of the Q-GaLore optimizer step.
+//
+// Method: AIMech curated page "Q-GaLore (Quantized GaLore with INT4 Projection and
+// Layer-Adaptive Low-Rank Gradients)", mechanism claim "INT4 projection and INT8 stochastic
+// rounding" (paper Section 3.2): W^Q <- W^Q + xi(alpha * P^Q * G~) with INT4 P, INT8 W and
+// INT8 low-rank moments M, V; and mechanism claim "layer-adaptive subspace cosine schedule"
+// (paper Section 3.1, Equation (5)) for the similarity test.
+//
+// One step of one layer is three launches:
+//   qg_project      R (split-K partials) = P~^T G          bf16 MFMA, fp32 accumulation
+//   qg_adam         R -> Adam with INT8 M, V -> N~ (bf16)  one wave per 256-element group
+//   qg_backproject  U = alpha * P~ N~ and the stochastic rounding of W, fused
+// A grouped launch runs each kernel once over a whole table of layers.
+#include "qg_gemm.hpp"
+#include "qg_kernels.hpp"
+
+namespace qg {
+
+// ======================================================================== projection ===
+
+__global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  int local;
+  const LayerDev L = fetch_layer(a, KPROJ, local);
+  const int per_split = L.p_tiles_i * L.p_tiles_j;
+  const int s = local / per_split;
+  const int rem = local - s * per_split;
+  const int ti = rem / L.p_tiles_j;
+  const int tj = rem - ti * L.p_tiles_j;
+  const int i0 = ti * TM, j0 = tj * TN;
+  const int64_t k_begin = (int64_t)s * L.kslab;
+  const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
+
+  // A = P~^T: P is stored [k][i] (m x r), so the tile rows i are columns of P.
+  StageInt4T sa(L.Pq, L.Ps, L.r, k_end, L.r, i0);
+  StageBf16T sb(L.G, L.n, k_end, L.n, j0);
+  f32x16 acc[2][2];
+  gemm_kloop(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
+             [j0](StageBf16T& st, uint16_t* p) { st.store(p, j0); }, k_begin, k_end, lds, acc);
+
+  float* out = reinterpret_cast<float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int64_t j = j0 + acc_col(y);
+      if (j >= L.n) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + acc_row(x, v);
+        if (i < L.r) gstore(out + i * L.n + j, (float)acc[x][y][v]);
+      }
+    }
+}
+
+// ============================================================================== Adam ===
+// One wave per group of 256 flat elements of the r x n moments; lane l owns elements
+// 4l .. 4l+3 of the group.
+
+__global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
+  int local;
+  const LayerDev L = fetch_layer(a, KADAM, local);
+  const int lane = threadIdx.x & 63;
+  const int64_t numel = L.r * L.n;
+  const int64_t ngroups = (numel + kGroup - 1) / kGroup;
+  const int64_t g = (int64_t)local * (kThreads / 64) + (threadIdx.x >> 6);
+  if (g >= ngroups) return;
+  const int64_t e0 = g * kGroup + 4 * lane;
+  const bool full = e0 + 4 <= numel;
+  uint16_t* Nb = reinterpret_cast<uint16_t*>(a.ws + L.off_n);
+
+  float R[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < L.split; ++s) {
+    const float* src = reinterpret_cast<const float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch + e0;
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (full) {
+      const float4 q = gload(reinterpret_cast<const float4*>(src));
+      p[0] = q.x; p[1] = q.y; p[2] = q.z; p[3] = q.w;
+    } else {
+      for (int t = 0; t < 4; ++t)
+        if (e0 + t < numel) p[t] = gload(src + t);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) R[t] = (s == 0) ? p[t] : add_rn(R[t], p[t]);
+  }
+
+  int8_t mq[4] = {0, 0, 0, 0}, vq[4] = {0, 0, 0, 0};
+  if (full) {
+    const uint32_t wm = gload(reinterpret_cast<const uint32_t*>(L.Mq + e0));
+    const uint32_t wv = gload(reinterpret_cast<const uint32_t*>(L.Vq + e0));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mq[t] = (int8_t)(wm >> (8 * t));
+      vq[t] = (int8_t)(wv >> (8 * t));
+    }
+  } else {
+    for (int t = 0; t < 4; ++t)
+      if (e0 + t < numel) {
+        mq[t] = gload(L.Mq + e0 + t);
+        vq[t] = gload(L.Vq + e0 + t);
+      }
+  }
+  const float ms = gload(L.Ms + g), vs = gload(L.Vs + g);
+
+  float m1[4], v1[4], N[4];
+  float am = 0.f, av = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float m0 = mul_rn((float)mq[t], ms);
+    const float v0 = mul_rn((float)vq[t], vs);
+    m1[t] = add_rn(mul_rn(a.beta1, m0), mul_rn(a.c1, R[t]));
+    v1[t] = add_rn(mul_rn(a.beta2, v0), mul_rn(a.c2, mul_rn(R[t], R[t])));
+    const float mh = div_rn(m1[t], a.bc1);
+    const float vh = div_rn(v1[t], a.bc2);
+    N[t] = -div_rn(mul_rn(L.lr, mh), add_rn(sqrt_rn(vh), L.eps));
+    if (e0 + t >= numel) {
+      m1[t] = 0.f;
+      v1[t] = 0.f;
+    }
+    am = fmaxf(am, fabsf(m1[t]));
+    av = fmaxf(av, fabsf(v1[t]));
+  }
+  am = wave_max(am);
+  av = wave_max(av);
+  const float sm = div_rn(am, 127.0f), sv = div_rn(av, 127.0f);
+  const float im = recip_or_zero(sm), iv = recip_or_zero(sv);
+  uint32_t om = 0, ov = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int qm = (int)fminf(fmaxf(rintf(mul_rn(m1[t], im)), -127.f), 127.f);
+    const int qv = (int)fminf(fmaxf(rintf(mul_rn(v1[t], iv)), -127.f), 127.f);
+    om |= (uint32_t)(qm & 0xFF) << (8 * t);
+    ov |= (uint32_t)(qv & 0xFF) << (8 * t);
+  }
+  if (full) {
+    gstore(reinterpret_cast<uint32_t*>(L.Mq + e0), om);
+    gstore(reinterpret_cast<uint32_t*>(L.Vq + e0), ov);
+    gstore(reinterpret_cast<uint2*>(Nb + e0),
+           make_uint2(pack_bf16x2(N[0], N[1]), pack_bf16x2(N[2], N[3])));
+    if (L.R_out)
+      gstore(reinterpret_cast<float4*>(L.R_out + e0), make_float4(R[0], R[1], R[2], R[3]));
+  } else {
+    for (int t = 0; t < 4; ++t)
+      if (e0 + t < numel) {
+        gstore(L.Mq + e0 + t, (int8_t)(om >> (8 * t)));
+        gstore(L.Vq + e0 + t, (int8_t)(ov >> (8 * t)));
+        gstore(Nb + e0 + t, to_bf16(N[t]));
+        if (L.R_out) gstore(L.R_out + e0 + t, R[t]);
+      }
+  }
+  if (lane == 0) {
+    gstore(L.Ms + g, sm);
+    gstore(L.Vs + g, sv);
+  }
+}
+
+// ===================================================== back-projection + rounding ===
+
+// Stochastic rounding of 8 consecutive weights (i, j8 .. j8+7), j8 a multiple of 8. One
+// Philox call yields the 8 16-bit uniforms of the column block.
+__device__ __forceinline__ void sr_block8(const LayerDev& L, const StepArgs& a, int64_t i,
+                                          int64_t j8, const float* S) {
+  if (j8 >= L.n) return;
+  const uint4 ph = philox4x32_10(
+      make_uint4((uint32_t)(j8 >> 3), (uint32_t)i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
+  const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
+  const int64_t e0 = i * L.n + j8;
+  float U[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) U[t] = mul_rn(L.alpha, S[t]);
+
+  if (L.n % 8 == 0) {
+    const float inv = recip_or_zero(gload(L.Ws + (e0 >> 8)));
+    const uint2 wv = gload(reinterpret_cast<const uint2*>(L.Wq + e0));
+    const uint32_t win[2] = {wv.x, wv.y};
+    uint32_t wout[2] = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int w = (int)(int8_t)(win[t >> 2] >> (8 * (t & 3)));
+      const float tp = add_rn((float)w, mul_rn(U[t], inv));
+      const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
+      const float d = add_rn(tp, (float)bits * (1.0f / 65536.0f));
+      const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
+      wout[t >> 2] |= (uint32_t)(nw & 0xFF) << (8 * (t & 3));
+    }
+    gstore(reinterpret_cast<uint2*>(L.Wq + e0), make_uint2(wout[0], wout[1]));
+    if (L.U_out) {
+      gstore(reinterpret_cast<float4*>(L.U_out + e0), make_float4(U[0], U[1], U[2], U[3]));
+      gstore(reinterpret_cast<float4*>(L.U_out + e0 + 4), make_float4(U[4], U[5], U[6], U[7]));
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (j8 + t >= L.n) continue;
+      const int64_t e = e0 + t;
+      const float inv = recip_or_zero(gload(L.Ws + (e >> 8)));
+      const int w = gload(L.Wq + e);
+      const float tp = add_rn((float)w, mul_rn(U[t], inv));
+      const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
+      const float d = add_rn(tp, (float)bits * (1.0f / 65536.0f));
+      const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
+      gstore(L.Wq + e, (int8_t)nw);
+      if (L.U_out) gstore(L.U_out + e, U[t]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  int local;
+  const LayerDev L = fetch_layer(a, KBACK, local);
+  const int ti = local / L.b_tiles_j;
+  const int tj = local - ti * L.b_tiles_j;
+  const int i0 = ti * TM, j0 = tj * TN;
+
+  // A = P~ (rows i of P, K = rank index contiguous), B = N~ stored [k][j] (r x n).
+  StageInt4N sa(L.Pq, L.Ps, L.r, L.m, i0);
+  StageBf16T sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.n, j0);
+  f32x16 acc[2][2];
+  gemm_kloop(sa, sb, [](StageInt4N& st, uint16_t* p) { st.store(p); },
+             [j0](StageBf16T& st, uint16_t* p) { st.store(p, j0); }, 0, L.r, lds, acc);
+
+  // Redistribute each wave's 64 x 64 block through LDS, 32 rows at a time, so that every
+  // lane owns 32 consecutive columns of one row: whole Philox blocks and wide W accesses.
+  constexpr int EP = 68;   // fp32 row pitch of the staging block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        E[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + 32 * y + (lane & 31)] = acc[x][y][v];
+    __syncthreads();
+    const int rr = lane >> 1, cc = (lane & 1) * 32;
+    float S[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(E + rr * EP + cc + 4 * q);
+      S[4 * q] = f.x; S[4 * q + 1] = f.y; S[4 * q + 2] = f.z; S[4 * q + 3] = f.w;
+    }
+    const int64_t i = (int64_t)i0 + wm * 64 + 32 * x + rr;
+    const int64_t jb = (int64_t)j0 + wn * 64 + cc;
+    if (i < L.m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sr_block8(L, a, i, jb + 8 * q, S + 8 * q);
+    }
+    __syncthreads();
+  }
+}
+
+// ========================================================== INT4 quantization of P ===
+
+__global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int64_t numel,
+                                                            uint8_t* Pq, float* Ps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t ngroups = (numel + kGroup - 1) / kGroup;
+  if (g >= ngroups) return;
+  const int64_t e0 = g * kGroup + 4 * lane;
+  float x[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) x[t] = (e0 + t < numel) ? P[e0 + t] : 0.0f;
+  float am = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  am = wave_max(am);
+  const float s = div_rn(am, 7.0f);
+  const float inv = recip_or_zero(s);
+  uint32_t nib = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int q = (int)fminf(fmaxf(rintf(mul_rn(x[t], inv)), -7.f), 7.f);
+    nib |= (uint32_t)(q & 0xF) << (4 * t);
+  }
+  if (e0 + 4 <= numel) {
+    *reinterpret_cast<uint16_t*>(Pq + (e0 >> 1)) = (uint16_t)nib;
+  } else if (e0 < numel) {
+    Pq[e0 >> 1] = (uint8_t)(nib & 0xFF);
+    if (e0 + 2 < numel) Pq[(e0 >> 1) + 1] = (uint8_t)(nib >> 8);
+  }
+  if (lane == 0) Ps[g] = s;
+}
+
+// ============================================================ subspace similarity ===
+
+// Cpart[s] = P~_new^T P~_old over rows [s*kslab, (s+1)*kslab) of the two m x r projections.
+__global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosArgs c) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  const int per_split = c.tiles * c.tiles;
+  const int s = blockIdx.x / per_split;
+  const int rem = blockIdx.x - s * per_split;
+  const int ti = rem / c.tiles, tj = rem - ti * c.tiles;
+  const int i0 = ti * TM, j0 = tj * TN;
+  const int64_t k_begin = (int64_t)s * c.kslab;
+  const int64_t k_end = min<int64_t>(c.m, k_begin + c.kslab);
+  StageInt4T sa(c.qa, c.sa, c.r, k_end, c.r, i0);
+  StageInt4T sb(c.qb, c.sb, c.r, k_end, c.r, j0);
+  f32x16 acc[2][2];
+  gemm_kloop(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
+             [j0](StageInt4T& st, uint16_t* p) { st.store(p, j0); }, k_begin, k_end, lds, acc);
+  float* out = c.Cpart + (int64_t)s * c.r * c.r;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int64_t j = j0 + acc_col(y);
+      if (j >= c.r) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + acc_row(x, v);
+        if (i < c.r) gstore(out + i * c.r + j, (float)acc[x][y][v]);
+      }
+    }
+}
+
+// Sum the split partials into C (fixed order) and emit per-block sums of squares.
+__global__ __launch_bounds__(kThreads) void qg_ns_reduce(const float* Cpart, int split,
+                                                        int64_t n2, float* C, float* blocksq) {
+  __shared__ float red[kThreads];
+  float sq = 0.0f;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads * 16 + threadIdx.x;
+       e < min<int64_t>(n2, (int64_t)(blockIdx.x + 1) * kThreads * 16); e += kThreads) {
+    float v = Cpart[e];
+    for (int s = 1; s < split; ++s) v += Cpart[(int64_t)s * n2 + e];
+    C[e] = v;
+    sq += v * v;
+  }
+  red[threadIdx.x] = sq;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blocksq[blockIdx.x] = red[0];
+}
+
+// X0 = C / ||C||_F (singular values in [0, 1], inside Newton-Schulz's region of convergence).
+__global__ __launch_bounds__(kThreads) void qg_ns_init(const float* C, int64_t n2,
+                                                      const float* blocksq, int nblocks,
+                                                      float* X) {
+  __shared__ float inv_norm;
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+    for (int b = 0; b < nblocks; ++b) t += blocksq[b];
+    inv_norm = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
+  }
+  __syncthreads();
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e < n2) X[e] = C[e] * inv_norm;
+}
+
+// fp32 GEMM for the r x r polar iteration: Y = alpha * op(A) B + beta * D, op(A) = A^T when
+// TA. 64 x 64 tile per workgroup, each thread a 4 x 4 block, K staged 16 at a time in LDS.
+template <bool TA>
+__global__ __launch_bounds__(kThreads) void qg_gemm_f32(const float* A, const float* B,
+                                                       const float* D, float* Y, int n,
+                                                       float alpha, float beta) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tiles = (n + 63) / 64;
+  const int bi = blockIdx.x / tiles, bj = blockIdx.x - bi * tiles;
+  const int i0 = bi * 64, j0 = bj * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    for (int l = threadIdx.x; l < 16 * 64; l += kThreads) {
+      const int kk = l >> 6, c = l & 63;
+      const int k = k0 + kk;
+      float av = 0.0f, bv = 0.0f;
+      if (k < n && i0 + c < n) av = TA ? A[(int64_t)k * n + i0 + c] : A[(int64_t)(i0 + c) * n + k];
+      if (k < n && j0 + c < n) bv = B[(int64_t)k * n + j0 + c];
+      As[kk][c] = av;
+      Bs[kk][c] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float ar[4], br[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ar[u] = As[kk][ty * 4 + u];
+        br[u] = Bs[kk][tx * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = __builtin_fmaf(ar[u], br[w], acc[u][w]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = i0 + ty * 4 + u, j = j0 + tx * 4 + w;
+      if (i < n && j < n) {
+        const int64_t e = (int64_t)i * n + j;
+        float y = alpha * acc[u][w];
+        if (D) y = __builtin_fmaf(beta, D[e], y);
+        Y[e] = y;
+      }
+    }
+}
+
+// Per-block partial sums of X .* C (the nuclear norm is trace(X^T C) at convergence).
+__global__ __launch_bounds__(kThreads) void qg_ns_trace(const float* X, const float* C,
+                                                       int64_t n2, float* blocksum) {
+  __shared__ float red[kThreads];
+  float acc = 0.0f;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads * 16 + threadIdx.x;
+       e < min<int64_t>(n2, (int64_t)(blockIdx.x + 1) * kThreads * 16); e += kThreads)
+    acc = __builtin_fmaf(X[e], C[e], acc);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
+}
+
+__global__ void qg_ns_finish(const float* blocksum, int nblocks, float inv_r, float* out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    double t = 0.0;
+    for (int b = 0; b < nblocks; ++b) t += blocksum[b];
+    out[0] = (float)(t * inv_r);
+  }
+}
+
+// ==================================================================== launchers ===
+
+hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(qg_project, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(qg_adam, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_backproject(const StepArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(qg_backproject, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,
+                                hipStream_t s) {
+  const int64_t groups = (numel + kGroup - 1) / kGroup;
+  const int grid = (int)((groups + 3) / 4);
+  hipLaunchKernelGGL(qg_quantize_int4, dim3(grid), dim3(kThreads), 0, s, P, numel, Pq, Ps);
+  return hipGetLastError();
+}
+
+hipError_t launch_cossim(const CosArgs& c, const CosWork& w, float* out, hipStream_t s) {
+  const int64_t n2 = (int64_t)c.r * c.r;
+  const int grid_gemm = c.tiles * c.tiles * c.split;
+  hipLaunchKernelGGL(qg_cossim_gemm, dim3(grid_gemm), dim3(kThreads), 0, s, c);
+  const int nred = (int)((n2 + kThreads * 16 - 1) / (kThreads * 16));
+  hipLaunchKernelGGL(qg_ns_reduce, dim3(nred), dim3(kThreads), 0, s, (const float*)c.Cpart,
+                     c.split, n2, w.C, w.blocks);
+  const int nel = (int)((n2 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(qg_ns_init, dim3(nel), dim3(kThreads), 0, s, (const float*)w.C, n2,
+                     (const float*)w.blocks, nred, w.X);
+  const int ft = (c.r + 63) / 64;
+  float* X = w.X;
+  float* Xn = w.Xn;
+  for (int it = 0; it < w.iters; ++it) {
+    // A = X^T X ; X <- 1.5 X - 0.5 X A
+    hipLaunchKernelGGL(qg_gemm_f32<true>, dim3(ft * ft), dim3(kThreads), 0, s, (const float*)X,
+                       (const float*)X, (const float*)nullptr, w.A, (int)c.r, 1.0f, 0.0f);
+    hipLaunchKernelGGL(qg_gemm_f32<false>, dim3(ft * ft), dim3(kThreads), 0, s, (const float*)X,
+                       (const float*)w.A, (const float*)X, Xn, (int)c.r, -0.5f, 1.5f);
+    float* t = X;
+    X = Xn;
+    Xn = t;
+  }
+  hipLaunchKernelGGL(qg_ns_trace, dim3(nred), dim3(kThreads), 0, s, (const float*)X,
+                     (const float*)w.C, n2, w.blocks);
+  hipLaunchKernelGGL(qg_ns_finish, dim3(1), dim3(64), 0, s, (const float*)w.blocks, nred,
+                     1.0f / (float)c.r, out);
+  return hipGetLastError();
+}
+
+}  // namespace qg

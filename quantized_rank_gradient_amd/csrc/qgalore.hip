@@ -1,0 +1,492 @@
+// Host side of the C ABI: argument validation, work partitioning, workspace layout and
+// launches. Every entry point validates its arguments completely before the first HIP call.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "qg_kernels.hpp"
+#include "qgalore.h"
+
+using qg::LayerDev;
+using qg::StepArgs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qg_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return QG_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+bool finite(float x) { return std::isfinite(x); }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kTile = 128;   // output tile edge of the MFMA kernels
+constexpr int kK = 32;       // K per stage of the MFMA kernels
+
+qg_status device_present() {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    cached = (e == hipSuccess && n > 0) ? 1 : 0;
+  }
+  return cached ? QG_OK : QG_ERR_NO_DEVICE;
+}
+
+qg_status check_shape(int64_t m, int64_t n, int64_t r) {
+  if (m < 1 || n < 1 || r < 1 || m > kMaxDim || n > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
+  if (r > m || r % 8 != 0) return QG_ERR_SHAPE;
+  if (cdiv(m, kTile) * cdiv(n, kTile) > kMaxDim / 2) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+// K-splits of the projection R = P~^T G for one layer launched on its own: enough
+// workgroups to cover the chip, bounded so the fp32 partial sums stay small next to G.
+int choose_split(int64_t m, int64_t n, int64_t r) {
+  const int64_t tiles = cdiv(r, kTile) * cdiv(n, kTile);
+  const int64_t kchunks = cdiv(m, kK);
+  int64_t s = cdiv(512, tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, m / (8 * r)));
+  s = std::min<int64_t>(s, kchunks);
+  s = std::max<int64_t>(s, 1);
+  const int64_t kslab = cdiv(kchunks, s) * kK;
+  return (int)cdiv(m, kslab);
+}
+int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kK), split) * kK; }
+
+struct WsLayout {
+  int64_t rpitch, off_r, off_n, bytes;
+};
+WsLayout ws_layout(int64_t n, int64_t r, int split, int64_t base) {
+  WsLayout w;
+  w.rpitch = round_up(r * n, 64);
+  w.off_r = base;
+  w.off_n = base + round_up((int64_t)split * w.rpitch * 4, 256);
+  w.bytes = (w.off_n - base) + round_up(r * n * 2, 256);
+  return w;
+}
+
+struct Hyper {
+  float lr, beta1, beta2, eps, alpha;
+};
+qg_status check_hyper(const qg_layer_desc* d) {
+  if (!finite(d->lr) || !finite(d->beta1) || !finite(d->beta2) || !finite(d->eps) ||
+      !finite(d->alpha))
+    return QG_ERR_ARG;
+  if (d->beta1 < 0.f || d->beta1 >= 1.f || d->beta2 < 0.f || d->beta2 >= 1.f || d->eps < 0.f)
+    return QG_ERR_ARG;
+  return QG_OK;
+}
+
+qg_status check_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, const float* W_scale,
+                      const uint8_t* P_q, const float* P_scale, int8_t* M_q, int8_t* V_q) {
+  if (!d || !G || !W_q || !W_scale || !P_q || !P_scale || !M_q || !V_q || !d->M_scale ||
+      !d->V_scale)
+    return QG_ERR_NULL;
+  qg_status st = check_shape(d->m, d->n, d->r);
+  if (st != QG_OK) return st;
+  if (!aligned(G, 16) || !aligned(W_q, 16) || !aligned(M_q, 16) || !aligned(V_q, 16) ||
+      !aligned(d->R_out, 16) || !aligned(d->U_out, 16) || !aligned(W_scale, 4) ||
+      !aligned(P_q, 4) || !aligned(P_scale, 4) || !aligned(d->M_scale, 4) ||
+      !aligned(d->V_scale, 4))
+    return QG_ERR_ALIGN;
+  return check_hyper(d);
+}
+
+qg_status check_step(int64_t step) {
+  return (step >= 1 && step < (int64_t(1) << 32)) ? QG_OK : QG_ERR_ARG;
+}
+
+// Adam's per-step constants: computed in double from the fp32 hyperparameters and rounded
+// once to fp32 (pow from the C library).
+void step_constants(float beta1, float beta2, int64_t step, StepArgs& a) {
+  const double b1 = beta1, b2 = beta2;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.c1 = (float)(1.0 - b1);
+  a.c2 = (float)(1.0 - b2);
+  a.bc1 = (float)(1.0 - std::pow(b1, (double)step));
+  a.bc2 = (float)(1.0 - std::pow(b2, (double)step));
+  a.step = (uint32_t)step;
+}
+
+LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, const float* W_scale,
+                    const uint8_t* P_q, const float* P_scale, int8_t* M_q, int8_t* V_q,
+                    int split, int64_t ws_base) {
+  LayerDev L;
+  std::memset(&L, 0, sizeof(L));
+  L.G = G;
+  L.Wq = W_q;
+  L.Ws = W_scale;
+  L.Pq = P_q;
+  L.Ps = P_scale;
+  L.Mq = M_q;
+  L.Ms = d->M_scale;
+  L.Vq = V_q;
+  L.Vs = d->V_scale;
+  L.R_out = d->R_out;
+  L.U_out = d->U_out;
+  L.m = d->m;
+  L.n = d->n;
+  L.r = d->r;
+  const WsLayout w = ws_layout(d->n, d->r, split, ws_base);
+  L.rpitch = w.rpitch;
+  L.off_r = w.off_r;
+  L.off_n = w.off_n;
+  L.layer_id = d->layer_id;
+  L.split = split;
+  L.kslab = (int32_t)kslab_for(d->m, split);
+  L.p_tiles_i = (int32_t)cdiv(d->r, kTile);
+  L.p_tiles_j = (int32_t)cdiv(d->n, kTile);
+  L.b_tiles_j = (int32_t)cdiv(d->n, kTile);
+  L.lr = d->lr;
+  L.eps = d->eps;
+  L.alpha = d->alpha;
+  return L;
+}
+
+int grid_project(const LayerDev& L) { return L.split * L.p_tiles_i * L.p_tiles_j; }
+int grid_adam(const LayerDev& L) { return (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4); }
+int grid_back(const LayerDev& L) { return (int)(cdiv(L.m, kTile) * L.b_tiles_j); }
+
+qg_status launch_step(const StepArgs& a, const int grid[3], hipStream_t s) {
+  hipError_t e = qg::launch_project(a, grid[0], s);
+  if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+  e = qg::launch_adam(a, grid[1], s);
+  if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
+  e = qg::launch_backproject(a, grid[2], s);
+  if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
+  return QG_OK;
+}
+
+}  // namespace
+
+// ===================================================================== single layer ===
+
+extern "C" size_t qgalore_workspace_bytes(int64_t m, int64_t n, int64_t r) {
+  if (check_shape(m, n, r) != QG_OK) return 0;
+  return (size_t)ws_layout(n, r, choose_split(m, n, r), 0).bytes;
+}
+
+extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q,
+                                  const float* W_scale, const uint8_t* P_q, const float* P_scale,
+                                  int8_t* M_q, int8_t* V_q, int64_t step, uint64_t seed) {
+  qg_status st = check_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q);
+  if (st != QG_OK) return st;
+  if ((st = check_step(step)) != QG_OK) return st;
+  const int split = choose_split(d->m, d->n, d->r);
+  const WsLayout w = ws_layout(d->n, d->r, split, 0);
+  if (!d->workspace) return QG_ERR_NULL;
+  if (!aligned(d->workspace, 16)) return QG_ERR_ALIGN;
+  if (d->workspace_bytes < (size_t)w.bytes) return QG_ERR_WORKSPACE;
+  if ((st = device_present()) != QG_OK) return st;
+
+  StepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.one = make_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q, split, 0);
+  a.ws = static_cast<char*>(d->workspace);
+  a.table = nullptr;
+  a.wg_layer = nullptr;
+  step_constants(d->beta1, d->beta2, step, a);
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  const int grid[3] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one)};
+  return launch_step(a, grid, static_cast<hipStream_t>(d->stream));
+}
+
+// ========================================================================= grouped ===
+
+struct qg_plan {
+  std::vector<LayerDev> layers;
+  LayerDev* d_table = nullptr;
+  int32_t* d_map[3] = {nullptr, nullptr, nullptr};
+  int grid[3] = {0, 0, 0};
+  int64_t ws_bytes = 0;
+  float beta1 = 0.f, beta2 = 0.f;
+  int device = 0;
+};
+
+extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, qg_plan** out) {
+  if (!layers || !out) return QG_ERR_NULL;
+  *out = nullptr;
+  if (count < 1) return QG_ERR_ARG;
+  for (int32_t l = 0; l < count; ++l) {
+    const qg_layer& x = layers[l];
+    qg_status st = check_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q);
+    if (st != QG_OK) return st;
+    if (x.desc.beta1 != layers[0].desc.beta1 || x.desc.beta2 != layers[0].desc.beta2)
+      return QG_ERR_ARG;
+  }
+  qg_status st = device_present();
+  if (st != QG_OK) return st;
+
+  // One K-split for every layer unless the whole set has too few projection tiles.
+  int64_t tiles = 0;
+  for (int32_t l = 0; l < count; ++l)
+    tiles += cdiv(layers[l].desc.r, kTile) * cdiv(layers[l].desc.n, kTile);
+  const bool grouped_fill = tiles >= 1024;
+
+  qg_plan* p = new (std::nothrow) qg_plan();
+  if (!p) return QG_ERR_ARG;
+  p->beta1 = layers[0].desc.beta1;
+  p->beta2 = layers[0].desc.beta2;
+  int64_t ws = 0;
+  int64_t base[3] = {0, 0, 0};
+  std::vector<int32_t> map[3];
+  for (int32_t l = 0; l < count; ++l) {
+    const qg_layer& x = layers[l];
+    const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
+    LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
+                            split, ws);
+    ws += ws_layout(x.desc.n, x.desc.r, split, ws).bytes;
+    const int g[3] = {grid_project(L), grid_adam(L), grid_back(L)};
+    for (int k = 0; k < 3; ++k) {
+      if (base[k] + g[k] > kMaxDim) {
+        delete p;
+        return QG_ERR_SHAPE;
+      }
+      L.wg_base[k] = (int32_t)base[k];
+      map[k].insert(map[k].end(), (size_t)g[k], l);
+      base[k] += g[k];
+    }
+    p->layers.push_back(L);
+  }
+  p->ws_bytes = ws;
+  for (int k = 0; k < 3; ++k) p->grid[k] = (int)base[k];
+
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = hipMalloc(&p->d_table, sizeof(LayerDev) * count);
+  for (int k = 0; k < 3 && e == hipSuccess; ++k)
+    e = hipMalloc(&p->d_map[k], sizeof(int32_t) * map[k].size());
+  if (e == hipSuccess)
+    e = hipMemcpy(p->d_table, p->layers.data(), sizeof(LayerDev) * count, hipMemcpyHostToDevice);
+  for (int k = 0; k < 3 && e == hipSuccess; ++k)
+    e = hipMemcpy(p->d_map[k], map[k].data(), sizeof(int32_t) * map[k].size(),
+                  hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    qgalore_plan_destroy(p);
+    return hip_fail(e, "plan upload");
+  }
+  *out = p;
+  return QG_OK;
+}
+
+extern "C" size_t qgalore_plan_workspace_bytes(const qg_plan* p) {
+  return p ? (size_t)p->ws_bytes : 0;
+}
+
+extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!p || !workspace) return QG_ERR_NULL;
+  qg_status st = check_step(step);
+  if (st != QG_OK) return st;
+  if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+  if (workspace_bytes < (size_t)p->ws_bytes) return QG_ERR_WORKSPACE;
+  StepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ws = static_cast<char*>(workspace);
+  a.table = p->d_table;
+  step_constants(p->beta1, p->beta2, step, a);
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  a.wg_layer = p->d_map[0];
+  hipError_t e = qg::launch_project(a, p->grid[0], s);
+  if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+  a.wg_layer = p->d_map[1];
+  e = qg::launch_adam(a, p->grid[1], s);
+  if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
+  a.wg_layer = p->d_map[2];
+  e = qg::launch_backproject(a, p->grid[2], s);
+  if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
+  return QG_OK;
+}
+
+extern "C" qg_status qgalore_plan_destroy(qg_plan* p) {
+  if (!p) return QG_ERR_NULL;
+  hipError_t e = hipSuccess;
+  if (p->d_table) e = hipFree(p->d_table);
+  for (int k = 0; k < 3; ++k)
+    if (p->d_map[k]) {
+      const hipError_t e2 = hipFree(p->d_map[k]);
+      if (e == hipSuccess) e = e2;
+    }
+  delete p;
+  return e == hipSuccess ? QG_OK : hip_fail(e, "plan free");
+}
+
+// ============================================================ subspace similarity ===
+
+namespace {
+constexpr int kNsIters = 48;
+
+struct CosLayout {
+  int split, kslab, tiles, nred;
+  int64_t off_part, off_c, off_x, off_xn, off_a, off_blocks, off_out, bytes;
+};
+CosLayout cos_layout(int64_t m, int64_t r) {
+  CosLayout c;
+  c.tiles = (int)cdiv(r, kTile);
+  const int64_t kchunks = cdiv(m, kK);
+  int64_t s = std::max<int64_t>(1, cdiv(256, (int64_t)c.tiles * c.tiles));
+  s = std::min<int64_t>(s, kchunks);
+  c.kslab = (int)(cdiv(kchunks, s) * kK);
+  c.split = (int)cdiv(m, c.kslab);
+  const int64_t n2 = r * r;
+  c.nred = (int)cdiv(n2, qg::kThreads * 16);
+  const int64_t mat = round_up(n2 * 4, 256);
+  c.off_part = 0;
+  c.off_c = c.off_part + round_up((int64_t)c.split * n2 * 4, 256);
+  c.off_x = c.off_c + mat;
+  c.off_xn = c.off_x + mat;
+  c.off_a = c.off_xn + mat;
+  c.off_blocks = c.off_a + mat;
+  c.off_out = c.off_blocks + round_up((int64_t)c.nred * 4, 256);
+  c.bytes = c.off_out + 256;
+  return c;
+}
+
+qg_status check_proj(const qg_proj* p) {
+  if (!p || !p->q || !p->scale) return QG_ERR_NULL;
+  if (p->m < 1 || p->r < 1 || p->m > kMaxDim || p->r > 8192 || p->r > p->m || p->r % 8 != 0)
+    return QG_ERR_SHAPE;
+  if (!aligned(p->q, 4) || !aligned(p->scale, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+}  // namespace
+
+extern "C" size_t qgalore_cossim_workspace_bytes(int64_t m, int64_t r) {
+  if (m < 1 || r < 1 || r > m || r % 8 != 0 || r > 8192) return 0;
+  return (size_t)cos_layout(m, r).bytes;
+}
+
+extern "C" qg_status qgalore_cossim_async(const qg_proj* P_new, const qg_proj* P_old,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          float* out_dev) {
+  qg_status st = check_proj(P_new);
+  if (st != QG_OK) return st;
+  if ((st = check_proj(P_old)) != QG_OK) return st;
+  if (P_new->m != P_old->m || P_new->r != P_old->r) return QG_ERR_SHAPE;
+  if (!workspace || !out_dev) return QG_ERR_NULL;
+  if (!aligned(workspace, 16) || !aligned(out_dev, 4)) return QG_ERR_ALIGN;
+  const CosLayout c = cos_layout(P_new->m, P_new->r);
+  if (workspace_bytes < (size_t)c.bytes) return QG_ERR_WORKSPACE;
+  if ((st = device_present()) != QG_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  qg::CosArgs ca;
+  ca.qa = P_new->q;
+  ca.sa = P_new->scale;
+  ca.qb = P_old->q;
+  ca.sb = P_old->scale;
+  ca.m = P_new->m;
+  ca.r = (int)P_new->r;
+  ca.tiles = c.tiles;
+  ca.split = c.split;
+  ca.kslab = c.kslab;
+  ca.Cpart = reinterpret_cast<float*>(ws + c.off_part);
+  qg::CosWork cw;
+  cw.C = reinterpret_cast<float*>(ws + c.off_c);
+  cw.X = reinterpret_cast<float*>(ws + c.off_x);
+  cw.Xn = reinterpret_cast<float*>(ws + c.off_xn);
+  cw.A = reinterpret_cast<float*>(ws + c.off_a);
+  cw.blocks = reinterpret_cast<float*>(ws + c.off_blocks);
+  cw.iters = kNsIters;
+  const hipError_t e = qg::launch_cossim(ca, cw, out_dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QG_OK : hip_fail(e, "similarity kernels");
+}
+
+extern "C" qg_status qgalore_cossim(const qg_proj* P_new, const qg_proj* P_old, void* workspace,
+                                    size_t workspace_bytes, void* stream, float* out_host) {
+  if (!out_host) return QG_ERR_NULL;
+  qg_status st = check_proj(P_new);
+  if (st != QG_OK) return st;
+  if ((st = check_proj(P_old)) != QG_OK) return st;
+  if (P_new->m != P_old->m || P_new->r != P_old->r) return QG_ERR_SHAPE;
+  const CosLayout c = cos_layout(P_new->m, P_new->r);
+  if (!workspace) return QG_ERR_NULL;
+  if (workspace_bytes < (size_t)c.bytes) return QG_ERR_WORKSPACE;
+  float* dev_out = reinterpret_cast<float*>(static_cast<char*>(workspace) + c.off_out);
+  st = qgalore_cossim_async(P_new, P_old, workspace, workspace_bytes, stream, dev_out);
+  if (st != QG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out_host, dev_out, sizeof(float), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? QG_OK : hip_fail(e, "similarity read-back");
+}
+
+// ==================================================================== quantize P ===
+
+extern "C" qg_status qgalore_quantize_proj(const float* P, int64_t m, int64_t r, uint8_t* P_q,
+                                           float* P_scale, void* stream) {
+  if (!P || !P_q || !P_scale) return QG_ERR_NULL;
+  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
+  if (!aligned(P, 16) || !aligned(P_q, 4) || !aligned(P_scale, 4)) return QG_ERR_ALIGN;
+  qg_status st = device_present();
+  if (st != QG_OK) return st;
+  const hipError_t e =
+      qg::launch_quantize_int4(P, m * r, P_q, P_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QG_OK : hip_fail(e, "INT4 quantization kernel");
+}
+
+// ====================================================================== schedule ===
+
+extern "C" qg_status qgalore_sched_init(qg_sched* s, int64_t delta0, float gamma) {
+  if (!s) return QG_ERR_NULL;
+  if (delta0 < 1 || !finite(gamma)) return QG_ERR_ARG;
+  s->delta = delta0;
+  s->next_refresh = 0;
+  s->count = 0;
+  s->gamma = gamma;
+  s->last_cossim = NAN;
+  return QG_OK;
+}
+
+extern "C" int32_t qgalore_sched_due(const qg_sched* s, int64_t t) {
+  if (!s) return -1;
+  return t >= s->next_refresh ? 1 : 0;
+}
+
+extern "C" qg_status qgalore_sched_refresh(qg_sched* s, int64_t t, float cossim, int32_t* doubled) {
+  if (!s) return QG_ERR_NULL;
+  int32_t d = 0;
+  if (s->count > 0) {
+    if (std::isnan(cossim)) return QG_ERR_ARG;
+    s->last_cossim = cossim;
+    if (cossim > s->gamma) {
+      if (s->delta > (int64_t(1) << 61)) return QG_ERR_ARG;
+      s->delta *= 2;
+      d = 1;
+    }
+  }
+  s->count += 1;
+  s->next_refresh = t + s->delta;
+  if (doubled) *doubled = d;
+  return QG_OK;
+}
+
+// ========================================================================= misc ===
+
+extern "C" const char* qgalore_status_str(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "null pointer argument";
+    case QG_ERR_SHAPE: return "invalid shape";
+    case QG_ERR_ALIGN: return "misaligned pointer";
+    case QG_ERR_WORKSPACE: return "workspace too small";
+    case QG_ERR_ARG: return "invalid argument";
+    case QG_ERR_HIP: return "HIP runtime error";
+    case QG_ERR_NO_DEVICE: return "no HIP device";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* qgalore_last_error(void) { return g_last_error.c_str(); }
+extern "C" const char* qgalore_version(void) { return "qgalore-gfx950 0.1.0"; }

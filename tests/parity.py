@@ -1,0 +1,131 @@
+"""Helpers shared by the GPU parity tests: building one layer's state on both sides from the
+seeded generators, and the comparison rules.
+
+Comparison rules (GPU against the oracle, same seeded inputs):
+  * fp32 R and U: |gpu - oracle| <= 2e-3 * |oracle| + 2e-3 * rms(oracle) elementwise.
+  * INT8 codes (W, M, V): identical, except +-1 differences at elements whose rounding input
+    sits at a decision boundary within the reach of the tolerated fp32 difference. For W the
+    rounding input is d = W + U/s + u and the boundary an integer; for M and V it is x * inv
+    and the boundary a half-integer. An element's allowed reach is
+        1e-5 + |input_gpu - input_oracle| estimated from the fp32 difference of its source
+    (U for W, R for M and V). At most 1e-4 of the elements may differ.
+  * Group scales of M and V: relative difference <= 1e-5.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import qgalore_oracle as O
+from quantized_rank_gradient_amd import workloads as WL
+
+F32 = np.float32
+
+
+def host_state(cfg, L, r, moments="zero", P=None):
+    """Oracle-side state of one layer (numpy) and the float projection it was made from."""
+    if P is None:
+        P = WL.orthonormal_f32(cfg, L, r)
+    Pq, Ps = O.quantize_proj(P)
+    if moments == "zero":
+        Mq, Ms, Vq, Vs = WL.zero_moments(r, L.n)
+    else:
+        Mq, Ms, Vq, Vs = WL.random_moments(cfg, L, r)
+    st = O.LayerState(L.m, L.n, r, L.layer_id, WL.weights_int8(cfg, L), WL.weight_scales(cfg, L),
+                      Pq, Ps, Mq, Ms, Vq, Vs)
+    return st, P
+
+
+def to_device(st, G_bits, P_float=None, quantize_on_gpu=True):
+    """GPU-side tensors for the library. The projection is quantized by the library's own
+    kernel from the same float P when `quantize_on_gpu` (the caller checks it against the
+    oracle's codes)."""
+    import torch
+    from quantized_rank_gradient_amd import binding as B
+    dev = torch.device("cuda:0")
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    if quantize_on_gpu and P_float is not None:
+        Pq, Ps = B.quantize_proj(t(P_float.astype(F32)))
+    else:
+        Pq, Ps = t(st.Pq), t(st.Ps)
+    G = t(G_bits.view(np.int16)).view(torch.bfloat16).reshape(st.m, st.n)
+    return B.LayerTensors(layer_id=st.layer_id, G=G, Wq=t(st.Wq), Ws=t(st.Ws), Pq=Pq, Ps=Ps,
+                          Mq=t(st.Mq), Ms=t(st.Ms), Vq=t(st.Vq), Vs=t(st.Vs), r=st.r)
+
+
+def assert_close_f32(gpu, ref, name, rtol=2e-3):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = np.abs(gpu - ref)
+    bound = rtol * np.abs(ref) + rtol * rms
+    bad = err > bound
+    assert not bad.any(), (f"{name}: {int(bad.sum())} of {ref.size} outside tolerance; worst "
+                           f"{float(err.max()):.3e} vs rms {rms:.3e}")
+
+
+def assert_codes(gpu, ref, x_ref, boundary, reach, name, cap=1e-4):
+    """INT8 code parity. x_ref: the oracle's rounding input; boundary: 'int' (floor) or 'half'
+    (round-half-even); reach: per-element allowed distance from the boundary."""
+    gpu = np.asarray(gpu).astype(np.int32).ravel()
+    ref = np.asarray(ref).astype(np.int32).ravel()
+    x = np.asarray(x_ref, np.float64).ravel()
+    diff = gpu - ref
+    bad = diff != 0
+    if not bad.any():
+        return 0
+    assert np.all(np.abs(diff) <= 1), f"{name}: a code differs by more than 1"
+    if boundary == "int":
+        margin = np.abs(x - np.rint(x))
+    else:
+        margin = np.abs(np.abs(x - np.floor(x)) - 0.5)
+    reach = np.broadcast_to(np.asarray(reach, np.float64), x.shape)
+    unexplained = bad & ~(margin <= reach)
+    assert not unexplained.any(), (
+        f"{name}: {int(unexplained.sum())} differing codes away from a rounding boundary "
+        f"(margins {margin[unexplained][:5]}, reach {reach[unexplained][:5]})")
+    frac = bad.mean()
+    assert frac <= cap, f"{name}: {int(bad.sum())} differing codes ({frac:.2e} > {cap})"
+    return int(bad.sum())
+
+
+def check_step(st_before, res, st_after, gpu_out, hp=O.Hyper(), rows=None):
+    """Compare one GPU step (gpu_out: dict of numpy arrays R, U, Wq, Mq, Ms, Vq, Vs) with the
+    oracle's step `res` that took `st_before` to `st_after`."""
+    assert_close_f32(gpu_out["R"], res.R, "R")
+    U_gpu = gpu_out["U"] if rows is None else gpu_out["U"][np.asarray(rows)]
+    assert_close_f32(U_gpu, res.U, "U")
+
+    # M and V: the rounding input is m1 * inv; the GPU's differs through R (and the scale)
+    g = np.arange(res.m1.size) // O.GROUP
+    invM = O.reciprocal_or_zero(st_after.Ms)[g]
+    invV = O.reciprocal_or_zero(st_after.Vs)[g]
+    c1, c2, _, _ = O.adam_constants(1, hp)
+    dR = np.abs(gpu_out["R"].astype(np.float64) - res.R.astype(np.float64)).ravel()
+    R64 = np.abs(res.R.astype(np.float64)).ravel()
+    xm = res.m1.astype(np.float64).ravel() * invM
+    xv = res.v1.astype(np.float64).ravel() * invV
+    invM_g = O.reciprocal_or_zero(gpu_out["Ms"])[g].astype(np.float64)
+    invV_g = O.reciprocal_or_zero(gpu_out["Vs"])[g].astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel_m = np.where(invM > 0, np.abs(invM_g / invM - 1.0), 0.0)
+        rel_v = np.where(invV > 0, np.abs(invV_g / invV - 1.0), 0.0)
+    reach_m = 1e-5 + 2 * np.float64(c1) * dR * invM + np.abs(xm) * (rel_m + 2e-7)
+    reach_v = 1e-5 + 2 * np.float64(c2) * 2 * R64 * dR * invV + np.abs(xv) * (rel_v + 2e-7)
+    assert np.allclose(gpu_out["Ms"], st_after.Ms, rtol=1e-5, atol=0), "M scales"
+    assert np.allclose(gpu_out["Vs"], st_after.Vs, rtol=1e-5, atol=0), "V scales"
+    assert_codes(gpu_out["Mq"], st_after.Mq, xm, "half", reach_m, "M")
+    assert_codes(gpu_out["Vq"], st_after.Vq, xv, "half", reach_v, "V")
+
+    # W: rounding input d = W + U * inv_s + u
+    Wg = gpu_out["Wq"] if rows is None else gpu_out["Wq"][np.asarray(rows)]
+    Wr = st_after.Wq if rows is None else st_after.Wq[np.asarray(rows)]
+    n = st_before.n
+    rows_idx = np.arange(Wr.shape[0]) if rows is None else np.asarray(rows)
+    e = (rows_idx[:, None] * n + np.arange(n)[None, :]).ravel()
+    inv = O.reciprocal_or_zero(st_before.Ws)[e // O.GROUP].astype(np.float64)
+    dU = np.abs(U_gpu.astype(np.float64) - res.U.astype(np.float64)).ravel()
+    reach_w = 1e-5 + dU * inv + 2 * np.spacing(np.float32(128.0))
+    return assert_codes(Wg, Wr, res.d, "int", reach_w, "W")

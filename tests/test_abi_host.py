@@ -1,0 +1,132 @@
+"""Host-only tests of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments with the documented status before touching HIP. No kernel runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import qgalore_oracle as O
+from quantized_rank_gradient_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgalore.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgalore_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(B.EXPORTS), "binding and header disagree"
+    assert L.qgalore_version().startswith(b"qgalore")
+
+
+def test_struct_layouts_match_header_sizes():
+    # int64 x3 + uint32 + 5 floats = 48 bytes, then 6 pointers and a size_t
+    assert ctypes.sizeof(B.LayerDesc) == 48 + 7 * 8
+    assert ctypes.sizeof(B.Layer) == ctypes.sizeof(B.LayerDesc) + 7 * 8
+    assert ctypes.sizeof(B.Proj) == 32
+    assert ctypes.sizeof(B.Sched) == 32
+
+
+def _desc(m=256, n=256, r=32, **kw):
+    d = B.LayerDesc()
+    d.m, d.n, d.r, d.layer_id = m, n, r, 0
+    d.lr, d.beta1, d.beta2, d.eps, d.alpha = 1e-3, 0.9, 0.999, 1e-8, 0.25
+    fake = 0x10000
+    d.M_scale = d.V_scale = fake
+    d.workspace = fake
+    d.workspace_bytes = 1 << 40
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _call(d, G=0x10000, W=0x10000, Ws=0x10000, Pq=0x10000, Ps=0x10000, M=0x10000, V=0x10000,
+          step=1):
+    return B.lib().qgalore_step(ctypes.byref(d), G, W, Ws, Pq, Ps, M, V, step, 1234)
+
+
+def test_step_validation_codes_without_touching_the_device():
+    assert _call(_desc(), G=None) == 1
+    assert _call(_desc(M_scale=None)) == 1
+    assert _call(_desc(r=0)) == 2
+    assert _call(_desc(r=300, m=256)) == 2          # r > m
+    assert _call(_desc(r=12)) == 2                  # r % 8 != 0
+    assert _call(_desc(n=0)) == 2
+    assert _call(_desc(), G=0x10001) == 3            # misaligned
+    assert _call(_desc(), Ws=0x10002) == 3
+    assert _call(_desc(), step=0) == 5
+    assert _call(_desc(), step=1 << 32) == 5
+    assert _call(_desc(beta1=1.0)) == 5
+    assert _call(_desc(eps=float("nan"))) == 5
+    assert _call(_desc(workspace_bytes=16)) == 4
+    assert _call(_desc(workspace=None)) == 1
+
+
+def test_workspace_size_query():
+    assert B.lib().qgalore_workspace_bytes(256, 256, 32) >= 256 * 32 * (4 + 2)
+    assert B.lib().qgalore_workspace_bytes(4096, 4096, 1024) >= 4096 * 1024 * 6
+    assert B.lib().qgalore_workspace_bytes(256, 256, 12) == 0
+    assert B.lib().qgalore_cossim_workspace_bytes(4096, 128) >= 5 * 128 * 128 * 4
+    assert B.lib().qgalore_cossim_workspace_bytes(100, 128) == 0
+
+
+def test_other_entry_points_validate_first():
+    L = B.lib()
+    p = B.Proj(m=256, r=32, q=0x10000, scale=0x10000)
+    bad = B.Proj(m=256, r=32, q=None, scale=0x10000)
+    out = ctypes.c_float()
+    assert L.qgalore_cossim(ctypes.byref(bad), ctypes.byref(p), 0x10000, 1 << 30, None,
+                            ctypes.byref(out)) == 1
+    q2 = B.Proj(m=128, r=32, q=0x10000, scale=0x10000)
+    assert L.qgalore_cossim(ctypes.byref(q2), ctypes.byref(p), 0x10000, 1 << 30, None,
+                            ctypes.byref(out)) == 2
+    assert L.qgalore_cossim(ctypes.byref(p), ctypes.byref(p), 0x10000, 16, None,
+                            ctypes.byref(out)) == 4
+    assert L.qgalore_quantize_proj(None, 4, 4, 0x10000, 0x10000, None) == 1
+    assert L.qgalore_quantize_proj(0x10004, 4, 4, 0x10000, 0x10000, None) == 3
+    handle = ctypes.c_void_p()
+    assert L.qgalore_plan_create(None, 1, ctypes.byref(handle)) == 1
+    arr = (B.Layer * 2)()
+    for k in range(2):
+        arr[k].desc = _desc()
+        for f in ("G", "W_q", "W_scale", "P_q", "P_scale", "M_q", "V_q"):
+            setattr(arr[k], f, 0x10000)
+    arr[1].desc.beta2 = 0.99
+    assert L.qgalore_plan_create(arr, 2, ctypes.byref(handle)) == 5   # betas must agree
+    assert L.qgalore_plan_step(None, 1, 0, 0x10000, 1, None) == 1
+
+
+def test_valid_arguments_without_a_gpu_report_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call(_desc()) == 7
+
+
+def test_library_schedule_matches_oracle_schedule():
+    """The host-side schedule in the library against the oracle's, on random similarity
+    sequences with values at, above and below the threshold."""
+    rng = np.random.default_rng(5)
+    for trial in range(50):
+        delta0 = int(rng.integers(1, 40))
+        T = int(rng.integers(50, 400))
+        vals = rng.choice([0.1, 0.39999, 0.4, 0.40001, 0.9], size=T)
+        lib_s = B.Schedule(delta0, 0.4)
+        ora = O.LayerSchedule(delta=delta0, gamma=np.float32(0.4))
+        for t in range(T):
+            assert lib_s.due(t) == ora.due(t)
+            if ora.due(t):
+                cs = float(np.float32(vals[t]))
+                assert lib_s.refresh(t, cs if ora.count else None) == ora.refresh(t, cs if ora.count else None)
+                assert (lib_s.delta, lib_s.next_refresh, lib_s.count) == (ora.delta, ora.next_refresh, ora.count)

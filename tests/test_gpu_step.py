@@ -1,0 +1,220 @@
+"""GPU parity of the Q-GaLore step: the library's HIP kernels against the CPU oracle on the
+same seeded inputs, through the C ABI. Rules are in tests/parity.py."""
+import numpy as np
+import pytest
+
+from oracle import qgalore_oracle as O
+from quantized_rank_gradient_amd import workloads as WL
+from tests import parity as PAR
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _B():
+    from quantized_rank_gradient_amd import binding as B
+    return B
+
+
+def gpu_step(Lt, t, seed=WL.SR_SEED, hp=None):
+    B = _B()
+    R_out = torch.empty((Lt.r, Lt.n), dtype=torch.float32, device="cuda")
+    U_out = torch.empty((Lt.m, Lt.n), dtype=torch.float32, device="cuda")
+    h = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, alpha=0.25)
+    h.update(hp or {})
+    B.step(Lt, t, seed, hp=h, R_out=R_out, U_out=U_out)
+    torch.cuda.synchronize()
+    return snapshot(Lt, R_out, U_out)
+
+
+def snapshot(Lt, R_out=None, U_out=None):
+    out = {k: getattr(Lt, k).cpu().numpy() for k in ("Wq", "Mq", "Ms", "Vq", "Vs")}
+    if R_out is not None:
+        out["R"] = R_out.cpu().numpy()
+    if U_out is not None:
+        out["U"] = U_out.cpu().numpy()
+    return out
+
+
+def custom_cfg(m, n, r, sigma=1e-3):
+    return WL.Config("custom", 9, (WL.LayerShape(3, f"{m}x{n}", m, n),), r=r, sigma=sigma)
+
+
+# ------------------------------------------------------------------ INT4 quantizer ---
+
+@pytest.mark.parametrize("m,r", [(256, 32), (1376, 128), (5461, 512), (7, 9), (4096, 1024)])
+def test_quantize_proj_bit_exact(m, r):
+    B = _B()
+    rng = np.random.default_rng(m * 131 + r)
+    P = np.linalg.qr(rng.standard_normal((m, min(r, m))))[0]
+    if P.shape[1] < r:
+        P = np.concatenate([P, rng.standard_normal((m, r - P.shape[1])) * 0.1], axis=1)
+    P = P.astype(np.float32)
+    P[: min(m, 3)] = 0.0                         # a zero run: a zero-scale group when r is small
+    Pq_o, Ps_o = O.quantize_proj(P)
+    Pq_g, Ps_g = B.quantize_proj(torch.from_numpy(P).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(Ps_g.cpu().numpy(), Ps_o)
+    assert np.array_equal(Pq_g.cpu().numpy(), Pq_o)
+
+
+# ------------------------------------------------------------------- step parity ---
+
+CASES = [
+    # m, n, r, moments, t
+    (512, 512, 128, "zero", 1),        # LLaMA-60M attention shape, first step
+    (1376, 512, 128, "random", 3),     # gate/up shape: m not a multiple of the 128 tile
+    (512, 1376, 128, "random", 2),     # down shape: n ragged, scale groups straddle rows
+    (300, 200, 64, "random", 5),       # ragged everywhere, short last groups
+    (2048, 5461, 64, "random", 2),     # odd n: unaligned rows take the element-wise path
+    (5461, 256, 32, "zero", 1),        # odd m: K tail of the projection, row tail of W
+    (64, 40, 8, "random", 2),          # smallest rank
+    (24, 13, 16, "random", 3),         # tiny, odd n, a single short group
+    (128, 96, 128, "random", 2),       # full rank r = m
+    (4096, 256, 1024, "random", 4),    # rank 1024: eight projection row tiles
+]
+
+
+@pytest.mark.parametrize("m,n,r,moments,t", CASES)
+def test_step_matches_oracle(m, n, r, moments, t):
+    cfg = custom_cfg(m, n, r)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, r, moments)
+    G = WL.gradient_bf16(cfg, L, t)
+    Lt = PAR.to_device(st, G, P)
+    assert np.array_equal(Lt.Pq.cpu().numpy(), st.Pq)
+    before = st.copy()
+    res = O.qgalore_step(st, G, t, WL.SR_SEED)
+    out = gpu_step(Lt, t)
+    PAR.check_step(before, res, st, out)
+
+
+def test_single256_ten_steps_each_from_the_oracle_state():
+    """The 256 x 256, rank-32 layer for ten steps. Before every step the GPU state is reset to
+    the oracle's, so every step is compared on identical inputs (moments non-zero from t = 2)."""
+    cfg = WL.CONFIGS["single256"]
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, cfg.r, "zero")
+    flips = 0
+    for t in range(1, cfg.steps + 1):
+        G = WL.gradient_bf16(cfg, L, t)
+        Lt = PAR.to_device(st, G, P)
+        before = st.copy()
+        res = O.qgalore_step(st, G, t, WL.SR_SEED)
+        out = gpu_step(Lt, t)
+        flips += PAR.check_step(before, res, st, out)
+    assert flips <= 2
+
+
+def test_zero_gradient_leaves_weights_and_moments_unchanged():
+    cfg = custom_cfg(512, 384, 64)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, 64, "zero")
+    Lt = PAR.to_device(st, np.zeros((L.m, L.n), np.uint16), P)
+    out = gpu_step(Lt, 1)
+    assert np.array_equal(out["Wq"], st.Wq)
+    assert not out["Mq"].any() and not out["Vq"].any() and not out["Ms"].any()
+
+
+def test_step_is_deterministic():
+    cfg = custom_cfg(1376, 512, 128)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, 128, "random")
+    G = WL.gradient_bf16(cfg, L, 2)
+    a = gpu_step(PAR.to_device(st, G, P), 2)
+    b = gpu_step(PAR.to_device(st, G, P), 2)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_clamp_and_zero_scale_groups():
+    """A large update saturates at +-127; a zero weight scale leaves its group untouched."""
+    cfg = custom_cfg(256, 256, 32, sigma=1e-2)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, 32, "zero")
+    st.Ws[:] = 1e-7                    # tiny scales: |U|/s >> 127
+    st.Ws[5] = 0.0
+    G = WL.gradient_bf16(cfg, L, 1)
+    Lt = PAR.to_device(st, G, P)
+    before = st.copy()
+    res = O.qgalore_step(st, G, 1, WL.SR_SEED)
+    out = gpu_step(Lt, 1)
+    PAR.check_step(before, res, st, out)
+    assert np.all(np.abs(out["Wq"]).max() == 127)
+    assert np.array_equal(out["Wq"].ravel()[5 * 256:6 * 256], before.Wq.ravel()[5 * 256:6 * 256])
+
+
+# --------------------------------------------------------------------- grouped step ---
+
+def test_plan_matches_oracle_over_mixed_layers():
+    B = _B()
+    shapes = [(512, 512), (1376, 512), (512, 1376), (300, 200)]
+    r = 64
+    cfg = WL.Config("mixed", 8, tuple(WL.LayerShape(k, "l", m, n) for k, (m, n) in enumerate(shapes)),
+                    r=r, sigma=1e-3)
+    t = 2
+    states, devs, Gs = [], [], []
+    for L in cfg.layers:
+        st, P = PAR.host_state(cfg, L, r, "random")
+        G = WL.gradient_bf16(cfg, L, t)
+        states.append(st)
+        devs.append(PAR.to_device(st, G, P))
+        Gs.append(G)
+    Rs = [torch.empty((r, L.n), dtype=torch.float32, device="cuda") for L in cfg.layers]
+    Us = [torch.empty((L.m, L.n), dtype=torch.float32, device="cuda") for L in cfg.layers]
+    plan = B.Plan(devs, hp=dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, alpha=0.25),
+                  R_out=Rs, U_out=Us)
+    plan.step(t, WL.SR_SEED)
+    torch.cuda.synchronize()
+    for st, Lt, G, Ro, Uo in zip(states, devs, Gs, Rs, Us):
+        before = st.copy()
+        res = O.qgalore_step(st, G, t, WL.SR_SEED)
+        PAR.check_step(before, res, st, snapshot(Lt, Ro, Uo))
+    plan.close()
+
+
+# ------------------------------------------------------------------------- CosSim ---
+
+@pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (4096, 1024)])
+def test_cossim_matches_oracle(m, r):
+    B = _B()
+    rng = np.random.default_rng(m + r)
+    full = np.linalg.qr(rng.standard_normal((m, 2 * r)))[0]
+    A0, A1 = full[:, :r], full[:, r:]
+    Prand = np.linalg.qr(rng.standard_normal((m, r)))[0]
+    for theta, other in ((None, A0), (1.159, None), (0.5, None), (None, Prand)):
+        Pb = other if theta is None else A0 * np.cos(theta) + A1 * np.sin(theta)
+        qa, sa = O.quantize_proj(A0.astype(np.float32))
+        qb, sb = O.quantize_proj(Pb.astype(np.float32))
+        want = O.cossim(qa, sa, qb, sb, m, r)
+        got = B.cossim(*(torch.from_numpy(x).cuda() for x in (qa, sa, qb, sb)), m, r)
+        assert abs(got - want) <= 1e-4, (theta, got, want)
+        if abs(want - 0.4) > 1e-4:
+            assert (got > 0.4) == (want > 0.4)
+
+
+def test_philox_matches_rocrand_if_available():
+    """External pin of the oracle's Philox4x32-10: rocRAND's host-side generator with the
+    same 64-bit seed produces counter blocks (c, 0, 0, 0), c = 0, 1, ... in order."""
+    import ctypes
+    try:
+        rr = ctypes.CDLL("librocrand.so")
+    except OSError:
+        pytest.skip("rocRAND not loadable")
+    gen = ctypes.c_void_p()
+    if rr.rocrand_create_generator_host_blocking(ctypes.byref(gen), 401) != 0:
+        pytest.skip("rocRAND host generator unavailable")
+    seed = 0x0123456789ABCDEF
+    assert rr.rocrand_set_seed(gen, ctypes.c_ulonglong(seed)) == 0
+    n = 4096
+    buf = (ctypes.c_uint32 * n)()
+    st = rr.rocrand_generate(gen, buf, ctypes.c_size_t(n))
+    rr.rocrand_destroy_generator(gen)
+    if st != 0:
+        pytest.skip(f"rocRAND generate status {st}")
+    got = np.frombuffer(buf, dtype=np.uint32)
+    ctr = np.zeros((n // 4, 4), np.uint32)
+    ctr[:, 0] = np.arange(n // 4)
+    want = O.philox4x32_10(ctr, (seed & 0xFFFFFFFF, seed >> 32)).ravel()
+    assert np.array_equal(got, want)
