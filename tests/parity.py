@@ -8,7 +8,8 @@ Comparison rules (GPU against the oracle, same seeded inputs):
     rounding input is d = W + U/s + u and the boundary an integer; for M and V it is x * inv
     and the boundary a half-integer. An element's allowed reach is
         1e-5 + |input_gpu - input_oracle| estimated from the fp32 difference of its source
-    (U for W, R for M and V). At most 1e-4 of the elements may differ.
+    (U for W, R for M and V). At most 1e-4 of the compared elements may differ (at least one
+    element is allowed, so that a tensor under 10^4 elements can show one explained flip).
   * Group scales of M and V: relative difference <= 1e-5.
 """
 from __future__ import annotations
@@ -87,7 +88,8 @@ def assert_codes(gpu, ref, x_ref, boundary, reach, name, cap=1e-4):
         f"{name}: {int(unexplained.sum())} differing codes away from a rounding boundary "
         f"(margins {margin[unexplained][:5]}, reach {reach[unexplained][:5]})")
     frac = bad.mean()
-    assert frac <= cap, f"{name}: {int(bad.sum())} differing codes ({frac:.2e} > {cap})"
+    assert bad.sum() <= max(1.0, cap * bad.size), (
+        f"{name}: {int(bad.sum())} differing codes ({frac:.2e} > {cap})")
     return int(bad.sum())
 
 
