@@ -1,0 +1,310 @@
+"""Benchmark of the Q-GaLore optimizer step on one MI355X.
+
+A step is one pass of the whole hot path over a LLaMA-7B-shaped layer set (32 blocks x
+{q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008} = 224 linear layers): the grouped
+optimizer step of every layer (INT4 projection dequant, R = P~^T G on bf16 MFMA, Adam with
+INT8 moments, U = alpha P~ N~ with the fused stochastic rounding into INT8 weights) plus the
+layer-adaptive refresh test of the layers whose refresh falls due at that step (CosSim of the
+stored projection with a new one, and the interval bookkeeping). Refreshes are staggered over
+the initial interval of 25 steps, so about 224/25 layers are tested per step.
+
+All inputs are synthetic and resident in HBM before timing starts (gradients ~N(0, 1e-4^2) in
+bf16, INT8 weights with group scales 1e-3, projections from seeded QR quantized to INT4).
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+DELTA0 = 25                    # initial refresh interval (200 steps / 8)
+GAMMA = 0.4
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL):
+    """Per-layer optimizer state for rank r (projections, moments) sharing G and W."""
+    layers, pnew = [], []
+    dev = torch.device("cuda:0")
+    shape_new = {}
+    for k, L in enumerate(cfg.layers):
+        P = WL.orthonormal_device(cfg, L, r, device=dev)
+        Pq, Ps = B.quantize_proj(P)
+        del P
+        ng = B.n_groups(r * L.n)
+        layers.append(B.LayerTensors(
+            layer_id=L.layer_id, G=G_list[k], Wq=W_list[k], Ws=Ws_list[k], Pq=Pq, Ps=Ps,
+            Mq=torch.zeros((r, L.n), dtype=torch.int8, device=dev),
+            Ms=torch.zeros(ng, dtype=torch.float32, device=dev),
+            Vq=torch.zeros((r, L.n), dtype=torch.int8, device=dev),
+            Vs=torch.zeros(ng, dtype=torch.float32, device=dev), r=r))
+        # one candidate "new" projection per distinct shape stands in for the SVD result
+        if (L.m, L.n) not in shape_new:
+            Pn = WL.orthonormal_device(cfg, L, r, tag=WL.TAG_PNEW, device=dev)
+            shape_new[(L.m, L.n)] = B.quantize_proj(Pn)
+            del Pn
+        pnew.append(shape_new[(L.m, L.n)])
+    torch.cuda.synchronize()
+    return layers, pnew
+
+
+class Variant:
+    """One rank variant of the layer set: a plan, refresh schedules and scratch."""
+
+    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL):
+        self.cfg, self.r = cfg, r
+        self.torch, self.B = torch, B
+        t0 = time.time()
+        self.layers, self.pnew = build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL)
+        self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
+                                                 eps=cfg.eps, alpha=cfg.alpha))
+        self.ws = B.alloc_workspace(self.plan.workspace_bytes)
+        cws = max(B.cossim_workspace_bytes(L.m, r) for L in cfg.layers)
+        self.cws = B.alloc_workspace(cws)
+        self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device="cuda")
+        # staggered schedules: layer l had its first refresh at (l mod 25) - 25
+        self.sched = []
+        for k in range(len(self.layers)):
+            s = B.Schedule(DELTA0, GAMMA)
+            s.refresh(k % DELTA0 - DELTA0, None)
+            self.sched.append(s)
+        self.t = 0
+        self.tests = 0
+        log(f"rank {r}: {len(self.layers)} layers ready in {time.time() - t0:.1f}s, "
+            f"workspace {self.plan.workspace_bytes / 2**30:.2f} GiB")
+
+    def step(self):
+        """One full step: grouped optimizer step, then the due refresh tests."""
+        self.t += 1
+        t = self.t
+        self.plan.step(t, 1234, self.ws)
+        due = [k for k, s in enumerate(self.sched) if s.due(t)]
+        for slot, k in enumerate(due):
+            L = self.layers[k]
+            Pq_new, Ps_new = self.pnew[k]
+            self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r,
+                                self.cs_out[slot:slot + 1], workspace=self.cws)
+        vals = self.cs_out[: len(due)].cpu().tolist() if due else []
+        for k, v in zip(due, vals):
+            self.sched[k].refresh(t, v)
+        self.tests += len(due)
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        self.plan.enable_timing(steps)
+        self.tests = 0
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            self.step()
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        kms, nrec = self.plan.kernel_times()
+        self.plan.enable_timing(0)
+        return total_ms / steps, kms, self.tests / steps
+
+    def time_cossim(self, reps=5):
+        """Mean latency of one refresh test (CosSim) per distinct layer shape."""
+        torch = self.torch
+        out = {}
+        for k, L in enumerate(self.layers[:7]):
+            key = f"{L.m}x{L.n}"
+            if key in out:
+                continue
+            Pq_new, Ps_new = self.pnew[k]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r, self.cs_out[:1],
+                                workspace=self.cws)
+            e0.record()
+            for _ in range(reps):
+                self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r, self.cs_out[:1],
+                                    workspace=self.cws)
+            e1.record()
+            torch.cuda.synchronize()
+            out[key] = e0.elapsed_time(e1) / reps
+        return out
+
+
+def algorithmic(cfg, r):
+    """FLOPs and bytes the method must do per step (per kernel), from the layer shapes."""
+    mn = sum(L.m * L.n for L in cfg.layers)
+    mr = sum(L.m * r for L in cfg.layers)
+    rn = sum(r * L.n for L in cfg.layers)
+    flops_proj = 2.0 * r * mn
+    flops_back = 2.0 * r * mn
+    # projection: G (bf16) + P (INT4 + fp32 scale per 256)
+    bytes_proj = 2.0 * mn + 0.5 * mr + mr / 64.0
+    # Adam: M, V read + write (int8) and their scales read + write
+    bytes_adam = 4.0 * rn + 4.0 * 4.0 * rn / 256.0
+    # back-projection + rounding: W read + write (int8), W scales, P again
+    bytes_back = 2.0 * mn + mn / 64.0 + 0.5 * mr + mr / 64.0
+    return dict(mn=mn, flops=(flops_proj, 0.0, flops_back),
+                bytes=(bytes_proj, bytes_adam, bytes_back))
+
+
+def roofline(cfg, r, kms):
+    a = algorithmic(cfg, r)
+    names = ("qg_project", "qg_adam", "qg_backproject")
+    k = max(range(3), key=lambda i: kms[i])            # dominant kernel
+    sec = kms[k] / 1e3
+    intensity = a["flops"][k] / a["bytes"][k] if a["bytes"][k] else 0.0
+    mfma_bound = intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        ach = a["flops"][k] / sec / 1e12
+        return dict(kernel=names[k], bound="mfma", achieved=round(ach, 2),
+                    peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                    ms_per_launch=round(kms[k], 4))
+    ach = a["bytes"][k] / sec / 1e9
+    return dict(kernel=names[k], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                ms_per_launch=round(kms[k], 4))
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on one 4096 x 4096 rank-1024 layer (q of block 0)."""
+    import numpy as np
+    from oracle import qgalore_oracle as O
+    from quantized_rank_gradient_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = WL.CONFIGS["llama7b_r1024"]
+    L = cfg.layers[0]
+    P = WL.orthonormal_f32(cfg, L, cfg.r)
+    Pq, Ps = O.quantize_proj(P)
+    Mq, Ms, Vq, Vs = WL.zero_moments(cfg.r, L.n)
+    st = O.LayerState(L.m, L.n, cfg.r, L.layer_id, WL.weights_int8(cfg, L),
+                      WL.weight_scales(cfg, L), Pq, Ps, Mq, Ms, Vq, Vs)
+    G = WL.gradient_bf16(cfg, L, 1)
+    t0 = time.time()
+    O.qgalore_step(st, G, 1, 1234, O.Hyper(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.alpha))
+    dt = time.time() - t0
+    return dict(value=round(L.m * L.n / dt, 1), unit="weight elems/s", cores=int(threads),
+                kind="oracle", seconds=round(dt, 2),
+                sample="one full oracle step of the 4096x4096 rank-1024 q layer of block 0")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama7b_r1024")
+    ap.add_argument("--secondary", default="llama7b_r128",
+                    help="a second rank variant reported alongside ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the Q-GaLore step runs on a single MI355X here; "
+              "multi-GPU runs are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_rank_gradient_amd import binding as B
+    from quantized_rank_gradient_amd import workloads as WL
+    B.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    cfg = WL.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    G_list, W_list, Ws_list = [], [], []
+    for L in cfg.layers:
+        G_list.append(WL.gradient_bf16_device(cfg, L, 1, device=dev))
+        W_list.append(WL.weights_int8_device(cfg, L, device=dev))
+        Ws_list.append(torch.full((B.n_groups(L.m * L.n),), cfg.w_scale, dtype=torch.float32,
+                                  device=dev))
+    torch.cuda.synchronize()
+    log(f"{len(cfg.layers)} gradients and INT8 weights resident in {time.time() - t0:.1f}s")
+
+    variants = [(cfg, cfg.r)]
+    if args.secondary != "none":
+        sec = WL.CONFIGS[args.secondary]
+        assert [(L.m, L.n) for L in sec.layers] == [(L.m, L.n) for L in cfg.layers]
+        variants.append((sec, sec.r))
+
+    results = []
+    for vcfg, r in variants:
+        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL)
+        ms, kms, tests = v.time_steps(args.steps, args.warmup)
+        cs_ms = v.time_cossim()
+        a = algorithmic(vcfg, r)
+        res = dict(config=vcfg.key, rank=r, ms_per_step=round(ms, 4),
+                   value=a["mn"] / (ms / 1e3),
+                   tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
+                   kernel_ms=dict(qg_project=round(kms[0], 4), qg_adam=round(kms[1], 4),
+                                  qg_backproject=round(kms[2], 4)),
+                   optimizer_ms=round(sum(kms), 4),
+                   refresh_tests_per_step=round(tests, 2),
+                   cossim_ms_per_test=cs_ms,
+                   roofline=roofline(vcfg, r, kms))
+        log(json.dumps(res))
+        results.append(res)
+        v.plan.close()
+        del v
+        torch.cuda.empty_cache()
+
+    main_res = results[0]
+    line = {
+        "metric": "Q-GaLore step: weight elems updated/s + % bf16-MFMA/HBM roofline, 7B layer set",
+        "value": round(main_res["value"], 1),
+        "unit": "weight elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.key}: LLaMA-7B-shaped layer set, 224 layers "
+                        f"(32 x q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), "
+                        f"rank {cfg.r}, one full optimizer step + due refresh tests",
+            "layers": len(cfg.layers), "rank": cfg.r, "weight_elems": algorithmic(cfg, cfg.r)["mn"],
+            "parallelism": "single GPU",
+        },
+        "tflops": main_res["tflops"],
+        "kernel_ms": main_res["kernel_ms"],
+        "optimizer_ms": main_res["optimizer_ms"],
+        "refresh_tests_per_step": main_res["refresh_tests_per_step"],
+        "cossim_ms_per_test": main_res["cossim_ms_per_test"],
+        "roofline": main_res["roofline"],
+        "variants": {r["config"]: {k: r[k] for k in ("rank", "value", "ms_per_step", "tflops",
+                                                    "kernel_ms", "optimizer_ms",
+                                                    "refresh_tests_per_step",
+                                                    "cossim_ms_per_test", "roofline")}
+                     for r in results[1:]},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one layer ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,6 +57,9 @@ EXPORTS = {
     "qgalore_plan_workspace_bytes": (c_size_t, [c_void_p]),
     "qgalore_plan_step": (c_int32, [c_void_p, c_int64, c_uint64, c_void_p, c_size_t, c_void_p]),
     "qgalore_plan_destroy": (c_int32, [c_void_p]),
+    "qgalore_plan_enable_timing": (c_int32, [c_void_p, c_int32]),
+    "qgalore_plan_kernel_times": (c_int32, [c_void_p, ctypes.POINTER(c_float),
+                                           ctypes.POINTER(c_int32)]),
     "qgalore_cossim_workspace_bytes": (c_size_t, [c_int64, c_int64]),
     "qgalore_cossim_async": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p,
                                        c_size_t, c_void_p, c_void_p]),
@@ -230,6 +233,19 @@ class Plan:
         _check(lib().qgalore_plan_step(self._h, int(t), int(seed) & (2 ** 64 - 1),
                                        _ptr(workspace, torch.uint8, None, "workspace"),
                                        workspace.numel(), _stream(stream)), "qgalore_plan_step")
+
+    def enable_timing(self, max_steps: int) -> None:
+        _check(lib().qgalore_plan_enable_timing(self._h, int(max_steps)),
+               "qgalore_plan_enable_timing")
+
+    def kernel_times(self):
+        """Mean (projection, Adam, back-projection) kernel milliseconds over the recorded
+        steps, and the number of steps recorded."""
+        out = (c_float * 3)()
+        steps = c_int32(0)
+        _check(lib().qgalore_plan_kernel_times(self._h, out, ctypes.byref(steps)),
+               "qgalore_plan_kernel_times")
+        return [float(x) for x in out], int(steps.value)
 
     def close(self) -> None:
         if self._h:

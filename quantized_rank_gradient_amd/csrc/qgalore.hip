@@ -212,7 +212,24 @@ struct qg_plan {
   int64_t ws_bytes = 0;
   float beta1 = 0.f, beta2 = 0.f;
   int device = 0;
+  std::vector<hipEvent_t> events;   // 4 per recorded step when timing is enabled
+  int timing_cap = 0;
+  int timing_used = 0;
 };
+
+namespace {
+hipError_t free_events(qg_plan* p) {
+  hipError_t e = hipSuccess;
+  for (hipEvent_t ev : p->events) {
+    const hipError_t e2 = hipEventDestroy(ev);
+    if (e == hipSuccess) e = e2;
+  }
+  p->events.clear();
+  p->timing_cap = 0;
+  p->timing_used = 0;
+  return e;
+}
+}  // namespace
 
 extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, qg_plan** out) {
   if (!layers || !out) return QG_ERR_NULL;
@@ -298,21 +315,68 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = nullptr;
+  if (p->timing_used < p->timing_cap) ev = &p->events[4 * p->timing_used++];
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], s);
+  if (e != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
-  hipError_t e = qg::launch_project(a, p->grid[0], s);
+  e = qg::launch_project(a, p->grid[0], s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[1];
   e = qg::launch_adam(a, p->grid[1], s);
   if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
+  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
   e = qg::launch_backproject(a, p->grid[2], s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
+  return QG_OK;
+}
+
+extern "C" qg_status qgalore_plan_enable_timing(qg_plan* p, int32_t max_steps) {
+  if (!p) return QG_ERR_NULL;
+  if (max_steps < 0 || max_steps > 100000) return QG_ERR_ARG;
+  hipError_t e = free_events(p);
+  if (e != hipSuccess) return hip_fail(e, "timing event destroy");
+  p->events.resize(4 * (size_t)max_steps);
+  for (size_t k = 0; k < p->events.size(); ++k) {
+    e = hipEventCreate(&p->events[k]);
+    if (e != hipSuccess) {
+      p->events.resize(k);
+      free_events(p);
+      return hip_fail(e, "timing event create");
+    }
+  }
+  p->timing_cap = max_steps;
+  p->timing_used = 0;
+  return QG_OK;
+}
+
+extern "C" qg_status qgalore_plan_kernel_times(qg_plan* p, float out_ms[3], int32_t* steps) {
+  if (!p || !out_ms) return QG_ERR_NULL;
+  double acc[3] = {0, 0, 0};
+  for (int k = 0; k < p->timing_used; ++k) {
+    hipEvent_t* ev = &p->events[4 * k];
+    hipError_t e = hipEventSynchronize(ev[3]);
+    for (int j = 0; j < 3 && e == hipSuccess; ++j) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[j], ev[j + 1]);
+      acc[j] += ms;
+    }
+    if (e != hipSuccess) return hip_fail(e, "timing event read");
+  }
+  const int used = p->timing_used;
+  for (int j = 0; j < 3; ++j) out_ms[j] = used ? (float)(acc[j] / used) : 0.f;
+  if (steps) *steps = used;
+  p->timing_used = 0;
   return QG_OK;
 }
 
 extern "C" qg_status qgalore_plan_destroy(qg_plan* p) {
   if (!p) return QG_ERR_NULL;
-  hipError_t e = hipSuccess;
+  hipError_t e = free_events(p);
   if (p->d_table) e = hipFree(p->d_table);
   for (int k = 0; k < 3; ++k)
     if (p->d_map[k]) {
