@@ -179,8 +179,9 @@ def roofline(cfg, r, kms):
                 ms_per_launch=round(kms[k], 4))
 
 
-def cpu_baseline():
-    """The oracle, as it stands, on one 4096 x 4096 rank-1024 layer (q of block 0)."""
+def cpu_baseline(nlayers=7):
+    """The oracle, as it stands, on the layers of block 0 (q, k, v, o, gate, up, down) at
+    rank 1024: one full oracle step per layer."""
     import numpy as np
     from oracle import qgalore_oracle as O
     from quantized_rank_gradient_amd import workloads as WL
@@ -190,19 +191,23 @@ def cpu_baseline():
     except Exception:
         threads = 1
     cfg = WL.CONFIGS["llama7b_r1024"]
-    L = cfg.layers[0]
-    P = WL.orthonormal_f32(cfg, L, cfg.r)
-    Pq, Ps = O.quantize_proj(P)
-    Mq, Ms, Vq, Vs = WL.zero_moments(cfg.r, L.n)
-    st = O.LayerState(L.m, L.n, cfg.r, L.layer_id, WL.weights_int8(cfg, L),
-                      WL.weight_scales(cfg, L), Pq, Ps, Mq, Ms, Vq, Vs)
-    G = WL.gradient_bf16(cfg, L, 1)
-    t0 = time.time()
-    O.qgalore_step(st, G, 1, 1234, O.Hyper(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.alpha))
-    dt = time.time() - t0
-    return dict(value=round(L.m * L.n / dt, 1), unit="weight elems/s", cores=int(threads),
+    h = O.Hyper(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.alpha)
+    dt, elems = 0.0, 0
+    for L in cfg.layers[:nlayers]:
+        P = WL.orthonormal_f32(cfg, L, cfg.r)
+        Pq, Ps = O.quantize_proj(P)
+        Mq, Ms, Vq, Vs = WL.zero_moments(cfg.r, L.n)
+        st = O.LayerState(L.m, L.n, cfg.r, L.layer_id, WL.weights_int8(cfg, L),
+                          WL.weight_scales(cfg, L), Pq, Ps, Mq, Ms, Vq, Vs)
+        G = WL.gradient_bf16(cfg, L, 1)
+        t0 = time.time()
+        O.qgalore_step(st, G, 1, 1234, h)
+        dt += time.time() - t0
+        elems += L.m * L.n
+    return dict(value=round(elems / dt, 1), unit="weight elems/s", cores=int(threads),
                 kind="oracle", seconds=round(dt, 2),
-                sample="one full oracle step of the 4096x4096 rank-1024 q layer of block 0")
+                sample=f"one full oracle step of each of the {nlayers} rank-1024 layers of "
+                       f"block 0 ({elems} weight elements); input generation not timed")
 
 
 def main():
