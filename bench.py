@@ -34,13 +34,22 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL):
+def projection(cfg, L, r, tag, torch, WL, dev, fast):
+    if not fast:
+        return WL.orthonormal_device(cfg, L, r, tag=tag, device=dev)
+    # profiling runs: Gaussian columns scaled to unit expected norm (no QR on the device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(WL.torch_seed(cfg, L.layer_id, 0, tag))
+    return torch.randn((L.m, r), generator=gen, device=dev) / (L.m ** 0.5)
+
+
+def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
     """Per-layer optimizer state for rank r (projections, moments) sharing G and W."""
     layers, pnew = [], []
     dev = torch.device("cuda:0")
     shape_new = {}
     for k, L in enumerate(cfg.layers):
-        P = WL.orthonormal_device(cfg, L, r, device=dev)
+        P = projection(cfg, L, r, WL.TAG_P, torch, WL, dev, fast)
         Pq, Ps = B.quantize_proj(P)
         del P
         ng = B.n_groups(r * L.n)
@@ -52,7 +61,7 @@ def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL):
             Vs=torch.zeros(ng, dtype=torch.float32, device=dev), r=r))
         # one candidate "new" projection per distinct shape stands in for the SVD result
         if (L.m, L.n) not in shape_new:
-            Pn = WL.orthonormal_device(cfg, L, r, tag=WL.TAG_PNEW, device=dev)
+            Pn = projection(cfg, L, r, WL.TAG_PNEW, torch, WL, dev, fast)
             shape_new[(L.m, L.n)] = B.quantize_proj(Pn)
             del Pn
         pnew.append(shape_new[(L.m, L.n)])
@@ -63,16 +72,16 @@ def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL):
 class Variant:
     """One rank variant of the layer set: a plan, refresh schedules and scratch."""
 
-    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL):
+    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
         self.cfg, self.r = cfg, r
         self.torch, self.B = torch, B
         t0 = time.time()
-        self.layers, self.pnew = build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL)
+        self.layers, self.pnew = build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL,
+                                                 fast)
         self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
                                                  eps=cfg.eps, alpha=cfg.alpha))
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
-        cws = max(B.cossim_workspace_bytes(L.m, r) for L in cfg.layers)
-        self.cws = B.alloc_workspace(cws)
+        self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(r, 32))
         self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device="cuda")
         # staggered schedules: layer l had its first refresh at (l mod 25) - 25
         self.sched = []
@@ -91,11 +100,10 @@ class Variant:
         t = self.t
         self.plan.step(t, 1234, self.ws)
         due = [k for k, s in enumerate(self.sched) if s.due(t)]
-        for slot, k in enumerate(due):
-            L = self.layers[k]
-            Pq_new, Ps_new = self.pnew[k]
-            self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r,
-                                self.cs_out[slot:slot + 1], workspace=self.cws)
+        if due:
+            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m)
+                     for k in due]
+            self.B.cossim_batch(pairs, self.r, self.cs_out, workspace=self.cws)
         vals = self.cs_out[: len(due)].cpu().tolist() if due else []
         for k, v in zip(due, vals):
             self.sched[k].refresh(t, v)
@@ -122,24 +130,21 @@ class Variant:
         return total_ms / steps, kms, self.tests / steps
 
     def time_cossim(self, reps=5):
-        """Mean latency of one refresh test (CosSim) per distinct layer shape."""
+        """Latency (ms) of the batched refresh test for one layer of each shape and for a
+        batch of nine layers (the per-step load of the staggered schedule)."""
         torch = self.torch
         out = {}
-        for k, L in enumerate(self.layers[:7]):
-            key = f"{L.m}x{L.n}"
-            if key in out:
-                continue
-            Pq_new, Ps_new = self.pnew[k]
+        for label, ks in (("1 layer", [0]), ("9 layers", list(range(9)))):
+            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m)
+                     for k in ks]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r, self.cs_out[:1],
-                                workspace=self.cws)
+            self.B.cossim_batch(pairs, self.r, self.cs_out, workspace=self.cws)
             e0.record()
             for _ in range(reps):
-                self.B.cossim_async(Pq_new, Ps_new, L.Pq, L.Ps, L.m, self.r, self.cs_out[:1],
-                                    workspace=self.cws)
+                self.B.cossim_batch(pairs, self.r, self.cs_out, workspace=self.cws)
             e1.record()
             torch.cuda.synchronize()
-            out[key] = e0.elapsed_time(e1) / reps
+            out[label] = round(e0.elapsed_time(e1) / reps, 4)
         return out
 
 
@@ -219,6 +224,8 @@ def main():
     ap.add_argument("--secondary", default="llama7b_r128",
                     help="a second rank variant reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fast-setup", action="store_true",
+                    help="Gaussian stand-in projections instead of QR (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the Q-GaLore step runs on a single MI355X here; "
@@ -253,7 +260,7 @@ def main():
 
     results = []
     for vcfg, r in variants:
-        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL)
+        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL, args.fast_setup)
         ms, kms, tests = v.time_steps(args.steps, args.warmup)
         cs_ms = v.time_cossim()
         a = algorithmic(vcfg, r)
@@ -264,7 +271,7 @@ def main():
                                   qg_backproject=round(kms[2], 4)),
                    optimizer_ms=round(sum(kms), 4),
                    refresh_tests_per_step=round(tests, 2),
-                   cossim_ms_per_test=cs_ms,
+                   cossim_ms=cs_ms,
                    roofline=roofline(vcfg, r, kms))
         log(json.dumps(res))
         results.append(res)
@@ -297,12 +304,12 @@ def main():
         "kernel_ms": main_res["kernel_ms"],
         "optimizer_ms": main_res["optimizer_ms"],
         "refresh_tests_per_step": main_res["refresh_tests_per_step"],
-        "cossim_ms_per_test": main_res["cossim_ms_per_test"],
+        "cossim_ms": main_res["cossim_ms"],
         "roofline": main_res["roofline"],
         "variants": {r["config"]: {k: r[k] for k in ("rank", "value", "ms_per_step", "tflops",
                                                     "kernel_ms", "optimizer_ms",
                                                     "refresh_tests_per_step",
-                                                    "cossim_ms_per_test", "roofline")}
+                                                    "cossim_ms", "roofline")}
                      for r in results[1:]},
     }
     if not args.no_cpu_baseline:

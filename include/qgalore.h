@@ -146,11 +146,20 @@ typedef struct {
 
 size_t qgalore_cossim_workspace_bytes(int64_t m, int64_t r);
 /* CosSim of two stored projections (each dequantized and rounded to bf16 as the step uses
- * it): C = P~_new^T P~_old, then (1/r) * nuclear norm of C, computed with a Newton-Schulz
- * polar iteration in fp32. Writes one fp32 to `out_dev` (device), asynchronously. */
+ * it): C = P~_new^T P~_old, then (1/r) * nuclear norm of C as trace(X^T C) with X the polar
+ * factor of C from a Newton-Schulz iteration (bf16 MFMA products for the iterations that
+ * lift small singular values, then hi/lo split products for fp32-level orthogonality);
+ * absolute error about 1e-5. Writes one fp32 to `out_dev` (device), asynchronously. */
 qg_status qgalore_cossim_async(const qg_proj *P_new, const qg_proj *P_old, void *workspace,
                                size_t workspace_bytes, void *stream, float *out_dev);
-/* Same, then synchronizes `stream` and stores the value in *out_host. */
+/* Many pairs at once (the layers whose refresh falls due at the same step): all pairs must
+ * share the rank r (their row counts may differ); out_dev[k] receives CosSim(P_new[k],
+ * P_old[k]). The workspace holds up to 32 pairs at a time; larger batches run in chunks. */
+size_t qgalore_cossim_batch_workspace_bytes(int64_t r, int32_t count);
+qg_status qgalore_cossim_batch(const qg_proj *P_new, const qg_proj *P_old, int32_t count,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               float *out_dev);
+/* One pair, then synchronizes `stream` and stores the value in *out_host. */
 qg_status qgalore_cossim(const qg_proj *P_new, const qg_proj *P_old, void *workspace,
                          size_t workspace_bytes, void *stream, float *out_host);
 

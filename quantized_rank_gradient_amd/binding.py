@@ -63,6 +63,9 @@ EXPORTS = {
     "qgalore_cossim_workspace_bytes": (c_size_t, [c_int64, c_int64]),
     "qgalore_cossim_async": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p,
                                        c_size_t, c_void_p, c_void_p]),
+    "qgalore_cossim_batch_workspace_bytes": (c_size_t, [c_int64, c_int32]),
+    "qgalore_cossim_batch": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_int32,
+                                       c_void_p, c_size_t, c_void_p, c_void_p]),
     "qgalore_cossim": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p, c_size_t,
                                  c_void_p, ctypes.POINTER(c_float)]),
     "qgalore_quantize_proj": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
@@ -282,6 +285,27 @@ def cossim_async(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, out: torch.Tens
                                       workspace.numel(), _stream(stream),
                                       _ptr(out, torch.float32, None, "out")),
            "qgalore_cossim_async")
+
+
+def cossim_batch_workspace_bytes(r: int, count: int) -> int:
+    return int(lib().qgalore_cossim_batch_workspace_bytes(r, count))
+
+
+def cossim_batch(pairs, r: int, out: torch.Tensor, workspace=None, stream=None) -> None:
+    """pairs: list of (Pq_new, Ps_new, Pq_old, Ps_old, m); out[k] (device fp32) receives
+    CosSim of pair k, asynchronously. All pairs share the rank r."""
+    n = len(pairs)
+    A = (Proj * n)()
+    Bp = (Proj * n)()
+    for k, (qn, sn, qo, so, m) in enumerate(pairs):
+        A[k] = _proj(qn, sn, m, r)
+        Bp[k] = _proj(qo, so, m, r)
+    if workspace is None:
+        workspace = alloc_workspace(cossim_batch_workspace_bytes(r, n), pairs[0][0].device)
+    _check(lib().qgalore_cossim_batch(A, Bp, n, _ptr(workspace, torch.uint8, None, "workspace"),
+                                      workspace.numel(), _stream(stream),
+                                      _ptr(out, torch.float32, None, "out")),
+           "qgalore_cossim_batch")
 
 
 def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, workspace=None, stream=None) -> float:

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgalore.so")
-SOURCES = ("qg_kernels.hip", "qgalore.hip")
+SOURCES = ("qg_kernels.hip", "qg_cossim.hip", "qgalore.hip")
 ARCH = os.environ.get("QGALORE_ARCH", "gfx950")
 
 FLAGS = [
@@ -49,7 +49,8 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+           "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")

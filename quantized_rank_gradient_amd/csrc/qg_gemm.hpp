@@ -169,15 +169,20 @@ struct StageInt4N {
 };
 
 // ---------------------------------------------------------------------------------------
-// The K loop: acc[ti][tj] (wave sub-tile rows 32*ti, cols 32*tj) += A_tile * B_tile over
-// K in [k_begin, k_end). `sa`/`sb` stage the A rows / B columns of the output tile.
+// The K loop: acc[x][y] (wave sub-tile rows 32*x, cols 32*y) += A_tile * B_tile over K in
+// [k_begin, k_end). A stage holds PARTS copies of the [A | B] tile pair: PARTS = 1 is the
+// plain bf16 product; PARTS = 2 holds the bf16 "high" parts followed by the bf16 "low"
+// remainders of fp32 operands, and the product keeps hi*hi + hi*lo + lo*hi (about 16
+// significant bits per operand). store_a(sa, stage) / store_b(sb, stage) fill one stage.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs,
-                                           f32x16 (&acc)[2][2]) {
+template <int PARTS>
+__device__ __forceinline__ void mfma_stage(const uint16_t* stage, f32x16 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hk = (lane >> 5) * 8;
+  const uint16_t* As = stage;
+  const uint16_t* Bs = stage + TM * LDK;
 #pragma unroll
   for (int ks = 0; ks < TK; ks += 16) {
     bf16x8 a[2], b[2];
@@ -191,13 +196,31 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
 #pragma unroll
       for (int y = 0; y < 2; ++y)
         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+    if constexpr (PARTS == 2) {
+      const uint16_t* Al = stage + STAGE_ELEMS;
+      const uint16_t* Bl = Al + TM * LDK;
+      bf16x8 al[2], bl[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        al[x] = *reinterpret_cast<const bf16x8*>(Al + (wm * 64 + 32 * x + l32) * LDK + ks + hk);
+        bl[x] = *reinterpret_cast<const bf16x8*>(Bl + (wn * 64 + 32 * x + l32) * LDK + ks + hk);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], bl[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[x], b[y], acc[x][y], 0, 0, 0);
+        }
+    }
   }
 }
 
-template <class SA, class SB, class StoreA, class StoreB>
+template <int PARTS, class SA, class SB, class StoreA, class StoreB>
 __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, StoreB store_b,
                                            int64_t k_begin, int64_t k_end, uint16_t* lds,
                                            f32x16 (&acc)[2][2]) {
+  constexpr int STAGE = PARTS * STAGE_ELEMS;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -209,7 +232,7 @@ __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, Store
   sa.load(k_begin);
   sb.load(k_begin);
   store_a(sa, lds);
-  store_b(sb, lds + TM * LDK);
+  store_b(sb, lds);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -218,12 +241,12 @@ __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, Store
       sa.load(k_begin + (int64_t)(kt + 1) * TK);
       sb.load(k_begin + (int64_t)(kt + 1) * TK);
     }
-    uint16_t* now = lds + cur * STAGE_ELEMS;
-    uint16_t* nxt = lds + (cur ^ 1) * STAGE_ELEMS;
-    mfma_stage(now, now + TM * LDK, acc);
+    uint16_t* now = lds + cur * STAGE;
+    uint16_t* nxt = lds + (cur ^ 1) * STAGE;
+    mfma_stage<PARTS>(now, acc);
     if (more) {
       store_a(sa, nxt);
-      store_b(sb, nxt + TM * LDK);
+      store_b(sb, nxt);
     }
     __syncthreads();
   }

@@ -35,8 +35,9 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
   StageInt4T sa(L.Pq, L.Ps, L.r, k_end, L.r, i0);
   StageBf16T sb(L.G, L.n, k_end, L.n, j0);
   f32x16 acc[2][2];
-  gemm_kloop(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
-             [j0](StageBf16T& st, uint16_t* p) { st.store(p, j0); }, k_begin, k_end, lds, acc);
+  gemm_kloop<1>(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
+                [j0](StageBf16T& st, uint16_t* p) { st.store(p + TM * LDK, j0); }, k_begin,
+                k_end, lds, acc);
 
   float* out = reinterpret_cast<float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch;
 #pragma unroll
@@ -217,8 +218,9 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
   StageInt4N sa(L.Pq, L.Ps, L.r, L.m, i0);
   StageBf16T sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.n, j0);
   f32x16 acc[2][2];
-  gemm_kloop(sa, sb, [](StageInt4N& st, uint16_t* p) { st.store(p); },
-             [j0](StageBf16T& st, uint16_t* p) { st.store(p, j0); }, 0, L.r, lds, acc);
+  gemm_kloop<1>(sa, sb, [](StageInt4N& st, uint16_t* p) { st.store(p); },
+                [j0](StageBf16T& st, uint16_t* p) { st.store(p + TM * LDK, j0); }, 0, L.r, lds,
+                acc);
 
   // Redistribute each wave's 64 x 64 block through LDS, 32 rows at a time, so that every
   // lane owns 32 consecutive columns of one row: whole Philox blocks and wide W accesses.
@@ -283,152 +285,6 @@ __global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int
   if (lane == 0) Ps[g] = s;
 }
 
-// ============================================================ subspace similarity ===
-
-// Cpart[s] = P~_new^T P~_old over rows [s*kslab, (s+1)*kslab) of the two m x r projections.
-__global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosArgs c) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
-  const int per_split = c.tiles * c.tiles;
-  const int s = blockIdx.x / per_split;
-  const int rem = blockIdx.x - s * per_split;
-  const int ti = rem / c.tiles, tj = rem - ti * c.tiles;
-  const int i0 = ti * TM, j0 = tj * TN;
-  const int64_t k_begin = (int64_t)s * c.kslab;
-  const int64_t k_end = min<int64_t>(c.m, k_begin + c.kslab);
-  StageInt4T sa(c.qa, c.sa, c.r, k_end, c.r, i0);
-  StageInt4T sb(c.qb, c.sb, c.r, k_end, c.r, j0);
-  f32x16 acc[2][2];
-  gemm_kloop(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
-             [j0](StageInt4T& st, uint16_t* p) { st.store(p, j0); }, k_begin, k_end, lds, acc);
-  float* out = c.Cpart + (int64_t)s * c.r * c.r;
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int64_t j = j0 + acc_col(y);
-      if (j >= c.r) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row(x, v);
-        if (i < c.r) gstore(out + i * c.r + j, (float)acc[x][y][v]);
-      }
-    }
-}
-
-// Sum the split partials into C (fixed order) and emit per-block sums of squares.
-__global__ __launch_bounds__(kThreads) void qg_ns_reduce(const float* Cpart, int split,
-                                                        int64_t n2, float* C, float* blocksq) {
-  __shared__ float red[kThreads];
-  float sq = 0.0f;
-  for (int64_t e = (int64_t)blockIdx.x * kThreads * 16 + threadIdx.x;
-       e < min<int64_t>(n2, (int64_t)(blockIdx.x + 1) * kThreads * 16); e += kThreads) {
-    float v = Cpart[e];
-    for (int s = 1; s < split; ++s) v += Cpart[(int64_t)s * n2 + e];
-    C[e] = v;
-    sq += v * v;
-  }
-  red[threadIdx.x] = sq;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) blocksq[blockIdx.x] = red[0];
-}
-
-// X0 = C / ||C||_F (singular values in [0, 1], inside Newton-Schulz's region of convergence).
-__global__ __launch_bounds__(kThreads) void qg_ns_init(const float* C, int64_t n2,
-                                                      const float* blocksq, int nblocks,
-                                                      float* X) {
-  __shared__ float inv_norm;
-  if (threadIdx.x == 0) {
-    float t = 0.0f;
-    for (int b = 0; b < nblocks; ++b) t += blocksq[b];
-    inv_norm = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
-  }
-  __syncthreads();
-  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (e < n2) X[e] = C[e] * inv_norm;
-}
-
-// fp32 GEMM for the r x r polar iteration: Y = alpha * op(A) B + beta * D, op(A) = A^T when
-// TA. 64 x 64 tile per workgroup, each thread a 4 x 4 block, K staged 16 at a time in LDS.
-template <bool TA>
-__global__ __launch_bounds__(kThreads) void qg_gemm_f32(const float* A, const float* B,
-                                                       const float* D, float* Y, int n,
-                                                       float alpha, float beta) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
-  const int tiles = (n + 63) / 64;
-  const int bi = blockIdx.x / tiles, bj = blockIdx.x - bi * tiles;
-  const int i0 = bi * 64, j0 = bj * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < n; k0 += 16) {
-    for (int l = threadIdx.x; l < 16 * 64; l += kThreads) {
-      const int kk = l >> 6, c = l & 63;
-      const int k = k0 + kk;
-      float av = 0.0f, bv = 0.0f;
-      if (k < n && i0 + c < n) av = TA ? A[(int64_t)k * n + i0 + c] : A[(int64_t)(i0 + c) * n + k];
-      if (k < n && j0 + c < n) bv = B[(int64_t)k * n + j0 + c];
-      As[kk][c] = av;
-      Bs[kk][c] = bv;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float ar[4], br[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ar[u] = As[kk][ty * 4 + u];
-        br[u] = Bs[kk][tx * 4 + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = __builtin_fmaf(ar[u], br[w], acc[u][w]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int i = i0 + ty * 4 + u, j = j0 + tx * 4 + w;
-      if (i < n && j < n) {
-        const int64_t e = (int64_t)i * n + j;
-        float y = alpha * acc[u][w];
-        if (D) y = __builtin_fmaf(beta, D[e], y);
-        Y[e] = y;
-      }
-    }
-}
-
-// Per-block partial sums of X .* C (the nuclear norm is trace(X^T C) at convergence).
-__global__ __launch_bounds__(kThreads) void qg_ns_trace(const float* X, const float* C,
-                                                       int64_t n2, float* blocksum) {
-  __shared__ float red[kThreads];
-  float acc = 0.0f;
-  for (int64_t e = (int64_t)blockIdx.x * kThreads * 16 + threadIdx.x;
-       e < min<int64_t>(n2, (int64_t)(blockIdx.x + 1) * kThreads * 16); e += kThreads)
-    acc = __builtin_fmaf(X[e], C[e], acc);
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
-}
-
-__global__ void qg_ns_finish(const float* blocksum, int nblocks, float inv_r, float* out) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double t = 0.0;
-    for (int b = 0; b < nblocks; ++b) t += blocksum[b];
-    out[0] = (float)(t * inv_r);
-  }
-}
-
 // ==================================================================== launchers ===
 
 hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
@@ -448,36 +304,6 @@ hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, floa
   const int64_t groups = (numel + kGroup - 1) / kGroup;
   const int grid = (int)((groups + 3) / 4);
   hipLaunchKernelGGL(qg_quantize_int4, dim3(grid), dim3(kThreads), 0, s, P, numel, Pq, Ps);
-  return hipGetLastError();
-}
-
-hipError_t launch_cossim(const CosArgs& c, const CosWork& w, float* out, hipStream_t s) {
-  const int64_t n2 = (int64_t)c.r * c.r;
-  const int grid_gemm = c.tiles * c.tiles * c.split;
-  hipLaunchKernelGGL(qg_cossim_gemm, dim3(grid_gemm), dim3(kThreads), 0, s, c);
-  const int nred = (int)((n2 + kThreads * 16 - 1) / (kThreads * 16));
-  hipLaunchKernelGGL(qg_ns_reduce, dim3(nred), dim3(kThreads), 0, s, (const float*)c.Cpart,
-                     c.split, n2, w.C, w.blocks);
-  const int nel = (int)((n2 + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(qg_ns_init, dim3(nel), dim3(kThreads), 0, s, (const float*)w.C, n2,
-                     (const float*)w.blocks, nred, w.X);
-  const int ft = (c.r + 63) / 64;
-  float* X = w.X;
-  float* Xn = w.Xn;
-  for (int it = 0; it < w.iters; ++it) {
-    // A = X^T X ; X <- 1.5 X - 0.5 X A
-    hipLaunchKernelGGL(qg_gemm_f32<true>, dim3(ft * ft), dim3(kThreads), 0, s, (const float*)X,
-                       (const float*)X, (const float*)nullptr, w.A, (int)c.r, 1.0f, 0.0f);
-    hipLaunchKernelGGL(qg_gemm_f32<false>, dim3(ft * ft), dim3(kThreads), 0, s, (const float*)X,
-                       (const float*)w.A, (const float*)X, Xn, (int)c.r, -0.5f, 1.5f);
-    float* t = X;
-    X = Xn;
-    Xn = t;
-  }
-  hipLaunchKernelGGL(qg_ns_trace, dim3(nred), dim3(kThreads), 0, s, (const float*)X,
-                     (const float*)w.C, n2, w.blocks);
-  hipLaunchKernelGGL(qg_ns_finish, dim3(1), dim3(64), 0, s, (const float*)w.blocks, nred,
-                     1.0f / (float)c.r, out);
   return hipGetLastError();
 }
 

@@ -5,28 +5,30 @@
 
 namespace qg {
 
-// The similarity GEMM C = P~_new^T P~_old (r x r), split over the m rows.
-struct CosArgs {
-  const uint8_t* qa;
+// A batch of projection pairs for the similarity test (same rank r, any row count m).
+constexpr int kCosMaxPairs = 32;
+
+struct CosPair {
+  const uint8_t* qa;   // P_new INT4 codes
   const float* sa;
-  const uint8_t* qb;
+  const uint8_t* qb;   // P_old INT4 codes
   const float* sb;
   int64_t m;
-  int r;
-  int tiles;     // output tiles per side (128 wide)
-  int split;     // K splits
-  int kslab;     // rows per split
-  float* Cpart;  // split x r x r partial sums
+  int kslab;           // rows per split of C = P~_new^T P~_old
+  int split;
+  int gemm_base;       // first workgroup of this pair in the C launch
 };
 
-// Scratch of the Newton-Schulz polar iteration on C.
-struct CosWork {
-  float* C;
-  float* X;
-  float* Xn;
-  float* A;
-  float* blocks;   // per-block partial sums
-  int iters;
+struct CosBatch {
+  CosPair pair[kCosMaxPairs];
+  char* ws;              // workspace base; pair p owns [p * pair_stride, (p+1) * pair_stride)
+  int64_t pair_stride;
+  int64_t off_part;      // split x r x r partial sums of C
+  int64_t off_c, off_x, off_xn, off_a;   // r x r fp32 matrices
+  int64_t off_blk;       // per-block partial sums
+  int64_t off_norm;      // squared Frobenius norm of C
+  int count, r, tiles, nblk;
+  int iters_bf16, iters_split;   // Newton-Schulz iterations with bf16 / split operands
 };
 
 hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s);
@@ -34,6 +36,6 @@ hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_backproject(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,
                                 hipStream_t s);
-hipError_t launch_cossim(const CosArgs& c, const CosWork& w, float* out, hipStream_t s);
+hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s);
 
 }  // namespace qg

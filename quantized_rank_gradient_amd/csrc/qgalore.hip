@@ -390,31 +390,28 @@ extern "C" qg_status qgalore_plan_destroy(qg_plan* p) {
 // ============================================================ subspace similarity ===
 
 namespace {
-constexpr int kNsIters = 48;
+constexpr int kNsItersBf16 = 30;   // Newton-Schulz iterations with bf16 operands
+constexpr int kNsItersSplit = 3;   // followed by iterations with hi/lo split operands
 
 struct CosLayout {
-  int split, kslab, tiles, nred;
-  int64_t off_part, off_c, off_x, off_xn, off_a, off_blocks, off_out, bytes;
+  int split, tiles, nblk;
+  int64_t off_part, off_c, off_x, off_xn, off_a, off_blk, off_norm, stride;
 };
-CosLayout cos_layout(int64_t m, int64_t r) {
+CosLayout cos_layout(int64_t r) {
   CosLayout c;
   c.tiles = (int)cdiv(r, kTile);
-  const int64_t kchunks = cdiv(m, kK);
-  int64_t s = std::max<int64_t>(1, cdiv(256, (int64_t)c.tiles * c.tiles));
-  s = std::min<int64_t>(s, kchunks);
-  c.kslab = (int)(cdiv(kchunks, s) * kK);
-  c.split = (int)cdiv(m, c.kslab);
+  c.split = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(64, (int64_t)c.tiles * c.tiles)));
   const int64_t n2 = r * r;
-  c.nred = (int)cdiv(n2, qg::kThreads * 16);
+  c.nblk = (int)cdiv(n2, (int64_t)qg::kThreads * 4);
   const int64_t mat = round_up(n2 * 4, 256);
   c.off_part = 0;
-  c.off_c = c.off_part + round_up((int64_t)c.split * n2 * 4, 256);
+  c.off_c = round_up((int64_t)c.split * n2 * 4, 256);
   c.off_x = c.off_c + mat;
   c.off_xn = c.off_x + mat;
   c.off_a = c.off_xn + mat;
-  c.off_blocks = c.off_a + mat;
-  c.off_out = c.off_blocks + round_up((int64_t)c.nred * 4, 256);
-  c.bytes = c.off_out + 256;
+  c.off_blk = c.off_a + mat;
+  c.off_norm = c.off_blk + round_up((int64_t)c.nblk * 4, 256);
+  c.stride = c.off_norm + 256;
   return c;
 }
 
@@ -425,60 +422,100 @@ qg_status check_proj(const qg_proj* p) {
   if (!aligned(p->q, 4) || !aligned(p->scale, 4)) return QG_ERR_ALIGN;
   return QG_OK;
 }
+
+qg_status check_pairs(const qg_proj* a, const qg_proj* b, int32_t count) {
+  if (!a || !b) return QG_ERR_NULL;
+  if (count < 1) return QG_ERR_ARG;
+  for (int32_t k = 0; k < count; ++k) {
+    qg_status st = check_proj(&a[k]);
+    if (st != QG_OK) return st;
+    if ((st = check_proj(&b[k])) != QG_OK) return st;
+    if (a[k].m != b[k].m || a[k].r != b[k].r || a[k].r != a[0].r) return QG_ERR_SHAPE;
+  }
+  return QG_OK;
+}
 }  // namespace
+
+extern "C" size_t qgalore_cossim_batch_workspace_bytes(int64_t r, int32_t count) {
+  if (r < 1 || r > 8192 || r % 8 != 0 || count < 1) return 0;
+  const int64_t per = cos_layout(r).stride;
+  return (size_t)(per * std::min<int64_t>(count, qg::kCosMaxPairs));
+}
 
 extern "C" size_t qgalore_cossim_workspace_bytes(int64_t m, int64_t r) {
   if (m < 1 || r < 1 || r > m || r % 8 != 0 || r > 8192) return 0;
-  return (size_t)cos_layout(m, r).bytes;
+  return (size_t)cos_layout(r).stride + 256;
+}
+
+extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P_old,
+                                          int32_t count, void* workspace, size_t workspace_bytes,
+                                          void* stream, float* out_dev) {
+  qg_status st = check_pairs(P_new, P_old, count);
+  if (st != QG_OK) return st;
+  if (!workspace || !out_dev) return QG_ERR_NULL;
+  if (!aligned(workspace, 16) || !aligned(out_dev, 4)) return QG_ERR_ALIGN;
+  const int64_t r = P_new[0].r;
+  if (workspace_bytes < qgalore_cossim_batch_workspace_bytes(r, count)) return QG_ERR_WORKSPACE;
+  if ((st = device_present()) != QG_OK) return st;
+  const CosLayout c = cos_layout(r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t first = 0; first < count; first += qg::kCosMaxPairs) {
+    qg::CosBatch b;
+    std::memset(&b, 0, sizeof(b));
+    b.count = std::min<int32_t>(qg::kCosMaxPairs, count - first);
+    b.r = (int)r;
+    b.tiles = c.tiles;
+    b.nblk = c.nblk;
+    b.ws = static_cast<char*>(workspace);
+    b.pair_stride = c.stride;
+    b.off_part = c.off_part;
+    b.off_c = c.off_c;
+    b.off_x = c.off_x;
+    b.off_xn = c.off_xn;
+    b.off_a = c.off_a;
+    b.off_blk = c.off_blk;
+    b.off_norm = c.off_norm;
+    b.iters_bf16 = kNsItersBf16;
+    b.iters_split = kNsItersSplit;
+    int base = 0;
+    for (int k = 0; k < b.count; ++k) {
+      const qg_proj& pn = P_new[first + k];
+      const qg_proj& po = P_old[first + k];
+      qg::CosPair& q = b.pair[k];
+      q.qa = pn.q;
+      q.sa = pn.scale;
+      q.qb = po.q;
+      q.sb = po.scale;
+      q.m = pn.m;
+      const int64_t kchunks = cdiv(pn.m, kK);
+      const int64_t split = std::min<int64_t>(c.split, kchunks);
+      q.kslab = (int)(cdiv(kchunks, split) * kK);
+      q.split = (int)cdiv(pn.m, q.kslab);
+      q.gemm_base = base;
+      base += q.split * c.tiles * c.tiles;
+    }
+    const hipError_t e = qg::launch_cossim_batch(b, out_dev + first, s);
+    if (e != hipSuccess) return hip_fail(e, "similarity kernels");
+  }
+  return QG_OK;
 }
 
 extern "C" qg_status qgalore_cossim_async(const qg_proj* P_new, const qg_proj* P_old,
                                           void* workspace, size_t workspace_bytes, void* stream,
                                           float* out_dev) {
-  qg_status st = check_proj(P_new);
-  if (st != QG_OK) return st;
-  if ((st = check_proj(P_old)) != QG_OK) return st;
-  if (P_new->m != P_old->m || P_new->r != P_old->r) return QG_ERR_SHAPE;
-  if (!workspace || !out_dev) return QG_ERR_NULL;
-  if (!aligned(workspace, 16) || !aligned(out_dev, 4)) return QG_ERR_ALIGN;
-  const CosLayout c = cos_layout(P_new->m, P_new->r);
-  if (workspace_bytes < (size_t)c.bytes) return QG_ERR_WORKSPACE;
-  if ((st = device_present()) != QG_OK) return st;
-  char* ws = static_cast<char*>(workspace);
-  qg::CosArgs ca;
-  ca.qa = P_new->q;
-  ca.sa = P_new->scale;
-  ca.qb = P_old->q;
-  ca.sb = P_old->scale;
-  ca.m = P_new->m;
-  ca.r = (int)P_new->r;
-  ca.tiles = c.tiles;
-  ca.split = c.split;
-  ca.kslab = c.kslab;
-  ca.Cpart = reinterpret_cast<float*>(ws + c.off_part);
-  qg::CosWork cw;
-  cw.C = reinterpret_cast<float*>(ws + c.off_c);
-  cw.X = reinterpret_cast<float*>(ws + c.off_x);
-  cw.Xn = reinterpret_cast<float*>(ws + c.off_xn);
-  cw.A = reinterpret_cast<float*>(ws + c.off_a);
-  cw.blocks = reinterpret_cast<float*>(ws + c.off_blocks);
-  cw.iters = kNsIters;
-  const hipError_t e = qg::launch_cossim(ca, cw, out_dev, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QG_OK : hip_fail(e, "similarity kernels");
+  return qgalore_cossim_batch(P_new, P_old, 1, workspace, workspace_bytes, stream, out_dev);
 }
 
 extern "C" qg_status qgalore_cossim(const qg_proj* P_new, const qg_proj* P_old, void* workspace,
                                     size_t workspace_bytes, void* stream, float* out_host) {
   if (!out_host) return QG_ERR_NULL;
-  qg_status st = check_proj(P_new);
+  qg_status st = check_pairs(P_new, P_old, 1);
   if (st != QG_OK) return st;
-  if ((st = check_proj(P_old)) != QG_OK) return st;
-  if (P_new->m != P_old->m || P_new->r != P_old->r) return QG_ERR_SHAPE;
-  const CosLayout c = cos_layout(P_new->m, P_new->r);
   if (!workspace) return QG_ERR_NULL;
-  if (workspace_bytes < (size_t)c.bytes) return QG_ERR_WORKSPACE;
-  float* dev_out = reinterpret_cast<float*>(static_cast<char*>(workspace) + c.off_out);
-  st = qgalore_cossim_async(P_new, P_old, workspace, workspace_bytes, stream, dev_out);
+  const int64_t need = cos_layout(P_new->r).stride;
+  if (workspace_bytes < (size_t)need + 256) return QG_ERR_WORKSPACE;
+  float* dev_out = reinterpret_cast<float*>(static_cast<char*>(workspace) + need);
+  st = qgalore_cossim_batch(P_new, P_old, 1, workspace, workspace_bytes, stream, dev_out);
   if (st != QG_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(out_host, dev_out, sizeof(float), hipMemcpyDeviceToHost, s);

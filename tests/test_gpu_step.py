@@ -176,6 +176,24 @@ def test_plan_matches_oracle_over_mixed_layers():
 
 # ------------------------------------------------------------------------- CosSim ---
 
+def test_cossim_batch_of_mixed_row_counts():
+    """One batched call over pairs with different m (same r) equals the oracle per pair."""
+    B = _B()
+    r = 128
+    pairs, want = [], []
+    for k, m in enumerate((512, 4096, 1376, 11008, 4096)):
+        rng = np.random.default_rng(100 + k)
+        A = np.linalg.qr(rng.standard_normal((m, r)))[0].astype(np.float32)
+        Bm = np.linalg.qr(A + 0.6 * k * rng.standard_normal((m, r)) / np.sqrt(m))[0].astype(np.float32)
+        qa, sa = O.quantize_proj(Bm)
+        qb, sb = O.quantize_proj(A)
+        want.append(O.cossim(qa, sa, qb, sb, m, r))
+        pairs.append(tuple(torch.from_numpy(x).cuda() for x in (qa, sa, qb, sb)) + (m,))
+    out = torch.full((len(pairs),), -1.0, device="cuda")
+    B.cossim_batch(pairs, r, out)
+    got = out.cpu().numpy()
+    assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
+
 @pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (4096, 1024)])
 def test_cossim_matches_oracle(m, r):
     B = _B()
