@@ -17,106 +17,113 @@
 
 namespace qg {
 
-// --------------------------------------------------------------- fp32 -> LDS stagers ---
+using CosTile = Tile<128, 128, 32, 2, 2, true, true>;     // C = P~n^T P~o, X^T X
+using NsTileNN = Tile<128, 128, 32, 2, 2, false, true>;   // X A
 
-// fp32 source stored [k][c] (row pitch ld, ld % 8 == 0), tile columns [c0, c0+128), written
-// to LDS [c][k] as bf16 (and, when PARTS == 2, the bf16 remainder x - bf16(x) into the low
-// copy). Thread t stages rows k+2p, k+2p+1 (p = t / 16), columns c0 + 8*(t % 16) .. +7.
-template <int PARTS>
-struct StageF32T {
+// --------------------------------------------------------------- fp32 -> LDS stagers ---
+// fp32 sources are rounded to bf16 on the way into LDS; with PARTS == 2 the bf16 remainder
+// x - bf16(x) goes to a second copy LO_OFF elements further on.
+
+// fp32 source [k][c] (row pitch ld, ld % 8 == 0) -> K-major LDS tile [k][c].
+template <int W, int BK, int PARTS, int LO_OFF>
+struct StageF32K {
+  static constexpr int CPR = W / 8;
+  static constexpr int NC = BK * CPR / kThreads;
   const float* src;
   int64_t ld, k_end, c_end;
-  int c, kp;
-  float f[2][8];
+  int c0;
+  float f[NC][8];
 
-  __device__ StageF32T(const float* s, int64_t ld_, int64_t k_end_, int64_t c_end_, int c0)
-      : src(s), ld(ld_), k_end(k_end_), c_end(c_end_) {
-    const int t = threadIdx.x;
-    kp = t >> 4;
-    c = c0 + 8 * (t & 15);
-  }
+  __device__ StageF32K(const float* s, int64_t ld_, int64_t k_end_, int64_t c_end_, int c0_)
+      : src(s), ld(ld_), k_end(k_end_), c_end(c_end_), c0(c0_) {}
 
   __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int64_t k = k0 + 2 * kp + rr;
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t k = k0 + q / CPR;
+      const int64_t c = c0 + 8 * (q % CPR);
       if (k < k_end && c < c_end) {
         const float4 x = gload(reinterpret_cast<const float4*>(src + k * ld + c));
         const float4 y = gload(reinterpret_cast<const float4*>(src + k * ld + c + 4));
-        f[rr][0] = x.x; f[rr][1] = x.y; f[rr][2] = x.z; f[rr][3] = x.w;
-        f[rr][4] = y.x; f[rr][5] = y.y; f[rr][6] = y.z; f[rr][7] = y.w;
+        f[u][0] = x.x; f[u][1] = x.y; f[u][2] = x.z; f[u][3] = x.w;
+        f[u][4] = y.x; f[u][5] = y.y; f[u][6] = y.z; f[u][7] = y.w;
       } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) f[rr][u] = 0.0f;
+        for (int e = 0; e < 8; ++e) f[u][e] = 0.0f;
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* hi, uint16_t* lo, int c0) const {
-    uint32_t* dh = reinterpret_cast<uint32_t*>(hi);
-    uint32_t* dl = reinterpret_cast<uint32_t*>(lo);
-    const int cl = c - c0;
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t h = pack_bf16x2(f[0][cc], f[1][cc]);
-      dh[(cl + cc) * (LDK / 2) + kp] = h;
-      if constexpr (PARTS == 2) {
-        const float r0 = f[0][cc] - bf16_to_f32(h & 0xFFFFu);
-        const float r1 = f[1][cc] - bf16_to_f32(h >> 16);
-        dl[(cl + cc) * (LDK / 2) + kp] = pack_bf16x2(r0, r1);
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int off = (q / CPR) * PITCH + 8 * (q % CPR);
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16x2(f[u][2 * e], f[u][2 * e + 1]);
+        if constexpr (PARTS == 2)
+          l[e] = pack_bf16x2(f[u][2 * e] - bf16_to_f32(h[e] & 0xFFFFu),
+                             f[u][2 * e + 1] - bf16_to_f32(h[e] >> 16));
       }
+      *reinterpret_cast<uint4*>(lds + off) = make_uint4(h[0], h[1], h[2], h[3]);
+      if constexpr (PARTS == 2)
+        *reinterpret_cast<uint4*>(lds + LO_OFF + off) = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
 };
 
-// fp32 source stored [c][k] (row pitch ld, K contiguous, ld % 8 == 0), tile rows
-// [c0, c0+128), written to LDS [c][k] as bf16 (+ remainder). Thread t stages two runs: row
-// (t / 4) + 64*h, columns k0 + 8*(t % 4) .. +7.
-template <int PARTS>
-struct StageF32N {
+// fp32 source [c][k] (row pitch ld = the K extent, ld % 8 == 0) -> K-contiguous LDS [c][k].
+template <int W, int BK, int PARTS, int LO_OFF>
+struct StageF32C {
+  static constexpr int CPR = BK / 8;
+  static constexpr int NC = W * CPR / kThreads;
   const float* src;
   int64_t ld, c_end;
   int c0;
-  float f[2][8];
+  float f[NC][8];
 
-  __device__ StageF32N(const float* s, int64_t ld_, int64_t c_end_, int c0_)
+  __device__ StageF32C(const float* s, int64_t ld_, int64_t c_end_, int c0_)
       : src(s), ld(ld_), c_end(c_end_), c0(c0_) {}
 
   __device__ __forceinline__ void load(int64_t k0) {
-    const int t = threadIdx.x;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t row = c0 + (t >> 2) + 64 * h;
-      const int64_t k = k0 + 8 * (t & 3);
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t row = c0 + q / CPR;
+      const int64_t k = k0 + 8 * (q % CPR);
       if (row < c_end && k < ld) {
         const float4 x = gload(reinterpret_cast<const float4*>(src + row * ld + k));
         const float4 y = gload(reinterpret_cast<const float4*>(src + row * ld + k + 4));
-        f[h][0] = x.x; f[h][1] = x.y; f[h][2] = x.z; f[h][3] = x.w;
-        f[h][4] = y.x; f[h][5] = y.y; f[h][6] = y.z; f[h][7] = y.w;
+        f[u][0] = x.x; f[u][1] = x.y; f[u][2] = x.z; f[u][3] = x.w;
+        f[u][4] = y.x; f[u][5] = y.y; f[u][6] = y.z; f[u][7] = y.w;
       } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) f[h][u] = 0.0f;
+        for (int e = 0; e < 8; ++e) f[u][e] = 0.0f;
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* hi, uint16_t* lo) const {
-    const int t = threadIdx.x;
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rl = (t >> 2) + 64 * h;
-      uint32_t w[4], wl[4];
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int off = (q / CPR) * PITCH + 8 * (q % CPR);
+      uint32_t h[4], l[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        w[u] = pack_bf16x2(f[h][2 * u], f[h][2 * u + 1]);
+      for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16x2(f[u][2 * e], f[u][2 * e + 1]);
         if constexpr (PARTS == 2)
-          wl[u] = pack_bf16x2(f[h][2 * u] - bf16_to_f32(w[u] & 0xFFFFu),
-                              f[h][2 * u + 1] - bf16_to_f32(w[u] >> 16));
+          l[e] = pack_bf16x2(f[u][2 * e] - bf16_to_f32(h[e] & 0xFFFFu),
+                             f[u][2 * e + 1] - bf16_to_f32(h[e] >> 16));
       }
-      *reinterpret_cast<uint4*>(hi + rl * LDK + 8 * (t & 3)) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(lds + off) = make_uint4(h[0], h[1], h[2], h[3]);
       if constexpr (PARTS == 2)
-        *reinterpret_cast<uint4*>(lo + rl * LDK + 8 * (t & 3)) =
-            make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        *reinterpret_cast<uint4*>(lds + LO_OFF + off) = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
 };
@@ -137,7 +144,7 @@ __device__ __forceinline__ float* pair_mat(const CosBatch& b, int p, int64_t off
 // ------------------------------------------------------------- 1: C = P~n^T P~o ---
 
 __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CosTile::STAGE];
   int local;
   const int p = pair_of_block(b, blockIdx.x, local);
   const CosPair& q = b.pair[p];
@@ -145,25 +152,26 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   const int s = local / per_split;
   const int rem = local - s * per_split;
   const int ti = rem / b.tiles, tj = rem - ti * b.tiles;
-  const int i0 = ti * TM, j0 = tj * TN;
+  const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int64_t k_begin = (int64_t)s * q.kslab;
   const int64_t k_end = min<int64_t>(q.m, k_begin + q.kslab);
-  StageInt4T sa(q.qa, q.sa, b.r, k_end, b.r, i0);
-  StageInt4T sb(q.qb, q.sb, b.r, k_end, b.r, j0);
+  StageInt4K<128, CosTile::BK> sa(q.qa, q.sa, b.r, k_end, b.r, i0);
+  StageInt4K<128, CosTile::BK> sb(q.qb, q.sb, b.r, k_end, b.r, j0);
   f32x16 acc[2][2];
-  gemm_kloop<1>(sa, sb, [i0](StageInt4T& st, uint16_t* st0) { st.store(st0, i0); },
-                [j0](StageInt4T& st, uint16_t* st0) { st.store(st0 + TM * LDK, j0); },
-                k_begin, k_end, lds, acc);
+  gemm_kloop<CosTile, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<CosTile::B_PITCH>(p + CosTile::A_ELEMS); },
+      k_begin, k_end, lds, acc);
   float* out = pair_mat(b, p, b.off_part) + (int64_t)s * b.r * b.r;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const int64_t j = j0 + acc_col(y);
+      const int64_t j = j0 + acc_col<CosTile>(y);
       if (j >= b.r) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row(x, v);
+        const int64_t i = i0 + acc_row<CosTile>(x, v);
         if (i < b.r) gstore(out + i * b.r + j, (float)acc[x][y][v]);
       }
     }
@@ -241,46 +249,44 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_init(CosBatch b) {
 template <bool TA, int PARTS>
 __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_x, int64_t off_a,
                                                       int64_t off_y) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PARTS * STAGE_ELEMS];
+  constexpr int STAGE = CosTile::STAGE > NsTileNN::STAGE ? CosTile::STAGE : NsTileNN::STAGE;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PARTS * STAGE];
   const int per_pair = b.tiles * b.tiles;
   const int p = blockIdx.x / per_pair;
   const int rem = blockIdx.x - p * per_pair;
   const int ti = rem / b.tiles, tj = rem - ti * b.tiles;
-  const int i0 = ti * TM, j0 = tj * TN;
+  const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int r = b.r;
   const float* X = pair_mat(b, p, off_x);
   const float* A = pair_mat(b, p, off_a);
   float* Y = pair_mat(b, p, off_y);
   f32x16 acc[2][2];
   if constexpr (TA) {
-    StageF32T<PARTS> sa(X, r, r, r, i0);
-    StageF32T<PARTS> sb(X, r, r, r, j0);
-    gemm_kloop<PARTS>(
-        sa, sb,
-        [i0](StageF32T<PARTS>& st, uint16_t* s0) { st.store(s0, s0 + STAGE_ELEMS, i0); },
-        [j0](StageF32T<PARTS>& st, uint16_t* s0) {
-          st.store(s0 + TM * LDK, s0 + STAGE_ELEMS + TM * LDK, j0);
-        },
-        0, r, lds, acc);
+    using T = CosTile;
+    StageF32K<128, T::BK, PARTS, T::STAGE> sa(X, r, r, r, i0);
+    StageF32K<128, T::BK, PARTS, T::STAGE> sb(X, r, r, r, j0);
+    gemm_kloop<T, PARTS>(
+        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
+        acc);
   } else {
-    StageF32N<PARTS> sa(X, r, r, i0);
-    StageF32T<PARTS> sb(A, r, r, r, j0);
-    gemm_kloop<PARTS>(
-        sa, sb, [](StageF32N<PARTS>& st, uint16_t* s0) { st.store(s0, s0 + STAGE_ELEMS); },
-        [j0](StageF32T<PARTS>& st, uint16_t* s0) {
-          st.store(s0 + TM * LDK, s0 + STAGE_ELEMS + TM * LDK, j0);
-        },
-        0, r, lds, acc);
+    using T = NsTileNN;
+    StageF32C<128, T::BK, PARTS, T::STAGE> sa(X, r, r, i0);
+    StageF32K<128, T::BK, PARTS, T::STAGE> sb(A, r, r, r, j0);
+    gemm_kloop<T, PARTS>(
+        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
+        acc);
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const int64_t j = j0 + acc_col(y);
+      const int64_t j = j0 + acc_col<CosTile>(y);
       if (j >= r) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row(x, v);
+        const int64_t i = i0 + acc_row<CosTile>(x, v);
         if (i >= r) continue;
         float out = acc[x][y][v];
         if constexpr (!TA) out = 1.5f * gload(X + i * r + j) - 0.5f * out;

@@ -32,6 +32,7 @@ struct LayerDev {
   int32_t kslab;       // rows of G per split (multiple of the K tile)
   int32_t p_tiles_i;   // projection tiles along r
   int32_t p_tiles_j;   // projection tiles along n
+  int32_t b_tiles_i;   // back-projection tiles along m
   int32_t b_tiles_j;   // back-projection tiles along n
   int32_t wg_base[3];  // first workgroup of this layer in the projection / Adam /
                        // back-projection launch of a grouped step
@@ -49,14 +50,16 @@ struct StepArgs {
 
 enum { KPROJ = 0, KADAM = 1, KBACK = 2 };
 
-__device__ __forceinline__ LayerDev fetch_layer(const StepArgs& a, int kernel, int& local) {
+// `logical` is the workgroup's position in the launch after any renumbering.
+__device__ __forceinline__ LayerDev fetch_layer(const StepArgs& a, int kernel, int logical,
+                                               int& local) {
   if (a.table == nullptr) {
-    local = blockIdx.x;
+    local = logical;
     return a.one;
   }
-  const int li = a.wg_layer[blockIdx.x];
+  const int li = a.wg_layer[logical];
   LayerDev L = a.table[li];
-  local = blockIdx.x - L.wg_base[kernel];
+  local = logical - L.wg_base[kernel];
   return L;
 }
 

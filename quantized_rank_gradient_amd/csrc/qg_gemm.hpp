@@ -1,214 +1,268 @@
 // MFMA tile machinery shared by the projection (R = P~^T G), back-projection (U = P~ N~)
-// and subspace-similarity (C = P~_new^T P~_old) kernels.
+// and subspace-similarity kernels.
 //
-// Workgroup tile 128 x 128 over the output, K consumed 32 at a time, 4 waves in a 2 x 2
-// arrangement, each wave owning a 64 x 64 sub-tile as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
-// Both operands live in LDS "k-contiguous": row c of the tile holds its 32 K values, so an
-// MFMA lane reads its 8 consecutive K values with one 16-byte LDS read. Sources whose K index
-// is the slow (row) index in memory -- the gradient G, the update N~ and the projection when
-// it is used transposed -- are transposed while being written to LDS; the INT4 dequant
-// (code * group scale, then bf16 rounding) happens in the same step, so P~ never exists in HBM.
+// A workgroup of 4 wave64 computes a BM x BN output tile; the waves sit in a WM x WN grid and
+// each owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation). K is consumed BK at a time through a
+// double-buffered LDS stage, with the next stage's global loads in flight while the current
+// one feeds the MFMAs.
+//
+// An MFMA lane needs 8 consecutive K values of one row of A (or one column of B). Operands
+// are kept in LDS in the layout their source has, so staging is a straight copy (plus the
+// INT4 dequant: code * group scale, then bf16 rounding, done on the way into LDS so P~
+// never exists in HBM):
+//   * "K-contiguous" tiles (source [c][k]: the projection in the back-projection) are read
+//     with one 16-byte ds_read_b128 per fragment;
+//   * "K-major" tiles (source [k][c]: the gradient G, the update N~, the projection used
+//     transposed) are read with two ds_read_b64_tr_b16, the gfx950 LDS transpose read: in a
+//     group of 16 lanes, lane i receives element i % 4 of the 8-byte chunks addressed by
+//     lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12. Addressing the chunk of row k0 + (i/4) + 4h,
+//     columns c0 + 16 ((l/16) % 2) + 4 (l % 4), gives lane l the K values k0 .. k0+3 (h = 0)
+//     and k0+4 .. k0+7 (h = 1) of column c0 + l % 32.
 #pragma once
 
 #include "qg_device.hpp"
 
 namespace qg {
 
-constexpr int TM = 128;             // output tile rows (MFMA "A" side)
-constexpr int TN = 128;             // output tile cols (MFMA "B" side)
-constexpr int TK = 32;              // K per stage
-constexpr int LDK = TK + 8;         // LDS row pitch in bf16 (80 bytes: keeps 16-byte reads aligned)
-constexpr int STAGE_ELEMS = (TM + TN) * LDK;
-constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;   // double-buffered: 40 KiB
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool A_KMAJOR_, bool B_KMAJOR_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_;
+  static_assert(WM * WN == 4, "four waves per workgroup");
+  static_assert(BK % 16 == 0, "K stage is a multiple of the MFMA K");
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave sub-tile
+  static constexpr int XM = WTM / 32, XN = WTN / 32;   // MFMA blocks per wave
+  static_assert(XM * 32 == WTM && XN * 32 == WTN, "wave tile is a multiple of 32");
+  // LDS pitches (bf16 elements): K-major tiles are BK rows of (edge + 16); K-contiguous tiles
+  // are edge rows of (BK + 8). Both keep 16-byte rows and spread rows over the banks.
+  static constexpr int A_PITCH = A_KMAJOR ? BM + 16 : BK + 8;
+  static constexpr int B_PITCH = B_KMAJOR ? BN + 16 : BK + 8;
+  static constexpr int A_ELEMS = A_KMAJOR ? BK * A_PITCH : BM * A_PITCH;
+  static constexpr int B_ELEMS = B_KMAJOR ? BK * B_PITCH : BN * B_PITCH;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;      // one [A | B] stage, bf16 elements
+};
 
 // ---------------------------------------------------------------------------------------
-// bf16 source stored [k][c] (row pitch ld), tile columns [c0, c0+128), written to LDS [c][k].
-// Thread t stages rows k+2p, k+2p+1 (p = t / 16) and columns c0 + 8*(t % 16) .. +7.
+// Stagers: each fills one operand tile (W = its edge along the output, BK along K) with 256
+// threads, in 8-element chunks. load() issues the global loads into registers, store()
+// converts and writes LDS. Consecutive lanes take consecutive chunks along the contiguous
+// dimension of the source, so global loads are coalesced.
 // ---------------------------------------------------------------------------------------
-struct StageBf16T {
+
+// bf16 source [k][c] (row pitch ld) -> K-major LDS tile [k][c].
+template <int W, int BK>
+struct StageBf16K {
+  static constexpr int CPR = W / 8;                    // chunks per row
+  static constexpr int NC = BK * CPR / kThreads;       // chunks per thread
+  static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
   const uint16_t* src;
   int64_t ld, k_end, c_end;
-  int c;            // first column this thread stages
-  int kp;           // row pair
-  bool vec_ok;      // 16-byte loads possible for in-bounds rows
-  uint4 v[2];
+  int c0;
+  bool vec_ld;
+  uint4 v[NC];
 
-  __device__ StageBf16T(const uint16_t* s, int64_t ld_, int64_t k_end_, int64_t c_end_, int c0)
-      : src(s), ld(ld_), k_end(k_end_), c_end(c_end_) {
-    const int t = threadIdx.x;
-    kp = t >> 4;
-    c = c0 + 8 * (t & 15);
-    vec_ok = (ld % 8 == 0) && (c + 8 <= c_end);
+  __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t k_end_, int64_t c_end_, int c0_)
+      : src(s), ld(ld_), k_end(k_end_), c_end(c_end_), c0(c0_) {
+    vec_ld = (ld % 8 == 0);
   }
 
   __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int64_t k = k0 + 2 * kp + rr;
-      if (k < k_end && vec_ok) {
-        v[rr] = gload(reinterpret_cast<const uint4*>(src + k * ld + c));
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t k = k0 + q / CPR;
+      const int64_t c = c0 + 8 * (q % CPR);
+      if (k < k_end && vec_ld && c + 8 <= c_end) {
+        v[u] = gload(reinterpret_cast<const uint4*>(src + k * ld + c));
       } else {
         uint32_t w[4] = {0, 0, 0, 0};
         if (k < k_end) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (c + e < c_end) w[e >> 1] |= (uint32_t)gload(src + k * ld + c + e) << (16 * (e & 1));
+            if (c + e < c_end)
+              w[e >> 1] |= (uint32_t)gload(src + k * ld + c + e) << (16 * (e & 1));
         }
-        v[rr] = make_uint4(w[0], w[1], w[2], w[3]);
+        v[u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }
 
-  // Transpose the 2 x 8 block into 8 dwords (k, k+1) and write them to LDS [c][k].
-  __device__ __forceinline__ void store(uint16_t* lds, int c0) const {
-    uint32_t* d = reinterpret_cast<uint32_t*>(lds);
-    const int cl = c - c0;
-    const uint32_t a[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t b[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-      d[(cl + cc) * (LDK / 2) + kp] = __builtin_amdgcn_perm(b[cc >> 1], a[cc >> 1], sel);
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v[u];
     }
   }
 };
 
-// ---------------------------------------------------------------------------------------
-// INT4 source stored [k][c] (row pitch ld codes, ld % 8 == 0), dequantized and written to LDS
-// [c][k]. Same thread mapping as StageBf16T. A run of 8 codes starting at a multiple of 8 in
-// the flat index lies inside one 256-element scale group, and since ld % 8 == 0 it is either
-// wholly inside the tile or wholly outside (then it stages zeros).
-// ---------------------------------------------------------------------------------------
-struct StageInt4T {
-  const uint8_t* q;
+// INT4 source [k][c] (row pitch ld codes, ld % 8 == 0) -> K-major LDS tile [k][c] in bf16.
+// A chunk of 8 codes starting at a multiple of 8 in the flat index lies inside one
+// 256-element scale group, and since ld % 8 == 0 it is either wholly inside the tile or
+// wholly outside (then it stages zeros).
+template <int W, int BK>
+struct StageInt4K {
+  static constexpr int CPR = W / 8;
+  static constexpr int NC = BK * CPR / kThreads;
+  static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
+  const uint8_t* q8;
   const float* sc;
   int64_t ld, k_end, c_end;
-  int c, kp;
-  uint32_t w[2];
-  float s[2];
+  int c0;
+  uint32_t w[NC];
+  float s[NC];
 
-  __device__ StageInt4T(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t k_end_,
-                        int64_t c_end_, int c0)
-      : q(q_), sc(sc_), ld(ld_), k_end(k_end_), c_end(c_end_) {
-    const int t = threadIdx.x;
-    kp = t >> 4;
-    c = c0 + 8 * (t & 15);
-  }
+  __device__ StageInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t k_end_,
+                        int64_t c_end_, int c0_)
+      : q8(q_), sc(sc_), ld(ld_), k_end(k_end_), c_end(c_end_), c0(c0_) {}
 
   __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int64_t k = k0 + 2 * kp + rr;
-      w[rr] = 0u;
-      s[rr] = 0.0f;
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t k = k0 + q / CPR;
+      const int64_t c = c0 + 8 * (q % CPR);
+      w[u] = 0u;
+      s[u] = 0.0f;
       if (k < k_end && c < c_end) {
         const int64_t e = k * ld + c;
-        w[rr] = gload(reinterpret_cast<const uint32_t*>(q + (e >> 1)));
-        s[rr] = gload(sc + (e >> 8));
+        w[u] = gload(reinterpret_cast<const uint32_t*>(q8 + (e >> 1)));
+        s[u] = gload(sc + (e >> 8));
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* lds, int c0) const {
-    uint32_t* d = reinterpret_cast<uint32_t*>(lds);
-    const int cl = c - c0;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const float f0 = mul_rn((float)nibble(w[0], cc), s[0]);
-      const float f1 = mul_rn((float)nibble(w[1], cc), s[1]);
-      d[(cl + cc) * (LDK / 2) + kp] = pack_bf16x2(f0, f1);
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------------------
-// INT4 source stored [c][k] (row pitch ld codes, K contiguous, ld % 8 == 0), tile rows
-// [c0, c0+128), dequantized and written to LDS [c][k] without transposition. Thread t stages
-// two runs: row (t / 4) + 64*h, codes k0 + 8*(t % 4) .. +7, h = 0, 1.
-// ---------------------------------------------------------------------------------------
-struct StageInt4N {
-  const uint8_t* q;
-  const float* sc;
-  int64_t ld, c_end;   // ld = K extent (codes per row)
-  int c0;
-  uint32_t w[2];
-  float s[2];
-
-  __device__ StageInt4N(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
-      : q(q_), sc(sc_), ld(ld_), c_end(c_end_), c0(c0_) {}
-
-  __device__ __forceinline__ void load(int64_t k0) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t row = c0 + (t >> 2) + 64 * h;
-      const int64_t k = k0 + 8 * (t & 3);
-      w[h] = 0u;
-      s[h] = 0.0f;
-      if (row < c_end && k < ld) {
-        const int64_t e = row * ld + k;
-        w[h] = gload(reinterpret_cast<const uint32_t*>(q + (e >> 1)));
-        s[h] = gload(sc + (e >> 8));
-      }
-    }
-  }
-
+  template <int PITCH>
   __device__ __forceinline__ void store(uint16_t* lds) const {
-    const int t = threadIdx.x;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
       float f[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) f[u] = mul_rn((float)nibble(w[h], u), s[h]);
-      const int rl = (t >> 2) + 64 * h;
-      const uint4 pk = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                  pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-      *reinterpret_cast<uint4*>(lds + rl * LDK + 8 * (t & 3)) = pk;
+      for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w[u], e), s[u]);
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) =
+          make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+  }
+};
+
+// INT4 source [c][k] (row pitch ld codes = the K extent, ld % 8 == 0) -> K-contiguous LDS
+// tile [c][k] in bf16.
+template <int W, int BK>
+struct StageInt4C {
+  static constexpr int CPR = BK / 8;
+  static constexpr int NC = W * CPR / kThreads;
+  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
+  const uint8_t* q8;
+  const float* sc;
+  int64_t ld, c_end;
+  int c0;
+  uint32_t w[NC];
+  float s[NC];
+
+  __device__ StageInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
+      : q8(q_), sc(sc_), ld(ld_), c_end(c_end_), c0(c0_) {}
+
+  __device__ __forceinline__ void load(int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t row = c0 + q / CPR;
+      const int64_t k = k0 + 8 * (q % CPR);
+      w[u] = 0u;
+      s[u] = 0.0f;
+      if (row < c_end && k < ld) {
+        const int64_t e = row * ld + k;
+        w[u] = gload(reinterpret_cast<const uint32_t*>(q8 + (e >> 1)));
+        s[u] = gload(sc + (e >> 8));
+      }
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w[u], e), s[u]);
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) =
+          make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
     }
   }
 };
 
 // ---------------------------------------------------------------------------------------
-// The K loop: acc[x][y] (wave sub-tile rows 32*x, cols 32*y) += A_tile * B_tile over K in
-// [k_begin, k_end). A stage holds PARTS copies of the [A | B] tile pair: PARTS = 1 is the
-// plain bf16 product; PARTS = 2 holds the bf16 "high" parts followed by the bf16 "low"
-// remainders of fp32 operands, and the product keeps hi*hi + hi*lo + lo*hi (about 16
-// significant bits per operand). store_a(sa, stage) / store_b(sb, stage) fill one stage.
+// Fragment reads and the K loop.
 // ---------------------------------------------------------------------------------------
-template <int PARTS>
-__device__ __forceinline__ void mfma_stage(const uint16_t* stage, f32x16 (&acc)[2][2]) {
+template <class T>
+__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / T::WN; }
+template <class T>
+__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % T::WN; }
+
+// 8 K values (ks .. ks+7 of this lane's half) of row/column `c` (c = tile-relative index of
+// lane 0's row for this 32-block) from a tile with the given layout.
+template <bool KMAJOR, int PITCH>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int c, int ks) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hk = (lane >> 5) * 8;
+  if constexpr (!KMAJOR) {
+    return *reinterpret_cast<const bf16x8*>(tile + (c + (lane & 31)) * PITCH + ks +
+                                            8 * (lane >> 5));
+  } else {
+    typedef __attribute__((address_space(3))) v4i16* lptr;
+    const int row = ks + 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = c + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint16_t* p0 = tile + row * PITCH + col;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lptr)(__attribute__((address_space(3))) void*)(p0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lptr)(__attribute__((address_space(3))) void*)(p0 + 4 * PITCH));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, all);
+  }
+}
+
+// PARTS = 1: plain bf16 product. PARTS = 2: the stage holds the bf16 "high" parts followed by
+// the bf16 "low" remainders of fp32 operands; the product keeps hi*hi + hi*lo + lo*hi (about
+// 16 significant bits per operand).
+template <class T, int PARTS>
+__device__ __forceinline__ void mfma_stage(const uint16_t* stage,
+                                           f32x16 (&acc)[T::XM][T::XN]) {
+  const int am = wave_m<T>() * T::WTM, bn = wave_n<T>() * T::WTN;
   const uint16_t* As = stage;
-  const uint16_t* Bs = stage + TM * LDK;
+  const uint16_t* Bs = stage + T::A_ELEMS;
 #pragma unroll
-  for (int ks = 0; ks < TK; ks += 16) {
-    bf16x8 a[2], b[2];
+  for (int ks = 0; ks < T::BK; ks += 16) {
+    bf16x8 a[T::XM], b[T::XN];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      a[x] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + 32 * x + l32) * LDK + ks + hk);
-      b[x] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + 32 * x + l32) * LDK + ks + hk);
-    }
+    for (int x = 0; x < T::XM; ++x) a[x] = frag<T::A_KMAJOR, T::A_PITCH>(As, am + 32 * x, ks);
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < T::XN; ++y) b[y] = frag<T::B_KMAJOR, T::B_PITCH>(Bs, bn + 32 * y, ks);
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
+    for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+      for (int y = 0; y < T::XN; ++y)
         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
     if constexpr (PARTS == 2) {
-      const uint16_t* Al = stage + STAGE_ELEMS;
-      const uint16_t* Bl = Al + TM * LDK;
-      bf16x8 al[2], bl[2];
+      bf16x8 al[T::XM], bl[T::XN];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        al[x] = *reinterpret_cast<const bf16x8*>(Al + (wm * 64 + 32 * x + l32) * LDK + ks + hk);
-        bl[x] = *reinterpret_cast<const bf16x8*>(Bl + (wn * 64 + 32 * x + l32) * LDK + ks + hk);
-      }
+      for (int x = 0; x < T::XM; ++x)
+        al[x] = frag<T::A_KMAJOR, T::A_PITCH>(As + T::STAGE, am + 32 * x, ks);
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int y = 0; y < T::XN; ++y)
+        bl[y] = frag<T::B_KMAJOR, T::B_PITCH>(Bs + T::STAGE, bn + 32 * y, ks);
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
+      for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+        for (int y = 0; y < T::XN; ++y) {
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], bl[y], acc[x][y], 0, 0, 0);
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[x], b[y], acc[x][y], 0, 0, 0);
         }
@@ -216,51 +270,58 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* stage, f32x16 (&acc)[
   }
 }
 
-template <int PARTS, class SA, class SB, class StoreA, class StoreB>
+// acc[x][y] += A_tile * B_tile over K in [k_begin, k_end). store_a(sa, stage) /
+// store_b(sb, stage) fill one stage from the loaded registers. The loop body has no branch,
+// so the scheduler can interleave the next stage's conversion and LDS writes with the MFMAs.
+template <class T, int PARTS, class SA, class SB, class StoreA, class StoreB>
 __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, StoreB store_b,
                                            int64_t k_begin, int64_t k_end, uint16_t* lds,
-                                           f32x16 (&acc)[2][2]) {
-  constexpr int STAGE = PARTS * STAGE_ELEMS;
+                                           f32x16 (&acc)[T::XM][T::XN]) {
+  constexpr int STAGE = PARTS * T::STAGE;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < T::XN; ++y)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
   if (k_end <= k_begin) return;
-  const int nk = (int)((k_end - k_begin + TK - 1) / TK);
+  const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
   sa.load(k_begin);
   sb.load(k_begin);
   store_a(sa, lds);
   store_b(sb, lds);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      sa.load(k_begin + (int64_t)(kt + 1) * TK);
-      sb.load(k_begin + (int64_t)(kt + 1) * TK);
-    }
-    uint16_t* now = lds + cur * STAGE;
-    uint16_t* nxt = lds + (cur ^ 1) * STAGE;
-    mfma_stage<PARTS>(now, acc);
-    if (more) {
-      store_a(sa, nxt);
-      store_b(sb, nxt);
-    }
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    sa.load(k_begin + (int64_t)(kt + 1) * T::BK);
+    sb.load(k_begin + (int64_t)(kt + 1) * T::BK);
+    mfma_stage<T, PARTS>(lds + (kt & 1) * STAGE, acc);
+    store_a(sa, lds + ((kt + 1) & 1) * STAGE);
+    store_b(sb, lds + ((kt + 1) & 1) * STAGE);
     __syncthreads();
   }
+  mfma_stage<T, PARTS>(lds + ((nk - 1) & 1) * STAGE, acc);
+  __syncthreads();
 }
 
 // Output coordinates of accumulator element v of block (x, y) for this lane, relative to the
-// workgroup tile: row = wm*64 + 32x + 8*(v/4) + 4*(lane/32) + v%4, col = wn*64 + 32y + lane%32.
+// workgroup tile: row = wm*WTM + 32x + 8(v/4) + 4(lane/32) + v%4, col = wn*WTN + 32y + lane%32.
+template <class T>
 __device__ __forceinline__ int acc_row(int x, int v) {
-  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-  return wm * 64 + 32 * x + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+  const int lane = threadIdx.x & 63;
+  return wave_m<T>() * T::WTM + 32 * x + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
+template <class T>
 __device__ __forceinline__ int acc_col(int y) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-  return wn * 64 + 32 * y + (lane & 31);
+  const int lane = threadIdx.x & 63;
+  return wave_n<T>() * T::WTN + 32 * y + (lane & 31);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin; renumber them so that consecutive
+// logical tiles (which share input rows or columns) run on the same XCD and hit its L2.
+__device__ __forceinline__ int xcd_remap(int b, int grid) {
+  const int n8 = (grid / 8) * 8;
+  if (b >= n8) return b;
+  return (b & 7) * (n8 >> 3) + (b >> 3);
 }
 
 }  // namespace qg

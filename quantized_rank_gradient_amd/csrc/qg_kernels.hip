@@ -18,37 +18,46 @@ namespace qg {
 
 // ======================================================================== projection ===
 
+// Tile shapes: rank above 128 takes 256 x 256 tiles with K stages of 64 (each wave a 128 x 128
+// block of 16 MFMA accumulators); rank up to 128 takes 128 (all of r) x 256 with K stages of 32.
+// Both operands are K-major in memory (P is [k][i], G is [k][j]).
+using ProjBig = Tile<256, 256, 64, 2, 2, true, true>;
+using ProjSmall = Tile<128, 256, 32, 2, 2, true, true>;
+
+template <class T>
 __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
   int local;
-  const LayerDev L = fetch_layer(a, KPROJ, local);
-  const int per_split = L.p_tiles_i * L.p_tiles_j;
-  const int s = local / per_split;
-  const int rem = local - s * per_split;
-  const int ti = rem / L.p_tiles_j;
-  const int tj = rem - ti * L.p_tiles_j;
-  const int i0 = ti * TM, j0 = tj * TN;
+  const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
+  // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
+  // columns are neighbours (and, after the renumbering, on the same XCD).
+  const int ti = local % L.p_tiles_i;
+  const int rest = local / L.p_tiles_i;
+  const int tj = rest % L.p_tiles_j;
+  const int s = rest / L.p_tiles_j;
+  const int i0 = ti * T::BM, j0 = tj * T::BN;
   const int64_t k_begin = (int64_t)s * L.kslab;
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
   // A = P~^T: P is stored [k][i] (m x r), so the tile rows i are columns of P.
-  StageInt4T sa(L.Pq, L.Ps, L.r, k_end, L.r, i0);
-  StageBf16T sb(L.G, L.n, k_end, L.n, j0);
-  f32x16 acc[2][2];
-  gemm_kloop<1>(sa, sb, [i0](StageInt4T& st, uint16_t* p) { st.store(p, i0); },
-                [j0](StageBf16T& st, uint16_t* p) { st.store(p + TM * LDK, j0); }, k_begin,
-                k_end, lds, acc);
+  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, k_end, L.r, i0);
+  StageBf16K<T::BN, T::BK> sb(L.G, L.n, k_end, L.n, j0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop<T, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
+      k_end, lds, acc);
 
   float* out = reinterpret_cast<float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int64_t j = j0 + acc_col(y);
+    for (int y = 0; y < T::XN; ++y) {
+      const int64_t j = j0 + acc_col<T>(y);
       if (j >= L.n) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row(x, v);
+        const int64_t i = i0 + acc_row<T>(x, v);
         if (i < L.r) gstore(out + i * L.n + j, (float)acc[x][y][v]);
       }
     }
@@ -60,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
 
 __global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
   int local;
-  const LayerDev L = fetch_layer(a, KADAM, local);
+  const LayerDev L = fetch_layer(a, KADAM, blockIdx.x, local);
   const int lane = threadIdx.x & 63;
   const int64_t numel = L.r * L.n;
   const int64_t ngroups = (numel + kGroup - 1) / kGroup;
@@ -206,49 +215,63 @@ __device__ __forceinline__ void sr_block8(const LayerDev& L, const StepArgs& a, 
   }
 }
 
+// P~ rows are K-contiguous ([i][k]); N~ is K-major ([k][j]).
+using BackBig = Tile<256, 128, 32, 2, 2, false, true>;
+using BackSmall = Tile<128, 128, 32, 2, 2, false, true>;
+static_assert(ProjBig::BM == kProjTileM(true) && ProjSmall::BM == kProjTileM(false) &&
+                  ProjBig::BN == kProjTileN && ProjSmall::BN == kProjTileN,
+              "host and device projection tiles agree");
+static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true) &&
+                  BackSmall::BM == kBackTileM(false) && BackSmall::BN == kBackTileN(false),
+              "host and device back-projection tiles agree");
+
+template <class T>
 __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  constexpr int EP = T::WTN + 4;   // fp32 row pitch of the redistribution block
+  constexpr int LDS_BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
+                                ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
   int local;
-  const LayerDev L = fetch_layer(a, KBACK, local);
+  const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
   const int ti = local / L.b_tiles_j;
   const int tj = local - ti * L.b_tiles_j;
-  const int i0 = ti * TM, j0 = tj * TN;
+  const int i0 = ti * T::BM, j0 = tj * T::BN;
 
   // A = P~ (rows i of P, K = rank index contiguous), B = N~ stored [k][j] (r x n).
-  StageInt4N sa(L.Pq, L.Ps, L.r, L.m, i0);
-  StageBf16T sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.n, j0);
-  f32x16 acc[2][2];
-  gemm_kloop<1>(sa, sb, [](StageInt4N& st, uint16_t* p) { st.store(p); },
-                [j0](StageBf16T& st, uint16_t* p) { st.store(p + TM * LDK, j0); }, 0, L.r, lds,
-                acc);
+  StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
+  StageBf16K<T::BN, T::BK> sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.n,
+                              j0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop<T, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, L.r, lds,
+      acc);
 
-  // Redistribute each wave's 64 x 64 block through LDS, 32 rows at a time, so that every
-  // lane owns 32 consecutive columns of one row: whole Philox blocks and wide W accesses.
-  constexpr int EP = 68;   // fp32 row pitch of the staging block
+  // Redistribute each wave's block through LDS, 32 rows at a time, so that every lane owns
+  // WTN/2 consecutive columns of one row: whole Philox blocks and wide W accesses.
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave_m<T>(), wn = wave_n<T>();
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
+  const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  for (int x = 0; x < T::XM; ++x) {
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < T::XN; ++y)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         E[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + 32 * y + (lane & 31)] = acc[x][y][v];
     __syncthreads();
-    const int rr = lane >> 1, cc = (lane & 1) * 32;
-    float S[32];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 f = *reinterpret_cast<const float4*>(E + rr * EP + cc + 4 * q);
-      S[4 * q] = f.x; S[4 * q + 1] = f.y; S[4 * q + 2] = f.z; S[4 * q + 3] = f.w;
-    }
-    const int64_t i = (int64_t)i0 + wm * 64 + 32 * x + rr;
-    const int64_t jb = (int64_t)j0 + wn * 64 + cc;
+    const int64_t i = (int64_t)i0 + wm * T::WTM + 32 * x + rr;
+    const int64_t jb = (int64_t)j0 + wn * T::WTN + cc;
     if (i < L.m) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sr_block8(L, a, i, jb + 8 * q, S + 8 * q);
+      for (int q = 0; q < T::WTN / 16; ++q) {
+        const float4 f0 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q);
+        const float4 f1 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q + 4);
+        const float S[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        sr_block8(L, a, i, jb + 8 * q, S);
+      }
     }
     __syncthreads();
   }
@@ -287,16 +310,22 @@ __global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int
 
 // ==================================================================== launchers ===
 
-hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(qg_project, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL(qg_project<ProjBig>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(qg_project<ProjSmall>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(qg_adam, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
-hipError_t launch_backproject(const StepArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(qg_backproject, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL(qg_backproject<BackBig>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(qg_backproject<BackSmall>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,

@@ -31,9 +31,15 @@ struct CosBatch {
   int iters_bf16, iters_split;   // Newton-Schulz iterations with bf16 / split operands
 };
 
-hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s);
+// Tile edges of the two configurations of each MFMA kernel ("big": rank above 128).
+constexpr int kProjTileM(bool big) { return big ? 256 : 128; }
+constexpr int kProjTileN = 256;
+constexpr int kBackTileM(bool big) { return big ? 256 : 128; }
+constexpr int kBackTileN(bool big) { return big ? 128 : 128; }
+
+hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
-hipError_t launch_backproject(const StepArgs& a, int grid, hipStream_t s);
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s);
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,
                                 hipStream_t s);
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s);

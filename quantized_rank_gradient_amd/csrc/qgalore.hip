@@ -28,7 +28,7 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 bool finite(float x) { return std::isfinite(x); }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-constexpr int kTile = 128;   // output tile edge of the MFMA kernels
+constexpr int kTile = 128;   // output tile edge of the similarity kernels
 constexpr int kK = 32;       // K per stage of the MFMA kernels
 
 qg_status device_present() {
@@ -48,10 +48,16 @@ qg_status check_shape(int64_t m, int64_t n, int64_t r) {
   return QG_OK;
 }
 
+// Tile configuration of the MFMA kernels: the larger tiles once the rank exceeds 128.
+bool big_tiles(int64_t r) { return r > 128; }
+int64_t proj_tiles(int64_t n, int64_t r, bool big) {
+  return cdiv(r, qg::kProjTileM(big)) * cdiv(n, qg::kProjTileN);
+}
+
 // K-splits of the projection R = P~^T G for one layer launched on its own: enough
 // workgroups to cover the chip, bounded so the fp32 partial sums stay small next to G.
 int choose_split(int64_t m, int64_t n, int64_t r) {
-  const int64_t tiles = cdiv(r, kTile) * cdiv(n, kTile);
+  const int64_t tiles = proj_tiles(n, r, big_tiles(r));
   const int64_t kchunks = cdiv(m, kK);
   int64_t s = cdiv(512, tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, m / (8 * r)));
@@ -120,7 +126,7 @@ void step_constants(float beta1, float beta2, int64_t step, StepArgs& a) {
 
 LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, const float* W_scale,
                     const uint8_t* P_q, const float* P_scale, int8_t* M_q, int8_t* V_q,
-                    int split, int64_t ws_base) {
+                    int split, int64_t ws_base, bool big) {
   LayerDev L;
   std::memset(&L, 0, sizeof(L));
   L.G = G;
@@ -144,9 +150,10 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.layer_id = d->layer_id;
   L.split = split;
   L.kslab = (int32_t)kslab_for(d->m, split);
-  L.p_tiles_i = (int32_t)cdiv(d->r, kTile);
-  L.p_tiles_j = (int32_t)cdiv(d->n, kTile);
-  L.b_tiles_j = (int32_t)cdiv(d->n, kTile);
+  L.p_tiles_i = (int32_t)cdiv(d->r, qg::kProjTileM(big));
+  L.p_tiles_j = (int32_t)cdiv(d->n, qg::kProjTileN);
+  L.b_tiles_i = (int32_t)cdiv(d->m, qg::kBackTileM(big));
+  L.b_tiles_j = (int32_t)cdiv(d->n, qg::kBackTileN(big));
   L.lr = d->lr;
   L.eps = d->eps;
   L.alpha = d->alpha;
@@ -155,14 +162,14 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
 
 int grid_project(const LayerDev& L) { return L.split * L.p_tiles_i * L.p_tiles_j; }
 int grid_adam(const LayerDev& L) { return (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4); }
-int grid_back(const LayerDev& L) { return (int)(cdiv(L.m, kTile) * L.b_tiles_j); }
+int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
 
-qg_status launch_step(const StepArgs& a, const int grid[3], hipStream_t s) {
-  hipError_t e = qg::launch_project(a, grid[0], s);
+qg_status launch_step(const StepArgs& a, const int grid[3], bool big, hipStream_t s) {
+  hipError_t e = qg::launch_project(a, grid[0], big, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   e = qg::launch_adam(a, grid[1], s);
   if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
-  e = qg::launch_backproject(a, grid[2], s);
+  e = qg::launch_backproject(a, grid[2], big, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   return QG_OK;
 }
@@ -191,7 +198,8 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
 
   StepArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.one = make_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q, split, 0);
+  const bool big = big_tiles(d->r);
+  a.one = make_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q, split, 0, big);
   a.ws = static_cast<char*>(d->workspace);
   a.table = nullptr;
   a.wg_layer = nullptr;
@@ -199,7 +207,7 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
   const int grid[3] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one)};
-  return launch_step(a, grid, static_cast<hipStream_t>(d->stream));
+  return launch_step(a, grid, big, static_cast<hipStream_t>(d->stream));
 }
 
 // ========================================================================= grouped ===
@@ -211,6 +219,7 @@ struct qg_plan {
   int grid[3] = {0, 0, 0};
   int64_t ws_bytes = 0;
   float beta1 = 0.f, beta2 = 0.f;
+  bool big = false;
   int device = 0;
   std::vector<hipEvent_t> events;   // 4 per recorded step when timing is enabled
   int timing_cap = 0;
@@ -245,14 +254,19 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   qg_status st = device_present();
   if (st != QG_OK) return st;
 
-  // One K-split for every layer unless the whole set has too few projection tiles.
+  // One tile configuration for the whole set (by its largest rank), and one K-split for every
+  // layer unless the set has too few projection tiles to fill the chip.
+  int64_t rmax = 0;
+  for (int32_t l = 0; l < count; ++l) rmax = std::max<int64_t>(rmax, layers[l].desc.r);
+  const bool big = big_tiles(rmax);
   int64_t tiles = 0;
   for (int32_t l = 0; l < count; ++l)
-    tiles += cdiv(layers[l].desc.r, kTile) * cdiv(layers[l].desc.n, kTile);
+    tiles += proj_tiles(layers[l].desc.n, layers[l].desc.r, big);
   const bool grouped_fill = tiles >= 1024;
 
   qg_plan* p = new (std::nothrow) qg_plan();
   if (!p) return QG_ERR_ARG;
+  p->big = big;
   p->beta1 = layers[0].desc.beta1;
   p->beta2 = layers[0].desc.beta2;
   int64_t ws = 0;
@@ -262,7 +276,7 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
     const qg_layer& x = layers[l];
     const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
     LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
-                            split, ws);
+                            split, ws, big);
     ws += ws_layout(x.desc.n, x.desc.r, split, ws).bytes;
     const int g[3] = {grid_project(L), grid_adam(L), grid_back(L)};
     for (int k = 0; k < 3; ++k) {
@@ -321,7 +335,7 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   if (ev) e = hipEventRecord(ev[0], s);
   if (e != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
-  e = qg::launch_project(a, p->grid[0], s);
+  e = qg::launch_project(a, p->grid[0], p->big, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[1];
@@ -329,7 +343,7 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
-  e = qg::launch_backproject(a, p->grid[2], s);
+  e = qg::launch_backproject(a, p->grid[2], p->big, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
   return QG_OK;
