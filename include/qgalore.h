@@ -63,7 +63,8 @@ extern "C" {
 typedef enum {
   QG_OK = 0,
   QG_ERR_NULL = 1,       /* a required pointer is NULL */
-  QG_ERR_SHAPE = 2,      /* m, n, r out of range (need 1 <= r <= m, m, n, r < 2^31) */
+  QG_ERR_SHAPE = 2,      /* m, n, r out of range: need 1 <= r <= m, r % 8 == 0, and
+                            m*n, r*n <= 2^29 (every per-layer tensor below 2 GiB) */
   QG_ERR_ALIGN = 3,      /* a base pointer breaks the alignment rule above */
   QG_ERR_WORKSPACE = 4,  /* workspace smaller than the size query returns */
   QG_ERR_ARG = 5,        /* step out of [1, 2^32), non-finite or out-of-range hyperparameter */

@@ -155,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int64_t k_begin = (int64_t)s * q.kslab;
   const int64_t k_end = min<int64_t>(q.m, k_begin + q.kslab);
-  StageInt4K<128, CosTile::BK> sa(q.qa, q.sa, b.r, k_end, b.r, i0);
-  StageInt4K<128, CosTile::BK> sb(q.qb, q.sb, b.r, k_end, b.r, j0);
+  StageInt4K<128, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+  StageInt4K<128, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
   f32x16 acc[2][2];
   gemm_kloop<CosTile, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },

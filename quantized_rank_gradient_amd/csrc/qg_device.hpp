@@ -85,6 +85,58 @@ __device__ __forceinline__ void gstore(T* p, T v) {
 #endif
 }
 
+// --------------------------------------------------------------- buffer accesses ---
+// Raw buffer loads and stores through a resource descriptor that bounds the tensor: an offset
+// at or past the end reads zeros and drops stores, so tile edges need no branches, and the
+// per-lane address is a 32-bit byte offset. Every tensor addressed this way is below 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past the end of any such tensor
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3: raw (untyped) access with a 32-bit data format, as gfx9 buffer loads require
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload128(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 bload64(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload16(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ float bloadf(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore32(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstoref(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore64(rsrc_t r, uint32_t off, uint2 v) {
+  typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+  const v2u32 x = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore128(rsrc_t r, uint32_t off, uint4 v) {
+  typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+  const v4u32 x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- numeric helpers ---
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -52,38 +52,47 @@ struct Tile {
 // dimension of the source, so global loads are coalesced.
 // ---------------------------------------------------------------------------------------
 
-// bf16 source [k][c] (row pitch ld) -> K-major LDS tile [k][c].
+// bf16 source [k][c] (row pitch ld, `rows` rows in all) -> K-major LDS tile [k][c].
 template <int W, int BK>
 struct StageBf16K {
   static constexpr int CPR = W / 8;                    // chunks per row
   static constexpr int NC = BK * CPR / kThreads;       // chunks per thread
   static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
-  const uint16_t* src;
-  int64_t ld, k_end, c_end;
+  rsrc_t rs;
+  uint32_t ld, k_end, c_end;
   int c0;
   bool vec_ld;
   uint4 v[NC];
 
-  __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t k_end_, int64_t c_end_, int c0_)
-      : src(s), ld(ld_), k_end(k_end_), c_end(c_end_), c0(c0_) {
-    vec_ld = (ld % 8 == 0);
+  __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t rows, int64_t k_end_,
+                        int64_t c_end_, int c0_)
+      : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
+    rs = make_rsrc(s, (uint32_t)(rows * ld_ * 2));
+    vec_ld = (ld_ % 8 == 0);
   }
 
-  __device__ __forceinline__ void load(int64_t k0) {
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
+    if (vec_ld) {
 #pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      const int64_t k = k0 + q / CPR;
-      const int64_t c = c0 + 8 * (q % CPR);
-      if (k < k_end && vec_ld && c + 8 <= c_end) {
-        v[u] = gload(reinterpret_cast<const uint4*>(src + k * ld + c));
-      } else {
+      for (int u = 0; u < NC; ++u) {
+        const int q = threadIdx.x + kThreads * u;
+        const uint32_t k = k0 + q / CPR;
+        const uint32_t c = c0 + 8 * (q % CPR);
+        const uint32_t off = (k < k_end && c < c_end) ? (k * ld + c) * 2 : kOOB;
+        v[u] = bload128(rs, off);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const int q = threadIdx.x + kThreads * u;
+        const uint32_t k = k0 + q / CPR;
+        const uint32_t c = c0 + 8 * (q % CPR);
         uint32_t w[4] = {0, 0, 0, 0};
-        if (k < k_end) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (c + e < c_end)
-              w[e >> 1] |= (uint32_t)gload(src + k * ld + c + e) << (16 * (e & 1));
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t off = (k < k_end && c + e < c_end) ? (k * ld + c + e) * 2 : kOOB;
+          w[e >> 1] |= bload16(rs, off) << (16 * (e & 1));
         }
         v[u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -100,8 +109,17 @@ struct StageBf16K {
   }
 };
 
-// INT4 source [k][c] (row pitch ld codes, ld % 8 == 0) -> K-major LDS tile [k][c] in bf16.
-// A chunk of 8 codes starting at a multiple of 8 in the flat index lies inside one
+// Dequantize one word of 8 INT4 codes with its group scale and pack the bf16 values.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w, e), s);
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// INT4 source [k][c] (row pitch ld codes, ld % 8 == 0, `rows` rows) -> K-major LDS tile [k][c]
+// in bf16. A chunk of 8 codes starting at a multiple of 8 in the flat index lies inside one
 // 256-element scale group, and since ld % 8 == 0 it is either wholly inside the tile or
 // wholly outside (then it stages zeros).
 template <int W, int BK>
@@ -109,30 +127,31 @@ struct StageInt4K {
   static constexpr int CPR = W / 8;
   static constexpr int NC = BK * CPR / kThreads;
   static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
-  const uint8_t* q8;
-  const float* sc;
-  int64_t ld, k_end, c_end;
+  rsrc_t rq, rsc;
+  uint32_t ld, k_end, c_end;
   int c0;
   uint32_t w[NC];
   float s[NC];
 
-  __device__ StageInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t k_end_,
-                        int64_t c_end_, int c0_)
-      : q8(q_), sc(sc_), ld(ld_), k_end(k_end_), c_end(c_end_), c0(c0_) {}
+  __device__ StageInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
+                        int64_t k_end_, int64_t c_end_, int c0_)
+      : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
+    const int64_t numel = rows * ld_;
+    rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
+    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
+  }
 
-  __device__ __forceinline__ void load(int64_t k0) {
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      const int64_t k = k0 + q / CPR;
-      const int64_t c = c0 + 8 * (q % CPR);
-      w[u] = 0u;
-      s[u] = 0.0f;
-      if (k < k_end && c < c_end) {
-        const int64_t e = k * ld + c;
-        w[u] = gload(reinterpret_cast<const uint32_t*>(q8 + (e >> 1)));
-        s[u] = gload(sc + (e >> 8));
-      }
+      const uint32_t k = k0 + q / CPR;
+      const uint32_t c = c0 + 8 * (q % CPR);
+      const bool in = k < k_end && c < c_end;
+      const uint32_t e = k * ld + c;
+      w[u] = bload32(rq, in ? (e >> 1) : kOOB);
+      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
     }
   }
 
@@ -141,46 +160,42 @@ struct StageInt4K {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w[u], e), s[u]);
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) =
-          make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
     }
   }
 };
 
-// INT4 source [c][k] (row pitch ld codes = the K extent, ld % 8 == 0) -> K-contiguous LDS
-// tile [c][k] in bf16.
+// INT4 source [c][k] (row pitch ld codes = the K extent, ld % 8 == 0, `rows` rows) ->
+// K-contiguous LDS tile [c][k] in bf16.
 template <int W, int BK>
 struct StageInt4C {
   static constexpr int CPR = BK / 8;
   static constexpr int NC = W * CPR / kThreads;
   static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
-  const uint8_t* q8;
-  const float* sc;
-  int64_t ld, c_end;
+  rsrc_t rq, rsc;
+  uint32_t ld, c_end;
   int c0;
   uint32_t w[NC];
   float s[NC];
 
   __device__ StageInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
-      : q8(q_), sc(sc_), ld(ld_), c_end(c_end_), c0(c0_) {}
+      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
+    const int64_t numel = c_end_ * ld_;
+    rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
+    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
+  }
 
-  __device__ __forceinline__ void load(int64_t k0) {
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      const int64_t row = c0 + q / CPR;
-      const int64_t k = k0 + 8 * (q % CPR);
-      w[u] = 0u;
-      s[u] = 0.0f;
-      if (row < c_end && k < ld) {
-        const int64_t e = row * ld + k;
-        w[u] = gload(reinterpret_cast<const uint32_t*>(q8 + (e >> 1)));
-        s[u] = gload(sc + (e >> 8));
-      }
+      const uint32_t row = c0 + q / CPR;
+      const uint32_t k = k0 + 8 * (q % CPR);
+      const bool in = row < c_end && k < ld;
+      const uint32_t e = row * ld + k;
+      w[u] = bload32(rq, in ? (e >> 1) : kOOB);
+      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
     }
   }
 
@@ -189,12 +204,7 @@ struct StageInt4C {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w[u], e), s[u]);
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) =
-          make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
     }
   }
 };

@@ -40,25 +40,27 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
   // A = P~^T: P is stored [k][i] (m x r), so the tile rows i are columns of P.
-  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, k_end, L.r, i0);
-  StageBf16K<T::BN, T::BK> sb(L.G, L.n, k_end, L.n, j0);
+  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, k_end, L.r, i0);
+  StageBf16K<T::BN, T::BK> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
       [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
       k_end, lds, acc);
 
-  float* out = reinterpret_cast<float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch;
+  // Partial sums of this K-split; out-of-range rows and columns are dropped by the buffer.
+  const rsrc_t ro = make_rsrc(a.ws + L.off_r + (int64_t)s * L.rpitch * 4,
+                              (uint32_t)(L.r * L.n * 4));
+  const uint32_t n = (uint32_t)L.n, r = (uint32_t)L.r;
 #pragma unroll
   for (int x = 0; x < T::XM; ++x)
 #pragma unroll
     for (int y = 0; y < T::XN; ++y) {
-      const int64_t j = j0 + acc_col<T>(y);
-      if (j >= L.n) continue;
+      const uint32_t j = j0 + acc_col<T>(y);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row<T>(x, v);
-        if (i < L.r) gstore(out + i * L.n + j, (float)acc[x][y][v]);
+        const uint32_t i = i0 + acc_row<T>(x, v);
+        bstoref(ro, (i < r && j < n) ? (i * n + j) * 4 : kOOB, acc[x][y][v]);
       }
     }
 }
@@ -166,22 +168,29 @@ __global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
 
 // ===================================================== back-projection + rounding ===
 
-// Stochastic rounding of 8 consecutive weights (i, j8 .. j8+7), j8 a multiple of 8. One
-// Philox call yields the 8 16-bit uniforms of the column block.
-__device__ __forceinline__ void sr_block8(const LayerDev& L, const StepArgs& a, int64_t i,
-                                          int64_t j8, const float* S) {
-  if (j8 >= L.n) return;
-  const uint4 ph = philox4x32_10(
-      make_uint4((uint32_t)(j8 >> 3), (uint32_t)i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
+// Stochastic rounding of 8 consecutive weights (i, j8 .. j8+7), j8 a multiple of 8: one
+// Philox call yields the 8 16-bit uniforms of the column block. `inv` is the reciprocal of the
+// block's weight group scale when the caller knows the 8 weights share one group (rows of
+// 8-multiple length); otherwise it is negative and the scale is looked up per element.
+struct SrCtx {
+  rsrc_t rw, rws, ru;
+  uint32_t n, m;
+  bool vec;          // n % 8 == 0: 8-byte weight accesses
+  bool write_u;
+};
+
+__device__ __forceinline__ void sr_block8(const SrCtx& c, const LayerDev& L, const StepArgs& a,
+                                          uint32_t i, uint32_t j8, const float* S, float inv) {
+  if (j8 >= c.n) return;
+  const uint4 ph = philox4x32_10(make_uint4(j8 >> 3, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
   const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
-  const int64_t e0 = i * L.n + j8;
+  const uint32_t e0 = i * c.n + j8;
   float U[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) U[t] = mul_rn(L.alpha, S[t]);
 
-  if (L.n % 8 == 0) {
-    const float inv = recip_or_zero(gload(L.Ws + (e0 >> 8)));
-    const uint2 wv = gload(reinterpret_cast<const uint2*>(L.Wq + e0));
+  if (c.vec) {
+    const uint2 wv = bload64(c.rw, e0);
     const uint32_t win[2] = {wv.x, wv.y};
     uint32_t wout[2] = {0, 0};
 #pragma unroll
@@ -193,24 +202,26 @@ __device__ __forceinline__ void sr_block8(const LayerDev& L, const StepArgs& a, 
       const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
       wout[t >> 2] |= (uint32_t)(nw & 0xFF) << (8 * (t & 3));
     }
-    gstore(reinterpret_cast<uint2*>(L.Wq + e0), make_uint2(wout[0], wout[1]));
-    if (L.U_out) {
-      gstore(reinterpret_cast<float4*>(L.U_out + e0), make_float4(U[0], U[1], U[2], U[3]));
-      gstore(reinterpret_cast<float4*>(L.U_out + e0 + 4), make_float4(U[4], U[5], U[6], U[7]));
+    bstore64(c.rw, e0, make_uint2(wout[0], wout[1]));
+    if (c.write_u) {
+      bstore128(c.ru, e0 * 4, make_uint4(__float_as_uint(U[0]), __float_as_uint(U[1]),
+                                         __float_as_uint(U[2]), __float_as_uint(U[3])));
+      bstore128(c.ru, e0 * 4 + 16, make_uint4(__float_as_uint(U[4]), __float_as_uint(U[5]),
+                                              __float_as_uint(U[6]), __float_as_uint(U[7])));
     }
   } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (j8 + t >= L.n) continue;
-      const int64_t e = e0 + t;
-      const float inv = recip_or_zero(gload(L.Ws + (e >> 8)));
-      const int w = gload(L.Wq + e);
-      const float tp = add_rn((float)w, mul_rn(U[t], inv));
+      const bool in = j8 + t < c.n;
+      const uint32_t e = e0 + t;
+      const float iv = recip_or_zero(bloadf(c.rws, in ? (e >> 8) * 4 : kOOB));
+      const int w = (int)(int8_t)bload8(c.rw, in ? e : kOOB);
+      const float tp = add_rn((float)w, mul_rn(U[t], iv));
       const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
       const float d = add_rn(tp, (float)bits * (1.0f / 65536.0f));
       const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
-      gstore(L.Wq + e, (int8_t)nw);
-      if (L.U_out) gstore(L.U_out + e, U[t]);
+      bstore8(c.rw, in ? e : kOOB, (uint32_t)nw);
+      if (c.write_u) bstoref(c.ru, in ? e * 4 : kOOB, U[t]);
     }
   }
 }
@@ -239,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
 
   // A = P~ (rows i of P, K = rank index contiguous), B = N~ stored [k][j] (r x n).
   StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
-  StageBf16K<T::BN, T::BK> sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.n,
-                              j0);
+  StageBf16K<T::BN, T::BK> sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.r,
+                              L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
@@ -254,6 +265,17 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
   const int wm = wave_m<T>(), wn = wave_n<T>();
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
   const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
+  SrCtx c;
+  c.n = (uint32_t)L.n;
+  c.m = (uint32_t)L.m;
+  c.vec = (L.n % 8 == 0);
+  c.write_u = (L.U_out != nullptr);
+  const uint32_t numel = (uint32_t)(L.m * L.n);
+  c.rw = make_rsrc(L.Wq, numel);
+  c.rws = make_rsrc(L.Ws, ((numel + kGroup - 1) / kGroup) * 4);
+  c.ru = make_rsrc(L.U_out, c.write_u ? numel * 4 : 0);
+  // a lane's WTN/2 columns lie in one weight scale group when rows are whole groups
+  const bool one_group = (L.n % kGroup == 0);
 #pragma unroll
   for (int x = 0; x < T::XM; ++x) {
 #pragma unroll
@@ -262,15 +284,22 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
       for (int v = 0; v < 16; ++v)
         E[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + 32 * y + (lane & 31)] = acc[x][y][v];
     __syncthreads();
-    const int64_t i = (int64_t)i0 + wm * T::WTM + 32 * x + rr;
-    const int64_t jb = (int64_t)j0 + wn * T::WTN + cc;
-    if (i < L.m) {
+    const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
+    const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
+    if (i < c.m) {
+      const float inv_row =
+          one_group ? recip_or_zero(bloadf(c.rws, ((i * c.n + jb) >> 8) * 4)) : 0.0f;
 #pragma unroll
       for (int q = 0; q < T::WTN / 16; ++q) {
         const float4 f0 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q);
         const float4 f1 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q + 4);
         const float S[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        sr_block8(L, a, i, jb + 8 * q, S);
+        const uint32_t j8 = jb + 8 * q;
+        const float inv =
+            one_group ? inv_row
+                      : (c.vec && j8 < c.n ? recip_or_zero(bloadf(c.rws, ((i * c.n + j8) >> 8) * 4))
+                                           : 0.0f);
+        sr_block8(c, L, a, i, j8, S, inv);
       }
     }
     __syncthreads();

@@ -41,9 +41,14 @@ qg_status device_present() {
   return cached ? QG_OK : QG_ERR_NO_DEVICE;
 }
 
+// Kernels address every tensor of a layer through 32-bit buffer offsets: the fp32 ones
+// (R: r x n, U: m x n) must stay below 2 GiB, hence m*n and r*n below 2^29 elements.
+constexpr int64_t kMaxElems = int64_t(1) << 29;
+
 qg_status check_shape(int64_t m, int64_t n, int64_t r) {
   if (m < 1 || n < 1 || r < 1 || m > kMaxDim || n > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
   if (r > m || r % 8 != 0) return QG_ERR_SHAPE;
+  if (m * n > kMaxElems || r * n > kMaxElems) return QG_ERR_SHAPE;
   if (cdiv(m, kTile) * cdiv(n, kTile) > kMaxDim / 2) return QG_ERR_SHAPE;
   return QG_OK;
 }
