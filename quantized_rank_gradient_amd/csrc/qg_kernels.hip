@@ -169,61 +169,105 @@ __global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
 // ===================================================== back-projection + rounding ===
 
 // Stochastic rounding of 8 consecutive weights (i, j8 .. j8+7), j8 a multiple of 8: one
-// Philox call yields the 8 16-bit uniforms of the column block. `inv` is the reciprocal of the
-// block's weight group scale when the caller knows the 8 weights share one group (rows of
-// 8-multiple length); otherwise it is negative and the scale is looked up per element.
+// Philox call yields the 8 16-bit uniforms of the column block.
 struct SrCtx {
   rsrc_t rw, rws, ru;
   uint32_t n, m;
-  bool vec;          // n % 8 == 0: 8-byte weight accesses
+  bool vec;          // n % 8 == 0: 8-byte weight accesses (prefetched by the caller)
   bool write_u;
 };
 
-__device__ __forceinline__ void sr_block8(const SrCtx& c, const LayerDev& L, const StepArgs& a,
-                                          uint32_t i, uint32_t j8, const float* S, float inv) {
+// New INT8 code of one weight: d = (w + U * inv) + u with one rounding per operation. u is a
+// multiple of 2^-16 below 1, so fma(bits, 2^-16, t) is exactly the rounded sum t + u.
+__device__ __forceinline__ float sr_pre(int w, float U, float inv, uint32_t bits) {
+  const float tp = add_rn((float)w, mul_rn(U, inv));
+  return __builtin_fmaf((float)bits, 1.0f / 65536.0f, tp);
+}
+__device__ __forceinline__ int sr_code(float d) {
+  return (int)fminf(fmaxf(floorf(d), -127.f), 127.f);
+}
+
+// Vector path: the 8 weights arrive prefetched in `wv` and share the scale reciprocal `inv`.
+__device__ __forceinline__ void sr_block8_vec(const SrCtx& c, const LayerDev& L,
+                                              const StepArgs& a, uint32_t i, uint32_t j8,
+                                              const float* S, float inv, uint2 wv) {
   if (j8 >= c.n) return;
   const uint4 ph = philox4x32_10(make_uint4(j8 >> 3, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
   const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
   const uint32_t e0 = i * c.n + j8;
-  float U[8];
+  const uint32_t win[2] = {wv.x, wv.y};
+  float U[8], d[8];
+  int w[8];
+  float sum = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) U[t] = mul_rn(L.alpha, S[t]);
-
-  if (c.vec) {
-    const uint2 wv = bload64(c.rw, e0);
-    const uint32_t win[2] = {wv.x, wv.y};
-    uint32_t wout[2] = {0, 0};
+  for (int t = 0; t < 8; ++t) {
+    U[t] = mul_rn(L.alpha, S[t]);
+    w[t] = (int)(int8_t)(win[t >> 2] >> (8 * (t & 3)));
+    const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
+    d[t] = sr_pre(w[t], U[t], inv, bits);
+    sum += d[t];   // finite exactly when all eight are (|d| stays below 2^8 when finite)
+  }
+  uint32_t wout[2] = {0, 0};
+  if (__builtin_isfinite(sum)) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int w = (int)(int8_t)(win[t >> 2] >> (8 * (t & 3)));
-      const float tp = add_rn((float)w, mul_rn(U[t], inv));
-      const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
-      const float d = add_rn(tp, (float)bits * (1.0f / 65536.0f));
-      const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
-      wout[t >> 2] |= (uint32_t)(nw & 0xFF) << (8 * (t & 3));
-    }
-    bstore64(c.rw, e0, make_uint2(wout[0], wout[1]));
-    if (c.write_u) {
-      bstore128(c.ru, e0 * 4, make_uint4(__float_as_uint(U[0]), __float_as_uint(U[1]),
-                                         __float_as_uint(U[2]), __float_as_uint(U[3])));
-      bstore128(c.ru, e0 * 4 + 16, make_uint4(__float_as_uint(U[4]), __float_as_uint(U[5]),
-                                              __float_as_uint(U[6]), __float_as_uint(U[7])));
-    }
+    for (int t = 0; t < 8; ++t) wout[t >> 2] |= (uint32_t)(sr_code(d[t]) & 0xFF) << (8 * (t & 3));
   } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const bool in = j8 + t < c.n;
-      const uint32_t e = e0 + t;
-      const float iv = recip_or_zero(bloadf(c.rws, in ? (e >> 8) * 4 : kOOB));
-      const int w = (int)(int8_t)bload8(c.rw, in ? e : kOOB);
-      const float tp = add_rn((float)w, mul_rn(U[t], iv));
-      const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
-      const float d = add_rn(tp, (float)bits * (1.0f / 65536.0f));
-      const int nw = __builtin_isfinite(d) ? (int)fminf(fmaxf(floorf(d), -127.f), 127.f) : w;
-      bstore8(c.rw, in ? e : kOOB, (uint32_t)nw);
-      if (c.write_u) bstoref(c.ru, in ? e * 4 : kOOB, U[t]);
+      const int nw = __builtin_isfinite(d[t]) ? sr_code(d[t]) : w[t];
+      wout[t >> 2] |= (uint32_t)(nw & 0xFF) << (8 * (t & 3));
     }
   }
+  bstore64(c.rw, e0, make_uint2(wout[0], wout[1]));
+  if (c.write_u) {
+    bstore128(c.ru, e0 * 4, make_uint4(__float_as_uint(U[0]), __float_as_uint(U[1]),
+                                       __float_as_uint(U[2]), __float_as_uint(U[3])));
+    bstore128(c.ru, e0 * 4 + 16, make_uint4(__float_as_uint(U[4]), __float_as_uint(U[5]),
+                                            __float_as_uint(U[6]), __float_as_uint(U[7])));
+  }
+}
+
+// Element path for rows whose length is not a multiple of 8 (unaligned, possibly straddling
+// scale groups): byte accesses and a scale lookup per element.
+__device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L,
+                                               const StepArgs& a, uint32_t i, uint32_t j8,
+                                               const float* S) {
+  if (j8 >= c.n) return;
+  const uint4 ph = philox4x32_10(make_uint4(j8 >> 3, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
+  const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
+  const uint32_t e0 = i * c.n + j8;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bool in = j8 + t < c.n;
+    const uint32_t e = e0 + t;
+    const float U = mul_rn(L.alpha, S[t]);
+    const float iv = recip_or_zero(bloadf(c.rws, in ? (e >> 8) * 4 : kOOB));
+    const int w = (int)(int8_t)bload8(c.rw, in ? e : kOOB);
+    const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
+    const float d = sr_pre(w, U, iv, bits);
+    const int nw = __builtin_isfinite(d) ? sr_code(d) : w;
+    bstore8(c.rw, in ? e : kOOB, (uint32_t)nw);
+    if (c.write_u) bstoref(c.ru, in ? e * 4 : kOOB, U);
+  }
+}
+
+// Write one 32-row chunk of a wave's accumulators (MFMA layout) to its LDS staging block.
+template <class T, int EP>
+__device__ __forceinline__ void stage_rows(float* E, const f32x16 (&accx)[T::XN]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      E[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + 32 * y + (lane & 31)] = accx[y][v];
+  __syncthreads();
+}
+
+__device__ __forceinline__ void read_run(const float* E, int off, float (&S)[8]) {
+  const float4 f0 = *reinterpret_cast<const float4*>(E + off);
+  const float4 f1 = *reinterpret_cast<const float4*>(E + off + 4);
+  S[0] = f0.x; S[1] = f0.y; S[2] = f0.z; S[3] = f0.w;
+  S[4] = f1.x; S[5] = f1.y; S[6] = f1.z; S[7] = f1.w;
 }
 
 // P~ rows are K-contiguous ([i][k]); N~ is K-major ([k][j]).
@@ -241,12 +285,49 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
   constexpr int EP = T::WTN + 4;   // fp32 row pitch of the redistribution block
   constexpr int LDS_BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
                                 ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
+  constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
   const int ti = local / L.b_tiles_j;
   const int tj = local - ti * L.b_tiles_j;
   const int i0 = ti * T::BM, j0 = tj * T::BN;
+
+  // After the product, each wave's block goes through LDS 32 rows at a time so that every
+  // lane owns WTN/2 consecutive columns of one row: whole Philox blocks and wide W accesses.
+  // The weights and scale reciprocals that lane will need do not depend on the product, so
+  // their loads are issued first and arrive while the MFMAs run.
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave_m<T>(), wn = wave_n<T>();
+  const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
+  SrCtx c;
+  c.n = (uint32_t)L.n;
+  c.m = (uint32_t)L.m;
+  c.vec = (L.n % 8 == 0);
+  c.write_u = (L.U_out != nullptr);
+  const uint32_t numel = (uint32_t)(L.m * L.n);
+  c.rw = make_rsrc(L.Wq, numel);
+  c.rws = make_rsrc(L.Ws, ((numel + kGroup - 1) / kGroup) * 4);
+  c.ru = make_rsrc(L.U_out, c.write_u ? numel * 4 : 0);
+  const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
+  // a lane's WTN/2 columns lie in one weight scale group when rows are whole groups
+  const bool one_group = (L.n % kGroup == 0);
+  uint2 wpre[T::XM][NQ];
+  float spre[T::XM];   // the scale of the lane's run when rows are whole groups
+  if (c.vec) {
+#pragma unroll
+    for (int x = 0; x < T::XM; ++x) {
+      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint32_t j8 = jb + 8 * q;
+        const bool in = i < c.m && j8 < c.n;
+        wpre[x][q] = bload64(c.rw, in ? i * c.n + j8 : kOOB);
+      }
+      spre[x] = bloadf(c.rws, (one_group && i < c.m && jb < c.n) ? ((i * c.n + jb) >> 8) * 4 : kOOB);
+    }
+  }
 
   // A = P~ (rows i of P, K = rank index contiguous), B = N~ stored [k][j] (r x n).
   StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
@@ -258,51 +339,41 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
       [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, L.r, lds,
       acc);
 
-  // Redistribute each wave's block through LDS, 32 rows at a time, so that every lane owns
-  // WTN/2 consecutive columns of one row: whole Philox blocks and wide W accesses.
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave_m<T>(), wn = wave_n<T>();
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
-  const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
-  SrCtx c;
-  c.n = (uint32_t)L.n;
-  c.m = (uint32_t)L.m;
-  c.vec = (L.n % 8 == 0);
-  c.write_u = (L.U_out != nullptr);
-  const uint32_t numel = (uint32_t)(L.m * L.n);
-  c.rw = make_rsrc(L.Wq, numel);
-  c.rws = make_rsrc(L.Ws, ((numel + kGroup - 1) / kGroup) * 4);
-  c.ru = make_rsrc(L.U_out, c.write_u ? numel * 4 : 0);
-  // a lane's WTN/2 columns lie in one weight scale group when rows are whole groups
-  const bool one_group = (L.n % kGroup == 0);
-#pragma unroll
-  for (int x = 0; x < T::XM; ++x) {
-#pragma unroll
-    for (int y = 0; y < T::XN; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        E[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + 32 * y + (lane & 31)] = acc[x][y][v];
-    __syncthreads();
-    const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
-    const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
-    if (i < c.m) {
-      const float inv_row =
-          one_group ? recip_or_zero(bloadf(c.rws, ((i * c.n + jb) >> 8) * 4)) : 0.0f;
-#pragma unroll
-      for (int q = 0; q < T::WTN / 16; ++q) {
-        const float4 f0 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q);
-        const float4 f1 = *reinterpret_cast<const float4*>(E + rr * EP + cc + 8 * q + 4);
-        const float S[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        const uint32_t j8 = jb + 8 * q;
-        const float inv =
-            one_group ? inv_row
-                      : (c.vec && j8 < c.n ? recip_or_zero(bloadf(c.rws, ((i * c.n + j8) >> 8) * 4))
-                                           : 0.0f);
-        sr_block8(c, L, a, i, j8, S, inv);
+  if (c.vec) {
+#pragma clang loop unroll(full)
+    for (int x = 0; x < T::XM; ++x) {
+      stage_rows<T, EP>(E, acc[x]);
+      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
+      if (i < c.m) {
+        const float inv0 = recip_or_zero(spre[x]);
+#pragma clang loop unroll(full)
+        for (int q = 0; q < NQ; ++q) {
+          float S[8];
+          read_run(E, rr * EP + cc + 8 * q, S);
+          const uint32_t j8 = jb + 8 * q;
+          const float inv =
+              one_group ? inv0
+                        : recip_or_zero(bloadf(c.rws, j8 < c.n ? ((i * c.n + j8) >> 8) * 4 : kOOB));
+          sr_block8_vec(c, L, a, i, j8, S, inv, wpre[x][q]);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
+  } else {
+#pragma clang loop unroll(full)
+    for (int x = 0; x < T::XM; ++x) {
+      stage_rows<T, EP>(E, acc[x]);
+      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
+      if (i < c.m) {
+        for (int q = 0; q < NQ; ++q) {
+          float S[8];
+          read_run(E, rr * EP + cc + 8 * q, S);
+          sr_block8_elem(c, L, a, i, jb + 8 * q, S);
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
