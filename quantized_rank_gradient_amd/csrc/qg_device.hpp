@@ -23,6 +23,7 @@ struct LayerDev {
   float* Vs;
   int64_t off_r;       // workspace byte offset: split x rpitch fp32 partial sums of R
   int64_t off_n;       // workspace byte offset: bf16 r x n update N~
+  int64_t off_p;       // workspace byte offset: bf16 m x r dequantized projection P~
   float* R_out;        // optional
   float* U_out;        // optional
   int64_t m, n, r;

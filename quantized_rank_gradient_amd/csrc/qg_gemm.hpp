@@ -36,10 +36,11 @@ struct Tile {
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave sub-tile
   static constexpr int XM = WTM / 32, XN = WTN / 32;   // MFMA blocks per wave
   static_assert(XM * 32 == WTM && XN * 32 == WTN, "wave tile is a multiple of 32");
-  // LDS pitches (bf16 elements): K-major tiles are BK rows of (edge + 16); K-contiguous tiles
-  // are edge rows of (BK + 8). Both keep 16-byte rows and spread rows over the banks.
-  static constexpr int A_PITCH = A_KMAJOR ? BM + 16 : BK + 8;
-  static constexpr int B_PITCH = B_KMAJOR ? BN + 16 : BK + 8;
+  // LDS pitches (bf16 elements): K-major tiles are BK rows of (edge + 32), so consecutive rows
+  // start 16 banks apart and the 4-row x 32-byte footprint of a 16-lane transpose read covers
+  // all 64 banks once; K-contiguous tiles are edge rows of (BK + 8).
+  static constexpr int A_PITCH = A_KMAJOR ? BM + 32 : BK + 8;
+  static constexpr int B_PITCH = B_KMAJOR ? BN + 32 : BK + 8;
   static constexpr int A_ELEMS = A_KMAJOR ? BK * A_PITCH : BM * A_PITCH;
   static constexpr int B_ELEMS = B_KMAJOR ? BK * B_PITCH : BN * B_PITCH;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;      // one [A | B] stage, bf16 elements
@@ -127,22 +128,27 @@ struct StageInt4K {
   static constexpr int CPR = W / 8;
   static constexpr int NC = BK * CPR / kThreads;
   static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
-  rsrc_t rq, rsc;
+  rsrc_t rq, rsc, rout;
   uint32_t ld, k_end, c_end;
   int c0;
+  bool emit;          // also write the bf16 tile to `out` (same [k][c] layout as the source)
+  uint32_t kcur;
   uint32_t w[NC];
   float s[NC];
 
   __device__ StageInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
-                        int64_t k_end_, int64_t c_end_, int c0_)
+                        int64_t k_end_, int64_t c_end_, int c0_, uint16_t* out = nullptr)
       : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
     const int64_t numel = rows * ld_;
     rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
     rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
+    emit = out != nullptr;
+    rout = make_rsrc(out, emit ? (uint32_t)(numel * 2) : 0u);
   }
 
   __device__ __forceinline__ void load(int64_t k0_) {
     const uint32_t k0 = (uint32_t)k0_;
+    kcur = k0;
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
@@ -160,7 +166,51 @@ struct StageInt4K {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
+      const uint4 v = dequant8(w[u], s[u]);
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v;
+      if (emit) {
+        const uint32_t k = kcur + q / CPR;
+        const uint32_t c = c0 + 8 * (q % CPR);
+        bstore128(rout, (k < k_end && c < c_end) ? (k * ld + c) * 2 : kOOB, v);
+      }
+    }
+  }
+};
+
+// bf16 source [c][k] (row pitch ld = the K extent, ld % 8 == 0, c_end rows) -> K-contiguous
+// LDS tile [c][k].
+template <int W, int BK>
+struct StageBf16C {
+  static constexpr int CPR = BK / 8;
+  static constexpr int NC = W * CPR / kThreads;
+  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
+  rsrc_t rs;
+  uint32_t ld, c_end;
+  int c0;
+  uint4 v[NC];
+
+  __device__ StageBf16C(const uint16_t* s, int64_t ld_, int64_t c_end_, int c0_)
+      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
+    rs = make_rsrc(s, (uint32_t)(c_end_ * ld_ * 2));
+  }
+
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const uint32_t row = c0 + q / CPR;
+      const uint32_t k = k0 + 8 * (q % CPR);
+      v[u] = bload128(rs, (row < c_end && k < ld) ? (row * ld + k) * 2 : kOOB);
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v[u];
     }
   }
 };

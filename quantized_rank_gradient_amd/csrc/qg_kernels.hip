@@ -40,7 +40,10 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
   // A = P~^T: P is stored [k][i] (m x r), so the tile rows i are columns of P.
-  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, k_end, L.r, i0);
+  // The workgroups of the first column tile also write the dequantized P~ they stage, in P's
+  // own layout, for the back-projection to read as bf16.
+  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, k_end, L.r, i0,
+                              tj == 0 ? reinterpret_cast<uint16_t*>(a.ws + L.off_p) : nullptr);
   StageBf16K<T::BN, T::BK> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
@@ -282,7 +285,7 @@ static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true)
 
 template <class T>
 __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
-  constexpr int EP = T::WTN + 4;   // fp32 row pitch of the redistribution block
+  constexpr int EP = T::WTN + 8;   // fp32 row pitch of the redistribution block
   constexpr int LDS_BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
                                 ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
   constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk
@@ -329,8 +332,9 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
     }
   }
 
-  // A = P~ (rows i of P, K = rank index contiguous), B = N~ stored [k][j] (r x n).
-  StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
+  // A = P~ (rows i, K = rank index contiguous: the bf16 copy the projection kernel wrote),
+  // B = N~ stored [k][j] (r x n).
+  StageBf16C<T::BM, T::BK> sa(reinterpret_cast<const uint16_t*>(a.ws + L.off_p), L.r, L.m, i0);
   StageBf16K<T::BN, T::BK> sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.r,
                               L.n, j0);
   f32x16 acc[T::XM][T::XN];

@@ -73,15 +73,19 @@ int choose_split(int64_t m, int64_t n, int64_t r) {
 }
 int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kK), split) * kK; }
 
+// Per-layer workspace: split-K partial sums of R (fp32), the bf16 update N~ (r x n) and the
+// bf16 dequantized projection P~ (m x r) that the projection kernel leaves for the
+// back-projection.
 struct WsLayout {
-  int64_t rpitch, off_r, off_n, bytes;
+  int64_t rpitch, off_r, off_n, off_p, bytes;
 };
-WsLayout ws_layout(int64_t n, int64_t r, int split, int64_t base) {
+WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base) {
   WsLayout w;
   w.rpitch = round_up(r * n, 64);
   w.off_r = base;
   w.off_n = base + round_up((int64_t)split * w.rpitch * 4, 256);
-  w.bytes = (w.off_n - base) + round_up(r * n * 2, 256);
+  w.off_p = w.off_n + round_up(r * n * 2, 256);
+  w.bytes = (w.off_p - base) + round_up(m * r * 2, 256);
   return w;
 }
 
@@ -148,10 +152,11 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.m = d->m;
   L.n = d->n;
   L.r = d->r;
-  const WsLayout w = ws_layout(d->n, d->r, split, ws_base);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base);
   L.rpitch = w.rpitch;
   L.off_r = w.off_r;
   L.off_n = w.off_n;
+  L.off_p = w.off_p;
   L.layer_id = d->layer_id;
   L.split = split;
   L.kslab = (int32_t)kslab_for(d->m, split);
@@ -185,7 +190,7 @@ qg_status launch_step(const StepArgs& a, const int grid[3], bool big, hipStream_
 
 extern "C" size_t qgalore_workspace_bytes(int64_t m, int64_t n, int64_t r) {
   if (check_shape(m, n, r) != QG_OK) return 0;
-  return (size_t)ws_layout(n, r, choose_split(m, n, r), 0).bytes;
+  return (size_t)ws_layout(m, n, r, choose_split(m, n, r), 0).bytes;
 }
 
 extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q,
@@ -195,7 +200,7 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   if (st != QG_OK) return st;
   if ((st = check_step(step)) != QG_OK) return st;
   const int split = choose_split(d->m, d->n, d->r);
-  const WsLayout w = ws_layout(d->n, d->r, split, 0);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0);
   if (!d->workspace) return QG_ERR_NULL;
   if (!aligned(d->workspace, 16)) return QG_ERR_ALIGN;
   if (d->workspace_bytes < (size_t)w.bytes) return QG_ERR_WORKSPACE;
@@ -282,7 +287,7 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
     const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
     LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
                             split, ws, big);
-    ws += ws_layout(x.desc.n, x.desc.r, split, ws).bytes;
+    ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws).bytes;
     const int g[3] = {grid_project(L), grid_adam(L), grid_back(L)};
     for (int k = 0; k < 3; ++k) {
       if (base[k] + g[k] > kMaxDim) {
