@@ -148,27 +148,31 @@ class Variant:
         return out
 
 
+KERNELS = ("qg_dequant", "qg_project", "qg_adam", "qg_backproject")
+
+
 def algorithmic(cfg, r):
-    """FLOPs and bytes the method must do per step (per kernel), from the layer shapes."""
+    """FLOPs and bytes the method must do per step, split by the kernel that does them (in
+    launch order: INT4 dequant of P, projection, Adam, back-projection + rounding). Bytes
+    count each algorithmic input once and each output once: P (INT4 + fp32 scale per 256)
+    once, G once, M and V (INT8 + scales) read and written, W (INT8) read and written with
+    its scales read. Workspace round trips (R partials, N~, the bf16 copy of P~) are not
+    algorithmic and are not counted."""
     mn = sum(L.m * L.n for L in cfg.layers)
     mr = sum(L.m * r for L in cfg.layers)
     rn = sum(r * L.n for L in cfg.layers)
-    flops_proj = 2.0 * r * mn
-    flops_back = 2.0 * r * mn
-    # projection: G (bf16) + P (INT4 + fp32 scale per 256)
-    bytes_proj = 2.0 * mn + 0.5 * mr + mr / 64.0
-    # Adam: M, V read + write (int8) and their scales read + write
-    bytes_adam = 4.0 * rn + 4.0 * 4.0 * rn / 256.0
-    # back-projection + rounding: W read + write (int8), W scales, P again
-    bytes_back = 2.0 * mn + mn / 64.0 + 0.5 * mr + mr / 64.0
-    return dict(mn=mn, flops=(flops_proj, 0.0, flops_back),
-                bytes=(bytes_proj, bytes_adam, bytes_back))
+    flops = (0.0, 2.0 * r * mn, 0.0, 2.0 * r * mn)
+    nbytes = (0.5 * mr + mr / 64.0,                 # P codes + scales
+              2.0 * mn,                               # G (bf16)
+              4.0 * rn + 4.0 * 4.0 * rn / 256.0,      # M, V in and out + their scales
+              2.0 * mn + mn / 64.0)                   # W in and out + W scales
+    return dict(mn=mn, flops=flops, bytes=nbytes)
 
 
 def roofline(cfg, r, kms):
     a = algorithmic(cfg, r)
-    names = ("qg_project", "qg_adam", "qg_backproject")
-    k = max(range(3), key=lambda i: kms[i])            # dominant kernel
+    names = KERNELS
+    k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
     intensity = a["flops"][k] / a["bytes"][k] if a["bytes"][k] else 0.0
     mfma_bound = intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -267,8 +271,7 @@ def main():
         res = dict(config=vcfg.key, rank=r, ms_per_step=round(ms, 4),
                    value=a["mn"] / (ms / 1e3),
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
-                   kernel_ms=dict(qg_project=round(kms[0], 4), qg_adam=round(kms[1], 4),
-                                  qg_backproject=round(kms[2], 4)),
+                   kernel_ms={nm: round(t, 4) for nm, t in zip(KERNELS, kms)},
                    optimizer_ms=round(sum(kms), 4),
                    refresh_tests_per_step=round(tests, 2),
                    cossim_ms=cs_ms,

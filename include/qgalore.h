@@ -126,14 +126,15 @@ qg_status qgalore_plan_step(qg_plan *plan, int64_t step, uint64_t seed, void *wo
 qg_status qgalore_plan_destroy(qg_plan *plan);
 
 /* Per-kernel timing of a plan (benchmark instrumentation). After
- * qgalore_plan_enable_timing(plan, max_steps) each qgalore_plan_step records hipEvents before
- * and after each of its three launches (projection, Adam, back-projection), for up to
- * max_steps steps; the events are created here and owned by the plan (max_steps = 0 frees
- * them and disables timing). qgalore_plan_kernel_times waits for the recorded events, writes
- * each kernel's mean duration over the recorded steps to out_ms[0..2] (milliseconds) and the
- * number of steps to *steps, then clears the record. */
+ * qgalore_plan_enable_timing(plan, max_steps) each qgalore_plan_step records hipEvents around
+ * each of its four launches, for up to max_steps steps; the events are created here and owned
+ * by the plan (max_steps = 0 frees them and disables timing). qgalore_plan_kernel_times waits
+ * for the recorded events, writes each kernel's mean duration over the recorded steps to
+ * out_ms[0..3] (milliseconds, in launch order: INT4 dequant of P, projection, Adam,
+ * back-projection with the rounding) and the number of steps to *steps, then clears the
+ * record. */
 qg_status qgalore_plan_enable_timing(qg_plan *plan, int32_t max_steps);
-qg_status qgalore_plan_kernel_times(qg_plan *plan, float out_ms[3], int32_t *steps);
+qg_status qgalore_plan_kernel_times(qg_plan *plan, float out_ms[4], int32_t *steps);
 
 /* ------------------------------------------------------------------------------------
  * Subspace similarity (AIMech Q-GaLore page, mechanism claim "layer-adaptive subspace

@@ -242,9 +242,9 @@ class Plan:
                "qgalore_plan_enable_timing")
 
     def kernel_times(self):
-        """Mean (projection, Adam, back-projection) kernel milliseconds over the recorded
-        steps, and the number of steps recorded."""
-        out = (c_float * 3)()
+        """Mean (dequant, projection, Adam, back-projection) kernel milliseconds over the
+        recorded steps, and the number of steps recorded."""
+        out = (c_float * 4)()
         steps = c_int32(0)
         _check(lib().qgalore_plan_kernel_times(self._h, out, ctypes.byref(steps)),
                "qgalore_plan_kernel_times")

@@ -24,6 +24,7 @@ struct LayerDev {
   int64_t off_r;       // workspace byte offset: split x rpitch fp32 partial sums of R
   int64_t off_n;       // workspace byte offset: bf16 r x n update N~
   int64_t off_p;       // workspace byte offset: bf16 m x r dequantized projection P~
+                       // (written at the start of every step, read by both MFMA kernels)
   float* R_out;        // optional
   float* U_out;        // optional
   int64_t m, n, r;
@@ -35,8 +36,8 @@ struct LayerDev {
   int32_t p_tiles_j;   // projection tiles along n
   int32_t b_tiles_i;   // back-projection tiles along m
   int32_t b_tiles_j;   // back-projection tiles along n
-  int32_t wg_base[3];  // first workgroup of this layer in the projection / Adam /
-                       // back-projection launch of a grouped step
+  int32_t wg_base[4];  // first workgroup of this layer in the projection / Adam /
+                       // back-projection / dequant launch of a grouped step
   float lr, eps, alpha;
 };
 
@@ -49,7 +50,7 @@ struct StepArgs {
   uint32_t step, seed_lo, seed_hi;
 };
 
-enum { KPROJ = 0, KADAM = 1, KBACK = 2 };
+enum { KPROJ = 0, KADAM = 1, KBACK = 2, KDEQ = 3 };
 
 // `logical` is the workgroup's position in the launch after any renumbering.
 __device__ __forceinline__ LayerDev fetch_layer(const StepArgs& a, int kernel, int logical,

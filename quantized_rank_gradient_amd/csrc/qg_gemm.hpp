@@ -128,27 +128,22 @@ struct StageInt4K {
   static constexpr int CPR = W / 8;
   static constexpr int NC = BK * CPR / kThreads;
   static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
-  rsrc_t rq, rsc, rout;
+  rsrc_t rq, rsc;
   uint32_t ld, k_end, c_end;
   int c0;
-  bool emit;          // also write the bf16 tile to `out` (same [k][c] layout as the source)
-  uint32_t kcur;
   uint32_t w[NC];
   float s[NC];
 
   __device__ StageInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
-                        int64_t k_end_, int64_t c_end_, int c0_, uint16_t* out = nullptr)
+                        int64_t k_end_, int64_t c_end_, int c0_)
       : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
     const int64_t numel = rows * ld_;
     rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
     rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
-    emit = out != nullptr;
-    rout = make_rsrc(out, emit ? (uint32_t)(numel * 2) : 0u);
   }
 
   __device__ __forceinline__ void load(int64_t k0_) {
     const uint32_t k0 = (uint32_t)k0_;
-    kcur = k0;
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
@@ -166,13 +161,7 @@ struct StageInt4K {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      const uint4 v = dequant8(w[u], s[u]);
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v;
-      if (emit) {
-        const uint32_t k = kcur + q / CPR;
-        const uint32_t c = c0 + 8 * (q % CPR);
-        bstore128(rout, (k < k_end && c < c_end) ? (k * ld + c) * 2 : kOOB, v);
-      }
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
     }
   }
 };
@@ -354,6 +343,8 @@ __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, Store
   for (int kt = 0; kt + 1 < nk; ++kt) {
     sa.load(k_begin + (int64_t)(kt + 1) * T::BK);
     sb.load(k_begin + (int64_t)(kt + 1) * T::BK);
+    // keep the next stage's global loads ahead of this stage's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     mfma_stage<T, PARTS>(lds + (kt & 1) * STAGE, acc);
     store_a(sa, lds + ((kt + 1) & 1) * STAGE);
     store_b(sb, lds + ((kt + 1) & 1) * STAGE);

@@ -16,6 +16,25 @@
 
 namespace qg {
 
+// ===================================================================== INT4 dequant ===
+// P~ = bf16(q * s) for the whole m x r projection, once per step, into the workspace: the
+// projection and the back-projection both stage P~ from it (the INT4 store is what persists;
+// this copy lives only for the step). 256 threads x 8 codes per workgroup.
+
+__global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
+  int local;
+  const LayerDev L = fetch_layer(a, KDEQ, blockIdx.x, local);
+  const uint32_t numel = (uint32_t)(L.m * L.r);
+  const uint32_t e = ((uint32_t)local * kThreads + threadIdx.x) * 8;
+  const bool in = e < numel;
+  const rsrc_t rq = make_rsrc(L.Pq, (numel + 1) / 2);
+  const rsrc_t rs = make_rsrc(L.Ps, ((numel + kGroup - 1) / kGroup) * 4);
+  const rsrc_t ro = make_rsrc(a.ws + L.off_p, numel * 2);
+  const uint32_t w = bload32(rq, in ? e >> 1 : kOOB);
+  const float sc = bloadf(rs, in ? (e >> 8) * 4 : kOOB);
+  bstore128(ro, in ? e * 2 : kOOB, dequant8(w, sc));
+}
+
 // ======================================================================== projection ===
 
 // Tile shapes: rank above 128 takes 256 x 256 tiles with K stages of 64 (each wave a 128 x 128
@@ -39,11 +58,9 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
   const int64_t k_begin = (int64_t)s * L.kslab;
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
-  // A = P~^T: P is stored [k][i] (m x r), so the tile rows i are columns of P.
-  // The workgroups of the first column tile also write the dequantized P~ they stage, in P's
-  // own layout, for the back-projection to read as bf16.
-  StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, k_end, L.r, i0,
-                              tj == 0 ? reinterpret_cast<uint16_t*>(a.ws + L.off_p) : nullptr);
+  // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
+  StageBf16K<T::BM, T::BK> sa(reinterpret_cast<const uint16_t*>(a.ws + L.off_p), L.r, L.m,
+                              k_end, L.r, i0);
   StageBf16K<T::BN, T::BK> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
@@ -419,6 +436,10 @@ hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s) 
     hipLaunchKernelGGL(qg_project<ProjBig>, dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(qg_project<ProjSmall>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(qg_dequant, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s) {

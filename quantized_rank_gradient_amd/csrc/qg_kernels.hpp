@@ -38,6 +38,7 @@ constexpr int kBackTileM(bool big) { return big ? 256 : 128; }
 constexpr int kBackTileN(bool big) { return big ? 128 : 128; }
 
 hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s);
+hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s);
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,

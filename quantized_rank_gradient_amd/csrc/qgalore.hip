@@ -173,9 +173,12 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
 int grid_project(const LayerDev& L) { return L.split * L.p_tiles_i * L.p_tiles_j; }
 int grid_adam(const LayerDev& L) { return (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4); }
 int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
+int grid_dequant(const LayerDev& L) { return (int)cdiv(L.m * L.r, qg::kThreads * 8); }
 
-qg_status launch_step(const StepArgs& a, const int grid[3], bool big, hipStream_t s) {
-  hipError_t e = qg::launch_project(a, grid[0], big, s);
+qg_status launch_step(const StepArgs& a, const int grid[4], bool big, hipStream_t s) {
+  hipError_t e = qg::launch_dequant(a, grid[3], s);
+  if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
+  e = qg::launch_project(a, grid[0], big, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   e = qg::launch_adam(a, grid[1], s);
   if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
@@ -216,7 +219,8 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   step_constants(d->beta1, d->beta2, step, a);
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
-  const int grid[3] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one)};
+  const int grid[4] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one),
+                       grid_dequant(a.one)};
   return launch_step(a, grid, big, static_cast<hipStream_t>(d->stream));
 }
 
@@ -225,13 +229,13 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
 struct qg_plan {
   std::vector<LayerDev> layers;
   LayerDev* d_table = nullptr;
-  int32_t* d_map[3] = {nullptr, nullptr, nullptr};
-  int grid[3] = {0, 0, 0};
+  int32_t* d_map[4] = {nullptr, nullptr, nullptr, nullptr};
+  int grid[4] = {0, 0, 0, 0};
   int64_t ws_bytes = 0;
   float beta1 = 0.f, beta2 = 0.f;
   bool big = false;
   int device = 0;
-  std::vector<hipEvent_t> events;   // 4 per recorded step when timing is enabled
+  std::vector<hipEvent_t> events;   // 5 per recorded step when timing is enabled
   int timing_cap = 0;
   int timing_used = 0;
 };
@@ -280,16 +284,16 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   p->beta1 = layers[0].desc.beta1;
   p->beta2 = layers[0].desc.beta2;
   int64_t ws = 0;
-  int64_t base[3] = {0, 0, 0};
-  std::vector<int32_t> map[3];
+  int64_t base[4] = {0, 0, 0, 0};
+  std::vector<int32_t> map[4];
   for (int32_t l = 0; l < count; ++l) {
     const qg_layer& x = layers[l];
     const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
     LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
                             split, ws, big);
     ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws).bytes;
-    const int g[3] = {grid_project(L), grid_adam(L), grid_back(L)};
-    for (int k = 0; k < 3; ++k) {
+    const int g[4] = {grid_project(L), grid_adam(L), grid_back(L), grid_dequant(L)};
+    for (int k = 0; k < 4; ++k) {
       if (base[k] + g[k] > kMaxDim) {
         delete p;
         return QG_ERR_SHAPE;
@@ -301,15 +305,15 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
     p->layers.push_back(L);
   }
   p->ws_bytes = ws;
-  for (int k = 0; k < 3; ++k) p->grid[k] = (int)base[k];
+  for (int k = 0; k < 4; ++k) p->grid[k] = (int)base[k];
 
   hipError_t e = hipGetDevice(&p->device);
   if (e == hipSuccess) e = hipMalloc(&p->d_table, sizeof(LayerDev) * count);
-  for (int k = 0; k < 3 && e == hipSuccess; ++k)
+  for (int k = 0; k < 4 && e == hipSuccess; ++k)
     e = hipMalloc(&p->d_map[k], sizeof(int32_t) * map[k].size());
   if (e == hipSuccess)
     e = hipMemcpy(p->d_table, p->layers.data(), sizeof(LayerDev) * count, hipMemcpyHostToDevice);
-  for (int k = 0; k < 3 && e == hipSuccess; ++k)
+  for (int k = 0; k < 4 && e == hipSuccess; ++k)
     e = hipMemcpy(p->d_map[k], map[k].data(), sizeof(int32_t) * map[k].size(),
                   hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -340,22 +344,26 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = nullptr;
-  if (p->timing_used < p->timing_cap) ev = &p->events[4 * p->timing_used++];
+  if (p->timing_used < p->timing_cap) ev = &p->events[5 * p->timing_used++];
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], s);
   if (e != hipSuccess) return hip_fail(e, "timing event");
+  a.wg_layer = p->d_map[3];
+  e = qg::launch_dequant(a, p->grid[3], s);
+  if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
   e = qg::launch_project(a, p->grid[0], p->big, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
-  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
+  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[1];
   e = qg::launch_adam(a, p->grid[1], s);
   if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
-  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
   e = qg::launch_backproject(a, p->grid[2], p->big, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
-  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
+  if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "timing event");
   return QG_OK;
 }
 
@@ -364,7 +372,7 @@ extern "C" qg_status qgalore_plan_enable_timing(qg_plan* p, int32_t max_steps) {
   if (max_steps < 0 || max_steps > 100000) return QG_ERR_ARG;
   hipError_t e = free_events(p);
   if (e != hipSuccess) return hip_fail(e, "timing event destroy");
-  p->events.resize(4 * (size_t)max_steps);
+  p->events.resize(5 * (size_t)max_steps);
   for (size_t k = 0; k < p->events.size(); ++k) {
     e = hipEventCreate(&p->events[k]);
     if (e != hipSuccess) {
@@ -378,13 +386,13 @@ extern "C" qg_status qgalore_plan_enable_timing(qg_plan* p, int32_t max_steps) {
   return QG_OK;
 }
 
-extern "C" qg_status qgalore_plan_kernel_times(qg_plan* p, float out_ms[3], int32_t* steps) {
+extern "C" qg_status qgalore_plan_kernel_times(qg_plan* p, float out_ms[4], int32_t* steps) {
   if (!p || !out_ms) return QG_ERR_NULL;
-  double acc[3] = {0, 0, 0};
+  double acc[4] = {0, 0, 0, 0};
   for (int k = 0; k < p->timing_used; ++k) {
-    hipEvent_t* ev = &p->events[4 * k];
-    hipError_t e = hipEventSynchronize(ev[3]);
-    for (int j = 0; j < 3 && e == hipSuccess; ++j) {
+    hipEvent_t* ev = &p->events[5 * k];
+    hipError_t e = hipEventSynchronize(ev[4]);
+    for (int j = 0; j < 4 && e == hipSuccess; ++j) {
       float ms = 0.f;
       e = hipEventElapsedTime(&ms, ev[j], ev[j + 1]);
       acc[j] += ms;
@@ -392,7 +400,7 @@ extern "C" qg_status qgalore_plan_kernel_times(qg_plan* p, float out_ms[3], int3
     if (e != hipSuccess) return hip_fail(e, "timing event read");
   }
   const int used = p->timing_used;
-  for (int j = 0; j < 3; ++j) out_ms[j] = used ? (float)(acc[j] / used) : 0.f;
+  for (int j = 0; j < 4; ++j) out_ms[j] = used ? (float)(acc[j] / used) : 0.f;
   if (steps) *steps = used;
   p->timing_used = 0;
   return QG_OK;
@@ -402,7 +410,7 @@ extern "C" qg_status qgalore_plan_destroy(qg_plan* p) {
   if (!p) return QG_ERR_NULL;
   hipError_t e = free_events(p);
   if (p->d_table) e = hipFree(p->d_table);
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < 4; ++k)
     if (p->d_map[k]) {
       const hipError_t e2 = hipFree(p->d_map[k]);
       if (e == hipSuccess) e = e2;
