@@ -174,18 +174,70 @@ def roofline(cfg, r, kms):
     names = KERNELS
     k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
+    traffic = measured_traffic(cfg.key, names[k])
     intensity = a["flops"][k] / a["bytes"][k] if a["bytes"][k] else 0.0
     mfma_bound = intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         ach = a["flops"][k] / sec / 1e12
         return dict(kernel=names[k], bound="mfma", achieved=round(ach, 2),
                     peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                    frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4), traffic=traffic,
                     ms_per_launch=round(kms[k], 4))
     ach = a["bytes"][k] / sec / 1e9
     return dict(kernel=names[k], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
                 ms_per_launch=round(kms[k], 4))
+
+
+KERNEL_SOURCES = ("qg_kernels.hip", "qg_gemm.hpp", "qg_device.hpp", "qg_kernels.hpp")
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the step kernels: HBM traffic figures taken by a counter
+    run apply only while this hash is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_rank_gradient_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_key, kernel):
+    """HBM bytes per launch of `kernel` on `config_key` from the counter summary in
+    profiles/traffic.json (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
+    reads for a copy of known size), or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = doc.get("configs", {}).get(config_key, {}).get(kernel)
+    return None if ent is None else float(ent["hbm_bytes"])
+
+
+def copy_bandwidth(torch, gib=2.0, reps=5):
+    """Read+write GB/s of a device-to-device copy of `gib` GiB (torch's copy kernel): the
+    achievable HBM rate beside the 8 TB/s peak, and the copy of known size against which the
+    memory counters are calibrated."""
+    n = int(gib * 2**30)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1))
 
 
 def cpu_baseline(nlayers=7):
@@ -228,6 +280,8 @@ def main():
     ap.add_argument("--secondary", default="llama7b_r128",
                     help="a second rank variant reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=2.0,
+                    help="size of the device copy timed for the achievable HBM rate (0: skip)")
     ap.add_argument("--fast-setup", action="store_true",
                     help="Gaussian stand-in projections instead of QR (profiling runs)")
     args = ap.parse_args()
@@ -246,6 +300,9 @@ def main():
 
     cfg = WL.CONFIGS[args.config]
     dev = torch.device("cuda:0")
+    copy = copy_bandwidth(torch, args.copy_gib) if args.copy_gib > 0 else None
+    if copy:
+        log(f"device copy: {json.dumps(copy)}")
     t0 = time.time()
     G_list, W_list, Ws_list = [], [], []
     for L in cfg.layers:
@@ -309,6 +366,7 @@ def main():
         "refresh_tests_per_step": main_res["refresh_tests_per_step"],
         "cossim_ms": main_res["cossim_ms"],
         "roofline": main_res["roofline"],
+        "copy_gbs": copy["gbs"] if copy else None,
         "variants": {r["config"]: {k: r[k] for k in ("rank", "value", "ms_per_step", "tflops",
                                                     "kernel_ms", "optimizer_ms",
                                                     "refresh_tests_per_step",
