@@ -5,13 +5,19 @@
 // For a batch of projection pairs (same rank r, any row counts):
 //   1. C = P~_new^T P~_old (r x r) on bf16 MFMA, INT4 dequant in LDS, split over the rows.
 //   2. The nuclear norm of C as trace(X^T C), where X is the orthogonal polar factor of C,
-//      obtained by the Newton-Schulz iteration X <- 1.5 X - 0.5 X (X^T X) from X0 = C/||C||_F
-//      (singular values in [0, 1], where the iteration converges to 1 for every nonzero one).
-//      The first iterations only have to lift small singular values towards 1 and run with
-//      bf16 operands; the last ones run with hi/lo split operands (about 16 significant bits)
-//      so that X ends orthogonal to fp32-level accuracy. trace(X^T C) is maximal at the exact
-//      polar factor, so the error that the bf16 phase leaves in X enters the trace only to
-//      second order.
+//      obtained by Newton-Schulz iterations on X, which map every singular value of X
+//      through an odd polynomial while keeping its singular vectors:
+//        * X0 = C / ||C||_F, then rescaled by ||X0^T X0||_F^(-1/2) = (sum_i s_i^4)^(-1/4),
+//          which keeps every singular value at most 1 and brings the large ones near 1;
+//        * quintic steps X <- a X + X (b A + c A^2), A = X^T X, with the coefficients of
+//          the Muon optimizer's orthogonalization (Jordan et al., 2024: a = 3.4445,
+//          b = -4.7750, c = 2.0315): small singular values grow 3.4x per step, and values
+//          already lifted stay in [0.68, 1.2];
+//        * cubic steps X <- 1.5 X - 0.5 X A, which converge all of them to 1.
+//      All but the last steps run with bf16 operands; the last ones use hi/lo split operands
+//      (about 16 significant bits) so that X ends orthogonal to fp32-level accuracy.
+//      trace(X^T C) is maximal at the exact polar factor, so what error the bf16 steps leave
+//      in X enters the trace only to second order.
 #include "qg_gemm.hpp"
 #include "qg_kernels.hpp"
 
@@ -112,7 +118,8 @@ struct StageF32C {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      const int off = (q / CPR) * PITCH + 8 * (q % CPR);
+      static_assert(PITCH == 32 && CPR == 4, "K-contiguous tiles take 32-element rows");
+      const int off = kc_off(q / CPR, q % CPR);
       uint32_t h[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -245,10 +252,12 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_init(CosBatch b) {
 
 // ---------------------------------------------------- 3: Newton-Schulz products ---
 
-// TA: Y = X^T X  (Y at off_y, X at off_x).   !TA: Y = 1.5 X - 0.5 X A  (A at off_a).
+// TA: Y = beta * (M^T M) + alpha * E      (M at off_m; E at off_e, skipped when alpha == 0)
+// !TA: Y = alpha * E + beta * (M Bop)     (Bop at off_bop)
 template <bool TA, int PARTS>
-__global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_x, int64_t off_a,
-                                                      int64_t off_y) {
+__global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_m,
+                                                      int64_t off_bop, int64_t off_e,
+                                                      int64_t off_y, float alpha, float beta) {
   constexpr int STAGE = CosTile::STAGE > NsTileNN::STAGE ? CosTile::STAGE : NsTileNN::STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PARTS * STAGE];
   const int per_pair = b.tiles * b.tiles;
@@ -257,22 +266,22 @@ __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_x
   const int ti = rem / b.tiles, tj = rem - ti * b.tiles;
   const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int r = b.r;
-  const float* X = pair_mat(b, p, off_x);
-  const float* A = pair_mat(b, p, off_a);
+  const float* M = pair_mat(b, p, off_m);
+  const float* E = pair_mat(b, p, off_e);
   float* Y = pair_mat(b, p, off_y);
   f32x16 acc[2][2];
   if constexpr (TA) {
     using T = CosTile;
-    StageF32K<128, T::BK, PARTS, T::STAGE> sa(X, r, r, r, i0);
-    StageF32K<128, T::BK, PARTS, T::STAGE> sb(X, r, r, r, j0);
+    StageF32K<128, T::BK, PARTS, T::STAGE> sa(M, r, r, r, i0);
+    StageF32K<128, T::BK, PARTS, T::STAGE> sb(M, r, r, r, j0);
     gemm_kloop<T, PARTS>(
         sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
         [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
         acc);
   } else {
     using T = NsTileNN;
-    StageF32C<128, T::BK, PARTS, T::STAGE> sa(X, r, r, i0);
-    StageF32K<128, T::BK, PARTS, T::STAGE> sb(A, r, r, r, j0);
+    StageF32C<128, T::BK, PARTS, T::STAGE> sa(M, r, r, i0);
+    StageF32K<128, T::BK, PARTS, T::STAGE> sb(pair_mat(b, p, off_bop), r, r, r, j0);
     gemm_kloop<T, PARTS>(
         sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
         [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
@@ -288,16 +297,19 @@ __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_x
       for (int v = 0; v < 16; ++v) {
         const int64_t i = i0 + acc_row<CosTile>(x, v);
         if (i >= r) continue;
-        float out = acc[x][y][v];
-        if constexpr (!TA) out = 1.5f * gload(X + i * r + j) - 0.5f * out;
+        float out = beta * acc[x][y][v];
+        if (alpha != 0.0f) out += alpha * gload(E + i * r + j);
         gstore(Y + i * r + j, out);
       }
     }
 }
 
-// ------------------------------------------------------- 4: trace(X^T C) per pair ---
+// ------------------------------------------- 4: sum of X .* Y per pair, rescaling ---
 
-__global__ __launch_bounds__(kThreads) void qg_cossim_trace(CosBatch b, int64_t off_x) {
+// Per-block partial sums of the elementwise product of two r x r matrices of each pair
+// (trace(X^T Y)); sum of squares when X == Y.
+__global__ __launch_bounds__(kThreads) void qg_cossim_dot(CosBatch b, int64_t off_x,
+                                                         int64_t off_y) {
   __shared__ float red[kThreads];
   const int p = blockIdx.x / b.nblk;
   const int blk = blockIdx.x - p * b.nblk;
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_trace(CosBatch b, int64_t 
   float acc = 0.0f;
   if (e0 < n2) {
     const float4 x = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_x) + e0));
-    const float4 c = gload(reinterpret_cast<const float4*>(pair_mat(b, p, b.off_c) + e0));
+    const float4 c = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_y) + e0));
     acc = x.x * c.x + x.y * c.y + x.z * c.z + x.w * c.w;
   }
   red[threadIdx.x] = acc;
@@ -318,9 +330,28 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_trace(CosBatch b, int64_t 
   if (threadIdx.x == 0) pair_mat(b, p, b.off_blk)[blk] = red[0];
 }
 
+// X *= s and A *= s^2 with s = ||A||_F^(-1/2) (A = X^T X): afterwards the singular values of
+// X are s_i / (sum_j s_j^4)^(1/4) <= 1.
+__global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
+  const int p = blockIdx.x / b.nblk;
+  const int blk = blockIdx.x - p * b.nblk;
+  const int64_t n2 = (int64_t)b.r * b.r;
+  const int64_t e0 = ((int64_t)blk * kThreads + threadIdx.x) * 4;
+  if (e0 >= n2) return;
+  const float sq = pair_mat(b, p, b.off_norm)[1];   // ||A||_F^2
+  const float s = sq > 0.0f ? 1.0f / sqrtf(sqrtf(sq)) : 0.0f;
+  const float s2 = s * s;
+  float4* X = reinterpret_cast<float4*>(pair_mat(b, p, b.off_x) + e0);
+  float4* A = reinterpret_cast<float4*>(pair_mat(b, p, b.off_a) + e0);
+  const float4 x = gload(X), a = gload(A);
+  gstore(X, make_float4(x.x * s, x.y * s, x.z * s, x.w * s));
+  gstore(A, make_float4(a.x * s2, a.y * s2, a.z * s2, a.w * s2));
+}
+
 // ------------------------------------------------------------------------ driver ---
 
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
+  constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
   int gemm_blocks = 0;
   for (int p = 0; p < b.count; ++p) gemm_blocks += b.pair[p].split * b.tiles * b.tiles;
   hipLaunchKernelGGL(qg_cossim_gemm, dim3(gemm_blocks), dim3(kThreads), 0, s, b);
@@ -330,20 +361,44 @@ hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
                      (float*)nullptr);
   hipLaunchKernelGGL(qg_cossim_init, dim3(eblocks), dim3(kThreads), 0, s, b);
   const int nsb = b.count * b.tiles * b.tiles;
+  // A = X0^T X0 and the rescaling by ||A||_F^(-1/2)
+  hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, b.off_x,
+                     int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
+  hipLaunchKernelGGL(qg_cossim_dot, dim3(eblocks), dim3(kThreads), 0, s, b, b.off_a, b.off_a);
+  hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b,
+                     b.off_norm + (int64_t)sizeof(float), 0.0f, (float*)nullptr);
+  hipLaunchKernelGGL(qg_ns_rescale, dim3(eblocks), dim3(kThreads), 0, s, b);
   int64_t x = b.off_x, xn = b.off_xn;
-  for (int it = 0; it < b.iters_bf16 + b.iters_split; ++it) {
-    if (it < b.iters_bf16) {
-      hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x, x, b.off_a);
-      hipLaunchKernelGGL((qg_ns_gemm<false, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x, b.off_a, xn);
+  for (int it = 0; it < b.iters_quintic; ++it) {
+    if (it > 0)
+      hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
+                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
+    // B = b A + c A^2 (A is symmetric: A^2 = A^T A), then X <- a X + X B
+    hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, b.off_a,
+                       int64_t(0), b.off_a, b.off_b, kQb, kQc);
+    hipLaunchKernelGGL((qg_ns_gemm<false, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x, b.off_b,
+                       x, xn, kQa, 1.0f);
+    const int64_t t = x;
+    x = xn;
+    xn = t;
+  }
+  for (int it = 0; it < b.iters_cubic_bf16 + b.iters_cubic_split; ++it) {
+    if (it < b.iters_cubic_bf16) {
+      hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
+                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
+      hipLaunchKernelGGL((qg_ns_gemm<false, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
+                         b.off_a, x, xn, 1.5f, -0.5f);
     } else {
-      hipLaunchKernelGGL((qg_ns_gemm<true, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x, x, b.off_a);
-      hipLaunchKernelGGL((qg_ns_gemm<false, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x, b.off_a, xn);
+      hipLaunchKernelGGL((qg_ns_gemm<true, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x,
+                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
+      hipLaunchKernelGGL((qg_ns_gemm<false, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x,
+                         b.off_a, x, xn, 1.5f, -0.5f);
     }
     const int64_t t = x;
     x = xn;
     xn = t;
   }
-  hipLaunchKernelGGL(qg_cossim_trace, dim3(eblocks), dim3(kThreads), 0, s, b, x);
+  hipLaunchKernelGGL(qg_cossim_dot, dim3(eblocks), dim3(kThreads), 0, s, b, x, b.off_c);
   hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b, (int64_t)0,
                      1.0f / (float)b.r, out);
   return hipGetLastError();

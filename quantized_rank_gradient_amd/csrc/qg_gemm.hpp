@@ -38,13 +38,24 @@ struct Tile {
   static_assert(XM * 32 == WTM && XN * 32 == WTN, "wave tile is a multiple of 32");
   // LDS pitches (bf16 elements): K-major tiles are BK rows of (edge + 32), so consecutive rows
   // start 16 banks apart and the 4-row x 32-byte footprint of a 16-lane transpose read covers
-  // all 64 banks once; K-contiguous tiles are edge rows of (BK + 8).
-  static constexpr int A_PITCH = A_KMAJOR ? BM + 32 : BK + 8;
-  static constexpr int B_PITCH = B_KMAJOR ? BN + 32 : BK + 8;
+  // all 64 banks once; K-contiguous tiles are edge rows of BK, unpadded, with the chunks of a
+  // row permuted (kc_off below).
+  static_assert(A_KMAJOR || BK == 32, "K-contiguous tiles take 32-element rows");
+  static_assert(B_KMAJOR || BK == 32, "K-contiguous tiles take 32-element rows");
+  static constexpr int A_PITCH = A_KMAJOR ? BM + 32 : BK;
+  static constexpr int B_PITCH = B_KMAJOR ? BN + 32 : BK;
   static constexpr int A_ELEMS = A_KMAJOR ? BK * A_PITCH : BM * A_PITCH;
   static constexpr int B_ELEMS = B_KMAJOR ? BK * B_PITCH : BN * B_PITCH;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;      // one [A | B] stage, bf16 elements
 };
+
+// Element offset of 8-element chunk `chunk` (0..3) of row `row` in a K-contiguous tile: rows
+// of 32 elements, chunk c of row i stored at position c ^ ((i / 4) % 4). A 16-lane group then
+// covers the 64 LDS banks exactly once both when it writes four whole rows (staging) and when
+// it reads one chunk of 16 consecutive rows (an MFMA fragment).
+__device__ __forceinline__ int kc_off(int row, int chunk) {
+  return row * 32 + 8 * (chunk ^ ((row >> 2) & 3));
+}
 
 // ---------------------------------------------------------------------------------------
 // Stagers: each fills one operand tile (W = its edge along the output, BK along K) with 256
@@ -54,35 +65,41 @@ struct Tile {
 // ---------------------------------------------------------------------------------------
 
 // bf16 source [k][c] (row pitch ld, `rows` rows in all) -> K-major LDS tile [k][c].
-template <int W, int BK>
+// VEC (requires ld % 8 == 0): each stage reads 16-byte chunks through a buffer resource that
+// starts at the stage's first row and ends at k_end, so rows past the K range read as zero
+// without a per-lane test and the per-lane offsets stay fixed for the whole loop. Otherwise
+// elements are read one by one with full bounds tests.
+template <int W, int BK, bool VEC>
 struct StageBf16K {
   static constexpr int CPR = W / 8;                    // chunks per row
   static constexpr int NC = BK * CPR / kThreads;       // chunks per thread
-  static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
+  static constexpr int RPU = kThreads / CPR;           // rows between a thread's chunks
+  static_assert(NC * kThreads == BK * CPR && RPU * CPR == kThreads,
+                "tile splits evenly over the threads");
+  const uint16_t* src;
   rsrc_t rs;
   uint32_t ld, k_end, c_end;
   int c0;
-  bool vec_ld;
+  uint32_t vo[NC];   // byte offset of chunk u from the stage's first row; kOOB off the tile
   uint4 v[NC];
 
   __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t rows, int64_t k_end_,
                         int64_t c_end_, int c0_)
-      : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
+      : src(s), ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
     rs = make_rsrc(s, (uint32_t)(rows * ld_ * 2));
-    vec_ld = (ld_ % 8 == 0);
+    const uint32_t c = c0 + 8 * (threadIdx.x % CPR);
+#pragma unroll
+    for (int u = 0; u < NC; ++u)
+      vo[u] = c < c_end ? ((threadIdx.x / CPR + u * RPU) * ld + c) * 2 : kOOB;
   }
 
   __device__ __forceinline__ void load(int64_t k0_) {
     const uint32_t k0 = (uint32_t)k0_;
-    if (vec_ld) {
+    if constexpr (VEC) {
+      const uint32_t kb = k0 < k_end ? k0 : k_end;
+      const rsrc_t st = make_rsrc(src + (size_t)kb * ld, (k_end - kb) * ld * 2);
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-        const int q = threadIdx.x + kThreads * u;
-        const uint32_t k = k0 + q / CPR;
-        const uint32_t c = c0 + 8 * (q % CPR);
-        const uint32_t off = (k < k_end && c < c_end) ? (k * ld + c) * 2 : kOOB;
-        v[u] = bload128(rs, off);
-      }
+      for (int u = 0; u < NC; ++u) v[u] = bload128(st, vo[u]);
     } else {
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
@@ -167,83 +184,50 @@ struct StageInt4K {
 };
 
 // bf16 source [c][k] (row pitch ld = the K extent, ld % 8 == 0, c_end rows) -> K-contiguous
-// LDS tile [c][k].
+// LDS tile [c][k]. Each stage reads through a buffer resource starting at column k0; rows past
+// c_end fall outside it. Only a last, partial stage (ld % BK != 0) tests columns per lane.
 template <int W, int BK>
 struct StageBf16C {
   static constexpr int CPR = BK / 8;
   static constexpr int NC = W * CPR / kThreads;
-  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
-  rsrc_t rs;
-  uint32_t ld, c_end;
+  static constexpr int RPU = kThreads / CPR;
+  static_assert(NC * kThreads == W * CPR && RPU * CPR == kThreads,
+                "tile splits evenly over the threads");
+  const uint16_t* src;
+  uint32_t ld, c_end, kk;
   int c0;
+  uint32_t vo[NC];
   uint4 v[NC];
 
   __device__ StageBf16C(const uint16_t* s, int64_t ld_, int64_t c_end_, int c0_)
-      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
-    rs = make_rsrc(s, (uint32_t)(c_end_ * ld_ * 2));
+      : src(s), ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
+    kk = 8 * (threadIdx.x % CPR);
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const uint32_t row = c0 + threadIdx.x / CPR + u * RPU;
+      vo[u] = row < c_end ? (row * ld + kk) * 2 : kOOB;
+    }
   }
 
   __device__ __forceinline__ void load(int64_t k0_) {
-    const uint32_t k0 = (uint32_t)k0_;
+    const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
+    const rsrc_t st = make_rsrc(src + k0, (c_end * ld - k0) * 2);
+    if (k0 + BK <= ld) {
 #pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      const uint32_t row = c0 + q / CPR;
-      const uint32_t k = k0 + 8 * (q % CPR);
-      v[u] = bload128(rs, (row < c_end && k < ld) ? (row * ld + k) * 2 : kOOB);
+      for (int u = 0; u < NC; ++u) v[u] = bload128(st, vo[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) v[u] = bload128(st, k0 + kk < ld ? vo[u] : kOOB);
     }
   }
 
   template <int PITCH>
   __device__ __forceinline__ void store(uint16_t* lds) const {
+    static_assert(PITCH == 32 && CPR == 4, "K-contiguous tiles take 32-element rows");
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v[u];
-    }
-  }
-};
-
-// INT4 source [c][k] (row pitch ld codes = the K extent, ld % 8 == 0, `rows` rows) ->
-// K-contiguous LDS tile [c][k] in bf16.
-template <int W, int BK>
-struct StageInt4C {
-  static constexpr int CPR = BK / 8;
-  static constexpr int NC = W * CPR / kThreads;
-  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
-  rsrc_t rq, rsc;
-  uint32_t ld, c_end;
-  int c0;
-  uint32_t w[NC];
-  float s[NC];
-
-  __device__ StageInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
-      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
-    const int64_t numel = c_end_ * ld_;
-    rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
-    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
-  }
-
-  __device__ __forceinline__ void load(int64_t k0_) {
-    const uint32_t k0 = (uint32_t)k0_;
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      const uint32_t row = c0 + q / CPR;
-      const uint32_t k = k0 + 8 * (q % CPR);
-      const bool in = row < c_end && k < ld;
-      const uint32_t e = row * ld + k;
-      w[u] = bload32(rq, in ? (e >> 1) : kOOB);
-      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
-    }
-  }
-
-  template <int PITCH>
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
+      *reinterpret_cast<uint4*>(lds + kc_off(q / CPR, q % CPR)) = v[u];
     }
   }
 };
@@ -262,8 +246,8 @@ template <bool KMAJOR, int PITCH>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int c, int ks) {
   const int lane = threadIdx.x & 63;
   if constexpr (!KMAJOR) {
-    return *reinterpret_cast<const bf16x8*>(tile + (c + (lane & 31)) * PITCH + ks +
-                                            8 * (lane >> 5));
+    return *reinterpret_cast<const bf16x8*>(tile +
+                                            kc_off(c + (lane & 31), (ks >> 3) + (lane >> 5)));
   } else {
     typedef __attribute__((address_space(3))) v4i16* lptr;
     const int row = ks + 8 * (lane >> 5) + ((lane & 15) >> 2);

@@ -43,11 +43,10 @@ __global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
 using ProjBig = Tile<256, 256, 64, 2, 2, true, true>;
 using ProjSmall = Tile<128, 256, 32, 2, 2, true, true>;
 
-template <class T>
-__global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
-  int local;
-  const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
+// VEC: rows of G are a multiple of 8 elements (16-byte chunk loads).
+template <class T, bool VEC>
+__device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& L, int local,
+                                             uint16_t* lds) {
   // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
   // columns are neighbours (and, after the renumbering, on the same XCD).
   const int ti = local % L.p_tiles_i;
@@ -59,9 +58,9 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
   // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
-  StageBf16K<T::BM, T::BK> sa(reinterpret_cast<const uint16_t*>(a.ws + L.off_p), L.r, L.m,
-                              k_end, L.r, i0);
-  StageBf16K<T::BN, T::BK> sb(L.G, L.n, L.m, k_end, L.n, j0);
+  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+  StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
+  StageBf16K<T::BN, T::BK, VEC> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
@@ -83,6 +82,19 @@ __global__ __launch_bounds__(kThreads) void qg_project(StepArgs a) {
         bstoref(ro, (i < r && j < n) ? (i * n + j) * 4 : kOOB, acc[x][y][v]);
       }
     }
+}
+
+// The smaller tile is held to 256 registers per lane so that two waves share each SIMD.
+template <class T>
+__global__ __launch_bounds__(kThreads, T::BM * T::BN < 256 * 256 ? 2 : 1) void qg_project(
+    StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
+  int local;
+  const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
+  if (L.n % 8 == 0)
+    project_tile<T, true>(a, L, local, lds);
+  else
+    project_tile<T, false>(a, L, local, lds);
 }
 
 // ============================================================================== Adam ===
@@ -301,16 +313,29 @@ static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true)
               "host and device back-projection tiles agree");
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
-  constexpr int EP = T::WTN + 8;   // fp32 row pitch of the redistribution block
-  constexpr int LDS_BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
-                                ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
+struct BackLds {
+  static constexpr int EP = T::WTN + 8;   // fp32 row pitch of the redistribution block
+  static constexpr int BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
+                                   ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
+};
+
+// VEC: rows of W (and of N~) are a multiple of 8 elements: 8-byte weight accesses
+// (prefetched before the product) and 16-byte chunk loads of N~.
+template <class T, bool VEC>
+__device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
+                                          uint16_t* lds) {
+  constexpr int EP = BackLds<T>::EP;
   constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
-  int local;
-  const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
-  const int ti = local / L.b_tiles_j;
-  const int tj = local - ti * L.b_tiles_j;
+  // Tiles are numbered in bands of 4 row tiles, column-major inside a band: the tiles that
+  // run together on one XCD (consecutive after the renumbering) cover about 4 row tiles x 8
+  // column tiles, whose P~ rows and N~ columns fit in that XCD's L2 together.
+  constexpr int GM = 4;
+  const int band = local / (GM * L.b_tiles_j);
+  const int first = band * GM;
+  const int gm = min(L.b_tiles_i - first, GM);
+  const int in_band = local - band * GM * L.b_tiles_j;
+  const int ti = first + in_band % gm;
+  const int tj = in_band / gm;
   const int i0 = ti * T::BM, j0 = tj * T::BN;
 
   // After the product, each wave's block goes through LDS 32 rows at a time so that every
@@ -324,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
   SrCtx c;
   c.n = (uint32_t)L.n;
   c.m = (uint32_t)L.m;
-  c.vec = (L.n % 8 == 0);
+  c.vec = VEC;
   c.write_u = (L.U_out != nullptr);
   const uint32_t numel = (uint32_t)(L.m * L.n);
   c.rw = make_rsrc(L.Wq, numel);
@@ -335,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
   const bool one_group = (L.n % kGroup == 0);
   uint2 wpre[T::XM][NQ];
   float spre[T::XM];   // the scale of the lane's run when rows are whole groups
-  if (c.vec) {
+  if constexpr (VEC) {
 #pragma unroll
     for (int x = 0; x < T::XM; ++x) {
       const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
@@ -351,9 +376,10 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
 
   // A = P~ (rows i, K = rank index contiguous: the bf16 copy the projection kernel wrote),
   // B = N~ stored [k][j] (r x n).
-  StageBf16C<T::BM, T::BK> sa(reinterpret_cast<const uint16_t*>(a.ws + L.off_p), L.r, L.m, i0);
-  StageBf16K<T::BN, T::BK> sb(reinterpret_cast<const uint16_t*>(a.ws + L.off_n), L.n, L.r, L.r,
-                              L.n, j0);
+  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+  const uint16_t* Nb = reinterpret_cast<const uint16_t*>(a.ws + L.off_n);
+  StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
+  StageBf16K<T::BN, T::BK, VEC> sb(Nb, L.n, L.r, L.r, L.n, j0);
   f32x16 acc[T::XM][T::XN];
   gemm_kloop<T, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
@@ -361,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
       acc);
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
-  if (c.vec) {
+  if constexpr (VEC) {
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
@@ -396,6 +422,19 @@ __global__ __launch_bounds__(kThreads) void qg_backproject(StepArgs a) {
       __syncthreads();
     }
   }
+}
+
+// Held to 256 registers per lane: two workgroups per CU (two waves per SIMD) hide the load
+// latency better than more registers in one.
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void qg_backproject(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::BYTES / 2];
+  int local;
+  const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
+  if (L.n % 8 == 0)
+    back_tile<T, true>(a, L, local, lds);
+  else
+    back_tile<T, false>(a, L, local, lds);
 }
 
 // ========================================================== INT4 quantization of P ===

@@ -24,11 +24,13 @@ struct CosBatch {
   char* ws;              // workspace base; pair p owns [p * pair_stride, (p+1) * pair_stride)
   int64_t pair_stride;
   int64_t off_part;      // split x r x r partial sums of C
-  int64_t off_c, off_x, off_xn, off_a;   // r x r fp32 matrices
+  int64_t off_c, off_x, off_xn, off_a, off_b;   // r x r fp32 matrices
   int64_t off_blk;       // per-block partial sums
-  int64_t off_norm;      // squared Frobenius norm of C
+  int64_t off_norm;      // [0]: squared Frobenius norm of C, [1]: of X0^T X0
   int count, r, tiles, nblk;
-  int iters_bf16, iters_split;   // Newton-Schulz iterations with bf16 / split operands
+  int iters_quintic;     // Newton-Schulz iterations lifting small singular values (bf16)
+  int iters_cubic_bf16;  // then cubic iterations with bf16 operands
+  int iters_cubic_split; // and with hi/lo split operands
 };
 
 // Tile edges of the two configurations of each MFMA kernel ("big": rank above 128).

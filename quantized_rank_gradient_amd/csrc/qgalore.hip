@@ -30,6 +30,7 @@ bool finite(float x) { return std::isfinite(x); }
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int kTile = 128;   // output tile edge of the similarity kernels
 constexpr int kK = 32;       // K per stage of the MFMA kernels
+constexpr int kKSlab = 64;   // split-K slab granularity: whole K stages of both tile sizes
 
 qg_status device_present() {
   static int cached = -1;
@@ -63,15 +64,15 @@ int64_t proj_tiles(int64_t n, int64_t r, bool big) {
 // workgroups to cover the chip, bounded so the fp32 partial sums stay small next to G.
 int choose_split(int64_t m, int64_t n, int64_t r) {
   const int64_t tiles = proj_tiles(n, r, big_tiles(r));
-  const int64_t kchunks = cdiv(m, kK);
+  const int64_t kchunks = cdiv(m, kKSlab);
   int64_t s = cdiv(512, tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, m / (8 * r)));
   s = std::min<int64_t>(s, kchunks);
   s = std::max<int64_t>(s, 1);
-  const int64_t kslab = cdiv(kchunks, s) * kK;
+  const int64_t kslab = cdiv(kchunks, s) * kKSlab;
   return (int)cdiv(m, kslab);
 }
-int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kK), split) * kK; }
+int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kKSlab), split) * kKSlab; }
 
 // Per-layer workspace: split-K partial sums of R (fp32), the bf16 update N~ (r x n) and the
 // bf16 dequantized projection P~ (m x r) that the projection kernel leaves for the
@@ -422,12 +423,15 @@ extern "C" qg_status qgalore_plan_destroy(qg_plan* p) {
 // ============================================================ subspace similarity ===
 
 namespace {
-constexpr int kNsItersBf16 = 30;   // Newton-Schulz iterations with bf16 operands
-constexpr int kNsItersSplit = 3;   // followed by iterations with hi/lo split operands
+// Newton-Schulz schedule of the similarity test: quintic iterations that lift small singular
+// values, then cubic ones that converge them to 1 (bf16 operands, then hi/lo split operands).
+constexpr int kNsQuintic = 7;
+constexpr int kNsCubicBf16 = 3;
+constexpr int kNsCubicSplit = 2;
 
 struct CosLayout {
   int split, tiles, nblk;
-  int64_t off_part, off_c, off_x, off_xn, off_a, off_blk, off_norm, stride;
+  int64_t off_part, off_c, off_x, off_xn, off_a, off_b, off_blk, off_norm, stride;
 };
 CosLayout cos_layout(int64_t r) {
   CosLayout c;
@@ -441,7 +445,8 @@ CosLayout cos_layout(int64_t r) {
   c.off_x = c.off_c + mat;
   c.off_xn = c.off_x + mat;
   c.off_a = c.off_xn + mat;
-  c.off_blk = c.off_a + mat;
+  c.off_b = c.off_a + mat;
+  c.off_blk = c.off_b + mat;
   c.off_norm = c.off_blk + round_up((int64_t)c.nblk * 4, 256);
   c.stride = c.off_norm + 256;
   return c;
@@ -505,10 +510,12 @@ extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P
     b.off_x = c.off_x;
     b.off_xn = c.off_xn;
     b.off_a = c.off_a;
+    b.off_b = c.off_b;
     b.off_blk = c.off_blk;
     b.off_norm = c.off_norm;
-    b.iters_bf16 = kNsItersBf16;
-    b.iters_split = kNsItersSplit;
+    b.iters_quintic = kNsQuintic;
+    b.iters_cubic_bf16 = kNsCubicBf16;
+    b.iters_cubic_split = kNsCubicSplit;
     int base = 0;
     for (int k = 0; k < b.count; ++k) {
       const qg_proj& pn = P_new[first + k];

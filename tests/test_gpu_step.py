@@ -201,7 +201,9 @@ def test_cossim_matches_oracle(m, r):
     full = np.linalg.qr(rng.standard_normal((m, 2 * r)))[0]
     A0, A1 = full[:, :r], full[:, r:]
     Prand = np.linalg.qr(rng.standard_normal((m, r)))[0]
-    for theta, other in ((None, A0), (1.159, None), (0.5, None), (None, Prand)):
+    half = np.concatenate([A0[:, : r // 2], A1[:, r // 2:]], axis=1)   # half the spectrum ~0
+    cases = ((None, A0), (1.159, None), (0.5, None), (None, Prand), (None, half), (None, A1))
+    for theta, other in cases:
         Pb = other if theta is None else A0 * np.cos(theta) + A1 * np.sin(theta)
         qa, sa = O.quantize_proj(A0.astype(np.float32))
         qb, sb = O.quantize_proj(Pb.astype(np.float32))
