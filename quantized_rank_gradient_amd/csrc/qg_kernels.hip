@@ -205,7 +205,6 @@ __global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
 struct SrCtx {
   rsrc_t rw, rws, ru;
   uint32_t n, m;
-  bool vec;          // n % 8 == 0: 8-byte weight accesses (prefetched by the caller)
   bool write_u;
 };
 
@@ -219,48 +218,59 @@ __device__ __forceinline__ int sr_code(float d) {
   return (int)fminf(fmaxf(floorf(d), -127.f), 127.f);
 }
 
-// Vector path: the 8 weights arrive prefetched in `wv` and share the scale reciprocal `inv`.
-__device__ __forceinline__ void sr_block8_vec(const SrCtx& c, const LayerDev& L,
-                                              const StepArgs& a, uint32_t i, uint32_t j8,
-                                              const float* S, float inv, uint2 wv) {
-  if (j8 >= c.n) return;
-  const uint4 ph = philox4x32_10(make_uint4(j8 >> 3, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
-  const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
-  const uint32_t e0 = i * c.n + j8;
-  const uint32_t win[2] = {wv.x, wv.y};
-  float U[8], d[8];
-  int w[8];
+// Vector path (rows a multiple of 16): 16 consecutive weights (i, j16 .. j16+15), j16 a
+// multiple of 16, arrive prefetched in `wv`; they lie in one scale group (reciprocal `inv`)
+// and take two Philox blocks.
+__device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
+                                           const StepArgs& a, uint32_t i, uint32_t j16,
+                                           const float* S, float inv, uint4 wv) {
+  uint32_t words[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 ph =
+        philox4x32_10(make_uint4((j16 >> 3) + h, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
+    words[4 * h + 0] = ph.x;
+    words[4 * h + 1] = ph.y;
+    words[4 * h + 2] = ph.z;
+    words[4 * h + 3] = ph.w;
+  }
+  const uint32_t e0 = i * c.n + j16;
+  const uint32_t win[4] = {wv.x, wv.y, wv.z, wv.w};
+  float U[16], d[16];
+  int w[16];
   float sum = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < 16; ++t) {
     U[t] = mul_rn(L.alpha, S[t]);
     w[t] = (int)(int8_t)(win[t >> 2] >> (8 * (t & 3)));
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
     d[t] = sr_pre(w[t], U[t], inv, bits);
-    sum += d[t];   // finite exactly when all eight are (|d| stays below 2^8 when finite)
+    sum += d[t];   // finite exactly when all sixteen are (|d| stays below 2^8 when finite)
   }
-  uint32_t wout[2] = {0, 0};
+  uint32_t wout[4] = {0, 0, 0, 0};
   if (__builtin_isfinite(sum)) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) wout[t >> 2] |= (uint32_t)(sr_code(d[t]) & 0xFF) << (8 * (t & 3));
+    for (int t = 0; t < 16; ++t)
+      wout[t >> 2] |= (uint32_t)(sr_code(d[t]) & 0xFF) << (8 * (t & 3));
   } else {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 16; ++t) {
       const int nw = __builtin_isfinite(d[t]) ? sr_code(d[t]) : w[t];
       wout[t >> 2] |= (uint32_t)(nw & 0xFF) << (8 * (t & 3));
     }
   }
-  bstore64(c.rw, e0, make_uint2(wout[0], wout[1]));
+  bstore128(c.rw, e0, make_uint4(wout[0], wout[1], wout[2], wout[3]));
   if (c.write_u) {
-    bstore128(c.ru, e0 * 4, make_uint4(__float_as_uint(U[0]), __float_as_uint(U[1]),
-                                       __float_as_uint(U[2]), __float_as_uint(U[3])));
-    bstore128(c.ru, e0 * 4 + 16, make_uint4(__float_as_uint(U[4]), __float_as_uint(U[5]),
-                                            __float_as_uint(U[6]), __float_as_uint(U[7])));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      bstore128(c.ru, (e0 + 4 * k) * 4,
+                make_uint4(__float_as_uint(U[4 * k]), __float_as_uint(U[4 * k + 1]),
+                           __float_as_uint(U[4 * k + 2]), __float_as_uint(U[4 * k + 3])));
   }
 }
 
-// Element path for rows whose length is not a multiple of 8 (unaligned, possibly straddling
-// scale groups): byte accesses and a scale lookup per element.
+// Element path for rows whose length is not a multiple of 16 (possibly straddling scale
+// groups): byte accesses and a scale lookup per element.
 __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L,
                                                const StepArgs& a, uint32_t i, uint32_t j8,
                                                const float* S) {
@@ -295,6 +305,17 @@ __device__ __forceinline__ void stage_rows(float* E, const f32x16 (&accx)[T::XN]
   __syncthreads();
 }
 
+__device__ __forceinline__ void read_run16(const float* E, int off, float (&S)[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 f = *reinterpret_cast<const float4*>(E + off + 4 * k);
+    S[4 * k] = f.x;
+    S[4 * k + 1] = f.y;
+    S[4 * k + 2] = f.z;
+    S[4 * k + 3] = f.w;
+  }
+}
+
 __device__ __forceinline__ void read_run(const float* E, int off, float (&S)[8]) {
   const float4 f0 = *reinterpret_cast<const float4*>(E + off);
   const float4 f1 = *reinterpret_cast<const float4*>(E + off + 4);
@@ -314,18 +335,23 @@ static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true)
 
 template <class T>
 struct BackLds {
-  static constexpr int EP = T::WTN + 8;   // fp32 row pitch of the redistribution block
+  // fp32 row pitch of the redistribution block: 4 (mod 16) words, so that the 16 lanes of a
+  // 16-byte read group (4 rows x 4 runs of 16 columns) hit distinct banks
+  static constexpr int EP = T::WTN + 4;
   static constexpr int BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
                                    ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
 };
 
-// VEC: rows of W (and of N~) are a multiple of 8 elements: 8-byte weight accesses
+// VEC: rows of W (and of N~) are a multiple of 16 elements: 16-byte weight accesses
 // (prefetched before the product) and 16-byte chunk loads of N~.
 template <class T, bool VEC>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
                                           uint16_t* lds) {
   constexpr int EP = BackLds<T>::EP;
-  constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk
+  constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk (element path)
+  constexpr int LPR = T::WTN / 16; // vector path: lanes per row, 16 columns each
+  constexpr int RPP = 64 / LPR;    //   rows per pass of a 32-row chunk
+  constexpr int NP = 32 / RPP;     //   passes per chunk
   // Tiles are numbered in bands of 4 row tiles, column-major inside a band: the tiles that
   // run together on one XCD (consecutive after the renumbering) cover about 4 row tiles x 8
   // column tiles, whose P~ rows and N~ columns fit in that XCD's L2 together.
@@ -338,40 +364,38 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   const int tj = in_band / gm;
   const int i0 = ti * T::BM, j0 = tj * T::BN;
 
-  // After the product, each wave's block goes through LDS 32 rows at a time so that every
-  // lane owns WTN/2 consecutive columns of one row: whole Philox blocks and wide W accesses.
-  // The weights and scale reciprocals that lane will need do not depend on the product, so
-  // their loads are issued first and arrive while the MFMAs run.
+  // After the product, each wave's block goes through LDS 32 rows at a time so that lanes
+  // own runs of consecutive columns of one row: whole Philox blocks and wide W accesses. On
+  // the vector path a lane takes 16 columns (one 16-byte weight access, two Philox blocks)
+  // and LPR lanes cover a row of the wave's block. The weights and scales a lane will need
+  // do not depend on the product, so their loads are issued first and arrive while the
+  // MFMAs run.
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave_m<T>(), wn = wave_n<T>();
-  const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
   SrCtx c;
   c.n = (uint32_t)L.n;
   c.m = (uint32_t)L.m;
-  c.vec = VEC;
   c.write_u = (L.U_out != nullptr);
   const uint32_t numel = (uint32_t)(L.m * L.n);
   c.rw = make_rsrc(L.Wq, numel);
   c.rws = make_rsrc(L.Ws, ((numel + kGroup - 1) / kGroup) * 4);
   c.ru = make_rsrc(L.U_out, c.write_u ? numel * 4 : 0);
-  const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
-  // a lane's WTN/2 columns lie in one weight scale group when rows are whole groups
-  const bool one_group = (L.n % kGroup == 0);
-  uint2 wpre[T::XM][NQ];
-  float spre[T::XM];   // the scale of the lane's run when rows are whole groups
+  const int vr = lane / LPR, vc = (lane % LPR) * 16;
+  const uint32_t j16 = (uint32_t)j0 + wn * T::WTN + vc;
+  uint4 wv[T::XM][NP];
+  float sv[T::XM][NP];
   if constexpr (VEC) {
 #pragma unroll
-    for (int x = 0; x < T::XM; ++x) {
-      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
+    for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const uint32_t j8 = jb + 8 * q;
-        const bool in = i < c.m && j8 < c.n;
-        wpre[x][q] = bload64(c.rw, in ? i * c.n + j8 : kOOB);
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + RPP * p + vr;
+        const uint32_t e = i * c.n + j16;
+        const bool in = i < c.m && j16 < c.n;
+        wv[x][p] = bload128(c.rw, in ? e : kOOB);
+        sv[x][p] = bloadf(c.rws, in ? (e >> 8) * 4 : kOOB);
       }
-      spre[x] = bloadf(c.rws, (one_group && i < c.m && jb < c.n) ? ((i * c.n + jb) >> 8) * 4 : kOOB);
-    }
   }
 
   // A = P~ (rows i, K = rank index contiguous: the bf16 copy the projection kernel wrote),
@@ -391,23 +415,21 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
-      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
-      if (i < c.m) {
-        const float inv0 = recip_or_zero(spre[x]);
 #pragma clang loop unroll(full)
-        for (int q = 0; q < NQ; ++q) {
-          float S[8];
-          read_run(E, rr * EP + cc + 8 * q, S);
-          const uint32_t j8 = jb + 8 * q;
-          const float inv =
-              one_group ? inv0
-                        : recip_or_zero(bloadf(c.rws, j8 < c.n ? ((i * c.n + j8) >> 8) * 4 : kOOB));
-          sr_block8_vec(c, L, a, i, j8, S, inv, wpre[x][q]);
+      for (int p = 0; p < NP; ++p) {
+        const int row = RPP * p + vr;
+        const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + row;
+        if (i < c.m && j16 < c.n) {
+          float S[16];
+          read_run16(E, row * EP + vc, S);
+          sr_block16(c, L, a, i, j16, S, recip_or_zero(sv[x][p]), wv[x][p]);
         }
       }
       __syncthreads();
     }
   } else {
+    const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
+    const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
@@ -431,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 2) void qg_backproject(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::BYTES / 2];
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
-  if (L.n % 8 == 0)
+  if (L.n % 16 == 0)
     back_tile<T, true>(a, L, local, lds);
   else
     back_tile<T, false>(a, L, local, lds);
