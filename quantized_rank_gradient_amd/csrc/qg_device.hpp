@@ -190,13 +190,24 @@ __device__ __forceinline__ int nibble(uint32_t w, int k) {
 // Section 3: each round multiplies words 0 and 2 by the round multipliers and mixes the
 // 64-bit products' halves with words 1, 3 and the key; the key advances by the Weyl
 // constants between rounds. Ten rounds.
+// Three-way XOR in one gfx950 bitop3 instruction (truth table 0x96 = a ^ b ^ c).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
     const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
-    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
-                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    if (round == 0) {
+      // plain XORs let the compiler fold the parts that are uniform across the wave
+      c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                     (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    } else {
+      c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
+                     xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0);
+    }
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
