@@ -14,8 +14,9 @@
 //          b = -4.7750, c = 2.0315): small singular values grow 3.4x per step, and values
 //          already lifted stay in [0.68, 1.2];
 //        * cubic steps X <- 1.5 X - 0.5 X A, which converge all of them to 1.
-//      All but the last steps run with bf16 operands; the last ones use hi/lo split operands
-//      (about 16 significant bits) so that X ends orthogonal to fp32-level accuracy.
+//      All but the last steps run with bf16 operands and keep X, A and B in bf16; the last
+//      ones keep X in fp32 and use hi/lo split operands (about 16 significant bits) so that
+//      X ends orthogonal to fp32-level accuracy.
 //      trace(X^T C) is maximal at the exact polar factor, so what error the bf16 steps leave
 //      in X enters the trace only to second order.
 #include "qg_gemm.hpp"
@@ -23,8 +24,9 @@
 
 namespace qg {
 
-using CosTile = Tile<128, 128, 32, 2, 2, true, true>;     // C = P~n^T P~o, X^T X
-using NsTileNN = Tile<128, 128, 32, 2, 2, false, true>;   // X A
+using CosTile = Tile<kCosTile, kCosTile, 32, 2, 2, true, true>;     // C = P~n^T P~o, X^T X
+using NsTileNN = Tile<kCosTile, kCosTile, 32, 2, 2, false, true>;   // X A
+static_assert(CosTile::XM == NsTileNN::XM && CosTile::XN == NsTileNN::XN, "same wave tiling");
 
 // --------------------------------------------------------------- fp32 -> LDS stagers ---
 // fp32 sources are rounded to bf16 on the way into LDS; with PARTS == 2 the bf16 remainder
@@ -147,13 +149,17 @@ __device__ __forceinline__ int pair_of_block(const CosBatch& b, int blk, int& lo
 __device__ __forceinline__ float* pair_mat(const CosBatch& b, int p, int64_t off) {
   return reinterpret_cast<float*>(b.ws + (int64_t)p * b.pair_stride + off);
 }
+__device__ __forceinline__ uint16_t* pair_bf(const CosBatch& b, int p, int64_t off) {
+  return reinterpret_cast<uint16_t*>(b.ws + (int64_t)p * b.pair_stride + off);
+}
 
 // ------------------------------------------------------------- 1: C = P~n^T P~o ---
 
 __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CosTile::STAGE];
   int local;
-  const int p = pair_of_block(b, blockIdx.x, local);
+  // consecutive blocks (one pair's tiles) share an XCD and its L2
+  const int p = pair_of_block(b, xcd_remap(blockIdx.x, gridDim.x), local);
   const CosPair& q = b.pair[p];
   const int per_split = b.tiles * b.tiles;
   const int s = local / per_split;
@@ -162,18 +168,18 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int64_t k_begin = (int64_t)s * q.kslab;
   const int64_t k_end = min<int64_t>(q.m, k_begin + q.kslab);
-  StageInt4K<128, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
-  StageInt4K<128, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
-  f32x16 acc[2][2];
+  StageInt4K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+  StageInt4K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
+  f32x16 acc[CosTile::XM][CosTile::XN];
   gemm_kloop<CosTile, 1>(
       sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },
       [](auto& st, uint16_t* p) { st.template store<CosTile::B_PITCH>(p + CosTile::A_ELEMS); },
       k_begin, k_end, lds, acc);
   float* out = pair_mat(b, p, b.off_part) + (int64_t)s * b.r * b.r;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < CosTile::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
+    for (int y = 0; y < CosTile::XN; ++y) {
       const int64_t j = j0 + acc_col<CosTile>(y);
       if (j >= b.r) continue;
 #pragma unroll
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_fold(CosBatch b, int64_t o
   }
 }
 
-// 2c: X0 = C / ||C||_F.
+// 2c: X0 = C / ||C||_F, stored in bf16 (the first iterations use bf16 operands).
 __global__ __launch_bounds__(kThreads) void qg_cossim_init(CosBatch b) {
   const int p = blockIdx.x / b.nblk;
   const int blk = blockIdx.x - p * b.nblk;
@@ -246,51 +252,82 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_init(CosBatch b) {
   const float sq = pair_mat(b, p, b.off_norm)[0];
   const float inv = sq > 0.0f ? 1.0f / sqrtf(sq) : 0.0f;
   const float4 c = gload(reinterpret_cast<const float4*>(pair_mat(b, p, b.off_c) + e0));
-  gstore(reinterpret_cast<float4*>(pair_mat(b, p, b.off_x) + e0),
-         make_float4(c.x * inv, c.y * inv, c.z * inv, c.w * inv));
+  gstore(reinterpret_cast<uint2*>(pair_bf(b, p, b.off_xb0) + e0),
+         make_uint2(pack_bf16x2(c.x * inv, c.y * inv), pack_bf16x2(c.z * inv, c.w * inv)));
 }
 
 // ---------------------------------------------------- 3: Newton-Schulz products ---
 
 // TA: Y = beta * (M^T M) + alpha * E      (M at off_m; E at off_e, skipped when alpha == 0)
 // !TA: Y = alpha * E + beta * (M Bop)     (Bop at off_bop)
-template <bool TA, int PARTS>
+// IN_BF16: M, Bop and E are stored in bf16 (then PARTS == 1); otherwise in fp32, split into
+// hi/lo bf16 parts on the way into LDS when PARTS == 2. OUT_BF16: Y is rounded to bf16.
+template <bool TA, int PARTS, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_m,
                                                       int64_t off_bop, int64_t off_e,
                                                       int64_t off_y, float alpha, float beta) {
+  static_assert(!IN_BF16 || PARTS == 1, "bf16 operands have no low part");
   constexpr int STAGE = CosTile::STAGE > NsTileNN::STAGE ? CosTile::STAGE : NsTileNN::STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PARTS * STAGE];
-  const int per_pair = b.tiles * b.tiles;
-  const int p = blockIdx.x / per_pair;
-  const int rem = blockIdx.x - p * per_pair;
-  const int ti = rem / b.tiles, tj = rem - ti * b.tiles;
+  // TA products are symmetric: only tiles with ti <= tj are computed, each written to both
+  // of its mirror positions.
+  const int per_pair = TA ? b.tiles * (b.tiles + 1) / 2 : b.tiles * b.tiles;
+  // consecutive blocks (one pair's tiles) share an XCD and its L2
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = blk / per_pair;
+  int rem = blk - p * per_pair;
+  int ti, tj;
+  if constexpr (TA) {
+    ti = 0;
+    while (rem >= b.tiles - ti) {
+      rem -= b.tiles - ti;
+      ++ti;
+    }
+    tj = ti + rem;
+  } else {
+    ti = rem / b.tiles;
+    tj = rem - ti * b.tiles;
+  }
   const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int r = b.r;
-  const float* M = pair_mat(b, p, off_m);
-  const float* E = pair_mat(b, p, off_e);
-  float* Y = pair_mat(b, p, off_y);
-  f32x16 acc[2][2];
-  if constexpr (TA) {
-    using T = CosTile;
-    StageF32K<128, T::BK, PARTS, T::STAGE> sa(M, r, r, r, i0);
-    StageF32K<128, T::BK, PARTS, T::STAGE> sb(M, r, r, r, j0);
-    gemm_kloop<T, PARTS>(
-        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
-        acc);
+  f32x16 acc[CosTile::XM][CosTile::XN];
+  if constexpr (IN_BF16) {
+    // short K loop over L2-resident operands: four stages in flight
+    constexpr int D = 4;
+    const uint16_t* M = pair_bf(b, p, off_m);
+    if constexpr (TA) {
+      StageBf16K<CosTile::BM, CosTile::BK, true, D> sa(M, r, r, r, r, i0);
+      StageBf16K<CosTile::BM, CosTile::BK, true, D> sb(M, r, r, r, r, j0);
+      gemm_kloop_ring<CosTile, D>(sa, sb, 0, r, lds, acc);
+    } else {
+      StageBf16C<NsTileNN::BM, NsTileNN::BK, D> sa(M, r, r, i0);
+      StageBf16K<NsTileNN::BN, NsTileNN::BK, true, D> sb(pair_bf(b, p, off_bop), r, r, r, r, j0);
+      gemm_kloop_ring<NsTileNN, D>(sa, sb, 0, r, lds, acc);
+    }
   } else {
-    using T = NsTileNN;
-    StageF32C<128, T::BK, PARTS, T::STAGE> sa(M, r, r, i0);
-    StageF32K<128, T::BK, PARTS, T::STAGE> sb(pair_mat(b, p, off_bop), r, r, r, j0);
-    gemm_kloop<T, PARTS>(
-        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r, lds,
-        acc);
+    const float* M = pair_mat(b, p, off_m);
+    if constexpr (TA) {
+      using T = CosTile;
+      StageF32K<T::BM, T::BK, PARTS, T::STAGE> sa(M, r, r, r, i0);
+      StageF32K<T::BN, T::BK, PARTS, T::STAGE> sb(M, r, r, r, j0);
+      gemm_kloop<T, PARTS>(
+          sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+          [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r,
+          lds, acc);
+    } else {
+      using T = NsTileNN;
+      StageF32C<T::BM, T::BK, PARTS, T::STAGE> sa(M, r, r, i0);
+      StageF32K<T::BN, T::BK, PARTS, T::STAGE> sb(pair_mat(b, p, off_bop), r, r, r, j0);
+      gemm_kloop<T, PARTS>(
+          sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+          [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, r,
+          lds, acc);
+    }
   }
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < CosTile::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
+    for (int y = 0; y < CosTile::XN; ++y) {
       const int64_t j = j0 + acc_col<CosTile>(y);
       if (j >= r) continue;
 #pragma unroll
@@ -298,8 +335,18 @@ __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_m
         const int64_t i = i0 + acc_row<CosTile>(x, v);
         if (i >= r) continue;
         float out = beta * acc[x][y][v];
-        if (alpha != 0.0f) out += alpha * gload(E + i * r + j);
-        gstore(Y + i * r + j, out);
+        if (alpha != 0.0f) {
+          const float e = IN_BF16 ? bf16_to_f32(gload(pair_bf(b, p, off_e) + i * r + j))
+                                  : gload(pair_mat(b, p, off_e) + i * r + j);
+          out += alpha * e;
+        }
+        if constexpr (OUT_BF16) {
+          gstore(pair_bf(b, p, off_y) + i * r + j, to_bf16(out));
+          if (TA && ti != tj) gstore(pair_bf(b, p, off_y) + j * r + i, to_bf16(out));
+        } else {
+          gstore(pair_mat(b, p, off_y) + i * r + j, out);
+          if (TA && ti != tj) gstore(pair_mat(b, p, off_y) + j * r + i, out);
+        }
       }
     }
 }
@@ -308,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void qg_ns_gemm(CosBatch b, int64_t off_m
 
 // Per-block partial sums of the elementwise product of two r x r matrices of each pair
 // (trace(X^T Y)); sum of squares when X == Y.
+template <bool BF16>
 __global__ __launch_bounds__(kThreads) void qg_cossim_dot(CosBatch b, int64_t off_x,
                                                          int64_t off_y) {
   __shared__ float red[kThreads];
@@ -317,8 +365,18 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_dot(CosBatch b, int64_t of
   const int64_t e0 = ((int64_t)blk * kThreads + threadIdx.x) * 4;
   float acc = 0.0f;
   if (e0 < n2) {
-    const float4 x = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_x) + e0));
-    const float4 c = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_y) + e0));
+    float4 x, c;
+    if constexpr (BF16) {
+      const uint2 xb = gload(reinterpret_cast<const uint2*>(pair_bf(b, p, off_x) + e0));
+      const uint2 cb = gload(reinterpret_cast<const uint2*>(pair_bf(b, p, off_y) + e0));
+      x = make_float4(bf16_to_f32(xb.x & 0xFFFFu), bf16_to_f32(xb.x >> 16),
+                      bf16_to_f32(xb.y & 0xFFFFu), bf16_to_f32(xb.y >> 16));
+      c = make_float4(bf16_to_f32(cb.x & 0xFFFFu), bf16_to_f32(cb.x >> 16),
+                      bf16_to_f32(cb.y & 0xFFFFu), bf16_to_f32(cb.y >> 16));
+    } else {
+      x = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_x) + e0));
+      c = gload(reinterpret_cast<const float4*>(pair_mat(b, p, off_y) + e0));
+    }
     acc = x.x * c.x + x.y * c.y + x.z * c.z + x.w * c.w;
   }
   red[threadIdx.x] = acc;
@@ -330,8 +388,8 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_dot(CosBatch b, int64_t of
   if (threadIdx.x == 0) pair_mat(b, p, b.off_blk)[blk] = red[0];
 }
 
-// X *= s and A *= s^2 with s = ||A||_F^(-1/2) (A = X^T X): afterwards the singular values of
-// X are s_i / (sum_j s_j^4)^(1/4) <= 1.
+// X *= s and A *= s^2 with s = ||A||_F^(-1/2) (A = X^T X; both in bf16): afterwards the
+// singular values of X are s_i / (sum_j s_j^4)^(1/4) <= 1.
 __global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
   const int p = blockIdx.x / b.nblk;
   const int blk = blockIdx.x - p * b.nblk;
@@ -341,11 +399,14 @@ __global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
   const float sq = pair_mat(b, p, b.off_norm)[1];   // ||A||_F^2
   const float s = sq > 0.0f ? 1.0f / sqrtf(sqrtf(sq)) : 0.0f;
   const float s2 = s * s;
-  float4* X = reinterpret_cast<float4*>(pair_mat(b, p, b.off_x) + e0);
-  float4* A = reinterpret_cast<float4*>(pair_mat(b, p, b.off_a) + e0);
-  const float4 x = gload(X), a = gload(A);
-  gstore(X, make_float4(x.x * s, x.y * s, x.z * s, x.w * s));
-  gstore(A, make_float4(a.x * s2, a.y * s2, a.z * s2, a.w * s2));
+  uint2* X = reinterpret_cast<uint2*>(pair_bf(b, p, b.off_xb0) + e0);
+  uint2* A = reinterpret_cast<uint2*>(pair_bf(b, p, b.off_ab) + e0);
+  const uint2 x = gload(X), a = gload(A);
+  gstore(X, make_uint2(pack_bf16x2(bf16_to_f32(x.x & 0xFFFFu) * s, bf16_to_f32(x.x >> 16) * s),
+                       pack_bf16x2(bf16_to_f32(x.y & 0xFFFFu) * s, bf16_to_f32(x.y >> 16) * s)));
+  gstore(A,
+         make_uint2(pack_bf16x2(bf16_to_f32(a.x & 0xFFFFu) * s2, bf16_to_f32(a.x >> 16) * s2),
+                    pack_bf16x2(bf16_to_f32(a.y & 0xFFFFu) * s2, bf16_to_f32(a.y >> 16) * s2)));
 }
 
 // ------------------------------------------------------------------------ driver ---
@@ -360,47 +421,59 @@ hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
   hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b, b.off_norm, 0.0f,
                      (float*)nullptr);
   hipLaunchKernelGGL(qg_cossim_init, dim3(eblocks), dim3(kThreads), 0, s, b);
-  const int nsb = b.count * b.tiles * b.tiles;
-  // A = X0^T X0 and the rescaling by ||A||_F^(-1/2)
-  hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, b.off_x,
-                     int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
-  hipLaunchKernelGGL(qg_cossim_dot, dim3(eblocks), dim3(kThreads), 0, s, b, b.off_a, b.off_a);
-  hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b,
+  const dim3 nsb(b.count * b.tiles * b.tiles), thr(kThreads);
+  const dim3 nsy(b.count * b.tiles * (b.tiles + 1) / 2);   // symmetric products
+  const int64_t z = 0;
+  // bf16 phase: X in xb0 / xb1, A and B in bf16. A = X0^T X0, then the rescaling.
+  hipLaunchKernelGGL((qg_ns_gemm<true, 1, true, true>), nsy, thr, 0, s, b, b.off_xb0, z,
+                     b.off_ab, b.off_ab, 0.0f, 1.0f);
+  hipLaunchKernelGGL(qg_cossim_dot<true>, dim3(eblocks), thr, 0, s, b, b.off_ab, b.off_ab);
+  hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), thr, 0, s, b,
                      b.off_norm + (int64_t)sizeof(float), 0.0f, (float*)nullptr);
-  hipLaunchKernelGGL(qg_ns_rescale, dim3(eblocks), dim3(kThreads), 0, s, b);
-  int64_t x = b.off_x, xn = b.off_xn;
+  hipLaunchKernelGGL(qg_ns_rescale, dim3(eblocks), thr, 0, s, b);
+  int64_t x = b.off_xb0, xn = b.off_xb1;
   for (int it = 0; it < b.iters_quintic; ++it) {
     if (it > 0)
-      hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
-                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
+      hipLaunchKernelGGL((qg_ns_gemm<true, 1, true, true>), nsy, thr, 0, s, b, x, z, b.off_ab,
+                         b.off_ab, 0.0f, 1.0f);
     // B = b A + c A^2 (A is symmetric: A^2 = A^T A), then X <- a X + X B
-    hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, b.off_a,
-                       int64_t(0), b.off_a, b.off_b, kQb, kQc);
-    hipLaunchKernelGGL((qg_ns_gemm<false, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x, b.off_b,
-                       x, xn, kQa, 1.0f);
+    hipLaunchKernelGGL((qg_ns_gemm<true, 1, true, true>), nsy, thr, 0, s, b, b.off_ab, z,
+                       b.off_ab, b.off_bb, kQb, kQc);
+    hipLaunchKernelGGL((qg_ns_gemm<false, 1, true, true>), nsb, thr, 0, s, b, x, b.off_bb, x,
+                       xn, kQa, 1.0f);
     const int64_t t = x;
     x = xn;
     xn = t;
   }
-  for (int it = 0; it < b.iters_cubic_bf16 + b.iters_cubic_split; ++it) {
-    if (it < b.iters_cubic_bf16) {
-      hipLaunchKernelGGL((qg_ns_gemm<true, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
-                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
-      hipLaunchKernelGGL((qg_ns_gemm<false, 1>), dim3(nsb), dim3(kThreads), 0, s, b, x,
-                         b.off_a, x, xn, 1.5f, -0.5f);
+  // cubic steps with bf16 operands; the last one writes X in fp32 for the split phase
+  for (int it = 0; it < b.iters_cubic_bf16; ++it) {
+    hipLaunchKernelGGL((qg_ns_gemm<true, 1, true, true>), nsy, thr, 0, s, b, x, z, b.off_ab,
+                       b.off_ab, 0.0f, 1.0f);
+    if (it + 1 < b.iters_cubic_bf16) {
+      hipLaunchKernelGGL((qg_ns_gemm<false, 1, true, true>), nsb, thr, 0, s, b, x, b.off_ab, x,
+                         xn, 1.5f, -0.5f);
+      const int64_t t = x;
+      x = xn;
+      xn = t;
     } else {
-      hipLaunchKernelGGL((qg_ns_gemm<true, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x,
-                         int64_t(0), b.off_a, b.off_a, 0.0f, 1.0f);
-      hipLaunchKernelGGL((qg_ns_gemm<false, 2>), dim3(nsb), dim3(kThreads), 0, s, b, x,
-                         b.off_a, x, xn, 1.5f, -0.5f);
+      hipLaunchKernelGGL((qg_ns_gemm<false, 1, true, false>), nsb, thr, 0, s, b, x, b.off_ab,
+                         x, b.off_x, 1.5f, -0.5f);
     }
+  }
+  // split phase in fp32
+  x = b.off_x;
+  xn = b.off_xn;
+  for (int it = 0; it < b.iters_cubic_split; ++it) {
+    hipLaunchKernelGGL((qg_ns_gemm<true, 2, false, false>), nsy, thr, 0, s, b, x, z, b.off_a,
+                       b.off_a, 0.0f, 1.0f);
+    hipLaunchKernelGGL((qg_ns_gemm<false, 2, false, false>), nsb, thr, 0, s, b, x, b.off_a, x,
+                       xn, 1.5f, -0.5f);
     const int64_t t = x;
     x = xn;
     xn = t;
   }
-  hipLaunchKernelGGL(qg_cossim_dot, dim3(eblocks), dim3(kThreads), 0, s, b, x, b.off_c);
-  hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b, (int64_t)0,
-                     1.0f / (float)b.r, out);
+  hipLaunchKernelGGL(qg_cossim_dot<false>, dim3(eblocks), thr, 0, s, b, x, b.off_c);
+  hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), thr, 0, s, b, z, 1.0f / (float)b.r, out);
   return hipGetLastError();
 }
 

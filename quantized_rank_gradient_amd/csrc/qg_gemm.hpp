@@ -21,6 +21,8 @@
 //     and k0+4 .. k0+7 (h = 1) of column c0 + l % 32.
 #pragma once
 
+#include <utility>
+
 #include "qg_device.hpp"
 
 namespace qg {
@@ -69,7 +71,7 @@ __device__ __forceinline__ int kc_off(int row, int chunk) {
 // starts at the stage's first row and ends at k_end, so rows past the K range read as zero
 // without a per-lane test and the per-lane offsets stay fixed for the whole loop. Otherwise
 // elements are read one by one with full bounds tests.
-template <int W, int BK, bool VEC>
+template <int W, int BK, bool VEC, int SETS = 1>
 struct StageBf16K {
   static constexpr int CPR = W / 8;                    // chunks per row
   static constexpr int NC = BK * CPR / kThreads;       // chunks per thread
@@ -81,7 +83,7 @@ struct StageBf16K {
   uint32_t ld, k_end, c_end;
   int c0;
   uint32_t vo[NC];   // byte offset of chunk u from the stage's first row; kOOB off the tile
-  uint4 v[NC];
+  uint4 v[SETS][NC];   // SETS stages in flight (see gemm_kloop_ring)
 
   __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t rows, int64_t k_end_,
                         int64_t c_end_, int c0_)
@@ -93,13 +95,14 @@ struct StageBf16K {
       vo[u] = c < c_end ? ((threadIdx.x / CPR + u * RPU) * ld + c) * 2 : kOOB;
   }
 
+  template <int S = 0>
   __device__ __forceinline__ void load(int64_t k0_) {
     const uint32_t k0 = (uint32_t)k0_;
     if constexpr (VEC) {
       const uint32_t kb = k0 < k_end ? k0 : k_end;
       const rsrc_t st = make_rsrc(src + (size_t)kb * ld, (k_end - kb) * ld * 2);
 #pragma unroll
-      for (int u = 0; u < NC; ++u) v[u] = bload128(st, vo[u]);
+      for (int u = 0; u < NC; ++u) v[S][u] = bload128(st, vo[u]);
     } else {
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
@@ -112,17 +115,17 @@ struct StageBf16K {
           const uint32_t off = (k < k_end && c + e < c_end) ? (k * ld + c + e) * 2 : kOOB;
           w[e >> 1] |= bload16(rs, off) << (16 * (e & 1));
         }
-        v[u] = make_uint4(w[0], w[1], w[2], w[3]);
+        v[S][u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }
 
-  template <int PITCH>
+  template <int PITCH, int S = 0>
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v[u];
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = v[S][u];
     }
   }
 };
@@ -186,7 +189,7 @@ struct StageInt4K {
 // bf16 source [c][k] (row pitch ld = the K extent, ld % 8 == 0, c_end rows) -> K-contiguous
 // LDS tile [c][k]. Each stage reads through a buffer resource starting at column k0; rows past
 // c_end fall outside it. Only a last, partial stage (ld % BK != 0) tests columns per lane.
-template <int W, int BK>
+template <int W, int BK, int SETS = 1>
 struct StageBf16C {
   static constexpr int CPR = BK / 8;
   static constexpr int NC = W * CPR / kThreads;
@@ -197,7 +200,7 @@ struct StageBf16C {
   uint32_t ld, c_end, kk;
   int c0;
   uint32_t vo[NC];
-  uint4 v[NC];
+  uint4 v[SETS][NC];   // SETS stages in flight (see gemm_kloop_ring)
 
   __device__ StageBf16C(const uint16_t* s, int64_t ld_, int64_t c_end_, int c0_)
       : src(s), ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
@@ -209,25 +212,26 @@ struct StageBf16C {
     }
   }
 
+  template <int S = 0>
   __device__ __forceinline__ void load(int64_t k0_) {
     const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
     const rsrc_t st = make_rsrc(src + k0, (c_end * ld - k0) * 2);
     if (k0 + BK <= ld) {
 #pragma unroll
-      for (int u = 0; u < NC; ++u) v[u] = bload128(st, vo[u]);
+      for (int u = 0; u < NC; ++u) v[S][u] = bload128(st, vo[u]);
     } else {
 #pragma unroll
-      for (int u = 0; u < NC; ++u) v[u] = bload128(st, k0 + kk < ld ? vo[u] : kOOB);
+      for (int u = 0; u < NC; ++u) v[S][u] = bload128(st, k0 + kk < ld ? vo[u] : kOOB);
     }
   }
 
-  template <int PITCH>
+  template <int PITCH, int S = 0>
   __device__ __forceinline__ void store(uint16_t* lds) const {
     static_assert(PITCH == 32 && CPR == 4, "K-contiguous tiles take 32-element rows");
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + kc_off(q / CPR, q % CPR)) = v[u];
+      *reinterpret_cast<uint4*>(lds + kc_off(q / CPR, q % CPR)) = v[S][u];
     }
   }
 };
@@ -336,6 +340,56 @@ __device__ __forceinline__ void gemm_kloop(SA& sa, SB& sb, StoreA store_a, Store
   }
   mfma_stage<T, PARTS>(lds + ((nk - 1) & 1) * STAGE, acc);
   __syncthreads();
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time unrolled).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The same product for latency-bound cases (short K loops over operands in L2): the stagers
+// hold D register sets (D even), and the loads of stage s + D are issued while stage s is
+// multiplied, so D stages are in flight. Stages past k_end read as zero; the loop runs a
+// whole number of D-stage rounds.
+template <class T, int D, class SA, class SB>
+__device__ __forceinline__ void gemm_kloop_ring(SA& sa, SB& sb, int64_t k_begin, int64_t k_end,
+                                                uint16_t* lds, f32x16 (&acc)[T::XM][T::XN]) {
+  static_assert(D % 2 == 0, "stage s sits in LDS buffer s % 2");
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  if (k_end <= k_begin) return;
+  const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
+  static_for<D>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    sa.template load<d>(k_begin + (int64_t)d * T::BK);
+    sb.template load<d>(k_begin + (int64_t)d * T::BK);
+  });
+  sa.template store<T::A_PITCH, 0>(lds);
+  sb.template store<T::B_PITCH, 0>(lds + T::A_ELEMS);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += D) {
+    static_for<D>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      const int64_t kn = k_begin + (int64_t)(kt + d + D) * T::BK;
+      sa.template load<d>(kn);
+      sb.template load<d>(kn);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_stage<T, 1>(lds + (d & 1) * T::STAGE, acc);
+      uint16_t* nxt = lds + ((d + 1) & 1) * T::STAGE;
+      sa.template store<T::A_PITCH, (d + 1) % D>(nxt);
+      sb.template store<T::B_PITCH, (d + 1) % D>(nxt + T::A_ELEMS);
+      __syncthreads();
+    });
+  }
 }
 
 // Output coordinates of accumulator element v of block (x, y) for this lane, relative to the

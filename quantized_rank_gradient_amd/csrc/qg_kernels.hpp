@@ -7,6 +7,9 @@ namespace qg {
 
 // A batch of projection pairs for the similarity test (same rank r, any row count m).
 constexpr int kCosMaxPairs = 32;
+// Output tile edge of the similarity kernels: small tiles, so that the short K loops of the
+// r x r products run with several workgroups per CU.
+constexpr int kCosTile = 64;
 
 struct CosPair {
   const uint8_t* qa;   // P_new INT4 codes
@@ -24,12 +27,13 @@ struct CosBatch {
   char* ws;              // workspace base; pair p owns [p * pair_stride, (p+1) * pair_stride)
   int64_t pair_stride;
   int64_t off_part;      // split x r x r partial sums of C
-  int64_t off_c, off_x, off_xn, off_a, off_b;   // r x r fp32 matrices
+  int64_t off_c, off_x, off_xn, off_a;        // r x r fp32 matrices
+  int64_t off_xb0, off_xb1, off_ab, off_bb;   // r x r bf16 matrices
   int64_t off_blk;       // per-block partial sums
   int64_t off_norm;      // [0]: squared Frobenius norm of C, [1]: of X0^T X0
   int count, r, tiles, nblk;
   int iters_quintic;     // Newton-Schulz iterations lifting small singular values (bf16)
-  int iters_cubic_bf16;  // then cubic iterations with bf16 operands
+  int iters_cubic_bf16;  // then cubic iterations with bf16 operands (at least one)
   int iters_cubic_split; // and with hi/lo split operands
 };
 

@@ -28,7 +28,6 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 bool finite(float x) { return std::isfinite(x); }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-constexpr int kTile = 128;   // output tile edge of the similarity kernels
 constexpr int kK = 32;       // K per stage of the MFMA kernels
 constexpr int kKSlab = 64;   // split-K slab granularity: whole K stages of both tile sizes
 
@@ -50,7 +49,6 @@ qg_status check_shape(int64_t m, int64_t n, int64_t r) {
   if (m < 1 || n < 1 || r < 1 || m > kMaxDim || n > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
   if (r > m || r % 8 != 0) return QG_ERR_SHAPE;
   if (m * n > kMaxElems || r * n > kMaxElems) return QG_ERR_SHAPE;
-  if (cdiv(m, kTile) * cdiv(n, kTile) > kMaxDim / 2) return QG_ERR_SHAPE;
   return QG_OK;
 }
 
@@ -426,16 +424,19 @@ namespace {
 // Newton-Schulz schedule of the similarity test: quintic iterations that lift small singular
 // values, then cubic ones that converge them to 1 (bf16 operands, then hi/lo split operands).
 constexpr int kNsQuintic = 7;
-constexpr int kNsCubicBf16 = 3;
-constexpr int kNsCubicSplit = 2;
+constexpr int kNsCubicBf16 = 4;
+constexpr int kNsCubicSplit = 1;
+
+static_assert(kNsCubicBf16 >= 1, "the last bf16 step hands X over in fp32");
 
 struct CosLayout {
   int split, tiles, nblk;
-  int64_t off_part, off_c, off_x, off_xn, off_a, off_b, off_blk, off_norm, stride;
+  int64_t off_part, off_c, off_x, off_xn, off_a, off_xb0, off_xb1, off_ab, off_bb, off_blk,
+      off_norm, stride;
 };
 CosLayout cos_layout(int64_t r) {
   CosLayout c;
-  c.tiles = (int)cdiv(r, kTile);
+  c.tiles = (int)cdiv(r, qg::kCosTile);
   c.split = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(64, (int64_t)c.tiles * c.tiles)));
   const int64_t n2 = r * r;
   c.nblk = (int)cdiv(n2, (int64_t)qg::kThreads * 4);
@@ -445,8 +446,12 @@ CosLayout cos_layout(int64_t r) {
   c.off_x = c.off_c + mat;
   c.off_xn = c.off_x + mat;
   c.off_a = c.off_xn + mat;
-  c.off_b = c.off_a + mat;
-  c.off_blk = c.off_b + mat;
+  const int64_t matb = round_up(n2 * 2, 256);
+  c.off_xb0 = c.off_a + mat;
+  c.off_xb1 = c.off_xb0 + matb;
+  c.off_ab = c.off_xb1 + matb;
+  c.off_bb = c.off_ab + matb;
+  c.off_blk = c.off_bb + matb;
   c.off_norm = c.off_blk + round_up((int64_t)c.nblk * 4, 256);
   c.stride = c.off_norm + 256;
   return c;
@@ -510,7 +515,10 @@ extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P
     b.off_x = c.off_x;
     b.off_xn = c.off_xn;
     b.off_a = c.off_a;
-    b.off_b = c.off_b;
+    b.off_xb0 = c.off_xb0;
+    b.off_xb1 = c.off_xb1;
+    b.off_ab = c.off_ab;
+    b.off_bb = c.off_bb;
     b.off_blk = c.off_blk;
     b.off_norm = c.off_norm;
     b.iters_quintic = kNsQuintic;
