@@ -31,6 +31,8 @@ struct LayerDev {
   int64_t rpitch;      // elements between split slabs of Rpart
   uint32_t layer_id;
   int32_t split;       // K-splits of the projection
+  int32_t fuse_adam;   // 1: one split and n % 256 == 0, so the projection kernel runs Adam
+                       // on its tile rows (no R partials, no Adam launch for this layer)
   int32_t kslab;       // rows of G per split (multiple of the K tile)
   int32_t p_tiles_i;   // projection tiles along r
   int32_t p_tiles_j;   // projection tiles along n
@@ -218,6 +220,12 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+// Maximum over each aligned group of 16 lanes.
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 16));
   return v;
 }
 

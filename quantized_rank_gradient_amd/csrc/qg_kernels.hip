@@ -35,116 +35,43 @@ __global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
   bstore128(ro, in ? e * 2 : kOOB, dequant8(w, sc));
 }
 
-// ======================================================================== projection ===
-
-// Tile shapes: rank above 128 takes 256 x 256 tiles with K stages of 64 (each wave a 128 x 128
-// block of 16 MFMA accumulators); rank up to 128 takes 128 (all of r) x 256 with K stages of 32.
-// Both operands are K-major in memory (P is [k][i], G is [k][j]).
-using ProjBig = Tile<256, 256, 64, 2, 2, true, true>;
-using ProjSmall = Tile<128, 256, 32, 2, 2, true, true>;
-
-// VEC: rows of G are a multiple of 8 elements (16-byte chunk loads).
-template <class T, bool VEC>
-__device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& L, int local,
-                                             uint16_t* lds) {
-  // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
-  // columns are neighbours (and, after the renumbering, on the same XCD).
-  const int ti = local % L.p_tiles_i;
-  const int rest = local / L.p_tiles_i;
-  const int tj = rest % L.p_tiles_j;
-  const int s = rest / L.p_tiles_j;
-  const int i0 = ti * T::BM, j0 = tj * T::BN;
-  const int64_t k_begin = (int64_t)s * L.kslab;
-  const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
-
-  // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
-  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
-  StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
-  StageBf16K<T::BN, T::BK, VEC> sb(L.G, L.n, L.m, k_end, L.n, j0);
-  f32x16 acc[T::XM][T::XN];
-  gemm_kloop<T, 1>(
-      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
-      k_end, lds, acc);
-
-  // Partial sums of this K-split; out-of-range rows and columns are dropped by the buffer.
-  const rsrc_t ro = make_rsrc(a.ws + L.off_r + (int64_t)s * L.rpitch * 4,
-                              (uint32_t)(L.r * L.n * 4));
-  const uint32_t n = (uint32_t)L.n, r = (uint32_t)L.r;
-#pragma unroll
-  for (int x = 0; x < T::XM; ++x)
-#pragma unroll
-    for (int y = 0; y < T::XN; ++y) {
-      const uint32_t j = j0 + acc_col<T>(y);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t i = i0 + acc_row<T>(x, v);
-        bstoref(ro, (i < r && j < n) ? (i * n + j) * 4 : kOOB, acc[x][y][v]);
-      }
-    }
-}
-
-// The smaller tile is held to 256 registers per lane so that two waves share each SIMD.
-template <class T>
-__global__ __launch_bounds__(kThreads, T::BM * T::BN < 256 * 256 ? 2 : 1) void qg_project(
-    StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
-  int local;
-  const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
-  if (L.n % 8 == 0)
-    project_tile<T, true>(a, L, local, lds);
-  else
-    project_tile<T, false>(a, L, local, lds);
-}
-
 // ============================================================================== Adam ===
 // One wave per group of 256 flat elements of the r x n moments; lane l owns elements
-// 4l .. 4l+3 of the group.
+// 4l .. 4l+3 of the group. adam_group takes the lane's four entries of R (its fp32 sums)
+// and does the rest: moments from their INT8 codes, the update, N~, absmax requantization.
 
-__global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
-  int local;
-  const LayerDev L = fetch_layer(a, KADAM, blockIdx.x, local);
-  const int lane = threadIdx.x & 63;
+// The lane's four M and V codes of group g (packed little-endian; zero past the end).
+__device__ __forceinline__ void adam_codes(const LayerDev& L, int64_t g, int lane,
+                                           uint32_t& wm, uint32_t& wv) {
   const int64_t numel = L.r * L.n;
-  const int64_t ngroups = (numel + kGroup - 1) / kGroup;
-  const int64_t g = (int64_t)local * (kThreads / 64) + (threadIdx.x >> 6);
-  if (g >= ngroups) return;
+  const int64_t e0 = g * kGroup + 4 * lane;
+  if (e0 + 4 <= numel) {
+    wm = gload(reinterpret_cast<const uint32_t*>(L.Mq + e0));
+    wv = gload(reinterpret_cast<const uint32_t*>(L.Vq + e0));
+  } else {
+    wm = wv = 0;
+    for (int t = 0; t < 4; ++t)
+      if (e0 + t < numel) {
+        wm |= (uint32_t)(uint8_t)gload(L.Mq + e0 + t) << (8 * t);
+        wv |= (uint32_t)(uint8_t)gload(L.Vq + e0 + t) << (8 * t);
+      }
+  }
+}
+
+// wm, wv: the lane's codes (adam_codes); ms, vs: the group's scales.
+__device__ __forceinline__ void adam_group(const StepArgs& a, const LayerDev& L, int64_t g,
+                                           int lane, const float (&R)[4], uint32_t wm,
+                                           uint32_t wv, float ms, float vs) {
+  const int64_t numel = L.r * L.n;
   const int64_t e0 = g * kGroup + 4 * lane;
   const bool full = e0 + 4 <= numel;
   uint16_t* Nb = reinterpret_cast<uint16_t*>(a.ws + L.off_n);
-
-  float R[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < L.split; ++s) {
-    const float* src = reinterpret_cast<const float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch + e0;
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
-    if (full) {
-      const float4 q = gload(reinterpret_cast<const float4*>(src));
-      p[0] = q.x; p[1] = q.y; p[2] = q.z; p[3] = q.w;
-    } else {
-      for (int t = 0; t < 4; ++t)
-        if (e0 + t < numel) p[t] = gload(src + t);
-    }
+  int8_t mq[4], vq[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) R[t] = (s == 0) ? p[t] : add_rn(R[t], p[t]);
+  for (int t = 0; t < 4; ++t) {
+    mq[t] = (int8_t)(wm >> (8 * t));
+    vq[t] = (int8_t)(wv >> (8 * t));
   }
-
-  int8_t mq[4] = {0, 0, 0, 0}, vq[4] = {0, 0, 0, 0};
-  if (full) {
-    const uint32_t wm = gload(reinterpret_cast<const uint32_t*>(L.Mq + e0));
-    const uint32_t wv = gload(reinterpret_cast<const uint32_t*>(L.Vq + e0));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      mq[t] = (int8_t)(wm >> (8 * t));
-      vq[t] = (int8_t)(wv >> (8 * t));
-    }
-  } else {
-    for (int t = 0; t < 4; ++t)
-      if (e0 + t < numel) {
-        mq[t] = gload(L.Mq + e0 + t);
-        vq[t] = gload(L.Vq + e0 + t);
-      }
-  }
-  const float ms = gload(L.Ms + g), vs = gload(L.Vs + g);
 
   float m1[4], v1[4], N[4];
   float am = 0.f, av = 0.f;
@@ -196,6 +123,214 @@ __global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
     gstore(L.Ms + g, sm);
     gstore(L.Vs + g, sv);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void qg_adam(StepArgs a) {
+  int local;
+  const LayerDev L = fetch_layer(a, KADAM, blockIdx.x, local);
+  const int lane = threadIdx.x & 63;
+  const int64_t numel = L.r * L.n;
+  const int64_t ngroups = (numel + kGroup - 1) / kGroup;
+  const int64_t g = (int64_t)local * (kThreads / 64) + (threadIdx.x >> 6);
+  if (g >= ngroups) return;
+  const int64_t e0 = g * kGroup + 4 * lane;
+  const bool full = e0 + 4 <= numel;
+  // R = the split-K partial sums, added in order
+  float R[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < L.split; ++s) {
+    const float* src = reinterpret_cast<const float*>(a.ws + L.off_r) + (int64_t)s * L.rpitch + e0;
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (full) {
+      const float4 q = gload(reinterpret_cast<const float4*>(src));
+      p[0] = q.x; p[1] = q.y; p[2] = q.z; p[3] = q.w;
+    } else {
+      for (int t = 0; t < 4; ++t)
+        if (e0 + t < numel) p[t] = gload(src + t);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) R[t] = (s == 0) ? p[t] : add_rn(R[t], p[t]);
+  }
+  uint32_t wm, wv;
+  adam_codes(L, g, lane, wm, wv);
+  adam_group(a, L, g, lane, R, wm, wv, gload(L.Ms + g), gload(L.Vs + g));
+}
+
+// Adam on one whole 256-element group by 16 lanes (the fused projection epilogue): lane l
+// of the group owns columns 64k + 4l .. 64k + 4l + 3 (k = 0..3) of the row. Same arithmetic
+// per element as adam_group; the group absmax is a max, so the lane layout does not change
+// the result. R holds the lane's 16 values (R[4k + t] for column 64k + 4l + t); cm / cv its
+// 4 words of M / V codes.
+__device__ __forceinline__ void adam_group16(const StepArgs& a, const LayerDev& L, int64_t g,
+                                             int l, const float (&R)[16],
+                                             const uint32_t (&cm)[4], const uint32_t (&cv)[4]) {
+  const int64_t e0 = g * kGroup + 4 * l;
+  uint16_t* Nb = reinterpret_cast<uint16_t*>(a.ws + L.off_n);
+  const float ms = gload(L.Ms + g), vs = gload(L.Vs + g);
+  // fresh moments and their group absmax first; the update is formed per 4-element run
+  // afterwards, so that only m1 and v1 stay live across the reduction
+  float m1[16], v1[16];
+  float am = 0.f, av = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float m0 = mul_rn((float)(int8_t)(cm[e >> 2] >> (8 * (e & 3))), ms);
+    const float v0 = mul_rn((float)(int8_t)(cv[e >> 2] >> (8 * (e & 3))), vs);
+    m1[e] = add_rn(mul_rn(a.beta1, m0), mul_rn(a.c1, R[e]));
+    v1[e] = add_rn(mul_rn(a.beta2, v0), mul_rn(a.c2, mul_rn(R[e], R[e])));
+    am = fmaxf(am, fabsf(m1[e]));
+    av = fmaxf(av, fabsf(v1[e]));
+  }
+  if (L.R_out) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      gstore(reinterpret_cast<float4*>(L.R_out + e0 + 64 * k),
+             make_float4(R[4 * k], R[4 * k + 1], R[4 * k + 2], R[4 * k + 3]));
+  }
+  am = max16(am);
+  av = max16(av);
+  const float sm = div_rn(am, 127.0f), sv = div_rn(av, 127.0f);
+  const float im = recip_or_zero(sm), iv = recip_or_zero(sv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t om = 0, ov = 0;
+    float N[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float mh = div_rn(m1[4 * k + t], a.bc1);
+      const float vh = div_rn(v1[4 * k + t], a.bc2);
+      N[t] = -div_rn(mul_rn(L.lr, mh), add_rn(sqrt_rn(vh), L.eps));
+      const int qm = (int)fminf(fmaxf(rintf(mul_rn(m1[4 * k + t], im)), -127.f), 127.f);
+      const int qv = (int)fminf(fmaxf(rintf(mul_rn(v1[4 * k + t], iv)), -127.f), 127.f);
+      om |= (uint32_t)(qm & 0xFF) << (8 * t);
+      ov |= (uint32_t)(qv & 0xFF) << (8 * t);
+    }
+    const int64_t e = e0 + 64 * k;
+    gstore(reinterpret_cast<uint32_t*>(L.Mq + e), om);
+    gstore(reinterpret_cast<uint32_t*>(L.Vq + e), ov);
+    gstore(reinterpret_cast<uint2*>(Nb + e),
+           make_uint2(pack_bf16x2(N[0], N[1]), pack_bf16x2(N[2], N[3])));
+  }
+  if (l == 0) {
+    gstore(L.Ms + g, sm);
+    gstore(L.Vs + g, sv);
+  }
+}
+
+// ======================================================================== projection ===
+
+// Tile: 128 rows of R (rank index) x 256 columns, K stages of 32, four waves of 64 x 128
+// (eight MFMA accumulator blocks each), two workgroups per CU. Both operands are K-major in
+// memory (P is [k][i], G is [k][j]).
+using ProjTile = Tile<128, 256, 32, 2, 2, true, true>;
+static_assert(ProjTile::BM == kProjTileM && ProjTile::BN == kProjTileN,
+              "host and device projection tiles agree");
+static_assert(ProjTile::BN == kGroup, "a tile row spans one Adam group when n % 256 == 0");
+
+// The fused Adam epilogue stages one 32-row chunk of both wave rows (64 rows x 256 columns,
+// fp32) in LDS; the row pitch is 8 (mod 16) words so that the two row halves a staging store
+// writes (rows R and R + 4) fall on disjoint banks.
+constexpr int kAdamPitch = ProjTile::BN + 8;
+constexpr int kAdamLdsElems = 2 * ProjTile::WM * 32 * kAdamPitch;   // fp32 = two bf16 slots
+constexpr int kProjLdsElems =
+    2 * ProjTile::STAGE > kAdamLdsElems ? 2 * ProjTile::STAGE : kAdamLdsElems;
+
+// VEC: rows of G are a multiple of 8 elements (16-byte chunk loads).
+template <class T, bool VEC>
+__device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& L, int local,
+                                             uint16_t* lds) {
+  // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
+  // columns are neighbours (and, after the renumbering, on the same XCD).
+  const int ti = local % L.p_tiles_i;
+  const int rest = local / L.p_tiles_i;
+  const int tj = rest % L.p_tiles_j;
+  const int s = rest / L.p_tiles_j;
+  const int i0 = ti * T::BM, j0 = tj * T::BN;
+  const int64_t k_begin = (int64_t)s * L.kslab;
+  const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
+
+  // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
+  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+  StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
+  StageBf16K<T::BN, T::BK, VEC> sb(L.G, L.n, L.m, k_end, L.n, j0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop<T, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
+      k_end, lds, acc);
+
+  if (L.fuse_adam) {
+    // One K split and rows made of whole 256-element groups: each tile row is one Adam group,
+    // complete in this workgroup, so Adam runs here instead of a separate pass over R.
+    // Chunk x holds rows 32x .. 32x+31 of both wave rows (tile rows wm*WTM + 32x + rr).
+    // Chunk x holds rows 32x .. 32x+31 of both wave rows (64 rows). Wave w takes rows
+    // 16w .. 16w+15 in four passes of four rows, 16 lanes per row (adam_group16).
+    float* E = reinterpret_cast<float*>(lds);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave_m<T>(), wn = wave_n<T>();
+    const int l16 = lane & 15;
+    const int64_t gpr = L.n / kGroup;   // groups per row of R
+    static_for<T::XM>([&](auto xc) {
+      constexpr int x = decltype(xc)::value;
+#pragma unroll
+      for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          E[(wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kAdamPitch + wn * T::WTN +
+            32 * y + (lane & 31)] = acc[x][y][v];
+      __syncthreads();
+#pragma unroll 1
+      for (int p = 0; p < 4; ++p) {
+        const int rc = 16 * wave + 4 * p + (lane >> 4);   // chunk row 0 .. 63
+        const uint32_t i = i0 + (rc >> 5) * T::WTM + 32 * x + (rc & 31);
+        if (i < (uint32_t)L.r) {
+          const int64_t g = (int64_t)i * gpr + j0 / kGroup;
+          const int64_t e0 = g * kGroup + 4 * l16;
+          uint32_t cm[4], cv[4];
+          float R[16];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            cm[k] = gload(reinterpret_cast<const uint32_t*>(L.Mq + e0 + 64 * k));
+            cv[k] = gload(reinterpret_cast<const uint32_t*>(L.Vq + e0 + 64 * k));
+            const float4 q =
+                *reinterpret_cast<const float4*>(E + rc * kAdamPitch + 64 * k + 4 * l16);
+            R[4 * k] = q.x;
+            R[4 * k + 1] = q.y;
+            R[4 * k + 2] = q.z;
+            R[4 * k + 3] = q.w;
+          }
+          adam_group16(a, L, g, l16, R, cm, cv);
+        }
+      }
+      __syncthreads();
+    });
+    return;
+  }
+
+  // Partial sums of this K-split; out-of-range rows and columns are dropped by the buffer.
+  const rsrc_t ro = make_rsrc(a.ws + L.off_r + (int64_t)s * L.rpitch * 4,
+                              (uint32_t)(L.r * L.n * 4));
+  const uint32_t n = (uint32_t)L.n, r = (uint32_t)L.r;
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y) {
+      const uint32_t j = j0 + acc_col<T>(y);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t i = i0 + acc_row<T>(x, v);
+        bstoref(ro, (i < r && j < n) ? (i * n + j) * 4 : kOOB, acc[x][y][v]);
+      }
+    }
+}
+
+// Held to 256 registers per lane so that two waves share each SIMD.
+__global__ __launch_bounds__(kThreads, 2) void qg_project(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kProjLdsElems];
+  int local;
+  const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
+  if (L.n % 8 == 0)
+    project_tile<ProjTile, true>(a, L, local, lds);
+  else
+    project_tile<ProjTile, false>(a, L, local, lds);
 }
 
 // ===================================================== back-projection + rounding ===
@@ -326,9 +461,6 @@ __device__ __forceinline__ void read_run(const float* E, int off, float (&S)[8])
 // P~ rows are K-contiguous ([i][k]); N~ is K-major ([k][j]).
 using BackBig = Tile<256, 128, 32, 2, 2, false, true>;
 using BackSmall = Tile<128, 128, 32, 2, 2, false, true>;
-static_assert(ProjBig::BM == kProjTileM(true) && ProjSmall::BM == kProjTileM(false) &&
-                  ProjBig::BN == kProjTileN && ProjSmall::BN == kProjTileN,
-              "host and device projection tiles agree");
 static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true) &&
                   BackSmall::BM == kBackTileM(false) && BackSmall::BN == kBackTileN(false),
               "host and device back-projection tiles agree");
@@ -492,11 +624,8 @@ __global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int
 
 // ==================================================================== launchers ===
 
-hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s) {
-  if (big)
-    hipLaunchKernelGGL(qg_project<ProjBig>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(qg_project<ProjSmall>, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(qg_project, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s) {

@@ -37,13 +37,13 @@ struct CosBatch {
   int iters_cubic_split; // and with hi/lo split operands
 };
 
-// Tile edges of the two configurations of each MFMA kernel ("big": rank above 128).
-constexpr int kProjTileM(bool big) { return big ? 256 : 128; }
+// Tile edges of the MFMA kernels (back-projection: "big" for rank above 128).
+constexpr int kProjTileM = 128;
 constexpr int kProjTileN = 256;
 constexpr int kBackTileM(bool big) { return big ? 256 : 128; }
 constexpr int kBackTileN(bool big) { return big ? 128 : 128; }
 
-hipError_t launch_project(const StepArgs& a, int grid, bool big, hipStream_t s);
+hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s);

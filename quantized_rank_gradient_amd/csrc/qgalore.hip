@@ -54,14 +54,17 @@ qg_status check_shape(int64_t m, int64_t n, int64_t r) {
 
 // Tile configuration of the MFMA kernels: the larger tiles once the rank exceeds 128.
 bool big_tiles(int64_t r) { return r > 128; }
-int64_t proj_tiles(int64_t n, int64_t r, bool big) {
-  return cdiv(r, qg::kProjTileM(big)) * cdiv(n, qg::kProjTileN);
+int64_t proj_tiles(int64_t n, int64_t r) {
+  return cdiv(r, qg::kProjTileM) * cdiv(n, qg::kProjTileN);
 }
+// With one K split and rows of whole 256-element groups, each projection tile row is a
+// complete Adam group and the projection kernel finishes Adam itself.
+bool fused_adam(int64_t n, int split) { return split == 1 && n % qg::kGroup == 0; }
 
 // K-splits of the projection R = P~^T G for one layer launched on its own: enough
 // workgroups to cover the chip, bounded so the fp32 partial sums stay small next to G.
 int choose_split(int64_t m, int64_t n, int64_t r) {
-  const int64_t tiles = proj_tiles(n, r, big_tiles(r));
+  const int64_t tiles = proj_tiles(n, r);
   const int64_t kchunks = cdiv(m, kKSlab);
   int64_t s = cdiv(512, tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, m / (8 * r)));
@@ -72,9 +75,9 @@ int choose_split(int64_t m, int64_t n, int64_t r) {
 }
 int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kKSlab), split) * kKSlab; }
 
-// Per-layer workspace: split-K partial sums of R (fp32), the bf16 update N~ (r x n) and the
-// bf16 dequantized projection P~ (m x r) that the projection kernel leaves for the
-// back-projection.
+// Per-layer workspace: split-K partial sums of R (fp32; absent when Adam is fused into the
+// projection), the bf16 update N~ (r x n) and the bf16 dequantized projection P~ (m x r)
+// that both MFMA kernels read.
 struct WsLayout {
   int64_t rpitch, off_r, off_n, off_p, bytes;
 };
@@ -82,7 +85,8 @@ WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base) {
   WsLayout w;
   w.rpitch = round_up(r * n, 64);
   w.off_r = base;
-  w.off_n = base + round_up((int64_t)split * w.rpitch * 4, 256);
+  const int64_t rbytes = fused_adam(n, split) ? 0 : (int64_t)split * w.rpitch * 4;
+  w.off_n = base + round_up(rbytes, 256);
   w.off_p = w.off_n + round_up(r * n * 2, 256);
   w.bytes = (w.off_p - base) + round_up(m * r * 2, 256);
   return w;
@@ -158,8 +162,9 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.off_p = w.off_p;
   L.layer_id = d->layer_id;
   L.split = split;
+  L.fuse_adam = fused_adam(d->n, split) ? 1 : 0;
   L.kslab = (int32_t)kslab_for(d->m, split);
-  L.p_tiles_i = (int32_t)cdiv(d->r, qg::kProjTileM(big));
+  L.p_tiles_i = (int32_t)cdiv(d->r, qg::kProjTileM);
   L.p_tiles_j = (int32_t)cdiv(d->n, qg::kProjTileN);
   L.b_tiles_i = (int32_t)cdiv(d->m, qg::kBackTileM(big));
   L.b_tiles_j = (int32_t)cdiv(d->n, qg::kBackTileN(big));
@@ -170,17 +175,19 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
 }
 
 int grid_project(const LayerDev& L) { return L.split * L.p_tiles_i * L.p_tiles_j; }
-int grid_adam(const LayerDev& L) { return (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4); }
+int grid_adam(const LayerDev& L) {
+  return L.fuse_adam ? 0 : (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4);
+}
 int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
 int grid_dequant(const LayerDev& L) { return (int)cdiv(L.m * L.r, qg::kThreads * 8); }
 
 qg_status launch_step(const StepArgs& a, const int grid[4], bool big, hipStream_t s) {
   hipError_t e = qg::launch_dequant(a, grid[3], s);
   if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
-  e = qg::launch_project(a, grid[0], big, s);
+  e = qg::launch_project(a, grid[0], s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
-  e = qg::launch_adam(a, grid[1], s);
-  if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
+  if (grid[1] > 0 && (e = qg::launch_adam(a, grid[1], s)) != hipSuccess)
+    return hip_fail(e, "Adam kernel launch");
   e = qg::launch_backproject(a, grid[2], big, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   return QG_OK;
@@ -273,8 +280,7 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   for (int32_t l = 0; l < count; ++l) rmax = std::max<int64_t>(rmax, layers[l].desc.r);
   const bool big = big_tiles(rmax);
   int64_t tiles = 0;
-  for (int32_t l = 0; l < count; ++l)
-    tiles += proj_tiles(layers[l].desc.n, layers[l].desc.r, big);
+  for (int32_t l = 0; l < count; ++l) tiles += proj_tiles(layers[l].desc.n, layers[l].desc.r);
   const bool grouped_fill = tiles >= 1024;
 
   qg_plan* p = new (std::nothrow) qg_plan();
@@ -309,12 +315,13 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   hipError_t e = hipGetDevice(&p->device);
   if (e == hipSuccess) e = hipMalloc(&p->d_table, sizeof(LayerDev) * count);
   for (int k = 0; k < 4 && e == hipSuccess; ++k)
-    e = hipMalloc(&p->d_map[k], sizeof(int32_t) * map[k].size());
+    e = hipMalloc(&p->d_map[k], sizeof(int32_t) * std::max<size_t>(1, map[k].size()));
   if (e == hipSuccess)
     e = hipMemcpy(p->d_table, p->layers.data(), sizeof(LayerDev) * count, hipMemcpyHostToDevice);
   for (int k = 0; k < 4 && e == hipSuccess; ++k)
-    e = hipMemcpy(p->d_map[k], map[k].data(), sizeof(int32_t) * map[k].size(),
-                  hipMemcpyHostToDevice);
+    if (!map[k].empty())
+      e = hipMemcpy(p->d_map[k], map[k].data(), sizeof(int32_t) * map[k].size(),
+                    hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     qgalore_plan_destroy(p);
     return hip_fail(e, "plan upload");
@@ -352,12 +359,13 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
-  e = qg::launch_project(a, p->grid[0], p->big, s);
+  e = qg::launch_project(a, p->grid[0], s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[1];
-  e = qg::launch_adam(a, p->grid[1], s);
-  if (e != hipSuccess) return hip_fail(e, "Adam kernel launch");
+  // layers whose Adam ran inside the projection kernel have no Adam workgroups
+  if (p->grid[1] > 0 && (e = qg::launch_adam(a, p->grid[1], s)) != hipSuccess)
+    return hip_fail(e, "Adam kernel launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
   e = qg::launch_backproject(a, p->grid[2], p->big, s);
