@@ -151,22 +151,32 @@ class Variant:
 KERNELS = ("qg_dequant", "qg_project", "qg_adam", "qg_backproject")
 
 
+def fused_adam(cfg):
+    """The grouped step runs Adam inside the projection kernel when every layer's rows are
+    whole 256-element groups (the 7B sets: n in {4096, 11008}) and the layer set fills the chip
+    with one K split per layer."""
+    return all(L.n % 256 == 0 for L in cfg.layers)
+
+
 def algorithmic(cfg, r):
     """FLOPs and bytes the method must do per step, split by the kernel that does them (in
     launch order: INT4 dequant of P, projection, Adam, back-projection + rounding). Bytes
     count each algorithmic input once and each output once: P (INT4 + fp32 scale per 256)
     once, G once, M and V (INT8 + scales) read and written, W (INT8) read and written with
     its scales read. Workspace round trips (R partials, N~, the bf16 copy of P~) are not
-    algorithmic and are not counted."""
+    algorithmic and are not counted. When Adam runs inside the projection kernel, its bytes
+    are that kernel's."""
     mn = sum(L.m * L.n for L in cfg.layers)
     mr = sum(L.m * r for L in cfg.layers)
     rn = sum(r * L.n for L in cfg.layers)
+    adam = 4.0 * rn + 4.0 * 4.0 * rn / 256.0          # M, V in and out + their scales
+    fused = fused_adam(cfg)
     flops = (0.0, 2.0 * r * mn, 0.0, 2.0 * r * mn)
-    nbytes = (0.5 * mr + mr / 64.0,                 # P codes + scales
-              2.0 * mn,                               # G (bf16)
-              4.0 * rn + 4.0 * 4.0 * rn / 256.0,      # M, V in and out + their scales
+    nbytes = (0.5 * mr + mr / 64.0,                   # P codes + scales
+              2.0 * mn + (adam if fused else 0.0),    # G (bf16) [+ Adam]
+              0.0 if fused else adam,
               2.0 * mn + mn / 64.0)                   # W in and out + W scales
-    return dict(mn=mn, flops=flops, bytes=nbytes)
+    return dict(mn=mn, flops=flops, bytes=nbytes, fused_adam=fused)
 
 
 def roofline(cfg, r, kms):
@@ -175,6 +185,9 @@ def roofline(cfg, r, kms):
     k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
     traffic = measured_traffic(cfg.key, names[k])
+    if k == 1 and a["fused_adam"]:
+        names = list(names)
+        names[1] = "qg_project (+ Adam)"
     intensity = a["flops"][k] / a["bytes"][k] if a["bytes"][k] else 0.0
     mfma_bound = intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
@@ -325,10 +338,13 @@ def main():
         ms, kms, tests = v.time_steps(args.steps, args.warmup)
         cs_ms = v.time_cossim()
         a = algorithmic(vcfg, r)
+        kernel_ms = {nm: round(t, 4) for nm, t in zip(KERNELS, kms)}
+        if a["fused_adam"]:
+            kernel_ms["qg_adam"] = "in qg_project"   # no separate launch
         res = dict(config=vcfg.key, rank=r, ms_per_step=round(ms, 4),
                    value=a["mn"] / (ms / 1e3),
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
-                   kernel_ms={nm: round(t, 4) for nm, t in zip(KERNELS, kms)},
+                   kernel_ms=kernel_ms,
                    optimizer_ms=round(sum(kms), 4),
                    refresh_tests_per_step=round(tests, 2),
                    cossim_ms=cs_ms,
