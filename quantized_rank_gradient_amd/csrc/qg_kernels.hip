@@ -459,7 +459,7 @@ __device__ __forceinline__ void read_run(const float* E, int off, float (&S)[8])
 }
 
 // P~ rows are K-contiguous ([i][k]); N~ is K-major ([k][j]).
-using BackBig = Tile<256, 128, 32, 2, 2, false, true>;
+using BackBig = Tile<128, 256, 32, 2, 2, false, true>;
 using BackSmall = Tile<128, 128, 32, 2, 2, false, true>;
 static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true) &&
                   BackSmall::BM == kBackTileM(false) && BackSmall::BN == kBackTileN(false),

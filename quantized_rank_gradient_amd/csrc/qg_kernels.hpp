@@ -40,8 +40,8 @@ struct CosBatch {
 // Tile edges of the MFMA kernels (back-projection: "big" for rank above 128).
 constexpr int kProjTileM = 128;
 constexpr int kProjTileN = 256;
-constexpr int kBackTileM(bool big) { return big ? 256 : 128; }
-constexpr int kBackTileN(bool big) { return big ? 128 : 128; }
+constexpr int kBackTileM(bool big) { return big ? 128 : 128; }
+constexpr int kBackTileN(bool big) { return big ? 256 : 128; }
 
 hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
