@@ -253,6 +253,35 @@ def copy_bandwidth(torch, gib=2.0, reps=5):
     return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1))
 
 
+def library_gemm_ms(torch, cfg, r, reps=20):
+    """torch (hipBLASLt) bf16 matmuls with the shapes of the two contractions, summed over
+    the layer set: R = P^T G with P^T stored contiguous, and P N (no fused epilogues). A
+    point of comparison for the MFMA kernels, not part of a step."""
+    by_shape = {}
+    for L in cfg.layers:
+        by_shape[(L.m, L.n)] = by_shape.get((L.m, L.n), 0) + 1
+    total = [0.0, 0.0]
+    for (m, n), count in by_shape.items():
+        P = torch.randn(m, r, device="cuda", dtype=torch.bfloat16)
+        PT = P.t().contiguous()
+        G = torch.randn(m, n, device="cuda", dtype=torch.bfloat16)
+        N = torch.randn(r, n, device="cuda", dtype=torch.bfloat16)
+        for k, fn in enumerate((lambda: torch.matmul(PT, G), lambda: torch.matmul(P, N))):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            total[k] += e0.elapsed_time(e1) / reps * count
+        del P, PT, G, N
+    torch.cuda.empty_cache()
+    return dict(projection_ms=round(total[0], 3), backprojection_ms=round(total[1], 3))
+
+
 def cpu_baseline(nlayers=7):
     """The oracle, as it stands, on the layers of block 0 (q, k, v, o, gate, up, down) at
     rank 1024: one full oracle step per layer."""
@@ -295,6 +324,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device copy timed for the achievable HBM rate (0: skip)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch bf16 matmuls of the same shapes (comparison only)")
     ap.add_argument("--fast-setup", action="store_true",
                     help="Gaussian stand-in projections instead of QR (profiling runs)")
     args = ap.parse_args()
@@ -349,6 +380,8 @@ def main():
                    refresh_tests_per_step=round(tests, 2),
                    cossim_ms=cs_ms,
                    roofline=roofline(vcfg, r, kms))
+        if args.library_gemm:
+            res["library_gemm"] = library_gemm_ms(torch, vcfg, r)
         log(json.dumps(res))
         results.append(res)
         v.plan.close()
@@ -389,6 +422,13 @@ def main():
                                                     "cossim_ms", "roofline")}
                      for r in results[1:]},
     }
+    line["variants"] = {
+        r["config"]: {**line["variants"][r["config"]],
+                      **({"library_gemm": r["library_gemm"]} if "library_gemm" in r else {})}
+        for r in results[1:]
+    }
+    if "library_gemm" in main_res:
+        line["library_gemm"] = main_res["library_gemm"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer ...")
         line["cpu_baseline"] = cpu_baseline()
