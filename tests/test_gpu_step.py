@@ -87,7 +87,7 @@ def test_step_matches_oracle(m, n, r, moments, t):
     before = st.copy()
     res = O.qgalore_step(st, G, t, WL.SR_SEED)
     out = gpu_step(Lt, t)
-    PAR.check_step(before, res, st, out)
+    PAR.check_step(before, res, st, out, t=t)
 
 
 def test_single256_ten_steps_each_from_the_oracle_state():
@@ -103,7 +103,7 @@ def test_single256_ten_steps_each_from_the_oracle_state():
         before = st.copy()
         res = O.qgalore_step(st, G, t, WL.SR_SEED)
         out = gpu_step(Lt, t)
-        flips += PAR.check_step(before, res, st, out)
+        flips += PAR.check_step(before, res, st, out, t=t)
     assert flips <= max(1, 1e-4 * cfg.steps * L.m * L.n)
 
 
@@ -170,7 +170,7 @@ def test_plan_matches_oracle_over_mixed_layers():
     for st, Lt, G, Ro, Uo in zip(states, devs, Gs, Rs, Us):
         before = st.copy()
         res = O.qgalore_step(st, G, t, WL.SR_SEED)
-        PAR.check_step(before, res, st, snapshot(Lt, Ro, Uo))
+        PAR.check_step(before, res, st, snapshot(Lt, Ro, Uo), t=t)
     plan.close()
 
 
