@@ -20,6 +20,7 @@ DATA_SEED = 0
 SR_SEED = 1234
 
 TAG_G, TAG_W, TAG_P, TAG_PNEW, TAG_M, TAG_V = 1, 2, 3, 4, 5, 6
+TAG_DRIFT_A, TAG_DRIFT_B, TAG_NOISE, TAG_SKETCH = 7, 8, 9, 10
 
 BLOCK_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -71,7 +72,16 @@ CONFIGS = {
                             sigma=1e-4),
     "llama7b_r128": Config("llama7b_r128", 3, llama_layers(32, 4096, 11008), r=128,
                            sigma=1e-4),
+    # adaptive refresh schedule: 7B shapes, rank 128, 200 steps of drifting low-rank gradients
+    "schedule7b": Config("schedule7b", 4, llama_layers(32, 4096, 11008), r=128, sigma=1e-4,
+                         steps=200),
 }
+
+# Drifting-subspace workload of the schedule configuration: layer k (0 .. 223) turns its
+# column space at rate rho_k = DRIFT_MAX * k / 223 radians per step.
+DRIFT_MAX = 0.05
+SCHEDULE_DELTA0 = 25          # initial refresh interval: 200 steps / 8
+SCHEDULE_GAMMA = 0.4
 
 
 def rng(cfg: Config, layer: int, step: int, tag: int) -> np.random.Generator:
@@ -157,3 +167,63 @@ def orthonormal_device(cfg: Config, L: LayerShape, r: int, tag: int = TAG_P, ste
     a = torch.randn((L.m, r), generator=gen, device=device, dtype=torch.float32)
     q, _ = torch.linalg.qr(a)
     return q.contiguous()
+
+
+# ------------------------------ drifting low-rank gradients ---------------------------
+# G_t = A_t S B^T + 0.1 sigma Z_t with A_t = A0 cos(rho t) + A1 sin(rho t): [A0 A1] is the Q of
+# a seeded Gaussian m x 2k, B the Q of a Gaussian n x k, S = diag(sigma sqrt(m n / k) *
+# linspace(1.5, 0.5, k)), Z_t standard normal. The top-k left singular subspace of the
+# noise-free G_t is span(A_t), so the subspace similarity of steps t and s is |cos(rho (t-s))|.
+
+def drift_rate(cfg: Config, index: int) -> float:
+    return DRIFT_MAX * index / max(1, len(cfg.layers) - 1)
+
+
+def drift_basis_device(cfg: Config, L: LayerShape, device="cuda"):
+    """(A0, A1, B scaled by S): A0, A1 m x k, BS = B S  n x k (fp32), with k = cfg.r."""
+    import torch
+    k = cfg.r
+    gen = torch.Generator(device=device)
+    gen.manual_seed(torch_seed(cfg, L.layer_id, 0, TAG_DRIFT_A))
+    a, _ = torch.linalg.qr(torch.randn((L.m, 2 * k), generator=gen, device=device))
+    gen.manual_seed(torch_seed(cfg, L.layer_id, 0, TAG_DRIFT_B))
+    b, _ = torch.linalg.qr(torch.randn((L.n, k), generator=gen, device=device))
+    sv = cfg.sigma * (L.m * L.n / k) ** 0.5 * torch.linspace(1.5, 0.5, k, device=device)
+    return a[:, :k].contiguous(), a[:, k:].contiguous(), (b * sv[None, :]).contiguous()
+
+
+def drift_gradient_device(cfg: Config, L: LayerShape, basis, rho: float, step: int, out=None):
+    """G_t (bf16, m x n) of the drifting workload; written into `out` when given."""
+    import math
+    import torch
+    A0, A1, BS = basis
+    At = A0 * math.cos(rho * step) + A1 * math.sin(rho * step)
+    gen = torch.Generator(device=A0.device)
+    gen.manual_seed(torch_seed(cfg, L.layer_id, step, TAG_NOISE))
+    G = torch.randn((L.m, L.n), generator=gen, device=A0.device) * (0.1 * cfg.sigma)
+    G.addmm_(At, BS.t())
+    if out is None:
+        return G.to(torch.bfloat16)
+    out.copy_(G)
+    return out
+
+
+def top_subspace_device(cfg: Config, L: LayerShape, G, k: int, step: int, oversample: int = 8,
+                        power_iters: int = 2):
+    """Orthonormal basis (m x k, fp32) of the top-k left singular subspace of G, by a
+    randomized range finder with power iterations (Halko, Martinsson and Tropp, 2011): a
+    Gaussian sketch of k + oversample columns, power iterations re-orthonormalized by QR, then
+    the leading eigenvectors of the small Gram matrix of the sketch's projection."""
+    import torch
+    Gf = G.float()
+    gen = torch.Generator(device=G.device)
+    gen.manual_seed(torch_seed(cfg, L.layer_id, step, TAG_SKETCH))
+    Om = torch.randn((L.n, k + oversample), generator=gen, device=G.device)
+    Q, _ = torch.linalg.qr(Gf @ Om)
+    for _ in range(power_iters):
+        Z, _ = torch.linalg.qr(Gf.t() @ Q)
+        Q, _ = torch.linalg.qr(Gf @ Z)
+    Bm = Q.t() @ Gf                        # (k + p) x n
+    evals, evecs = torch.linalg.eigh(Bm @ Bm.t())
+    top = evecs[:, torch.argsort(evals, descending=True)[:k]]
+    return (Q @ top).contiguous()
