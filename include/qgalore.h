@@ -21,6 +21,9 @@
  *            of byte k, 2k+1 in the high nibble, two's complement, codes in [-7, 7]);
  *            ceil(m*r/2) bytes.
  *   P_scale  fp32, ceil(m*r/256) group scales of P.
+ *            Two other projection formats can be selected per layer (qg_p_format): INT8
+ *            codes in [-127, 127] (m*r bytes) with the same group scales, or bf16 values
+ *            (m*r uint16, P_scale unused).
  *   M_q, V_q int8, r x n row-major; M_scale, V_scale fp32, ceil(r*n/256) group scales.
  *            All four are rewritten in place by every step (absmax requantization).
  * Group quantization everywhere is symmetric absmax over 256 flat elements:
@@ -72,6 +75,17 @@ typedef enum {
   QG_ERR_NO_DEVICE = 7   /* no HIP device is present */
 } qg_status;
 
+/* Storage format of a projection P. INT4 is the method's (AIMech Q-GaLore page, mechanism
+ * claim "INT4 projection and INT8 stochastic rounding", paper Section 3.2: a quarter of the
+ * bf16 projection's memory); the other two are the projections it is compared with on the
+ * same page (identity notes): GaLore's 16-bit projection and the 8-bit one of the Q-GaLore
+ * baseline. */
+typedef enum {
+  QG_P_INT4 = 0,   /* P_q: ceil(m*r/2) bytes of packed INT4 codes; P_scale: group scales */
+  QG_P_INT8 = 1,   /* P_q: m*r int8 codes in [-127, 127]; P_scale: group scales */
+  QG_P_BF16 = 2    /* P_q: m*r bf16 values (16-byte aligned); P_scale: unused (may be NULL) */
+} qg_p_format;
+
 /* Per-layer description for qgalore_step. */
 typedef struct {
   int64_t m, n, r;          /* W, G: m x n; P: m x r; M, V: r x n */
@@ -83,6 +97,7 @@ typedef struct {
   void *workspace;          /* caller-owned device scratch, >= qgalore_workspace_bytes() */
   size_t workspace_bytes;
   void *stream;             /* hipStream_t */
+  int32_t p_format;         /* qg_p_format of P_q / P_scale (0 = INT4) */
 } qg_layer_desc;
 
 /* Device scratch one qgalore_step call needs for an m x n layer of rank r. */
@@ -142,8 +157,9 @@ qg_status qgalore_plan_kernel_times(qg_plan *plan, float out_ms[4], int32_t *ste
  * ---------------------------------------------------------------------------------- */
 typedef struct {
   int64_t m, r;             /* P is m x r */
-  const uint8_t *q;         /* INT4 codes, layout as P_q above */
-  const float *scale;       /* ceil(m*r/256) group scales */
+  const uint8_t *q;         /* codes (or bf16 values), layout as P_q above */
+  const float *scale;       /* ceil(m*r/256) group scales (unused for bf16) */
+  int32_t format;           /* qg_p_format; both projections of a pair share it */
 } qg_proj;
 
 size_t qgalore_cossim_workspace_bytes(int64_t m, int64_t r);
@@ -169,6 +185,9 @@ qg_status qgalore_cossim(const qg_proj *P_new, const qg_proj *P_old, void *works
  * used when a refresh installs a new projection). Asynchronous on `stream`. */
 qg_status qgalore_quantize_proj(const float *P, int64_t m, int64_t r, uint8_t *P_q,
                                 float *P_scale, void *stream);
+/* The same with INT8 codes (QG_P_INT8: m*r bytes of codes in [-127, 127]). */
+qg_status qgalore_quantize_proj_int8(const float *P, int64_t m, int64_t r, int8_t *P_q,
+                                     float *P_scale, void *stream);
 
 /* ------------------------------------------------------------------------------------
  * Per-layer refresh schedule (host only; same page and claim as CosSim). A refresh falls

@@ -156,15 +156,38 @@ def unpack_int4(packed, numel: int) -> np.ndarray:
     return nib[:numel].astype(np.int8)
 
 
-def quantize_proj(P):
-    """INT4 projection store [QG-int]: (packed uint8[ceil(m*r/2)], scales fp32[groups])."""
-    q, s = absmax_quantize(P, QMAX_INT4)
-    return pack_int4(q), s
+# Projection storage formats. INT4 is the method's store [QG-int]; the same page sets it
+# against GaLore's 16-bit projection and the 8-bit projection of the Q-GaLore baseline
+# (identity notes), which these formats reproduce for comparison.
+P_FORMATS = ("int4", "int8", "bf16")
 
 
-def dequant_proj(Pq, Ps, m: int, r: int) -> np.ndarray:
-    """P~ = bf(fl(q * s)) as an m x r fp32 array whose values are bf16-exact."""
-    q = unpack_int4(Pq, m * r)
+def quantize_proj(P, fmt: str = "int4"):
+    """Store an fp32 m x r projection in format fmt: INT4 (packed uint8[ceil(m*r/2)], fp32
+    group scales), INT8 (int8[m*r], fp32 group scales) or bf16 (bit patterns uint16[m*r],
+    no scales)."""
+    if fmt == "int4":
+        q, s = absmax_quantize(P, QMAX_INT4)
+        return pack_int4(q), s
+    if fmt == "int8":
+        q, s = absmax_quantize(P, QMAX_INT8)
+        return q.ravel().astype(np.int8), s
+    if fmt == "bf16":
+        return f32_to_bf16_bits(np.asarray(P, dtype=F32).ravel()), None
+    raise ValueError(f"unknown projection format {fmt!r}")
+
+
+def dequant_proj(Pq, Ps, m: int, r: int, fmt: str = "int4") -> np.ndarray:
+    """P~ = bf(fl(q * s)) (or the stored bf16 values) as an m x r fp32 array whose values are
+    bf16-exact."""
+    if fmt == "int4":
+        q = unpack_int4(Pq, m * r)
+    elif fmt == "int8":
+        q = np.asarray(Pq, dtype=np.int8).ravel()[: m * r]
+    elif fmt == "bf16":
+        return bf16_bits_to_f32(np.asarray(Pq).view(np.uint16).ravel()[: m * r]).reshape(m, r)
+    else:
+        raise ValueError(f"unknown projection format {fmt!r}")
     return bf16_round(dequantize(q, Ps)).reshape(m, r)
 
 
@@ -336,15 +359,17 @@ class LayerState:
     layer_id: int
     Wq: np.ndarray      # int8 m x n
     Ws: np.ndarray      # fp32 [groups(m*n)]   (fixed during the step)
-    Pq: np.ndarray      # uint8 [ceil(m*r/2)]  INT4 packed
-    Ps: np.ndarray      # fp32 [groups(m*r)]
+    Pq: np.ndarray      # INT4: uint8 [ceil(m*r/2)] packed; INT8: int8 [m*r]; bf16: uint16
+    Ps: np.ndarray      # fp32 [groups(m*r)] (None for bf16)
     Mq: np.ndarray      # int8 r x n
     Ms: np.ndarray      # fp32 [groups(r*n)]
     Vq: np.ndarray      # int8 r x n
     Vs: np.ndarray      # fp32 [groups(r*n)]
+    p_format: str = "int4"
 
     def copy(self) -> "LayerState":
-        return dataclasses.replace(self, **{f: getattr(self, f).copy() for f in
+        return dataclasses.replace(self, **{f: (None if getattr(self, f) is None
+                                                else getattr(self, f).copy()) for f in
                                             ("Wq", "Ws", "Pq", "Ps", "Mq", "Ms", "Vq", "Vs")})
 
 
@@ -374,7 +399,7 @@ def qgalore_step(st: LayerState, G_bits, t: int, seed: int, h: Hyper = Hyper(),
     """
     assert 1 <= t < 2 ** 32
     m, n, r = st.m, st.n, st.r
-    Pt = dequant_proj(st.Pq, st.Ps, m, r)
+    Pt = dequant_proj(st.Pq, st.Ps, m, r, st.p_format)
     G = bf16_bits_to_f32(np.asarray(G_bits, dtype=np.uint16).reshape(m, n))
     R = project(Pt, G).astype(F32)
     N, Mq, Ms, Vq, Vs, m1, v1 = adam_int8(R, st.Mq, st.Ms, st.Vq, st.Vs, t, h)
@@ -406,10 +431,11 @@ def cossim_float(A, B) -> float:
     return float(np.sum(np.linalg.svd(C, compute_uv=False)) / r)
 
 
-def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int) -> float:
-    """CosSim between two stored INT4 projections, each dequantized and bf16-rounded as
-    the step uses it."""
-    return cossim_float(dequant_proj(Pq_new, Ps_new, m, r), dequant_proj(Pq_old, Ps_old, m, r))
+def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, fmt: str = "int4") -> float:
+    """CosSim between two stored projections (format fmt), each dequantized and bf16-rounded
+    as the step uses it."""
+    return cossim_float(dequant_proj(Pq_new, Ps_new, m, r, fmt),
+                        dequant_proj(Pq_old, Ps_old, m, r, fmt))
 
 
 @dataclasses.dataclass

@@ -32,7 +32,7 @@ class LayerDesc(ctypes.Structure):
                 ("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
                 ("alpha", c_float), ("M_scale", c_void_p), ("V_scale", c_void_p),
                 ("R_out", c_void_p), ("U_out", c_void_p), ("workspace", c_void_p),
-                ("workspace_bytes", c_size_t), ("stream", c_void_p)]
+                ("workspace_bytes", c_size_t), ("stream", c_void_p), ("p_format", c_int32)]
 
 
 class Layer(ctypes.Structure):
@@ -41,7 +41,12 @@ class Layer(ctypes.Structure):
 
 
 class Proj(ctypes.Structure):
-    _fields_ = [("m", c_int64), ("r", c_int64), ("q", c_void_p), ("scale", c_void_p)]
+    _fields_ = [("m", c_int64), ("r", c_int64), ("q", c_void_p), ("scale", c_void_p),
+                ("format", c_int32)]
+
+
+# projection storage formats (qg_p_format)
+P_FORMATS = {"int4": 0, "int8": 1, "bf16": 2}
 
 
 class Sched(ctypes.Structure):
@@ -69,6 +74,8 @@ EXPORTS = {
     "qgalore_cossim": (c_int32, [ctypes.POINTER(Proj), ctypes.POINTER(Proj), c_void_p, c_size_t,
                                  c_void_p, ctypes.POINTER(c_float)]),
     "qgalore_quantize_proj": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "qgalore_quantize_proj_int8": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p,
+                                             c_void_p]),
     "qgalore_sched_init": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float]),
     "qgalore_sched_due": (c_int32, [ctypes.POINTER(Sched), c_int64]),
     "qgalore_sched_refresh": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float,
@@ -145,13 +152,14 @@ class LayerTensors:
     G: torch.Tensor          # bf16 m x n
     Wq: torch.Tensor         # int8 m x n
     Ws: torch.Tensor         # fp32 [groups(m*n)]
-    Pq: torch.Tensor         # uint8 [ceil(m*r/2)]
-    Ps: torch.Tensor         # fp32 [groups(m*r)]
+    Pq: torch.Tensor         # int4: uint8 [ceil(m*r/2)]; int8: int8 m*r; bf16: bf16 m*r
+    Ps: torch.Tensor         # fp32 [groups(m*r)] (None for bf16)
     Mq: torch.Tensor         # int8 r x n
     Ms: torch.Tensor         # fp32 [groups(r*n)]
     Vq: torch.Tensor         # int8 r x n
     Vs: torch.Tensor         # fp32 [groups(r*n)]
     r: int
+    p_format: str = "int4"   # storage format of P: "int4", "int8" or "bf16"
 
     @property
     def m(self) -> int:
@@ -160,6 +168,17 @@ class LayerTensors:
     @property
     def n(self) -> int:
         return int(self.Wq.shape[1])
+
+
+def _proj_codes(Pq, m: int, r: int, fmt: str):
+    """Pointer to a projection's codes (or bf16 values) in format fmt, checked."""
+    if fmt == "int4":
+        return _ptr(Pq, torch.uint8, ((m * r + 1) // 2,), "P_q")
+    if fmt == "int8":
+        return _ptr(Pq, torch.int8, (m * r,), "P_q")
+    if fmt == "bf16":
+        return _ptr(Pq.reshape(-1) if Pq is not None else None, torch.bfloat16, (m * r,), "P_q")
+    raise ValueError(f"unknown projection format {fmt!r}")
 
 
 def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None):
@@ -172,10 +191,11 @@ def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None):
     d.V_scale = _ptr(L.Vs, torch.float32, (n_groups(r * n),), "Vs")
     d.R_out = _ptr(R_out, torch.float32, (r, n), "R_out")
     d.U_out = _ptr(U_out, torch.float32, (m, n), "U_out")
+    d.p_format = P_FORMATS[L.p_format]
     ptrs = dict(G=_ptr(L.G, torch.bfloat16, (m, n), "G"),
                 W_q=_ptr(L.Wq, torch.int8, (m, n), "Wq"),
                 W_scale=_ptr(L.Ws, torch.float32, (n_groups(m * n),), "Ws"),
-                P_q=_ptr(L.Pq, torch.uint8, ((m * r + 1) // 2,), "Pq"),
+                P_q=_proj_codes(L.Pq, m, r, L.p_format),
                 P_scale=_ptr(L.Ps, torch.float32, (n_groups(m * r),), "Ps"),
                 M_q=_ptr(L.Mq, torch.int8, (r, n), "Mq"),
                 V_q=_ptr(L.Vq, torch.int8, (r, n), "Vq"))
@@ -262,11 +282,12 @@ class Plan:
             pass
 
 
-def _proj(Pq, Ps, m, r) -> Proj:
+def _proj(Pq, Ps, m, r, fmt="int4") -> Proj:
     p = Proj()
     p.m, p.r = m, r
-    p.q = _ptr(Pq, torch.uint8, ((m * r + 1) // 2,), "P_q")
+    p.q = _proj_codes(Pq, m, r, fmt)
     p.scale = _ptr(Ps, torch.float32, (n_groups(m * r),), "P_scale")
+    p.format = P_FORMATS[fmt]
     return p
 
 
@@ -275,9 +296,9 @@ def cossim_workspace_bytes(m: int, r: int) -> int:
 
 
 def cossim_async(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, out: torch.Tensor,
-                 workspace=None, stream=None) -> None:
-    """CosSim of two stored INT4 projections into out[0] (device fp32), asynchronously."""
-    a, b = _proj(Pq_new, Ps_new, m, r), _proj(Pq_old, Ps_old, m, r)
+                 workspace=None, stream=None, fmt: str = "int4") -> None:
+    """CosSim of two stored projections into out[0] (device fp32), asynchronously."""
+    a, b = _proj(Pq_new, Ps_new, m, r, fmt), _proj(Pq_old, Ps_old, m, r, fmt)
     if workspace is None:
         workspace = alloc_workspace(cossim_workspace_bytes(m, r), Pq_new.device)
     _check(lib().qgalore_cossim_async(ctypes.byref(a), ctypes.byref(b),
@@ -292,14 +313,16 @@ def cossim_batch_workspace_bytes(r: int, count: int) -> int:
 
 
 def cossim_batch(pairs, r: int, out: torch.Tensor, workspace=None, stream=None) -> None:
-    """pairs: list of (Pq_new, Ps_new, Pq_old, Ps_old, m); out[k] (device fp32) receives
-    CosSim of pair k, asynchronously. All pairs share the rank r."""
+    """pairs: list of (Pq_new, Ps_new, Pq_old, Ps_old, m[, format]); out[k] (device fp32)
+    receives CosSim of pair k, asynchronously. All pairs share the rank r."""
     n = len(pairs)
     A = (Proj * n)()
     Bp = (Proj * n)()
-    for k, (qn, sn, qo, so, m) in enumerate(pairs):
-        A[k] = _proj(qn, sn, m, r)
-        Bp[k] = _proj(qo, so, m, r)
+    for k, pr in enumerate(pairs):
+        qn, sn, qo, so, m = pr[:5]
+        fmt = pr[5] if len(pr) > 5 else "int4"
+        A[k] = _proj(qn, sn, m, r, fmt)
+        Bp[k] = _proj(qo, so, m, r, fmt)
     if workspace is None:
         workspace = alloc_workspace(cossim_batch_workspace_bytes(r, n), pairs[0][0].device)
     _check(lib().qgalore_cossim_batch(A, Bp, n, _ptr(workspace, torch.uint8, None, "workspace"),
@@ -308,8 +331,9 @@ def cossim_batch(pairs, r: int, out: torch.Tensor, workspace=None, stream=None) 
            "qgalore_cossim_batch")
 
 
-def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, workspace=None, stream=None) -> float:
-    a, b = _proj(Pq_new, Ps_new, m, r), _proj(Pq_old, Ps_old, m, r)
+def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, workspace=None, stream=None,
+           fmt: str = "int4") -> float:
+    a, b = _proj(Pq_new, Ps_new, m, r, fmt), _proj(Pq_old, Ps_old, m, r, fmt)
     if workspace is None:
         workspace = alloc_workspace(cossim_workspace_bytes(m, r), Pq_new.device)
     out = c_float()
@@ -320,13 +344,24 @@ def cossim(Pq_new, Ps_new, Pq_old, Ps_old, m: int, r: int, workspace=None, strea
     return float(out.value)
 
 
-def quantize_proj(P: torch.Tensor, stream=None):
-    """INT4 group quantization of an fp32 m x r projection -> (P_q uint8, P_scale fp32)."""
+def quantize_proj(P: torch.Tensor, stream=None, fmt: str = "int4"):
+    """Group quantization of an fp32 m x r projection -> (P_q, P_scale): INT4 (uint8 packed
+    codes), INT8 (int8 codes), or for "bf16" the bf16 values (a cast; no scales)."""
     m, r = P.shape
-    Pq = torch.empty((m * r + 1) // 2, dtype=torch.uint8, device=P.device)
+    src = _ptr(P, torch.float32, (m, r), "P")
+    if fmt == "bf16":
+        return P.to(torch.bfloat16).reshape(-1).contiguous(), None
     Ps = torch.empty(n_groups(m * r), dtype=torch.float32, device=P.device)
-    _check(lib().qgalore_quantize_proj(_ptr(P, torch.float32, (m, r), "P"), m, r, Pq.data_ptr(),
-                                       Ps.data_ptr(), _stream(stream)), "qgalore_quantize_proj")
+    if fmt == "int8":
+        Pq = torch.empty(m * r, dtype=torch.int8, device=P.device)
+        _check(lib().qgalore_quantize_proj_int8(src, m, r, Pq.data_ptr(), Ps.data_ptr(),
+                                                _stream(stream)), "qgalore_quantize_proj_int8")
+        return Pq, Ps
+    if fmt != "int4":
+        raise ValueError(f"unknown projection format {fmt!r}")
+    Pq = torch.empty((m * r + 1) // 2, dtype=torch.uint8, device=P.device)
+    _check(lib().qgalore_quantize_proj(src, m, r, Pq.data_ptr(), Ps.data_ptr(), _stream(stream)),
+           "qgalore_quantize_proj")
     return Pq, Ps
 
 

@@ -3,7 +3,8 @@
 // Equation (5)): CosSim(P_new, P_old) = (1/r) * sum_i sigma_i(P_new^T P_old).
 //
 // For a batch of projection pairs (same rank r, any row counts):
-//   1. C = P~_new^T P~_old (r x r) on bf16 MFMA, INT4 dequant in LDS, split over the rows.
+//   1. C = P~_new^T P~_old (r x r) on bf16 MFMA, the INT4 (or INT8) dequant on the way into
+//      LDS, split over the rows.
 //   2. The nuclear norm of C as trace(X^T C), where X is the orthogonal polar factor of C,
 //      obtained by Newton-Schulz iterations on X, which map every singular value of X
 //      through an odd polynomial while keeping its singular vectors:
@@ -155,6 +156,18 @@ __device__ __forceinline__ uint16_t* pair_bf(const CosBatch& b, int p, int64_t o
 
 // ------------------------------------------------------------- 1: C = P~n^T P~o ---
 
+// The projections' dequant (INT4 or INT8 codes times the group scale, rounded to bf16) or
+// the bf16 values themselves, staged straight into LDS.
+template <class SA>
+__device__ __forceinline__ void cos_c_product(SA& sa, SA& sb, int64_t k_begin, int64_t k_end,
+                                              uint16_t* lds,
+                                              f32x16 (&acc)[CosTile::XM][CosTile::XN]) {
+  gemm_kloop<CosTile, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<CosTile::B_PITCH>(p + CosTile::A_ELEMS); },
+      k_begin, k_end, lds, acc);
+}
+
 __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CosTile::STAGE];
   int local;
@@ -168,13 +181,22 @@ __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
   const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
   const int64_t k_begin = (int64_t)s * q.kslab;
   const int64_t k_end = min<int64_t>(q.m, k_begin + q.kslab);
-  StageInt4K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
-  StageInt4K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
   f32x16 acc[CosTile::XM][CosTile::XN];
-  gemm_kloop<CosTile, 1>(
-      sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },
-      [](auto& st, uint16_t* p) { st.template store<CosTile::B_PITCH>(p + CosTile::A_ELEMS); },
-      k_begin, k_end, lds, acc);
+  if (q.format == kPInt8) {
+    StageInt8K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+    StageInt8K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+  } else if (q.format == kPBf16) {
+    const uint16_t* pa = reinterpret_cast<const uint16_t*>(q.qa);
+    const uint16_t* pb = reinterpret_cast<const uint16_t*>(q.qb);
+    StageBf16K<CosTile::BM, CosTile::BK, true> sa(pa, b.r, q.m, k_end, b.r, i0);
+    StageBf16K<CosTile::BM, CosTile::BK, true> sb(pb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+  } else {
+    StageInt4K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+    StageInt4K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+  }
   float* out = pair_mat(b, p, b.off_part) + (int64_t)s * b.r * b.r;
 #pragma unroll
   for (int x = 0; x < CosTile::XM; ++x)

@@ -30,6 +30,7 @@ struct LayerDev {
   int64_t m, n, r;
   int64_t rpitch;      // elements between split slabs of Rpart
   uint32_t layer_id;
+  int32_t p_format;    // 0: INT4 codes, 1: INT8 codes, 2: bf16 values (Pq then holds them)
   int32_t split;       // K-splits of the projection
   int32_t fuse_adam;   // 1: one split and n % 256 == 0, so the projection kernel runs Adam
                        // on its tile rows (no R partials, no Adam launch for this layer)
@@ -55,6 +56,16 @@ struct StepArgs {
 enum { KPROJ = 0, KADAM = 1, KBACK = 2, KDEQ = 3 };
 
 // `logical` is the workgroup's position in the launch after any renumbering.
+// Projection storage formats (the values of qg_p_format).
+constexpr int kPInt4 = 0, kPInt8 = 1, kPBf16 = 2;
+
+// The bf16 projection P~ both MFMA kernels stage: the caller's own bf16 P, or the copy the
+// dequant kernel writes into the workspace.
+__device__ __forceinline__ const uint16_t* p_tilde(const StepArgs& a, const LayerDev& L) {
+  return L.p_format == kPBf16 ? reinterpret_cast<const uint16_t*>(L.Pq)
+                              : reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+}
+
 __device__ __forceinline__ LayerDev fetch_layer(const StepArgs& a, int kernel, int logical,
                                                int& local) {
   if (a.table == nullptr) {

@@ -186,6 +186,57 @@ struct StageInt4K {
   }
 };
 
+// INT8 source [k][c] (row pitch ld codes, ld % 8 == 0, `rows` rows) -> K-major LDS tile [k][c]
+// in bf16; like StageInt4K with one byte per code.
+template <int W, int BK>
+struct StageInt8K {
+  static constexpr int CPR = W / 8;
+  static constexpr int NC = BK * CPR / kThreads;
+  static_assert(NC * kThreads == BK * CPR, "tile splits evenly over the threads");
+  rsrc_t rq, rsc;
+  uint32_t ld, k_end, c_end;
+  int c0;
+  uint2 w[NC];
+  float s[NC];
+
+  __device__ StageInt8K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
+                        int64_t k_end_, int64_t c_end_, int c0_)
+      : ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
+    const int64_t numel = rows * ld_;
+    rq = make_rsrc(q_, (uint32_t)numel);
+    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
+  }
+
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const uint32_t k = k0 + q / CPR;
+      const uint32_t c = c0 + 8 * (q % CPR);
+      const bool in = k < k_end && c < c_end;
+      const uint32_t e = k * ld + c;
+      w[u] = bload64(rq, in ? e : kOOB);
+      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = mul_rn((float)(int8_t)((e < 4 ? w[u].x : w[u].y) >> (8 * (e & 3))), s[u]);
+      *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) =
+          make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7]));
+    }
+  }
+};
+
 // bf16 source [c][k] (row pitch ld = the K extent, ld % 8 == 0, c_end rows) -> K-contiguous
 // LDS tile [c][k]. Each stage reads through a buffer resource starting at column k0; rows past
 // c_end fall outside it. Only a last, partial stage (ld % BK != 0) tests columns per lane.

@@ -16,10 +16,21 @@
 
 namespace qg {
 
-// ===================================================================== INT4 dequant ===
+// ========================================================================== dequant ===
 // P~ = bf16(q * s) for the whole m x r projection, once per step, into the workspace: the
-// projection and the back-projection both stage P~ from it (the INT4 store is what persists;
-// this copy lives only for the step). 256 threads x 8 codes per workgroup.
+// projection and the back-projection both stage P~ from it (the INT4 (or INT8) store is
+// what persists; this copy lives only for the step). 256 threads x 8 codes per workgroup.
+// A bf16 projection needs no pass (its layers have no workgroups here).
+
+// Dequantize 8 INT8 codes (two little-endian words) with their group scale.
+__device__ __forceinline__ uint4 dequant8_i8(uint2 w, float s) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    f[e] = mul_rn((float)(int8_t)((e < 4 ? w.x : w.y) >> (8 * (e & 3))), s);
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
 
 __global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
   int local;
@@ -27,12 +38,18 @@ __global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
   const uint32_t numel = (uint32_t)(L.m * L.r);
   const uint32_t e = ((uint32_t)local * kThreads + threadIdx.x) * 8;
   const bool in = e < numel;
-  const rsrc_t rq = make_rsrc(L.Pq, (numel + 1) / 2);
   const rsrc_t rs = make_rsrc(L.Ps, ((numel + kGroup - 1) / kGroup) * 4);
   const rsrc_t ro = make_rsrc(a.ws + L.off_p, numel * 2);
-  const uint32_t w = bload32(rq, in ? e >> 1 : kOOB);
   const float sc = bloadf(rs, in ? (e >> 8) * 4 : kOOB);
-  bstore128(ro, in ? e * 2 : kOOB, dequant8(w, sc));
+  uint4 out;
+  if (L.p_format == kPInt8) {
+    const rsrc_t rq = make_rsrc(L.Pq, numel);
+    out = dequant8_i8(bload64(rq, in ? e : kOOB), sc);
+  } else {
+    const rsrc_t rq = make_rsrc(L.Pq, (numel + 1) / 2);
+    out = dequant8(bload32(rq, in ? e >> 1 : kOOB), sc);
+  }
+  bstore128(ro, in ? e * 2 : kOOB, out);
 }
 
 // ============================================================================== Adam ===
@@ -248,7 +265,7 @@ __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& 
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
   // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
-  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+  const uint16_t* Pb = p_tilde(a, L);
   StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
   StageBf16K<T::BN, T::BK, VEC> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
@@ -532,7 +549,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
   // A = P~ (rows i, K = rank index contiguous: the bf16 copy the projection kernel wrote),
   // B = N~ stored [k][j] (r x n).
-  const uint16_t* Pb = reinterpret_cast<const uint16_t*>(a.ws + L.off_p);
+  const uint16_t* Pb = p_tilde(a, L);
   const uint16_t* Nb = reinterpret_cast<const uint16_t*>(a.ws + L.off_n);
   StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
   StageBf16K<T::BN, T::BK, VEC> sb(Nb, L.n, L.r, L.r, L.n, j0);
@@ -591,7 +608,8 @@ __global__ __launch_bounds__(kThreads, 2) void qg_backproject(StepArgs a) {
     back_tile<T, false>(a, L, local, lds);
 }
 
-// ========================================================== INT4 quantization of P ===
+// ================================================================ quantization of P ===
+// Symmetric absmax over groups of 256 flat elements: one wave per group, 4 elements a lane.
 
 __global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int64_t numel,
                                                             uint8_t* Pq, float* Ps) {
@@ -622,6 +640,26 @@ __global__ __launch_bounds__(kThreads) void qg_quantize_int4(const float* P, int
   if (lane == 0) Ps[g] = s;
 }
 
+__global__ __launch_bounds__(kThreads) void qg_quantize_int8(const float* P, int64_t numel,
+                                                            int8_t* Pq, float* Ps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t ngroups = (numel + kGroup - 1) / kGroup;
+  if (g >= ngroups) return;
+  const int64_t e0 = g * kGroup + 4 * lane;
+  float x[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) x[t] = (e0 + t < numel) ? P[e0 + t] : 0.0f;
+  float am = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  am = wave_max(am);
+  const float s = div_rn(am, 127.0f);
+  const float inv = recip_or_zero(s);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (e0 + t < numel) Pq[e0 + t] = (int8_t)fminf(fmaxf(rintf(mul_rn(x[t], inv)), -127.f), 127.f);
+  if (lane == 0) Ps[g] = s;
+}
+
 // ==================================================================== launchers ===
 
 hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
@@ -648,6 +686,13 @@ hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, floa
   const int64_t groups = (numel + kGroup - 1) / kGroup;
   const int grid = (int)((groups + 3) / 4);
   hipLaunchKernelGGL(qg_quantize_int4, dim3(grid), dim3(kThreads), 0, s, P, numel, Pq, Ps);
+  return hipGetLastError();
+}
+hipError_t launch_quantize_int8(const float* P, int64_t numel, int8_t* Pq, float* Ps,
+                                hipStream_t s) {
+  const int64_t groups = (numel + kGroup - 1) / kGroup;
+  const int grid = (int)((groups + 3) / 4);
+  hipLaunchKernelGGL(qg_quantize_int8, dim3(grid), dim3(kThreads), 0, s, P, numel, Pq, Ps);
   return hipGetLastError();
 }
 

@@ -12,9 +12,10 @@ constexpr int kCosMaxPairs = 32;
 constexpr int kCosTile = 64;
 
 struct CosPair {
-  const uint8_t* qa;   // P_new INT4 codes
+  int format;          // projection storage format of both (kPInt4, kPInt8, kPBf16)
+  const uint8_t* qa;   // P_new codes (or bf16 values)
   const float* sa;
-  const uint8_t* qb;   // P_old INT4 codes
+  const uint8_t* qb;   // P_old codes (or bf16 values)
   const float* sb;
   int64_t m;
   int kslab;           // rows per split of C = P~_new^T P~_old
@@ -48,6 +49,8 @@ hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s);
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,
+                                hipStream_t s);
+hipError_t launch_quantize_int8(const float* P, int64_t numel, int8_t* Pq, float* Ps,
                                 hipStream_t s);
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s);
 

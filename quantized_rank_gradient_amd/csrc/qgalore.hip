@@ -81,14 +81,16 @@ int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kKSlab), split) * 
 struct WsLayout {
   int64_t rpitch, off_r, off_n, off_p, bytes;
 };
-WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base) {
+WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base,
+                   int32_t p_format = QG_P_INT4) {
   WsLayout w;
   w.rpitch = round_up(r * n, 64);
   w.off_r = base;
   const int64_t rbytes = fused_adam(n, split) ? 0 : (int64_t)split * w.rpitch * 4;
   w.off_n = base + round_up(rbytes, 256);
   w.off_p = w.off_n + round_up(r * n * 2, 256);
-  w.bytes = (w.off_p - base) + round_up(m * r * 2, 256);
+  // a bf16 projection is staged from the caller's tensor: no dequantized copy
+  w.bytes = (w.off_p - base) + (p_format == QG_P_BF16 ? 0 : round_up(m * r * 2, 256));
   return w;
 }
 
@@ -104,17 +106,27 @@ qg_status check_hyper(const qg_layer_desc* d) {
   return QG_OK;
 }
 
+bool valid_format(int32_t f) { return f == QG_P_INT4 || f == QG_P_INT8 || f == QG_P_BF16; }
+
+// A projection in format f: codes with group scales (INT4, INT8: 4-byte aligned) or bf16
+// values that the MFMA kernels read directly (16-byte aligned, no scales).
+qg_status check_p(int32_t f, const void* P_q, const float* P_scale) {
+  if (!valid_format(f)) return QG_ERR_ARG;
+  if (!P_q || (f != QG_P_BF16 && !P_scale)) return QG_ERR_NULL;
+  if (!aligned(P_q, f == QG_P_BF16 ? 16 : 4) || !aligned(P_scale, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
 qg_status check_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, const float* W_scale,
                       const uint8_t* P_q, const float* P_scale, int8_t* M_q, int8_t* V_q) {
-  if (!d || !G || !W_q || !W_scale || !P_q || !P_scale || !M_q || !V_q || !d->M_scale ||
-      !d->V_scale)
+  if (!d || !G || !W_q || !W_scale || !M_q || !V_q || !d->M_scale || !d->V_scale)
     return QG_ERR_NULL;
   qg_status st = check_shape(d->m, d->n, d->r);
   if (st != QG_OK) return st;
+  if ((st = check_p(d->p_format, P_q, P_scale)) != QG_OK) return st;
   if (!aligned(G, 16) || !aligned(W_q, 16) || !aligned(M_q, 16) || !aligned(V_q, 16) ||
       !aligned(d->R_out, 16) || !aligned(d->U_out, 16) || !aligned(W_scale, 4) ||
-      !aligned(P_q, 4) || !aligned(P_scale, 4) || !aligned(d->M_scale, 4) ||
-      !aligned(d->V_scale, 4))
+      !aligned(d->M_scale, 4) || !aligned(d->V_scale, 4))
     return QG_ERR_ALIGN;
   return check_hyper(d);
 }
@@ -155,12 +167,13 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.m = d->m;
   L.n = d->n;
   L.r = d->r;
-  const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base, d->p_format);
   L.rpitch = w.rpitch;
   L.off_r = w.off_r;
   L.off_n = w.off_n;
   L.off_p = w.off_p;
   L.layer_id = d->layer_id;
+  L.p_format = d->p_format;
   L.split = split;
   L.fuse_adam = fused_adam(d->n, split) ? 1 : 0;
   L.kslab = (int32_t)kslab_for(d->m, split);
@@ -179,11 +192,14 @@ int grid_adam(const LayerDev& L) {
   return L.fuse_adam ? 0 : (int)cdiv(cdiv(L.r * L.n, qg::kGroup), 4);
 }
 int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
-int grid_dequant(const LayerDev& L) { return (int)cdiv(L.m * L.r, qg::kThreads * 8); }
+int grid_dequant(const LayerDev& L) {
+  return L.p_format == QG_P_BF16 ? 0 : (int)cdiv(L.m * L.r, qg::kThreads * 8);
+}
 
 qg_status launch_step(const StepArgs& a, const int grid[4], bool big, hipStream_t s) {
-  hipError_t e = qg::launch_dequant(a, grid[3], s);
-  if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
+  hipError_t e = hipSuccess;
+  if (grid[3] > 0 && (e = qg::launch_dequant(a, grid[3], s)) != hipSuccess)
+    return hip_fail(e, "dequant kernel launch");
   e = qg::launch_project(a, grid[0], s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (grid[1] > 0 && (e = qg::launch_adam(a, grid[1], s)) != hipSuccess)
@@ -209,7 +225,7 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   if (st != QG_OK) return st;
   if ((st = check_step(step)) != QG_OK) return st;
   const int split = choose_split(d->m, d->n, d->r);
-  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0, d->p_format);
   if (!d->workspace) return QG_ERR_NULL;
   if (!aligned(d->workspace, 16)) return QG_ERR_ALIGN;
   if (d->workspace_bytes < (size_t)w.bytes) return QG_ERR_WORKSPACE;
@@ -296,7 +312,7 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
     const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
     LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
                             split, ws, big);
-    ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws).bytes;
+    ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws, x.desc.p_format).bytes;
     const int g[4] = {grid_project(L), grid_adam(L), grid_back(L), grid_dequant(L)};
     for (int k = 0; k < 4; ++k) {
       if (base[k] + g[k] > kMaxDim) {
@@ -355,8 +371,9 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   if (ev) e = hipEventRecord(ev[0], s);
   if (e != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[3];
-  e = qg::launch_dequant(a, p->grid[3], s);
-  if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
+  // bf16 projections are staged directly: their layers have no dequant workgroups
+  if (p->grid[3] > 0 && (e = qg::launch_dequant(a, p->grid[3], s)) != hipSuccess)
+    return hip_fail(e, "dequant kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
   e = qg::launch_project(a, p->grid[0], s);
@@ -466,10 +483,11 @@ CosLayout cos_layout(int64_t r) {
 }
 
 qg_status check_proj(const qg_proj* p) {
-  if (!p || !p->q || !p->scale) return QG_ERR_NULL;
+  if (!p) return QG_ERR_NULL;
+  qg_status st = check_p(p->format, p->q, p->scale);
+  if (st != QG_OK) return st;
   if (p->m < 1 || p->r < 1 || p->m > kMaxDim || p->r > 8192 || p->r > p->m || p->r % 8 != 0)
     return QG_ERR_SHAPE;
-  if (!aligned(p->q, 4) || !aligned(p->scale, 4)) return QG_ERR_ALIGN;
   return QG_OK;
 }
 
@@ -481,6 +499,7 @@ qg_status check_pairs(const qg_proj* a, const qg_proj* b, int32_t count) {
     if (st != QG_OK) return st;
     if ((st = check_proj(&b[k])) != QG_OK) return st;
     if (a[k].m != b[k].m || a[k].r != b[k].r || a[k].r != a[0].r) return QG_ERR_SHAPE;
+    if (a[k].format != b[k].format) return QG_ERR_ARG;
   }
   return QG_OK;
 }
@@ -537,6 +556,7 @@ extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P
       const qg_proj& pn = P_new[first + k];
       const qg_proj& po = P_old[first + k];
       qg::CosPair& q = b.pair[k];
+      q.format = pn.format;
       q.qa = pn.q;
       q.sa = pn.scale;
       q.qb = po.q;
@@ -590,6 +610,18 @@ extern "C" qg_status qgalore_quantize_proj(const float* P, int64_t m, int64_t r,
   const hipError_t e =
       qg::launch_quantize_int4(P, m * r, P_q, P_scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QG_OK : hip_fail(e, "INT4 quantization kernel");
+}
+
+extern "C" qg_status qgalore_quantize_proj_int8(const float* P, int64_t m, int64_t r,
+                                                int8_t* P_q, float* P_scale, void* stream) {
+  if (!P || !P_q || !P_scale) return QG_ERR_NULL;
+  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
+  if (!aligned(P, 16) || !aligned(P_q, 4) || !aligned(P_scale, 4)) return QG_ERR_ALIGN;
+  qg_status st = device_present();
+  if (st != QG_OK) return st;
+  const hipError_t e =
+      qg::launch_quantize_int8(P, m * r, P_q, P_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QG_OK : hip_fail(e, "INT8 quantization kernel");
 }
 
 // ====================================================================== schedule ===

@@ -25,17 +25,17 @@ from quantized_rank_gradient_amd import workloads as WL
 F32 = np.float32
 
 
-def host_state(cfg, L, r, moments="zero", P=None):
+def host_state(cfg, L, r, moments="zero", P=None, fmt="int4"):
     """Oracle-side state of one layer (numpy) and the float projection it was made from."""
     if P is None:
         P = WL.orthonormal_f32(cfg, L, r)
-    Pq, Ps = O.quantize_proj(P)
+    Pq, Ps = O.quantize_proj(P, fmt)
     if moments == "zero":
         Mq, Ms, Vq, Vs = WL.zero_moments(r, L.n)
     else:
         Mq, Ms, Vq, Vs = WL.random_moments(cfg, L, r)
     st = O.LayerState(L.m, L.n, r, L.layer_id, WL.weights_int8(cfg, L), WL.weight_scales(cfg, L),
-                      Pq, Ps, Mq, Ms, Vq, Vs)
+                      Pq, Ps, Mq, Ms, Vq, Vs, p_format=fmt)
     return st, P
 
 
@@ -50,13 +50,17 @@ def to_device(st, G_bits, P_float=None, quantize_on_gpu=True):
     def t(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
+    fmt = st.p_format
     if quantize_on_gpu and P_float is not None:
-        Pq, Ps = B.quantize_proj(t(P_float.astype(F32)))
+        Pq, Ps = B.quantize_proj(t(P_float.astype(F32)), fmt=fmt)
+    elif fmt == "bf16":
+        Pq, Ps = t(st.Pq.view(np.int16)).view(torch.bfloat16), None
     else:
         Pq, Ps = t(st.Pq), t(st.Ps)
     G = t(G_bits.view(np.int16)).view(torch.bfloat16).reshape(st.m, st.n)
     return B.LayerTensors(layer_id=st.layer_id, G=G, Wq=t(st.Wq), Ws=t(st.Ws), Pq=Pq, Ps=Ps,
-                          Mq=t(st.Mq), Ms=t(st.Ms), Vq=t(st.Vq), Vs=t(st.Vs), r=st.r)
+                          Mq=t(st.Mq), Ms=t(st.Ms), Vq=t(st.Vq), Vs=t(st.Vs), r=st.r,
+                          p_format=fmt)
 
 
 def assert_close_f32(gpu, ref, name, rtol=2e-3, extra=0.0):
@@ -109,7 +113,7 @@ def check_step(st_before, res, st_after, gpu_out, hp=O.Hyper(), rows=None, t=1):
     assert_close_f32(gpu_out["R"], res.R, "R")
     U_gpu = gpu_out["U"] if rows is None else gpu_out["U"][np.asarray(rows)]
     m, r = st_before.m, st_before.r
-    Pt = O.dequant_proj(st_before.Pq, st_before.Ps, m, r)
+    Pt = O.dequant_proj(st_before.Pq, st_before.Ps, m, r, st_before.p_format)
     P_rows = Pt if rows is None else Pt[np.asarray(rows)]
     R_gpu = np.asarray(gpu_out["R"], F32).reshape(res.R.shape)
     N_g = O.adam_int8(R_gpu, st_before.Mq, st_before.Ms, st_before.Vq, st_before.Vs, t, hp)[0]

@@ -30,12 +30,31 @@ def test_library_exports_every_declared_function():
     assert L.qgalore_version().startswith(b"qgalore")
 
 
-def test_struct_layouts_match_header_sizes():
-    # int64 x3 + uint32 + 5 floats = 48 bytes, then 6 pointers and a size_t
-    assert ctypes.sizeof(B.LayerDesc) == 48 + 7 * 8
-    assert ctypes.sizeof(B.Layer) == ctypes.sizeof(B.LayerDesc) + 7 * 8
-    assert ctypes.sizeof(B.Proj) == 32
-    assert ctypes.sizeof(B.Sched) == 32
+def test_struct_layouts_match_header_sizes(tmp_path):
+    """The ctypes structs have the size and field offsets the C compiler gives the header's."""
+    import subprocess
+    fields = {"qg_layer_desc": (B.LayerDesc, [f[0] for f in B.LayerDesc._fields_]),
+              "qg_layer": (B.Layer, [f[0] for f in B.Layer._fields_]),
+              "qg_proj": (B.Proj, [f[0] for f in B.Proj._fields_]),
+              "qg_sched": (B.Sched, [f[0] for f in B.Sched._fields_])}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "qgalore.h"', "int main(void) {"]
+    for cname, (_, names) in fields.items():
+        lines.append(f'  printf("%zu\\n", sizeof({cname}));')
+        for nm in names:
+            lines.append(f'  printf("%zu\\n", offsetof({cname}, {nm}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "sizes.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = []
+    for cname, (cls, names) in fields.items():
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, nm).offset for nm in names]
+    assert got == want
 
 
 def _desc(m=256, n=256, r=32, **kw):

@@ -102,6 +102,33 @@ def test_int4_projection_memory_matches_pages():
     assert Ps.size == m * r // 256
 
 
+def test_projection_formats():
+    """The three stores of P: INT4 and INT8 dequantize to bf16(code * scale) with the group
+    quantizer's codes; bf16 is torch's bf16 cast of P; every format's P~ is bf16-exact and
+    within its quantization error of P."""
+    torch = pytest.importorskip("torch")
+    m, r = 512, 64
+    P = np.linalg.qr(np.random.default_rng(5).standard_normal((m, r)))[0].astype(F32)
+    g = np.arange(m * r) // 256
+    for fmt, qmax in (("int4", 7), ("int8", 127)):
+        Pq, Ps = O.quantize_proj(P, fmt)
+        q, s = O.absmax_quantize(P, qmax)
+        codes = O.unpack_int4(Pq, m * r) if fmt == "int4" else Pq
+        assert np.array_equal(codes, q.ravel()) and np.array_equal(Ps, s)
+        Pt = O.dequant_proj(Pq, Ps, m, r, fmt)
+        want = torch.from_numpy(q.ravel().astype(F32) * s[g]).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(Pt.ravel(), want)
+        # |q s - P| <= s/2, and the bf16 rounding of q s adds at most half an ulp of |q s|
+        # (<= 2^-8 |q s|, with |q s| <= |P| + s/2)
+        half = s[g].astype(np.float64) * 0.5
+        bound = half + (np.abs(P.ravel()).astype(np.float64) + half) * 2.0 ** -8
+        assert np.all(np.abs(Pt.ravel().astype(np.float64) - P.ravel()) <= bound * (1 + 1e-6))
+    Pq, Ps = O.quantize_proj(P, "bf16")
+    assert Ps is None and Pq.dtype == np.uint16 and Pq.size == m * r
+    Pt = O.dequant_proj(Pq, None, m, r, "bf16")
+    assert np.array_equal(Pt, torch.from_numpy(P).to(torch.bfloat16).float().numpy())
+
+
 # ------------------------------------------------------------------------ projection ---
 
 def test_full_rank_projection_reconstructs_gradient():
