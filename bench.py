@@ -43,14 +43,15 @@ def projection(cfg, L, r, tag, torch, WL, dev, fast):
     return torch.randn((L.m, r), generator=gen, device=dev) / (L.m ** 0.5)
 
 
-def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
-    """Per-layer optimizer state for rank r (projections, moments) sharing G and W."""
+def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4"):
+    """Per-layer optimizer state for rank r (projections stored in format fmt, moments)
+    sharing G and W."""
     layers, pnew = [], []
     dev = torch.device("cuda:0")
     shape_new = {}
     for k, L in enumerate(cfg.layers):
         P = projection(cfg, L, r, WL.TAG_P, torch, WL, dev, fast)
-        Pq, Ps = B.quantize_proj(P)
+        Pq, Ps = B.quantize_proj(P, fmt=fmt)
         del P
         ng = B.n_groups(r * L.n)
         layers.append(B.LayerTensors(
@@ -58,11 +59,11 @@ def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
             Mq=torch.zeros((r, L.n), dtype=torch.int8, device=dev),
             Ms=torch.zeros(ng, dtype=torch.float32, device=dev),
             Vq=torch.zeros((r, L.n), dtype=torch.int8, device=dev),
-            Vs=torch.zeros(ng, dtype=torch.float32, device=dev), r=r))
+            Vs=torch.zeros(ng, dtype=torch.float32, device=dev), r=r, p_format=fmt))
         # one candidate "new" projection per distinct shape stands in for the SVD result
         if (L.m, L.n) not in shape_new:
             Pn = projection(cfg, L, r, WL.TAG_PNEW, torch, WL, dev, fast)
-            shape_new[(L.m, L.n)] = B.quantize_proj(Pn)
+            shape_new[(L.m, L.n)] = B.quantize_proj(Pn, fmt=fmt)
             del Pn
         pnew.append(shape_new[(L.m, L.n)])
     torch.cuda.synchronize()
@@ -72,12 +73,12 @@ def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
 class Variant:
     """One rank variant of the layer set: a plan, refresh schedules and scratch."""
 
-    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False):
-        self.cfg, self.r = cfg, r
+    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4"):
+        self.cfg, self.r, self.fmt = cfg, r, fmt
         self.torch, self.B = torch, B
         t0 = time.time()
         self.layers, self.pnew = build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL,
-                                                 fast)
+                                                 fast, fmt)
         self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
                                                  eps=cfg.eps, alpha=cfg.alpha))
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
@@ -101,8 +102,8 @@ class Variant:
         self.plan.step(t, 1234, self.ws)
         due = [k for k, s in enumerate(self.sched) if s.due(t)]
         if due:
-            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m)
-                     for k in due]
+            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m,
+                      self.fmt) for k in due]
             self.B.cossim_batch(pairs, self.r, self.cs_out, workspace=self.cws)
         vals = self.cs_out[: len(due)].cpu().tolist() if due else []
         for k, v in zip(due, vals):
@@ -135,8 +136,8 @@ class Variant:
         torch = self.torch
         out = {}
         for label, ks in (("1 layer", [0]), ("9 layers", list(range(9)))):
-            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m)
-                     for k in ks]
+            pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m,
+                      self.fmt) for k in ks]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             self.B.cossim_batch(pairs, self.r, self.cs_out, workspace=self.cws)
             e0.record()
@@ -158,7 +159,7 @@ def fused_adam(cfg):
     return all(L.n % 256 == 0 for L in cfg.layers)
 
 
-def algorithmic(cfg, r):
+def algorithmic(cfg, r, fmt="int4"):
     """FLOPs and bytes the method must do per step, split by the kernel that does them (in
     launch order: INT4 dequant of P, projection, Adam, back-projection + rounding). Bytes
     count each algorithmic input once and each output once: P (INT4 + fp32 scale per 256)
@@ -172,19 +173,20 @@ def algorithmic(cfg, r):
     adam = 4.0 * rn + 4.0 * 4.0 * rn / 256.0          # M, V in and out + their scales
     fused = fused_adam(cfg)
     flops = (0.0, 2.0 * r * mn, 0.0, 2.0 * r * mn)
-    nbytes = (0.5 * mr + mr / 64.0,                   # P codes + scales
+    p_bytes = {"int4": 0.5 * mr + mr / 64.0, "int8": mr + mr / 64.0, "bf16": 0.0}[fmt]
+    nbytes = (p_bytes,                                # P codes + scales (bf16: no pass)
               2.0 * mn + (adam if fused else 0.0),    # G (bf16) [+ Adam]
               0.0 if fused else adam,
               2.0 * mn + mn / 64.0)                   # W in and out + W scales
     return dict(mn=mn, flops=flops, bytes=nbytes, fused_adam=fused)
 
 
-def roofline(cfg, r, kms):
-    a = algorithmic(cfg, r)
+def roofline(cfg, r, kms, fmt="int4"):
+    a = algorithmic(cfg, r, fmt)
     names = KERNELS
     k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
-    traffic = measured_traffic(cfg.key, names[k])
+    traffic = measured_traffic(cfg.key, names[k]) if fmt == "int4" else None
     if k == 1 and a["fused_adam"]:
         names = list(names)
         names[1] = "qg_project (+ Adam)"
@@ -327,6 +329,8 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="instead: run the adaptive refresh schedule (7B shapes, rank 128, 200 "
                          "steps of drifting gradients) and report the SVDs it saves")
+    ap.add_argument("--p-format", default="int4", choices=("int4", "int8", "bf16"),
+                    help="storage format of the projections (int8, bf16: comparison runs)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch bf16 matmuls of the same shapes (comparison only)")
     ap.add_argument("--fast-setup", action="store_true",
@@ -390,13 +394,16 @@ def main():
 
     results = []
     for vcfg, r in variants:
-        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL, args.fast_setup)
+        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL, args.fast_setup,
+                    args.p_format)
         ms, kms, tests = v.time_steps(args.steps, args.warmup)
         cs_ms = v.time_cossim()
-        a = algorithmic(vcfg, r)
+        a = algorithmic(vcfg, r, args.p_format)
         kernel_ms = {nm: round(t, 4) for nm, t in zip(KERNELS, kms)}
         if a["fused_adam"]:
             kernel_ms["qg_adam"] = "in qg_project"   # no separate launch
+        if args.p_format == "bf16":
+            kernel_ms["qg_dequant"] = "none (bf16 projection)"
         res = dict(config=vcfg.key, rank=r, ms_per_step=round(ms, 4),
                    value=a["mn"] / (ms / 1e3),
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
@@ -404,7 +411,7 @@ def main():
                    optimizer_ms=round(sum(kms), 4),
                    refresh_tests_per_step=round(tests, 2),
                    cossim_ms=cs_ms,
-                   roofline=roofline(vcfg, r, kms))
+                   roofline=roofline(vcfg, r, kms, args.p_format))
         if args.library_gemm:
             res["library_gemm"] = library_gemm_ms(torch, vcfg, r)
         log(json.dumps(res))
@@ -432,6 +439,7 @@ def main():
                         f"(32 x q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), "
                         f"rank {cfg.r}, one full optimizer step + due refresh tests",
             "layers": len(cfg.layers), "rank": cfg.r, "weight_elems": algorithmic(cfg, cfg.r)["mn"],
+            "projection_format": args.p_format,
             "parallelism": "single GPU",
         },
         "tflops": main_res["tflops"],
