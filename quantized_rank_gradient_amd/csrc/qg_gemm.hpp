@@ -3,9 +3,9 @@
 //
 // A workgroup of 4 wave64 computes a BM x BN output tile; the waves sit in a WM x WN grid and
 // each owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation). K is consumed BK at a time through a
-// double-buffered LDS stage, with the next stage's global loads in flight while the current
-// one feeds the MFMAs.
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation). K is consumed BK at a time through LDS
+// stages: either a double buffer filled from registers (gemm_kloop), or a ring of three
+// stages filled by LDS DMA with two stages in flight (gemm_kloop_dma).
 //
 // An MFMA lane needs 8 consecutive K values of one row of A (or one column of B). Operands
 // are kept in LDS in the layout their source has, so staging is a straight copy (plus the
@@ -29,10 +29,13 @@ namespace qg {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool A_KMAJOR_, bool B_KMAJOR_>
+// DMA_ selects the layout the direct-to-LDS stagers write (kmaj_swz below): K-major tiles
+// unpadded with permuted chunks instead of padded rows.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool A_KMAJOR_, bool B_KMAJOR_,
+          bool DMA_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_;
+  static constexpr bool A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_, DMA = DMA_;
   static_assert(WM * WN == 4, "four waves per workgroup");
   static_assert(BK % 16 == 0, "K stage is a multiple of the MFMA K");
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave sub-tile
@@ -44,8 +47,8 @@ struct Tile {
   // row permuted (kc_off below).
   static_assert(A_KMAJOR || BK == 32, "K-contiguous tiles take 32-element rows");
   static_assert(B_KMAJOR || BK == 32, "K-contiguous tiles take 32-element rows");
-  static constexpr int A_PITCH = A_KMAJOR ? BM + 32 : BK;
-  static constexpr int B_PITCH = B_KMAJOR ? BN + 32 : BK;
+  static constexpr int A_PITCH = A_KMAJOR ? BM + (DMA ? 0 : 32) : BK;
+  static constexpr int B_PITCH = B_KMAJOR ? BN + (DMA ? 0 : 32) : BK;
   static constexpr int A_ELEMS = A_KMAJOR ? BK * A_PITCH : BM * A_PITCH;
   static constexpr int B_ELEMS = B_KMAJOR ? BK * B_PITCH : BN * B_PITCH;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;      // one [A | B] stage, bf16 elements
@@ -57,6 +60,17 @@ struct Tile {
 // it reads one chunk of 16 consecutive rows (an MFMA fragment).
 __device__ __forceinline__ int kc_off(int row, int chunk) {
   return row * 32 + 8 * (chunk ^ ((row >> 2) & 3));
+}
+
+// Position of 16-byte chunk j of row k in an unpadded K-major tile of W >= 128 columns (rows
+// of 256 or 512 bytes, so every row starts on the same bank): chunk j sits at j ^ 4 (k % 4).
+// The 32 lanes of a transpose read address four consecutive rows and the four chunks of one
+// aligned 64-byte column block; the permutation puts the four rows' blocks in the four
+// distinct 64-byte bank groups.
+template <int W>
+__device__ __forceinline__ int kmaj_slot(int k, int j) {
+  static_assert(W >= 128 && W % 64 == 0, "rows span whole bank rows");
+  return j ^ (4 * (k & 3));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -288,6 +302,116 @@ struct StageBf16C {
 };
 
 // ---------------------------------------------------------------------------------------
+// Direct-to-LDS staging (gfx950 LDS DMA). buffer_load_dwordx4 with the lds flag writes lane
+// i's 16 bytes to LDS at M0 + 16 i, whatever address the lane read: data goes from memory to
+// LDS without registers or LDS store instructions, so several stages can be in flight at no
+// register cost. One wave-level load fills one contiguous KiB; the tile layout inside it is
+// chosen through the chunk each lane fetches. Lanes whose offset is out of the resource's
+// range write zeros.
+//
+// The load is issued from inline assembly: the compiler's own wait insertion does not tell
+// these loads apart from the stage being read, and would wait for every load in flight
+// before each LDS transpose read. Completion is tracked by hand instead (wait_vm_lds in
+// gemm_kloop_dma); loads the compiler does not know of can only make its own vmcnt waits
+// stricter, never looser, since vector loads complete in issue order. M0 is saved and
+// restored around the load (the hardware reads it when the load issues).
+// ---------------------------------------------------------------------------------------
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource words (as make_rsrc builds them) for use as an assembly operand. The
+// values are uniform across the wave; readfirstlane makes that explicit, so that they are
+// held in scalar registers as the instruction requires.
+__device__ __forceinline__ v4i32 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return v4i32{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+__device__ __forceinline__ void dma16(v4i32 rs, uint32_t off, uint16_t* lds_kib) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(lds_kib));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(rs), "s"(m0)
+      : "memory");
+}
+
+// bf16 source [k][c] (row pitch ld, ld % 8 == 0 and c_end % 8 == 0) -> unpadded K-major
+// tile [k][c] in the kmaj_slot layout. Each stage reads through a resource that starts at
+// the stage's first row and ends at k_end, so rows past the K range are zeros.
+template <int W, int BK>
+struct DmaBf16K {
+  static constexpr int CPR = W / 8;                 // chunks per row
+  static constexpr int RPI = 64 / CPR;              // rows per wave-level load (one KiB)
+  static constexpr int NI = BK / (4 * RPI);         // loads per wave and stage
+  static_assert(NI * 4 * RPI == BK, "a stage splits evenly over the four waves");
+  const uint16_t* src;
+  uint32_t ld, k_end;
+  uint32_t vo[NI];   // byte offset of this lane's chunk from the stage's first row
+
+  __device__ DmaBf16K(const uint16_t* s, int64_t ld_, int64_t k_end_, int64_t c_end, int c0)
+      : src(s), ld((uint32_t)ld_), k_end((uint32_t)k_end_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int row = (wave * NI + q) * RPI + lane / CPR;
+      const uint32_t c = c0 + 8 * kmaj_slot<W>(row, lane % CPR);   // the permutation is an
+      vo[q] = c < (uint32_t)c_end ? (row * ld + c) * 2 : kOOB;      // involution
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint16_t* tile) const {
+    const uint32_t k0 = (uint32_t)k0_ < k_end ? (uint32_t)k0_ : k_end;
+    const v4i32 st = rsrc_words(src + (size_t)k0 * ld, (k_end - k0) * ld * 2);
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) dma16(st, vo[q], tile + (wave * NI + q) * RPI * W);
+  }
+};
+
+// bf16 source [c][k] (row pitch ld = the K extent, ld % 8 == 0, c_end rows) -> K-contiguous
+// tile [c][k] in the kc_off layout (rows of BK = 32, 16 rows per wave-level load). Chunks
+// past the K extent (a last, partial stage) and rows past c_end are zeros.
+template <int W, int BK>
+struct DmaBf16C {
+  static_assert(BK == 32, "K-contiguous tiles take 32-element rows");
+  static constexpr int NI = W / (4 * 16);
+  static_assert(NI * 64 == W, "a stage splits evenly over the four waves");
+  const uint16_t* src;
+  uint32_t ld, c_end;
+  uint32_t vo[NI], kc[NI];   // byte offset of this lane's chunk from column 0; its K offset
+
+  __device__ DmaBf16C(const uint16_t* s, int64_t ld_, int64_t c_end_, int c0)
+      : src(s), ld((uint32_t)ld_), c_end((uint32_t)c_end_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int row = (wave * NI + q) * 16 + lane / 4;
+      const uint32_t rg = c0 + row;
+      kc[q] = 8 * ((lane & 3) ^ ((row >> 2) & 3));   // kc_off is an involution on chunks
+      vo[q] = rg < c_end ? (rg * ld + kc[q]) * 2 : kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint16_t* tile) const {
+    const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
+    const v4i32 st = rsrc_words(src + k0, (c_end * ld - k0) * 2);
+    const uint32_t lim = ld - k0;   // K values left in the rows
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < NI; ++q)
+      dma16(st, kc[q] < lim ? vo[q] : kOOB, tile + (wave * NI + q) * 16 * 32);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Fragment reads and the K loop.
 // ---------------------------------------------------------------------------------------
 template <class T>
@@ -297,7 +421,7 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % T::WN; }
 
 // 8 K values (ks .. ks+7 of this lane's half) of row/column `c` (c = tile-relative index of
 // lane 0's row for this 32-block) from a tile with the given layout.
-template <bool KMAJOR, int PITCH>
+template <bool KMAJOR, int PITCH, bool DMA = false>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int c, int ks) {
   const int lane = threadIdx.x & 63;
   if constexpr (!KMAJOR) {
@@ -307,7 +431,12 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int c, int ks) {
     typedef __attribute__((address_space(3))) v4i16* lptr;
     const int row = ks + 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int col = c + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const uint16_t* p0 = tile + row * PITCH + col;
+    // the hi half reads row + 4, which has the same chunk permutation as row
+    const uint16_t* p0;
+    if constexpr (DMA)
+      p0 = tile + row * PITCH + 8 * kmaj_slot<PITCH>(row, col >> 3) + (col & 7);
+    else
+      p0 = tile + row * PITCH + col;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lptr)(__attribute__((address_space(3))) void*)(p0));
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -331,9 +460,9 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* stage,
   for (int ks = 0; ks < T::BK; ks += 16) {
     bf16x8 a[T::XM], b[T::XN];
 #pragma unroll
-    for (int x = 0; x < T::XM; ++x) a[x] = frag<T::A_KMAJOR, T::A_PITCH>(As, am + 32 * x, ks);
+    for (int x = 0; x < T::XM; ++x) a[x] = frag<T::A_KMAJOR, T::A_PITCH, T::DMA>(As, am + 32 * x, ks);
 #pragma unroll
-    for (int y = 0; y < T::XN; ++y) b[y] = frag<T::B_KMAJOR, T::B_PITCH>(Bs, bn + 32 * y, ks);
+    for (int y = 0; y < T::XN; ++y) b[y] = frag<T::B_KMAJOR, T::B_PITCH, T::DMA>(Bs, bn + 32 * y, ks);
 #pragma unroll
     for (int x = 0; x < T::XM; ++x)
 #pragma unroll
@@ -343,10 +472,10 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* stage,
       bf16x8 al[T::XM], bl[T::XN];
 #pragma unroll
       for (int x = 0; x < T::XM; ++x)
-        al[x] = frag<T::A_KMAJOR, T::A_PITCH>(As + T::STAGE, am + 32 * x, ks);
+        al[x] = frag<T::A_KMAJOR, T::A_PITCH, T::DMA>(As + T::STAGE, am + 32 * x, ks);
 #pragma unroll
       for (int y = 0; y < T::XN; ++y)
-        bl[y] = frag<T::B_KMAJOR, T::B_PITCH>(Bs + T::STAGE, bn + 32 * y, ks);
+        bl[y] = frag<T::B_KMAJOR, T::B_PITCH, T::DMA>(Bs + T::STAGE, bn + 32 * y, ks);
 #pragma unroll
       for (int x = 0; x < T::XM; ++x)
 #pragma unroll
@@ -441,6 +570,62 @@ __device__ __forceinline__ void gemm_kloop_ring(SA& sa, SB& sb, int64_t k_begin,
       __syncthreads();
     });
   }
+}
+
+// Waits until at most N of this wave's vector-memory operations are outstanding (vmcnt;
+// vector loads complete in issue order) and all of its LDS operations are done (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier without the memory fence of __syncthreads (which would also wait for the
+// LDS loads still in flight); the asm memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// The product with direct-to-LDS stages in a ring of three LDS buffers: stage kt + 2 is
+// loaded while stage kt is multiplied. Per iteration: wait for this wave's share of stage
+// kt and for its own LDS reads of the previous iteration, barrier (every share of stage kt
+// is in LDS, and no wave still reads buffer (kt+2) % 3), issue stage kt + 2 into that
+// buffer, multiply stage kt. The lds area holds 3 * T::STAGE elements.
+template <class T, class SA, class SB>
+__device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64_t k_begin,
+                                               int64_t k_end, uint16_t* lds,
+                                               f32x16 (&acc)[T::XM][T::XN]) {
+  static_assert(T::DMA, "tile in the DMA layout");
+  constexpr int NI = SA::NI + SB::NI;   // loads per wave and stage
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  if (k_end <= k_begin) return;
+  const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
+  sa.issue(k_begin, lds);
+  sb.issue(k_begin, lds + T::A_ELEMS);
+  if (nk > 1) {
+    sa.issue(k_begin + T::BK, lds + T::STAGE);
+    sb.issue(k_begin + T::BK, lds + T::STAGE + T::A_ELEMS);
+  }
+  int buf = 0;   // kt % 3
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk)
+      wait_vm_lds<NI>();
+    else
+      wait_vm_lds<0>();
+    barrier_nofence();
+    if (kt + 2 < nk) {
+      uint16_t* nxt = lds + (buf == 0 ? 2 : buf - 1) * T::STAGE;
+      sa.issue(k_begin + (int64_t)(kt + 2) * T::BK, nxt);
+      sb.issue(k_begin + (int64_t)(kt + 2) * T::BK, nxt + T::A_ELEMS);
+    }
+    mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+  // the caller may reuse the LDS area: every wave is done with the last stage
+  __syncthreads();
 }
 
 // Output coordinates of accumulator element v of block (x, y) for this lane, relative to the

@@ -238,6 +238,7 @@ __device__ __forceinline__ void adam_group16(const StepArgs& a, const LayerDev& 
 // (eight MFMA accumulator blocks each), two workgroups per CU. Both operands are K-major in
 // memory (P is [k][i], G is [k][j]).
 using ProjTile = Tile<128, 256, 32, 2, 2, true, true>;
+using ProjTileD = Tile<128, 256, 32, 2, 2, true, true, true>;   // direct-to-LDS staging
 static_assert(ProjTile::BM == kProjTileM && ProjTile::BN == kProjTileN,
               "host and device projection tiles agree");
 static_assert(ProjTile::BN == kGroup, "a tile row spans one Adam group when n % 256 == 0");
@@ -247,13 +248,16 @@ static_assert(ProjTile::BN == kGroup, "a tile row spans one Adam group when n % 
 // writes (rows R and R + 4) fall on disjoint banks.
 constexpr int kAdamPitch = ProjTile::BN + 8;
 constexpr int kAdamLdsElems = 2 * ProjTile::WM * 32 * kAdamPitch;   // fp32 = two bf16 slots
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int kProjLdsElems =
-    2 * ProjTile::STAGE > kAdamLdsElems ? 2 * ProjTile::STAGE : kAdamLdsElems;
+    cmax(cmax(2 * ProjTile::STAGE, 3 * ProjTileD::STAGE), kAdamLdsElems);
 
-// VEC: rows of G are a multiple of 8 elements (16-byte chunk loads).
+// VEC: rows of G are a multiple of 8 elements: 16-byte chunks staged straight into LDS
+// (T in the DMA layout). Otherwise G is read element by element through registers.
 template <class T, bool VEC>
 __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& L, int local,
                                              uint16_t* lds) {
+  static_assert(T::DMA == VEC, "DMA layout exactly on the vector path");
   // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
   // columns are neighbours (and, after the renumbering, on the same XCD).
   const int ti = local % L.p_tiles_i;
@@ -266,13 +270,19 @@ __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& 
 
   // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
   const uint16_t* Pb = p_tilde(a, L);
-  StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
-  StageBf16K<T::BN, T::BK, VEC> sb(L.G, L.n, L.m, k_end, L.n, j0);
   f32x16 acc[T::XM][T::XN];
-  gemm_kloop<T, 1>(
-      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
-      k_end, lds, acc);
+  if constexpr (VEC) {
+    const DmaBf16K<T::BM, T::BK> sa(Pb, L.r, k_end, L.r, i0);
+    const DmaBf16K<T::BN, T::BK> sb(L.G, L.n, k_end, L.n, j0);
+    gemm_kloop_dma<T>(sa, sb, k_begin, k_end, lds, acc);
+  } else {
+    StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
+    StageBf16K<T::BN, T::BK, false> sb(L.G, L.n, L.m, k_end, L.n, j0);
+    gemm_kloop<T, 1>(
+        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
+        k_end, lds, acc);
+  }
 
   if (L.fuse_adam) {
     // One K split and rows made of whole 256-element groups: each tile row is one Adam group,
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void qg_project(StepArgs a) {
   int local;
   const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
   if (L.n % 8 == 0)
-    project_tile<ProjTile, true>(a, L, local, lds);
+    project_tile<ProjTileD, true>(a, L, local, lds);
   else
     project_tile<ProjTile, false>(a, L, local, lds);
 }
@@ -482,21 +492,27 @@ static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true)
                   BackSmall::BM == kBackTileM(false) && BackSmall::BN == kBackTileN(false),
               "host and device back-projection tiles agree");
 
+// The same tile in the direct-to-LDS layout (vector path).
+template <class T>
+using DmaOf = Tile<T::BM, T::BN, T::BK, T::WM, T::WN, T::A_KMAJOR, T::B_KMAJOR, true>;
+
 template <class T>
 struct BackLds {
   // fp32 row pitch of the redistribution block: 4 (mod 16) words, so that the 16 lanes of a
   // 16-byte read group (4 rows x 4 runs of 16 columns) hit distinct banks
   static constexpr int EP = T::WTN + 4;
-  static constexpr int BYTES = 2 * T::STAGE * 2 > kThreads / 64 * 32 * EP * 4
-                                   ? 2 * T::STAGE * 2 : kThreads / 64 * 32 * EP * 4;
+  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, 3 * DmaOf<T>::STAGE * 2),
+                                    kThreads / 64 * 32 * EP * 4);
 };
 
 // VEC: rows of W (and of N~) are a multiple of 16 elements: 16-byte weight accesses
-// (prefetched before the product) and 16-byte chunk loads of N~.
-template <class T, bool VEC>
+// (prefetched before the product) and 16-byte chunks of N~ staged straight into LDS (T in
+// the DMA layout). BASE is the tile whose LDS area the kernel declares.
+template <class T, bool VEC, class BASE>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
                                           uint16_t* lds) {
-  constexpr int EP = BackLds<T>::EP;
+  static_assert(T::DMA == VEC, "DMA layout exactly on the vector path");
+  constexpr int EP = BackLds<BASE>::EP;
   constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk (element path)
   constexpr int LPR = T::WTN / 16; // vector path: lanes per row, 16 columns each
   constexpr int RPP = 64 / LPR;    //   rows per pass of a 32-row chunk
@@ -551,13 +567,19 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   // B = N~ stored [k][j] (r x n).
   const uint16_t* Pb = p_tilde(a, L);
   const uint16_t* Nb = reinterpret_cast<const uint16_t*>(a.ws + L.off_n);
-  StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
-  StageBf16K<T::BN, T::BK, VEC> sb(Nb, L.n, L.r, L.r, L.n, j0);
   f32x16 acc[T::XM][T::XN];
-  gemm_kloop<T, 1>(
-      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, L.r, lds,
-      acc);
+  if constexpr (VEC) {
+    const DmaBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
+    const DmaBf16K<T::BN, T::BK> sb(Nb, L.n, L.r, L.n, j0);
+    gemm_kloop_dma<T>(sa, sb, 0, L.r, lds, acc);
+  } else {
+    StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
+    StageBf16K<T::BN, T::BK, false> sb(Nb, L.n, L.r, L.r, L.n, j0);
+    gemm_kloop<T, 1>(
+        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, L.r,
+        lds, acc);
+  }
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
   if constexpr (VEC) {
@@ -603,9 +625,9 @@ __global__ __launch_bounds__(kThreads, 2) void qg_backproject(StepArgs a) {
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
   if (L.n % 16 == 0)
-    back_tile<T, true>(a, L, local, lds);
+    back_tile<DmaOf<T>, true, T>(a, L, local, lds);
   else
-    back_tile<T, false>(a, L, local, lds);
+    back_tile<T, false, T>(a, L, local, lds);
 }
 
 // ================================================================ quantization of P ===
