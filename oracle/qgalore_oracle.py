@@ -491,3 +491,28 @@ def simulate_schedule(cossim_fn, delta0: int, T: int, gamma: float = GAMMA_DEFAU
 def fixed_interval_refreshes(delta0: int, T: int) -> int:
     """Refresh count of the fixed-interval baseline (an SVD every delta0 steps)."""
     return len(range(0, T, delta0))
+
+
+# ---------------------------------------------------------------------------------------
+# The refresh itself  [QG-def], [QG-int]: a layer's projection holds the r leading
+# singular vectors of its gradient, recomputed by an SVD (projection on the left: the
+# left singular vectors, P is m x r).
+# ---------------------------------------------------------------------------------------
+
+def normalize_column_signs(P) -> np.ndarray:
+    """Singular vectors are defined up to sign; this library's convention makes each
+    column's entry of largest magnitude positive (the first such row on ties)."""
+    P = np.array(P, dtype=F64, copy=True)
+    idx = np.argmax(np.abs(P), axis=0)
+    neg = P[idx, np.arange(P.shape[1])] < 0
+    P[:, neg] *= -1.0
+    return P
+
+
+def refresh_projection(G_bits, r: int):
+    """P = the r leading left singular vectors of G (bf16 bit patterns, m x n), by a full
+    SVD in float64, with the sign convention above; also returns the r leading singular
+    values."""
+    G = bf16_bits_to_f32(G_bits).astype(F64)
+    U, S, _ = np.linalg.svd(G, full_matrices=False)
+    return normalize_column_signs(U[:, :r]), S[:r]

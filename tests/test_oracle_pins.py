@@ -392,3 +392,61 @@ def test_schedule_drifting_subspace_closed_form():
         s_mat, d_mat = O.simulate_schedule(lambda a, b: O.cossim_float(P(a), P(b)), 25, 200)
         s_cf, d_cf = O.simulate_schedule(lambda a, b: abs(math.cos(rho * (a - b))), 25, 200)
         assert s_mat == s_cf and d_mat == d_cf
+
+
+# -------------------------------------------------------------------------- refresh ---
+
+def _hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_refresh_projection_closed_form_bf16_exact():
+    """G = A diag(s) B^T with orthonormal Hadamard columns (entries +-1/4) and s = 8, 4, 2, 1:
+    every entry of G is a multiple of 1/16 below 1, so G is exact in bf16, and its leading
+    left singular vectors are A's columns. All |entries| tie, so the first row fixes the
+    sign."""
+    H = _hadamard(16) / 4.0
+    A, B = H[:, [1, 2, 3, 5]], H[:, [4, 6, 7, 9]]
+    s = np.array([8.0, 4.0, 2.0, 1.0])
+    G = (A * s) @ B.T
+    bits = O.f32_to_bf16_bits(G.astype(np.float32))
+    assert np.array_equal(O.bf16_bits_to_f32(bits).astype(np.float64), G)
+    P, S = O.refresh_projection(bits, 3)
+    want = A[:, :3] * np.sign(A[0, :3])
+    np.testing.assert_allclose(P, want, atol=1e-12)
+    np.testing.assert_allclose(S, s[:3], rtol=1e-12)
+    assert np.all(P[0] > 0)
+
+
+def test_refresh_projection_properties():
+    """Random G: orthonormal columns, the eigen-equation G G^T p = sigma^2 p, the sign rule,
+    and invariance under G -> -G (singular vectors flip, the convention flips them back)."""
+    rng = np.random.default_rng(7)
+    m, n, r = 40, 56, 6
+    G = rng.standard_normal((m, n)).astype(np.float32)
+    bits = O.f32_to_bf16_bits(G)
+    Gd = O.bf16_bits_to_f32(bits).astype(np.float64)
+    P, S = O.refresh_projection(bits, r)
+    np.testing.assert_allclose(P.T @ P, np.eye(r), atol=1e-12)
+    np.testing.assert_allclose(Gd @ (Gd.T @ P), P * S ** 2, rtol=0, atol=1e-9 * S[0] ** 2)
+    assert np.all(np.diff(S) <= 0)
+    idx = np.argmax(np.abs(P), axis=0)
+    assert np.all(P[idx, np.arange(r)] > 0)
+    Pn, Sn = O.refresh_projection(O.f32_to_bf16_bits(-G), r)
+    np.testing.assert_allclose(Pn, P, atol=1e-12)
+    np.testing.assert_allclose(Sn, S, rtol=1e-12)
+    # library routine: the same subspace as numpy's eigh of G G^T
+    w, V = np.linalg.eigh(Gd @ Gd.T)
+    top = V[:, np.argsort(w)[::-1][:r]]
+    np.testing.assert_allclose(np.abs(top.T @ P), np.eye(r), atol=1e-8)
+
+
+def test_column_sign_rule_by_hand():
+    P = np.array([[0.5, -0.2, 0.3], [-0.7, 0.2, -0.3], [0.1, 0.1, 0.0]])
+    out = O.normalize_column_signs(P)
+    # column 0: max |.| at row 1 (negative) -> flipped; column 1: tie at rows 0/1, row 0 is
+    # negative -> flipped; column 2: tie, row 0 positive -> kept
+    np.testing.assert_array_equal(out, P * np.array([-1.0, -1.0, 1.0]))
