@@ -234,6 +234,42 @@ def measured_traffic(config_key, kernel):
     return None if ent is None else float(ent["hbm_bytes"])
 
 
+def refresh_ms(torch, B, WL, cfg, reps=10):
+    """Time of one projection refresh per distinct 7B shape at rank cfg.r: the library's
+    (qgalore_refresh_proj, INT4 output included) against the same randomized range finder
+    in torch (plus the library's INT4 quantization), on a drifting-workload gradient."""
+    out = {}
+    dev = torch.device("cuda:0")
+    seen = set()
+    for L in cfg.layers:
+        if (L.m, L.n) in seen:
+            continue
+        seen.add((L.m, L.n))
+        G = WL.drift_gradient_device(cfg, L, WL.drift_basis_device(cfg, L, device=dev), 0.01, 3)
+        k = cfg.r + 8
+        Om = WL.sketch_device(cfg, L, k, 3, device=dev)
+        ws = B.alloc_workspace(B.refresh_workspace_bytes(L.m, L.n, cfg.r, 8))
+        for _ in range(2):
+            B.refresh_proj(G, cfg.r, Om, workspace=ws)
+            B.quantize_proj(WL.top_subspace_device(cfg, L, G, cfg.r, 3))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            B.refresh_proj(G, cfg.r, Om, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        lib = e0.elapsed_time(e1) / reps
+        t0 = time.time()
+        for _ in range(reps):
+            B.quantize_proj(WL.top_subspace_device(cfg, L, G, cfg.r, 3))
+        torch.cuda.synchronize()
+        ref = (time.time() - t0) / reps * 1e3
+        out[f"{L.m}x{L.n}"] = {"library": round(lib, 3), "torch": round(ref, 3)}
+        del G, Om, ws
+    return out
+
+
 def copy_bandwidth(torch, gib=2.0, reps=5):
     """Read+write GB/s of a device-to-device copy of `gib` GiB (torch's copy kernel): the
     achievable HBM rate beside the 8 TB/s peak, and the copy of known size against which the
@@ -329,6 +365,9 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="instead: run the adaptive refresh schedule (7B shapes, rank 128, 200 "
                          "steps of drifting gradients) and report the SVDs it saves")
+    ap.add_argument("--refresh", default="library", choices=("library", "torch"),
+                    help="with --schedule: who computes the new projections (torch: the same "
+                         "randomized range finder in torch, for comparison)")
     ap.add_argument("--p-format", default="int4", choices=("int4", "int8", "bf16"),
                     help="storage format of the projections (int8, bf16: comparison runs)")
     ap.add_argument("--library-gemm", action="store_true",
@@ -352,8 +391,10 @@ def main():
     if args.schedule:
         from quantized_rank_gradient_amd.schedule_run import ScheduleRun
         scfg = WL.CONFIGS["schedule7b"]
+        rf = refresh_ms(torch, B, WL, scfg)
+        log(f"one refresh (rank {scfg.r}): {json.dumps(rf)}")
         t0 = time.time()
-        run = ScheduleRun(scfg)
+        run = ScheduleRun(scfg, refresh=args.refresh)
         log(f"schedule workload ready in {time.time() - t0:.1f}s")
         t0 = time.time()
         summ = run.run()
@@ -367,7 +408,7 @@ def main():
             "config": {"workload": "schedule7b: LLaMA-7B-shaped layer set, 224 layers, rank 128, "
                                    "200 steps, drifting low-rank gradients (0 .. 0.05 rad/step), "
                                    "interval 25 doubling when CosSim > 0.4"},
-            **summ, "layers_by_refresh_count": hist,
+            **summ, "layers_by_refresh_count": hist, "refresh_ms": rf,
             "wall_s": round(time.time() - t0, 1)}), flush=True)
         return
 

@@ -190,6 +190,33 @@ qg_status qgalore_quantize_proj_int8(const float *P, int64_t m, int64_t r, int8_
                                      float *P_scale, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Subspace refresh on the GPU (AIMech curated page on Q-GaLore, definition paragraph and
+ * mechanism claims: a layer's projection holds the rank-r leading singular vectors of its
+ * gradient, recomputed by an SVD at each refresh and stored in INT4).
+ *
+ * P (m x r) = the r leading left singular vectors of G (bf16 m x n), approximated by a
+ * randomized range finder with power iterations (Halko, Martinsson and Tropp, SIAM Review
+ * 2011, Algorithms 4.4 and 5.1):
+ *   Y = G Omega, Q = orth(Y); power_iters times: Z = orth(G^T Q), Q = orth(G Z);
+ *   B = Q^T G; B B^T = V diag(sigma^2) V^T; P = Q V[:, :r],
+ * with orth() a CholeskyQR2 in fp32, the products with G on bf16 MFMA (fp32 bases entered
+ * as bf16 hi + lo parts), the small eigenproblem by Jacobi rotations in fp32. Each column of
+ * P is negated if needed so that its entry of largest magnitude (the first such row) is
+ * positive. P is then quantized to INT4 (P_q, P_scale, as qgalore_quantize_proj).
+ *   Omega      bf16 n x k row-major sketch (k = r + oversample), drawn by the caller
+ *              (standard Gaussian entries); device pointer, 16-byte aligned.
+ *   oversample multiple of 8, k <= 136, k <= min(m, n); n % 8 == 0; power_iters 0..8.
+ *   P_out      optional fp32 m x r (16-byte aligned): P before quantization.
+ *   sigma_out  optional fp32 r: the approximated leading singular values of G.
+ * The result approximates the SVD's: its error grows with sigma_{k+1}/sigma_r of G and
+ * shrinks with power_iters. Asynchronous on `stream`; allocates nothing. */
+size_t qgalore_refresh_workspace_bytes(int64_t m, int64_t n, int64_t r, int32_t oversample);
+qg_status qgalore_refresh_proj(const uint16_t *G, int64_t m, int64_t n, int64_t r,
+                               const uint16_t *Omega, int32_t oversample, int32_t power_iters,
+                               uint8_t *P_q, float *P_scale, float *P_out, float *sigma_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Per-layer refresh schedule (host only; same page and claim as CosSim). A refresh falls
  * due when t >= next_refresh. At each refresh after the first, a similarity above gamma
  * doubles the interval; the next refresh is then t + interval.

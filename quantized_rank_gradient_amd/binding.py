@@ -76,6 +76,10 @@ EXPORTS = {
     "qgalore_quantize_proj": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     "qgalore_quantize_proj_int8": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                              c_void_p]),
+    "qgalore_refresh_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int32]),
+    "qgalore_refresh_proj": (c_int32, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32,
+                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
     "qgalore_sched_init": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float]),
     "qgalore_sched_due": (c_int32, [ctypes.POINTER(Sched), c_int64]),
     "qgalore_sched_refresh": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float,
@@ -362,6 +366,36 @@ def quantize_proj(P: torch.Tensor, stream=None, fmt: str = "int4"):
     Pq = torch.empty((m * r + 1) // 2, dtype=torch.uint8, device=P.device)
     _check(lib().qgalore_quantize_proj(src, m, r, Pq.data_ptr(), Ps.data_ptr(), _stream(stream)),
            "qgalore_quantize_proj")
+    return Pq, Ps
+
+
+def refresh_workspace_bytes(m: int, n: int, r: int, oversample: int = 8) -> int:
+    return int(lib().qgalore_refresh_workspace_bytes(m, n, r, oversample))
+
+
+def refresh_proj(G: torch.Tensor, r: int, Omega: torch.Tensor, power_iters: int = 2,
+                 P_out=None, sigma_out=None, workspace=None, stream=None):
+    """New projection of the gradient G (bf16 m x n): the r leading left singular vectors by
+    the library's randomized range finder with the caller's sketch Omega (bf16 n x k,
+    k = r + oversample), quantized to INT4 -> (P_q, P_scale). P_out (fp32 m x r) and
+    sigma_out (fp32 r) optionally receive P before quantization and the singular values."""
+    m, n = G.shape
+    k = Omega.shape[1]
+    g = _ptr(G, torch.bfloat16, (m, n), "G")
+    om = _ptr(Omega, torch.bfloat16, (n, k), "Omega")
+    Pq = torch.empty((m * r + 1) // 2, dtype=torch.uint8, device=G.device)
+    Ps = torch.empty(n_groups(m * r), dtype=torch.float32, device=G.device)
+    if workspace is None:
+        nbytes = refresh_workspace_bytes(m, n, r, k - r)
+        if nbytes == 0:
+            raise ValueError(f"refresh of a {m} x {n} gradient at rank {r} with sketch width "
+                             f"{k} is not supported")
+        workspace = alloc_workspace(nbytes, G.device)
+    _check(lib().qgalore_refresh_proj(
+        g, m, n, r, om, k - r, int(power_iters), Pq.data_ptr(), Ps.data_ptr(),
+        _ptr(P_out, torch.float32, (m, r), "P_out"), _ptr(sigma_out, torch.float32, (r,), "sigma_out"),
+        _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)),
+        "qgalore_refresh_proj")
     return Pq, Ps
 
 

@@ -54,4 +54,34 @@ hipError_t launch_quantize_int8(const float* P, int64_t numel, int8_t* Pq, float
                                 hipStream_t s);
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s);
 
+// ---- subspace refresh (randomized range finder of G's leading left singular vectors) ----
+constexpr int kRfMaxK = 136;   // widest sketch (rank + oversampling) the k x k kernels hold
+constexpr int kRfTileM = 128;  // output tile of the products with G
+constexpr int kRfTileN = 64;
+
+// part[s] (M x N fp32) = A (M x K, K slab s) * B (K x N), bf16 operands. A is K-contiguous
+// (a_kmajor = 0: A[i][k] at A + i*lda + k, lda == K) or K-major (A[i][k] at A + k*lda + i);
+// B is K-major (B[k][j] at B + k*ldb + j). lda and ldb are multiples of 8.
+struct RfGemm {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* part;
+  int64_t M, N, K, lda, ldb, kslab;
+  int tiles_m, tiles_n, split, a_kmajor;
+};
+
+hipError_t launch_rf_gemm(const RfGemm& g, hipStream_t s);
+hipError_t launch_rf_reduce(const float* part, int split, int64_t M, int N, int k, float* out,
+                            hipStream_t s);
+// Gram matrix of Y (M x k): partials over row chunks into part, their sum into out (k x k).
+hipError_t launch_rf_gram(const float* Y, int64_t M, int k, int64_t rows_per_chunk,
+                          int chunks, float* part, float* out, hipStream_t s);
+hipError_t launch_rf_chol_inv(const float* W, int k, float shift_rel, float* Wt, hipStream_t s);
+hipError_t launch_rf_smallmul(const float* Y, const float* Wm, int64_t M, int k, int N,
+                              float* out, uint16_t* outb, float* amax_v, hipStream_t s);
+hipError_t launch_rf_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
+                            float* evals, float* Vr, float* sigma, int* sweeps, hipStream_t s);
+hipError_t launch_rf_signs(float* P, int64_t m, int r, const float* amax_v, float* sgn,
+                           hipStream_t s);
+
 }  // namespace qg

@@ -1,5 +1,6 @@
 // Host side of the C ABI: argument validation, work partitioning, workspace layout and
 // launches. Every entry point validates its arguments completely before the first HIP call.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -622,6 +623,180 @@ extern "C" qg_status qgalore_quantize_proj_int8(const float* P, int64_t m, int64
   const hipError_t e =
       qg::launch_quantize_int8(P, m * r, P_q, P_scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QG_OK : hip_fail(e, "INT8 quantization kernel");
+}
+
+// ======================================================================= refresh ===
+
+namespace {
+constexpr int kRfMaxPowerIters = 8;
+constexpr int64_t kRfGramChunk = 64;     // rows per partial Gram matrix
+constexpr int kRfMaxSweeps = 20;         // Jacobi sweeps at most
+constexpr float kRfJacobiTol = 1e-6f;    // relative off-diagonal level that ends a sweep
+constexpr float kRfShift = 1e-6f;        // diagonal shift (x trace / k) of the first
+                                         // CholeskyQR pass
+
+struct RfGemmPlan {
+  int split, tiles_m, tiles_n;
+  int64_t kslab;
+};
+// Split-K of one product with G: enough workgroups to cover the chip.
+RfGemmPlan rf_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  RfGemmPlan p;
+  p.tiles_m = (int)cdiv(M, qg::kRfTileM);
+  p.tiles_n = (int)cdiv(N, qg::kRfTileN);
+  const int64_t stages = cdiv(K, kK);
+  int64_t sp = std::max<int64_t>(1, cdiv(512, (int64_t)p.tiles_m * p.tiles_n));
+  sp = std::min<int64_t>(std::min<int64_t>(sp, 16), stages);
+  p.kslab = cdiv(stages, sp) * kK;
+  p.split = (int)cdiv(K, p.kslab);
+  return p;
+}
+
+struct RfLayout {
+  int64_t off_part, off_y, off_t, off_qf, off_qb, off_gpart, off_gram, off_wt, off_eval, off_vr,
+      off_info, off_amax, off_sgn, off_p, bytes;
+};
+RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
+  const int64_t mx = std::max(m, n);
+  int64_t part = 0;
+  const int64_t shapes[3][3] = {{m, k, n}, {m, 2 * k, n}, {n, 2 * k, m}};
+  for (const auto& sh : shapes)
+    part = std::max<int64_t>(part, rf_gemm_plan(sh[0], sh[1], sh[2]).split * sh[0] * sh[1]);
+  RfLayout L;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += round_up(std::max<int64_t>(bytes, 1), 256);
+    return o;
+  };
+  L.off_part = take(part * 4);
+  L.off_y = take(mx * k * 4);
+  L.off_t = take(mx * k * 4);
+  L.off_qf = take(mx * k * 4);
+  L.off_qb = take(mx * 2 * k * 2);
+  L.off_gpart = take(cdiv(mx, kRfGramChunk) * k * k * 4);
+  L.off_gram = take(k * k * 4);
+  L.off_wt = take(k * k * 4);
+  L.off_eval = take(k * 4);
+  L.off_vr = take(k * r * 4);
+  L.off_info = take(16);
+  L.off_amax = take(cdiv(m, 64) * r * 4);
+  L.off_sgn = take(r * 4);
+  L.off_p = take(m * r * 4);
+  L.bytes = off;
+  return L;
+}
+
+qg_status check_refresh(int64_t m, int64_t n, int64_t r, int32_t oversample, int32_t iters) {
+  if (m < 1 || n < 1 || r < 8 || r % 8 != 0 || m > kMaxDim || n > kMaxDim) return QG_ERR_SHAPE;
+  if (oversample < 0 || oversample % 8 != 0 || iters < 0 || iters > kRfMaxPowerIters)
+    return QG_ERR_ARG;
+  const int64_t k = r + oversample;
+  if (k > qg::kRfMaxK || k > m || k > n || n % 8 != 0) return QG_ERR_SHAPE;
+  // fp32 slabs of up to max(m, n) x 2k (and G itself) stay below 2^29 elements
+  if (m * n > kMaxElems || std::max(m, n) * 2 * k > kMaxElems) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+}  // namespace
+
+extern "C" size_t qgalore_refresh_workspace_bytes(int64_t m, int64_t n, int64_t r,
+                                                  int32_t oversample) {
+  if (check_refresh(m, n, r, oversample, 0) != QG_OK) return 0;
+  return (size_t)rf_layout(m, n, r, r + oversample).bytes;
+}
+
+extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t n, int64_t r,
+                                          const uint16_t* Omega, int32_t oversample,
+                                          int32_t power_iters, uint8_t* P_q, float* P_scale,
+                                          float* P_out, float* sigma_out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (!G || !Omega || !P_q || !P_scale || !workspace) return QG_ERR_NULL;
+  qg_status st = check_refresh(m, n, r, oversample, power_iters);
+  if (st != QG_OK) return st;
+  if (!aligned(G, 16) || !aligned(Omega, 16) || !aligned(P_q, 4) || !aligned(P_scale, 4) ||
+      !aligned(workspace, 16) || (P_out && !aligned(P_out, 16)) ||
+      (sigma_out && !aligned(sigma_out, 4)))
+    return QG_ERR_ALIGN;
+  const int64_t k = r + oversample;
+  const RfLayout lay = rf_layout(m, n, r, k);
+  if (workspace_bytes < (size_t)lay.bytes) return QG_ERR_WORKSPACE;
+  if ((st = device_present()) != QG_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + lay.off_part);
+  float* Y = reinterpret_cast<float*>(ws + lay.off_y);
+  float* T = reinterpret_cast<float*>(ws + lay.off_t);
+  float* Qf = reinterpret_cast<float*>(ws + lay.off_qf);
+  uint16_t* Qb = reinterpret_cast<uint16_t*>(ws + lay.off_qb);
+  float* gpart = reinterpret_cast<float*>(ws + lay.off_gpart);
+  float* gram = reinterpret_cast<float*>(ws + lay.off_gram);
+  float* Wt = reinterpret_cast<float*>(ws + lay.off_wt);
+  float* evals = reinterpret_cast<float*>(ws + lay.off_eval);
+  float* Vr = reinterpret_cast<float*>(ws + lay.off_vr);
+  int* info = reinterpret_cast<int*>(ws + lay.off_info);
+  float* amax = reinterpret_cast<float*>(ws + lay.off_amax);
+  float* sgn = reinterpret_cast<float*>(ws + lay.off_sgn);
+  float* P = P_out ? P_out : reinterpret_cast<float*>(ws + lay.off_p);
+  const int kk = (int)k;
+
+  hipError_t e = hipSuccess;
+  // out (M x k) = A B, with A = G (M = m, K = n) or G^T (M = n, K = m) and B a basis of
+  // width nb (k for the sketch, 2k for the hi/lo parts of an fp32 basis)
+  auto product = [&](bool transposed, const uint16_t* B, int64_t nb, float* out) {
+    const int64_t M = transposed ? n : m, K = transposed ? m : n;
+    const RfGemmPlan pl = rf_gemm_plan(M, nb, K);
+    qg::RfGemm g;
+    g.A = G;
+    g.B = B;
+    g.part = part;
+    g.M = M;
+    g.N = nb;
+    g.K = K;
+    g.lda = n;
+    g.ldb = nb;
+    g.kslab = pl.kslab;
+    g.tiles_m = pl.tiles_m;
+    g.tiles_n = pl.tiles_n;
+    g.split = pl.split;
+    g.a_kmajor = transposed ? 1 : 0;
+    if (e == hipSuccess) e = qg::launch_rf_gemm(g, s);
+    if (e == hipSuccess) e = qg::launch_rf_reduce(part, pl.split, M, (int)nb, kk, out, s);
+  };
+  auto gram_of = [&](const float* X, int64_t M) {
+    if (e == hipSuccess)
+      e = qg::launch_rf_gram(X, M, kk, kRfGramChunk, (int)cdiv(M, kRfGramChunk), gpart, gram, s);
+  };
+  // Qf, Qb = orth(Y) for Y of M rows: CholeskyQR with `passes` passes (the first shifted)
+  auto orth = [&](int64_t M, int passes) {
+    const float* in = Y;
+    for (int pass = 0; pass < passes; ++pass) {
+      const bool last = pass == passes - 1;
+      float* out = last ? Qf : T;
+      gram_of(in, M);
+      if (e == hipSuccess) e = qg::launch_rf_chol_inv(gram, kk, pass == 0 ? kRfShift : 0.0f, Wt, s);
+      if (e == hipSuccess)
+        e = qg::launch_rf_smallmul(in, Wt, M, kk, kk, out, last ? Qb : nullptr, nullptr, s);
+      in = out;
+    }
+  };
+  product(false, Omega, k, Y);            // Y = G Omega
+  orth(m, power_iters == 0 ? 2 : 1);
+  for (int it = 0; it < power_iters; ++it) {
+    product(true, Qb, 2 * k, Y);          // G^T Q
+    orth(n, 1);
+    product(false, Qb, 2 * k, Y);         // G Z
+    orth(m, it == power_iters - 1 ? 2 : 1);
+  }
+  product(true, Qb, 2 * k, Y);            // B^T = G^T Q  (n x k)
+  gram_of(Y, n);                          // B B^T
+  if (e == hipSuccess)
+    e = qg::launch_rf_jacobi(gram, kk, (int)r, kRfMaxSweeps, kRfJacobiTol, evals, Vr,
+                             sigma_out, info, s);
+  if (e == hipSuccess) e = qg::launch_rf_smallmul(Qf, Vr, m, kk, (int)r, P, nullptr, amax, s);
+  if (e == hipSuccess) e = qg::launch_rf_signs(P, m, (int)r, amax, sgn, s);
+  if (e == hipSuccess) e = qg::launch_quantize_int4(P, m * r, P_q, P_scale, s);
+  return e == hipSuccess ? QG_OK : hip_fail(e, "subspace refresh kernels");
 }
 
 // ====================================================================== schedule ===

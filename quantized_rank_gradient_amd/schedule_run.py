@@ -6,10 +6,11 @@ gradient at an interval; at every refresh after the first, the new projection is
 with the previous one and a similarity above gamma doubles that layer's interval.
 
 This module is caller-side code around the library: it generates the drifting gradients
-(workloads.drift_gradient_device), computes each due layer's new projection with a randomized
-range finder in torch (the SVD is the caller's; the library quantizes the result to INT4),
-runs the library's batched similarity test and schedule bookkeeping, and the grouped
-optimizer step of every layer at every step.
+(workloads.drift_gradient_device) and, for each due layer, the Gaussian sketch of the
+refresh; the library computes the new INT4 projection (qgalore_refresh_proj: randomized range
+finder with two power iterations), the batched similarity test, the schedule bookkeeping and
+the grouped optimizer step of every layer at every step. refresh="torch" computes the new
+projection with the same algorithm in torch instead (comparison).
 """
 from __future__ import annotations
 
@@ -23,9 +24,13 @@ from . import workloads as WL
 
 class ScheduleRun:
     def __init__(self, cfg: WL.Config, device: str = "cuda", delta0: int = WL.SCHEDULE_DELTA0,
-                 gamma: float = WL.SCHEDULE_GAMMA, debug_layers=()):
+                 gamma: float = WL.SCHEDULE_GAMMA, debug_layers=(), refresh: str = "library",
+                 oversample: int = 8, power_iters: int = 2):
         """debug_layers: indices of layers whose R and U the step also writes out (R_out,
-        U_out), for checking."""
+        U_out), for checking. refresh: "library" or "torch" (see the module docstring)."""
+        if refresh not in ("library", "torch"):
+            raise ValueError(f"unknown refresh {refresh!r}")
+        self.refresh, self.oversample, self.power_iters = refresh, oversample, power_iters
         self.cfg, self.r = cfg, cfg.r
         dev = torch.device(device)
         self.basis, self.rho, self.G, self.layers = [], [], [], []
@@ -53,6 +58,10 @@ class ScheduleRun:
                            R_out=self.R_out, U_out=self.U_out)
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(self.r, 32))
+        self.rws = None
+        if refresh == "library":
+            self.rws = B.alloc_workspace(max(
+                B.refresh_workspace_bytes(L.m, L.n, self.r, oversample) for L in cfg.layers))
         self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device=dev)
         self.sched = [B.Schedule(delta0, gamma) for _ in self.layers]
         self.refreshed_at = [None] * len(self.layers)   # step of each layer's current P
@@ -85,8 +94,16 @@ class ScheduleRun:
             def subspaces():
                 out = {}
                 for k in due:
-                    P = WL.top_subspace_device(cfg, cfg.layers[k], self.G[k], self.r, t)
-                    out[k] = B.quantize_proj(P)
+                    L = cfg.layers[k]
+                    if self.refresh == "torch":
+                        P = WL.top_subspace_device(cfg, L, self.G[k], self.r, t,
+                                                   self.oversample, self.power_iters)
+                        out[k] = B.quantize_proj(P)
+                    else:
+                        Om = WL.sketch_device(cfg, L, self.r + self.oversample, t,
+                                              device=self.G[k].device)
+                        out[k] = B.refresh_proj(self.G[k], self.r, Om, self.power_iters,
+                                                workspace=self.rws)
                 return out
             new = self._timed("subspaces", subspaces)
             tested = [k for k in due if self.sched[k].count > 0]
@@ -121,7 +138,8 @@ class ScheduleRun:
         counts = [s.count for s in self.sched]
         fixed = len(range(0, self.cfg.steps, self.delta0))
         total_fixed = fixed * len(counts)
-        return dict(svds=int(sum(counts)), svds_fixed_interval=int(total_fixed),
+        return dict(refresh=self.refresh,
+                    svds=int(sum(counts)), svds_fixed_interval=int(total_fixed),
                     svds_saved=round(1.0 - sum(counts) / total_fixed, 4),
                     similarity_tests=self.tests,
                     per_layer_counts=counts,

@@ -208,6 +208,14 @@ def drift_gradient_device(cfg: Config, L: LayerShape, basis, rho: float, step: i
     return out
 
 
+def sketch_device(cfg: Config, L: LayerShape, width: int, step: int, device="cuda"):
+    """Gaussian sketch (bf16 n x width) of the randomized refresh of layer L at `step`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(torch_seed(cfg, L.layer_id, step, TAG_SKETCH))
+    return torch.randn((L.n, width), generator=gen, device=device).to(torch.bfloat16)
+
+
 def top_subspace_device(cfg: Config, L: LayerShape, G, k: int, step: int, oversample: int = 8,
                         power_iters: int = 2):
     """Orthonormal basis (m x k, fp32) of the top-k left singular subspace of G, by a
