@@ -516,3 +516,40 @@ def refresh_projection(G_bits, r: int):
     G = bf16_bits_to_f32(G_bits).astype(F64)
     U, S, _ = np.linalg.svd(G, full_matrices=False)
     return normalize_column_signs(U[:, :r]), S[:r]
+
+
+# ---------------------------------------------------------------------------------------
+# A linear layer whose weight is stored as INT8  [QG-lim]: activations stay 16-bit, and the
+# INT8 weight (with its group scales, the format of W_q / W_s above) is dequantized to bf16
+# inside the forward and backward products. Shapes: X is T x n (tokens x inputs), W is m x n
+# (outputs x inputs, as the optimizer holds it), Y and dY are T x m. Products are summed in
+# float64, rounded once to fp32 and then to bf16 (the activation format).
+# ---------------------------------------------------------------------------------------
+
+def dequant_weight(Wq, Ws, m: int, n: int) -> np.ndarray:
+    """W~ = bf(fl(q * s)) as an m x n fp32 array of bf16-exact values."""
+    q = np.asarray(Wq, dtype=np.int8).ravel()[: m * n]
+    return bf16_round(dequantize(q, Ws)).reshape(m, n)
+
+
+def _to_bf16_bits(x64) -> np.ndarray:
+    return f32_to_bf16_bits(np.asarray(x64, dtype=F64).astype(F32))
+
+
+def linear_forward(X_bits, Wq, Ws, m: int, n: int) -> np.ndarray:
+    """Y = X W~^T (T x m), bf16 bit patterns."""
+    X = bf16_bits_to_f32(X_bits).astype(F64).reshape(-1, n)
+    return _to_bf16_bits(X @ dequant_weight(Wq, Ws, m, n).astype(F64).T)
+
+
+def linear_backward_data(dY_bits, Wq, Ws, m: int, n: int) -> np.ndarray:
+    """dX = dY W~ (T x n), bf16 bit patterns."""
+    dY = bf16_bits_to_f32(dY_bits).astype(F64).reshape(-1, m)
+    return _to_bf16_bits(dY @ dequant_weight(Wq, Ws, m, n).astype(F64))
+
+
+def linear_backward_weight(dY_bits, X_bits) -> np.ndarray:
+    """G = dY^T X (m x n), bf16 bit patterns: the weight gradient the optimizer step takes."""
+    dY = bf16_bits_to_f32(dY_bits).astype(F64)
+    X = bf16_bits_to_f32(X_bits).astype(F64)
+    return _to_bf16_bits(dY.T @ X)

@@ -450,3 +450,50 @@ def test_column_sign_rule_by_hand():
     # column 0: max |.| at row 1 (negative) -> flipped; column 1: tie at rows 0/1, row 0 is
     # negative -> flipped; column 2: tie, row 0 positive -> kept
     np.testing.assert_array_equal(out, P * np.array([-1.0, -1.0, 1.0]))
+
+
+# --------------------------------------------------------------- INT8-weight linear ---
+
+def test_int8_linear_exact_integer_case():
+    """Small integers everywhere (codes, a power-of-two scale, activations): every product
+    and sum is exact, so the three products equal integer matrix products, checked by
+    brute force on Python integers."""
+    rng = np.random.default_rng(3)
+    T, m, n = 5, 6, 256
+    Wq = rng.integers(-3, 4, size=(m, n)).astype(np.int8)
+    Ws = np.full(O.n_groups(m * n), 0.5, dtype=np.float32)
+    X = rng.integers(-2, 3, size=(T, n)).astype(np.float32)
+    dY = rng.integers(-2, 3, size=(T, m)).astype(np.float32)
+    Xb, dYb = O.f32_to_bf16_bits(X), O.f32_to_bf16_bits(dY)
+    Wi = [[int(v) for v in row] for row in Wq]
+    Xi = [[int(v) for v in row] for row in X]
+    dYi = [[int(v) for v in row] for row in dY]
+    Y = O.bf16_bits_to_f32(O.linear_forward(Xb, Wq, Ws, m, n))
+    want = [[sum(Xi[t][i] * Wi[o][i] for i in range(n)) / 2 for o in range(m)] for t in range(T)]
+    np.testing.assert_array_equal(Y, np.array(want, dtype=np.float32))
+    dX = O.bf16_bits_to_f32(O.linear_backward_data(dYb, Wq, Ws, m, n))
+    want = [[sum(dYi[t][o] * Wi[o][i] for o in range(m)) / 2 for i in range(n)] for t in range(T)]
+    np.testing.assert_array_equal(dX, np.array(want, dtype=np.float32))
+    G = O.bf16_bits_to_f32(O.linear_backward_weight(dYb, Xb))
+    want = [[sum(dYi[t][o] * Xi[t][i] for t in range(T)) for i in range(n)] for o in range(m)]
+    np.testing.assert_array_equal(G, np.array(want, dtype=np.float32))
+
+
+def test_int8_linear_transpose_identities():
+    """With one scale for every group, the data gradient is the forward product with the
+    transposed weight, and the weight gradient's transpose is the product with the roles of
+    X and dY exchanged; both catch a transposed or swapped operand."""
+    rng = np.random.default_rng(4)
+    T, m, n = 7, 256, 512
+    Wq = rng.integers(-127, 128, size=(m, n)).astype(np.int8)
+    Ws = np.full(O.n_groups(m * n), 3e-3, dtype=np.float32)
+    dYb = O.f32_to_bf16_bits(rng.standard_normal((T, m)).astype(np.float32))
+    Xb = O.f32_to_bf16_bits(rng.standard_normal((T, n)).astype(np.float32))
+    WqT = np.ascontiguousarray(Wq.T)
+    np.testing.assert_array_equal(O.linear_backward_data(dYb, Wq, Ws, m, n),
+                                  O.linear_forward(dYb, WqT, Ws, n, m))
+    np.testing.assert_array_equal(O.linear_backward_weight(dYb, Xb).T,
+                                  O.linear_backward_weight(Xb, dYb))
+    # the dequantized weight is the per-group q * s rounded to bf16
+    Wt = O.dequant_weight(Wq, Ws, m, n)
+    np.testing.assert_array_equal(Wt, O.bf16_round(Wq.astype(np.float32) * np.float32(3e-3)))
