@@ -270,6 +270,68 @@ def refresh_ms(torch, B, WL, cfg, reps=10):
     return out
 
 
+def linear_bench(torch, B, WL, T, reps):
+    """The three products of an INT8-weight linear layer for each distinct 7B shape at T
+    tokens: per-call time and TFLOP/s of the library kernels (dequantization fused), against
+    torch doing the same with an explicit dequantization to bf16 and hipBLASLt products."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    shapes = sorted({(L.m, L.n) for L in WL.CONFIGS["llama7b_r1024"].layers})
+    rows = {}
+    tot_flop = tot_lib = tot_ref = 0.0
+    count = {}
+    for L in WL.CONFIGS["llama7b_r1024"].layers:
+        count[(L.m, L.n)] = count.get((L.m, L.n), 0) + 1
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for (m, n) in shapes:
+        Wq = torch.randint(-127, 128, (m, n), generator=gen, device=dev, dtype=torch.int8)
+        Ws = torch.rand(B.n_groups(m * n), generator=gen, device=dev) * 1e-3 + 5e-4
+        X = torch.randn((T, n), generator=gen, device=dev).to(torch.bfloat16)
+        dY = torch.randn((T, m), generator=gen, device=dev).to(torch.bfloat16)
+        Y = torch.empty((T, m), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((T, n), dtype=torch.bfloat16, device=dev)
+        G = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        flop = 2.0 * T * m * n
+
+        def deq():
+            return (Wq.float().reshape(-1)[: m * n].reshape(-1, 256) *
+                    Ws[:, None]).reshape(m, n).to(torch.bfloat16) if (m * n) % 256 == 0 else None
+        lib = [timed(lambda: B.int8_linear_fwd(X, Wq, Ws, out=Y)),
+               timed(lambda: B.int8_linear_bwd_data(dY, Wq, Ws, out=dX)),
+               timed(lambda: B.linear_bwd_weight(dY, X, out=G))]
+        ref = [timed(lambda: torch.matmul(X, deq().t())),
+               timed(lambda: torch.matmul(dY, deq())),
+               timed(lambda: torch.matmul(dY.t(), X))]
+        key = f"{m}x{n}"
+        rows[key] = {"library_ms": [round(x, 4) for x in lib],
+                     "torch_dequant_matmul_ms": [round(x, 4) for x in ref],
+                     "library_tflops": [round(flop / (x * 1e-3) / 1e12, 1) for x in lib]}
+        c = count[(m, n)]
+        tot_flop += 3 * flop * c
+        tot_lib += sum(lib) * c
+        tot_ref += sum(ref) * c
+        del Wq, Ws, X, dY, Y, dX, G
+        torch.cuda.empty_cache()
+    return {"metric": "INT8-weight linear layer products (forward, data and weight gradients), "
+                      "LLaMA-7B layer set", "tokens": T,
+            "value": round(tot_flop / (tot_lib * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(tot_flop / (tot_lib * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "layer_set_ms": round(tot_lib, 2), "torch_layer_set_ms": round(tot_ref, 2),
+            "shapes": rows}
+
+
 def copy_bandwidth(torch, gib=2.0, reps=5):
     """Read+write GB/s of a device-to-device copy of `gib` GiB (torch's copy kernel): the
     achievable HBM rate beside the 8 TB/s peak, and the copy of known size against which the
@@ -365,6 +427,11 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="instead: run the adaptive refresh schedule (7B shapes, rank 128, 200 "
                          "steps of drifting gradients) and report the SVDs it saves")
+    ap.add_argument("--linear", action="store_true",
+                    help="instead: time the INT8-weight linear products (forward, data and "
+                         "weight gradients) on the 7B layer shapes")
+    ap.add_argument("--tokens", type=int, default=8192,
+                    help="with --linear: tokens per batch (batch x sequence length)")
     ap.add_argument("--refresh", default="library", choices=("library", "torch"),
                     help="with --schedule: who computes the new projections (torch: the same "
                          "randomized range finder in torch, for comparison)")
@@ -410,6 +477,10 @@ def main():
                                    "interval 25 doubling when CosSim > 0.4"},
             **summ, "layers_by_refresh_count": hist, "refresh_ms": rf,
             "wall_s": round(time.time() - t0, 1)}), flush=True)
+        return
+
+    if args.linear:
+        print(json.dumps(linear_bench(torch, B, WL, args.tokens, args.steps)), flush=True)
         return
 
     cfg = WL.CONFIGS[args.config]

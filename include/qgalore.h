@@ -217,6 +217,25 @@ qg_status qgalore_refresh_proj(const uint16_t *G, int64_t m, int64_t n, int64_t 
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Products of a linear layer whose weight is the INT8 W_q / W_scale above (AIMech curated
+ * page on Q-GaLore, limitation claim "simulated weight quantization throughput": the
+ * activations stay 16-bit and the INT8 weight is dequantized inside the forward and
+ * backward passes). W~ = bf16(q_W * s_W) is formed inside the kernels and never stored.
+ *   X, dX   bf16 T x n row-major (T tokens, n inputs)
+ *   Y, dY   bf16 T x m row-major (m outputs)
+ *   G       bf16 m x n row-major (the weight gradient qgalore_step takes)
+ * Each product accumulates in fp32 (bf16 MFMA) and rounds to bf16. m and n must be
+ * multiples of 8; T*m, T*n and m*n at most 2^29. bf16 tensors and W_q 16-byte aligned.
+ * Asynchronous on `stream`; no workspace. */
+qg_status qgalore_int8_linear_fwd(const uint16_t *X, const int8_t *W_q, const float *W_scale,
+                                  int64_t T, int64_t m, int64_t n, uint16_t *Y, void *stream);
+qg_status qgalore_int8_linear_bwd_data(const uint16_t *dY, const int8_t *W_q,
+                                       const float *W_scale, int64_t T, int64_t m, int64_t n,
+                                       uint16_t *dX, void *stream);
+qg_status qgalore_linear_bwd_weight(const uint16_t *dY, const uint16_t *X, int64_t T, int64_t m,
+                                    int64_t n, uint16_t *G, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Per-layer refresh schedule (host only; same page and claim as CosSim). A refresh falls
  * due when t >= next_refresh. At each refresh after the first, a similarity above gamma
  * doubles the interval; the next refresh is then t + interval.

@@ -80,6 +80,12 @@ EXPORTS = {
     "qgalore_refresh_proj": (c_int32, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32,
                                        c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
+    "qgalore_int8_linear_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                          c_int64, c_void_p, c_void_p]),
+    "qgalore_int8_linear_bwd_data": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                               c_int64, c_void_p, c_void_p]),
+    "qgalore_linear_bwd_weight": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                            c_void_p, c_void_p]),
     "qgalore_sched_init": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float]),
     "qgalore_sched_due": (c_int32, [ctypes.POINTER(Sched), c_int64]),
     "qgalore_sched_refresh": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float,
@@ -397,6 +403,43 @@ def refresh_proj(G: torch.Tensor, r: int, Omega: torch.Tensor, power_iters: int 
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)),
         "qgalore_refresh_proj")
     return Pq, Ps
+
+
+def int8_linear_fwd(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, out=None,
+                    stream=None) -> torch.Tensor:
+    """Y = X W~^T (bf16 T x m) for the INT8 weight Wq (m x n) with group scales Ws."""
+    T, n = X.shape
+    m = Wq.shape[0]
+    Y = out if out is not None else torch.empty((T, m), dtype=torch.bfloat16, device=X.device)
+    _check(lib().qgalore_int8_linear_fwd(
+        _ptr(X, torch.bfloat16, (T, n), "X"), _ptr(Wq, torch.int8, (m, n), "Wq"),
+        _ptr(Ws, torch.float32, (n_groups(m * n),), "Ws"), T, m, n,
+        _ptr(Y, torch.bfloat16, (T, m), "Y"), _stream(stream)), "qgalore_int8_linear_fwd")
+    return Y
+
+
+def int8_linear_bwd_data(dY: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, out=None,
+                         stream=None) -> torch.Tensor:
+    """dX = dY W~ (bf16 T x n)."""
+    T, m = dY.shape
+    n = Wq.shape[1]
+    dX = out if out is not None else torch.empty((T, n), dtype=torch.bfloat16, device=dY.device)
+    _check(lib().qgalore_int8_linear_bwd_data(
+        _ptr(dY, torch.bfloat16, (T, m), "dY"), _ptr(Wq, torch.int8, (m, n), "Wq"),
+        _ptr(Ws, torch.float32, (n_groups(m * n),), "Ws"), T, m, n,
+        _ptr(dX, torch.bfloat16, (T, n), "dX"), _stream(stream)), "qgalore_int8_linear_bwd_data")
+    return dX
+
+
+def linear_bwd_weight(dY: torch.Tensor, X: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """G = dY^T X (bf16 m x n): the weight gradient the optimizer step takes."""
+    T, m = dY.shape
+    n = X.shape[1]
+    G = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dY.device)
+    _check(lib().qgalore_linear_bwd_weight(
+        _ptr(dY, torch.bfloat16, (T, m), "dY"), _ptr(X, torch.bfloat16, (T, n), "X"), T, m, n,
+        _ptr(G, torch.bfloat16, (m, n), "G"), _stream(stream)), "qgalore_linear_bwd_weight")
+    return G
 
 
 class Schedule:

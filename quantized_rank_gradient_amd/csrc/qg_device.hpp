@@ -148,6 +148,9 @@ __device__ __forceinline__ void bstore128(rsrc_t r, uint32_t off, uint4 v) {
   const v4u32 x = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
 }
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, off, 0, 0);
 }

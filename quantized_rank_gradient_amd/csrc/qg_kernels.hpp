@@ -84,4 +84,21 @@ hipError_t launch_rf_jacobi(const float* C, int k, int r, int max_sweeps, float 
 hipError_t launch_rf_signs(float* P, int64_t m, int r, const float* amax_v, float* sgn,
                            hipStream_t s);
 
+// ---- products of a linear layer with an INT8-stored weight (dequantized in the stager) ----
+constexpr int kLinTileM = 128;
+constexpr int kLinTileN = 256;
+enum { kLinFwd = 0, kLinBwdData = 1, kLinBwdWeight = 2 };
+// forward:      act = X (T x n),  out = Y  (T x m)
+// data grad:    act = dY (T x m), out = dX (T x n)
+// weight grad:  act = dY (T x m), act2 = X (T x n), out = G (m x n)
+struct LinArgs {
+  const uint16_t* act;
+  const uint16_t* act2;
+  const int8_t* Wq;
+  const float* Ws;
+  uint16_t* out;
+  int64_t T, m, n;
+};
+hipError_t launch_linear(const LinArgs& a, int which, hipStream_t s);
+
 }  // namespace qg

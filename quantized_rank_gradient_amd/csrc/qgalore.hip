@@ -799,6 +799,59 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
   return e == hipSuccess ? QG_OK : hip_fail(e, "subspace refresh kernels");
 }
 
+// ========================================================= INT8-weight linear layer ===
+
+namespace {
+qg_status check_linear(int64_t T, int64_t m, int64_t n) {
+  if (T < 1 || m < 1 || n < 1 || T > kMaxDim || m > kMaxDim || n > kMaxDim) return QG_ERR_SHAPE;
+  if (m % 8 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
+  if (m * n > kMaxElems || T * m > kMaxElems || T * n > kMaxElems) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+qg_status run_linear(const qg::LinArgs& a, int which, void* stream, const char* what) {
+  qg_status st = device_present();
+  if (st != QG_OK) return st;
+  const hipError_t e = qg::launch_linear(a, which, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QG_OK : hip_fail(e, what);
+}
+}  // namespace
+
+extern "C" qg_status qgalore_int8_linear_fwd(const uint16_t* X, const int8_t* W_q,
+                                             const float* W_scale, int64_t T, int64_t m,
+                                             int64_t n, uint16_t* Y, void* stream) {
+  if (!X || !W_q || !W_scale || !Y) return QG_ERR_NULL;
+  qg_status st = check_linear(T, m, n);
+  if (st != QG_OK) return st;
+  if (!aligned(X, 16) || !aligned(W_q, 16) || !aligned(W_scale, 4) || !aligned(Y, 16))
+    return QG_ERR_ALIGN;
+  qg::LinArgs a{X, nullptr, W_q, W_scale, Y, T, m, n};
+  return run_linear(a, qg::kLinFwd, stream, "INT8-weight forward kernel");
+}
+
+extern "C" qg_status qgalore_int8_linear_bwd_data(const uint16_t* dY, const int8_t* W_q,
+                                                  const float* W_scale, int64_t T, int64_t m,
+                                                  int64_t n, uint16_t* dX, void* stream) {
+  if (!dY || !W_q || !W_scale || !dX) return QG_ERR_NULL;
+  qg_status st = check_linear(T, m, n);
+  if (st != QG_OK) return st;
+  if (!aligned(dY, 16) || !aligned(W_q, 16) || !aligned(W_scale, 4) || !aligned(dX, 16))
+    return QG_ERR_ALIGN;
+  qg::LinArgs a{dY, nullptr, W_q, W_scale, dX, T, m, n};
+  return run_linear(a, qg::kLinBwdData, stream, "INT8-weight data-gradient kernel");
+}
+
+extern "C" qg_status qgalore_linear_bwd_weight(const uint16_t* dY, const uint16_t* X, int64_t T,
+                                               int64_t m, int64_t n, uint16_t* G,
+                                               void* stream) {
+  if (!dY || !X || !G) return QG_ERR_NULL;
+  qg_status st = check_linear(T, m, n);
+  if (st != QG_OK) return st;
+  if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(G, 16)) return QG_ERR_ALIGN;
+  qg::LinArgs a{dY, X, nullptr, nullptr, G, T, m, n};
+  return run_linear(a, qg::kLinBwdWeight, stream, "weight-gradient kernel");
+}
+
 // ====================================================================== schedule ===
 
 extern "C" qg_status qgalore_sched_init(qg_sched* s, int64_t delta0, float gamma) {
