@@ -430,6 +430,8 @@ def main():
     ap.add_argument("--linear", action="store_true",
                     help="instead: time the INT8-weight linear products (forward, data and "
                          "weight gradients) on the 7B layer shapes")
+    ap.add_argument("--refresh-only", action="store_true",
+                    help="instead: time one projection refresh per 7B shape (library vs torch)")
     ap.add_argument("--tokens", type=int, default=8192,
                     help="with --linear: tokens per batch (batch x sequence length)")
     ap.add_argument("--refresh", default="library", choices=("library", "torch"),
@@ -481,6 +483,12 @@ def main():
 
     if args.linear:
         print(json.dumps(linear_bench(torch, B, WL, args.tokens, args.steps)), flush=True)
+        return
+    if args.refresh_only:
+        scfg = WL.CONFIGS["schedule7b"]
+        print(json.dumps({"metric": "projection refresh time (rank 128, 8 extra columns, 2 power "
+                                    "iterations): library vs torch range finder",
+                          "unit": "ms", "shapes": refresh_ms(torch, B, WL, scfg)}), flush=True)
         return
 
     cfg = WL.CONFIGS[args.config]
