@@ -196,6 +196,40 @@ __device__ __forceinline__ float recip_or_zero(float s) {
   return s == 0.0f ? 0.0f : div_rn(1.0f, s);
 }
 
+// floor(x) converted to int32 in one instruction (v_cvt_flr_i32_f32; saturates outside the
+// int32 range). Only called on finite x.
+__device__ __forceinline__ int floor_to_int(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Signed byte K (0..3) of w converted to float in one instruction (SDWA operand select with
+// sign extension).
+template <int K>
+__device__ __forceinline__ float sbyte_to_f32(uint32_t w) {
+  float r;
+  if constexpr (K == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+        : "=v"(r) : "v"(w));
+  else if constexpr (K == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+        : "=v"(r) : "v"(w));
+  else if constexpr (K == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+        : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+        : "=v"(r) : "v"(w));
+  return r;
+}
+
+// The low bytes of four int32 values packed into one word (byte t from q_t).
+__device__ __forceinline__ uint32_t pack4_bytes(int q0, int q1, int q2, int q3) {
+  return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
+         __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
+}
+
 // Sign-extend nibble k (0..7) of a 32-bit word holding 8 packed INT4 codes.
 __device__ __forceinline__ int nibble(uint32_t w, int k) {
   return ((int)(w << (28 - 4 * k))) >> 28;

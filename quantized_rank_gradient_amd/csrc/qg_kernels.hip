@@ -398,23 +398,30 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
   }
   const uint32_t e0 = i * c.n + j16;
   const uint32_t win[4] = {wv.x, wv.y, wv.z, wv.w};
-  float U[16], d[16];
-  int w[16];
+  float U[16], d[16], wf[16];
   float sum = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  static_for<16>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
     U[t] = mul_rn(L.alpha, S[t]);
-    w[t] = (int)(int8_t)(win[t >> 2] >> (8 * (t & 3)));
+    wf[t] = sbyte_to_f32<t & 3>(win[t >> 2]);
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
-    d[t] = sr_pre(w[t], U[t], inv, bits);
-    sum += d[t];   // finite exactly when all sixteen are (|d| stays below 2^8 when finite)
-  }
+    d[t] = __builtin_fmaf((float)bits, 1.0f / 65536.0f, add_rn(wf[t], mul_rn(U[t], inv)));
+    sum += d[t];   // not finite when any of the sixteen is not (or when they overflow a sum)
+  });
   uint32_t wout[4] = {0, 0, 0, 0};
   if (__builtin_isfinite(sum)) {
+    // clamp(floor(d), -127, 127): floor converted in one instruction, then an integer clamp
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      wout[t >> 2] |= (uint32_t)(sr_code(d[t]) & 0xFF) << (8 * (t & 3));
+    for (int k = 0; k < 4; ++k) {
+      int q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = min(max(floor_to_int(d[4 * k + u]), -127), 127);
+      wout[k] = pack4_bytes(q[0], q[1], q[2], q[3]);
+    }
   } else {
+    int w[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) w[t] = (int)wf[t];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int nw = __builtin_isfinite(d[t]) ? sr_code(d[t]) : w[t];
