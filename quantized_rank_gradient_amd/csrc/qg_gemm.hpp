@@ -584,16 +584,18 @@ __device__ __forceinline__ void wait_vm_lds() {
 // accesses across it.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
-// The product with direct-to-LDS stages in a ring of three LDS buffers: stage kt + 2 is
-// loaded while stage kt is multiplied. Per iteration: wait for this wave's share of stage
-// kt and for its own LDS reads of the previous iteration, barrier (every share of stage kt
-// is in LDS, and no wave still reads buffer (kt+2) % 3), issue stage kt + 2 into that
-// buffer, multiply stage kt. The lds area holds 3 * T::STAGE elements.
-template <class T, class SA, class SB>
+// The product with direct-to-LDS stages in a ring of NST LDS buffers (NST = 3: stage kt + 2
+// is loaded while stage kt is multiplied; NST = 2: stage kt + 1). Per iteration: wait for this
+// wave's share of stage kt and for its own LDS reads of the previous iteration, barrier
+// (every share of stage kt is in LDS, and no wave still reads buffer (kt - 1) % NST), issue
+// stage kt + NST - 1 into that buffer, multiply stage kt. The lds area holds NST * T::STAGE
+// elements.
+template <class T, int NST = 3, class SA, class SB>
 __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64_t k_begin,
                                                int64_t k_end, uint16_t* lds,
                                                f32x16 (&acc)[T::XM][T::XN]) {
   static_assert(T::DMA, "tile in the DMA layout");
+  static_assert(NST == 2 || NST == 3, "two or three LDS buffers");
   constexpr int NI = SA::NI + SB::NI;   // loads per wave and stage
 #pragma unroll
   for (int x = 0; x < T::XM; ++x)
@@ -605,24 +607,24 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
   const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
   sa.issue(k_begin, lds);
   sb.issue(k_begin, lds + T::A_ELEMS);
-  if (nk > 1) {
+  if (NST == 3 && nk > 1) {
     sa.issue(k_begin + T::BK, lds + T::STAGE);
     sb.issue(k_begin + T::BK, lds + T::STAGE + T::A_ELEMS);
   }
-  int buf = 0;   // kt % 3
+  int buf = 0;   // kt % NST
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk)
+    if (NST == 3 && kt + 1 < nk)
       wait_vm_lds<NI>();
     else
       wait_vm_lds<0>();
     barrier_nofence();
-    if (kt + 2 < nk) {
-      uint16_t* nxt = lds + (buf == 0 ? 2 : buf - 1) * T::STAGE;
-      sa.issue(k_begin + (int64_t)(kt + 2) * T::BK, nxt);
-      sb.issue(k_begin + (int64_t)(kt + 2) * T::BK, nxt + T::A_ELEMS);
+    if (kt + NST - 1 < nk) {
+      uint16_t* nxt = lds + (buf == 0 ? NST - 1 : buf - 1) * T::STAGE;
+      sa.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt);
+      sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + T::A_ELEMS);
     }
     mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
-    buf = buf == 2 ? 0 : buf + 1;
+    buf = buf == NST - 1 ? 0 : buf + 1;
   }
   // the caller may reuse the LDS area: every wave is done with the last stage
   __syncthreads();

@@ -503,12 +503,18 @@ static_assert(BackBig::BM == kBackTileM(true) && BackBig::BN == kBackTileN(true)
 template <class T>
 using DmaOf = Tile<T::BM, T::BN, T::BK, T::WM, T::WN, T::A_KMAJOR, T::B_KMAJOR, true>;
 
+// LDS and occupancy of a back-projection tile. The small tile (rank up to 128: a K loop of a
+// few stages, time dominated by streaming W) keeps two DMA buffers, so that four workgroups
+// fit on a CU and more weight traffic is in flight; the large one three.
 template <class T>
 struct BackLds {
   // fp32 row pitch of the redistribution block: 4 (mod 16) words, so that the 16 lanes of a
   // 16-byte read group (4 rows x 4 runs of 16 columns) hit distinct banks
   static constexpr int EP = T::WTN + 4;
-  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, 3 * DmaOf<T>::STAGE * 2),
+  static constexpr bool SMALL = T::BN == 128;
+  static constexpr int NST = SMALL ? 2 : 3;   // DMA ring buffers
+  static constexpr int MINB = SMALL ? 4 : 2;  // workgroups per CU
+  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, NST * DmaOf<T>::STAGE * 2),
                                     kThreads / 64 * 32 * EP * 4);
 };
 
@@ -578,7 +584,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   if constexpr (VEC) {
     const DmaBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
     const DmaBf16K<T::BN, T::BK> sb(Nb, L.n, L.r, L.n, j0);
-    gemm_kloop_dma<T>(sa, sb, 0, L.r, lds, acc);
+    gemm_kloop_dma<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, acc);
   } else {
     StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
     StageBf16K<T::BN, T::BK, false> sb(Nb, L.n, L.r, L.r, L.n, j0);
@@ -624,10 +630,10 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   }
 }
 
-// Held to 256 registers per lane: two workgroups per CU (two waves per SIMD) hide the load
-// latency better than more registers in one.
+// The large tile is held to 256 registers per lane: two workgroups per CU (two waves per
+// SIMD) hide the load latency better than more registers in one. The small one to 128.
 template <class T>
-__global__ __launch_bounds__(kThreads, 2) void qg_backproject(StepArgs a) {
+__global__ __launch_bounds__(kThreads, BackLds<T>::MINB) void qg_backproject(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::BYTES / 2];
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
