@@ -313,8 +313,10 @@ struct StageBf16C {
 // these loads apart from the stage being read, and would wait for every load in flight
 // before each LDS transpose read. Completion is tracked by hand instead (wait_vm_lds in
 // gemm_kloop_dma); loads the compiler does not know of can only make its own vmcnt waits
-// stricter, never looser, since vector loads complete in issue order. M0 is saved and
-// restored around the load (the hardware reads it when the load issues).
+// stricter, never looser, since vector loads complete in issue order. M0 (which the hardware
+// reads when the load issues) is set in the same assembly block and declared clobbered.
+// Destinations are LDS byte addresses held in scalar registers: the area's base is converted
+// once per loop, and each load adds constant offsets to it.
 // ---------------------------------------------------------------------------------------
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
@@ -328,19 +330,21 @@ __device__ __forceinline__ v4i32 rsrc_words(const void* base, uint32_t bytes) {
                __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-__device__ __forceinline__ void dma16(v4i32 rs, uint32_t off, uint16_t* lds_kib) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(lds_kib));
-  uint32_t saved;
+// LDS byte address of a pointer into a __shared__ array (uniform across the wave).
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(p));
+}
+
+// One wave-level load of 64 x 16 bytes into the KiB at LDS byte address m0.
+__device__ __forceinline__ void dma16(v4i32 rs, uint32_t off, uint32_t m0) {
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
       : "v"(off), "s"(rs), "s"(m0)
-      : "memory");
+      : "memory", "m0");
 }
 
 // bf16 source [k][c] (row pitch ld, ld % 8 == 0 and c_end % 8 == 0) -> unpadded K-major
@@ -354,11 +358,13 @@ struct DmaBf16K {
   static_assert(NI * 4 * RPI == BK, "a stage splits evenly over the four waves");
   const uint16_t* src;
   uint32_t ld, k_end;
+  uint32_t wofs;     // byte offset of this wave's rows in the tile
   uint32_t vo[NI];   // byte offset of this lane's chunk from the stage's first row
 
   __device__ DmaBf16K(const uint16_t* s, int64_t ld_, int64_t k_end_, int64_t c_end, int c0)
       : src(s), ld((uint32_t)ld_), k_end((uint32_t)k_end_) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wofs = __builtin_amdgcn_readfirstlane(wave * NI * RPI * W * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int row = (wave * NI + q) * RPI + lane / CPR;
@@ -367,12 +373,12 @@ struct DmaBf16K {
     }
   }
 
-  __device__ __forceinline__ void issue(int64_t k0_, uint16_t* tile) const {
+  // tile: LDS byte address of the stage's tile
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t tile) const {
     const uint32_t k0 = (uint32_t)k0_ < k_end ? (uint32_t)k0_ : k_end;
     const v4i32 st = rsrc_words(src + (size_t)k0 * ld, (k_end - k0) * ld * 2);
-    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < NI; ++q) dma16(st, vo[q], tile + (wave * NI + q) * RPI * W);
+    for (int q = 0; q < NI; ++q) dma16(st, vo[q], tile + wofs + q * RPI * W * 2);
   }
 };
 
@@ -386,11 +392,13 @@ struct DmaBf16C {
   static_assert(NI * 64 == W, "a stage splits evenly over the four waves");
   const uint16_t* src;
   uint32_t ld, c_end;
+  uint32_t wofs;             // byte offset of this wave's rows in the tile
   uint32_t vo[NI], kc[NI];   // byte offset of this lane's chunk from column 0; its K offset
 
   __device__ DmaBf16C(const uint16_t* s, int64_t ld_, int64_t c_end_, int c0)
       : src(s), ld((uint32_t)ld_), c_end((uint32_t)c_end_) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wofs = __builtin_amdgcn_readfirstlane(wave * NI * 16 * 32 * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int row = (wave * NI + q) * 16 + lane / 4;
@@ -400,14 +408,19 @@ struct DmaBf16C {
     }
   }
 
-  __device__ __forceinline__ void issue(int64_t k0_, uint16_t* tile) const {
+  // tile: LDS byte address of the stage's tile
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t tile) const {
     const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
     const v4i32 st = rsrc_words(src + k0, (c_end * ld - k0) * 2);
     const uint32_t lim = ld - k0;   // K values left in the rows
-    const int wave = threadIdx.x >> 6;
+    if (lim >= (uint32_t)BK) {
 #pragma unroll
-    for (int q = 0; q < NI; ++q)
-      dma16(st, kc[q] < lim ? vo[q] : kOOB, tile + (wave * NI + q) * 16 * 32);
+      for (int q = 0; q < NI; ++q) dma16(st, vo[q], tile + wofs + q * 16 * 32 * 2);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NI; ++q)
+        dma16(st, kc[q] < lim ? vo[q] : kOOB, tile + wofs + q * 16 * 32 * 2);
+    }
   }
 };
 
@@ -605,11 +618,12 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
   if (k_end <= k_begin) return;
   const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
-  sa.issue(k_begin, lds);
-  sb.issue(k_begin, lds + T::A_ELEMS);
+  const uint32_t base = lds_addr(lds);   // byte addresses: stage s at base + 2 s STAGE
+  sa.issue(k_begin, base);
+  sb.issue(k_begin, base + 2 * T::A_ELEMS);
   if (NST == 3 && nk > 1) {
-    sa.issue(k_begin + T::BK, lds + T::STAGE);
-    sb.issue(k_begin + T::BK, lds + T::STAGE + T::A_ELEMS);
+    sa.issue(k_begin + T::BK, base + 2 * T::STAGE);
+    sb.issue(k_begin + T::BK, base + 2 * (T::STAGE + T::A_ELEMS));
   }
   int buf = 0;   // kt % NST
   for (int kt = 0; kt < nk; ++kt) {
@@ -619,9 +633,9 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
       wait_vm_lds<0>();
     barrier_nofence();
     if (kt + NST - 1 < nk) {
-      uint16_t* nxt = lds + (buf == 0 ? NST - 1 : buf - 1) * T::STAGE;
+      const uint32_t nxt = base + 2 * (buf == 0 ? NST - 1 : buf - 1) * T::STAGE;
       sa.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt);
-      sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + T::A_ELEMS);
+      sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + 2 * T::A_ELEMS);
     }
     mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
     buf = buf == NST - 1 ? 0 : buf + 1;
