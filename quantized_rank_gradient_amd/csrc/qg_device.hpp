@@ -50,6 +50,7 @@ struct StepArgs {
   const LayerDev* table;     // grouped launch: per-layer descriptors
   const int32_t* wg_layer;   // grouped launch: workgroup -> layer index for this kernel
   float beta1, beta2, c1, c2, bc1, bc2;
+  double ibc1, ibc2;         // RN64(1 / bc1), RN64(1 / bc2)
   uint32_t step, seed_lo, seed_hi;
 };
 
@@ -172,20 +173,19 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Correctly rounded fp32 square root: the hardware estimate is within one ulp; the exact
-// residuals x - s_lo*s and x - s_hi*s (one rounding each in an fma) tell which of the
-// neighbours is nearest. A midpoint can never be an exact square root of an fp32 value,
-// so no tie occurs.
-__device__ __forceinline__ float sqrt_rn(float x) {
-  float s = __builtin_sqrtf(x);
-  if (!(x > 0.0f) || !__builtin_isfinite(x)) return s;
-  const float s_lo = __uint_as_float(__float_as_uint(s) - 1u);
-  const float s_hi = __uint_as_float(__float_as_uint(s) + 1u);
-  const float r_lo = __builtin_fmaf(-s_lo, s, x);
-  const float r_hi = __builtin_fmaf(-s_hi, s, x);
-  if (r_lo <= 0.0f) s = s_lo;
-  if (r_hi > 0.0f) s = s_hi;
-  return s;
+// Correctly rounded fp32 square root. The compiler's sqrtf lowering (HIP's default
+// correctly rounded fp32 divide and sqrt) already refines the hardware estimate with the
+// exact residuals of its two neighbours, scaling tiny inputs first.
+__device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
+// a / b correctly rounded to fp32, for a divisor known on the host as yd = RN64(1 / b):
+// the fp64 product a * yd is within 2^-52 (relative) of a / b, while the quotient of two
+// fp32 values is either a float or at least ~2^-48 (relative) away from every midpoint
+// between floats (its distance to a 25-bit midpoint is a non-zero multiple of 2^-47 of
+// its size), so rounding the product to fp32 gives RN(a / b). Zeros, infinities, NaN,
+// subnormal quotients and overflow all round as the quotient does.
+__device__ __forceinline__ float div_by_recip64(float a, double yd) {
+  return (float)((double)a * yd);
 }
 
 __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }

@@ -98,8 +98,8 @@ __device__ __forceinline__ void adam_group(const StepArgs& a, const LayerDev& L,
     const float v0 = mul_rn((float)vq[t], vs);
     m1[t] = add_rn(mul_rn(a.beta1, m0), mul_rn(a.c1, R[t]));
     v1[t] = add_rn(mul_rn(a.beta2, v0), mul_rn(a.c2, mul_rn(R[t], R[t])));
-    const float mh = div_rn(m1[t], a.bc1);
-    const float vh = div_rn(v1[t], a.bc2);
+    const float mh = div_by_recip64(m1[t], a.ibc1);   // RN(m1 / bc1)
+    const float vh = div_by_recip64(v1[t], a.ibc2);   // RN(v1 / bc2)
     N[t] = -div_rn(mul_rn(L.lr, mh), add_rn(sqrt_rn(vh), L.eps));
     if (e0 + t >= numel) {
       m1[t] = 0.f;
@@ -212,8 +212,8 @@ __device__ __forceinline__ void adam_group16(const StepArgs& a, const LayerDev& 
     float N[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float mh = div_rn(m1[4 * k + t], a.bc1);
-      const float vh = div_rn(v1[4 * k + t], a.bc2);
+      const float mh = div_by_recip64(m1[4 * k + t], a.ibc1);   // RN(m1 / bc1)
+      const float vh = div_by_recip64(v1[4 * k + t], a.ibc2);   // RN(v1 / bc2)
       N[t] = -div_rn(mul_rn(L.lr, mh), add_rn(sqrt_rn(vh), L.eps));
       const int qm = (int)fminf(fmaxf(rintf(mul_rn(m1[4 * k + t], im)), -127.f), 127.f);
       const int qv = (int)fminf(fmaxf(rintf(mul_rn(v1[4 * k + t], iv)), -127.f), 127.f);

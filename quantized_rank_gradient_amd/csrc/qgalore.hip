@@ -146,6 +146,10 @@ void step_constants(float beta1, float beta2, int64_t step, StepArgs& a) {
   a.c2 = (float)(1.0 - b2);
   a.bc1 = (float)(1.0 - std::pow(b1, (double)step));
   a.bc2 = (float)(1.0 - std::pow(b2, (double)step));
+  // reciprocals of the fp32 bias corrections, correctly rounded in fp64 (the kernels divide
+  // by bc1 and bc2 through them); bc is positive for 0 <= beta < 1 and step >= 1
+  a.ibc1 = 1.0 / (double)a.bc1;
+  a.ibc2 = 1.0 / (double)a.bc2;
   a.step = (uint32_t)step;
 }
 
