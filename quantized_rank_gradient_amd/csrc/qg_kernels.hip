@@ -19,9 +19,10 @@ namespace qg {
 // ========================================================================== dequant ===
 // P~ = bf16(q * s) for the whole m x r projection, once per step, into the workspace: the
 // projection and the back-projection both stage P~ from it (the INT4 (or INT8) store is
-// what persists; this copy lives only for the step). 256 threads x 8 codes per workgroup.
-// A bf16 projection needs no pass (its layers have no workgroups here).
-
+// what persists; this copy lives only for the step). Each thread converts 32 consecutive
+// codes (one 16-byte INT4 load, 64 bytes of bf16 out), which lie in one 256-element scale
+// group; a chunk that runs past the end of P is converted 8 codes at a time. A bf16
+// projection needs no pass (its layers have no workgroups here).
 // Dequantize 8 INT8 codes (two little-endian words) with their group scale.
 __device__ __forceinline__ uint4 dequant8_i8(uint2 w, float s) {
   float f[8];
@@ -36,20 +37,34 @@ __global__ __launch_bounds__(kThreads) void qg_dequant(StepArgs a) {
   int local;
   const LayerDev L = fetch_layer(a, KDEQ, blockIdx.x, local);
   const uint32_t numel = (uint32_t)(L.m * L.r);
-  const uint32_t e = ((uint32_t)local * kThreads + threadIdx.x) * 8;
-  const bool in = e < numel;
+  const uint32_t e = ((uint32_t)local * kThreads + threadIdx.x) * kDeqCodes;
+  if (e >= numel) return;
   const rsrc_t rs = make_rsrc(L.Ps, ((numel + kGroup - 1) / kGroup) * 4);
   const rsrc_t ro = make_rsrc(a.ws + L.off_p, numel * 2);
-  const float sc = bloadf(rs, in ? (e >> 8) * 4 : kOOB);
-  uint4 out;
-  if (L.p_format == kPInt8) {
-    const rsrc_t rq = make_rsrc(L.Pq, numel);
-    out = dequant8_i8(bload64(rq, in ? e : kOOB), sc);
+  const float sc = bloadf(rs, (e >> 8) * 4);
+  const bool i8 = L.p_format == kPInt8;
+  const rsrc_t rq = make_rsrc(L.Pq, i8 ? numel : (numel + 1) / 2);
+  if (e + kDeqCodes <= numel) {
+    uint32_t w[8];   // INT4: words 0..3 hold the 32 codes; INT8: words 0..7
+    if (i8) {
+      const uint4 w0 = bload128(rq, e), w1 = bload128(rq, e + 16);
+      w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+      w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+    } else {
+      const uint4 w0 = bload128(rq, e >> 1);
+      w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bstore128(ro, (e + 8 * c) * 2,
+                i8 ? dequant8_i8(make_uint2(w[2 * c], w[2 * c + 1]), sc) : dequant8(w[c], sc));
   } else {
-    const rsrc_t rq = make_rsrc(L.Pq, (numel + 1) / 2);
-    out = dequant8(bload32(rq, in ? e >> 1 : kOOB), sc);
+    // the last, partial chunk: numel is a multiple of 8
+    for (uint32_t e8 = e; e8 < numel; e8 += 8) {
+      const uint4 out = i8 ? dequant8_i8(bload64(rq, e8), sc) : dequant8(bload32(rq, e8 >> 1), sc);
+      bstore128(ro, e8 * 2, out);
+    }
   }
-  bstore128(ro, in ? e * 2 : kOOB, out);
 }
 
 // ============================================================================== Adam ===

@@ -38,6 +38,8 @@ struct CosBatch {
   int iters_cubic_split; // and with hi/lo split operands
 };
 
+constexpr int kDeqCodes = 32;   // projection codes each dequant thread converts
+
 // Tile edges of the MFMA kernels (back-projection: "big" for rank above 128).
 constexpr int kProjTileM = 128;
 constexpr int kProjTileN = 256;

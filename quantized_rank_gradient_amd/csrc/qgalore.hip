@@ -198,7 +198,7 @@ int grid_adam(const LayerDev& L) {
 }
 int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
 int grid_dequant(const LayerDev& L) {
-  return L.p_format == QG_P_BF16 ? 0 : (int)cdiv(L.m * L.r, qg::kThreads * 8);
+  return L.p_format == QG_P_BF16 ? 0 : (int)cdiv(L.m * L.r, qg::kThreads * qg::kDeqCodes);
 }
 
 qg_status launch_step(const StepArgs& a, const int grid[4], bool big, hipStream_t s) {
