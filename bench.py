@@ -353,6 +353,34 @@ def copy_bandwidth(torch, gib=2.0, reps=5):
     return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1))
 
 
+def mfma_sustained(torch, B, grid=1024, iters=2000, reps=3):
+    """TFLOP/s of the library's MFMA calibration kernel (bf16 32x32x16 products from register
+    operands, no memory traffic) on random operands like the step's (bf16 ~N(0, 0.05^2)) and
+    on constant ones: the rate the matrix cores sustain under the clock the load allows,
+    beside the published dense peak that the roofline fraction is taken against."""
+    out = {}
+    buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20240711)
+    for label, ops in (("random_operands", (torch.randn(1 << 23, generator=gen, device="cuda")
+                                             * 0.05).to(torch.bfloat16)),
+                       ("constant_operands", torch.full((1 << 23,), 0.01, device="cuda",
+                                                        dtype=torch.bfloat16))):
+        flops = B.mfma_probe(ops, buf, grid, iters)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            B.mfma_probe(ops, buf, grid, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[label] = round(flops / (ms / 1e3) / 1e12, 1)
+        del ops
+    out["unit"] = "TFLOP/s"
+    return out
+
+
 def library_gemm_ms(torch, cfg, r, reps=20):
     """torch (hipBLASLt) bf16 matmuls with the shapes of the two contractions, summed over
     the layer set: R = P^T G with P^T stored contiguous, and P N (no fused epilogues). A
@@ -496,6 +524,9 @@ def main():
     copy = copy_bandwidth(torch, args.copy_gib) if args.copy_gib > 0 else None
     if copy:
         log(f"device copy: {json.dumps(copy)}")
+    sustained = mfma_sustained(torch, B) if args.copy_gib > 0 else None
+    if sustained:
+        log(f"sustained MFMA rate: {json.dumps(sustained)}")
     t0 = time.time()
     G_list, W_list, Ws_list = [], [], []
     for L in cfg.layers:
@@ -569,6 +600,7 @@ def main():
         "cossim_ms": main_res["cossim_ms"],
         "roofline": main_res["roofline"],
         "copy_gbs": copy["gbs"] if copy else None,
+        "mfma_sustained": sustained,
         "variants": {r["config"]: {k: r[k] for k in ("rank", "value", "ms_per_step", "tflops",
                                                     "kernel_ms", "optimizer_ms",
                                                     "refresh_tests_per_step",

@@ -255,6 +255,19 @@ int32_t qgalore_sched_due(const qg_sched *s, int64_t t);
  * *doubled (optional) is set to 1 when the interval doubled. */
 qg_status qgalore_sched_refresh(qg_sched *s, int64_t t, float cossim, int32_t *doubled);
 
+/* ------------------------------------------------------------------------------------
+ * Calibration of the compute roofline (not part of a step): the bf16 MFMA rate the chip
+ * sustains on given operand data, since the clock under sustained matrix load depends on
+ * the operands' switching activity. `grid` workgroups of 4 waves; every wave reads 4 A and
+ * 4 B MFMA fragments (8 bf16 each, consecutive 16-byte chunks of `operands`, wrapping
+ * around) once and runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 (32768 flops each),
+ * so a launch does grid * 4 * iters * 16 * 32768 flops. out: grid * 256 floats (one
+ * checksum per lane). operands: n_elems bf16, n_elems a multiple of 8 (>= 8), 16-byte
+ * aligned. grid in [1, 65536], iters in [1, 2^20]. Asynchronous on `stream`.
+ * ---------------------------------------------------------------------------------- */
+qg_status qgalore_mfma_probe(const uint16_t *operands, int64_t n_elems, float *out, int32_t grid,
+                             int32_t iters, void *stream);
+
 /* ------------------------------------------------------------------------------------ */
 const char *qgalore_status_str(qg_status s);
 const char *qgalore_last_error(void);   /* thread-local text of the last QG_ERR_HIP */

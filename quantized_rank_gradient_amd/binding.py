@@ -90,6 +90,7 @@ EXPORTS = {
     "qgalore_sched_due": (c_int32, [ctypes.POINTER(Sched), c_int64]),
     "qgalore_sched_refresh": (c_int32, [ctypes.POINTER(Sched), c_int64, c_float,
                                         ctypes.POINTER(c_int32)]),
+    "qgalore_mfma_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_int32, c_void_p]),
     "qgalore_status_str": (ctypes.c_char_p, [c_int32]),
     "qgalore_last_error": (ctypes.c_char_p, []),
     "qgalore_version": (ctypes.c_char_p, []),
@@ -373,6 +374,19 @@ def quantize_proj(P: torch.Tensor, stream=None, fmt: str = "int4"):
     _check(lib().qgalore_quantize_proj(src, m, r, Pq.data_ptr(), Ps.data_ptr(), _stream(stream)),
            "qgalore_quantize_proj")
     return Pq, Ps
+
+
+def mfma_probe(operands: torch.Tensor, out: torch.Tensor, grid: int, iters: int,
+               stream=None) -> float:
+    """Launch the MFMA calibration kernel on bf16 `operands` (see qgalore_mfma_probe);
+    returns the flops the launch performs."""
+    if operands.dtype != torch.bfloat16 or not operands.is_contiguous():
+        raise TypeError("operands must be a contiguous bf16 tensor")
+    if out.dtype != torch.float32 or out.numel() < grid * 256:
+        raise ValueError("out must hold grid * 256 float32 values")
+    _check(lib().qgalore_mfma_probe(operands.data_ptr(), operands.numel(), out.data_ptr(), grid,
+                                    iters, _stream(stream)), "qgalore_mfma_probe")
+    return float(grid) * 4 * iters * 16 * 32768
 
 
 def refresh_workspace_bytes(m: int, n: int, r: int, oversample: int = 8) -> int:

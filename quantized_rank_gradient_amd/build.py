@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgalore.so")
-SOURCES = ("qg_kernels.hip", "qg_cossim.hip", "qg_refresh.hip", "qg_linear.hip", "qgalore.hip")
+SOURCES = ("qg_kernels.hip", "qg_cossim.hip", "qg_refresh.hip", "qg_linear.hip", "qg_probe.hip",
+           "qgalore.hip")
 ARCH = os.environ.get("QGALORE_ARCH", "gfx950")
 
 FLAGS = [

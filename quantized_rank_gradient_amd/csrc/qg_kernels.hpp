@@ -54,6 +54,10 @@ hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, floa
                                 hipStream_t s);
 hipError_t launch_quantize_int8(const float* P, int64_t numel, int8_t* Pq, float* Ps,
                                 hipStream_t s);
+// Calibration kernel (qg_probe.hip): `grid` workgroups of 4 waves, each wave 16 bf16 MFMA
+// 32x32x16 per round for `iters` rounds on fragments read from `operands`.
+hipError_t launch_mfma_probe(const uint16_t* operands, int64_t n_elems, float* out, int grid,
+                             int iters, hipStream_t s);
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s);
 
 // ---- subspace refresh (randomized range finder of G's leading left singular vectors) ----

@@ -892,6 +892,19 @@ extern "C" qg_status qgalore_sched_refresh(qg_sched* s, int64_t t, float cossim,
   return QG_OK;
 }
 
+// ================================================================== calibration ===
+
+extern "C" qg_status qgalore_mfma_probe(const uint16_t* operands, int64_t n_elems, float* out,
+                                        int32_t grid, int32_t iters, void* stream) {
+  if (!operands || !out) return QG_ERR_NULL;
+  if (n_elems < 8 || n_elems % 8 != 0 || n_elems > (int64_t(1) << 32)) return QG_ERR_SHAPE;
+  if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 20)) return QG_ERR_ARG;
+  if (!aligned(operands, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
+  const hipError_t e = qg::launch_mfma_probe(operands, n_elems, out, grid, iters,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QG_OK : hip_fail(e, "mfma probe launch");
+}
+
 // ========================================================================= misc ===
 
 extern "C" const char* qgalore_status_str(qg_status s) {

@@ -153,3 +153,17 @@ def test_library_schedule_matches_oracle_schedule():
                 cs = float(np.float32(vals[t]))
                 assert lib_s.refresh(t, cs if ora.count else None) == ora.refresh(t, cs if ora.count else None)
                 assert (lib_s.delta, lib_s.next_refresh, lib_s.count) == (ora.delta, ora.next_refresh, ora.count)
+
+
+def test_mfma_probe_rejects_bad_arguments_before_hip():
+    L = B.lib()
+    buf = (ctypes.c_uint16 * 64)()
+    out = (ctypes.c_float * 256)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    o = ctypes.cast(out, ctypes.c_void_p)
+    assert L.qgalore_mfma_probe(None, 64, o, 1, 1, None) == 1            # QG_ERR_NULL
+    assert L.qgalore_mfma_probe(p, 60, o, 1, 1, None) == 2               # not a multiple of 8
+    assert L.qgalore_mfma_probe(p, 0, o, 1, 1, None) == 2
+    assert L.qgalore_mfma_probe(p, 64, o, 0, 1, None) == 5               # grid < 1
+    assert L.qgalore_mfma_probe(p, 64, o, 1, 0, None) == 5               # iters < 1
+    assert L.qgalore_mfma_probe(p, 64, o, 70000, 1, None) == 5
