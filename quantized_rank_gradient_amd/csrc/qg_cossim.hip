@@ -27,6 +27,7 @@ namespace qg {
 
 using CosTile = Tile<kCosTile, kCosTile, 32, 2, 2, true, true>;     // C = P~n^T P~o, X^T X
 using NsTileNN = Tile<kCosTile, kCosTile, 32, 2, 2, false, true>;   // X A
+using CosTileC = Tile<kCosCTile, kCosCTile, 32, 2, 2, true, true>;  // C at rank >= 256
 static_assert(CosTile::XM == NsTileNN::XM && CosTile::XN == NsTileNN::XN, "same wave tiling");
 
 // --------------------------------------------------------------- fp32 -> LDS stagers ---
@@ -158,55 +159,56 @@ __device__ __forceinline__ uint16_t* pair_bf(const CosBatch& b, int p, int64_t o
 
 // The projections' dequant (INT4 or INT8 codes times the group scale, rounded to bf16) or
 // the bf16 values themselves, staged straight into LDS.
-template <class SA>
+template <class T, class SA>
 __device__ __forceinline__ void cos_c_product(SA& sa, SA& sb, int64_t k_begin, int64_t k_end,
-                                              uint16_t* lds,
-                                              f32x16 (&acc)[CosTile::XM][CosTile::XN]) {
-  gemm_kloop<CosTile, 1>(
-      sa, sb, [](auto& st, uint16_t* p) { st.template store<CosTile::A_PITCH>(p); },
-      [](auto& st, uint16_t* p) { st.template store<CosTile::B_PITCH>(p + CosTile::A_ELEMS); },
+                                              uint16_t* lds, f32x16 (&acc)[T::XM][T::XN]) {
+  gemm_kloop<T, 1>(
+      sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
+      [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); },
       k_begin, k_end, lds, acc);
 }
 
+// T: CosTile (edge kCosTile) or CosTileC (edge kCosCTile), as cos_ctile(r) selects.
+template <class T>
 __global__ __launch_bounds__(kThreads) void qg_cossim_gemm(CosBatch b) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CosTile::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
   int local;
   // consecutive blocks (one pair's tiles) share an XCD and its L2
   const int p = pair_of_block(b, xcd_remap(blockIdx.x, gridDim.x), local);
   const CosPair& q = b.pair[p];
-  const int per_split = b.tiles * b.tiles;
+  const int per_split = b.ctiles * b.ctiles;
   const int s = local / per_split;
   const int rem = local - s * per_split;
-  const int ti = rem / b.tiles, tj = rem - ti * b.tiles;
-  const int i0 = ti * CosTile::BM, j0 = tj * CosTile::BN;
+  const int ti = rem / b.ctiles, tj = rem - ti * b.ctiles;
+  const int i0 = ti * T::BM, j0 = tj * T::BN;
   const int64_t k_begin = (int64_t)s * q.kslab;
   const int64_t k_end = min<int64_t>(q.m, k_begin + q.kslab);
-  f32x16 acc[CosTile::XM][CosTile::XN];
+  f32x16 acc[T::XM][T::XN];
   if (q.format == kPInt8) {
-    StageInt8K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
-    StageInt8K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
-    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+    StageInt8K<T::BM, T::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+    StageInt8K<T::BM, T::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product<T>(sa, sb, k_begin, k_end, lds, acc);
   } else if (q.format == kPBf16) {
     const uint16_t* pa = reinterpret_cast<const uint16_t*>(q.qa);
     const uint16_t* pb = reinterpret_cast<const uint16_t*>(q.qb);
-    StageBf16K<CosTile::BM, CosTile::BK, true> sa(pa, b.r, q.m, k_end, b.r, i0);
-    StageBf16K<CosTile::BM, CosTile::BK, true> sb(pb, b.r, q.m, k_end, b.r, j0);
-    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+    StageBf16K<T::BM, T::BK, true> sa(pa, b.r, q.m, k_end, b.r, i0);
+    StageBf16K<T::BM, T::BK, true> sb(pb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product<T>(sa, sb, k_begin, k_end, lds, acc);
   } else {
-    StageInt4K<CosTile::BM, CosTile::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
-    StageInt4K<CosTile::BM, CosTile::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
-    cos_c_product(sa, sb, k_begin, k_end, lds, acc);
+    StageInt4K<T::BM, T::BK> sa(q.qa, q.sa, b.r, q.m, k_end, b.r, i0);
+    StageInt4K<T::BM, T::BK> sb(q.qb, q.sb, b.r, q.m, k_end, b.r, j0);
+    cos_c_product<T>(sa, sb, k_begin, k_end, lds, acc);
   }
   float* out = pair_mat(b, p, b.off_part) + (int64_t)s * b.r * b.r;
 #pragma unroll
-  for (int x = 0; x < CosTile::XM; ++x)
+  for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < CosTile::XN; ++y) {
-      const int64_t j = j0 + acc_col<CosTile>(y);
+    for (int y = 0; y < T::XN; ++y) {
+      const int64_t j = j0 + acc_col<T>(y);
       if (j >= b.r) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + acc_row<CosTile>(x, v);
+        const int64_t i = i0 + acc_row<T>(x, v);
         if (i < b.r) gstore(out + i * b.r + j, (float)acc[x][y][v]);
       }
     }
@@ -436,8 +438,11 @@ __global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
   constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
   int gemm_blocks = 0;
-  for (int p = 0; p < b.count; ++p) gemm_blocks += b.pair[p].split * b.tiles * b.tiles;
-  hipLaunchKernelGGL(qg_cossim_gemm, dim3(gemm_blocks), dim3(kThreads), 0, s, b);
+  for (int p = 0; p < b.count; ++p) gemm_blocks += b.pair[p].split * b.ctiles * b.ctiles;
+  if (cos_ctile(b.r) == kCosCTile)
+    hipLaunchKernelGGL(qg_cossim_gemm<CosTileC>, dim3(gemm_blocks), dim3(kThreads), 0, s, b);
+  else
+    hipLaunchKernelGGL(qg_cossim_gemm<CosTile>, dim3(gemm_blocks), dim3(kThreads), 0, s, b);
   const int eblocks = b.count * b.nblk;
   hipLaunchKernelGGL(qg_cossim_reduce, dim3(eblocks), dim3(kThreads), 0, s, b);
   hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b, b.off_norm, 0.0f,

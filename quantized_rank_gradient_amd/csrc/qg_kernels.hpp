@@ -10,6 +10,11 @@ constexpr int kCosMaxPairs = 32;
 // Output tile edge of the similarity kernels: small tiles, so that the short K loops of the
 // r x r products run with several workgroups per CU.
 constexpr int kCosTile = 64;
+// Output tile edge of the cross product C = P~_new^T P~_old (K = the projections' rows) for
+// rank 256 and above, where the long K loop pays for a larger tile and split-K fills the
+// chip; smaller ranks use kCosTile.
+constexpr int kCosCTile = 128;
+constexpr int cos_ctile(int r) { return r >= 256 ? kCosCTile : kCosTile; }
 
 struct CosPair {
   int format;          // projection storage format of both (kPInt4, kPInt8, kPBf16)
@@ -33,6 +38,7 @@ struct CosBatch {
   int64_t off_blk;       // per-block partial sums
   int64_t off_norm;      // [0]: squared Frobenius norm of C, [1]: of X0^T X0
   int count, r, tiles, nblk;
+  int ctiles;             // tiles per edge of the C product (edge cos_ctile(r))
   int iters_quintic;     // Newton-Schulz iterations lifting small singular values (bf16)
   int iters_cubic_bf16;  // then cubic iterations with bf16 operands (at least one)
   int iters_cubic_split; // and with hi/lo split operands

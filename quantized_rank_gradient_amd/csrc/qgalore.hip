@@ -460,14 +460,18 @@ constexpr int kNsCubicSplit = 1;
 static_assert(kNsCubicBf16 >= 1, "the last bf16 step hands X over in fp32");
 
 struct CosLayout {
-  int split, tiles, nblk;
+  int split, tiles, ctiles, nblk;
   int64_t off_part, off_c, off_x, off_xn, off_a, off_xb0, off_xb1, off_ab, off_bb, off_blk,
       off_norm, stride;
 };
 CosLayout cos_layout(int64_t r) {
   CosLayout c;
   c.tiles = (int)cdiv(r, qg::kCosTile);
-  c.split = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(64, (int64_t)c.tiles * c.tiles)));
+  // the C product: edge cos_ctile(r); enough K splits for about 64 (64-edge tiles) or 256
+  // (128-edge tiles) workgroups per pair, at most 8
+  c.ctiles = (int)cdiv(r, qg::cos_ctile((int)r));
+  const int64_t want = qg::cos_ctile((int)r) == qg::kCosCTile ? 256 : 64;
+  c.split = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(want, (int64_t)c.ctiles * c.ctiles)));
   const int64_t n2 = r * r;
   c.nblk = (int)cdiv(n2, (int64_t)qg::kThreads * 4);
   const int64_t mat = round_up(n2 * 4, 256);
@@ -539,6 +543,7 @@ extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P
     b.count = std::min<int32_t>(qg::kCosMaxPairs, count - first);
     b.r = (int)r;
     b.tiles = c.tiles;
+    b.ctiles = c.ctiles;
     b.nblk = c.nblk;
     b.ws = static_cast<char*>(workspace);
     b.pair_stride = c.stride;
@@ -572,7 +577,7 @@ extern "C" qg_status qgalore_cossim_batch(const qg_proj* P_new, const qg_proj* P
       q.kslab = (int)(cdiv(kchunks, split) * kK);
       q.split = (int)cdiv(pn.m, q.kslab);
       q.gemm_base = base;
-      base += q.split * c.tiles * c.tiles;
+      base += q.split * c.ctiles * c.ctiles;
     }
     const hipError_t e = qg::launch_cossim_batch(b, out_dev + first, s);
     if (e != hipSuccess) return hip_fail(e, "similarity kernels");

@@ -194,7 +194,7 @@ def test_cossim_batch_of_mixed_row_counts():
     got = out.cpu().numpy()
     assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
 
-@pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (4096, 1024)])
+@pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (1376, 264), (4096, 1024)])
 def test_cossim_matches_oracle(m, r):
     B = _B()
     rng = np.random.default_rng(m + r)
