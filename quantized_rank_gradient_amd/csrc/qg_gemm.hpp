@@ -4,8 +4,8 @@
 // A workgroup of 4 wave64 computes a BM x BN output tile; the waves sit in a WM x WN grid and
 // each owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulation). K is consumed BK at a time through LDS
-// stages: either a double buffer filled from registers (gemm_kloop), or a ring of three
-// stages filled by LDS DMA with two stages in flight (gemm_kloop_dma).
+// stages: either a double buffer filled from registers (gemm_kloop), or a ring of two or
+// three stages filled by LDS DMA with one or two stages in flight (gemm_kloop_dma).
 //
 // An MFMA lane needs 8 consecutive K values of one row of A (or one column of B). Operands
 // are kept in LDS in the layout their source has, so staging is a straight copy (plus the
