@@ -208,13 +208,18 @@ KERNEL_SOURCES = ("qg_kernels.hip", "qg_gemm.hpp", "qg_device.hpp", "qg_kernels.
 
 
 def kernel_source_hash():
-    """sha256 over the sources of the step kernels: HBM traffic figures taken by a counter
-    run apply only while this hash is unchanged."""
+    """sha256 over the code of the step kernels' sources (comments and blank lines
+    dropped): HBM traffic figures taken by a counter run apply only while this hash is
+    unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "quantized_rank_gradient_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantized_rank_gradient_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [ln.split("//")[0].rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
