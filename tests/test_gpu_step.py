@@ -194,6 +194,26 @@ def test_cossim_batch_of_mixed_row_counts():
     got = out.cpu().numpy()
     assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
 
+def test_cossim_batch_large_rank():
+    """A batch of eight pairs at rank 1024 (the cross product on 128-edge tiles with split-K),
+    with similarities from near 0 to 1."""
+    B = _B()
+    r, m = 1024, 1024 + 8 * 44
+    pairs, want = [], []
+    for k in range(8):
+        rng = np.random.default_rng(500 + k)
+        A = np.linalg.qr(rng.standard_normal((m, r)))[0].astype(np.float32)
+        Bm = np.linalg.qr(A + 0.25 * k * rng.standard_normal((m, r)) / np.sqrt(m))[0].astype(np.float32)
+        qa, sa = O.quantize_proj(Bm)
+        qb, sb = O.quantize_proj(A)
+        want.append(O.cossim(qa, sa, qb, sb, m, r))
+        pairs.append(tuple(torch.from_numpy(x).cuda() for x in (qa, sa, qb, sb)) + (m,))
+    out = torch.full((len(pairs),), -1.0, device="cuda")
+    B.cossim_batch(pairs, r, out)
+    got = out.cpu().numpy()
+    assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
+
+
 @pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (1376, 264), (4096, 1024)])
 def test_cossim_matches_oracle(m, r):
     B = _B()
