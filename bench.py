@@ -81,6 +81,9 @@ class Variant:
                                                  fast, fmt)
         self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
                                                  eps=cfg.eps, alpha=cfg.alpha))
+        # dequantized projections are kept between steps; a refresh replaces a layer's P, so
+        # every tested layer is marked changed and dequantized again at the next step
+        self.plan.cache_proj(True)
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(r, 32))
         self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device="cuda")
@@ -96,7 +99,8 @@ class Variant:
             f"workspace {self.plan.workspace_bytes / 2**30:.2f} GiB")
 
     def step(self):
-        """One full step: grouped optimizer step, then the due refresh tests."""
+        """One full step: grouped optimizer step, then the due refresh tests. A layer due
+        for a refresh gets a new projection, which the next step dequantizes again."""
         self.t += 1
         t = self.t
         self.plan.step(t, 1234, self.ws)
@@ -108,6 +112,7 @@ class Variant:
         vals = self.cs_out[: len(due)].cpu().tolist() if due else []
         for k, v in zip(due, vals):
             self.sched[k].refresh(t, v)
+            self.plan.proj_changed(k)
         self.tests += len(due)
 
     def time_steps(self, steps, warmup):

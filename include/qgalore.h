@@ -151,6 +151,18 @@ qg_status qgalore_plan_destroy(qg_plan *plan);
 qg_status qgalore_plan_enable_timing(qg_plan *plan, int32_t max_steps);
 qg_status qgalore_plan_kernel_times(qg_plan *plan, float out_ms[4], int32_t *steps);
 
+/* Keeping dequantized projections between steps. A step dequantizes every INT4 (or INT8)
+ * projection into its bf16 copy in the workspace; a projection changes only when the
+ * schedule refreshes it, so with caching on (enable = 1) a step dequantizes only the layers
+ * marked by qgalore_plan_proj_changed since the previous step (plus all of them on the
+ * first step, and whenever the workspace pointer differs from the previous step's).
+ * Caller's contract while caching is on: call qgalore_plan_proj_changed(plan, layer) after
+ * writing a layer's P_q or P_scale and before the next step, and let nothing but the plan's
+ * steps write the workspace. Off (the default), every step dequantizes every projection.
+ * `layer` indexes the qg_layer array given to qgalore_plan_create (QG_ERR_ARG outside it). */
+qg_status qgalore_plan_cache_proj(qg_plan *plan, int32_t enable);
+qg_status qgalore_plan_proj_changed(qg_plan *plan, int32_t layer);
+
 /* ------------------------------------------------------------------------------------
  * Subspace similarity (AIMech Q-GaLore page, mechanism claim "layer-adaptive subspace
  * cosine schedule", paper Section 3.1, Equation (5)).

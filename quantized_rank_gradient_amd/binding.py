@@ -63,6 +63,8 @@ EXPORTS = {
     "qgalore_plan_step": (c_int32, [c_void_p, c_int64, c_uint64, c_void_p, c_size_t, c_void_p]),
     "qgalore_plan_destroy": (c_int32, [c_void_p]),
     "qgalore_plan_enable_timing": (c_int32, [c_void_p, c_int32]),
+    "qgalore_plan_cache_proj": (c_int32, [c_void_p, c_int32]),
+    "qgalore_plan_proj_changed": (c_int32, [c_void_p, c_int32]),
     "qgalore_plan_kernel_times": (c_int32, [c_void_p, ctypes.POINTER(c_float),
                                            ctypes.POINTER(c_int32)]),
     "qgalore_cossim_workspace_bytes": (c_size_t, [c_int64, c_int64]),
@@ -267,6 +269,15 @@ class Plan:
         _check(lib().qgalore_plan_step(self._h, int(t), int(seed) & (2 ** 64 - 1),
                                        _ptr(workspace, torch.uint8, None, "workspace"),
                                        workspace.numel(), _stream(stream)), "qgalore_plan_step")
+
+    def cache_proj(self, enable: bool = True) -> None:
+        """Keep dequantized projections between steps (qgalore_plan_cache_proj); the caller
+        then reports every projection it rewrites with proj_changed()."""
+        _check(lib().qgalore_plan_cache_proj(self._h, 1 if enable else 0),
+               "qgalore_plan_cache_proj")
+
+    def proj_changed(self, layer: int) -> None:
+        _check(lib().qgalore_plan_proj_changed(self._h, int(layer)), "qgalore_plan_proj_changed")
 
     def enable_timing(self, max_steps: int) -> None:
         _check(lib().qgalore_plan_enable_timing(self._h, int(max_steps)),

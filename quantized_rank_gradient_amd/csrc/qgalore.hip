@@ -265,6 +265,11 @@ struct qg_plan {
   std::vector<hipEvent_t> events;   // 5 per recorded step when timing is enabled
   int timing_cap = 0;
   int timing_used = 0;
+  // kept dequantized projections (qgalore_plan_cache_proj): layers whose P changed since
+  // the last step, and the workspace that holds the others' bf16 copies
+  bool cache_proj = false;
+  std::vector<uint8_t> proj_dirty;
+  const void* deq_ws = nullptr;
 };
 
 namespace {
@@ -332,6 +337,7 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   }
   p->ws_bytes = ws;
   for (int k = 0; k < 4; ++k) p->grid[k] = (int)base[k];
+  p->proj_dirty.assign((size_t)count, 1);
 
   hipError_t e = hipGetDevice(&p->device);
   if (e == hipSuccess) e = hipMalloc(&p->d_table, sizeof(LayerDev) * count);
@@ -376,9 +382,32 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   if (ev) e = hipEventRecord(ev[0], s);
   if (e != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[3];
-  // bf16 projections are staged directly: their layers have no dequant workgroups
-  if (p->grid[3] > 0 && (e = qg::launch_dequant(a, p->grid[3], s)) != hipSuccess)
-    return hip_fail(e, "dequant kernel launch");
+  // bf16 projections are staged directly: their layers have no dequant workgroups. With
+  // kept projections, only the layers marked changed are dequantized, one launch each while
+  // they are few.
+  if (p->grid[3] > 0) {
+    const bool all = !p->cache_proj || p->deq_ws != workspace;
+    std::vector<int32_t> dirty;
+    if (!all)
+      for (size_t l = 0; l < p->layers.size(); ++l)
+        if (p->proj_dirty[l] && grid_dequant(p->layers[l]) > 0) dirty.push_back((int32_t)l);
+    if (all || dirty.size() > 32) {
+      e = qg::launch_dequant(a, p->grid[3], s);
+    } else {
+      for (const int32_t l : dirty) {
+        StepArgs one = a;
+        one.table = nullptr;
+        one.wg_layer = nullptr;
+        one.one = p->layers[(size_t)l];
+        if ((e = qg::launch_dequant(one, grid_dequant(one.one), s)) != hipSuccess) break;
+      }
+    }
+    if (e != hipSuccess) return hip_fail(e, "dequant kernel launch");
+  }
+  if (p->cache_proj) {
+    std::fill(p->proj_dirty.begin(), p->proj_dirty.end(), 0);
+    p->deq_ws = workspace;
+  }
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
   e = qg::launch_project(a, p->grid[0], s);
@@ -393,6 +422,22 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   e = qg::launch_backproject(a, p->grid[2], p->big, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "timing event");
+  return QG_OK;
+}
+
+extern "C" qg_status qgalore_plan_cache_proj(qg_plan* p, int32_t enable) {
+  if (!p) return QG_ERR_NULL;
+  if (enable != 0 && enable != 1) return QG_ERR_ARG;
+  p->cache_proj = enable == 1;
+  p->deq_ws = nullptr;   // the next step dequantizes every layer
+  std::fill(p->proj_dirty.begin(), p->proj_dirty.end(), 1);
+  return QG_OK;
+}
+
+extern "C" qg_status qgalore_plan_proj_changed(qg_plan* p, int32_t layer) {
+  if (!p) return QG_ERR_NULL;
+  if (layer < 0 || (size_t)layer >= p->proj_dirty.size()) return QG_ERR_ARG;
+  p->proj_dirty[(size_t)layer] = 1;
   return QG_OK;
 }
 

@@ -56,6 +56,8 @@ class ScheduleRun:
         self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
                                                 eps=cfg.eps, alpha=cfg.alpha),
                            R_out=self.R_out, U_out=self.U_out)
+        # dequantized projections are kept between steps; a refresh marks its layer changed
+        self.plan.cache_proj(True)
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(self.r, 32))
         self.rws = None
@@ -123,6 +125,7 @@ class ScheduleRun:
                 self.refreshed_at[k] = t
                 self.layers[k].Pq.copy_(new[k][0])
                 self.layers[k].Ps.copy_(new[k][1])
+                self.plan.proj_changed(k)
         if before_step is not None:
             before_step(t)
         self._timed("step", lambda: self.plan.step(t + 1, WL.SR_SEED, self.ws))

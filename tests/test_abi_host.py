@@ -167,3 +167,9 @@ def test_mfma_probe_rejects_bad_arguments_before_hip():
     assert L.qgalore_mfma_probe(p, 64, o, 0, 1, None) == 5               # grid < 1
     assert L.qgalore_mfma_probe(p, 64, o, 1, 0, None) == 5               # iters < 1
     assert L.qgalore_mfma_probe(p, 64, o, 70000, 1, None) == 5
+
+
+def test_plan_projection_cache_entry_points_reject_null():
+    L = B.lib()
+    assert L.qgalore_plan_cache_proj(None, 1) == 1            # QG_ERR_NULL
+    assert L.qgalore_plan_proj_changed(None, 0) == 1

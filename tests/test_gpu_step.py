@@ -174,6 +174,43 @@ def test_plan_matches_oracle_over_mixed_layers():
     plan.close()
 
 
+def test_plan_kept_projections_match_fresh_dequant():
+    """With dequantized projections kept between steps, three steps in which one layer's P is
+    replaced (and reported) before the third give the same state, bit for bit, as a plan that
+    dequantizes every projection at every step."""
+    B = _B()
+    shapes = [(512, 512), (1376, 512), (512, 1376)]
+    r = 64
+    cfg = WL.Config("mixed", 8, tuple(WL.LayerShape(k, "l", m, n) for k, (m, n) in enumerate(shapes)),
+                    r=r, sigma=1e-3)
+    runs = []
+    for keep in (False, True):
+        devs = []
+        for L in cfg.layers:
+            st, P = PAR.host_state(cfg, L, r, "random")
+            devs.append(PAR.to_device(st, WL.gradient_bf16(cfg, L, 1), P))
+        plan = B.Plan(devs, hp=dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, alpha=0.25))
+        if keep:
+            plan.cache_proj(True)
+        ws = B.alloc_workspace(plan.workspace_bytes)
+        for t in (1, 2, 3):
+            if t == 3:   # a refresh replaces layer 1's projection
+                rng = np.random.default_rng(77)
+                Pn = np.linalg.qr(rng.standard_normal((shapes[1][0], r)))[0].astype(np.float32)
+                q, sc = B.quantize_proj(torch.from_numpy(Pn).cuda())
+                devs[1].Pq.copy_(q)
+                devs[1].Ps.copy_(sc)
+                if keep:
+                    plan.proj_changed(1)
+            plan.step(t, WL.SR_SEED, ws)
+        torch.cuda.synchronize()
+        runs.append([snapshot(Lt) for Lt in devs])
+        plan.close()
+    for a, b in zip(*runs):
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+
+
 # ------------------------------------------------------------------------- CosSim ---
 
 def test_cossim_batch_of_mixed_row_counts():
