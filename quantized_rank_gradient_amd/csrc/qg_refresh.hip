@@ -427,12 +427,22 @@ __global__ __launch_bounds__(kRfJacobiThreads) void qg_rf_jacobi(
   __shared__ int rotated;
   __shared__ int rank_of[kRfMaxK];
   __shared__ float abs_tol_sh;
+  // the 2 x 2 blocks (w1, w2), w1 <= w2, of a round as one list (w1 in the high byte)
+  constexpr int kMaxBlocks = (kRfMaxK / 2) * (kRfMaxK / 2 + 1) / 2;
+  __shared__ uint16_t blk[kMaxBlocks];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = wave; i < k; i += NW)
     for (int j = lane; j < k; j += 64) {
       A[i * PT + j] = gload(Cm + i * k + j);
       V[i * PT + j] = i == j ? 1.0f : 0.0f;
     }
+  const int half = k / 2;
+  const int nblocks = half * (half + 1) / 2;
+  if ((int)threadIdx.x < half) {
+    const int w1 = threadIdx.x;
+    const int first = w1 * half - w1 * (w1 - 1) / 2;   // blocks of rows before w1
+    for (int w2 = w1; w2 < half; ++w2) blk[first + w2 - w1] = (uint16_t)((w1 << 8) | w2);
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     float tr = 0.0f;
@@ -441,7 +451,6 @@ __global__ __launch_bounds__(kRfJacobiThreads) void qg_rf_jacobi(
   }
   __syncthreads();
   const float abs_tol = abs_tol_sh;
-  const int half = k / 2;
   int sweeps = 0;
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     if (threadIdx.x == 0) rotated = 0;
@@ -476,34 +485,77 @@ __global__ __launch_bounds__(kRfJacobiThreads) void qg_rf_jacobi(
       // blocks (w1, w2), w1 <= w2: rows p1, q1 rotated by pair w1, columns p2, q2 by w2.
       // Only the upper triangle of C is stored (entry (i, j) at (min, max)); every stored
       // entry belongs to exactly one block with w1 <= w2. Blocks of two unrotated pairs and
-      // V columns of an unrotated pair do not change.
-      for (int w1 = wave; w1 < half; w1 += NW) {
-        const int r1 = rot[w1];
-        const int p1 = pp[w1], q1 = pq[w1];
-        const float c1 = cs_c[w1], s1 = cs_s[w1];
-        for (int w2 = w1 + lane; w2 < half; w2 += 64) {
-          if (!(r1 | rot[w2])) continue;
-          const int p2 = pp[w2], q2 = pq[w2];
-          const float c2 = cs_c[w2], s2 = cs_s[w2];
-          const int o0 = min(p1, p2) * PT + max(p1, p2), o1 = min(p1, q2) * PT + max(p1, q2);
-          const int o2 = min(q1, p2) * PT + max(q1, p2), o3 = min(q1, q2) * PT + max(q1, q2);
-          const float a = A[o0], b = A[o1], c = A[o2], d = A[o3];
-          const float ra = c1 * a - s1 * c, rb = c1 * b - s1 * d;   // J1^T rows
-          const float rc = s1 * a + c1 * c, rd = s1 * b + c1 * d;
-          A[o0] = c2 * ra - s2 * rb;   // * J2 columns
-          A[o1] = s2 * ra + c2 * rb;
-          if (w2 != w1) A[o2] = c2 * rc - s2 * rd;   // on the diagonal block o2 == o1
-          A[o3] = s2 * rc + c2 * rd;
+      // V columns of an unrotated pair do not change. Each thread takes every 1024th block
+      // of the list and every 1024th (pair, row) update of V, and reads all of its entries
+      // before it writes any, so the LDS latencies overlap.
+      constexpr int BPT = (kMaxBlocks + kRfJacobiThreads - 1) / kRfJacobiThreads;
+      constexpr int VPT = (kRfMaxK / 2 * kRfMaxK + kRfJacobiThreads - 1) / kRfJacobiThreads;
+      {
+        int o[BPT][4], wb[BPT];   // entry offsets; block code (w1 << 8 | w2), -1 when idle
+        float x[BPT][4];
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+          const int b = threadIdx.x + u * kRfJacobiThreads;
+          wb[u] = -1;
+          if (b < nblocks) {
+            const int w1 = blk[b] >> 8, w2 = blk[b] & 0xFF;
+            if (rot[w1] | rot[w2]) {
+              wb[u] = blk[b];
+              const int p1 = pp[w1], q1 = pq[w1], p2 = pp[w2], q2 = pq[w2];
+              o[u][0] = min(p1, p2) * PT + max(p1, p2);
+              o[u][1] = min(p1, q2) * PT + max(p1, q2);
+              o[u][2] = min(q1, p2) * PT + max(q1, p2);
+              o[u][3] = min(q1, q2) * PT + max(q1, q2);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
+            }
+          }
         }
-      }
-      for (int w = wave; w < half; w += NW) {
-        if (!rot[w]) continue;
-        const int p = pp[w], qq = pq[w];
-        const float c = cs_c[w], s = cs_s[w];
-        for (int i = lane; i < k; i += 64) {
-          const float vx = V[i * PT + p], vy = V[i * PT + qq];
-          V[i * PT + p] = c * vx - s * vy;
-          V[i * PT + qq] = s * vx + c * vy;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+          if (wb[u] < 0) continue;
+          const int w1 = wb[u] >> 8, w2 = wb[u] & 0xFF;
+          const float c1 = cs_c[w1], s1 = cs_s[w1], c2 = cs_c[w2], s2 = cs_s[w2];
+          const float a = x[u][0], bb = x[u][1], c = x[u][2], d = x[u][3];
+          const float ra = c1 * a - s1 * c, rb = c1 * bb - s1 * d;   // J1^T rows
+          const float rc = s1 * a + c1 * c, rd = s1 * bb + c1 * d;
+          A[o[u][0]] = c2 * ra - s2 * rb;   // * J2 columns
+          A[o[u][1]] = s2 * ra + c2 * rb;
+          if (w1 != w2) A[o[u][2]] = c2 * rc - s2 * rd;   // on the diagonal o2 == o1
+          A[o[u][3]] = s2 * rc + c2 * rd;
+        }
+        // V: the (pair, row) updates idx = threadIdx.x + 1024 u, in two batches of reads
+        // then writes; (pair, row) = (idx / k, idx % k) advanced incrementally
+        int w = threadIdx.x / k, i = threadIdx.x - w * k;
+        const int dq = kRfJacobiThreads / k, dr = kRfJacobiThreads - dq * k;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          constexpr int NB = (VPT + 1) / 2;
+          int vo[NB];   // row offset << 8 | pair, -1 when idle
+          float vx[NB], vy[NB];
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            vo[u] = -1;
+            if (w < half && rot[w]) {
+              vo[u] = ((i * PT) << 8) | w;
+              vx[u] = V[i * PT + pp[w]];
+              vy[u] = V[i * PT + pq[w]];
+            }
+            w += dq;
+            i += dr;
+            if (i >= k) {
+              i -= k;
+              ++w;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            if (vo[u] < 0) continue;
+            const int wu = vo[u] & 0xFF, row = vo[u] >> 8;
+            const float c = cs_c[wu], sn = cs_s[wu];
+            V[row + pp[wu]] = c * vx[u] - sn * vy[u];
+            V[row + pq[wu]] = sn * vx[u] + c * vy[u];
+          }
         }
       }
       __syncthreads();
