@@ -625,20 +625,26 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
     sa.issue(k_begin + T::BK, base + 2 * T::STAGE);
     sb.issue(k_begin + T::BK, base + 2 * (T::STAGE + T::A_ELEMS));
   }
-  int buf = 0;   // kt % NST
-  for (int kt = 0; kt < nk; ++kt) {
-    if (NST == 3 && kt + 1 < nk)
-      wait_vm_lds<NI>();
-    else
-      wait_vm_lds<0>();
-    barrier_nofence();
-    if (kt + NST - 1 < nk) {
-      const uint32_t nxt = base + 2 * (buf == 0 ? NST - 1 : buf - 1) * T::STAGE;
-      sa.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt);
-      sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + 2 * T::A_ELEMS);
-    }
-    mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
-    buf = buf == NST - 1 ? 0 : buf + 1;
+  // The loop is unrolled over the ring, so that each copy reads a buffer known at compile
+  // time: the fragment addresses are then loop-invariant registers plus immediate offsets.
+  for (int k0 = 0; k0 < nk; k0 += NST) {
+    static_for<NST>([&](auto dc) {
+      constexpr int buf = decltype(dc)::value;   // kt % NST
+      const int kt = k0 + buf;
+      if (kt < nk) {
+        if (NST == 3 && kt + 1 < nk)
+          wait_vm_lds<NI>();
+        else
+          wait_vm_lds<0>();
+        barrier_nofence();
+        if (kt + NST - 1 < nk) {
+          const uint32_t nxt = base + 2 * ((buf + NST - 1) % NST) * T::STAGE;
+          sa.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt);
+          sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + 2 * T::A_ELEMS);
+        }
+        mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+      }
+    });
   }
   // the caller may reuse the LDS area: every wave is done with the last stage
   __syncthreads();
