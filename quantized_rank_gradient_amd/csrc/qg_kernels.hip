@@ -302,9 +302,9 @@ __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& 
   if (L.fuse_adam) {
     // One K split and rows made of whole 256-element groups: each tile row is one Adam group,
     // complete in this workgroup, so Adam runs here instead of a separate pass over R.
-    // Chunk x holds rows 32x .. 32x+31 of both wave rows (tile rows wm*WTM + 32x + rr).
-    // Chunk x holds rows 32x .. 32x+31 of both wave rows (64 rows). Wave w takes rows
-    // 16w .. 16w+15 in four passes of four rows, 16 lanes per row (adam_group16).
+    // Chunk x holds rows 32x .. 32x+31 of both wave rows (64 rows: tile rows wm*WTM + 32x +
+    // rr). Wave w takes chunk rows 16w .. 16w+15 in four passes of four rows, 16 lanes per
+    // row (adam_group16).
     float* E = reinterpret_cast<float*>(lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave_m<T>(), wn = wave_n<T>();
