@@ -73,6 +73,10 @@ CASES = [
     (24, 13, 16, "random", 3),         # tiny, odd n, a single short group
     (128, 96, 128, "random", 2),       # full rank r = m
     (4096, 256, 1024, "random", 4),    # rank 1024: eight projection row tiles
+    # back-projection K loops (K = r, 32 per stage) ending at each position of the LDS ring:
+    (256, 512, 96, "random", 3),       # small tile, two buffers, 3 stages
+    (384, 768, 192, "zero", 1),        # large tile, three buffers, 6 stages
+    (640, 512, 224, "random", 2),      # large tile, 7 stages
 ]
 
 
