@@ -141,6 +141,8 @@ class Variant:
         torch = self.torch
         out = {}
         for label, ks in (("1 layer", [0]), ("9 layers", list(range(9)))):
+            if ks[-1] >= len(self.layers):   # a set of fewer layers has no nine-layer batch
+                continue
             pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m,
                       self.fmt) for k in ks]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -155,6 +157,25 @@ class Variant:
 
 
 KERNELS = ("qg_dequant", "qg_project", "qg_adam", "qg_backproject")
+
+
+def describe_layers(cfg) -> str:
+    """The layer set in words: LLaMA-shaped sets by their per-block shapes (q, k, v, o d x d;
+    gate, up f x d; down d x f), anything else by its shape counts."""
+    shapes = [(L.m, L.n) for L in cfg.layers]
+    if len(shapes) == 1:
+        return f"one {shapes[0][0]}x{shapes[0][1]} layer"
+    if len(shapes) % 7 == 0:
+        d, f = shapes[0][0], shapes[4][0]
+        block = [(d, d)] * 4 + [(f, d)] * 2 + [(d, f)]
+        if shapes == block * (len(shapes) // 7):
+            name = {4096: "LLaMA-7B", 2048: "LLaMA-1B", 512: "LLaMA-60M"}.get(d, "LLaMA")
+            return (f"{name}-shaped layer set, {len(shapes)} layers ({len(shapes) // 7} x "
+                    f"q,k,v,o {d}x{d}; gate,up {f}x{d}; down {d}x{f})")
+    counts = {}
+    for sh in shapes:
+        counts[sh] = counts.get(sh, 0) + 1
+    return f"{len(shapes)} layers (" + "; ".join(f"{c} x {m}x{n}" for (m, n), c in counts.items()) + ")"
 
 
 def fused_adam(cfg):
@@ -596,9 +617,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.key}: LLaMA-7B-shaped layer set, 224 layers "
-                        f"(32 x q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), "
-                        f"rank {cfg.r}, one full optimizer step + due refresh tests",
+            "workload": f"{cfg.key}: {describe_layers(cfg)}, rank {cfg.r}, "
+                        f"one full optimizer step + due refresh tests",
             "layers": len(cfg.layers), "rank": cfg.r, "weight_elems": algorithmic(cfg, cfg.r)["mn"],
             "projection_format": args.p_format,
             "parallelism": "single GPU",
