@@ -43,13 +43,14 @@ qg_status device_present() {
 }
 
 // Kernels address every tensor of a layer through 32-bit buffer offsets: the fp32 ones
-// (R: r x n, U: m x n) must stay below 2 GiB, hence m*n and r*n below 2^29 elements.
+// (R: r x n, U: m x n) must stay below 2 GiB, hence m*n and r*n below 2^29 elements; the
+// projection (m x r, up to 4 bytes per element where a kernel stages it) likewise.
 constexpr int64_t kMaxElems = int64_t(1) << 29;
 
 qg_status check_shape(int64_t m, int64_t n, int64_t r) {
   if (m < 1 || n < 1 || r < 1 || m > kMaxDim || n > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
   if (r > m || r % 8 != 0) return QG_ERR_SHAPE;
-  if (m * n > kMaxElems || r * n > kMaxElems) return QG_ERR_SHAPE;
+  if (m * n > kMaxElems || r * n > kMaxElems || m * r > kMaxElems) return QG_ERR_SHAPE;
   return QG_OK;
 }
 
@@ -658,7 +659,7 @@ extern "C" qg_status qgalore_cossim(const qg_proj* P_new, const qg_proj* P_old, 
 extern "C" qg_status qgalore_quantize_proj(const float* P, int64_t m, int64_t r, uint8_t* P_q,
                                            float* P_scale, void* stream) {
   if (!P || !P_q || !P_scale) return QG_ERR_NULL;
-  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
+  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim || m * r > kMaxElems) return QG_ERR_SHAPE;
   if (!aligned(P, 16) || !aligned(P_q, 4) || !aligned(P_scale, 4)) return QG_ERR_ALIGN;
   qg_status st = device_present();
   if (st != QG_OK) return st;
@@ -670,7 +671,7 @@ extern "C" qg_status qgalore_quantize_proj(const float* P, int64_t m, int64_t r,
 extern "C" qg_status qgalore_quantize_proj_int8(const float* P, int64_t m, int64_t r,
                                                 int8_t* P_q, float* P_scale, void* stream) {
   if (!P || !P_q || !P_scale) return QG_ERR_NULL;
-  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim) return QG_ERR_SHAPE;
+  if (m < 1 || r < 1 || m > kMaxDim || r > kMaxDim || m * r > kMaxElems) return QG_ERR_SHAPE;
   if (!aligned(P, 16) || !aligned(P_q, 4) || !aligned(P_scale, 4)) return QG_ERR_ALIGN;
   qg_status st = device_present();
   if (st != QG_OK) return st;

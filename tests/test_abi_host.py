@@ -90,6 +90,13 @@ def test_step_validation_codes_without_touching_the_device():
     assert _call(_desc(eps=float("nan"))) == 5
     assert _call(_desc(workspace_bytes=16)) == 4
     assert _call(_desc(workspace=None)) == 1
+    # m*r past 2^29 (r > n is allowed, so m*n and r*n alone do not bound the projection)
+    assert _call(_desc(m=65536, n=8, r=32768)) == 2
+    assert _call(_desc(m=65536, n=8, r=8192), G=None) == 1
+    assert B.lib().qgalore_workspace_bytes(65536, 8, 32768) == 0
+    assert B.lib().qgalore_quantize_proj(0x10000, 65536, 16384, 0x10000, 0x10000, None) == 2
+    assert B.lib().qgalore_quantize_proj_int8(0x10000, 65536, 16384, 0x10000, 0x10000,
+                                              None) == 2
 
 
 def test_workspace_size_query():

@@ -273,3 +273,54 @@ def test_cossim_matches_oracle(m, r):
         assert abs(got - want) <= 1e-4, (theta, got, want)
         if abs(want - 0.4) > 1e-4:
             assert (got > 0.4) == (want > 0.4)
+
+
+@pytest.mark.parametrize("m,n", [(256, 256), (256, 200)])
+def test_non_finite_rounding_inputs_keep_the_old_code(m, n):
+    """Group scales chosen so that the rounding input d = W + U/s + u is not finite, or so
+    large that it clamps. n = 256 takes the 16-wide vector path (whose fast branch tests the
+    sum of a 16-element run), n = 200 the element-wise path.
+      group 0: s = 1e-45 (subnormal): 1/s = inf, so d = +-inf (or NaN where U = 0) and every
+               code is kept;
+      group 1: s = 3e-39 (subnormal): 1/s = 3.3e38 is finite, U/s overflows for |U| > ~1 and
+               stays finite below: kept and clamped codes side by side;
+      group 2: s = 1.5e-38: every d is finite (|d| < 0.6 * FLT_MAX) but a run's fp32 sum can
+               overflow, which sends the vector path to its element-by-element branch;
+      other groups: s = 1, ordinary rounding.
+    Both sides must keep the old code exactly where d is not finite."""
+    cfg = custom_cfg(m, n, 32, sigma=1e-2)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, 32, "zero")
+    st.Ws[:] = 1.0
+    st.Ws[0] = 1e-45
+    st.Ws[1] = 3e-39
+    st.Ws[2] = 1.5e-38
+    hp = O.Hyper(lr=10.0)                  # |N| ~ 10, so |U| is of order 1
+    G = WL.gradient_bf16(cfg, L, 1)
+    Lt = PAR.to_device(st, G, P)
+    before = st.copy()
+    with np.errstate(over="ignore", invalid="ignore"):
+        res = O.qgalore_step(st, G, 1, WL.SR_SEED, hp)
+    out = gpu_step(Lt, 1, hp=dict(lr=10.0))
+    with np.errstate(over="ignore", invalid="ignore"):
+        PAR.check_step(before, res, st, out, hp=hp)
+
+    d = res.d.ravel()
+    w0 = before.Wq.ravel()
+    g0, g1, g2 = slice(0, 256), slice(256, 512), slice(512, 768)
+    assert not np.isfinite(d[g0]).any()
+    assert np.array_equal(out["Wq"].ravel()[g0], w0[g0])
+    fin1 = np.isfinite(d[g1])
+    assert fin1.any() and (~fin1).any(), "group 1 should mix finite and infinite d"
+    assert np.array_equal(out["Wq"].ravel()[g1][~fin1], w0[g1][~fin1])
+    big = fin1 & (np.abs(np.nan_to_num(d[g1])) > 128)
+    assert big.any() and np.all(np.abs(out["Wq"].ravel()[g1][big]) == 127)
+    assert np.isfinite(d[g2]).all()
+    if n % 16 == 0:
+        # the vector path's test: the run's values added one after another in fp32
+        sums = np.zeros(16, np.float32)
+        runs = d[g2].reshape(16, 16).astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for t in range(16):
+                sums = (sums + runs[:, t]).astype(np.float32)
+        assert (~np.isfinite(sums)).any(), "no 16-element run of group 2 overflows its sum"

@@ -1,0 +1,83 @@
+"""CPU checks of the comparison rules the GPU parity tests apply (tests/parity.py): the rule
+for N~ elements that round to the other bf16 neighbour must accept a flip that the R
+difference explains and reject every other kind of difference."""
+import numpy as np
+import pytest
+
+from oracle import qgalore_oracle as O
+from tests import parity as PAR
+
+F32 = np.float32
+
+
+def _case(r=32, n=64, m=48, seed=0):
+    rng = np.random.default_rng(seed)
+    N_o = (rng.standard_normal((r, n)) * 1e-3).astype(F32)
+    P = O.bf16_round(rng.standard_normal((m, r)).astype(F32) * 0.1)
+    return N_o, P
+
+
+def _midpoint_pair(x):
+    """A value just below the bf16 midpoint above x and one just above it (fp32)."""
+    lo = O.bf16_round(np.array([x], F32))[0]
+    hi = np.nextafter(lo, F32(np.inf) if lo >= 0 else F32(-np.inf), dtype=F32)
+    for _ in range(1 << 16):            # the next bf16 value away from zero
+        if O.bf16_round(np.array([hi], F32))[0] != lo:
+            break
+        hi = np.nextafter(hi, F32(np.inf) if lo >= 0 else F32(-np.inf), dtype=F32)
+    hi_b = O.bf16_round(np.array([hi], F32))[0]
+    mid = (np.float64(lo) + np.float64(hi_b)) / 2
+    below = F32(mid - abs(mid) * 2e-7)
+    above = F32(mid + abs(mid) * 2e-7)
+    return below, above
+
+
+def test_no_flip_carries_nothing():
+    N_o, P = _case()
+    assert np.all(PAR.explained_n_flips(N_o, O.bf16_round(N_o), N_o, O.bf16_round(N_o), P,
+                                        0.25) == 0)
+
+
+def test_an_explained_flip_is_accepted_and_carried_in_its_column_only():
+    N_o, P = _case()
+    N_g = N_o.copy()
+    below, above = _midpoint_pair(N_o[3, 7])
+    N_o[3, 7], N_g[3, 7] = below, above
+    Nb_o, Nb_g = O.bf16_round(N_o), O.bf16_round(N_g)
+    assert Nb_o[3, 7] != Nb_g[3, 7]
+    carried = PAR.explained_n_flips(N_g, Nb_g, N_o, Nb_o, P, 0.25)
+    assert carried.shape == (P.shape[0], N_o.shape[1])
+    assert np.all(carried[:, 7] > 0)
+    assert not np.any(np.delete(carried, 7, axis=1))
+    d = abs(float(Nb_g[3, 7]) - float(Nb_o[3, 7]))
+    assert np.allclose(carried[:, 7], 0.25 * np.abs(P[:, 3]) * d)
+
+
+def test_a_flip_that_skips_a_bf16_value_is_rejected():
+    N_o, P = _case()
+    Nb_o = O.bf16_round(N_o)
+    Nb_g = Nb_o.copy()
+    bits = Nb_g.view(np.uint32)
+    bits[2, 2] += 2 << 16                   # two bf16 units away
+    with pytest.raises(AssertionError, match="skips"):
+        PAR.explained_n_flips(Nb_g, Nb_g, N_o, Nb_o, P, 0.25)
+
+
+def test_a_flip_far_from_the_midpoint_is_rejected():
+    N_o, P = _case()
+    Nb_o = O.bf16_round(N_o)
+    Nb_g = Nb_o.copy()
+    bits = Nb_g.view(np.uint32)
+    bits[5, 9] += 1 << 16                   # the neighbour, but N itself did not move
+    with pytest.raises(AssertionError, match="midpoint"):
+        PAR.explained_n_flips(N_o, Nb_g, N_o, Nb_o, P, 0.25)
+
+
+def test_too_many_flips_are_rejected():
+    N_o, P = _case(r=64, n=256)             # 16384 elements: the cap allows one flip
+    N_g = N_o.copy()
+    for (i, j) in ((1, 1), (2, 2)):
+        below, above = _midpoint_pair(N_o[i, j])
+        N_o[i, j], N_g[i, j] = below, above
+    with pytest.raises(AssertionError, match="other bf16 neighbour"):
+        PAR.explained_n_flips(N_g, O.bf16_round(N_g), N_o, O.bf16_round(N_o), P, 0.25)
