@@ -15,6 +15,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -34,13 +35,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+_HOST_QR = {}
+
+
 def projection(cfg, L, r, tag, torch, WL, dev, fast):
+    """An orthonormal m x r projection for layer L: the Q of a seeded Gaussian, by QR on the
+    device, or with `fast` (profiling runs) by numpy QR on the host, computed once per shape and
+    tag and shared by the layers of that shape, so that no device QR (rocsolver) runs inside a
+    profiled process."""
     if not fast:
         return WL.orthonormal_device(cfg, L, r, tag=tag, device=dev)
-    # profiling runs: Gaussian columns scaled to unit expected norm (no QR on the device)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(WL.torch_seed(cfg, L.layer_id, 0, tag))
-    return torch.randn((L.m, r), generator=gen, device=dev) / (L.m ** 0.5)
+    key = (L.m, r, tag)
+    if key not in _HOST_QR:
+        _HOST_QR[key] = torch.from_numpy(WL.orthonormal_f32(cfg, L, r, tag=tag))
+    return _HOST_QR[key].to(dev)
 
 
 def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4"):
@@ -71,19 +79,32 @@ def build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False, f
 
 
 class Variant:
-    """One rank variant of the layer set: a plan, refresh schedules and scratch."""
+    """One rank variant of the layer set: plans, refresh schedules and scratch.
 
-    def __init__(self, cfg, r, G_list, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4"):
+    G_sets holds one or more gradient sets (each a list with one bf16 G per layer, all
+    resident in HBM); step t uses set t mod len(G_sets), through a plan of its own (plans
+    differ only in their G pointers and share the workspace), so that the moments see a fresh
+    gradient each step instead of settling on a repeated one."""
+
+    def __init__(self, cfg, r, G_sets, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4",
+                 dequant="auto", keep_proj=False):
         self.cfg, self.r, self.fmt = cfg, r, fmt
         self.torch, self.B = torch, B
         t0 = time.time()
-        self.layers, self.pnew = build_layer_set(cfg, r, G_list, W_list, Ws_list, torch, B, WL,
-                                                 fast, fmt)
-        self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
-                                                 eps=cfg.eps, alpha=cfg.alpha))
-        # dequantized projections are kept between steps; a refresh replaces a layer's P, so
-        # every tested layer is marked changed and dequantized again at the next step
-        self.plan.cache_proj(True)
+        self.layers, self.pnew = build_layer_set(cfg, r, G_sets[0], W_list, Ws_list, torch, B,
+                                                 WL, fast, fmt)
+        hp = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, alpha=cfg.alpha)
+        self.plans = []
+        for Gs in G_sets:
+            lt = [dataclasses.replace(L, G=G) for L, G in zip(self.layers, Gs)]
+            self.plans.append(B.Plan(lt, hp=hp, dequant=dequant))
+        self.plan = self.plans[0]
+        # keep_proj (comparison runs only): with the separate dequant pass, keep the bf16
+        # projections between steps and re-dequantize only the layers a refresh test replaced.
+        # The step proper dequantizes every projection every step.
+        self.keep_proj = keep_proj and len(self.plans) == 1
+        if self.keep_proj:
+            self.plan.cache_proj(True)
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(r, 32))
         self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device="cuda")
@@ -103,7 +124,7 @@ class Variant:
         for a refresh gets a new projection, which the next step dequantizes again."""
         self.t += 1
         t = self.t
-        self.plan.step(t, 1234, self.ws)
+        self.plans[t % len(self.plans)].step(t, 1234, self.ws)
         due = [k for k, s in enumerate(self.sched) if s.due(t)]
         if due:
             pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m,
@@ -112,7 +133,8 @@ class Variant:
         vals = self.cs_out[: len(due)].cpu().tolist() if due else []
         for k, v in zip(due, vals):
             self.sched[k].refresh(t, v)
-            self.plan.proj_changed(k)
+            if self.keep_proj:
+                self.plan.proj_changed(k)
         self.tests += len(due)
 
     def time_steps(self, steps, warmup):
@@ -120,7 +142,8 @@ class Variant:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        self.plan.enable_timing(steps)
+        for p in self.plans:
+            p.enable_timing(steps)
         self.tests = 0
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -131,9 +154,18 @@ class Variant:
         end.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
-        kms, nrec = self.plan.kernel_times()
-        self.plan.enable_timing(0)
+        acc, nrec = [0.0] * 4, 0
+        for p in self.plans:
+            kms_p, n_p = p.kernel_times()
+            acc = [a + k * n_p for a, k in zip(acc, kms_p)]
+            nrec += n_p
+            p.enable_timing(0)
+        kms = [a / max(1, nrec) for a in acc]
         return total_ms / steps, kms, self.tests / steps
+
+    def close(self):
+        for p in self.plans:
+            p.close()
 
     def time_cossim(self, reps=5):
         """Latency (ms) of the batched refresh test for one layer of each shape and for a
@@ -185,7 +217,14 @@ def fused_adam(cfg):
     return all(L.n % 256 == 0 for L in cfg.layers)
 
 
-def algorithmic(cfg, r, fmt="int4"):
+def inline_dequant(fmt, r, mode):
+    """Whether the library dequantizes the INT4 projections of rank r inside its MFMA kernels
+    (the rule of qg_dequant_mode: INLINE asked for, INT4, r % 32 == 0 and r % 128 == 0 or
+    256 % r == 0; AUTO is the separate pass)."""
+    return fmt == "int4" and mode == "inline" and r % 32 == 0 and (r % 128 == 0 or 256 % r == 0)
+
+
+def algorithmic(cfg, r, fmt="int4", inline=False):
     """FLOPs and bytes the method must do per step, split by the kernel that does them (in
     launch order: INT4 dequant of P, projection, Adam, back-projection + rounding). Bytes
     count each algorithmic input once and each output once: P (INT4 + fp32 scale per 256)
@@ -200,15 +239,17 @@ def algorithmic(cfg, r, fmt="int4"):
     fused = fused_adam(cfg)
     flops = (0.0, 2.0 * r * mn, 0.0, 2.0 * r * mn)
     p_bytes = {"int4": 0.5 * mr + mr / 64.0, "int8": mr + mr / 64.0, "bf16": 0.0}[fmt]
-    nbytes = (p_bytes,                                # P codes + scales (bf16: no pass)
-              2.0 * mn + (adam if fused else 0.0),    # G (bf16) [+ Adam]
+    # P codes + scales: the dequant pass's input, or read by the projection kernel when the
+    # MFMA kernels dequantize it themselves (bf16: read directly, not counted)
+    nbytes = (0.0 if inline else p_bytes,
+              2.0 * mn + (adam if fused else 0.0) + (p_bytes if inline else 0.0),
               0.0 if fused else adam,
               2.0 * mn + mn / 64.0)                   # W in and out + W scales
     return dict(mn=mn, flops=flops, bytes=nbytes, fused_adam=fused)
 
 
-def roofline(cfg, r, kms, fmt="int4"):
-    a = algorithmic(cfg, r, fmt)
+def roofline(cfg, r, kms, fmt="int4", inline=False):
+    a = algorithmic(cfg, r, fmt, inline)
     names = KERNELS
     k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
@@ -441,35 +482,67 @@ def library_gemm_ms(torch, cfg, r, reps=20):
     return dict(projection_ms=round(total[0], 3), backprojection_ms=round(total[1], 3))
 
 
-def cpu_baseline(nlayers=7):
-    """The oracle, as it stands, on the layers of block 0 (q, k, v, o, gate, up, down) at
-    rank 1024: one full oracle step per layer."""
-    import numpy as np
+def _oracle_worker(layer_ids, barrier, out):
+    """One process of the CPU baseline: builds the inputs of its layers (not timed), waits for
+    every worker, then runs one oracle step per layer with one BLAS thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
     from oracle import qgalore_oracle as O
     from quantized_rank_gradient_amd import workloads as WL
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     cfg = WL.CONFIGS["llama7b_r1024"]
     h = O.Hyper(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.alpha)
-    dt, elems = 0.0, 0
-    for L in cfg.layers[:nlayers]:
+    jobs = []
+    for k in layer_ids:
+        L = cfg.layers[k]
         P = WL.orthonormal_f32(cfg, L, cfg.r)
         Pq, Ps = O.quantize_proj(P)
         Mq, Ms, Vq, Vs = WL.zero_moments(cfg.r, L.n)
         st = O.LayerState(L.m, L.n, cfg.r, L.layer_id, WL.weights_int8(cfg, L),
                           WL.weight_scales(cfg, L), Pq, Ps, Mq, Ms, Vq, Vs)
-        G = WL.gradient_bf16(cfg, L, 1)
-        t0 = time.time()
+        jobs.append((st, WL.gradient_bf16(cfg, L, 1), L.m * L.n))
+    barrier.wait()
+    t0 = time.time()
+    for st, G, _ in jobs:
         O.qgalore_step(st, G, 1, 1234, h)
-        dt += time.time() - t0
-        elems += L.m * L.n
-    return dict(value=round(elems / dt, 1), unit="weight elems/s", cores=int(threads),
-                kind="oracle", seconds=round(dt, 2),
+    t1 = time.time()
+    out.put((sum(e for _, _, e in jobs), t0, t1))
+
+
+def cpu_baseline(nlayers=7):
+    """The oracle, as it stands, on the layers of block 0 of the 7B set at rank 1024 (q, k, v,
+    o, gate, up, down): one full oracle step per layer. The layers are spread over worker
+    processes, one per host core this process may run on (at most one per layer), each with
+    one BLAS thread; every worker builds its inputs first, and the timed span runs from the
+    common start to the last worker's end. Call it before the process touches the GPU: the
+    workers are forked."""
+    import multiprocessing as mp
+    host = len(os.sched_getaffinity(0))
+    workers = max(1, min(host, nlayers))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(workers)
+    out = ctx.Queue()
+    # largest layers first, round robin, so the workers' loads are close
+    order = sorted(range(nlayers), key=lambda k: -k)
+    parts = [order[w::workers] for w in range(workers)]
+    procs = [ctx.Process(target=_oracle_worker, args=(parts[w], barrier, out))
+             for w in range(workers)]
+    for pr in procs:
+        pr.start()
+    res = [out.get() for _ in procs]
+    for pr in procs:
+        pr.join()
+    elems = sum(e for e, _, _ in res)
+    span = max(t1 for _, _, t1 in res) - min(t0 for _, t0, _ in res)
+    busy = sum(t1 - t0 for _, t0, t1 in res)
+    return dict(value=round(elems / span, 1), unit="weight elems/s", cores=workers,
+                kind="oracle", host_cores=host, blas_threads_per_worker=1,
+                seconds=round(span, 2), cpu_seconds=round(busy, 2),
                 sample=f"one full oracle step of each of the {nlayers} rank-1024 layers of "
-                       f"block 0 ({elems} weight elements); input generation not timed")
+                       f"block 0 of the 7B set ({elems} weight elements) over {workers} worker "
+                       f"processes; input generation not timed")
 
 
 def main():
@@ -501,12 +574,36 @@ def main():
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch bf16 matmuls of the same shapes (comparison only)")
     ap.add_argument("--fast-setup", action="store_true",
-                    help="Gaussian stand-in projections instead of QR (profiling runs)")
+                    help="profiling runs: projections from numpy QR on the host, one per shape "
+                         "(no device QR in the profiled process)")
+    ap.add_argument("--dequant", default="auto", choices=("auto", "inline", "pass"),
+                    help="where INT4 projections are dequantized: in the MFMA kernels' stagers "
+                         "(inline), by a separate pass into the workspace (pass), or the "
+                         "library's choice (auto)")
+    ap.add_argument("--keep-proj", action="store_true",
+                    help="comparison: with the separate pass, keep dequantized projections "
+                         "between steps (only refreshed layers are dequantized again)")
+    ap.add_argument("--g-sets", type=int, default=4,
+                    help="gradient sets resident in HBM, used in turn by the timed steps")
+    ap.add_argument("--configs", default="single256,llama60m,llama1b",
+                    help="the other layer sets timed and reported under 'configs' "
+                         "(comma-separated; 'none' to skip)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed steps of each of the other layer sets")
+    ap.add_argument("--no-schedule", action="store_true",
+                    help="skip the adaptive-schedule run (200 steps) reported under 'configs'")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the Q-GaLore step runs on a single MI355X here; "
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)
         sys.exit(2)
+
+    # the oracle's baseline runs first, in forked worker processes, before the GPU is touched
+    cpu = None
+    if not (args.no_cpu_baseline or args.schedule or args.linear or args.refresh_only):
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {json.dumps(cpu)}")
 
     import torch
     from quantized_rank_gradient_amd import binding as B
@@ -558,50 +655,10 @@ def main():
     sustained = mfma_sustained(torch, B) if args.copy_gib > 0 else None
     if sustained:
         log(f"sustained MFMA rate: {json.dumps(sustained)}")
-    t0 = time.time()
-    G_list, W_list, Ws_list = [], [], []
-    for L in cfg.layers:
-        G_list.append(WL.gradient_bf16_device(cfg, L, 1, device=dev))
-        W_list.append(WL.weights_int8_device(cfg, L, device=dev))
-        Ws_list.append(torch.full((B.n_groups(L.m * L.n),), cfg.w_scale, dtype=torch.float32,
-                                  device=dev))
-    torch.cuda.synchronize()
-    log(f"{len(cfg.layers)} gradients and INT8 weights resident in {time.time() - t0:.1f}s")
 
-    variants = [(cfg, cfg.r)]
-    if args.secondary != "none":
-        sec = WL.CONFIGS[args.secondary]
-        assert [(L.m, L.n) for L in sec.layers] == [(L.m, L.n) for L in cfg.layers]
-        variants.append((sec, sec.r))
-
-    results = []
-    for vcfg, r in variants:
-        v = Variant(vcfg, r, G_list, W_list, Ws_list, torch, B, WL, args.fast_setup,
-                    args.p_format)
-        ms, kms, tests = v.time_steps(args.steps, args.warmup)
-        cs_ms = v.time_cossim()
-        a = algorithmic(vcfg, r, args.p_format)
-        kernel_ms = {nm: round(t, 4) for nm, t in zip(KERNELS, kms)}
-        if a["fused_adam"]:
-            kernel_ms["qg_adam"] = "in qg_project"   # no separate launch
-        if args.p_format == "bf16":
-            kernel_ms["qg_dequant"] = "none (bf16 projection)"
-        res = dict(config=vcfg.key, rank=r, ms_per_step=round(ms, 4),
-                   value=a["mn"] / (ms / 1e3),
-                   tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
-                   kernel_ms=kernel_ms,
-                   optimizer_ms=round(sum(kms), 4),
-                   refresh_tests_per_step=round(tests, 2),
-                   cossim_ms=cs_ms,
-                   roofline=roofline(vcfg, r, kms, args.p_format))
-        if args.library_gemm:
-            res["library_gemm"] = library_gemm_ms(torch, vcfg, r)
-        log(json.dumps(res))
-        results.append(res)
-        v.plan.close()
-        del v
-        torch.cuda.empty_cache()
-
+    results = run_layer_set(args, torch, B, WL, cfg,
+                            None if args.secondary == "none" else WL.CONFIGS[args.secondary],
+                            args.g_sets, args.steps, args.warmup)
     main_res = results[0]
     line = {
         "metric": "Q-GaLore step: weight elems updated/s + % bf16-MFMA/HBM roofline, 7B layer set",
@@ -621,33 +678,114 @@ def main():
                         f"one full optimizer step + due refresh tests",
             "layers": len(cfg.layers), "rank": cfg.r, "weight_elems": algorithmic(cfg, cfg.r)["mn"],
             "projection_format": args.p_format,
+            "gradient_sets": main_res["gradient_sets"],
             "parallelism": "single GPU",
         },
-        "tflops": main_res["tflops"],
-        "kernel_ms": main_res["kernel_ms"],
-        "optimizer_ms": main_res["optimizer_ms"],
-        "refresh_tests_per_step": main_res["refresh_tests_per_step"],
-        "cossim_ms": main_res["cossim_ms"],
-        "roofline": main_res["roofline"],
+        **{k: main_res[k] for k in ("tflops", "dequant", "workspace_gib", "projection_gib",
+                                    "kernel_ms", "optimizer_ms", "refresh_tests_per_step",
+                                    "cossim_ms", "roofline")},
         "copy_gbs": copy["gbs"] if copy else None,
         "mfma_sustained": sustained,
-        "variants": {r["config"]: {k: r[k] for k in ("rank", "value", "ms_per_step", "tflops",
-                                                    "kernel_ms", "optimizer_ms",
-                                                    "refresh_tests_per_step",
-                                                    "cossim_ms", "roofline")}
-                     for r in results[1:]},
-    }
-    line["variants"] = {
-        r["config"]: {**line["variants"][r["config"]],
-                      **({"library_gemm": r["library_gemm"]} if "library_gemm" in r else {})}
-        for r in results[1:]
     }
     if "library_gemm" in main_res:
         line["library_gemm"] = main_res["library_gemm"]
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one layer ...")
-        line["cpu_baseline"] = cpu_baseline()
+    subs = {}
+    for r in results[1:]:
+        subs[r["config"]] = r
+    torch.cuda.empty_cache()
+    if args.configs != "none":
+        for key in args.configs.split(","):
+            c = WL.CONFIGS[key]
+            steps = c.steps if c.steps > 1 else args.config_steps
+            subs[key] = run_layer_set(args, torch, B, WL, c, None, 2, steps, args.warmup)[0]
+            torch.cuda.empty_cache()
+    if not args.no_schedule:
+        subs["schedule7b"] = schedule_summary(torch, B, WL)
+        torch.cuda.empty_cache()
+    line["configs"] = subs
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+
+
+def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
+    """Times the step on cfg's layer set (and on `secondary`, a rank variant with the same
+    shapes, sharing its gradients and weights). Returns one result per variant."""
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    G_sets = [[WL.gradient_bf16_device(cfg, L, 1 + g, device=dev) for L in cfg.layers]
+              for g in range(g_sets)]
+    W_list, Ws_list = [], []
+    for L in cfg.layers:
+        W_list.append(WL.weights_int8_device(cfg, L, device=dev))
+        Ws_list.append(torch.full((B.n_groups(L.m * L.n),), cfg.w_scale, dtype=torch.float32,
+                                  device=dev))
+    torch.cuda.synchronize()
+    log(f"{cfg.key}: {g_sets} x {len(cfg.layers)} gradients and INT8 weights resident in "
+        f"{time.time() - t0:.1f}s")
+    variants = [(cfg, cfg.r)]
+    if secondary is not None:
+        assert [(L.m, L.n) for L in secondary.layers] == [(L.m, L.n) for L in cfg.layers]
+        variants.append((secondary, secondary.r))
+    results = []
+    for vcfg, r in variants:
+        v = Variant(vcfg, r, G_sets, W_list, Ws_list, torch, B, WL, args.fast_setup,
+                    args.p_format, args.dequant, args.keep_proj)
+        ms, kms, tests = v.time_steps(steps, warmup)
+        cs_ms = v.time_cossim()
+        a = algorithmic(vcfg, r, args.p_format)
+        inl = inline_dequant(args.p_format, r, args.dequant)
+        kernel_ms = {nm: round(t, 4) for nm, t in zip(KERNELS, kms)}
+        if inl:
+            kernel_ms["qg_dequant"] = "in qg_project and qg_backproject"   # no separate launch
+        if a["fused_adam"]:
+            kernel_ms["qg_adam"] = "in qg_project"   # no separate launch
+        if args.p_format == "bf16":
+            kernel_ms["qg_dequant"] = "none (bf16 projection)"
+        p_bytes = sum(int(L.Pq.numel() * L.Pq.element_size()) +
+                      (int(L.Ps.numel() * 4) if L.Ps is not None else 0) for L in v.layers)
+        res = dict(config=vcfg.key,
+                   workload=f"{vcfg.key}: {describe_layers(vcfg)}, rank {r}",
+                   rank=r, steps=steps, ms_per_step=round(ms, 4),
+                   value=a["mn"] / (ms / 1e3),
+                   tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
+                   gradient_sets=g_sets,
+                   dequant=args.dequant + ("+keep" if v.keep_proj else ""),
+                   workspace_gib=round(v.plan.workspace_bytes / 2**30, 3),
+                   projection_gib=round(p_bytes / 2**30, 3),
+                   kernel_ms=kernel_ms,
+                   optimizer_ms=round(sum(kms), 4),
+                   refresh_tests_per_step=round(tests, 2),
+                   cossim_ms=cs_ms,
+                   roofline=roofline(vcfg, r, kms, args.p_format, inl))
+        if args.library_gemm:
+            res["library_gemm"] = library_gemm_ms(torch, vcfg, r)
+        log(json.dumps(res))
+        results.append(res)
+        v.close()
+        del v
+        torch.cuda.empty_cache()
+    del G_sets, W_list, Ws_list
+    return results
+
+
+def schedule_summary(torch, B, WL):
+    """The adaptive refresh schedule on the drifting 7B workload (224 layers, rank 128, 200
+    steps): refreshes by the library, similarity tests, the grouped step every step."""
+    from quantized_rank_gradient_amd.schedule_run import ScheduleRun
+    scfg = WL.CONFIGS["schedule7b"]
+    t0 = time.time()
+    run = ScheduleRun(scfg)
+    setup = time.time() - t0
+    t0 = time.time()
+    summ = run.run()
+    run.close()
+    counts = summ.pop("per_layer_counts")
+    return dict(workload="schedule7b: LLaMA-7B-shaped layer set, 224 layers, rank 128, 200 steps, "
+                         "drifting low-rank gradients (0 .. 0.05 rad/step), interval 25 doubling "
+                         "when CosSim > 0.4",
+                **summ, layers_by_refresh_count={str(c): counts.count(c) for c in sorted(set(counts))},
+                setup_s=round(setup, 1), wall_s=round(time.time() - t0, 1))
 
 
 if __name__ == "__main__":

@@ -20,7 +20,8 @@
  *   P_q      INT4, m x r row-major, two codes per byte (flat element 2k in the low nibble
  *            of byte k, 2k+1 in the high nibble, two's complement, codes in [-7, 7]);
  *            ceil(m*r/2) bytes.
- *   P_scale  fp32, ceil(m*r/256) group scales of P.
+ *   P_scale  fp32, ceil(m*r/256) group scales of P, finite and of magnitude below 2^125
+ *            (the INT4 dequantization computes q*s as one fma with -8*s).
  *            Two other projection formats can be selected per layer (qg_p_format): INT8
  *            codes in [-127, 127] (m*r bytes) with the same group scales, or bf16 values
  *            (m*r uint16, P_scale unused).
@@ -86,6 +87,21 @@ typedef enum {
   QG_P_BF16 = 2    /* P_q: m*r bf16 values (16-byte aligned); P_scale: unused (may be NULL) */
 } qg_p_format;
 
+/* Where an INT4 projection is dequantized (the step's first stage, P~ = bf16(q_P * s_P)).
+ * INLINE: inside the two MFMA kernels, on the way into LDS (the packed codes and their scales
+ * reach LDS by DMA and are converted there): no bf16 copy of P exists outside LDS and the
+ * workspace holds none (m*r*2 bytes less per layer). It needs a rank r with r % 32 == 0 and
+ * (r % 128 == 0 or 256 % r == 0); other ranks, and INT8 projections, fall back to PASS.
+ * PASS: a separate kernel writes the bf16 P~ to the workspace at the start of the step and
+ * both MFMA kernels read it. AUTO is PASS, the faster one on MI355X (about 10% of the step at
+ * rank 1024, 4% at rank 128, on the LLaMA-7B layer set); INLINE trades that for memory. The
+ * results are bit-identical either way. */
+typedef enum {
+  QG_DEQUANT_AUTO = 0,
+  QG_DEQUANT_INLINE = 1,
+  QG_DEQUANT_PASS = 2
+} qg_dequant_mode;
+
 /* Per-layer description for qgalore_step. */
 typedef struct {
   int64_t m, n, r;          /* W, G: m x n; P: m x r; M, V: r x n */
@@ -98,10 +114,15 @@ typedef struct {
   size_t workspace_bytes;
   void *stream;             /* hipStream_t */
   int32_t p_format;         /* qg_p_format of P_q / P_scale (0 = INT4) */
+  int32_t dequant_mode;     /* qg_dequant_mode (0 = AUTO); QG_ERR_ARG outside the enum */
 } qg_layer_desc;
 
-/* Device scratch one qgalore_step call needs for an m x n layer of rank r. */
+/* Device scratch one qgalore_step call needs for an m x n layer of rank r, for any format and
+ * dequant mode (the largest case: a bf16 copy of P in the workspace). 0 for an invalid shape. */
 size_t qgalore_workspace_bytes(int64_t m, int64_t n, int64_t r);
+/* The same for the layer as `desc` describes it (m, n, r, p_format, dequant_mode): without the
+ * bf16 copy of P when the projection is dequantized inline or stored in bf16. 0 when invalid. */
+size_t qgalore_layer_workspace_bytes(const qg_layer_desc *desc);
 
 /* One Q-GaLore optimizer step for one layer (AIMech Q-GaLore page, mechanism claim "INT4
  * projection and INT8 stochastic rounding", paper Section 3.2). Updates W_q, M_q, V_q and

@@ -32,7 +32,8 @@ class LayerDesc(ctypes.Structure):
                 ("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
                 ("alpha", c_float), ("M_scale", c_void_p), ("V_scale", c_void_p),
                 ("R_out", c_void_p), ("U_out", c_void_p), ("workspace", c_void_p),
-                ("workspace_bytes", c_size_t), ("stream", c_void_p), ("p_format", c_int32)]
+                ("workspace_bytes", c_size_t), ("stream", c_void_p), ("p_format", c_int32),
+                ("dequant_mode", c_int32)]
 
 
 class Layer(ctypes.Structure):
@@ -47,6 +48,8 @@ class Proj(ctypes.Structure):
 
 # projection storage formats (qg_p_format)
 P_FORMATS = {"int4": 0, "int8": 1, "bf16": 2}
+# where an INT4 projection is dequantized (qg_dequant_mode)
+DEQUANT_MODES = {"auto": 0, "inline": 1, "pass": 2}
 
 
 class Sched(ctypes.Structure):
@@ -56,6 +59,7 @@ class Sched(ctypes.Structure):
 
 EXPORTS = {
     "qgalore_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
+    "qgalore_layer_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerDesc)]),
     "qgalore_step": (c_int32, [ctypes.POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_int64, c_uint64]),
     "qgalore_plan_create": (c_int32, [ctypes.POINTER(Layer), c_int32, ctypes.POINTER(c_void_p)]),
@@ -194,7 +198,8 @@ def _proj_codes(Pq, m: int, r: int, fmt: str):
     raise ValueError(f"unknown projection format {fmt!r}")
 
 
-def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None):
+def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None,
+               dequant: str = "auto"):
     m, n, r = L.m, L.n, L.r
     d.m, d.n, d.r = m, n, r
     d.layer_id = L.layer_id
@@ -205,6 +210,7 @@ def _fill_desc(d: LayerDesc, L: LayerTensors, hp: dict, R_out=None, U_out=None):
     d.R_out = _ptr(R_out, torch.float32, (r, n), "R_out")
     d.U_out = _ptr(U_out, torch.float32, (m, n), "U_out")
     d.p_format = P_FORMATS[L.p_format]
+    d.dequant_mode = DEQUANT_MODES[dequant]
     ptrs = dict(G=_ptr(L.G, torch.bfloat16, (m, n), "G"),
                 W_q=_ptr(L.Wq, torch.int8, (m, n), "Wq"),
                 W_scale=_ptr(L.Ws, torch.float32, (n_groups(m * n),), "Ws"),
@@ -224,12 +230,13 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 def step(L: LayerTensors, t: int, seed: int, hp: dict | None = None, workspace=None,
-         R_out=None, U_out=None, stream=None) -> None:
-    """One optimizer step of one layer (asynchronous on the current stream)."""
+         R_out=None, U_out=None, stream=None, dequant: str = "auto") -> None:
+    """One optimizer step of one layer (asynchronous on the current stream). `dequant`:
+    where an INT4 projection is dequantized ("auto", "inline", "pass"; qg_dequant_mode)."""
     hp = hp or {}
     d = LayerDesc()
-    ptrs = _fill_desc(d, L, hp, R_out, U_out)
-    need = workspace_bytes(L.m, L.n, L.r)
+    ptrs = _fill_desc(d, L, hp, R_out, U_out, dequant)
+    need = int(lib().qgalore_layer_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
         workspace = alloc_workspace(need, L.Wq.device)
     d.workspace = _ptr(workspace, torch.uint8, None, "workspace")
@@ -244,14 +251,16 @@ class Plan:
     """A grouped step over many layers: one launch per kernel for the whole set."""
 
     def __init__(self, layers: list, hp: dict | None = None, per_layer_hp: list | None = None,
-                 R_out: list | None = None, U_out: list | None = None):
+                 R_out: list | None = None, U_out: list | None = None, dequant="auto"):
+        """`dequant`: one qg_dequant_mode name for every layer, or a list with one per layer."""
         hp = hp or {}
         arr = (Layer * len(layers))()
         self._keep = list(layers) + list(R_out or []) + list(U_out or [])
         for k, L in enumerate(layers):
             h = per_layer_hp[k] if per_layer_hp else hp
+            dq = dequant if isinstance(dequant, str) else dequant[k]
             ptrs = _fill_desc(arr[k].desc, L, h, R_out[k] if R_out else None,
-                              U_out[k] if U_out else None)
+                              U_out[k] if U_out else None, dq)
             for name, val in ptrs.items():
                 setattr(arr[k], name, val)
         handle = c_void_p()

@@ -24,13 +24,17 @@ struct LayerDev {
   int64_t off_r;       // workspace byte offset: split x rpitch fp32 partial sums of R
   int64_t off_n;       // workspace byte offset: bf16 r x n update N~
   int64_t off_p;       // workspace byte offset: bf16 m x r dequantized projection P~
-                       // (written at the start of every step, read by both MFMA kernels)
+                       // (written at the start of every step, read by both MFMA kernels;
+                       // absent when p_inline)
   float* R_out;        // optional
   float* U_out;        // optional
   int64_t m, n, r;
   int64_t rpitch;      // elements between split slabs of Rpart
   uint32_t layer_id;
   int32_t p_format;    // 0: INT4 codes, 1: INT8 codes, 2: bf16 values (Pq then holds them)
+  int32_t p_inline;    // 1: INT4 codes dequantized inside the MFMA kernels' stagers (no P~
+                       // region in the workspace, no dequant workgroups); 0: the kernels
+                       // stage the bf16 P~ (the dequant kernel's copy or the caller's bf16 P)
   int32_t split;       // K-splits of the projection
   int32_t fuse_adam;   // 1: one split and n % 256 == 0, so the projection kernel runs Adam
                        // on its tile rows (no R partials, no Adam launch for this layer)
@@ -55,6 +59,10 @@ struct StepArgs {
 };
 
 enum { KPROJ = 0, KADAM = 1, KBACK = 2, KDEQ = 3 };
+
+// Which projection paths a launch of the MFMA kernels compiles in: every layer stages a bf16
+// P~, every layer dequantizes its INT4 P in the stagers, or a mix of both.
+enum { kPStaged = 0, kPInline = 1, kPMixed = 2 };
 
 // `logical` is the workgroup's position in the launch after any renumbering.
 // Projection storage formats (the values of qg_p_format).
@@ -228,11 +236,6 @@ __device__ __forceinline__ float sbyte_to_f32(uint32_t w) {
 __device__ __forceinline__ uint32_t pack4_bytes(int q0, int q1, int q2, int q3) {
   return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
          __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
-}
-
-// Sign-extend nibble k (0..7) of a 32-bit word holding 8 packed INT4 codes.
-__device__ __forceinline__ int nibble(uint32_t w, int k) {
-  return ((int)(w << (28 - 4 * k))) >> 28;
 }
 
 // ---------------------------------------------------------------- Philox4x32-10 ---

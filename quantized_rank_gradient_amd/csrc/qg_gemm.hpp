@@ -8,9 +8,10 @@
 // three stages filled by LDS DMA with one or two stages in flight (gemm_kloop_dma).
 //
 // An MFMA lane needs 8 consecutive K values of one row of A (or one column of B). Operands
-// are kept in LDS in the layout their source has, so staging is a straight copy (plus the
-// INT4 dequant: code * group scale, then bf16 rounding, done on the way into LDS so P~
-// never exists in HBM):
+// are kept in LDS in the layout their source has, so staging is a straight copy, or for an
+// INT4 projection a dequantization on the way into LDS (code * group scale, then bf16
+// rounding: the DmaInt4 stagers below, whose codes arrive by LDS DMA and are converted in
+// LDS, so that the bf16 P~ exists only in LDS):
 //   * "K-contiguous" tiles (source [c][k]: the projection in the back-projection) are read
 //     with one 16-byte ds_read_b128 per fragment;
 //   * "K-major" tiles (source [k][c]: the gradient G, the update N~, the projection used
@@ -144,11 +145,25 @@ struct StageBf16K {
   }
 };
 
-// Dequantize one word of 8 INT4 codes with its group scale and pack the bf16 values.
+// Dequantize one word of 8 INT4 codes with its group scale: bf16(fl(q * s)) for each code,
+// packed. With u = q + 8 (the nibble with its top bit flipped, 0..15, converted exactly by a
+// byte-to-float conversion) a single fma gives RN(u * s - 8 s) = RN(q * s): the exact value of
+// u * s - 8 s is q * s, and -8 s is exact (a power-of-two multiple of s). That holds for every
+// scale of magnitude below 2^125, where 8 s stays finite; larger projection scales (entries
+// near the fp32 maximum) are outside the contract. (A code 0 with a negative scale gives +0
+// where the product gives -0; the quantizers never produce negative scales.) Every kernel
+// that reads INT4 projections converts them here, so all paths agree bit for bit.
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu;          // u of elements 0, 2, 4, 6 (bytes 0..3)
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // u of elements 1, 3, 5, 7
+  const float c = -8.0f * s;
   float f[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = mul_rn((float)nibble(w, e), s);
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = __builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), s, c);
+    f[2 * k + 1] = __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), s, c);
+  }
   return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                     pack_bf16x2(f[6], f[7]));
 }
@@ -196,6 +211,56 @@ struct StageInt4K {
     for (int u = 0; u < NC; ++u) {
       const int q = threadIdx.x + kThreads * u;
       *reinterpret_cast<uint4*>(lds + (q / CPR) * PITCH + 8 * (q % CPR)) = dequant8(w[u], s[u]);
+    }
+  }
+};
+
+// INT4 source [c][k] (row pitch ld = the K extent in codes, ld % 8 == 0, c_end rows) ->
+// K-contiguous LDS tile [c][k] in bf16 (kc_off layout), through registers. Each 8-code chunk
+// starts at a multiple of 8 in the flat index, so it lies inside one 256-element scale group;
+// chunks past the K extent or past c_end stage zeros.
+template <int W, int BK>
+struct StageInt4C {
+  static_assert(BK == 32, "K-contiguous tiles take 32-element rows");
+  static constexpr int CPR = BK / 8;
+  static constexpr int NC = W * CPR / kThreads;
+  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
+  rsrc_t rq, rsc;
+  uint32_t ld, c_end;
+  int c0;
+  uint32_t w[NC];
+  float s[NC];
+
+  __device__ StageInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_,
+                        int c0_)
+      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
+    const int64_t numel = c_end_ * ld_;
+    rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
+    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
+  }
+
+  template <int S = 0>
+  __device__ __forceinline__ void load(int64_t k0_) {
+    const uint32_t k0 = (uint32_t)k0_;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const uint32_t row = c0 + q / CPR;
+      const uint32_t k = k0 + 8 * (q % CPR);
+      const bool in = row < c_end && k < ld;
+      const uint32_t e = row * ld + k;
+      w[u] = bload32(rq, in ? (e >> 1) : kOOB);
+      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
+    }
+  }
+
+  template <int PITCH, int S = 0>
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+    static_assert(PITCH == 32, "K-contiguous tiles take 32-element rows");
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      *reinterpret_cast<uint4*>(lds + kc_off(q / CPR, q % CPR)) = dequant8(w[u], s[u]);
     }
   }
 };
@@ -424,6 +489,148 @@ struct DmaBf16C {
   }
 };
 
+// One wave-level load of 64 x 4 bytes: active lane i's word lands at LDS byte address
+// m0 + 4 i (inactive lanes write nothing). m0 is uniform across the wave (readfirstlane
+// states it, so that it is held in a scalar register).
+__device__ __forceinline__ void dma4(v4i32 rs, uint32_t off, uint32_t m0) {
+  const uint32_t m0s = __builtin_amdgcn_readfirstlane(m0);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(off), "s"(rs), "s"(m0s)
+      : "memory", "m0");
+}
+
+// ---------------------------------------------------------------------------------------
+// INT4 projection operands staged by LDS DMA and converted in LDS. Per K stage the packed
+// codes and one group scale per tile row go by DMA into a small code area; convert() then
+// writes the bf16 tile the MFMA fragments read (bf16(fl(q * s)), dequant8). The codes are a
+// quarter of the bf16 tile's bytes, so the projection is fetched from L2 at a quarter of the
+// traffic, and no bf16 copy of it exists outside LDS. One scale per row needs each row's run
+// of the stage inside one 256-element group; the host checks the rank for that.
+// ---------------------------------------------------------------------------------------
+
+// The projection P (m x r, INT4 row-major: row pitch ld = r codes) read as P~^T by the
+// projection kernel: tile rows are rows k of P (the K dimension), tile columns c0 .. c0 + W - 1
+// are rank indices. Each row's W codes lie in one group when r % 128 == 0 (c0 a multiple of
+// 128) or r divides 256 (then c0 = 0). Produces the K-major tile [BK][W] in the kmaj_slot
+// layout.
+template <int W, int BK>
+struct DmaInt4K {
+  static_assert(W == 128 && BK == 32, "the projection kernel's tile");
+  static constexpr int ROWB = W / 2;               // code bytes per tile row
+  static constexpr int CODE_BYTES = BK * ROWB;     // 2 KiB
+  static constexpr int AREA = CODE_BYTES + 256;    // + the BK row scales (a wave-load's span)
+  static constexpr int RPI = 256 / ROWB;           // tile rows per wave-level load
+  static constexpr int NI = BK / (4 * RPI);        // code loads per wave and stage
+  static constexpr int NV = NI + 1;                // vector memory operations per wave, stage
+  static_assert(NI * 4 * RPI == BK, "a stage splits evenly over the four waves");
+  const uint8_t* q;
+  v4i32 rsc;
+  uint32_t ld, k_end, c0;
+  uint32_t vo[NI];   // byte offset of this lane's code word from the stage's first row
+
+  __device__ DmaInt4K(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
+                      int64_t k_end_, int c0_)
+      : q(q_), ld((uint32_t)ld_), k_end((uint32_t)k_end_), c0((uint32_t)c0_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsc = rsrc_words(sc_, (uint32_t)(((rows * ld_ + kGroup - 1) / kGroup) * 4));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t row = (wave * NI + i) * RPI + lane / (ROWB / 4);
+      const uint32_t word = lane % (ROWB / 4);
+      const uint32_t col = c0 + 8 * word;
+      vo[i] = col < ld ? row * (ld / 2) + c0 / 2 + 4 * word : kOOB;
+    }
+  }
+
+  // area: LDS byte address of the stage's code area
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t area) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)k0_ < k_end ? (uint32_t)k0_ : k_end;
+    const v4i32 st = rsrc_words(q + (size_t)k0 * (ld / 2), (k_end - k0) * (ld / 2));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma4(st, vo[i], area + (wave * NI + i) * 256);
+    // the scales of tile rows 8 w .. 8 w + 7 (lane = tile row)
+    if (lane >= 8 * wave && lane < 8 * wave + 8) {
+      const uint32_t k = k0 + lane;
+      const uint32_t off = k < k_end ? ((k * ld + c0) >> 8) * 4 : kOOB;
+      dma4(rsc, off, area + CODE_BYTES);
+    }
+  }
+  // Thread t converts chunk t % 16 of tile rows t / 16 and t / 16 + 16 (16 lanes write one
+  // whole 256-byte row: every bank once).
+  __device__ __forceinline__ void convert(const uint8_t* area, uint16_t* tile) const {
+    const int c = threadIdx.x % 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = threadIdx.x / 16 + 16 * h;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(area + row * ROWB + 4 * c);
+      const float sc = *reinterpret_cast<const float*>(area + CODE_BYTES + 4 * row);
+      *reinterpret_cast<uint4*>(tile + row * W + 8 * kmaj_slot<W>(row, c)) = dequant8(w, sc);
+    }
+  }
+};
+
+// The projection P (m x r) read by rows in the back-projection: tile rows c0 .. c0 + W - 1 are
+// rows of P, K is the rank (ld = r codes per row, r % 32 == 0, so that a row's 32 codes of a
+// stage lie in one group). Produces the K-contiguous tile [W][BK] in the kc_off layout.
+template <int W, int BK>
+struct DmaInt4C {
+  static_assert(W == 128 && BK == 32, "the back-projection kernel's tile");
+  static constexpr int ROWB = BK / 2;              // code bytes per tile row and stage
+  static constexpr int CODE_BYTES = W * ROWB;      // 2 KiB
+  static constexpr int AREA = CODE_BYTES + 4 * W;  // + the W row scales
+  static constexpr int RPI = 256 / ROWB;           // tile rows per wave-level load
+  static constexpr int NI = W / (4 * RPI);         // code loads per wave and stage
+  static constexpr int NV = NI + 1;
+  static_assert(NI * 4 * RPI == W, "a stage splits evenly over the four waves");
+  const uint8_t* q;
+  v4i32 rsc;
+  uint32_t ld, c_end, c0;
+  uint32_t vo[NI];   // byte offset of this lane's code word from column 0 of the stage
+
+  __device__ DmaInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
+      : q(q_), ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0((uint32_t)c0_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsc = rsrc_words(sc_, (uint32_t)(((c_end_ * ld_ + kGroup - 1) / kGroup) * 4));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t rg = c0 + (wave * NI + i) * RPI + lane / (ROWB / 4);
+      vo[i] = rg < c_end ? rg * (ld / 2) + 4 * (lane % (ROWB / 4)) : kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t area) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
+    const v4i32 st = rsrc_words(q + k0 / 2, (c_end * ld - k0) / 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma4(st, vo[i], area + (wave * NI + i) * 256);
+    // the scales: wave w loads tile rows 64 (w / 2) + lane for the lanes of half w % 2
+    if ((lane >> 5) == (wave & 1)) {
+      const uint32_t rg = c0 + 64 * (wave >> 1) + lane;
+      const uint32_t off = rg < c_end ? ((rg * ld + k0) >> 8) * 4 : kOOB;
+      dma4(rsc, off, area + CODE_BYTES + 256 * (wave >> 1));
+    }
+  }
+
+  // Thread t converts chunk t % 4 of tile rows t / 4 and t / 4 + 64 (16 lanes write four whole
+  // 64-byte rows: every bank once).
+  __device__ __forceinline__ void convert(const uint8_t* area, uint16_t* tile) const {
+    const int c = threadIdx.x % 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = threadIdx.x / 4 + 64 * h;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(area + row * ROWB + 4 * c);
+      const float sc = *reinterpret_cast<const float*>(area + CODE_BYTES + 4 * row);
+      *reinterpret_cast<uint4*>(tile + kc_off(row, c)) = dequant8(w, sc);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // Fragment reads and the K loop.
 // ---------------------------------------------------------------------------------------
@@ -643,6 +850,86 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
           sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + 2 * T::A_ELEMS);
         }
         mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+      }
+    });
+  }
+  // the caller may reuse the LDS area: every wave is done with the last stage
+  __syncthreads();
+}
+
+// The product with an INT4 first operand converted in LDS (SA: DmaInt4K or DmaInt4C) and a
+// bf16 second operand by LDS DMA (SB), in a ring of NST LDS buffers (stage s in buffer
+// s % NST) and NST code areas (codes of stage s in area s % NST; `codes` holds NST * SA::AREA
+// bytes). Stage s's codes are issued one iteration before its B operand and converted one
+// iteration before it is multiplied. Per iteration j:
+//   wait until the B operand of stage j and the codes of stage j + 1 are in LDS (NST = 3:
+//   the loads issued in iteration j - 1 stay in flight; NST = 2: nothing does), and for this
+//   wave's LDS writes; barrier;
+//   issue the B operand of stage j + NST - 1 (into the buffer stage j - 1 left) and the codes
+//   of stage j + NST (into the area stage j's codes left);
+//   multiply stage j;
+//   convert the codes of stage j + 1 into the A tile of its buffer (free since stage j + 1 - NST
+//   was multiplied, before the previous barrier).
+template <class T, int NST, class SA, class SB>
+__device__ __forceinline__ void gemm_kloop_dma_cvt(const SA& sa, const SB& sb, int64_t k_begin,
+                                                   int64_t k_end, uint16_t* lds, uint8_t* codes,
+                                                   f32x16 (&acc)[T::XM][T::XN]) {
+  static_assert(T::DMA, "tile in the DMA layout");
+  static_assert(NST == 2 || NST == 3, "two or three LDS buffers");
+  constexpr int NB = SB::NI;   // B loads per wave and stage
+  constexpr int NC = SA::NV;   // code and scale loads per wave and stage
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  if (k_end <= k_begin) return;
+  const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
+  const uint32_t base = lds_addr(lds);   // byte addresses: stage s at base + 2 s STAGE
+  const uint32_t cbase = lds_addr(reinterpret_cast<const uint16_t*>(codes));
+  auto issue_b = [&](int s) {
+    sb.issue(k_begin + (int64_t)s * T::BK, base + 2 * ((s % NST) * T::STAGE + T::A_ELEMS));
+  };
+  auto issue_c = [&](int s) { sa.issue(k_begin + (int64_t)s * T::BK, cbase + (s % NST) * SA::AREA); };
+  // codes(0); then what iterations -(NST-1) .. -1 would have issued: B(s), codes(s + 1)
+  issue_c(0);
+  issue_b(0);
+  if (nk > 1) {
+    issue_c(1);
+    wait_vm_lds<NC>();
+  } else {
+    wait_vm_lds<0>();
+  }
+  barrier_nofence();
+  sa.convert(codes, lds);
+  if constexpr (NST == 3) {
+    if (nk > 1) issue_b(1);
+    if (nk > 2) issue_c(2);
+  }
+  for (int k0 = 0; k0 < nk; k0 += NST) {
+    static_for<NST>([&](auto dc) {
+      constexpr int buf = decltype(dc)::value;   // j % NST
+      const int j = k0 + buf;
+      if (j < nk) {
+        if constexpr (NST == 3) {
+          if (j + 2 < nk)
+            wait_vm_lds<NB + NC>();
+          else if (j + 1 < nk)
+            wait_vm_lds<NB>();
+          else
+            wait_vm_lds<0>();
+        } else {
+          wait_vm_lds<0>();
+        }
+        barrier_nofence();
+        if (j + NST - 1 < nk) issue_b(j + NST - 1);
+        if (j + NST < nk) issue_c(j + NST);
+        mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+        if (j + 1 < nk) {
+          constexpr int nb = (buf + 1) % NST;
+          sa.convert(codes + nb * SA::AREA, lds + nb * T::STAGE);
+        }
       }
     });
   }

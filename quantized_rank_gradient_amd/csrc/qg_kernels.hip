@@ -267,11 +267,23 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int kProjLdsElems =
     cmax(cmax(2 * ProjTile::STAGE, 3 * ProjTileD::STAGE), kAdamLdsElems);
 
+// LDS code areas of the projection kernel's INT4 stager (three stages). They sit after the
+// DMA ring in the kernel's LDS array, which the register-staged path and the Adam epilogue
+// share as well (neither of them uses code areas).
+using ProjCodes = DmaInt4K<ProjTile::BM, ProjTile::BK>;
+constexpr int kProjRingBytes = 3 * ProjTileD::STAGE * 2;
+constexpr int kProjLdsBytes(int pm) {
+  return pm == kPStaged ? kProjLdsElems * 2
+                        : cmax(kProjLdsElems * 2, kProjRingBytes + 3 * ProjCodes::AREA);
+}
+
 // VEC: rows of G are a multiple of 8 elements: 16-byte chunks staged straight into LDS
 // (T in the DMA layout). Otherwise G is read element by element through registers.
-template <class T, bool VEC>
+// PM: which projection paths to compile (kPStaged, kPInline, kPMixed); a layer takes the
+// INT4 stager path when L.p_inline.
+template <class T, bool VEC, int PM>
 __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& L, int local,
-                                             uint16_t* lds) {
+                                             uint16_t* lds, uint8_t* codes) {
   static_assert(T::DMA == VEC, "DMA layout exactly on the vector path");
   // local = ((s * tiles_j) + tj) * tiles_i + ti: the row tiles that share a block of G
   // columns are neighbours (and, after the renumbering, on the same XCD).
@@ -283,20 +295,30 @@ __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& 
   const int64_t k_begin = (int64_t)s * L.kslab;
   const int64_t k_end = min<int64_t>(L.m, k_begin + L.kslab);
 
-  // A = P~^T from the bf16 P~ (m x r, [k][i]) the dequant kernel wrote for this step.
-  const uint16_t* Pb = p_tilde(a, L);
+  // A = P~^T: the INT4 codes of P (m x r, [k][i]) dequantized on their way into LDS, or the
+  // bf16 P~ the dequant kernel wrote for this step (or the caller's bf16 P).
+  const bool inl = PM == kPInline || (PM == kPMixed && L.p_inline);
   f32x16 acc[T::XM][T::XN];
+  auto store_a = [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); };
+  auto store_b = [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); };
   if constexpr (VEC) {
-    const DmaBf16K<T::BM, T::BK> sa(Pb, L.r, k_end, L.r, i0);
     const DmaBf16K<T::BN, T::BK> sb(L.G, L.n, k_end, L.n, j0);
-    gemm_kloop_dma<T>(sa, sb, k_begin, k_end, lds, acc);
+    if (PM != kPStaged && inl) {
+      const ProjCodes sa(L.Pq, L.Ps, L.r, L.m, k_end, i0);
+      gemm_kloop_dma_cvt<T, 3>(sa, sb, k_begin, k_end, lds, codes, acc);
+    } else if (PM != kPInline) {
+      const DmaBf16K<T::BM, T::BK> sa(p_tilde(a, L), L.r, k_end, L.r, i0);
+      gemm_kloop_dma<T>(sa, sb, k_begin, k_end, lds, acc);
+    }
   } else {
-    StageBf16K<T::BM, T::BK, true> sa(Pb, L.r, L.m, k_end, L.r, i0);
     StageBf16K<T::BN, T::BK, false> sb(L.G, L.n, L.m, k_end, L.n, j0);
-    gemm_kloop<T, 1>(
-        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, k_begin,
-        k_end, lds, acc);
+    if (PM != kPStaged && inl) {
+      StageInt4K<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, k_end, L.r, i0);
+      gemm_kloop<T, 1>(sa, sb, store_a, store_b, k_begin, k_end, lds, acc);
+    } else if (PM != kPInline) {
+      StageBf16K<T::BM, T::BK, true> sa(p_tilde(a, L), L.r, L.m, k_end, L.r, i0);
+      gemm_kloop<T, 1>(sa, sb, store_a, store_b, k_begin, k_end, lds, acc);
+    }
   }
 
   if (L.fuse_adam) {
@@ -365,14 +387,16 @@ __device__ __forceinline__ void project_tile(const StepArgs& a, const LayerDev& 
 }
 
 // Held to 256 registers per lane so that two waves share each SIMD.
+template <int PM>
 __global__ __launch_bounds__(kThreads, 2) void qg_project(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kProjLdsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kProjLdsBytes(PM) / 2];
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + kProjRingBytes;
   int local;
   const LayerDev L = fetch_layer(a, KPROJ, xcd_remap(blockIdx.x, gridDim.x), local);
   if (L.n % 8 == 0)
-    project_tile<ProjTileD, true>(a, L, local, lds);
+    project_tile<ProjTileD, true, PM>(a, L, local, lds, codes);
   else
-    project_tile<ProjTile, false>(a, L, local, lds);
+    project_tile<ProjTile, false, PM>(a, L, local, lds, codes);
 }
 
 // ===================================================== back-projection + rounding ===
@@ -529,16 +553,24 @@ struct BackLds {
   static constexpr bool SMALL = T::BN == 128;
   static constexpr int NST = SMALL ? 2 : 3;   // DMA ring buffers
   static constexpr int MINB = SMALL ? 4 : 2;  // workgroups per CU
-  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, NST * DmaOf<T>::STAGE * 2),
-                                    kThreads / 64 * 32 * EP * 4);
+  static constexpr int RING = NST * DmaOf<T>::STAGE * 2;   // bytes of the DMA ring
+  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, RING), kThreads / 64 * 32 * EP * 4);
+  // with the INT4 stager's code areas after the ring (they share the array with the
+  // register-staged buffers and the epilogue, neither of which uses them)
+  static constexpr int bytes(int pm) {
+    return pm == kPStaged ? BYTES : cmax(BYTES, RING + NST * DmaInt4C<128, 32>::AREA);
+  }
 };
+
+using BackCodes = DmaInt4C<128, 32>;
 
 // VEC: rows of W (and of N~) are a multiple of 16 elements: 16-byte weight accesses
 // (prefetched before the product) and 16-byte chunks of N~ staged straight into LDS (T in
-// the DMA layout). BASE is the tile whose LDS area the kernel declares.
-template <class T, bool VEC, class BASE>
+// the DMA layout). BASE is the tile whose LDS area the kernel declares. PM as for the
+// projection.
+template <class T, bool VEC, class BASE, int PM>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
-                                          uint16_t* lds) {
+                                          uint16_t* lds, uint8_t* codes) {
   static_assert(T::DMA == VEC, "DMA layout exactly on the vector path");
   constexpr int EP = BackLds<BASE>::EP;
   constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk (element path)
@@ -591,22 +623,32 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
       }
   }
 
-  // A = P~ (rows i, K = rank index contiguous: the bf16 copy the projection kernel wrote),
+  // A = P~ (rows i, K = rank index contiguous): the INT4 codes of P dequantized on their way
+  // into LDS, or the bf16 P~ (the dequant kernel's copy or the caller's bf16 P).
   // B = N~ stored [k][j] (r x n).
-  const uint16_t* Pb = p_tilde(a, L);
+  const bool inl = PM == kPInline || (PM == kPMixed && L.p_inline);
   const uint16_t* Nb = reinterpret_cast<const uint16_t*>(a.ws + L.off_n);
   f32x16 acc[T::XM][T::XN];
+  auto store_a = [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); };
+  auto store_b = [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); };
   if constexpr (VEC) {
-    const DmaBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
     const DmaBf16K<T::BN, T::BK> sb(Nb, L.n, L.r, L.n, j0);
-    gemm_kloop_dma<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, acc);
+    if (PM != kPStaged && inl) {
+      const BackCodes sa(L.Pq, L.Ps, L.r, L.m, i0);
+      gemm_kloop_dma_cvt<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, codes, acc);
+    } else if (PM != kPInline) {
+      const DmaBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
+      gemm_kloop_dma<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, acc);
+    }
   } else {
-    StageBf16C<T::BM, T::BK> sa(Pb, L.r, L.m, i0);
     StageBf16K<T::BN, T::BK, false> sb(Nb, L.n, L.r, L.r, L.n, j0);
-    gemm_kloop<T, 1>(
-        sa, sb, [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); },
-        [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); }, 0, L.r,
-        lds, acc);
+    if (PM != kPStaged && inl) {
+      StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
+      gemm_kloop<T, 1>(sa, sb, store_a, store_b, 0, L.r, lds, acc);
+    } else if (PM != kPInline) {
+      StageBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
+      gemm_kloop<T, 1>(sa, sb, store_a, store_b, 0, L.r, lds, acc);
+    }
   }
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
@@ -647,15 +689,16 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
 // The large tile is held to 256 registers per lane: two workgroups per CU (two waves per
 // SIMD) hide the load latency better than more registers in one. The small one to 128.
-template <class T>
+template <class T, int PM>
 __global__ __launch_bounds__(kThreads, BackLds<T>::MINB) void qg_backproject(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::bytes(PM) / 2];
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + BackLds<T>::RING;
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
   if (L.n % 16 == 0)
-    back_tile<DmaOf<T>, true, T>(a, L, local, lds);
+    back_tile<DmaOf<T>, true, T, PM>(a, L, local, lds, codes);
   else
-    back_tile<T, false, T>(a, L, local, lds);
+    back_tile<T, false, T, PM>(a, L, local, lds, codes);
 }
 
 // ================================================================ quantization of P ===
@@ -712,8 +755,13 @@ __global__ __launch_bounds__(kThreads) void qg_quantize_int8(const float* P, int
 
 // ==================================================================== launchers ===
 
-hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(qg_project, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_project(const StepArgs& a, int grid, int pmode, hipStream_t s) {
+  if (pmode == kPInline)
+    hipLaunchKernelGGL(qg_project<kPInline>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (pmode == kPMixed)
+    hipLaunchKernelGGL(qg_project<kPMixed>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(qg_project<kPStaged>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s) {
@@ -724,11 +772,20 @@ hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(qg_adam, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
-hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s) {
-  if (big)
-    hipLaunchKernelGGL(qg_backproject<BackBig>, dim3(grid), dim3(kThreads), 0, s, a);
+template <class T>
+static void launch_back_t(const StepArgs& a, int grid, int pmode, hipStream_t s) {
+  if (pmode == kPInline)
+    hipLaunchKernelGGL((qg_backproject<T, kPInline>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (pmode == kPMixed)
+    hipLaunchKernelGGL((qg_backproject<T, kPMixed>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(qg_backproject<BackSmall>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((qg_backproject<T, kPStaged>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, hipStream_t s) {
+  if (big)
+    launch_back_t<BackBig>(a, grid, pmode, s);
+  else
+    launch_back_t<BackSmall>(a, grid, pmode, s);
   return hipGetLastError();
 }
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,

@@ -52,10 +52,15 @@ constexpr int kProjTileN = 256;
 constexpr int kBackTileM(bool big) { return big ? 128 : 128; }
 constexpr int kBackTileN(bool big) { return big ? 256 : 128; }
 
-hipError_t launch_project(const StepArgs& a, int grid, hipStream_t s);
+// pmode: kPStaged, kPInline or kPMixed (the layers of the launch).
+hipError_t launch_project(const StepArgs& a, int grid, int pmode, hipStream_t s);
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
-hipError_t launch_backproject(const StepArgs& a, int grid, bool big, hipStream_t s);
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, hipStream_t s);
+// A rank whose INT4 projection the MFMA kernels can dequantize in their stagers: each row's
+// run of a projection tile (128 rank indices) and of a back-projection stage (32) lies inside
+// one 256-element scale group.
+constexpr bool inline_rank(int64_t r) { return r % 32 == 0 && (r % 128 == 0 || 256 % r == 0); }
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,
                                 hipStream_t s);
 hipError_t launch_quantize_int8(const float* P, int64_t numel, int8_t* Pq, float* Ps,

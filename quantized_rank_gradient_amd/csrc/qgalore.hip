@@ -77,22 +77,37 @@ int choose_split(int64_t m, int64_t n, int64_t r) {
 }
 int64_t kslab_for(int64_t m, int split) { return cdiv(cdiv(m, kKSlab), split) * kKSlab; }
 
+// Whether a layer's INT4 projection is dequantized inside the MFMA kernels' stagers (no bf16
+// copy in the workspace, no dequant pass): the method's INT4 format, a rank whose tile rows
+// lie inside single scale groups, and the INLINE mode. The automatic choice is the separate
+// pass: on MI355X it is the faster of the two at every rank measured (the stagers convert
+// each projection element once per column tile, n / 256 times a step, where the pass
+// converts it once), and INLINE is the choice that saves the workspace's bf16 copy.
+bool p_inline(int32_t p_format, int64_t r, int32_t mode) {
+  return p_format == QG_P_INT4 && qg::inline_rank(r) && mode == QG_DEQUANT_INLINE;
+}
+bool valid_dequant_mode(int32_t mode) {
+  return mode == QG_DEQUANT_AUTO || mode == QG_DEQUANT_INLINE || mode == QG_DEQUANT_PASS;
+}
+
 // Per-layer workspace: split-K partial sums of R (fp32; absent when Adam is fused into the
-// projection), the bf16 update N~ (r x n) and the bf16 dequantized projection P~ (m x r)
-// that both MFMA kernels read.
+// projection), the bf16 update N~ (r x n) and, for projections the MFMA kernels do not
+// dequantize themselves, the bf16 dequantized projection P~ (m x r) that both read.
 struct WsLayout {
   int64_t rpitch, off_r, off_n, off_p, bytes;
 };
 WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base,
-                   int32_t p_format = QG_P_INT4) {
+                   int32_t p_format = QG_P_INT4, bool inl = false) {
   WsLayout w;
   w.rpitch = round_up(r * n, 64);
   w.off_r = base;
   const int64_t rbytes = fused_adam(n, split) ? 0 : (int64_t)split * w.rpitch * 4;
   w.off_n = base + round_up(rbytes, 256);
   w.off_p = w.off_n + round_up(r * n * 2, 256);
-  // a bf16 projection is staged from the caller's tensor: no dequantized copy
-  w.bytes = (w.off_p - base) + (p_format == QG_P_BF16 ? 0 : round_up(m * r * 2, 256));
+  // a bf16 projection is staged from the caller's tensor, an inline INT4 one from its codes:
+  // no dequantized copy
+  const bool copy = p_format != QG_P_BF16 && !inl;
+  w.bytes = (w.off_p - base) + (copy ? round_up(m * r * 2, 256) : 0);
   return w;
 }
 
@@ -126,6 +141,7 @@ qg_status check_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, co
   qg_status st = check_shape(d->m, d->n, d->r);
   if (st != QG_OK) return st;
   if ((st = check_p(d->p_format, P_q, P_scale)) != QG_OK) return st;
+  if (!valid_dequant_mode(d->dequant_mode)) return QG_ERR_ARG;
   if (!aligned(G, 16) || !aligned(W_q, 16) || !aligned(M_q, 16) || !aligned(V_q, 16) ||
       !aligned(d->R_out, 16) || !aligned(d->U_out, 16) || !aligned(W_scale, 4) ||
       !aligned(d->M_scale, 4) || !aligned(d->V_scale, 4))
@@ -173,13 +189,15 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.m = d->m;
   L.n = d->n;
   L.r = d->r;
-  const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base, d->p_format);
+  const bool inl = p_inline(d->p_format, d->r, d->dequant_mode);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base, d->p_format, inl);
   L.rpitch = w.rpitch;
   L.off_r = w.off_r;
   L.off_n = w.off_n;
   L.off_p = w.off_p;
   L.layer_id = d->layer_id;
   L.p_format = d->p_format;
+  L.p_inline = inl ? 1 : 0;
   L.split = split;
   L.fuse_adam = fused_adam(d->n, split) ? 1 : 0;
   L.kslab = (int32_t)kslab_for(d->m, split);
@@ -199,18 +217,19 @@ int grid_adam(const LayerDev& L) {
 }
 int grid_back(const LayerDev& L) { return L.b_tiles_i * L.b_tiles_j; }
 int grid_dequant(const LayerDev& L) {
-  return L.p_format == QG_P_BF16 ? 0 : (int)cdiv(L.m * L.r, qg::kThreads * qg::kDeqCodes);
+  return (L.p_format == QG_P_BF16 || L.p_inline) ? 0
+                                                 : (int)cdiv(L.m * L.r, qg::kThreads * qg::kDeqCodes);
 }
 
-qg_status launch_step(const StepArgs& a, const int grid[4], bool big, hipStream_t s) {
+qg_status launch_step(const StepArgs& a, const int grid[4], bool big, int pmode, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (grid[3] > 0 && (e = qg::launch_dequant(a, grid[3], s)) != hipSuccess)
     return hip_fail(e, "dequant kernel launch");
-  e = qg::launch_project(a, grid[0], s);
+  e = qg::launch_project(a, grid[0], pmode, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (grid[1] > 0 && (e = qg::launch_adam(a, grid[1], s)) != hipSuccess)
     return hip_fail(e, "Adam kernel launch");
-  e = qg::launch_backproject(a, grid[2], big, s);
+  e = qg::launch_backproject(a, grid[2], big, pmode, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   return QG_OK;
 }
@@ -224,6 +243,15 @@ extern "C" size_t qgalore_workspace_bytes(int64_t m, int64_t n, int64_t r) {
   return (size_t)ws_layout(m, n, r, choose_split(m, n, r), 0).bytes;
 }
 
+extern "C" size_t qgalore_layer_workspace_bytes(const qg_layer_desc* d) {
+  if (!d || check_shape(d->m, d->n, d->r) != QG_OK || !valid_format(d->p_format) ||
+      !valid_dequant_mode(d->dequant_mode))
+    return 0;
+  return (size_t)ws_layout(d->m, d->n, d->r, choose_split(d->m, d->n, d->r), 0, d->p_format,
+                           p_inline(d->p_format, d->r, d->dequant_mode))
+      .bytes;
+}
+
 extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q,
                                   const float* W_scale, const uint8_t* P_q, const float* P_scale,
                                   int8_t* M_q, int8_t* V_q, int64_t step, uint64_t seed) {
@@ -231,7 +259,8 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   if (st != QG_OK) return st;
   if ((st = check_step(step)) != QG_OK) return st;
   const int split = choose_split(d->m, d->n, d->r);
-  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0, d->p_format);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0, d->p_format,
+                               p_inline(d->p_format, d->r, d->dequant_mode));
   if (!d->workspace) return QG_ERR_NULL;
   if (!aligned(d->workspace, 16)) return QG_ERR_ALIGN;
   if (d->workspace_bytes < (size_t)w.bytes) return QG_ERR_WORKSPACE;
@@ -249,7 +278,8 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   a.seed_hi = (uint32_t)(seed >> 32);
   const int grid[4] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one),
                        grid_dequant(a.one)};
-  return launch_step(a, grid, big, static_cast<hipStream_t>(d->stream));
+  return launch_step(a, grid, big, a.one.p_inline ? qg::kPInline : qg::kPStaged,
+                     static_cast<hipStream_t>(d->stream));
 }
 
 // ========================================================================= grouped ===
@@ -262,6 +292,7 @@ struct qg_plan {
   int64_t ws_bytes = 0;
   float beta1 = 0.f, beta2 = 0.f;
   bool big = false;
+  int pmode = qg::kPStaged;   // projection paths of the MFMA launches (all staged / inline / mix)
   int device = 0;
   std::vector<hipEvent_t> events;   // 5 per recorded step when timing is enabled
   int timing_cap = 0;
@@ -323,7 +354,8 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
     const int split = grouped_fill ? 1 : choose_split(x.desc.m, x.desc.n, x.desc.r);
     LayerDev L = make_layer(&x.desc, x.G, x.W_q, x.W_scale, x.P_q, x.P_scale, x.M_q, x.V_q,
                             split, ws, big);
-    ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws, x.desc.p_format).bytes;
+    ws += ws_layout(x.desc.m, x.desc.n, x.desc.r, split, ws, x.desc.p_format, L.p_inline != 0)
+              .bytes;
     const int g[4] = {grid_project(L), grid_adam(L), grid_back(L), grid_dequant(L)};
     for (int k = 0; k < 4; ++k) {
       if (base[k] + g[k] > kMaxDim) {
@@ -338,6 +370,9 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   }
   p->ws_bytes = ws;
   for (int k = 0; k < 4; ++k) p->grid[k] = (int)base[k];
+  int n_inline = 0;
+  for (const LayerDev& L : p->layers) n_inline += L.p_inline;
+  p->pmode = n_inline == 0 ? qg::kPStaged : n_inline == count ? qg::kPInline : qg::kPMixed;
   p->proj_dirty.assign((size_t)count, 1);
 
   hipError_t e = hipGetDevice(&p->device);
@@ -411,7 +446,7 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
   }
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[0];
-  e = qg::launch_project(a, p->grid[0], s);
+  e = qg::launch_project(a, p->grid[0], p->pmode, s);
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[1];
@@ -420,7 +455,7 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
     return hip_fail(e, "Adam kernel launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
-  e = qg::launch_backproject(a, p->grid[2], p->big, s);
+  e = qg::launch_backproject(a, p->grid[2], p->big, p->pmode, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "timing event");
   return QG_OK;

@@ -56,7 +56,9 @@ class ScheduleRun:
         self.plan = B.Plan(self.layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2,
                                                 eps=cfg.eps, alpha=cfg.alpha),
                            R_out=self.R_out, U_out=self.U_out)
-        # dequantized projections are kept between steps; a refresh marks its layer changed
+        # with the separate dequant pass (INT4 ranks the MFMA kernels cannot dequantize
+        # themselves), dequantized projections are kept between steps and a refresh marks its
+        # layer changed; inline-dequantized layers keep nothing
         self.plan.cache_proj(True)
         self.ws = B.alloc_workspace(self.plan.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(self.r, 32))

@@ -4,10 +4,11 @@ seeded generators, and the comparison rules.
 Comparison rules (GPU against the oracle, same seeded inputs):
   * fp32 R and U: |gpu - oracle| <= 2e-3 * |oracle| + 2e-3 * rms(oracle) elementwise. U is
     compared at that bound with the oracle's back-projection of the N~ that the GPU's own R
-    gives. End to end, N~ elements that the two R round to different bf16 neighbours are
-    allowed only as explained flips (explained_n_flips: adjacent values, the oracle's N
-    within the R difference's reach of the midpoint, at most 1e-4 of the elements), and the
-    bound grows by alpha * |P~| |delta N~| in the columns that hold such a flip.
+    gives. End to end, N~ elements that the two R round to different bf16 values are allowed
+    only as flips the R difference explains (explained_n_flips: the GPU's N~ is the rounding
+    of the N its R gives, the oracle's N lies within the R difference's reach of a rounding
+    boundary, at most 1e-4 of the elements), and the bound grows by alpha * |P~| |delta N~|
+    in the columns that hold such a flip.
   * INT8 codes (W, M, V): identical, except +-1 differences at elements whose rounding input
     sits at a decision boundary within the reach of the tolerated fp32 difference. For W the
     rounding input is d = W + U/s + u and the boundary an integer; for M and V it is x * inv
@@ -105,40 +106,52 @@ def assert_codes(gpu, ref, x_ref, boundary, reach, name, cap=1e-4):
 N_FLIP_CAP = 1e-4
 
 
+def _bf16_step(b, up):
+    """The bf16 value next to the bf16-exact fp32 values b (bit patterns as int64), one unit
+    up (towards +inf) where `up`, else down."""
+    o = np.where(b < 0, -(b & 0x7FFFFFFF), b) >> 16          # sign-magnitude to integer line
+    o = o + np.where(up, 1, -1)
+    bits = np.where(o >= 0, o << 16, ((-o) << 16) | 0x80000000)
+    return bits.astype(np.uint32).view(F32)
+
+
 def explained_n_flips(N_g, Nb_g, N_o, Nb_o, P_rows, alpha, cap=N_FLIP_CAP):
     """The N~ elements that the GPU's R and the oracle's R round to different bf16 values, each
-    checked to be an explained flip, and the effect those flips carry into U.
+    checked to be a flip that the R difference explains, and the effect those flips carry
+    into U.
 
-    N_g is the oracle's Adam on the GPU's own fp32 R, N_o the oracle's end to end (both fp32,
-    before rounding); Nb_g, Nb_o their bf16 roundings. A flip is explained when:
-      * the two values are bf16 neighbours (one unit apart in the last place), and
-      * the oracle's N lies within reach of the midpoint that separates them, the reach being
-        |N_g - N_o| (what the tolerated R difference moves N by) plus 4 fp32 ulps of N.
-    At most `cap` of the r*n elements may flip (at least one is allowed). Returns the bound
-    extension for the end-to-end U check: alpha * |P~| |Nb_g - Nb_o|, which is non-zero only in
-    the columns of N~ that hold a flip."""
+    N_g is the oracle's Adam on the GPU's own fp32 R (which the caller has checked against the
+    R bound), N_o the oracle's end to end (both fp32, before rounding); Nb_g, Nb_o their bf16
+    roundings. Where N is steep in R (first step, R near zero: N = -lr R / (|R| + eps)) a
+    tolerated R difference can move N across several bf16 values, so the rule is:
+      * Nb_g is the rounding of N_g (the GPU's N~ is the one its R gives);
+      * the oracle's N lies within reach of the rounding boundary next to it in the direction
+        of N_g, the reach being |N_g - N_o| (what the R difference moves N by) plus 4 fp32
+        ulps of N (given the two roundings, a consistency check);
+      * at most `cap` of the r*n elements flip (at least one is allowed).
+    Returns the bound extension for the end-to-end U check: alpha * |P~| |Nb_g - Nb_o|, which
+    is non-zero only in the columns of N~ that hold a flip."""
+    from oracle import qgalore_oracle as O
     Nb_g = np.asarray(Nb_g, F32)
     Nb_o = np.asarray(Nb_o, F32)
+    assert np.array_equal(O.bf16_round(np.asarray(N_g, F32)), Nb_g), "GPU N~ is not bf16(N) of its R"
+    assert np.array_equal(O.bf16_round(np.asarray(N_o, F32)), Nb_o), "oracle N~ is not bf16(N)"
     flips = Nb_g != Nb_o
     nflip = int(flips.sum())
     if nflip == 0:
         return 0.0
     assert nflip <= max(1.0, cap * flips.size), (
-        f"N~: {nflip} of {flips.size} elements round to the other bf16 neighbour "
+        f"N~: {nflip} of {flips.size} elements round to another bf16 value "
         f"({nflip / flips.size:.2e} > {cap})")
-    bg = Nb_g[flips].view(np.int32).astype(np.int64)
+    ng = np.asarray(N_g, F32)[flips].astype(np.float64)
+    no = np.asarray(N_o, F32)[flips].astype(np.float64)
     bo = Nb_o[flips].view(np.int32).astype(np.int64)
-    # bf16 values as signed integers on one line (sign-magnitude to two's complement order)
-    def ordered(b):
-        return np.where(b < 0, -(b & 0x7FFFFFFF), b) >> 16
-    assert np.all(np.abs(ordered(bg) - ordered(bo)) == 1), "N~: a flip skips a bf16 value"
-    ng = np.asarray(N_g, np.float64)[flips]
-    no = np.asarray(N_o, np.float64)[flips]
-    mid = (Nb_g[flips].astype(np.float64) + Nb_o[flips].astype(np.float64)) / 2
+    nxt = _bf16_step(bo, ng > no).astype(np.float64)
+    mid = (Nb_o[flips].astype(np.float64) + nxt) / 2
     reach = np.abs(ng - no) + 4 * np.spacing(np.abs(np.asarray(N_o, F32)[flips])).astype(np.float64)
     margin = np.abs(no - mid)
     assert np.all(margin <= reach), (
-        f"N~: flips away from a bf16 midpoint (margins {margin[margin > reach][:4]}, "
+        f"N~: flips away from a bf16 rounding boundary (margins {margin[margin > reach][:4]}, "
         f"reach {reach[margin > reach][:4]})")
     dNb = np.abs(Nb_g.astype(np.float64) - Nb_o.astype(np.float64))
     cols = np.flatnonzero(flips.any(axis=0))

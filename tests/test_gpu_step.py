@@ -324,3 +324,82 @@ def test_non_finite_rounding_inputs_keep_the_old_code(m, n):
             for t in range(16):
                 sums = (sums + runs[:, t]).astype(np.float32)
         assert (~np.isfinite(sums)).any(), "no 16-element run of group 2 overflows its sum"
+
+
+# ------------------------------------------- where the INT4 projection is dequantized ---
+
+@pytest.mark.parametrize("m,n,r", [
+    (512, 512, 128),      # small back-projection tile, vector paths
+    (1376, 512, 128),     # row tail of the projection's K loop
+    (2048, 5461, 64),     # odd n: register-staged paths of both kernels
+    (5461, 256, 32),      # odd m, rank 32 (one projection tile covers the whole rank)
+    (4096, 256, 1024),    # rank 1024: eight projection row tiles, 32 back-projection stages
+    (640, 512, 256),      # rank 256, large back-projection tile
+])
+def test_inline_and_pass_dequant_give_identical_steps(m, n, r):
+    """The INT4 projection dequantized inside the MFMA kernels' stagers and by the separate
+    pass into the workspace: the same bf16 P~ enters the same products in the same order, so
+    every output is bit-identical; the inline step also matches the oracle."""
+    cfg = custom_cfg(m, n, r)
+    L = cfg.layers[0]
+    st, P = PAR.host_state(cfg, L, r, "random")
+    G = WL.gradient_bf16(cfg, L, 2)
+    outs = {}
+    for mode in ("inline", "pass"):
+        Lt = PAR.to_device(st, G, P)
+        R_out = torch.empty((r, n), dtype=torch.float32, device="cuda")
+        U_out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        _B().step(Lt, 2, WL.SR_SEED, hp=dict(lr=1e-3, alpha=0.25), R_out=R_out, U_out=U_out,
+                  dequant=mode)
+        torch.cuda.synchronize()
+        outs[mode] = snapshot(Lt, R_out, U_out)
+    for k in outs["pass"]:
+        assert np.array_equal(outs["inline"][k].view(np.uint8), outs["pass"][k].view(np.uint8)), k
+    before = st.copy()
+    res = O.qgalore_step(st, G, 2, WL.SR_SEED)
+    PAR.check_step(before, res, st, outs["inline"], t=2)
+
+
+def test_workspace_without_a_bf16_projection_copy():
+    """A layer whose INT4 projection is dequantized inline needs no bf16 copy of P in its
+    workspace: the size query drops m * r * 2 bytes against the separate pass."""
+    B = _B()
+    import ctypes
+    d = B.LayerDesc()
+    d.m, d.n, d.r, d.p_format = 4096, 4096, 1024, 0
+    d.dequant_mode = B.DEQUANT_MODES["pass"]
+    with_copy = B.lib().qgalore_layer_workspace_bytes(ctypes.byref(d))
+    d.dequant_mode = B.DEQUANT_MODES["inline"]
+    inline = B.lib().qgalore_layer_workspace_bytes(ctypes.byref(d))
+    assert with_copy - inline == 4096 * 1024 * 2
+    d.r = 96                                          # no inline path at this rank
+    assert B.lib().qgalore_layer_workspace_bytes(ctypes.byref(d)) >= 4096 * 96 * 2
+
+
+def test_mixed_plan_of_inline_and_pass_layers():
+    """One grouped launch over layers dequantized inline, by the pass, and at a rank that has
+    only the pass: every layer matches the oracle."""
+    B = _B()
+    shapes = [(512, 512, 128, "inline"), (512, 512, 128, "pass"), (300, 200, 64, "auto"),
+              (256, 512, 96, "auto"), (1376, 512, 128, "inline")]
+    states, devs, Gs, Rs, Us, modes = [], [], [], [], [], []
+    for k, (m, n, r, mode) in enumerate(shapes):
+        cfg = WL.Config("custom", 9, (WL.LayerShape(20 + k, f"{m}x{n}", m, n),), r=r,
+                        sigma=1e-3)
+        L = cfg.layers[0]
+        st, P = PAR.host_state(cfg, L, r, "random")
+        G = WL.gradient_bf16(cfg, L, 3)
+        states.append(st)
+        devs.append(PAR.to_device(st, G, P))
+        Gs.append(G)
+        Rs.append(torch.empty((r, n), dtype=torch.float32, device="cuda"))
+        Us.append(torch.empty((m, n), dtype=torch.float32, device="cuda"))
+        modes.append(mode)
+    plan = B.Plan(devs, hp=dict(lr=1e-3, alpha=0.25), R_out=Rs, U_out=Us, dequant=modes)
+    plan.step(3, WL.SR_SEED)
+    torch.cuda.synchronize()
+    for st, Lt, G, Ro, Uo in zip(states, devs, Gs, Rs, Us):
+        before = st.copy()
+        res = O.qgalore_step(st, G, 3, WL.SR_SEED)
+        PAR.check_step(before, res, st, snapshot(Lt, Ro, Uo), t=3)
+    plan.close()

@@ -49,3 +49,30 @@ def test_division_by_recip64_subnormal_and_overflowing_quotients():
     a = np.array([1e-45, 3e-45, 1.17e-38, 1.2e-38, 3.4e38, -3.4e38, 3.0e37], np.float32)
     with np.errstate(all="ignore"):
         assert _same(_via_recip64(a, np.full_like(a, b)), a / b).all()
+
+
+def _fma32(a, b, c):
+    """RN32(a * b + c) for fp32 inputs: the product of two fp32 values and its sum with an
+    fp32 value of at most 2^4 times its size is exact in fp64 here (|a| <= 15), so one
+    rounding to fp32 is the fused multiply-add."""
+    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
+
+
+def test_int4_dequant_by_one_fma_is_the_rounded_product():
+    """The INT4 dequantization computes fl(q * s) as RN(u * s - 8 s) with u = q + 8: for every
+    code q in [-8, 7] and scales across the fp32 range below 2^125 (subnormal, tiny, typical,
+    large), including scales with full 24-bit significands where q * s itself rounds."""
+    rng = np.random.default_rng(5)
+    n = 200_000
+    s = (rng.random(n) + 1.0) * np.exp2(rng.integers(-149, 125, n))
+    s = s.astype(np.float32)
+    s[:6] = [1e-45, 3e-39, 1.17549435e-38, 0.1, 1.0, np.float32(2.0 ** 124 * 1.9999999)]
+    s = s[np.abs(s) < np.float32(2.0 ** 125)]
+    for q in range(-8, 8):
+        u = np.full(s.shape, q + 8, np.float32)
+        c = (np.float32(-8.0) * s).astype(np.float32)
+        assert np.isfinite(c).all()
+        got = _fma32(u, s, c)
+        want = (np.float32(q) * s).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32) & 0x7FFFFFFF, want.view(np.uint32) & 0x7FFFFFFF) \
+            and np.array_equal(got, want), q
