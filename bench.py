@@ -511,22 +511,24 @@ def _oracle_worker(layer_ids, barrier, out):
     out.put((sum(e for _, _, e in jobs), t0, t1))
 
 
-def cpu_baseline(nlayers=7):
-    """The oracle, as it stands, on the layers of block 0 of the 7B set at rank 1024 (q, k, v,
-    o, gate, up, down): one full oracle step per layer. The layers are spread over worker
-    processes, one per host core this process may run on (at most one per layer), each with
-    one BLAS thread; every worker builds its inputs first, and the timed span runs from the
-    common start to the last worker's end. Call it before the process touches the GPU: the
-    workers are forked."""
+def cpu_baseline(max_layers=8):
+    """The oracle, as it stands, on a bounded sample of the 7B set at rank 1024: one full oracle
+    step on each of the first attention layers (4096 x 4096: q, k, v, o of blocks 0, 1, ...),
+    one layer per worker process, as many workers as host cores this process may run on (at
+    most max_layers), each with one BLAS thread. Every worker builds its inputs first; the timed
+    span runs from the common start to the last worker's end. Call it before the process touches
+    the GPU: the workers are forked."""
     import multiprocessing as mp
+    from quantized_rank_gradient_amd import workloads as WL
     host = len(os.sched_getaffinity(0))
-    workers = max(1, min(host, nlayers))
+    workers = max(1, min(host, max_layers))
+    cfg = WL.CONFIGS["llama7b_r1024"]
+    sample = [k for k, L in enumerate(cfg.layers) if L.m == L.n][:workers]
+    nlayers = len(sample)
     ctx = mp.get_context("fork")
     barrier = ctx.Barrier(workers)
     out = ctx.Queue()
-    # largest layers first, round robin, so the workers' loads are close
-    order = sorted(range(nlayers), key=lambda k: -k)
-    parts = [order[w::workers] for w in range(workers)]
+    parts = [[k] for k in sample]
     procs = [ctx.Process(target=_oracle_worker, args=(parts[w], barrier, out))
              for w in range(workers)]
     for pr in procs:
@@ -540,9 +542,9 @@ def cpu_baseline(nlayers=7):
     return dict(value=round(elems / span, 1), unit="weight elems/s", cores=workers,
                 kind="oracle", host_cores=host, blas_threads_per_worker=1,
                 seconds=round(span, 2), cpu_seconds=round(busy, 2),
-                sample=f"one full oracle step of each of the {nlayers} rank-1024 layers of "
-                       f"block 0 of the 7B set ({elems} weight elements) over {workers} worker "
-                       f"processes; input generation not timed")
+                sample=f"one full oracle step of each of {nlayers} rank-1024 4096x4096 layers "
+                       f"(q, k, v, o of the first blocks) of the 7B set ({elems} weight "
+                       f"elements), one per worker process; input generation not timed")
 
 
 def main():
