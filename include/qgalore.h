@@ -133,6 +133,20 @@ qg_status qgalore_step(const qg_layer_desc *desc, const uint16_t *G, int8_t *W_q
                        const float *W_scale, const uint8_t *P_q, const float *P_scale,
                        int8_t *M_q, int8_t *V_q, int64_t step, uint64_t seed);
 
+/* For callers that cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): qgalore_step with the scratch taken from a fixed
+ * device array inside the library instead of desc->workspace (ignored, as is
+ * desc->workspace_bytes). The array holds QG_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, stays
+ * resident until the process ends, and is shared by every call on that GPU: calls that overlap
+ * on one GPU race and must be serialized by the caller. A layer whose workspace
+ * (qgalore_layer_workspace_bytes) exceeds the array returns QG_ERR_WORKSPACE, with the sizes
+ * in qgalore_last_error(); every 7B-shaped layer up to rank 1024 fits. Allocates nothing;
+ * otherwise as qgalore_step (same validation, results identical to it). */
+#define QG_NOALLOC_SCRATCH_BYTES (64u << 20)
+qg_status qgalore_step_noalloc(const qg_layer_desc *desc, const uint16_t *G, int8_t *W_q,
+                               const float *W_scale, const uint8_t *P_q, const float *P_scale,
+                               int8_t *M_q, int8_t *V_q, int64_t step, uint64_t seed);
+
 /* ------------------------------------------------------------------------------------
  * Grouped step: one launch per kernel over a whole set of layers (the per-layer step of
  * the same page, applied to every linear layer of a model at once).
@@ -303,7 +317,8 @@ qg_status qgalore_mfma_probe(const uint16_t *operands, int64_t n_elems, float *o
 
 /* ------------------------------------------------------------------------------------ */
 const char *qgalore_status_str(qg_status s);
-const char *qgalore_last_error(void);   /* thread-local text of the last QG_ERR_HIP */
+const char *qgalore_last_error(void);   /* thread-local text of the last QG_ERR_HIP (or of
+                                           qgalore_step_noalloc's QG_ERR_WORKSPACE) */
 const char *qgalore_version(void);
 
 #ifdef __cplusplus

@@ -62,6 +62,8 @@ EXPORTS = {
     "qgalore_layer_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerDesc)]),
     "qgalore_step": (c_int32, [ctypes.POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_int64, c_uint64]),
+    "qgalore_step_noalloc": (c_int32, [ctypes.POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_uint64]),
     "qgalore_plan_create": (c_int32, [ctypes.POINTER(Layer), c_int32, ctypes.POINTER(c_void_p)]),
     "qgalore_plan_workspace_bytes": (c_size_t, [c_void_p]),
     "qgalore_plan_step": (c_int32, [c_void_p, c_int64, c_uint64, c_void_p, c_size_t, c_void_p]),
@@ -245,6 +247,23 @@ def step(L: LayerTensors, t: int, seed: int, hp: dict | None = None, workspace=N
     _check(lib().qgalore_step(ctypes.byref(d), ptrs["G"], ptrs["W_q"], ptrs["W_scale"],
                               ptrs["P_q"], ptrs["P_scale"], ptrs["M_q"], ptrs["V_q"], int(t),
                               int(seed) & (2 ** 64 - 1)), "qgalore_step")
+
+
+# size of the library's own scratch array used by step_noalloc (QG_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def step_noalloc(L: LayerTensors, t: int, seed: int, hp: dict | None = None, R_out=None,
+                 U_out=None, stream=None, dequant: str = "auto") -> None:
+    """qgalore_step_noalloc: one layer's step with the library's fixed scratch array instead
+    of a workspace (no device allocation anywhere on this path)."""
+    hp = hp or {}
+    d = LayerDesc()
+    ptrs = _fill_desc(d, L, hp, R_out, U_out, dequant)
+    d.stream = _stream(stream)
+    _check(lib().qgalore_step_noalloc(ctypes.byref(d), ptrs["G"], ptrs["W_q"], ptrs["W_scale"],
+                                      ptrs["P_q"], ptrs["P_scale"], ptrs["M_q"], ptrs["V_q"],
+                                      int(t), int(seed) & (2 ** 64 - 1)), "qgalore_step_noalloc")
 
 
 class Plan:

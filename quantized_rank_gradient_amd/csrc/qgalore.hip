@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -273,6 +274,75 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   a.ws = static_cast<char*>(d->workspace);
   a.table = nullptr;
   a.wg_layer = nullptr;
+  step_constants(d->beta1, d->beta2, step, a);
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  const int grid[4] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one),
+                       grid_dequant(a.one)};
+  return launch_step(a, grid, big, a.one.p_inline ? qg::kPInline : qg::kPStaged,
+                     static_cast<hipStream_t>(d->stream));
+}
+
+// ============================================= single layer without a workspace argument ===
+// For callers that cannot allocate device memory: the step's scratch (split-K partial sums of
+// R, N~ and the dequantized projection) lives in a file-scope device array of fixed size, one
+// per GPU, kept until the process ends. Every call on a GPU shares that GPU's array, so calls
+// that overlap on one GPU (different streams, or threads) race on it. The step writes every
+// scratch element it later reads, so nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = QG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's scratch array, looked up once per device (with
+// that device current). The array's name on the host is only a stand-in for the symbol.
+qg_status device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "device index beyond the scratch table";
+    return QG_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QG_OK;
+}
+}  // namespace
+
+extern "C" qg_status qgalore_step_noalloc(const qg_layer_desc* d, const uint16_t* G,
+                                          int8_t* W_q, const float* W_scale, const uint8_t* P_q,
+                                          const float* P_scale, int8_t* M_q, int8_t* V_q,
+                                          int64_t step, uint64_t seed) {
+  qg_status st = check_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q);
+  if (st != QG_OK) return st;
+  if ((st = check_step(step)) != QG_OK) return st;
+  const int split = choose_split(d->m, d->n, d->r);
+  const WsLayout w = ws_layout(d->m, d->n, d->r, split, 0, d->p_format,
+                               p_inline(d->p_format, d->r, d->dequant_mode));
+  if ((size_t)w.bytes > kNoAllocScratchBytes) {
+    g_last_error = "layer needs " + std::to_string(w.bytes) + " bytes of scratch, more than the " +
+                   std::to_string(kNoAllocScratchBytes) + " of the no-alloc step";
+    return QG_ERR_WORKSPACE;
+  }
+  if ((st = device_present()) != QG_OK) return st;
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws)) != QG_OK) return st;
+
+  StepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const bool big = big_tiles(d->r);
+  a.one = make_layer(d, G, W_q, W_scale, P_q, P_scale, M_q, V_q, split, 0, big);
+  a.ws = static_cast<char*>(ws);
   step_constants(d->beta1, d->beta2, step, a);
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
