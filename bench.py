@@ -87,25 +87,33 @@ class Variant:
     gradient each step instead of settling on a repeated one."""
 
     def __init__(self, cfg, r, G_sets, W_list, Ws_list, torch, B, WL, fast=False, fmt="int4",
-                 dequant="auto", keep_proj=False):
+                 dequant="auto", keep_proj=False, window=0):
+        """window > 0: the step runs as consecutive plans of `window` layers each, sharing one
+        workspace sized for the largest (the step-transient N~ and bf16 P~ of only `window`
+        layers exist at a time)."""
         self.cfg, self.r, self.fmt = cfg, r, fmt
         self.torch, self.B = torch, B
         t0 = time.time()
         self.layers, self.pnew = build_layer_set(cfg, r, G_sets[0], W_list, Ws_list, torch, B,
                                                  WL, fast, fmt)
         hp = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, alpha=cfg.alpha)
-        self.plans = []
+        nl = len(self.layers)
+        w = window if 0 < window < nl else nl
+        self.chunks = [(a, min(nl, a + w)) for a in range(0, nl, w)]
+        self.plans = []     # per gradient set: one plan per chunk of layers
         for Gs in G_sets:
             lt = [dataclasses.replace(L, G=G) for L, G in zip(self.layers, Gs)]
-            self.plans.append(B.Plan(lt, hp=hp, dequant=dequant))
-        self.plan = self.plans[0]
+            self.plans.append([B.Plan(lt[a:b], hp=hp, dequant=dequant) for a, b in self.chunks])
+        self.all_plans = [p for ps in self.plans for p in ps]
+        self.plan = self.plans[0][0]
+        self.workspace_bytes = max(p.workspace_bytes for p in self.all_plans)
         # keep_proj (comparison runs only): with the separate dequant pass, keep the bf16
         # projections between steps and re-dequantize only the layers a refresh test replaced.
         # The step proper dequantizes every projection every step.
-        self.keep_proj = keep_proj and len(self.plans) == 1
+        self.keep_proj = keep_proj and len(self.all_plans) == 1
         if self.keep_proj:
             self.plan.cache_proj(True)
-        self.ws = B.alloc_workspace(self.plan.workspace_bytes)
+        self.ws = B.alloc_workspace(self.workspace_bytes)
         self.cws = B.alloc_workspace(B.cossim_batch_workspace_bytes(r, 32))
         self.cs_out = torch.zeros(len(self.layers), dtype=torch.float32, device="cuda")
         # staggered schedules: layer l had its first refresh at (l mod 25) - 25
@@ -124,7 +132,8 @@ class Variant:
         for a refresh gets a new projection, which the next step dequantizes again."""
         self.t += 1
         t = self.t
-        self.plans[t % len(self.plans)].step(t, 1234, self.ws)
+        for p in self.plans[t % len(self.plans)]:
+            p.step(t, 1234, self.ws)
         due = [k for k, s in enumerate(self.sched) if s.due(t)]
         if due:
             pairs = [(*self.pnew[k], self.layers[k].Pq, self.layers[k].Ps, self.layers[k].m,
@@ -142,7 +151,7 @@ class Variant:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        for p in self.plans:
+        for p in self.all_plans:
             p.enable_timing(steps)
         self.tests = 0
         start = torch.cuda.Event(enable_timing=True)
@@ -154,17 +163,16 @@ class Variant:
         end.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
-        acc, nrec = [0.0] * 4, 0
-        for p in self.plans:
+        acc = [0.0] * 4     # summed over the chunks of a step, averaged over the steps
+        for p in self.all_plans:
             kms_p, n_p = p.kernel_times()
             acc = [a + k * n_p for a, k in zip(acc, kms_p)]
-            nrec += n_p
             p.enable_timing(0)
-        kms = [a / max(1, nrec) for a in acc]
+        kms = [a / steps for a in acc]
         return total_ms / steps, kms, self.tests / steps
 
     def close(self):
-        for p in self.plans:
+        for p in self.all_plans:
             p.close()
 
     def time_cossim(self, reps=5):
@@ -582,6 +590,9 @@ def main():
                     help="where INT4 projections are dequantized: in the MFMA kernels' stagers "
                          "(inline), by a separate pass into the workspace (pass), or the "
                          "library's choice (auto)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="run the step as consecutive plans of this many layers sharing one "
+                         "workspace (0: one plan over the whole set)")
     ap.add_argument("--keep-proj", action="store_true",
                     help="comparison: with the separate pass, keep dequantized projections "
                          "between steps (only refreshed layers are dequantized again)")
@@ -732,7 +743,7 @@ def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
     results = []
     for vcfg, r in variants:
         v = Variant(vcfg, r, G_sets, W_list, Ws_list, torch, B, WL, args.fast_setup,
-                    args.p_format, args.dequant, args.keep_proj)
+                    args.p_format, args.dequant, args.keep_proj, args.window)
         ms, kms, tests = v.time_steps(steps, warmup)
         cs_ms = v.time_cossim()
         a = algorithmic(vcfg, r, args.p_format)
@@ -753,7 +764,8 @@ def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
                    gradient_sets=g_sets,
                    dequant=args.dequant + ("+keep" if v.keep_proj else ""),
-                   workspace_gib=round(v.plan.workspace_bytes / 2**30, 3),
+                   window=len(v.chunks) > 1 and args.window or None,
+                   workspace_gib=round(v.workspace_bytes / 2**30, 3),
                    projection_gib=round(p_bytes / 2**30, 3),
                    kernel_ms=kernel_ms,
                    optimizer_ms=round(sum(kms), 4),

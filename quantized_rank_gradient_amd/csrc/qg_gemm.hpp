@@ -401,14 +401,16 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(p));
 }
 
-// One wave-level load of 64 x 16 bytes into the KiB at LDS byte address m0.
+// One wave-level load of 64 x 16 bytes into the KiB at LDS byte address m0 (uniform across
+// the wave; readfirstlane states it).
 __device__ __forceinline__ void dma16(v4i32 rs, uint32_t off, uint32_t m0) {
+  const uint32_t m0s = __builtin_amdgcn_readfirstlane(m0);
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
-      : "v"(off), "s"(rs), "s"(m0)
+      : "v"(off), "s"(rs), "s"(m0s)
       : "memory", "m0");
 }
 
@@ -669,8 +671,10 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int c, int ks) {
 
 // PARTS = 1: plain bf16 product. PARTS = 2: the stage holds the bf16 "high" parts followed by
 // the bf16 "low" remainders of fp32 operands; the product keeps hi*hi + hi*lo + lo*hi (about
-// 16 significant bits per operand).
-template <class T, int PARTS>
+// 16 significant bits per operand). FIRST: the stage is the first of the product, so the
+// accumulators start from zero as the first MFMAs' inline-constant C operand (no register
+// clearing).
+template <class T, int PARTS, bool FIRST = false>
 __device__ __forceinline__ void mfma_stage(const uint16_t* stage,
                                            f32x16 (&acc)[T::XM][T::XN]) {
   const int am = wave_m<T>() * T::WTM, bn = wave_n<T>() * T::WTN;
@@ -687,7 +691,8 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* stage,
     for (int x = 0; x < T::XM; ++x)
 #pragma unroll
       for (int y = 0; y < T::XN; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a[x], b[y], (FIRST && ks == 0) ? f32x16{} : acc[x][y], 0, 0, 0);
     if constexpr (PARTS == 2) {
       bf16x8 al[T::XM], bl[T::XN];
 #pragma unroll
@@ -810,20 +815,32 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // (every share of stage kt is in LDS, and no wave still reads buffer (kt - 1) % NST), issue
 // stage kt + NST - 1 into that buffer, multiply stage kt. The lds area holds NST * T::STAGE
 // elements.
-template <class T, int NST = 3, class SA, class SB>
+// ZFIRST: the first stage's MFMAs start from an inline zero instead of cleared accumulator
+// registers (worth it for short K loops; a long loop keeps the simpler code).
+template <class T, int NST = 3, bool ZFIRST = false, class SA, class SB>
 __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64_t k_begin,
                                                int64_t k_end, uint16_t* lds,
                                                f32x16 (&acc)[T::XM][T::XN]) {
   static_assert(T::DMA, "tile in the DMA layout");
   static_assert(NST == 2 || NST == 3, "two or three LDS buffers");
   constexpr int NI = SA::NI + SB::NI;   // loads per wave and stage
+  if (k_end <= k_begin) {
 #pragma unroll
-  for (int x = 0; x < T::XM; ++x)
+    for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < T::XN; ++y)
+      for (int y = 0; y < T::XN; ++y)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
-  if (k_end <= k_begin) return;
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+    return;
+  }
+  if constexpr (!ZFIRST) {
+#pragma unroll
+    for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+      for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  }
   const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
   const uint32_t base = lds_addr(lds);   // byte addresses: stage s at base + 2 s STAGE
   sa.issue(k_begin, base);
@@ -849,7 +866,10 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
           sa.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt);
           sb.issue(k_begin + (int64_t)(kt + NST - 1) * T::BK, nxt + 2 * T::A_ELEMS);
         }
-        mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+        if (ZFIRST && buf == 0 && kt == 0)
+          mfma_stage<T, 1, true>(lds, acc);
+        else
+          mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
       }
     });
   }
@@ -870,7 +890,7 @@ __device__ __forceinline__ void gemm_kloop_dma(const SA& sa, const SB& sb, int64
 //   multiply stage j;
 //   convert the codes of stage j + 1 into the A tile of its buffer (free since stage j + 1 - NST
 //   was multiplied, before the previous barrier).
-template <class T, int NST, class SA, class SB>
+template <class T, int NST, bool ZFIRST = false, class SA, class SB>
 __device__ __forceinline__ void gemm_kloop_dma_cvt(const SA& sa, const SB& sb, int64_t k_begin,
                                                    int64_t k_end, uint16_t* lds, uint8_t* codes,
                                                    f32x16 (&acc)[T::XM][T::XN]) {
@@ -878,13 +898,23 @@ __device__ __forceinline__ void gemm_kloop_dma_cvt(const SA& sa, const SB& sb, i
   static_assert(NST == 2 || NST == 3, "two or three LDS buffers");
   constexpr int NB = SB::NI;   // B loads per wave and stage
   constexpr int NC = SA::NV;   // code and scale loads per wave and stage
+  if (k_end <= k_begin) {
 #pragma unroll
-  for (int x = 0; x < T::XM; ++x)
+    for (int x = 0; x < T::XM; ++x)
 #pragma unroll
-    for (int y = 0; y < T::XN; ++y)
+      for (int y = 0; y < T::XN; ++y)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
-  if (k_end <= k_begin) return;
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+    return;
+  }
+  if constexpr (!ZFIRST) {
+#pragma unroll
+    for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+      for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  }
   const int nk = (int)((k_end - k_begin + T::BK - 1) / T::BK);
   const uint32_t base = lds_addr(lds);   // byte addresses: stage s at base + 2 s STAGE
   const uint32_t cbase = lds_addr(reinterpret_cast<const uint16_t*>(codes));
@@ -925,7 +955,10 @@ __device__ __forceinline__ void gemm_kloop_dma_cvt(const SA& sa, const SB& sb, i
         barrier_nofence();
         if (j + NST - 1 < nk) issue_b(j + NST - 1);
         if (j + NST < nk) issue_c(j + NST);
-        mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
+        if (ZFIRST && buf == 0 && j == 0)
+          mfma_stage<T, 1, true>(lds, acc);
+        else
+          mfma_stage<T, 1>(lds + buf * T::STAGE, acc);
         if (j + 1 < nk) {
           constexpr int nb = (buf + 1) % NST;
           sa.convert(codes + nb * SA::AREA, lds + nb * T::STAGE);

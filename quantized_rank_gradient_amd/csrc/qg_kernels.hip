@@ -438,17 +438,20 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
   const uint32_t e0 = i * c.n + j16;
   const uint32_t win[4] = {wv.x, wv.y, wv.z, wv.w};
   float U[16], d[16], wf[16];
-  float sum = 0.0f;
+  // d = W + a + u (|W| <= 127, 0 <= u < 1) is finite exactly when a = U * inv is, so the run
+  // is tested once: the largest |a|, by the NaN-propagating maximum (v_maximum3_f32)
+  float amax = 0.0f;
   static_for<16>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     U[t] = mul_rn(L.alpha, S[t]);
     wf[t] = sbyte_to_f32<t & 3>(win[t >> 2]);
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
-    d[t] = __builtin_fmaf((float)bits, 1.0f / 65536.0f, add_rn(wf[t], mul_rn(U[t], inv)));
-    sum += d[t];   // not finite when any of the sixteen is not (or when they overflow a sum)
+    const float a = mul_rn(U[t], inv);
+    amax = t == 0 ? __builtin_fabsf(a) : __builtin_elementwise_maximum(amax, __builtin_fabsf(a));
+    d[t] = __builtin_fmaf((float)bits, 1.0f / 65536.0f, add_rn(wf[t], a));
   });
   uint32_t wout[4] = {0, 0, 0, 0};
-  if (__builtin_isfinite(sum)) {
+  if (__builtin_isfinite(amax)) {
     // clamp(floor(d), -127, 127): floor converted in one instruction, then an integer clamp
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -635,10 +638,10 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
     const DmaBf16K<T::BN, T::BK> sb(Nb, L.n, L.r, L.n, j0);
     if (PM != kPStaged && inl) {
       const BackCodes sa(L.Pq, L.Ps, L.r, L.m, i0);
-      gemm_kloop_dma_cvt<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, codes, acc);
+      gemm_kloop_dma_cvt<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, codes, acc);
     } else if (PM != kPInline) {
       const DmaBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
-      gemm_kloop_dma<T, BackLds<BASE>::NST>(sa, sb, 0, L.r, lds, acc);
+      gemm_kloop_dma<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, acc);
     }
   } else {
     StageBf16K<T::BN, T::BK, false> sb(Nb, L.n, L.r, L.r, L.n, j0);

@@ -117,5 +117,10 @@ struct LinArgs {
   int64_t T, m, n;
 };
 hipError_t launch_linear(const LinArgs& a, int which, hipStream_t s);
+// Shapes whose forward / data-gradient product stages the INT8 weight by LDS DMA: a row's
+// 32 codes of a K stage (forward) or a column tile's 128 codes of a row (data gradient) lie
+// in one 256-element scale group.
+constexpr bool lin_fwd_dma(int64_t n) { return n % 32 == 0; }
+constexpr bool lin_bwd_data_dma(int64_t n) { return n % 128 == 0; }
 
 }  // namespace qg

@@ -16,6 +16,8 @@
 
 namespace qg {
 
+constexpr int cmax_i_(int a, int b) { return a > b ? a : b; }
+
 // INT8 source [c][k] (row pitch ld codes = the K extent, ld % 8 == 0, c_end rows) with
 // group scales over the flat index -> K-contiguous bf16 LDS tile [c][k] (kc_off layout).
 // A chunk of 8 codes starting at a multiple of 8 lies inside one 256-element group.
@@ -67,6 +69,189 @@ struct StageInt8C {
     }
   }
 };
+
+// Dequantize 8 INT8 codes (two little-endian words) with their group scale: bf16(fl(q * s)).
+__device__ __forceinline__ uint4 dequant8_int8(uint2 w, float s) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = mul_rn((float)(int8_t)(w.x >> (8 * e)), s);
+    f[4 + e] = mul_rn((float)(int8_t)(w.y >> (8 * e)), s);
+  }
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------------------------------
+// The INT8 weight as the first MFMA operand, staged by LDS DMA and converted in LDS (the
+// machinery of the INT4 projection stagers): per K stage the codes of the tile's 128 weight
+// rows or columns and one group scale per tile row reach a code area by DMA; convert() then
+// writes the bf16 tile. The weight is the 128-edge of the tile and the tokens the 256-edge,
+// so each weight element is converted once per 256 tokens.
+// ---------------------------------------------------------------------------------------
+
+// W [o][i] read by rows (forward: tile rows o, K = i = n codes per row, n % 32 == 0 so that
+// a row's 32 codes of a stage lie in one group). K-contiguous tile [128][32] (kc_off).
+struct DmaInt8C {
+  static constexpr int W = 128, BK = 32;
+  static constexpr int ROWB = BK;                  // code bytes per tile row and stage
+  static constexpr int CODE_BYTES = W * ROWB;      // 4 KiB
+  static constexpr int AREA = CODE_BYTES + 4 * W;  // + the row scales
+  static constexpr int RPI = 1024 / ROWB;          // tile rows per 16-byte wave-level load
+  static constexpr int NI = W / (4 * RPI);         // code loads per wave and stage (one)
+  static constexpr int NV = NI + 1;
+  static_assert(NI * 4 * RPI == W, "a stage splits evenly over the four waves");
+  const int8_t* q;
+  v4i32 rsc;
+  uint32_t ld, c_end, c0;
+  uint32_t vo[NI];
+
+  __device__ DmaInt8C(const int8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_, int c0_)
+      : q(q_), ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0((uint32_t)c0_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsc = rsrc_words(sc_, (uint32_t)(((c_end_ * ld_ + kGroup - 1) / kGroup) * 4));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t rg = c0 + (wave * NI + i) * RPI + lane / (ROWB / 16);
+      vo[i] = rg < c_end ? rg * ld + 16 * (lane % (ROWB / 16)) : kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t area) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)k0_ < ld ? (uint32_t)k0_ : ld;
+    const v4i32 st = rsrc_words(q + k0, c_end * ld - k0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(st, vo[i], area + (wave * NI + i) * 1024);
+    if ((lane >> 5) == (wave & 1)) {   // tile rows 64 (w / 2) + lane
+      const uint32_t rg = c0 + 64 * (wave >> 1) + lane;
+      const uint32_t off = rg < c_end ? ((rg * ld + k0) >> 8) * 4 : kOOB;
+      dma4(rsc, off, area + CODE_BYTES + 256 * (wave >> 1));
+    }
+  }
+
+  // thread t: chunk t % 4 of tile rows t / 4 and t / 4 + 64
+  __device__ __forceinline__ void convert(const uint8_t* area, uint16_t* tile) const {
+    const int c = threadIdx.x % 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = threadIdx.x / 4 + 64 * h;
+      const uint2 w = *reinterpret_cast<const uint2*>(area + row * ROWB + 8 * c);
+      const float sc = *reinterpret_cast<const float*>(area + CODE_BYTES + 4 * row);
+      *reinterpret_cast<uint4*>(tile + kc_off(row, c)) = dequant8_int8(w, sc);
+    }
+  }
+};
+
+// W [o][i] read by columns (data gradient: tile rows are K = o, tile columns i0 .. i0 + 127;
+// n % 128 == 0, so that a row's 128 codes lie in one group). K-major tile [32][128]
+// (kmaj_slot layout).
+struct DmaInt8K {
+  static constexpr int W = 128, BK = 32;
+  static constexpr int ROWB = W;                   // code bytes per tile row
+  static constexpr int CODE_BYTES = BK * ROWB;     // 4 KiB
+  static constexpr int AREA = CODE_BYTES + 256;    // + the BK row scales
+  static constexpr int RPI = 1024 / ROWB;          // tile rows per 16-byte wave-level load
+  static constexpr int NI = BK / (4 * RPI);        // code loads per wave and stage (one)
+  static constexpr int NV = NI + 1;
+  static_assert(NI * 4 * RPI == BK, "a stage splits evenly over the four waves");
+  const int8_t* q;
+  v4i32 rsc;
+  uint32_t ld, k_end, c0;
+  uint32_t vo[NI];
+
+  __device__ DmaInt8K(const int8_t* q_, const float* sc_, int64_t ld_, int64_t rows,
+                      int64_t k_end_, int c0_)
+      : q(q_), ld((uint32_t)ld_), k_end((uint32_t)k_end_), c0((uint32_t)c0_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsc = rsrc_words(sc_, (uint32_t)(((rows * ld_ + kGroup - 1) / kGroup) * 4));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t row = (wave * NI + i) * RPI + lane / (ROWB / 16);
+      const uint32_t col = c0 + 16 * (lane % (ROWB / 16));
+      vo[i] = col < ld ? row * ld + col : kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t area) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)k0_ < k_end ? (uint32_t)k0_ : k_end;
+    const v4i32 st = rsrc_words(q + (size_t)k0 * ld, (k_end - k0) * ld);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(st, vo[i], area + (wave * NI + i) * 1024);
+    if (lane >= 8 * wave && lane < 8 * wave + 8) {   // tile rows 8 w .. 8 w + 7
+      const uint32_t k = k0 + lane;
+      const uint32_t off = k < k_end ? ((k * ld + c0) >> 8) * 4 : kOOB;
+      dma4(rsc, off, area + CODE_BYTES);
+    }
+  }
+
+  // thread t: chunk t % 16 of tile rows t / 16 and t / 16 + 16
+  __device__ __forceinline__ void convert(const uint8_t* area, uint16_t* tile) const {
+    const int c = threadIdx.x % 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = threadIdx.x / 16 + 16 * h;
+      const uint2 w = *reinterpret_cast<const uint2*>(area + row * ROWB + 8 * c);
+      const float sc = *reinterpret_cast<const float*>(area + CODE_BYTES + 4 * row);
+      *reinterpret_cast<uint4*>(tile + row * W + 8 * kmaj_slot<W>(row, c)) =
+          dequant8_int8(w, sc);
+    }
+  }
+};
+
+// Tiles of the DMA products: weight side 128 (M), tokens 256 (N, K-contiguous rows of the
+// activation). Forward: A = W rows (K-contiguous); data gradient: A = W^T (K-major).
+using LinFwdTileD = Tile<128, 256, 32, 2, 2, false, false, true>;
+using LinBwdDataTileD = Tile<128, 256, 32, 2, 2, true, false, true>;
+constexpr int kLinNst = 2;   // LDS ring depth of the DMA products (two workgroups per CU)
+
+// Writes the accumulator tile (rows: weight side, columns: tokens) transposed into out
+// (tokens x ld, row-major bf16): each wave rounds its 64 x 128 block to bf16 in LDS 32 rows
+// at a time, then stores 16-byte runs of one token's outputs. Positions past the matrix are
+// dropped by the buffer range.
+template <class T>
+__device__ __forceinline__ void store_bf16_transposed(uint16_t* out, int64_t tokens, int64_t ld,
+                                                      int64_t wcols, int i0, int j0,
+                                                      const f32x16 (&acc)[T::XM][T::XN],
+                                                      uint16_t* lds) {
+  constexpr int PI = 40;   // bf16 pitch of a token row of the staging block (32 + 8)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave_m<T>(), wn = wave_n<T>();
+  uint16_t* E = lds + wave * (T::WTN * PI);
+  const rsrc_t ro = make_rsrc(out, (uint32_t)(tokens * ld * 2));
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x) {
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int jl = 32 * y + (lane & 31);
+        const int il = 8 * qd + 4 * (lane >> 5);
+        *reinterpret_cast<uint2*>(E + jl * PI + il) =
+            make_uint2(pack_bf16x2(acc[x][y][4 * qd], acc[x][y][4 * qd + 1]),
+                       pack_bf16x2(acc[x][y][4 * qd + 2], acc[x][y][4 * qd + 3]));
+      }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < T::WTN * 4 / 64; ++c) {
+      const int q = c * 64 + lane;
+      const int jl = q / 4, ic = q % 4;
+      const uint32_t j = (uint32_t)(j0 + wn * T::WTN + jl);
+      const uint32_t i = (uint32_t)(i0 + wm * T::WTM + 32 * x + 8 * ic);
+      const uint4 v = *reinterpret_cast<const uint4*>(E + jl * PI + 8 * ic);
+      bstore128(ro, (j < (uint32_t)tokens && i < (uint32_t)wcols) ? (j * (uint32_t)ld + i) * 2
+                                                                   : kOOB, v);
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int lin_dma_lds_bytes() {
+  return cmax_i_(cmax_i_(kLinNst * LinFwdTileD::STAGE * 2 + kLinNst * DmaInt8C::AREA,
+                         kLinNst * LinBwdDataTileD::STAGE * 2 + kLinNst * DmaInt8K::AREA),
+                 4 * LinFwdTileD::WTN * 40 * 2);
+}
 
 using LinFwdTile = Tile<128, 256, 32, 2, 2, false, false>;
 using LinBwdDataTile = Tile<128, 256, 32, 2, 2, false, true>;
@@ -148,12 +333,50 @@ __global__ __launch_bounds__(kThreads, 2) void qg_lin_bwd_weight(LinArgs a) {
   store_bf16_tile<T>(a.out, a.m, a.n, i0, j0, acc);
 }
 
+// Forward by DMA (n % 32 == 0): the tile is Y^T (weight rows o x tokens t) = W~ X^T.
+__global__ __launch_bounds__(kThreads, 2) void qg_lin_fwd_dma(LinArgs a) {
+  using T = LinFwdTileD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[lin_dma_lds_bytes() / 2];
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + kLinNst * T::STAGE * 2;
+  const int local = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles_m = (int)((a.m + T::BM - 1) / T::BM);
+  const int i0 = (local % tiles_m) * T::BM, j0 = (local / tiles_m) * T::BN;
+  const DmaInt8C sa(a.Wq, a.Ws, a.n, a.m, i0);
+  const DmaBf16C<T::BN, T::BK> sb(a.act, a.n, a.T, j0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop_dma_cvt<T, kLinNst>(sa, sb, 0, a.n, lds, codes, acc);
+  store_bf16_transposed<T>(a.out, a.T, a.m, a.m, i0, j0, acc, lds);
+}
+
+// Data gradient by DMA (n % 128 == 0): the tile is dX^T (inputs i x tokens t) = W~^T dY^T.
+__global__ __launch_bounds__(kThreads, 2) void qg_lin_bwd_data_dma(LinArgs a) {
+  using T = LinBwdDataTileD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[lin_dma_lds_bytes() / 2];
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + kLinNst * T::STAGE * 2;
+  const int local = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles_m = (int)((a.n + T::BM - 1) / T::BM);
+  const int i0 = (local % tiles_m) * T::BM, j0 = (local / tiles_m) * T::BN;
+  const DmaInt8K sa(a.Wq, a.Ws, a.n, a.m, a.m, i0);
+  const DmaBf16C<T::BN, T::BK> sb(a.act, a.m, a.T, j0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop_dma_cvt<T, kLinNst>(sa, sb, 0, a.m, lds, codes, acc);
+  store_bf16_transposed<T>(a.out, a.T, a.n, a.n, i0, j0, acc, lds);
+}
+
 hipError_t launch_linear(const LinArgs& a, int which, hipStream_t s) {
   const int64_t tm = (which == kLinBwdWeight ? a.m : a.T);
   const int64_t tn = (which == kLinFwd ? a.m : a.n);
   const int grid = (int)(((tm + kLinTileM - 1) / kLinTileM) * ((tn + kLinTileN - 1) / kLinTileN));
-  if (which == kLinFwd)
+  // weight side 128 x tokens 256 tiles for the DMA forward and data-gradient kernels
+  const int64_t wside = which == kLinFwd ? a.m : a.n;
+  const int grid_dma =
+      (int)(((wside + kLinTileM - 1) / kLinTileM) * ((a.T + kLinTileN - 1) / kLinTileN));
+  if (which == kLinFwd && lin_fwd_dma(a.n))
+    hipLaunchKernelGGL(qg_lin_fwd_dma, dim3(grid_dma), dim3(kThreads), 0, s, a);
+  else if (which == kLinFwd)
     hipLaunchKernelGGL(qg_lin_fwd, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (which == kLinBwdData && lin_bwd_data_dma(a.n))
+    hipLaunchKernelGGL(qg_lin_bwd_data_dma, dim3(grid_dma), dim3(kThreads), 0, s, a);
   else if (which == kLinBwdData)
     hipLaunchKernelGGL(qg_lin_bwd_data, dim3(grid), dim3(kThreads), 0, s, a);
   else

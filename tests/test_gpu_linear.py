@@ -53,6 +53,9 @@ def make(T, m, n, seed):
     (136, 384, 1376),
     (8, 8, 8),           # a single partial tile, K of one chunk
     (77, 264, 40),
+    (300, 264, 1408),    # n % 128 == 0: both weight products stage the codes by LDS DMA,
+                         # with ragged token and weight-row tiles
+    (520, 136, 256),     # one full and one partial weight-side tile, three token tiles
 ])
 def test_int8_linear_products(T, m, n):
     from quantized_rank_gradient_amd import binding as B
