@@ -247,16 +247,24 @@ qg_status qgalore_quantize_proj_int8(const float *P, int64_t m, int64_t r, int8_
  *   Y = G Omega, Q = orth(Y); power_iters times: Z = orth(G^T Q), Q = orth(G Z);
  *   B = Q^T G; B B^T = V diag(sigma^2) V^T; P = Q V[:, :r],
  * with orth() a CholeskyQR2 in fp32, the products with G on bf16 MFMA (fp32 bases entered
- * as bf16 hi + lo parts), the small eigenproblem by Jacobi rotations in fp32. Each column of
+ * as bf16 hi + lo parts), the small eigenproblem by Jacobi rotations. Sketches up to k = 136
+ * keep the k x k work in one workgroup per step; wider ones (up to 2048) orthonormalize by
+ * block Gram-Schmidt with reorthogonalization (blocks of 128 columns, each by CholeskyQR2)
+ * and solve the eigenproblem by parallel block Jacobi across workgroups with C, V and the
+ * rotations held in fp64 (fp32 products of the k x k work on fp32 MFMA). Each column of
  * P is negated if needed so that its entry of largest magnitude (the first such row) is
  * positive. P is then quantized to INT4 (P_q, P_scale, as qgalore_quantize_proj).
+ *   G          bf16 m x n row-major, 16-byte aligned; when n is not a multiple of 8 the
+ *              library works on a zero-padded copy in the workspace.
  *   Omega      bf16 n x k row-major sketch (k = r + oversample), drawn by the caller
  *              (standard Gaussian entries); device pointer, 16-byte aligned.
- *   oversample multiple of 8, k <= 136, k <= min(m, n); n % 8 == 0; power_iters 0..8.
+ *   oversample multiple of 8, k <= 2048, k <= min(m, n); power_iters 0..8.
  *   P_out      optional fp32 m x r (16-byte aligned): P before quantization.
  *   sigma_out  optional fp32 r: the approximated leading singular values of G.
  * The result approximates the SVD's: its error grows with sigma_{k+1}/sigma_r of G and
- * shrinks with power_iters. Asynchronous on `stream`; allocates nothing. */
+ * shrinks with power_iters. Asynchronous on `stream` (the block Jacobi solver issues a fixed
+ * number of sweeps whose kernels return at once after convergence, so nothing is read back);
+ * allocates nothing. */
 size_t qgalore_refresh_workspace_bytes(int64_t m, int64_t n, int64_t r, int32_t oversample);
 qg_status qgalore_refresh_proj(const uint16_t *G, int64_t m, int64_t n, int64_t r,
                                const uint16_t *Omega, int32_t oversample, int32_t power_iters,

@@ -93,6 +93,8 @@ hipError_t launch_rf_reduce(const float* part, int split, int64_t M, int N, int 
 // Gram matrix of Y (M x k): partials over row chunks into part, their sum into out (k x k).
 hipError_t launch_rf_gram(const float* Y, int64_t M, int k, int64_t rows_per_chunk,
                           int chunks, float* part, float* out, hipStream_t s);
+// out[e] = sum over c < chunks of part[c * n + e], in order of c.
+hipError_t launch_rf_sum(const float* part, int chunks, int64_t n, float* out, hipStream_t s);
 hipError_t launch_rf_chol_inv(const float* W, int k, float shift_rel, float* Wt, hipStream_t s);
 hipError_t launch_rf_smallmul(const float* Y, const float* Wm, int64_t M, int k, int N,
                               float* out, uint16_t* outb, float* amax_v, hipStream_t s);
@@ -100,6 +102,55 @@ hipError_t launch_rf_jacobi(const float* C, int k, int r, int max_sweeps, float 
                             float* evals, float* Vr, float* sigma, int* sweeps, hipStream_t s);
 hipError_t launch_rf_signs(float* P, int64_t m, int r, const float* amax_v, float* sgn,
                            hipStream_t s);
+
+// ---- wide sketches (k above kRfMaxK): fp32 products on the matrix cores, block Jacobi ----
+constexpr int kRfMaxKWide = 2048;
+constexpr int kSgTile = 128;   // output tile of the fp32 products
+enum { kSgPartial = 0, kSgSubtract = 1, kSgStore = 2 };
+// out (M x N) op= A (M x K) B (K x N) in fp32. A is K-major (a_kmajor = 1: A[i][t] at
+// A + t*lda + i) or K-contiguous (A + i*lda + t); B is K-major (B + t*ldb + j). kSgPartial
+// writes the product over K slab s densely at out + s*M*N; kSgSubtract: out[i*ldo + j] -=
+// product; kSgStore: out[i*ldo + j] = product. The contiguous extent of each operand (K of a
+// K-contiguous A, M of a K-major A, N of B) and every leading dimension are multiples of 4,
+// kslab a multiple of 16, and the pointers 16-byte aligned.
+struct SGemm {
+  const float* A;
+  const float* B;
+  float* out;
+  int64_t M, N, K, lda, ldb, ldo, kslab;
+  int tiles_m, tiles_n, split, a_kmajor, mode;
+};
+hipError_t launch_rf_sgemm(const SGemm& g, hipStream_t s);
+// Qb (M x 2k bf16): hi parts of Qf (M x k fp32) in columns 0 .. k-1, lo parts in k .. 2k-1.
+hipError_t launch_rf_split(const float* Qf, int64_t M, int k, uint16_t* Qb, hipStream_t s);
+// Gp (m x n8 bf16) = G (m x n) padded with zero columns.
+hipError_t launch_rf_pad(const uint16_t* G, int64_t m, int64_t n, int64_t n8, uint16_t* Gp,
+                         hipStream_t s);
+// Per 64-row tile and column of P (m x r): the signed entry of largest magnitude.
+hipError_t launch_rf_colmax(const float* P, int64_t m, int r, float* amax_v, hipStream_t s);
+
+constexpr int kRfJacobiBlock = 32;   // indices per block of the block Jacobi solver
+// Blocks of the padded problem: ceil(k / 32) rounded up to an even count.
+constexpr int rf_bj_blocks(int k) {
+  return (k + 2 * kRfJacobiBlock - 1) / (2 * kRfJacobiBlock) * 2;
+}
+// Device buffers of the block Jacobi solver for K = 32 * rf_bj_blocks(k): C and V (fp64
+// K x K), J (fp64, K / 64 pieces of 64 x 64), jrot (K / 64), abs_tol (1), rot (max_sweeps),
+// rank_of (k).
+struct RfBj {
+  double* C;
+  double* V;
+  double* J;
+  int* jrot;
+  float* abs_tol;
+  int* rot;
+  int* rank_of;
+};
+// Eigen-decomposition of the symmetric C (k x k, k <= kRfMaxKWide) with the outputs of
+// launch_rf_jacobi.
+hipError_t launch_rf_block_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
+                                  const RfBj& w, float* evals, float* Vr, float* sigma,
+                                  int* sweeps, hipStream_t s);
 
 // ---- products of a linear layer with an INT8-stored weight (dequantized in the stager) ----
 constexpr int kLinTileM = 128;

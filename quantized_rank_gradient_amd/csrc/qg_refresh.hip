@@ -615,6 +615,12 @@ hipError_t launch_rf_gram(const float* Y, int64_t M, int k, int64_t rows_per_chu
   return hipGetLastError();
 }
 
+hipError_t launch_rf_sum(const float* part, int chunks, int64_t n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(qg_rf_sum, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, part, chunks, (int)n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rf_chol_inv(const float* W, int k, float shift_rel, float* Wt, hipStream_t s) {
   hipLaunchKernelGGL(qg_rf_chol_inv, dim3(1), dim3(kThreads), 0, s, W, k, shift_rel, Wt);
   return hipGetLastError();

@@ -1,0 +1,678 @@
+// Subspace refresh for wide sketches (k = r + oversample above what one workgroup holds):
+// the k x k work of the range finder spread over the whole chip.
+//
+//  * fp32 products (qg_rf_sgemm) on the matrix cores: v_mfma_f32_32x32x2_f32 multiplies fp32
+//    operands exactly and accumulates in fp32. They form the Gram matrices, the projections
+//    of block Gram-Schmidt and P = Q V.
+//  * orth() of a wide basis is block classical Gram-Schmidt with reorthogonalization (BCGS2:
+//    each block of columns has its projection on the finished blocks removed twice, which
+//    leaves it orthogonal to them to working accuracy as long as it is not numerically inside
+//    their span), then the block is orthonormalized by the one-workgroup CholeskyQR kernels.
+//  * The eigenproblem C = V diag(lambda) V^T is solved by parallel block Jacobi (Golub and Van
+//    Loan, Matrix Computations, Section 8.5 on the parallel ordering and block Jacobi): the
+//    indices are cut into blocks of 32 and padded to an even number of blocks; in each round
+//    of a round-robin tournament on the blocks, every pair of blocks forms a 64 x 64
+//    subproblem that one workgroup treats with one cyclic sweep of 2 x 2 rotations
+//    (qg_rf_bj_solve), and the product J of the round's rotations is applied to all of C and
+//    V at once (qg_rf_bj_apply: C <- J^T C J and V <- V J, 64 x 64 pieces on the matrix cores).
+//    A sweep is nb - 1 rounds; the kernels of later sweeps return at once after a sweep in
+//    which no subproblem rotated, so the whole solve is issued without reading anything back.
+#include "qg_gemm.hpp"
+#include "qg_kernels.hpp"
+
+namespace qg {
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// ==================================================================== fp32 products ===
+// A 128 x 128 output tile per workgroup of four waves (2 x 2, each 64 x 64: 2 x 2 blocks of
+// 32 x 32). K advances in stages of 16, both operands staged in LDS K-major ([k][i], pitch
+// kSgPitch: the two half-waves of a fragment read land in opposite halves of the banks); the
+// next stage's global loads are in flight while the current stage's products run.
+constexpr int kSgBM = 128;
+constexpr int kSgBK = 16;
+constexpr int kSgPitch = kSgBM + 32;
+constexpr int kSgStage = 2 * kSgBK * kSgPitch;   // floats per stage (A then B)
+static_assert(kSgBM == kSgTile, "host and device tiles agree");
+
+__device__ __forceinline__ float4 ld4(const float* p, bool ok) {
+  return ok ? gload(reinterpret_cast<const float4*>(p)) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// One stage of a K-major operand (rows k of length `cols`, contiguous): 16 rows x 128
+// columns, two float4 per thread.
+struct SgKmaj {
+  const float* base;
+  int64_t ld, cols;
+  int c0;
+  float4 v[2];
+  __device__ void load(int64_t k0, int64_t k_end) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t kr = k0 + (q >> 5);
+      const int64_t c = c0 + 4 * (q & 31);
+      v[u] = ld4(base + kr * ld + c, kr < k_end && c < cols);
+    }
+  }
+  __device__ void store(float* lds) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      *reinterpret_cast<float4*>(lds + (q >> 5) * kSgPitch + 4 * (q & 31)) = v[u];
+    }
+  }
+};
+
+// One stage of a K-contiguous operand (row i holds its K values contiguously): 128 rows x 16
+// K values, two float4 per thread, transposed into the K-major LDS layout.
+struct SgKcon {
+  const float* base;
+  int64_t ld, rows;
+  int r0;
+  float4 v[2];
+  __device__ void load(int64_t k0, int64_t k_end) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int64_t row = r0 + (q >> 2);
+      const int64_t kc = k0 + 4 * (q & 3);
+      v[u] = ld4(base + row * ld + kc, row < rows && kc < k_end);
+    }
+  }
+  __device__ void store(float* lds) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = threadIdx.x + kThreads * u;
+      const int row = q >> 2, kc = 4 * (q & 3);
+      lds[(kc + 0) * kSgPitch + row] = v[u].x;
+      lds[(kc + 1) * kSgPitch + row] = v[u].y;
+      lds[(kc + 2) * kSgPitch + row] = v[u].z;
+      lds[(kc + 3) * kSgPitch + row] = v[u].w;
+    }
+  }
+};
+
+template <class SA>
+__device__ __forceinline__ void sgemm_tile(const SGemm& g, SA& sa, int i0, int j0, int s,
+                                           float* lds) {
+  const int64_t k_begin = (int64_t)s * g.kslab;
+  const int64_t k_end = min<int64_t>(g.K, k_begin + g.kslab);
+  SgKmaj sb{g.B, g.ldb, g.N, j0};
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int am = (wave >> 1) * 64, bn = (wave & 1) * 64;
+  const int kh = lane >> 5, li = lane & 31;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  if (k_begin < k_end) {
+    sa.load(k_begin, k_end);
+    sb.load(k_begin, k_end);
+    sa.store(lds);
+    sb.store(lds + kSgBK * kSgPitch);
+    __syncthreads();
+    int it = 0;
+    for (int64_t k0 = k_begin; k0 < k_end; k0 += kSgBK, ++it) {
+      const float* As = lds + (it & 1) * kSgStage;
+      const float* Bs = As + kSgBK * kSgPitch;
+      const bool more = k0 + kSgBK < k_end;
+      if (more) {
+        sa.load(k0 + kSgBK, k_end);
+        sb.load(k0 + kSgBK, k_end);
+      }
+#pragma unroll
+      for (int kp = 0; kp < kSgBK / 2; ++kp) {
+        const int kr = (2 * kp + kh) * kSgPitch;
+        float a[2], b[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) a[x] = As[kr + am + 32 * x + li];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) b[y] = Bs[kr + bn + 32 * y + li];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f32(a[x], b[y], acc[x][y]);
+      }
+      if (more) {
+        float* nxt = lds + ((it + 1) & 1) * kSgStage;
+        sa.store(nxt);
+        sb.store(nxt + kSgBK * kSgPitch);
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int64_t j = j0 + bn + 32 * y + li;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + am + 32 * x + 8 * (v >> 2) + 4 * kh + (v & 3);
+        if (i >= g.M || j >= g.N) continue;
+        const float val = acc[x][y][v];
+        if (g.mode == kSgPartial) {
+          gstore(g.out + (int64_t)s * g.M * g.N + i * g.N + j, val);
+        } else if (g.mode == kSgSubtract) {
+          float* o = g.out + i * g.ldo + j;
+          gstore(o, gload(o) - val);
+        } else {
+          gstore(g.out + i * g.ldo + j, val);
+        }
+      }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void qg_rf_sgemm(SGemm g) {
+  __shared__ __attribute__((aligned(16))) float lds[2 * kSgStage];
+  const int local = xcd_remap(blockIdx.x, gridDim.x);
+  const int ti = local % g.tiles_m;
+  const int rest = local / g.tiles_m;
+  const int tj = rest % g.tiles_n;
+  const int s = rest / g.tiles_n;
+  const int i0 = ti * kSgBM, j0 = tj * kSgBM;
+  if (g.a_kmajor) {
+    SgKmaj sa{g.A, g.lda, g.M, i0};
+    sgemm_tile(g, sa, i0, j0, s, lds);
+  } else {
+    SgKcon sa{g.A, g.lda, g.M, i0};
+    sgemm_tile(g, sa, i0, j0, s, lds);
+  }
+}
+
+// ============================================================ basis format helpers ===
+// Qb (M x 2k bf16) = the hi parts bf16(x) of Qf (M x k) in columns 0 .. k-1 and the lo parts
+// bf16(x - hi) in k .. 2k-1.
+__global__ __launch_bounds__(kThreads) void qg_rf_split(const float* Qf, int64_t M, int k,
+                                                        uint16_t* Qb) {
+  const int64_t numel = M * k;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < numel; e += stride) {
+    const int64_t i = e / k;
+    const int j = (int)(e - i * k);
+    const float v = gload(Qf + e);
+    const uint16_t hi = to_bf16(v);
+    gstore(Qb + i * 2 * k + j, hi);
+    gstore(Qb + i * 2 * k + k + j, to_bf16(v - bf16_to_f32(hi)));
+  }
+}
+
+// Gp (m x n8) = G (m x n) with zero columns n .. n8-1, so that rows start on 16-byte bounds.
+__global__ __launch_bounds__(kThreads) void qg_rf_pad(const uint16_t* G, int64_t m, int64_t n,
+                                                      int64_t n8, uint16_t* Gp) {
+  const int64_t numel = m * n8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < numel; e += stride) {
+    const int64_t i = e / n8, j = e - i * n8;
+    gstore(Gp + e, j < n ? gload(G + i * n + j) : (uint16_t)0);
+  }
+}
+
+// Per 64-row tile and column of P (m x r): the entry of largest magnitude (signed; the first
+// such row on ties), the input of the column sign rule.
+__global__ __launch_bounds__(kThreads) void qg_rf_colmax(const float* P, int64_t m, int r,
+                                                         float* amax_v) {
+  const int c = blockIdx.y * kThreads + threadIdx.x;
+  if (c >= r) return;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int64_t i1 = min<int64_t>(m, i0 + 64);
+  float bv = gload(P + i0 * r + c);
+  for (int64_t i = i0 + 1; i < i1; ++i) {
+    const float v = gload(P + i * r + c);
+    if (fabsf(v) > fabsf(bv)) bv = v;
+  }
+  gstore(amax_v + (int64_t)blockIdx.x * r + c, bv);
+}
+
+// ================================================================ block Jacobi eigen ===
+// C, V and the block rotations J are held in fp64, so that the thousands of rotations a solve
+// applies leave V orthogonal and the eigenvalues unmoved to far below fp32 resolution. Inside
+// a subproblem the rotations are chosen on an fp32 copy (enough to decide them; any
+// orthogonal J serves Jacobi), while J itself is accumulated in fp64 from each rotation's
+// (c, s) renormalized in fp64.
+constexpr int kBjB = kRfJacobiBlock;   // indices per block
+constexpr int kBjS = 2 * kBjB;         // order of a subproblem (a pair of blocks)
+constexpr int kBjP = kBjS + 1;         // LDS pitch
+constexpr int kBjPairs = kBjS / 2;     // disjoint index pairs per inner round
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// The two blocks of pair w in round `round` of the round-robin tournament on nb blocks
+// (position 0 holds block 0, positions 1 .. nb-1 the others rotated by `round`; position w
+// meets position nb - 1 - w), smaller first.
+__device__ __forceinline__ void bj_pair(int nb, int round, int w, int& lo, int& hi) {
+  const int a = w == 0 ? 0 : 1 + (w - 1 + round) % (nb - 1);
+  const int b = 1 + (nb - 2 - w + round) % (nb - 1);
+  lo = min(a, b);
+  hi = max(a, b);
+}
+// Index of a subproblem's local index l (0 .. 63): the first block, then the second.
+__device__ __forceinline__ int bj_index(int lo, int hi, int l) {
+  return (l < kBjB ? lo : hi) * kBjB + (l & (kBjB - 1));
+}
+// A sweep is skipped when the previous one rotated nothing.
+__device__ __forceinline__ bool bj_converged(const int* rot, int sweep) {
+  return sweep > 0 && gload(rot + sweep - 1) == 0;
+}
+
+// Cj (K x K) = C (k x k) symmetrized from its upper triangle, zero outside k x k; Vj = I.
+__global__ __launch_bounds__(kThreads) void qg_rf_bj_init(const float* C, int k, int K,
+                                                          double* Cj, double* Vj) {
+  const int64_t numel = (int64_t)K * K;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < numel; e += stride) {
+    const int i = (int)(e / K), j = (int)(e - (int64_t)i * K);
+    const int lo = min(i, j), hi = max(i, j);
+    gstore(Cj + e, hi < k ? (double)gload(C + (int64_t)lo * k + hi) : 0.0);
+    gstore(Vj + e, i == j ? 1.0 : 0.0);
+  }
+}
+
+// abs_tol = 1e-7 * (largest diagonal entry of C), the level of fp32 rounding noise in the
+// entries of a positive semidefinite matrix; the rotation flags of all sweeps cleared.
+__global__ __launch_bounds__(kThreads) void qg_rf_bj_prep(const float* C, int k, float* abs_tol,
+                                                          int* rot, int max_sweeps) {
+  __shared__ float red[kThreads];
+  float mx = 0.0f;
+  for (int i = threadIdx.x; i < k; i += kThreads)
+    mx = fmaxf(mx, fabsf(gload(C + (int64_t)i * k + i)));
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + h]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) gstore(abs_tol, 1e-7f * red[0]);
+  for (int s = threadIdx.x; s < max_sweeps; s += kThreads) gstore(rot + s, 0);
+}
+
+// A rotation of the pair (p, q) is taken while |a_pq| exceeds both tol * sqrt(|a_pp a_qq|)
+// and abs_tol.
+__device__ __forceinline__ bool bj_needs(float app, float aqq, float apq, float tol,
+                                         float abs_tol) {
+  return fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
+}
+
+// One workgroup per pair of blocks: the 64 x 64 subproblem S of C (as fp32), one cyclic
+// sweep of 2 x 2 rotations on it (a round-robin over its 64 indices: 63 inner rounds of 32
+// disjoint rotations, S <- R^T S R, Q <- Q R from Q = I), then Q (fp64) goes to Jm[w] and
+// whether it differs from I to jrot[w]. Only the upper triangle of S is kept (entry (i, j) at
+// (min, max)), updated 2 x 2 block by 2 x 2 block: a block (w1, w2) holds rows p1, q1 of
+// pair w1 and columns p2, q2 of pair w2, and every stored entry lies in exactly one block
+// with w1 <= w2. A subproblem with no pair over the rotation level is left as it is.
+__global__ __launch_bounds__(kThreads) void qg_rf_bj_solve(const double* Cj, int K, int nb,
+                                                           int round, int sweep, float tol,
+                                                           const float* abs_tol_p, int* rot,
+                                                           double* Jm, int* jrot) {
+  if (bj_converged(rot, sweep)) return;
+  __shared__ float A[kBjS * kBjP];
+  __shared__ double Q[kBjS * kBjP];
+  __shared__ float cs_c[kBjPairs], cs_s[kBjPairs];
+  __shared__ double cd_c[kBjPairs], cd_s[kBjPairs];
+  __shared__ int pp[kBjPairs], pq[kBjPairs], go_[kBjPairs];
+  constexpr int kBlocks = kBjPairs * (kBjPairs + 1) / 2;
+  __shared__ uint16_t blk[kBlocks];
+  __shared__ int need;
+  int lo, hi;
+  bj_pair(nb, round, blockIdx.x, lo, hi);
+  for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+    const int i = e / kBjS, j = e % kBjS;
+    A[i * kBjP + j] = (float)gload(Cj + (int64_t)bj_index(lo, hi, i) * K + bj_index(lo, hi, j));
+    Q[i * kBjP + j] = i == j ? 1.0 : 0.0;
+  }
+  if ((int)threadIdx.x < kBjPairs) {
+    const int w1 = threadIdx.x;
+    const int first = w1 * kBjPairs - w1 * (w1 - 1) / 2;
+    for (int w2 = w1; w2 < kBjPairs; ++w2) blk[first + w2 - w1] = (uint16_t)((w1 << 8) | w2);
+  }
+  if (threadIdx.x == 0) need = 0;
+  const float abs_tol = gload(abs_tol_p);
+  __syncthreads();
+  // is any pair of the subproblem over the rotation level?
+  {
+    int mine = 0;
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+      const int i = e / kBjS, j = e % kBjS;
+      if (i < j && bj_needs(A[i * kBjP + i], A[j * kBjP + j], A[i * kBjP + j], tol, abs_tol))
+        mine = 1;
+    }
+    if (mine) need = 1;
+  }
+  __syncthreads();
+  const bool active = need != 0;
+  for (int rd = 0; active && rd < kBjS - 1; ++rd) {
+    if ((int)threadIdx.x < kBjPairs) {
+      const int u = threadIdx.x;
+      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (kBjS - 1);
+      const int b = 1 + (kBjS - 2 - u + rd) % (kBjS - 1);
+      const int p = min(a, b), q = max(a, b);
+      const float app = A[p * kBjP + p], aqq = A[q * kBjP + q], apq = A[p * kBjP + q];
+      float c = 1.0f, s = 0.0f;
+      double cd = 1.0, sd = 0.0;
+      const bool go = bj_needs(app, aqq, apq, tol, abs_tol);
+      if (go) {
+        // the symmetric 2 x 2 Schur rotation (Golub and Van Loan, Algorithm 8.5.1)
+        const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.0f * apq);
+        const float t = (tau >= 0.0f ? 1.0f : -1.0f) *
+                        __builtin_amdgcn_rcpf(fabsf(tau) + sqrtf(1.0f + tau * tau));
+        c = __builtin_amdgcn_rsqf(1.0f + t * t);
+        s = t * c;
+        // in fp64, (c, s) scaled to unit length: h = c^2 + s^2 is 1 to fp32 accuracy, and
+        // 1.5 - h / 2 is 1 / sqrt(h) up to (h - 1)^2
+        const double h = (double)c * c + (double)s * s;
+        const double g = 1.5 - 0.5 * h;
+        cd = c * g;
+        sd = s * g;
+      }
+      pp[u] = p;
+      pq[u] = q;
+      cs_c[u] = c;
+      cs_s[u] = s;
+      cd_c[u] = cd;
+      cd_s[u] = sd;
+      go_[u] = go ? 1 : 0;
+    }
+    __syncthreads();
+    constexpr int BPT = (kBlocks + kThreads - 1) / kThreads;
+    int o[BPT][4], wb[BPT];
+    float x[BPT][4];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int bi = threadIdx.x + u * kThreads;
+      wb[u] = -1;
+      if (bi < kBlocks) {
+        const int w1 = blk[bi] >> 8, w2 = blk[bi] & 0xFF;
+        if (go_[w1] | go_[w2]) {
+          wb[u] = blk[bi];
+          const int p1 = pp[w1], q1 = pq[w1], p2 = pp[w2], q2 = pq[w2];
+          o[u][0] = min(p1, p2) * kBjP + max(p1, p2);
+          o[u][1] = min(p1, q2) * kBjP + max(p1, q2);
+          o[u][2] = min(q1, p2) * kBjP + max(q1, p2);
+          o[u][3] = min(q1, q2) * kBjP + max(q1, q2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
+        }
+      }
+    }
+    constexpr int QPT = kBjPairs * kBjS / kThreads;
+    static_assert(QPT * kThreads == kBjPairs * kBjS, "rotation updates split evenly");
+    double qx[QPT], qy[QPT];
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int idx = threadIdx.x + u * kThreads;
+      const int w = idx / kBjS, row = idx % kBjS;
+      if (go_[w]) {
+        qx[u] = Q[row * kBjP + pp[w]];
+        qy[u] = Q[row * kBjP + pq[w]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      if (wb[u] < 0) continue;
+      const int w1 = wb[u] >> 8, w2 = wb[u] & 0xFF;
+      const float c1 = cs_c[w1], s1 = cs_s[w1], c2 = cs_c[w2], s2 = cs_s[w2];
+      const float a = x[u][0], bb = x[u][1], c = x[u][2], d = x[u][3];
+      const float ra = c1 * a - s1 * c, rb = c1 * bb - s1 * d;
+      const float rc = s1 * a + c1 * c, rd2 = s1 * bb + c1 * d;
+      A[o[u][0]] = c2 * ra - s2 * rb;
+      A[o[u][1]] = s2 * ra + c2 * rb;
+      if (w1 != w2) A[o[u][2]] = c2 * rc - s2 * rd2;
+      A[o[u][3]] = s2 * rc + c2 * rd2;
+    }
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int idx = threadIdx.x + u * kThreads;
+      const int w = idx / kBjS, row = idx % kBjS;
+      if (go_[w]) {
+        const double c = cd_c[w], sn = cd_s[w];
+        Q[row * kBjP + pp[w]] = c * qx[u] - sn * qy[u];
+        Q[row * kBjP + pq[w]] = sn * qx[u] + c * qy[u];
+      }
+    }
+    __syncthreads();
+  }
+  double* out = Jm + (int64_t)blockIdx.x * kBjS * kBjS;
+  for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads)
+    gstore(out + e, Q[(e / kBjS) * kBjP + e % kBjS]);
+  if (threadIdx.x == 0) {
+    gstore(jrot + blockIdx.x, active ? 1 : 0);
+    if (active) gstore(rot + sweep, 1);
+  }
+}
+
+// This wave's 32 x 32 block (rows wm*32, columns wn*32) of a 64 x 64 fp64 product
+// sum over t < 64 of A(i, t) B(t, j), as 2 x 2 tiles of 16 x 16 (v_mfma_f64_16x16x4_f64).
+// A and B are LDS matrices with pitch kBjP; A is read as stored ([i][t]) or transposed
+// (stored [t][i]).
+template <bool A_TRANSPOSED>
+__device__ __forceinline__ void bj_mul(const double* Am, const double* Bm, f64x4 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i0 = (wave >> 1) * 32, j0 = (wave & 1) * 32;
+  const int l16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int t = 0; t < kBjS; t += 4) {
+    double a[2], b[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int i = i0 + 16 * x + l16;
+      a[x] = A_TRANSPOSED ? Am[(t + kq) * kBjP + i] : Am[i * kBjP + t + kq];
+    }
+#pragma unroll
+    for (int y = 0; y < 2; ++y) b[y] = Bm[(t + kq) * kBjP + j0 + 16 * y + l16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f64(a[x], b[y], acc[x][y]);
+  }
+}
+// Output coordinates of element v of tile (x, y) for this lane: v_mfma_f64_16x16x4_f64 gives
+// lane l the entries (l / 16 + 4 v, l % 16) of its 16 x 16 tile.
+__device__ __forceinline__ int bj_row(int x, int v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave >> 1) * 32 + 16 * x + (lane >> 4) + 4 * v;
+}
+__device__ __forceinline__ int bj_col(int y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave & 1) * 32 + 16 * y + (lane & 15);
+}
+__device__ __forceinline__ void bj_put(double* X, const f64x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) X[bj_row(x, v) * kBjP + bj_col(y)] = acc[x][y][v];
+}
+
+// The round's rotations applied to C and V. Workgroups 0 .. nC-1 take the 64 x 64 pieces
+// (pairs w1 <= w2) of C: X = C[rows of w1][columns of w2], X' = J1^T X J2, written at
+// (w1, w2) and transposed at (w2, w1); a diagonal piece is symmetrized from its upper
+// triangle. The others take 64-row strips of V restricted to one pair's columns: V' = V J.
+// Pieces whose rotations are all the identity are left as they are.
+__global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* Vj, int K, int nb,
+                                                           int round, int sweep, const int* rot,
+                                                           const double* Jm, const int* jrot) {
+  if (bj_converged(rot, sweep)) return;
+  __shared__ double X[kBjS * kBjP];
+  __shared__ double J1[kBjS * kBjP];
+  __shared__ double J2[kBjS * kBjP];
+  const int P = nb / 2;
+  const int nC = P * (P + 1) / 2;
+  int bid = blockIdx.x;
+  auto load_j = [&](double* dst, int w) {
+    const double* src = Jm + (int64_t)w * kBjS * kBjS;
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads)
+      dst[(e / kBjS) * kBjP + e % kBjS] = gload(src + e);
+  };
+  f64x4 acc[2][2];
+  if (bid < nC) {
+    int w1 = 0;
+    while (bid >= P - w1) {
+      bid -= P - w1;
+      ++w1;
+    }
+    const int w2 = w1 + bid;
+    if (gload(jrot + w1) == 0 && gload(jrot + w2) == 0) return;
+    int lo1, hi1, lo2, hi2;
+    bj_pair(nb, round, w1, lo1, hi1);
+    bj_pair(nb, round, w2, lo2, hi2);
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+      const int i = e / kBjS, j = e % kBjS;
+      X[i * kBjP + j] = gload(Cj + (int64_t)bj_index(lo1, hi1, i) * K + bj_index(lo2, hi2, j));
+    }
+    load_j(J1, w1);
+    load_j(J2, w2);
+    __syncthreads();
+    bj_mul<true>(J1, X, acc);   // J1^T X
+    __syncthreads();
+    bj_put(X, acc);
+    __syncthreads();
+    bj_mul<false>(X, J2, acc);   // (J1^T X) J2
+    __syncthreads();
+    bj_put(X, acc);
+    __syncthreads();
+    const bool diag = w1 == w2;
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+      const int i = e / kBjS, j = e % kBjS;
+      const double v = diag ? X[min(i, j) * kBjP + max(i, j)] : X[i * kBjP + j];
+      gstore(Cj + (int64_t)bj_index(lo1, hi1, i) * K + bj_index(lo2, hi2, j), v);
+      if (!diag) {   // transposed piece, element (ti, tj) of X to (tj, ti): coalesced stores
+        const int ti = e % kBjS, tj = e / kBjS;
+        gstore(Cj + (int64_t)bj_index(lo2, hi2, tj) * K + bj_index(lo1, hi1, ti),
+               X[ti * kBjP + tj]);
+      }
+    }
+  } else {
+    bid -= nC;
+    const int w = bid % P, strip = bid / P;
+    if (gload(jrot + w) == 0) return;
+    int lo, hi;
+    bj_pair(nb, round, w, lo, hi);
+    const int64_t r0 = (int64_t)strip * kBjS;
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+      const int i = e / kBjS, j = e % kBjS;
+      X[i * kBjP + j] = gload(Vj + (r0 + i) * K + bj_index(lo, hi, j));
+    }
+    load_j(J1, w);
+    __syncthreads();
+    bj_mul<false>(X, J1, acc);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int j = bj_index(lo, hi, bj_col(y));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gstore(Vj + (r0 + bj_row(x, v)) * K + j, acc[x][y][v]);
+      }
+  }
+}
+
+// Eigenvalues (the diagonal of the converged C) ranked in descending order (ties by index),
+// over the k real indices; evals (k), sigma (the square roots of the r largest), the rank of
+// each index, and the number of sweeps run (those that rotated, plus the one that found
+// nothing left to rotate, at most max_sweeps).
+__global__ __launch_bounds__(1024) void qg_rf_bj_rank(const double* Cj, int K, int k, int r,
+                                                      const int* rot, int max_sweeps,
+                                                      float* evals, float* sigma, int* rank_of,
+                                                      int* sweeps_out) {
+  __shared__ double d[kRfMaxKWide];
+  for (int i = threadIdx.x; i < k; i += 1024) d[i] = gload(Cj + (int64_t)i * K + i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += 1024) {
+    const double li = d[i];
+    int rk = 0;
+    for (int j = 0; j < k; ++j) rk += (d[j] > li || (d[j] == li && j < i)) ? 1 : 0;
+    gstore(rank_of + i, rk);
+    gstore(evals + rk, (float)li);
+    if (sigma && rk < r) gstore(sigma + rk, (float)sqrt(fmax(li, 0.0)));
+  }
+  if (threadIdx.x == 0 && sweeps_out) {
+    int s = 0;
+    while (s < max_sweeps && gload(rot + s) != 0) ++s;
+    gstore(sweeps_out, min(s + 1, max_sweeps));
+  }
+}
+
+// Vr (k x r, fp32): the eigenvectors of the r largest eigenvalues, in rank order.
+__global__ __launch_bounds__(kThreads) void qg_rf_bj_gather(const double* Vj, int K, int k, int r,
+                                                            const int* rank_of, float* Vr) {
+  const int64_t numel = (int64_t)k * k;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < numel; e += stride) {
+    const int i = (int)(e / k), col = (int)(e - (int64_t)i * k);
+    const int rk = gload(rank_of + col);
+    if (rk < r) gstore(Vr + (int64_t)i * r + rk, (float)gload(Vj + (int64_t)i * K + col));
+  }
+}
+
+// ======================================================================= launchers ===
+namespace {
+unsigned grid_for(int64_t numel) {
+  const int64_t want = (numel + kThreads - 1) / kThreads;
+  return (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+}
+}  // namespace
+
+hipError_t launch_rf_sgemm(const SGemm& g, hipStream_t s) {
+  const int grid = g.tiles_m * g.tiles_n * g.split;
+  hipLaunchKernelGGL(qg_rf_sgemm, dim3(grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_rf_split(const float* Qf, int64_t M, int k, uint16_t* Qb, hipStream_t s) {
+  hipLaunchKernelGGL(qg_rf_split, dim3(grid_for(M * k)), dim3(kThreads), 0, s, Qf, M, k, Qb);
+  return hipGetLastError();
+}
+
+hipError_t launch_rf_pad(const uint16_t* G, int64_t m, int64_t n, int64_t n8, uint16_t* Gp,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(qg_rf_pad, dim3(grid_for(m * n8)), dim3(kThreads), 0, s, G, m, n, n8, Gp);
+  return hipGetLastError();
+}
+
+hipError_t launch_rf_colmax(const float* P, int64_t m, int r, float* amax_v, hipStream_t s) {
+  const dim3 grid((unsigned)((m + 63) / 64), (unsigned)((r + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(qg_rf_colmax, grid, dim3(kThreads), 0, s, P, m, r, amax_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_rf_block_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
+                                  const RfBj& w, float* evals, float* Vr, float* sigma,
+                                  int* sweeps, hipStream_t s) {
+  const int nb = rf_bj_blocks(k);
+  const int K = nb * kBjB;
+  const int P = nb / 2;
+  hipLaunchKernelGGL(qg_rf_bj_init, dim3(grid_for((int64_t)K * K)), dim3(kThreads), 0, s, C, k,
+                     K, w.C, w.V);
+  hipLaunchKernelGGL(qg_rf_bj_prep, dim3(1), dim3(kThreads), 0, s, C, k, w.abs_tol, w.rot,
+                     max_sweeps);
+  hipError_t e = hipGetLastError();
+  const int apply_grid = P * (P + 1) / 2 + (K / kBjS) * P;
+  for (int sweep = 0; sweep < max_sweeps && e == hipSuccess; ++sweep)
+    for (int round = 0; round < nb - 1 && e == hipSuccess; ++round) {
+      hipLaunchKernelGGL(qg_rf_bj_solve, dim3(P), dim3(kThreads), 0, s, w.C, K, nb, round, sweep,
+                         tol, w.abs_tol, w.rot, w.J, w.jrot);
+      hipLaunchKernelGGL(qg_rf_bj_apply, dim3(apply_grid), dim3(kThreads), 0, s, w.C, w.V, K, nb,
+                         round, sweep, w.rot, w.J, w.jrot);
+      e = hipGetLastError();
+    }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qg_rf_bj_rank, dim3(1), dim3(1024), 0, s, w.C, K, k, r, w.rot, max_sweeps,
+                     evals, sigma, w.rank_of, sweeps);
+  hipLaunchKernelGGL(qg_rf_bj_gather, dim3(grid_for((int64_t)k * k)), dim3(kThreads), 0, s, w.V,
+                     K, k, r, w.rank_of, Vr);
+  return hipGetLastError();
+}
+
+}  // namespace qg

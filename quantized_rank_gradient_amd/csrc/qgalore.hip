@@ -794,6 +794,8 @@ constexpr int kRfMaxSweeps = 20;         // Jacobi sweeps at most
 constexpr float kRfJacobiTol = 1e-6f;    // relative off-diagonal level that ends a sweep
 constexpr float kRfShift = 1e-6f;        // diagonal shift (x trace / k) of the first
                                          // CholeskyQR pass
+constexpr int64_t kRfBlockW = 128;       // columns per block of the wide orthonormalization
+constexpr int kRfWideSweeps = 16;        // block Jacobi sweeps at most
 
 struct RfGemmPlan {
   int split, tiles_m, tiles_n;
@@ -812,16 +814,53 @@ RfGemmPlan rf_gemm_plan(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// Split-K of an fp32 product (qg::SGemm): about 512 workgroups, K slabs of 4 stages or more.
+RfGemmPlan sg_plan(int64_t M, int64_t N, int64_t K, bool split_k) {
+  RfGemmPlan p;
+  p.tiles_m = (int)cdiv(M, qg::kSgTile);
+  p.tiles_n = (int)cdiv(N, qg::kSgTile);
+  const int64_t stages = cdiv(K, 16);
+  int64_t sp = 1;
+  if (split_k) {
+    sp = std::max<int64_t>(1, cdiv(512, (int64_t)p.tiles_m * p.tiles_n));
+    sp = std::max<int64_t>(1, std::min<int64_t>(sp, stages / 4));
+  }
+  p.kslab = cdiv(stages, sp) * 16;
+  p.split = (int)cdiv(K, p.kslab);
+  return p;
+}
+int64_t sg_part_elems(int64_t M, int64_t N, int64_t K) {
+  const RfGemmPlan p = sg_plan(M, N, K, true);
+  return p.split > 1 ? p.split * M * N : 0;
+}
+
+bool rf_wide(int64_t k) { return k > qg::kRfMaxK; }
+
 struct RfLayout {
   int64_t off_part, off_y, off_t, off_qf, off_qb, off_gpart, off_gram, off_wt, off_eval, off_vr,
-      off_info, off_amax, off_sgn, off_p, bytes;
+      off_info, off_amax, off_sgn, off_p, off_gpad, off_spart, off_s, off_bjc, off_bjv, off_bjj,
+      off_bjjrot, off_bjtol, off_bjrot, off_bjrank, bytes;
 };
 RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
   const int64_t mx = std::max(m, n);
+  const bool wide = rf_wide(k);
   int64_t part = 0;
   const int64_t shapes[3][3] = {{m, k, n}, {m, 2 * k, n}, {n, 2 * k, m}};
   for (const auto& sh : shapes)
     part = std::max<int64_t>(part, rf_gemm_plan(sh[0], sh[1], sh[2]).split * sh[0] * sh[1]);
+  // partial sums of the split fp32 products: the Gram matrices of column blocks and of the
+  // whole basis, and the projections on the finished blocks
+  int64_t spart = 0;
+  if (wide) {
+    for (const int64_t M : {m, n}) {
+      spart = std::max(spart, sg_part_elems(kRfBlockW, kRfBlockW, M));
+      for (int64_t c0 = kRfBlockW; c0 < k; c0 += kRfBlockW)
+        spart = std::max(spart, sg_part_elems(c0, kRfBlockW, M));
+    }
+    spart = std::max(spart, sg_part_elems(k, k, n));
+  }
+  const int nbj = qg::rf_bj_blocks((int)k);
+  const int64_t KJ = (int64_t)nbj * qg::kRfJacobiBlock;
   RfLayout L;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -834,7 +873,7 @@ RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
   L.off_t = take(mx * k * 4);
   L.off_qf = take(mx * k * 4);
   L.off_qb = take(mx * 2 * k * 2);
-  L.off_gpart = take(cdiv(mx, kRfGramChunk) * k * k * 4);
+  L.off_gpart = take(wide ? 0 : cdiv(mx, kRfGramChunk) * k * k * 4);
   L.off_gram = take(k * k * 4);
   L.off_wt = take(k * k * 4);
   L.off_eval = take(k * 4);
@@ -843,6 +882,16 @@ RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
   L.off_amax = take(cdiv(m, 64) * r * 4);
   L.off_sgn = take(r * 4);
   L.off_p = take(m * r * 4);
+  L.off_gpad = take(n % 8 ? m * round_up(n, 8) * 2 : 0);
+  L.off_spart = take(spart * 4);
+  L.off_s = take(wide ? k * kRfBlockW * 4 : 0);
+  L.off_bjc = take(wide ? KJ * KJ * 8 : 0);
+  L.off_bjv = take(wide ? KJ * KJ * 8 : 0);
+  L.off_bjj = take(wide ? (KJ / 64) * 64 * 64 * 8 : 0);
+  L.off_bjjrot = take((KJ / 64) * 4);
+  L.off_bjtol = take(4);
+  L.off_bjrot = take(kRfWideSweeps * 4);
+  L.off_bjrank = take(k * 4);
   L.bytes = off;
   return L;
 }
@@ -852,9 +901,9 @@ qg_status check_refresh(int64_t m, int64_t n, int64_t r, int32_t oversample, int
   if (oversample < 0 || oversample % 8 != 0 || iters < 0 || iters > kRfMaxPowerIters)
     return QG_ERR_ARG;
   const int64_t k = r + oversample;
-  if (k > qg::kRfMaxK || k > m || k > n || n % 8 != 0) return QG_ERR_SHAPE;
+  if (k > qg::kRfMaxKWide || k > m || k > n) return QG_ERR_SHAPE;
   // fp32 slabs of up to max(m, n) x 2k (and G itself) stay below 2^29 elements
-  if (m * n > kMaxElems || std::max(m, n) * 2 * k > kMaxElems) return QG_ERR_SHAPE;
+  if (m * round_up(n, 8) > kMaxElems || std::max(m, n) * 2 * k > kMaxElems) return QG_ERR_SHAPE;
   return QG_OK;
 }
 }  // namespace
@@ -884,36 +933,49 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + lay.off_part);
-  float* Y = reinterpret_cast<float*>(ws + lay.off_y);
-  float* T = reinterpret_cast<float*>(ws + lay.off_t);
-  float* Qf = reinterpret_cast<float*>(ws + lay.off_qf);
+  auto at = [&](int64_t off) { return reinterpret_cast<float*>(ws + off); };
+  float* part = at(lay.off_part);
+  float* Y = at(lay.off_y);
+  float* T = at(lay.off_t);
+  float* Qf = at(lay.off_qf);
   uint16_t* Qb = reinterpret_cast<uint16_t*>(ws + lay.off_qb);
-  float* gpart = reinterpret_cast<float*>(ws + lay.off_gpart);
-  float* gram = reinterpret_cast<float*>(ws + lay.off_gram);
-  float* Wt = reinterpret_cast<float*>(ws + lay.off_wt);
-  float* evals = reinterpret_cast<float*>(ws + lay.off_eval);
-  float* Vr = reinterpret_cast<float*>(ws + lay.off_vr);
+  float* gpart = at(lay.off_gpart);
+  float* gram = at(lay.off_gram);
+  float* Wt = at(lay.off_wt);
+  float* evals = at(lay.off_eval);
+  float* Vr = at(lay.off_vr);
   int* info = reinterpret_cast<int*>(ws + lay.off_info);
-  float* amax = reinterpret_cast<float*>(ws + lay.off_amax);
-  float* sgn = reinterpret_cast<float*>(ws + lay.off_sgn);
-  float* P = P_out ? P_out : reinterpret_cast<float*>(ws + lay.off_p);
+  float* amax = at(lay.off_amax);
+  float* sgn = at(lay.off_sgn);
+  float* P = P_out ? P_out : at(lay.off_p);
+  float* spart = at(lay.off_spart);
+  float* S = at(lay.off_s);
   const int kk = (int)k;
+  const bool wide = rf_wide(k);
 
   hipError_t e = hipSuccess;
+  // G with rows on 16-byte bounds: a zero-padded copy when n is not a multiple of 8 (the
+  // padding columns add nothing to the products)
+  const uint16_t* Ga = G;
+  const int64_t lda = round_up(n, 8);
+  if (n % 8) {
+    uint16_t* Gp = reinterpret_cast<uint16_t*>(ws + lay.off_gpad);
+    e = qg::launch_rf_pad(G, m, n, lda, Gp, s);
+    Ga = Gp;
+  }
   // out (M x k) = A B, with A = G (M = m, K = n) or G^T (M = n, K = m) and B a basis of
   // width nb (k for the sketch, 2k for the hi/lo parts of an fp32 basis)
   auto product = [&](bool transposed, const uint16_t* B, int64_t nb, float* out) {
     const int64_t M = transposed ? n : m, K = transposed ? m : n;
     const RfGemmPlan pl = rf_gemm_plan(M, nb, K);
     qg::RfGemm g;
-    g.A = G;
+    g.A = Ga;
     g.B = B;
     g.part = part;
     g.M = M;
     g.N = nb;
     g.K = K;
-    g.lda = n;
+    g.lda = lda;
     g.ldb = nb;
     g.kslab = pl.kslab;
     g.tiles_m = pl.tiles_m;
@@ -922,6 +984,32 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
     g.a_kmajor = transposed ? 1 : 0;
     if (e == hipSuccess) e = qg::launch_rf_gemm(g, s);
     if (e == hipSuccess) e = qg::launch_rf_reduce(part, pl.split, M, (int)nb, kk, out, s);
+  };
+  // fp32 product out op= A B (qg::SGemm). With mode kSgPartial the K slabs' partial products
+  // are summed, in order, into the dense out (M x N).
+  auto sgemm = [&](const float* A, int64_t lda_, bool a_kmajor, const float* B, int64_t ldb,
+                   int64_t M, int64_t N, int64_t K, float* out, int64_t ldo, int mode) {
+    const bool reduce = mode == qg::kSgPartial;
+    const RfGemmPlan pl = sg_plan(M, N, K, reduce);
+    qg::SGemm g;
+    g.A = A;
+    g.B = B;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = lda_;
+    g.ldb = ldb;
+    g.kslab = pl.kslab;
+    g.tiles_m = pl.tiles_m;
+    g.tiles_n = pl.tiles_n;
+    g.split = pl.split;
+    g.a_kmajor = a_kmajor ? 1 : 0;
+    const bool summed = reduce && pl.split > 1;
+    g.out = summed ? spart : out;
+    g.ldo = ldo;
+    g.mode = reduce && !summed ? qg::kSgStore : mode;
+    if (e == hipSuccess) e = qg::launch_rf_sgemm(g, s);
+    if (summed && e == hipSuccess) e = qg::launch_rf_sum(spart, pl.split, M * N, out, s);
   };
   auto gram_of = [&](const float* X, int64_t M) {
     if (e == hipSuccess)
@@ -940,20 +1028,67 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
       in = out;
     }
   };
+  // The same for a wide basis, block by block of kRfBlockW columns: the block's projection on
+  // the finished blocks removed twice (S = Q^T X, X -= Q S), then CholeskyQR with `passes`
+  // passes on the block alone.
+  auto orth_wide = [&](int64_t M, int passes) {
+    for (int64_t c0 = 0; c0 < k; c0 += kRfBlockW) {
+      const int64_t bw = std::min<int64_t>(kRfBlockW, k - c0);
+      float* X = Y + c0;
+      if (c0 > 0)
+        for (int rep = 0; rep < 2; ++rep) {
+          sgemm(Qf, k, true, X, k, c0, bw, M, S, bw, qg::kSgPartial);
+          sgemm(Qf, k, false, S, bw, M, bw, c0, X, k, qg::kSgSubtract);
+        }
+      const float* in = X;
+      for (int pass = 0; pass < passes; ++pass) {
+        float* out = (pass == passes - 1 ? Qf : T) + c0;
+        sgemm(in, k, true, in, k, bw, bw, M, gram, bw, qg::kSgPartial);
+        if (e == hipSuccess)
+          e = qg::launch_rf_chol_inv(gram, (int)bw, pass == 0 ? kRfShift : 0.0f, Wt, s);
+        sgemm(in, k, false, Wt, bw, M, bw, bw, out, k, qg::kSgStore);
+        in = out;
+      }
+    }
+    if (e == hipSuccess) e = qg::launch_rf_split(Qf, M, kk, Qb, s);
+  };
+  auto orthogonalize = [&](int64_t M, int passes) {
+    if (wide)
+      orth_wide(M, passes);
+    else
+      orth(M, passes);
+  };
   product(false, Omega, k, Y);            // Y = G Omega
-  orth(m, power_iters == 0 ? 2 : 1);
+  orthogonalize(m, power_iters == 0 ? 2 : 1);
   for (int it = 0; it < power_iters; ++it) {
     product(true, Qb, 2 * k, Y);          // G^T Q
-    orth(n, 1);
+    orthogonalize(n, 1);
     product(false, Qb, 2 * k, Y);         // G Z
-    orth(m, it == power_iters - 1 ? 2 : 1);
+    orthogonalize(m, it == power_iters - 1 ? 2 : 1);
   }
   product(true, Qb, 2 * k, Y);            // B^T = G^T Q  (n x k)
-  gram_of(Y, n);                          // B B^T
-  if (e == hipSuccess)
-    e = qg::launch_rf_jacobi(gram, kk, (int)r, kRfMaxSweeps, kRfJacobiTol, evals, Vr,
-                             sigma_out, info, s);
-  if (e == hipSuccess) e = qg::launch_rf_smallmul(Qf, Vr, m, kk, (int)r, P, nullptr, amax, s);
+  if (!wide) {
+    gram_of(Y, n);                        // B B^T
+    if (e == hipSuccess)
+      e = qg::launch_rf_jacobi(gram, kk, (int)r, kRfMaxSweeps, kRfJacobiTol, evals, Vr,
+                               sigma_out, info, s);
+    if (e == hipSuccess) e = qg::launch_rf_smallmul(Qf, Vr, m, kk, (int)r, P, nullptr, amax, s);
+  } else {
+    sgemm(Y, k, true, Y, k, k, k, n, gram, k, qg::kSgPartial);   // B B^T
+    qg::RfBj bj;
+    bj.C = reinterpret_cast<double*>(ws + lay.off_bjc);
+    bj.V = reinterpret_cast<double*>(ws + lay.off_bjv);
+    bj.J = reinterpret_cast<double*>(ws + lay.off_bjj);
+    bj.jrot = reinterpret_cast<int*>(ws + lay.off_bjjrot);
+    bj.abs_tol = at(lay.off_bjtol);
+    bj.rot = reinterpret_cast<int*>(ws + lay.off_bjrot);
+    bj.rank_of = reinterpret_cast<int*>(ws + lay.off_bjrank);
+    if (e == hipSuccess)
+      e = qg::launch_rf_block_jacobi(gram, kk, (int)r, kRfWideSweeps, kRfJacobiTol, bj, evals,
+                                     Vr, sigma_out, info, s);
+    sgemm(Qf, k, false, Vr, r, m, r, k, P, r, qg::kSgStore);      // P = Q V_r
+    if (e == hipSuccess) e = qg::launch_rf_colmax(P, m, (int)r, amax, s);
+  }
   if (e == hipSuccess) e = qg::launch_rf_signs(P, m, (int)r, amax, sgn, s);
   if (e == hipSuccess) e = qg::launch_quantize_int4(P, m * r, P_q, P_scale, s);
   return e == hipSuccess ? QG_OK : hip_fail(e, "subspace refresh kernels");

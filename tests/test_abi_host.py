@@ -111,6 +111,24 @@ def test_workspace_size_query():
     assert B.lib().qgalore_cossim_workspace_bytes(100, 128) == 0
 
 
+def test_refresh_workspace_size_query():
+    """Sketch widths up to 2048 (the wide path above 136: fp64 block Jacobi buffers and the
+    fp32 products' partial sums) and gradients whose column count is not a multiple of 8 (a
+    zero-padded copy of G)."""
+    q = B.lib().qgalore_refresh_workspace_bytes
+    small = q(4096, 4096, 128, 8)
+    assert small >= 3 * 4096 * 136 * 4
+    wide = q(4096, 4096, 1024, 8)
+    K = 1088   # 1032 padded to an even number of 32-index blocks
+    assert wide >= 3 * 4096 * 1032 * 4 + 2 * K * K * 8
+    ragged = q(2048, 5461, 512, 8)
+    assert ragged >= 2048 * 5464 * 2 + 3 * 5461 * 520 * 4
+    assert q(4096, 4096, 2040, 8) > 0          # k = 2048, the widest sketch
+    assert q(4096, 4096, 2048, 8) == 0         # k = 2056
+    assert q(1000, 1040, 1024, 24) == 0        # k = 1048 > m
+    assert q(512, 389, 32, 8) > 0              # n % 8 != 0 is accepted
+
+
 def test_other_entry_points_validate_first():
     L = B.lib()
     p = B.Proj(m=256, r=32, q=0x10000, scale=0x10000)

@@ -11,6 +11,11 @@ The library's result approximates the SVD. Its error has two parts:
     eps moves an individual singular vector by about eps / (relative gap of sigma_i^2 to its
     neighbours); the spectra below keep that gap at 1.5% or more at r = 32 and 0.8% at
     r = 128, so vectors move by well under 1e-3.
+Sketches wider than 136 (ranks 192 to 1024 here) take the library's wide path (block
+Gram-Schmidt and a block Jacobi eigensolver in fp64); the spectra below keep the relative gap
+of sigma_i^2 at 0.2% or more up to rank 1024, so vectors still move by well under 1e-3.
+Gradients whose column count is not a multiple of 8 are padded with zero columns inside the
+library, which leaves every product unchanged.
 Checks: each column within 2e-3 of the oracle's (max abs entry difference, unit vectors),
 the subspace (1 - the smallest singular value of P*^T P below 1e-5), orthonormality, the
 singular values (relative 1e-4 of sigma_1), and the INT4 codes equal to the oracle's
@@ -76,6 +81,29 @@ def check(bits, r, P, sig, Pq, Ps, col_tol=2e-3):
 def test_refresh_matches_svd(m, n, r, k):
     bits = spectrum_gradient(m, n, r, k - r + 24, seed=m + n + r)
     check(bits, r, *gpu_refresh(bits, r, k))
+
+
+@pytest.mark.parametrize("m,n,r,k", [
+    (600, 400, 192, 200),     # the narrowest wide sketch: 7 blocks of 32 padded to 8
+    (1376, 520, 256, 264),    # 3 blocks of 128 columns in the Gram-Schmidt, the last of 8
+    (512, 389, 32, 40),       # n % 8 != 0 on the one-workgroup path
+    (700, 333, 200, 208),     # n % 8 != 0 on the wide path, k close to n
+])
+def test_refresh_matches_svd_wide_and_ragged(m, n, r, k):
+    bits = spectrum_gradient(m, n, r, k - r + 24, seed=m + n + r)
+    check(bits, r, *gpu_refresh(bits, r, k))
+
+
+def test_refresh_1b_down_shape_rank_512():
+    """2048 x 5461 (the 1B down projection, 5461 columns), rank 512, k = 520."""
+    bits = spectrum_gradient(2048, 5461, 512, 32, seed=17)
+    check(bits, 512, *gpu_refresh(bits, 512, 520))
+
+
+def test_refresh_7b_rank_1024():
+    """4096 x 4096 (the 7B attention projections), rank 1024, k = 1032."""
+    bits = spectrum_gradient(4096, 4096, 1024, 32, seed=19)
+    check(bits, 1024, *gpu_refresh(bits, 1024, 1032))
 
 
 def test_refresh_7b_gate_shape():
