@@ -317,7 +317,8 @@ def measured_traffic(config_key, kernel):
 def refresh_ms(torch, B, WL, cfg, reps=10):
     """Time of one projection refresh per distinct 7B shape at rank cfg.r: the library's
     (qgalore_refresh_proj, INT4 output included) against the same randomized range finder
-    in torch (plus the library's INT4 quantization), on a drifting-workload gradient."""
+    in torch (plus the library's INT4 quantization), on a drifting-workload gradient whose
+    leading subspace has the refresh's rank."""
     out = {}
     dev = torch.device("cuda:0")
     seen = set()
@@ -574,6 +575,9 @@ def main():
                          "weight gradients) on the 7B layer shapes")
     ap.add_argument("--refresh-only", action="store_true",
                     help="instead: time one projection refresh per 7B shape (library vs torch)")
+    ap.add_argument("--refresh-ranks", default="128",
+                    help="with --refresh-only: the ranks timed (comma-separated; 8 extra "
+                         "sketch columns each)")
     ap.add_argument("--tokens", type=int, default=8192,
                     help="with --linear: tokens per batch (batch x sequence length)")
     ap.add_argument("--refresh", default="library", choices=("library", "torch"),
@@ -655,9 +659,13 @@ def main():
         return
     if args.refresh_only:
         scfg = WL.CONFIGS["schedule7b"]
-        print(json.dumps({"metric": "projection refresh time (rank 128, 8 extra columns, 2 power "
+        ranks = [int(x) for x in args.refresh_ranks.split(",")]
+        print(json.dumps({"metric": "projection refresh time (8 extra columns, 2 power "
                                     "iterations): library vs torch range finder",
-                          "unit": "ms", "shapes": refresh_ms(torch, B, WL, scfg)}), flush=True)
+                          "unit": "ms",
+                          "ranks": {str(r): refresh_ms(torch, B, WL,
+                                                       dataclasses.replace(scfg, r=r))
+                                    for r in ranks}}), flush=True)
         return
 
     cfg = WL.CONFIGS[args.config]

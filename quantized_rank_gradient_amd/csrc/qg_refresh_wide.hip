@@ -300,59 +300,108 @@ __device__ __forceinline__ bool bj_needs(float app, float aqq, float apq, float 
   return fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
 }
 
-// One workgroup per pair of blocks: the 64 x 64 subproblem S of C (as fp32), one cyclic
-// sweep of 2 x 2 rotations on it (a round-robin over its 64 indices: 63 inner rounds of 32
-// disjoint rotations, S <- R^T S R, Q <- Q R from Q = I), then Q (fp64) goes to Jm[w] and
-// whether it differs from I to jrot[w]. Only the upper triangle of S is kept (entry (i, j) at
-// (min, max)), updated 2 x 2 block by 2 x 2 block: a block (w1, w2) holds rows p1, q1 of
-// pair w1 and columns p2, q2 of pair w2, and every stored entry lies in exactly one block
-// with w1 <= w2. A subproblem with no pair over the rotation level is left as it is.
-__global__ __launch_bounds__(kThreads) void qg_rf_bj_solve(const double* Cj, int K, int nb,
-                                                           int round, int sweep, float tol,
-                                                           const float* abs_tol_p, int* rot,
-                                                           double* Jm, int* jrot) {
+constexpr int kBjSolveThreads = 512;
+constexpr int kBjFullRounds = kBjS - 1;   // inner rounds over all pairs of a subproblem
+constexpr int kBjCrossRounds = kBjB;      // inner rounds over the pairs across its two blocks
+
+// One workgroup per pair of blocks: the 64 x 64 subproblem S of C (as fp32), one sweep of
+// 2 x 2 rotations on it, S <- R^T S R and Q <- Q R from Q = I; then Q (fp64) goes to Jm[w]
+// and whether it differs from I to jrot[w].
+//
+// In the first round of an outer sweep every block is in exactly one subproblem, and the
+// sweep there covers all 2016 index pairs of the subproblem (63 inner rounds of a round-robin
+// on its 64 indices). In the other rounds it covers only the 1024 pairs across the two blocks
+// (32 inner rounds: index i of the first block with index (i + t) mod 32 of the second), since
+// the pairs inside a block were treated in the first round: every index pair of C is thus
+// rotated once per outer sweep, as in cyclic Jacobi.
+//
+// Only the upper triangle of S is kept (entry (i, j) at (min, max)), updated 2 x 2 block by
+// 2 x 2 block: block (u1, u2), u1 <= u2, holds rows p1, q1 of pair slot u1 and columns p2, q2
+// of slot u2, and every stored entry lies in exactly one such block. Each thread keeps the
+// same blocks, and the same pair slot of Q with four of its rows, in every inner round; the
+// pairs of each inner round come from a table. A round is the rotation parameters of the 32
+// slots, a barrier, the updates (all reads issued before any write), and a barrier. A
+// subproblem with no pair over the rotation level is left as it is.
+__global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
+    const double* Cj, int K, int nb, int round, int sweep, float tol, const float* abs_tol_p,
+    int* rot, double* Jm, int* jrot) {
   if (bj_converged(rot, sweep)) return;
+  constexpr int NT = kBjSolveThreads;
   __shared__ float A[kBjS * kBjP];
   __shared__ double Q[kBjS * kBjP];
-  __shared__ float cs_c[kBjPairs], cs_s[kBjPairs];
-  __shared__ double cd_c[kBjPairs], cd_s[kBjPairs];
-  __shared__ int pp[kBjPairs], pq[kBjPairs], go_[kBjPairs];
-  constexpr int kBlocks = kBjPairs * (kBjPairs + 1) / 2;
-  __shared__ uint16_t blk[kBlocks];
+  __shared__ float4 cs[kBjPairs];     // c, s (fp32), rotate flag
+  __shared__ double2 csd[kBjPairs];   // c, s (fp64, unit length)
+  __shared__ uint16_t pt[kBjFullRounds * kBjPairs];   // pairs of each inner round: p | q << 8
   __shared__ int need;
+  const bool full = round == 0;
+  const int rounds = full ? kBjFullRounds : kBjCrossRounds;
   int lo, hi;
   bj_pair(nb, round, blockIdx.x, lo, hi);
-  for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+  for (int e = threadIdx.x; e < kBjS * kBjS; e += NT) {
     const int i = e / kBjS, j = e % kBjS;
     A[i * kBjP + j] = (float)gload(Cj + (int64_t)bj_index(lo, hi, i) * K + bj_index(lo, hi, j));
     Q[i * kBjP + j] = i == j ? 1.0 : 0.0;
   }
-  if ((int)threadIdx.x < kBjPairs) {
-    const int w1 = threadIdx.x;
-    const int first = w1 * kBjPairs - w1 * (w1 - 1) / 2;
-    for (int w2 = w1; w2 < kBjPairs; ++w2) blk[first + w2 - w1] = (uint16_t)((w1 << 8) | w2);
+  for (int e = threadIdx.x; e < rounds * kBjPairs; e += NT) {
+    const int rd = e / kBjPairs, u = e % kBjPairs;
+    int p, q;
+    if (full) {   // positions u and 63 - u of the round-robin on 64 indices
+      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (kBjS - 1);
+      const int b = 1 + (kBjS - 2 - u + rd) % (kBjS - 1);
+      p = min(a, b);
+      q = max(a, b);
+    } else {
+      p = u;
+      q = kBjB + ((u + rd) & (kBjB - 1));
+    }
+    pt[e] = (uint16_t)(p | (q << 8));
   }
   if (threadIdx.x == 0) need = 0;
   const float abs_tol = gload(abs_tol_p);
   __syncthreads();
-  // is any pair of the subproblem over the rotation level?
   {
     int mine = 0;
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
+    for (int e = threadIdx.x; e < kBjS * kBjS; e += NT) {
       const int i = e / kBjS, j = e % kBjS;
-      if (i < j && bj_needs(A[i * kBjP + i], A[j * kBjP + j], A[i * kBjP + j], tol, abs_tol))
+      const bool considered = full ? i < j : (i < kBjB && j >= kBjB);
+      if (considered &&
+          bj_needs(A[i * kBjP + i], A[j * kBjP + j], A[i * kBjP + j], tol, abs_tol))
         mine = 1;
     }
     if (mine) need = 1;
   }
   __syncthreads();
   const bool active = need != 0;
-  for (int rd = 0; active && rd < kBjS - 1; ++rd) {
+  // this thread's 2 x 2 blocks (slot pairs u1 <= u2, by number)
+  constexpr int kBlocks = kBjPairs * (kBjPairs + 1) / 2;
+  constexpr int BPT = (kBlocks + NT - 1) / NT;
+  int bu1[BPT], bu2[BPT];
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    int bi = threadIdx.x + u * NT, w1 = 0;
+    if (bi >= kBlocks) {
+      bu1[u] = -1;
+      bu2[u] = -1;
+      continue;
+    }
+    while (bi >= kBjPairs - w1) {
+      bi -= kBjPairs - w1;
+      ++w1;
+    }
+    bu1[u] = w1;
+    bu2[u] = w1 + bi;
+  }
+  // and its slot of Q with four rows
+  constexpr int QR = kBjPairs * kBjS / NT;
+  static_assert(QR * NT == kBjPairs * kBjS && kBjS % QR == 0, "Q rows split evenly");
+  const int qw = threadIdx.x / (kBjS / QR);
+  const int qrow = (threadIdx.x % (kBjS / QR)) * QR;
+  for (int rd = 0; active && rd < rounds; ++rd) {
+    const uint16_t* prd = pt + rd * kBjPairs;
     if ((int)threadIdx.x < kBjPairs) {
       const int u = threadIdx.x;
-      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (kBjS - 1);
-      const int b = 1 + (kBjS - 2 - u + rd) % (kBjS - 1);
-      const int p = min(a, b), q = max(a, b);
+      const int pq = prd[u];
+      const int p = pq & 0xFF, q = pq >> 8;
       const float app = A[p * kBjP + p], aqq = A[q * kBjP + q], apq = A[p * kBjP + q];
       float c = 1.0f, s = 0.0f;
       double cd = 1.0, sd = 0.0;
@@ -371,75 +420,61 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_solve(const double* Cj, int
         cd = c * g;
         sd = s * g;
       }
-      pp[u] = p;
-      pq[u] = q;
-      cs_c[u] = c;
-      cs_s[u] = s;
-      cd_c[u] = cd;
-      cd_s[u] = sd;
-      go_[u] = go ? 1 : 0;
+      cs[u] = make_float4(c, s, go ? 1.0f : 0.0f, 0.0f);
+      csd[u] = make_double2(cd, sd);
     }
     __syncthreads();
-    constexpr int BPT = (kBlocks + kThreads - 1) / kThreads;
-    int o[BPT][4], wb[BPT];
+    // reads: rotation parameters and old entries of this thread's blocks and Q rows
+    float4 r1[BPT], r2[BPT];
     float x[BPT][4];
+    int o[BPT][4];
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      const int bi = threadIdx.x + u * kThreads;
-      wb[u] = -1;
-      if (bi < kBlocks) {
-        const int w1 = blk[bi] >> 8, w2 = blk[bi] & 0xFF;
-        if (go_[w1] | go_[w2]) {
-          wb[u] = blk[bi];
-          const int p1 = pp[w1], q1 = pq[w1], p2 = pp[w2], q2 = pq[w2];
-          o[u][0] = min(p1, p2) * kBjP + max(p1, p2);
-          o[u][1] = min(p1, q2) * kBjP + max(p1, q2);
-          o[u][2] = min(q1, p2) * kBjP + max(q1, p2);
-          o[u][3] = min(q1, q2) * kBjP + max(q1, q2);
+      if (bu1[u] < 0) continue;
+      const int pq1 = prd[bu1[u]], pq2 = prd[bu2[u]];
+      const int p1 = pq1 & 0xFF, q1 = pq1 >> 8, p2 = pq2 & 0xFF, q2 = pq2 >> 8;
+      o[u][0] = min(p1, p2) * kBjP + max(p1, p2);
+      o[u][1] = min(p1, q2) * kBjP + max(p1, q2);
+      o[u][2] = min(q1, p2) * kBjP + max(q1, p2);
+      o[u][3] = min(q1, q2) * kBjP + max(q1, q2);
+      r1[u] = cs[bu1[u]];
+      r2[u] = cs[bu2[u]];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
-        }
-      }
+      for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
     }
-    constexpr int QPT = kBjPairs * kBjS / kThreads;
-    static_assert(QPT * kThreads == kBjPairs * kBjS, "rotation updates split evenly");
-    double qx[QPT], qy[QPT];
+    const int qpq = prd[qw];
+    const int qp = qrow * kBjP + (qpq & 0xFF), qq = qrow * kBjP + (qpq >> 8);
+    const double2 qcs = csd[qw];
+    double qx[QR], qy[QR];
 #pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int idx = threadIdx.x + u * kThreads;
-      const int w = idx / kBjS, row = idx % kBjS;
-      if (go_[w]) {
-        qx[u] = Q[row * kBjP + pp[w]];
-        qy[u] = Q[row * kBjP + pq[w]];
-      }
+    for (int v = 0; v < QR; ++v) {
+      qx[v] = Q[qp + v * kBjP];
+      qy[v] = Q[qq + v * kBjP];
     }
+    // writes: only blocks and rows touched by a rotation change
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      if (wb[u] < 0) continue;
-      const int w1 = wb[u] >> 8, w2 = wb[u] & 0xFF;
-      const float c1 = cs_c[w1], s1 = cs_s[w1], c2 = cs_c[w2], s2 = cs_s[w2];
+      if (bu1[u] < 0 || (r1[u].z == 0.0f && r2[u].z == 0.0f)) continue;
+      const float c1 = r1[u].x, s1 = r1[u].y, c2 = r2[u].x, s2 = r2[u].y;
       const float a = x[u][0], bb = x[u][1], c = x[u][2], d = x[u][3];
       const float ra = c1 * a - s1 * c, rb = c1 * bb - s1 * d;
       const float rc = s1 * a + c1 * c, rd2 = s1 * bb + c1 * d;
       A[o[u][0]] = c2 * ra - s2 * rb;
       A[o[u][1]] = s2 * ra + c2 * rb;
-      if (w1 != w2) A[o[u][2]] = c2 * rc - s2 * rd2;
+      if (bu1[u] != bu2[u]) A[o[u][2]] = c2 * rc - s2 * rd2;
       A[o[u][3]] = s2 * rc + c2 * rd2;
     }
+    if (cs[qw].z != 0.0f) {
 #pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int idx = threadIdx.x + u * kThreads;
-      const int w = idx / kBjS, row = idx % kBjS;
-      if (go_[w]) {
-        const double c = cd_c[w], sn = cd_s[w];
-        Q[row * kBjP + pp[w]] = c * qx[u] - sn * qy[u];
-        Q[row * kBjP + pq[w]] = sn * qx[u] + c * qy[u];
+      for (int v = 0; v < QR; ++v) {
+        Q[qp + v * kBjP] = qcs.x * qx[v] - qcs.y * qy[v];
+        Q[qq + v * kBjP] = qcs.y * qx[v] + qcs.x * qy[v];
       }
     }
     __syncthreads();
   }
   double* out = Jm + (int64_t)blockIdx.x * kBjS * kBjS;
-  for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads)
+  for (int e = threadIdx.x; e < kBjS * kBjS; e += NT)
     gstore(out + e, Q[(e / kBjS) * kBjP + e % kBjS]);
   if (threadIdx.x == 0) {
     gstore(jrot + blockIdx.x, active ? 1 : 0);
@@ -661,8 +696,8 @@ hipError_t launch_rf_block_jacobi(const float* C, int k, int r, int max_sweeps, 
   const int apply_grid = P * (P + 1) / 2 + (K / kBjS) * P;
   for (int sweep = 0; sweep < max_sweeps && e == hipSuccess; ++sweep)
     for (int round = 0; round < nb - 1 && e == hipSuccess; ++round) {
-      hipLaunchKernelGGL(qg_rf_bj_solve, dim3(P), dim3(kThreads), 0, s, w.C, K, nb, round, sweep,
-                         tol, w.abs_tol, w.rot, w.J, w.jrot);
+      hipLaunchKernelGGL(qg_rf_bj_solve, dim3(P), dim3(kBjSolveThreads), 0, s, w.C, K, nb, round,
+                         sweep, tol, w.abs_tol, w.rot, w.J, w.jrot);
       hipLaunchKernelGGL(qg_rf_bj_apply, dim3(apply_grid), dim3(kThreads), 0, s, w.C, w.V, K, nb,
                          round, sweep, w.rot, w.J, w.jrot);
       e = hipGetLastError();
