@@ -247,11 +247,11 @@ qg_status qgalore_quantize_proj_int8(const float *P, int64_t m, int64_t r, int8_
  *   Y = G Omega, Q = orth(Y); power_iters times: Z = orth(G^T Q), Q = orth(G Z);
  *   B = Q^T G; B B^T = V diag(sigma^2) V^T; P = Q V[:, :r],
  * with orth() a CholeskyQR2 in fp32, the products with G on bf16 MFMA (fp32 bases entered
- * as bf16 hi + lo parts), the small eigenproblem by Jacobi rotations. Sketches up to k = 136
- * keep the k x k work in one workgroup per step; wider ones (up to 2048) orthonormalize by
- * block Gram-Schmidt with reorthogonalization (blocks of 128 columns, each by CholeskyQR2)
- * and solve the eigenproblem by parallel block Jacobi across workgroups with C, V and the
- * rotations held in fp64 (fp32 products of the k x k work on fp32 MFMA). Each column of
+ * as bf16 hi + lo parts), and the eigenproblem of B B^T by parallel block Jacobi across
+ * workgroups (blocks of 32 indices, 64 x 64 subproblems, C, V and the rotations held in
+ * fp64). Sketches up to k = 136 orthonormalize with the k x k work in one workgroup per
+ * step; wider ones (up to 2048) by block Gram-Schmidt with reorthogonalization (blocks of
+ * 128 columns, each by CholeskyQR2, the k x k products on fp32 MFMA). Each column of
  * P is negated if needed so that its entry of largest magnitude (the first such row) is
  * positive. P is then quantized to INT4 (P_q, P_scale, as qgalore_quantize_proj).
  *   G          bf16 m x n row-major, 16-byte aligned; when n is not a multiple of 8 the

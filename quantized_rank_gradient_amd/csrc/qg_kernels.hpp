@@ -98,8 +98,6 @@ hipError_t launch_rf_sum(const float* part, int chunks, int64_t n, float* out, h
 hipError_t launch_rf_chol_inv(const float* W, int k, float shift_rel, float* Wt, hipStream_t s);
 hipError_t launch_rf_smallmul(const float* Y, const float* Wm, int64_t M, int k, int N,
                               float* out, uint16_t* outb, float* amax_v, hipStream_t s);
-hipError_t launch_rf_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
-                            float* evals, float* Vr, float* sigma, int* sweeps, hipStream_t s);
 hipError_t launch_rf_signs(float* P, int64_t m, int r, const float* amax_v, float* sgn,
                            hipStream_t s);
 
@@ -129,14 +127,16 @@ hipError_t launch_rf_pad(const uint16_t* G, int64_t m, int64_t n, int64_t n8, ui
 // Per 64-row tile and column of P (m x r): the signed entry of largest magnitude.
 hipError_t launch_rf_colmax(const float* P, int64_t m, int r, float* amax_v, hipStream_t s);
 
-constexpr int kRfJacobiBlock = 32;   // indices per block of the block Jacobi solver
-// Blocks of the padded problem: ceil(k / 32) rounded up to an even count.
-constexpr int rf_bj_blocks(int k) {
-  return (k + 2 * kRfJacobiBlock - 1) / (2 * kRfJacobiBlock) * 2;
-}
-// Device buffers of the block Jacobi solver for K = 32 * rf_bj_blocks(k): C and V (fp64
-// K x K), J (fp64, K / 64 pieces of 64 x 64), jrot (K / 64), abs_tol (1), rot (max_sweeps),
-// rank_of (k).
+// Indices per block of the block Jacobi solver (subproblems of twice that order): 16 or 32.
+// Blocks of 32 halve the rounds of a sweep, whose fixed cost (two dependent launches) dominates
+// the per-round time of either size at the sketch widths measured (136 to 1032).
+constexpr int kRfJacobiBlockSwitch = 0;   // sketch width from which blocks of 32 are used
+constexpr int rf_bj_block(int k) { return k >= kRfJacobiBlockSwitch ? 32 : 16; }
+// Blocks of the padded problem: ceil(k / B) rounded up to an even count.
+constexpr int rf_bj_blocks(int k, int B) { return (k + 2 * B - 1) / (2 * B) * 2; }
+// Device buffers of the block Jacobi solver for K = B * rf_bj_blocks(k, B), B = rf_bj_block(k):
+// C and V (fp64 K x K), J (fp64, K / 2B pieces of 2B x 2B), jrot (K / 2B), abs_tol (1), rot
+// (max_sweeps), rank_of (k).
 struct RfBj {
   double* C;
   double* V;
@@ -146,8 +146,10 @@ struct RfBj {
   int* rot;
   int* rank_of;
 };
-// Eigen-decomposition of the symmetric C (k x k, k <= kRfMaxKWide) with the outputs of
-// launch_rf_jacobi.
+// Eigen-decomposition of the symmetric C (k x k, k <= kRfMaxKWide): the eigenvalues in
+// descending order (ties by index) to evals (k), the eigenvectors of the r largest to the
+// columns of Vr (k x r, fp32), the square roots of the r largest to sigma (when given), the
+// number of sweeps run to sweeps.
 hipError_t launch_rf_block_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
                                   const RfBj& w, float* evals, float* Vr, float* sigma,
                                   int* sweeps, hipStream_t s);

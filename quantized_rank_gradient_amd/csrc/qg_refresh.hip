@@ -7,7 +7,7 @@
 //
 //   Y = G Omega (m x k, k = r + oversample, Omega supplied by the caller), Q = orth(Y)
 //   q times:  Z = orth(G^T Q),  Q = orth(G Z)
-//   B^T = G^T Q (n x k);  C = B B^T (k x k);  C = V diag(lambda) V^T (Jacobi)
+//   B^T = G^T Q (n x k);  C = B B^T (k x k);  C = V diag(lambda) V^T (block Jacobi)
 //   P = Q V[:, leading r], each column's sign fixed so that its largest |entry| is positive,
 //   then INT4 group quantization (qg_quantize_int4).
 //
@@ -17,8 +17,10 @@
 // products with G run on bf16 MFMA with fp32 accumulation: G is bf16 already and each fp32
 // basis enters as two bf16 parts, hi = bf16(x) and lo = bf16(x - hi), side by side as 2k
 // columns whose products are added back together (about 16 significant bits per basis
-// entry, so that directions far below the leading singular value stay resolved). The k x k
-// work runs in fp32 in one workgroup, and P = Q V in fp32. Sizes: k <= kRfMaxK.
+// entry, so that directions far below the leading singular value stay resolved). Up to
+// k = kRfMaxK the orthonormalization's k x k work runs in fp32 in one workgroup per step and
+// P = Q V in fp32 here; wider sketches, and the eigenproblem at every width, are in
+// qg_refresh_wide.hip.
 #include "qg_gemm.hpp"
 #include "qg_kernels.hpp"
 
@@ -398,192 +400,6 @@ __global__ __launch_bounds__(kThreads) void qg_rf_flip(float* P, int64_t numel, 
   }
 }
 
-// =================================================================== Jacobi eigen ===
-// One workgroup: C (k x k symmetric, k even) diagonalized by cyclic Jacobi rotations
-// (Golub and Van Loan, Matrix Computations, Section 8.5: the 2 x 2 symmetric Schur
-// decomposition and the parallel ordering). In each of the k - 1 rounds of a sweep the k/2
-// disjoint index pairs of a round-robin tournament are rotated together: C <- J^T C J and
-// V <- V J, with J the product of the round's plane rotations. C' = J^T C J is formed 2 x 2
-// block by 2 x 2 block (rows of one pair, columns of another), each block from its own old
-// entries, so a round needs one pass; C stays symmetric, so only its upper triangle is kept
-// and only blocks on or above the block diagonal are computed. A pair is rotated while
-// |c_pq| exceeds both tol * sqrt(|c_pp c_qq|) and 1e-7 * trace(C) (the level of fp32
-// rounding noise in the entries); a sweep without rotations ends the iteration. The
-// eigenvalues are ranked in descending order (ties by index); the eigenvectors of the r
-// largest go to the columns of Vr (k x r), the eigenvalues to evals (k, descending) and,
-// when sigma is given, the square roots of the r largest to sigma.
-constexpr int kRfJacobiThreads = 1024;
-constexpr int kRfJacobiPitch = kRfMaxK + 1;
-
-__global__ __launch_bounds__(kRfJacobiThreads) void qg_rf_jacobi(
-    const float* Cm, int k, int r, int max_sweeps, float tol, float* evals, float* Vr,
-    float* sigma, int* sweeps_out) {
-  constexpr int PT = kRfJacobiPitch;
-  constexpr int NW = kRfJacobiThreads / 64;
-  __shared__ float A[kRfMaxK * PT];
-  __shared__ float V[kRfMaxK * PT];
-  __shared__ float cs_c[kRfMaxK / 2], cs_s[kRfMaxK / 2];
-  __shared__ int pp[kRfMaxK / 2], pq[kRfMaxK / 2], rot[kRfMaxK / 2];
-  __shared__ int rotated;
-  __shared__ int rank_of[kRfMaxK];
-  __shared__ float abs_tol_sh;
-  // the 2 x 2 blocks (w1, w2), w1 <= w2, of a round as one list (w1 in the high byte)
-  constexpr int kMaxBlocks = (kRfMaxK / 2) * (kRfMaxK / 2 + 1) / 2;
-  __shared__ uint16_t blk[kMaxBlocks];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = wave; i < k; i += NW)
-    for (int j = lane; j < k; j += 64) {
-      A[i * PT + j] = gload(Cm + i * k + j);
-      V[i * PT + j] = i == j ? 1.0f : 0.0f;
-    }
-  const int half = k / 2;
-  const int nblocks = half * (half + 1) / 2;
-  if ((int)threadIdx.x < half) {
-    const int w1 = threadIdx.x;
-    const int first = w1 * half - w1 * (w1 - 1) / 2;   // blocks of rows before w1
-    for (int w2 = w1; w2 < half; ++w2) blk[first + w2 - w1] = (uint16_t)((w1 << 8) | w2);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float tr = 0.0f;
-    for (int i = 0; i < k; ++i) tr += fabsf(A[i * PT + i]);
-    abs_tol_sh = 1e-7f * tr;
-  }
-  __syncthreads();
-  const float abs_tol = abs_tol_sh;
-  int sweeps = 0;
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    if (threadIdx.x == 0) rotated = 0;
-    __syncthreads();
-    for (int round = 0; round < k - 1; ++round) {
-      // round-robin pairing: position 0 holds index 0, positions 1 .. k-1 the others
-      // rotated by `round`; position w meets position k - 1 - w
-      if (threadIdx.x < half) {
-        const int w = threadIdx.x;
-        const int a = w == 0 ? 0 : 1 + (w - 1 + round) % (k - 1);
-        const int b = 1 + (k - 2 - w + round) % (k - 1);
-        const int p = min(a, b), qq = max(a, b);
-        const float app = A[p * PT + p], aqq = A[qq * PT + qq], apq = A[p * PT + qq];
-        float c = 1.0f, s = 0.0f;
-        const bool go = fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
-        if (go) {
-          // the rotation's own rounding only needs c^2 + s^2 = 1 to fp32 accuracy
-          const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.0f * apq);
-          const float t = (tau >= 0.0f ? 1.0f : -1.0f) *
-                          __builtin_amdgcn_rcpf(fabsf(tau) + sqrtf(1.0f + tau * tau));
-          c = __builtin_amdgcn_rsqf(1.0f + t * t);
-          s = t * c;
-          rotated = 1;
-        }
-        pp[w] = p;
-        pq[w] = qq;
-        cs_c[w] = c;
-        cs_s[w] = s;
-        rot[w] = go ? 1 : 0;
-      }
-      __syncthreads();
-      // blocks (w1, w2), w1 <= w2: rows p1, q1 rotated by pair w1, columns p2, q2 by w2.
-      // Only the upper triangle of C is stored (entry (i, j) at (min, max)); every stored
-      // entry belongs to exactly one block with w1 <= w2. Blocks of two unrotated pairs and
-      // V columns of an unrotated pair do not change. Each thread takes every 1024th block
-      // of the list and every 1024th (pair, row) update of V, and reads all of its entries
-      // before it writes any, so the LDS latencies overlap.
-      constexpr int BPT = (kMaxBlocks + kRfJacobiThreads - 1) / kRfJacobiThreads;
-      constexpr int VPT = (kRfMaxK / 2 * kRfMaxK + kRfJacobiThreads - 1) / kRfJacobiThreads;
-      {
-        int o[BPT][4], wb[BPT];   // entry offsets; block code (w1 << 8 | w2), -1 when idle
-        float x[BPT][4];
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-          const int b = threadIdx.x + u * kRfJacobiThreads;
-          wb[u] = -1;
-          if (b < nblocks) {
-            const int w1 = blk[b] >> 8, w2 = blk[b] & 0xFF;
-            if (rot[w1] | rot[w2]) {
-              wb[u] = blk[b];
-              const int p1 = pp[w1], q1 = pq[w1], p2 = pp[w2], q2 = pq[w2];
-              o[u][0] = min(p1, p2) * PT + max(p1, p2);
-              o[u][1] = min(p1, q2) * PT + max(p1, q2);
-              o[u][2] = min(q1, p2) * PT + max(q1, p2);
-              o[u][3] = min(q1, q2) * PT + max(q1, q2);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-          if (wb[u] < 0) continue;
-          const int w1 = wb[u] >> 8, w2 = wb[u] & 0xFF;
-          const float c1 = cs_c[w1], s1 = cs_s[w1], c2 = cs_c[w2], s2 = cs_s[w2];
-          const float a = x[u][0], bb = x[u][1], c = x[u][2], d = x[u][3];
-          const float ra = c1 * a - s1 * c, rb = c1 * bb - s1 * d;   // J1^T rows
-          const float rc = s1 * a + c1 * c, rd = s1 * bb + c1 * d;
-          A[o[u][0]] = c2 * ra - s2 * rb;   // * J2 columns
-          A[o[u][1]] = s2 * ra + c2 * rb;
-          if (w1 != w2) A[o[u][2]] = c2 * rc - s2 * rd;   // on the diagonal o2 == o1
-          A[o[u][3]] = s2 * rc + c2 * rd;
-        }
-        // V: the (pair, row) updates idx = threadIdx.x + 1024 u, in two batches of reads
-        // then writes; (pair, row) = (idx / k, idx % k) advanced incrementally
-        int w = threadIdx.x / k, i = threadIdx.x - w * k;
-        const int dq = kRfJacobiThreads / k, dr = kRfJacobiThreads - dq * k;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          constexpr int NB = (VPT + 1) / 2;
-          int vo[NB];   // row offset << 8 | pair, -1 when idle
-          float vx[NB], vy[NB];
-#pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            vo[u] = -1;
-            if (w < half && rot[w]) {
-              vo[u] = ((i * PT) << 8) | w;
-              vx[u] = V[i * PT + pp[w]];
-              vy[u] = V[i * PT + pq[w]];
-            }
-            w += dq;
-            i += dr;
-            if (i >= k) {
-              i -= k;
-              ++w;
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            if (vo[u] < 0) continue;
-            const int wu = vo[u] & 0xFF, row = vo[u] >> 8;
-            const float c = cs_c[wu], sn = cs_s[wu];
-            V[row + pp[wu]] = c * vx[u] - sn * vy[u];
-            V[row + pq[wu]] = sn * vx[u] + c * vy[u];
-          }
-        }
-      }
-      __syncthreads();
-    }
-    ++sweeps;
-    if (!rotated) break;
-    __syncthreads();
-  }
-  for (int i = threadIdx.x; i < k; i += kRfJacobiThreads) {
-    const float li = A[i * PT + i];
-    int rk = 0;
-    for (int j = 0; j < k; ++j) {
-      const float lj = A[j * PT + j];
-      rk += (lj > li || (lj == li && j < i)) ? 1 : 0;
-    }
-    rank_of[i] = rk;
-    gstore(evals + rk, li);
-    if (sigma && rk < r) gstore(sigma + rk, sqrtf(fmaxf(li, 0.0f)));
-  }
-  __syncthreads();
-  for (int i = wave; i < k; i += NW)
-    for (int col = lane; col < k; col += 64) {   // V[i][col]: entry i of eigenvector col
-      const int rk = rank_of[col];
-      if (rk < r) gstore(Vr + i * r + rk, V[i * PT + col]);
-    }
-  if (threadIdx.x == 0 && sweeps_out) gstore(sweeps_out, sweeps);
-}
-
 // ======================================================================= launchers ===
 hipError_t launch_rf_gemm(const RfGemm& g, hipStream_t s) {
   const int grid = g.tiles_m * g.tiles_n * g.split;
@@ -631,13 +447,6 @@ hipError_t launch_rf_smallmul(const float* Y, const float* Wm, int64_t M, int k,
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64));
   hipLaunchKernelGGL(qg_rf_smallmul, grid, dim3(kThreads), 0, s, Y, Wm, M, k, N, out, outb,
                      amax_v);
-  return hipGetLastError();
-}
-
-hipError_t launch_rf_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
-                            float* evals, float* Vr, float* sigma, int* sweeps, hipStream_t s) {
-  hipLaunchKernelGGL(qg_rf_jacobi, dim3(1), dim3(kRfJacobiThreads), 0, s, C, k, r, max_sweeps,
-                     tol, evals, Vr, sigma, sweeps);
   return hipGetLastError();
 }
 

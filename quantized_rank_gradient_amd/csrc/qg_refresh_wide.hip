@@ -234,11 +234,6 @@ __global__ __launch_bounds__(kThreads) void qg_rf_colmax(const float* P, int64_t
 // a subproblem the rotations are chosen on an fp32 copy (enough to decide them; any
 // orthogonal J serves Jacobi), while J itself is accumulated in fp64 from each rotation's
 // (c, s) renormalized in fp64.
-constexpr int kBjB = kRfJacobiBlock;   // indices per block
-constexpr int kBjS = 2 * kBjB;         // order of a subproblem (a pair of blocks)
-constexpr int kBjP = kBjS + 1;         // LDS pitch
-constexpr int kBjPairs = kBjS / 2;     // disjoint index pairs per inner round
-
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -253,9 +248,10 @@ __device__ __forceinline__ void bj_pair(int nb, int round, int w, int& lo, int& 
   lo = min(a, b);
   hi = max(a, b);
 }
-// Index of a subproblem's local index l (0 .. 63): the first block, then the second.
+// Index of a subproblem's local index l (0 .. 2B-1): the first block, then the second.
+template <int B>
 __device__ __forceinline__ int bj_index(int lo, int hi, int l) {
-  return (l < kBjB ? lo : hi) * kBjB + (l & (kBjB - 1));
+  return (l < B ? lo : hi) * B + (l & (B - 1));
 }
 // A sweep is skipped when the previous one rotated nothing.
 __device__ __forceinline__ bool bj_converged(const int* rot, int sweep) {
@@ -300,18 +296,19 @@ __device__ __forceinline__ bool bj_needs(float app, float aqq, float apq, float 
   return fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
 }
 
-constexpr int kBjSolveThreads = 512;
-constexpr int kBjFullRounds = kBjS - 1;   // inner rounds over all pairs of a subproblem
-constexpr int kBjCrossRounds = kBjB;      // inner rounds over the pairs across its two blocks
+// Threads of the subproblem kernel for blocks of B indices: one Q row pair update of four
+// rows per thread.
+template <int B>
+constexpr int bj_solve_threads() { return B * 2 * B / 4; }
 
-// One workgroup per pair of blocks: the 64 x 64 subproblem S of C (as fp32), one sweep of
+// One workgroup per pair of blocks: the 2B x 2B subproblem S of C (as fp32), one sweep of
 // 2 x 2 rotations on it, S <- R^T S R and Q <- Q R from Q = I; then Q (fp64) goes to Jm[w]
 // and whether it differs from I to jrot[w].
 //
 // In the first round of an outer sweep every block is in exactly one subproblem, and the
-// sweep there covers all 2016 index pairs of the subproblem (63 inner rounds of a round-robin
-// on its 64 indices). In the other rounds it covers only the 1024 pairs across the two blocks
-// (32 inner rounds: index i of the first block with index (i + t) mod 32 of the second), since
+// sweep there covers all index pairs of the subproblem (2B - 1 inner rounds of a round-robin
+// on its 2B indices). In the other rounds it covers only the B^2 pairs across the two blocks
+// (B inner rounds: index i of the first block with index (i + t) mod B of the second), since
 // the pairs inside a block were treated in the first round: every index pair of C is thus
 // rotated once per outer sweep, as in cyclic Jacobi.
 //
@@ -319,40 +316,42 @@ constexpr int kBjCrossRounds = kBjB;      // inner rounds over the pairs across 
 // 2 x 2 block: block (u1, u2), u1 <= u2, holds rows p1, q1 of pair slot u1 and columns p2, q2
 // of slot u2, and every stored entry lies in exactly one such block. Each thread keeps the
 // same blocks, and the same pair slot of Q with four of its rows, in every inner round; the
-// pairs of each inner round come from a table. A round is the rotation parameters of the 32
+// pairs of each inner round come from a table. A round is the rotation parameters of the B
 // slots, a barrier, the updates (all reads issued before any write), and a barrier. A
 // subproblem with no pair over the rotation level is left as it is.
-__global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
+template <int B>
+__global__ __launch_bounds__(bj_solve_threads<B>()) void qg_rf_bj_solve(
     const double* Cj, int K, int nb, int round, int sweep, float tol, const float* abs_tol_p,
     int* rot, double* Jm, int* jrot) {
   if (bj_converged(rot, sweep)) return;
-  constexpr int NT = kBjSolveThreads;
-  __shared__ float A[kBjS * kBjP];
-  __shared__ double Q[kBjS * kBjP];
-  __shared__ float4 cs[kBjPairs];     // c, s (fp32), rotate flag
-  __shared__ double2 csd[kBjPairs];   // c, s (fp64, unit length)
-  __shared__ uint16_t pt[kBjFullRounds * kBjPairs];   // pairs of each inner round: p | q << 8
+  constexpr int S = 2 * B, PT = S + 1, NT = bj_solve_threads<B>();
+  constexpr int kFullRounds = S - 1, kCrossRounds = B;
+  __shared__ float A[S * PT];
+  __shared__ double Q[S * PT];
+  __shared__ float4 cs[B];     // c, s (fp32), rotate flag
+  __shared__ double2 csd[B];   // c, s (fp64, unit length)
+  __shared__ uint16_t pt[kFullRounds * B];   // pairs of each inner round: p | q << 8
   __shared__ int need;
   const bool full = round == 0;
-  const int rounds = full ? kBjFullRounds : kBjCrossRounds;
+  const int rounds = full ? kFullRounds : kCrossRounds;
   int lo, hi;
   bj_pair(nb, round, blockIdx.x, lo, hi);
-  for (int e = threadIdx.x; e < kBjS * kBjS; e += NT) {
-    const int i = e / kBjS, j = e % kBjS;
-    A[i * kBjP + j] = (float)gload(Cj + (int64_t)bj_index(lo, hi, i) * K + bj_index(lo, hi, j));
-    Q[i * kBjP + j] = i == j ? 1.0 : 0.0;
+  for (int e = threadIdx.x; e < S * S; e += NT) {
+    const int i = e / S, j = e % S;
+    A[i * PT + j] = (float)gload(Cj + (int64_t)bj_index<B>(lo, hi, i) * K + bj_index<B>(lo, hi, j));
+    Q[i * PT + j] = i == j ? 1.0 : 0.0;
   }
-  for (int e = threadIdx.x; e < rounds * kBjPairs; e += NT) {
-    const int rd = e / kBjPairs, u = e % kBjPairs;
+  for (int e = threadIdx.x; e < rounds * B; e += NT) {
+    const int rd = e / B, u = e % B;
     int p, q;
-    if (full) {   // positions u and 63 - u of the round-robin on 64 indices
-      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (kBjS - 1);
-      const int b = 1 + (kBjS - 2 - u + rd) % (kBjS - 1);
+    if (full) {   // positions u and S - 1 - u of the round-robin on S indices
+      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (S - 1);
+      const int b = 1 + (S - 2 - u + rd) % (S - 1);
       p = min(a, b);
       q = max(a, b);
     } else {
       p = u;
-      q = kBjB + ((u + rd) & (kBjB - 1));
+      q = B + ((u + rd) & (B - 1));
     }
     pt[e] = (uint16_t)(p | (q << 8));
   }
@@ -361,11 +360,10 @@ __global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
   __syncthreads();
   {
     int mine = 0;
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += NT) {
-      const int i = e / kBjS, j = e % kBjS;
-      const bool considered = full ? i < j : (i < kBjB && j >= kBjB);
-      if (considered &&
-          bj_needs(A[i * kBjP + i], A[j * kBjP + j], A[i * kBjP + j], tol, abs_tol))
+    for (int e = threadIdx.x; e < S * S; e += NT) {
+      const int i = e / S, j = e % S;
+      const bool considered = full ? i < j : (i < B && j >= B);
+      if (considered && bj_needs(A[i * PT + i], A[j * PT + j], A[i * PT + j], tol, abs_tol))
         mine = 1;
     }
     if (mine) need = 1;
@@ -373,7 +371,7 @@ __global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
   __syncthreads();
   const bool active = need != 0;
   // this thread's 2 x 2 blocks (slot pairs u1 <= u2, by number)
-  constexpr int kBlocks = kBjPairs * (kBjPairs + 1) / 2;
+  constexpr int kBlocks = B * (B + 1) / 2;
   constexpr int BPT = (kBlocks + NT - 1) / NT;
   int bu1[BPT], bu2[BPT];
 #pragma unroll
@@ -384,25 +382,25 @@ __global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
       bu2[u] = -1;
       continue;
     }
-    while (bi >= kBjPairs - w1) {
-      bi -= kBjPairs - w1;
+    while (bi >= B - w1) {
+      bi -= B - w1;
       ++w1;
     }
     bu1[u] = w1;
     bu2[u] = w1 + bi;
   }
   // and its slot of Q with four rows
-  constexpr int QR = kBjPairs * kBjS / NT;
-  static_assert(QR * NT == kBjPairs * kBjS && kBjS % QR == 0, "Q rows split evenly");
-  const int qw = threadIdx.x / (kBjS / QR);
-  const int qrow = (threadIdx.x % (kBjS / QR)) * QR;
+  constexpr int QR = 4;
+  static_assert(QR * NT == B * S, "Q rows split evenly");
+  const int qw = threadIdx.x / (S / QR);
+  const int qrow = (threadIdx.x % (S / QR)) * QR;
   for (int rd = 0; active && rd < rounds; ++rd) {
-    const uint16_t* prd = pt + rd * kBjPairs;
-    if ((int)threadIdx.x < kBjPairs) {
+    const uint16_t* prd = pt + rd * B;
+    if ((int)threadIdx.x < B) {
       const int u = threadIdx.x;
       const int pq = prd[u];
       const int p = pq & 0xFF, q = pq >> 8;
-      const float app = A[p * kBjP + p], aqq = A[q * kBjP + q], apq = A[p * kBjP + q];
+      const float app = A[p * PT + p], aqq = A[q * PT + q], apq = A[p * PT + q];
       float c = 1.0f, s = 0.0f;
       double cd = 1.0, sd = 0.0;
       const bool go = bj_needs(app, aqq, apq, tol, abs_tol);
@@ -433,23 +431,23 @@ __global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
       if (bu1[u] < 0) continue;
       const int pq1 = prd[bu1[u]], pq2 = prd[bu2[u]];
       const int p1 = pq1 & 0xFF, q1 = pq1 >> 8, p2 = pq2 & 0xFF, q2 = pq2 >> 8;
-      o[u][0] = min(p1, p2) * kBjP + max(p1, p2);
-      o[u][1] = min(p1, q2) * kBjP + max(p1, q2);
-      o[u][2] = min(q1, p2) * kBjP + max(q1, p2);
-      o[u][3] = min(q1, q2) * kBjP + max(q1, q2);
+      o[u][0] = min(p1, p2) * PT + max(p1, p2);
+      o[u][1] = min(p1, q2) * PT + max(p1, q2);
+      o[u][2] = min(q1, p2) * PT + max(q1, p2);
+      o[u][3] = min(q1, q2) * PT + max(q1, q2);
       r1[u] = cs[bu1[u]];
       r2[u] = cs[bu2[u]];
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
     }
     const int qpq = prd[qw];
-    const int qp = qrow * kBjP + (qpq & 0xFF), qq = qrow * kBjP + (qpq >> 8);
+    const int qp = qrow * PT + (qpq & 0xFF), qq = qrow * PT + (qpq >> 8);
     const double2 qcs = csd[qw];
     double qx[QR], qy[QR];
 #pragma unroll
     for (int v = 0; v < QR; ++v) {
-      qx[v] = Q[qp + v * kBjP];
-      qy[v] = Q[qq + v * kBjP];
+      qx[v] = Q[qp + v * PT];
+      qy[v] = Q[qq + v * PT];
     }
     // writes: only blocks and rows touched by a rotation change
 #pragma unroll
@@ -467,90 +465,93 @@ __global__ __launch_bounds__(kBjSolveThreads) void qg_rf_bj_solve(
     if (cs[qw].z != 0.0f) {
 #pragma unroll
       for (int v = 0; v < QR; ++v) {
-        Q[qp + v * kBjP] = qcs.x * qx[v] - qcs.y * qy[v];
-        Q[qq + v * kBjP] = qcs.y * qx[v] + qcs.x * qy[v];
+        Q[qp + v * PT] = qcs.x * qx[v] - qcs.y * qy[v];
+        Q[qq + v * PT] = qcs.y * qx[v] + qcs.x * qy[v];
       }
     }
     __syncthreads();
   }
-  double* out = Jm + (int64_t)blockIdx.x * kBjS * kBjS;
-  for (int e = threadIdx.x; e < kBjS * kBjS; e += NT)
-    gstore(out + e, Q[(e / kBjS) * kBjP + e % kBjS]);
+  double* out = Jm + (int64_t)blockIdx.x * S * S;
+  for (int e = threadIdx.x; e < S * S; e += NT) gstore(out + e, Q[(e / S) * PT + e % S]);
   if (threadIdx.x == 0) {
     gstore(jrot + blockIdx.x, active ? 1 : 0);
     if (active) gstore(rot + sweep, 1);
   }
 }
 
-// This wave's 32 x 32 block (rows wm*32, columns wn*32) of a 64 x 64 fp64 product
-// sum over t < 64 of A(i, t) B(t, j), as 2 x 2 tiles of 16 x 16 (v_mfma_f64_16x16x4_f64).
-// A and B are LDS matrices with pitch kBjP; A is read as stored ([i][t]) or transposed
-// (stored [t][i]).
-template <bool A_TRANSPOSED>
-__device__ __forceinline__ void bj_mul(const double* Am, const double* Bm, f64x4 (&acc)[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i0 = (wave >> 1) * 32, j0 = (wave & 1) * 32;
-  const int l16 = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-  for (int t = 0; t < kBjS; t += 4) {
-    double a[2], b[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int i = i0 + 16 * x + l16;
-      a[x] = A_TRANSPOSED ? Am[(t + kq) * kBjP + i] : Am[i * kBjP + t + kq];
-    }
-#pragma unroll
-    for (int y = 0; y < 2; ++y) b[y] = Bm[(t + kq) * kBjP + j0 + 16 * y + l16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f64(a[x], b[y], acc[x][y]);
+// A 2B x 2B fp64 product on four waves: wave (wm, wn) holds the B x B quarter at rows wm*B,
+// columns wn*B, as (B/16)^2 tiles of 16 x 16 (v_mfma_f64_16x16x4_f64, which gives lane l the
+// entries (l / 16 + 4 v, l % 16) of a tile). acc = sum over t < 2B of A(i, t) B(t, j), A and
+// B in LDS with pitch 2B + 1, A read as stored ([i][t]) or transposed (stored [t][i]).
+template <int B>
+struct BjMul {
+  static constexpr int S = 2 * B, PT = S + 1, T = B / 16;
+  f64x4 acc[T][T];
+  __device__ static int row(int x, int v) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave >> 1) * B + 16 * x + (lane >> 4) + 4 * v;
   }
-}
-// Output coordinates of element v of tile (x, y) for this lane: v_mfma_f64_16x16x4_f64 gives
-// lane l the entries (l / 16 + 4 v, l % 16) of its 16 x 16 tile.
-__device__ __forceinline__ int bj_row(int x, int v) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave >> 1) * 32 + 16 * x + (lane >> 4) + 4 * v;
-}
-__device__ __forceinline__ int bj_col(int y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 1) * 32 + 16 * y + (lane & 15);
-}
-__device__ __forceinline__ void bj_put(double* X, const f64x4 (&acc)[2][2]) {
+  __device__ static int col(int y) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave & 1) * B + 16 * y + (lane & 15);
+  }
+  template <bool A_TRANSPOSED>
+  __device__ void mul(const double* Am, const double* Bm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i0 = (wave >> 1) * B, j0 = (wave & 1) * B;
+    const int l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < T; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int y = 0; y < T; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int t = 0; t < S; t += 4) {
+      double a[T], b[T];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) X[bj_row(x, v) * kBjP + bj_col(y)] = acc[x][y][v];
-}
+      for (int x = 0; x < T; ++x) {
+        const int i = i0 + 16 * x + l16;
+        a[x] = A_TRANSPOSED ? Am[(t + kq) * PT + i] : Am[i * PT + t + kq];
+      }
+#pragma unroll
+      for (int y = 0; y < T; ++y) b[y] = Bm[(t + kq) * PT + j0 + 16 * y + l16];
+#pragma unroll
+      for (int x = 0; x < T; ++x)
+#pragma unroll
+        for (int y = 0; y < T; ++y) acc[x][y] = mfma_f64(a[x], b[y], acc[x][y]);
+    }
+  }
+  __device__ void put(double* X) const {
+#pragma unroll
+    for (int x = 0; x < T; ++x)
+#pragma unroll
+      for (int y = 0; y < T; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) X[row(x, v) * PT + col(y)] = acc[x][y][v];
+  }
+};
 
-// The round's rotations applied to C and V. Workgroups 0 .. nC-1 take the 64 x 64 pieces
+// The round's rotations applied to C and V. Workgroups 0 .. nC-1 take the 2B x 2B pieces
 // (pairs w1 <= w2) of C: X = C[rows of w1][columns of w2], X' = J1^T X J2, written at
 // (w1, w2) and transposed at (w2, w1); a diagonal piece is symmetrized from its upper
-// triangle. The others take 64-row strips of V restricted to one pair's columns: V' = V J.
+// triangle. The others take 2B-row strips of V restricted to one pair's columns: V' = V J.
 // Pieces whose rotations are all the identity are left as they are.
+template <int B>
 __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* Vj, int K, int nb,
                                                            int round, int sweep, const int* rot,
                                                            const double* Jm, const int* jrot) {
   if (bj_converged(rot, sweep)) return;
-  __shared__ double X[kBjS * kBjP];
-  __shared__ double J1[kBjS * kBjP];
-  __shared__ double J2[kBjS * kBjP];
+  constexpr int S = 2 * B, PT = S + 1;
+  __shared__ double X[S * PT];
+  __shared__ double J1[S * PT];
+  __shared__ double J2[S * PT];
   const int P = nb / 2;
   const int nC = P * (P + 1) / 2;
   int bid = blockIdx.x;
   auto load_j = [&](double* dst, int w) {
-    const double* src = Jm + (int64_t)w * kBjS * kBjS;
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads)
-      dst[(e / kBjS) * kBjP + e % kBjS] = gload(src + e);
+    const double* src = Jm + (int64_t)w * S * S;
+    for (int e = threadIdx.x; e < S * S; e += kThreads) dst[(e / S) * PT + e % S] = gload(src + e);
   };
-  f64x4 acc[2][2];
+  BjMul<B> m;
   if (bid < nC) {
     int w1 = 0;
     while (bid >= P - w1) {
@@ -562,30 +563,31 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
     int lo1, hi1, lo2, hi2;
     bj_pair(nb, round, w1, lo1, hi1);
     bj_pair(nb, round, w2, lo2, hi2);
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
-      const int i = e / kBjS, j = e % kBjS;
-      X[i * kBjP + j] = gload(Cj + (int64_t)bj_index(lo1, hi1, i) * K + bj_index(lo2, hi2, j));
+    for (int e = threadIdx.x; e < S * S; e += kThreads) {
+      const int i = e / S, j = e % S;
+      X[i * PT + j] =
+          gload(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K + bj_index<B>(lo2, hi2, j));
     }
     load_j(J1, w1);
     load_j(J2, w2);
     __syncthreads();
-    bj_mul<true>(J1, X, acc);   // J1^T X
+    m.template mul<true>(J1, X);   // J1^T X
     __syncthreads();
-    bj_put(X, acc);
+    m.put(X);
     __syncthreads();
-    bj_mul<false>(X, J2, acc);   // (J1^T X) J2
+    m.template mul<false>(X, J2);   // (J1^T X) J2
     __syncthreads();
-    bj_put(X, acc);
+    m.put(X);
     __syncthreads();
     const bool diag = w1 == w2;
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
-      const int i = e / kBjS, j = e % kBjS;
-      const double v = diag ? X[min(i, j) * kBjP + max(i, j)] : X[i * kBjP + j];
-      gstore(Cj + (int64_t)bj_index(lo1, hi1, i) * K + bj_index(lo2, hi2, j), v);
+    for (int e = threadIdx.x; e < S * S; e += kThreads) {
+      const int i = e / S, j = e % S;
+      const double v = diag ? X[min(i, j) * PT + max(i, j)] : X[i * PT + j];
+      gstore(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K + bj_index<B>(lo2, hi2, j), v);
       if (!diag) {   // transposed piece, element (ti, tj) of X to (tj, ti): coalesced stores
-        const int ti = e % kBjS, tj = e / kBjS;
-        gstore(Cj + (int64_t)bj_index(lo2, hi2, tj) * K + bj_index(lo1, hi1, ti),
-               X[ti * kBjP + tj]);
+        const int ti = e % S, tj = e / S;
+        gstore(Cj + (int64_t)bj_index<B>(lo2, hi2, tj) * K + bj_index<B>(lo1, hi1, ti),
+               X[ti * PT + tj]);
       }
     }
   } else {
@@ -594,21 +596,22 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
     if (gload(jrot + w) == 0) return;
     int lo, hi;
     bj_pair(nb, round, w, lo, hi);
-    const int64_t r0 = (int64_t)strip * kBjS;
-    for (int e = threadIdx.x; e < kBjS * kBjS; e += kThreads) {
-      const int i = e / kBjS, j = e % kBjS;
-      X[i * kBjP + j] = gload(Vj + (r0 + i) * K + bj_index(lo, hi, j));
+    const int64_t r0 = (int64_t)strip * S;
+    for (int e = threadIdx.x; e < S * S; e += kThreads) {
+      const int i = e / S, j = e % S;
+      X[i * PT + j] = gload(Vj + (r0 + i) * K + bj_index<B>(lo, hi, j));
     }
     load_j(J1, w);
     __syncthreads();
-    bj_mul<false>(X, J1, acc);
+    m.template mul<false>(X, J1);
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < BjMul<B>::T; ++x)
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const int j = bj_index(lo, hi, bj_col(y));
+      for (int y = 0; y < BjMul<B>::T; ++y) {
+        const int j = bj_index<B>(lo, hi, BjMul<B>::col(y));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) gstore(Vj + (r0 + bj_row(x, v)) * K + j, acc[x][y][v]);
+        for (int v = 0; v < 4; ++v)
+          gstore(Vj + (r0 + BjMul<B>::row(x, v)) * K + j, m.acc[x][y][v]);
       }
   }
 }
@@ -682,26 +685,38 @@ hipError_t launch_rf_colmax(const float* P, int64_t m, int r, float* amax_v, hip
   return hipGetLastError();
 }
 
+template <int B>
+static hipError_t block_jacobi_sweeps(int k, int max_sweeps, float tol, const RfBj& w,
+                                      hipStream_t s) {
+  const int nb = rf_bj_blocks(k, B);
+  const int K = nb * B;
+  const int P = nb / 2;
+  const int apply_grid = P * (P + 1) / 2 + (K / (2 * B)) * P;
+  hipError_t e = hipSuccess;
+  for (int sweep = 0; sweep < max_sweeps && e == hipSuccess; ++sweep)
+    for (int round = 0; round < nb - 1 && e == hipSuccess; ++round) {
+      hipLaunchKernelGGL(qg_rf_bj_solve<B>, dim3(P), dim3(bj_solve_threads<B>()), 0, s, w.C, K,
+                         nb, round, sweep, tol, w.abs_tol, w.rot, w.J, w.jrot);
+      hipLaunchKernelGGL(qg_rf_bj_apply<B>, dim3(apply_grid), dim3(kThreads), 0, s, w.C, w.V, K,
+                         nb, round, sweep, w.rot, w.J, w.jrot);
+      e = hipGetLastError();
+    }
+  return e;
+}
+
 hipError_t launch_rf_block_jacobi(const float* C, int k, int r, int max_sweeps, float tol,
                                   const RfBj& w, float* evals, float* Vr, float* sigma,
                                   int* sweeps, hipStream_t s) {
-  const int nb = rf_bj_blocks(k);
-  const int K = nb * kBjB;
-  const int P = nb / 2;
+  const int B = rf_bj_block(k);
+  const int K = rf_bj_blocks(k, B) * B;
   hipLaunchKernelGGL(qg_rf_bj_init, dim3(grid_for((int64_t)K * K)), dim3(kThreads), 0, s, C, k,
                      K, w.C, w.V);
   hipLaunchKernelGGL(qg_rf_bj_prep, dim3(1), dim3(kThreads), 0, s, C, k, w.abs_tol, w.rot,
                      max_sweeps);
   hipError_t e = hipGetLastError();
-  const int apply_grid = P * (P + 1) / 2 + (K / kBjS) * P;
-  for (int sweep = 0; sweep < max_sweeps && e == hipSuccess; ++sweep)
-    for (int round = 0; round < nb - 1 && e == hipSuccess; ++round) {
-      hipLaunchKernelGGL(qg_rf_bj_solve, dim3(P), dim3(kBjSolveThreads), 0, s, w.C, K, nb, round,
-                         sweep, tol, w.abs_tol, w.rot, w.J, w.jrot);
-      hipLaunchKernelGGL(qg_rf_bj_apply, dim3(apply_grid), dim3(kThreads), 0, s, w.C, w.V, K, nb,
-                         round, sweep, w.rot, w.J, w.jrot);
-      e = hipGetLastError();
-    }
+  if (e == hipSuccess)
+    e = B == 16 ? block_jacobi_sweeps<16>(k, max_sweeps, tol, w, s)
+                : block_jacobi_sweeps<32>(k, max_sweeps, tol, w, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(qg_rf_bj_rank, dim3(1), dim3(1024), 0, s, w.C, K, k, r, w.rot, max_sweeps,
                      evals, sigma, w.rank_of, sweeps);

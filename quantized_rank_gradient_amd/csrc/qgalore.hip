@@ -790,12 +790,11 @@ extern "C" qg_status qgalore_quantize_proj_int8(const float* P, int64_t m, int64
 namespace {
 constexpr int kRfMaxPowerIters = 8;
 constexpr int64_t kRfGramChunk = 64;     // rows per partial Gram matrix
-constexpr int kRfMaxSweeps = 20;         // Jacobi sweeps at most
 constexpr float kRfJacobiTol = 1e-6f;    // relative off-diagonal level that ends a sweep
 constexpr float kRfShift = 1e-6f;        // diagonal shift (x trace / k) of the first
                                          // CholeskyQR pass
 constexpr int64_t kRfBlockW = 128;       // columns per block of the wide orthonormalization
-constexpr int kRfWideSweeps = 16;        // block Jacobi sweeps at most
+constexpr int kRfSweeps = 16;            // block Jacobi sweeps at most
 
 struct RfGemmPlan {
   int split, tiles_m, tiles_n;
@@ -859,8 +858,8 @@ RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
     }
     spart = std::max(spart, sg_part_elems(k, k, n));
   }
-  const int nbj = qg::rf_bj_blocks((int)k);
-  const int64_t KJ = (int64_t)nbj * qg::kRfJacobiBlock;
+  const int bjb = qg::rf_bj_block((int)k);
+  const int64_t KJ = (int64_t)qg::rf_bj_blocks((int)k, bjb) * bjb;
   RfLayout L;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -885,12 +884,12 @@ RfLayout rf_layout(int64_t m, int64_t n, int64_t r, int64_t k) {
   L.off_gpad = take(n % 8 ? m * round_up(n, 8) * 2 : 0);
   L.off_spart = take(spart * 4);
   L.off_s = take(wide ? k * kRfBlockW * 4 : 0);
-  L.off_bjc = take(wide ? KJ * KJ * 8 : 0);
-  L.off_bjv = take(wide ? KJ * KJ * 8 : 0);
-  L.off_bjj = take(wide ? (KJ / 64) * 64 * 64 * 8 : 0);
-  L.off_bjjrot = take((KJ / 64) * 4);
+  L.off_bjc = take(KJ * KJ * 8);
+  L.off_bjv = take(KJ * KJ * 8);
+  L.off_bjj = take(KJ * 2 * bjb * 8);
+  L.off_bjjrot = take(KJ / (2 * bjb) * 4);
   L.off_bjtol = take(4);
-  L.off_bjrot = take(kRfWideSweeps * 4);
+  L.off_bjrot = take(kRfSweeps * 4);
   L.off_bjrank = take(k * 4);
   L.bytes = off;
   return L;
@@ -1067,26 +1066,27 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
     orthogonalize(m, it == power_iters - 1 ? 2 : 1);
   }
   product(true, Qb, 2 * k, Y);            // B^T = G^T Q  (n x k)
+  // B B^T and its eigen-decomposition
+  if (wide)
+    sgemm(Y, k, true, Y, k, k, k, n, gram, k, qg::kSgPartial);
+  else
+    gram_of(Y, n);
+  qg::RfBj bj;
+  bj.C = reinterpret_cast<double*>(ws + lay.off_bjc);
+  bj.V = reinterpret_cast<double*>(ws + lay.off_bjv);
+  bj.J = reinterpret_cast<double*>(ws + lay.off_bjj);
+  bj.jrot = reinterpret_cast<int*>(ws + lay.off_bjjrot);
+  bj.abs_tol = at(lay.off_bjtol);
+  bj.rot = reinterpret_cast<int*>(ws + lay.off_bjrot);
+  bj.rank_of = reinterpret_cast<int*>(ws + lay.off_bjrank);
+  if (e == hipSuccess)
+    e = qg::launch_rf_block_jacobi(gram, kk, (int)r, kRfSweeps, kRfJacobiTol, bj, evals, Vr,
+                                   sigma_out, info, s);
+  // P = Q V_r with the per-tile column maxima of the sign rule
   if (!wide) {
-    gram_of(Y, n);                        // B B^T
-    if (e == hipSuccess)
-      e = qg::launch_rf_jacobi(gram, kk, (int)r, kRfMaxSweeps, kRfJacobiTol, evals, Vr,
-                               sigma_out, info, s);
     if (e == hipSuccess) e = qg::launch_rf_smallmul(Qf, Vr, m, kk, (int)r, P, nullptr, amax, s);
   } else {
-    sgemm(Y, k, true, Y, k, k, k, n, gram, k, qg::kSgPartial);   // B B^T
-    qg::RfBj bj;
-    bj.C = reinterpret_cast<double*>(ws + lay.off_bjc);
-    bj.V = reinterpret_cast<double*>(ws + lay.off_bjv);
-    bj.J = reinterpret_cast<double*>(ws + lay.off_bjj);
-    bj.jrot = reinterpret_cast<int*>(ws + lay.off_bjjrot);
-    bj.abs_tol = at(lay.off_bjtol);
-    bj.rot = reinterpret_cast<int*>(ws + lay.off_bjrot);
-    bj.rank_of = reinterpret_cast<int*>(ws + lay.off_bjrank);
-    if (e == hipSuccess)
-      e = qg::launch_rf_block_jacobi(gram, kk, (int)r, kRfWideSweeps, kRfJacobiTol, bj, evals,
-                                     Vr, sigma_out, info, s);
-    sgemm(Qf, k, false, Vr, r, m, r, k, P, r, qg::kSgStore);      // P = Q V_r
+    sgemm(Qf, k, false, Vr, r, m, r, k, P, r, qg::kSgStore);
     if (e == hipSuccess) e = qg::launch_rf_colmax(P, m, (int)r, amax, s);
   }
   if (e == hipSuccess) e = qg::launch_rf_signs(P, m, (int)r, amax, sgn, s);
