@@ -27,6 +27,22 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+# Vector ALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes per cycle (a 64-lane
+# instruction takes 4 cycles) x 2.4 GHz, in lane operations per second. The published fp32
+# vector peak, 157.3 TFLOP/s, is this rate x 2 (an FMA) x 2 (packed fp32).
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Operations the method's arithmetic needs per element, counted one per fp32/int32 operation
+# of the contract (a division, square root or 32 x 32 -> 64-bit multiply counts one):
+#   rounding of one weight: U = alpha*S, a = U*inv, w to fp32, t = w + a, the 16 random bits
+#   to fp32, d = t + u, floor, clamp (8), plus Philox4x32-10 for 8 weights: 10 rounds of two
+#   multiplies and two three-way XORs, 40 per 8 weights (5);
+SR_OPS_PER_WEIGHT = 8 + 5
+#   Adam on one element of R: two moment dequantizations (4), m1 (3), v1 (4), the two bias
+#   corrections (2), sqrt, + eps, lr * m^, the division (4), the two absmax steps (2), the
+#   two requantizations (6), N~ to bf16 (1);
+ADAM_OPS_PER_ELEM = 26
+#   INT4 dequantization of one P element: code to fp32, one fma (2).
+DEQUANT_OPS_PER_ELEM = 2
 DELTA0 = 25                    # initial refresh interval (200 steps / 8)
 GAMMA = 0.4
 
@@ -253,7 +269,12 @@ def algorithmic(cfg, r, fmt="int4", inline=False):
               2.0 * mn + (adam if fused else 0.0) + (p_bytes if inline else 0.0),
               0.0 if fused else adam,
               2.0 * mn + mn / 64.0)                   # W in and out + W scales
-    return dict(mn=mn, flops=flops, bytes=nbytes, fused_adam=fused)
+    deq = 0.0 if fmt == "bf16" else DEQUANT_OPS_PER_ELEM * mr
+    ops = (0.0 if inline else deq,
+           (ADAM_OPS_PER_ELEM * rn if fused else 0.0) + (deq if inline else 0.0),
+           0.0 if fused else ADAM_OPS_PER_ELEM * rn,
+           SR_OPS_PER_WEIGHT * mn)
+    return dict(mn=mn, flops=flops, bytes=nbytes, ops=ops, fused_adam=fused)
 
 
 def roofline(cfg, r, kms, fmt="int4", inline=False):
@@ -265,18 +286,25 @@ def roofline(cfg, r, kms, fmt="int4", inline=False):
     if k == 1 and a["fused_adam"]:
         names = list(names)
         names[1] = "qg_project (+ Adam)"
-    intensity = a["flops"][k] / a["bytes"][k] if a["bytes"][k] else 0.0
-    mfma_bound = intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
+    # the binding unit: the largest of the kernel's lower-bound times on HBM, the bf16 matrix
+    # cores and the vector ALUs
+    t_hbm = a["bytes"][k] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = a["flops"][k] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    t_alu = a["ops"][k] / (ALU_PEAK_TOPS * 1e12)
+    common = dict(kernel=names[k], traffic=traffic, ms_per_launch=round(kms[k], 4),
+                  lower_bound_ms={"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4),
+                                  "alu": round(t_alu * 1e3, 4)})
+    if t_mfma >= max(t_hbm, t_alu):
         ach = a["flops"][k] / sec / 1e12
-        return dict(kernel=names[k], bound="mfma", achieved=round(ach, 2),
-                    peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4), traffic=traffic,
-                    ms_per_launch=round(kms[k], 4))
+        return dict(bound="mfma", achieved=round(ach, 2), peak=BF16_MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4), **common)
+    if t_alu >= t_hbm:
+        ach = a["ops"][k] / sec / 1e12
+        return dict(bound="alu", achieved=round(ach, 2), peak=round(ALU_PEAK_TOPS, 2),
+                    unit="TOP/s", frac=round(ach / ALU_PEAK_TOPS, 4), **common)
     ach = a["bytes"][k] / sec / 1e9
-    return dict(kernel=names[k], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
-                ms_per_launch=round(kms[k], 4))
+    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), **common)
 
 
 KERNEL_SOURCES = ("qg_kernels.hip", "qg_gemm.hpp", "qg_device.hpp", "qg_kernels.hpp")
