@@ -174,6 +174,9 @@ hipError_t launch_linear(const LinArgs& a, int which, hipStream_t s);
 // 32 codes of a K stage (forward) or a column tile's 128 codes of a row (data gradient) lie
 // in one 256-element scale group.
 constexpr bool lin_fwd_dma(int64_t n) { return n % 32 == 0; }
+// Forward shapes staged in 64-K stages (whole lines of the activation rows, halves of the
+// weight rows).
+constexpr bool lin_fwd_rows(int64_t n) { return n % 128 == 0; }
 constexpr bool lin_bwd_data_dma(int64_t n) { return n % 128 == 0; }
 
 }  // namespace qg

@@ -143,6 +143,139 @@ struct DmaInt8C {
   }
 };
 
+// The forward product for n % 128 == 0 (every LLaMA shape), in stages of 64 K values: both
+// operands are K-contiguous, and a stage of 32 reads only 64 bytes of each activation row and
+// 32 of each weight row, so that a wave-level load touches 16 or 32 cache lines and waits
+// long for them (counters: the same instruction mix as the data gradient's, 50% more wait
+// cycles). Here the activation rows come as full 128-byte lines (tile [256][64] bf16,
+// 16-byte chunk c of row r at slot c ^ ((r / 2) % 8)) and the weight codes as 64-byte halves
+// (area [128][64], chunk c of row r at slot c ^ ((r / 4) % 4)); the swizzles keep the
+// fragment reads of 16 (bf16) or 32 (codes) consecutive rows on distinct banks. Each wave
+// dequantizes its own A fragments from the codes straight into registers, bf16(fl(q s)) with
+// the row's group scale held in a register (a 64-code run starting at a multiple of 64 of
+// the flat index lies in one 256-element group). Two buffers of each operand (80 KiB, two
+// workgroups per CU); every stage issues the next stage's codes, scales and activations after
+// its barrier, so waiting for the current stage needs nothing else in flight.
+struct Fwd64 {
+  static constexpr int BK = 64;
+  static constexpr int BROWS = 256, WROWS = 128;
+  static constexpr int B_BYTES = BROWS * BK * 2;    // 32 KiB
+  static constexpr int C_BYTES = WROWS * BK;        // 8 KiB
+  static constexpr int NIB = B_BYTES / 1024 / 4;    // activation loads per wave (eight)
+  static constexpr int NIC = C_BYTES / 1024 / 4;    // code loads per wave (two)
+  const uint16_t* act;
+  const int8_t* q;
+  rsrc_t rsc;
+  uint32_t ld, t_end, m_end, w0;
+  uint32_t vb[NIB], vc[NIC];
+
+  __device__ Fwd64(const uint16_t* act_, const int8_t* q_, const float* sc_, int64_t ld_,
+                   int64_t t_end_, int64_t m_end_, int t0, int w0_)
+      : act(act_), q(q_), ld((uint32_t)ld_), t_end((uint32_t)t_end_), m_end((uint32_t)m_end_),
+        w0((uint32_t)w0_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsc = make_rsrc(sc_, (uint32_t)(((m_end_ * ld_ + kGroup - 1) / kGroup) * 4));
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) {
+      const int row = 8 * (NIB * wave + i) + lane / 8;
+      const int chunk = (lane % 8) ^ ((row >> 1) & 7);
+      const uint32_t rg = t0 + row;
+      vb[i] = rg < t_end ? (rg * ld + 8 * chunk) * 2 : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < NIC; ++i) {
+      const int row = 16 * (NIC * wave + i) + lane / 4;
+      const int chunk = (lane % 4) ^ ((row >> 2) & 3);
+      const uint32_t rg = w0 + row;
+      vc[i] = rg < m_end ? rg * ld + 16 * chunk : kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0_, uint32_t btile, uint32_t carea) const {
+    const int wave = threadIdx.x >> 6;
+    const uint32_t k0 = (uint32_t)k0_;
+    const v4i32 sq = rsrc_words(q + k0, m_end * ld - k0);
+#pragma unroll
+    for (int i = 0; i < NIC; ++i) dma16(sq, vc[i], carea + (NIC * wave + i) * 1024);
+    const v4i32 sa = rsrc_words(act + k0, (t_end * ld - k0) * 2);
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) dma16(sa, vb[i], btile + (NIB * wave + i) * 1024);
+  }
+  __device__ __forceinline__ float scale(int row, int64_t k0) const {
+    const uint32_t rg = w0 + row;
+    return bloadf(rsc, rg < m_end ? ((rg * ld + (uint32_t)k0) >> 8) * 4 : kOOB);
+  }
+  // bf16 of K values kk .. kk + 7 of weight row `row` (kk a multiple of 8)
+  __device__ __forceinline__ bf16x8 afrag(const uint8_t* area, int row, int kk, float s) const {
+    const int off = row * BK + 16 * ((kk >> 4) ^ ((row >> 2) & 3)) + 8 * ((kk >> 3) & 1);
+    return __builtin_bit_cast(bf16x8, dequant8_int8(*reinterpret_cast<const uint2*>(area + off), s));
+  }
+  // K values kk .. kk + 7 of activation row `row`
+  __device__ __forceinline__ bf16x8 bfrag(const uint16_t* tile, int row, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + row * BK + 8 * ((kk >> 3) ^ ((row >> 1) & 7)));
+  }
+};
+
+template <class T>
+__device__ __forceinline__ void gemm_kloop_fwd64(const Fwd64& st, int64_t K, uint16_t* lds,
+                                                 f32x16 (&acc)[T::XM][T::XN]) {
+  static_assert(T::BM == Fwd64::WROWS && T::BN == Fwd64::BROWS, "tile edges");
+  constexpr int BK = Fwd64::BK;
+  const int lane = threadIdx.x & 63;
+  const int am = wave_m<T>() * T::WTM, bn = wave_n<T>() * T::WTN;
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+    for (int y = 0; y < T::XN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  const int nk = (int)(K / BK);
+  if (nk <= 0) return;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + 2 * Fwd64::B_BYTES;
+  const uint32_t base = lds_addr(lds);
+  const uint32_t cbase = lds_addr(reinterpret_cast<const uint16_t*>(codes));
+  float sc_next[T::XM], sc[T::XM];
+#pragma unroll
+  for (int x = 0; x < T::XM; ++x) sc_next[x] = st.scale(am + 32 * x + (lane & 31), 0);
+  st.issue(0, base, cbase);
+  for (int k0 = 0; k0 < nk; k0 += 2) {
+    static_for<2>([&](auto dc) {
+      constexpr int buf = decltype(dc)::value;
+      const int j = k0 + buf;
+      if (j < nk) {
+        wait_vm_lds<0>();
+        barrier_nofence();
+#pragma unroll
+        for (int x = 0; x < T::XM; ++x) sc[x] = sc_next[x];
+        if (j + 1 < nk) {
+          const int64_t kn = (int64_t)(j + 1) * BK;
+#pragma unroll
+          for (int x = 0; x < T::XM; ++x) sc_next[x] = st.scale(am + 32 * x + (lane & 31), kn);
+          st.issue(kn, base + (buf ^ 1) * Fwd64::B_BYTES, cbase + (buf ^ 1) * Fwd64::C_BYTES);
+        }
+        const uint16_t* Bs = lds + buf * (Fwd64::B_BYTES / 2);
+        const uint8_t* area = codes + buf * Fwd64::C_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 16) {
+          bf16x8 a[T::XM], b[T::XN];
+#pragma unroll
+          for (int x = 0; x < T::XM; ++x)
+            a[x] = st.afrag(area, am + 32 * x + (lane & 31), ks + 8 * (lane >> 5), sc[x]);
+#pragma unroll
+          for (int y = 0; y < T::XN; ++y)
+            b[y] = st.bfrag(Bs, bn + 32 * y + (lane & 31), ks + 8 * (lane >> 5));
+#pragma unroll
+          for (int x = 0; x < T::XM; ++x)
+#pragma unroll
+            for (int y = 0; y < T::XN; ++y)
+              acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+      }
+    });
+  }
+  __syncthreads();
+}
+
 // W [o][i] read by columns (data gradient: tile rows are K = o, tile columns i0 .. i0 + 127;
 // n % 128 == 0, so that a row's 128 codes lie in one group). K-major tile [32][128]
 // (kmaj_slot layout).
@@ -348,6 +481,24 @@ __global__ __launch_bounds__(kThreads, 2) void qg_lin_fwd_dma(LinArgs a) {
   store_bf16_transposed<T>(a.out, a.T, a.m, a.m, i0, j0, acc, lds);
 }
 
+// Forward by 64-K stages (n % 128 == 0): the tile is Y^T (weight rows o x tokens t) = W~ X^T.
+constexpr int lin_fwd64_lds_bytes() {
+  return cmax_i_(2 * Fwd64::B_BYTES + 2 * Fwd64::C_BYTES, 4 * LinFwdTileD::WTN * 40 * 2);
+}
+static_assert(lin_fwd64_lds_bytes() <= 80 * 1024, "two workgroups per CU");
+
+__global__ __launch_bounds__(kThreads, 2) void qg_lin_fwd64(LinArgs a) {
+  using T = LinFwdTileD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[lin_fwd64_lds_bytes() / 2];
+  const int local = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles_m = (int)((a.m + T::BM - 1) / T::BM);
+  const int i0 = (local % tiles_m) * T::BM, j0 = (local / tiles_m) * T::BN;
+  const Fwd64 st(a.act, a.Wq, a.Ws, a.n, a.T, a.m, j0, i0);
+  f32x16 acc[T::XM][T::XN];
+  gemm_kloop_fwd64<T>(st, a.n, lds, acc);
+  store_bf16_transposed<T>(a.out, a.T, a.m, a.m, i0, j0, acc, lds);
+}
+
 // Data gradient by DMA (n % 128 == 0): the tile is dX^T (inputs i x tokens t) = W~^T dY^T.
 __global__ __launch_bounds__(kThreads, 2) void qg_lin_bwd_data_dma(LinArgs a) {
   using T = LinBwdDataTileD;
@@ -371,7 +522,9 @@ hipError_t launch_linear(const LinArgs& a, int which, hipStream_t s) {
   const int64_t wside = which == kLinFwd ? a.m : a.n;
   const int grid_dma =
       (int)(((wside + kLinTileM - 1) / kLinTileM) * ((a.T + kLinTileN - 1) / kLinTileN));
-  if (which == kLinFwd && lin_fwd_dma(a.n))
+  if (which == kLinFwd && lin_fwd_rows(a.n))
+    hipLaunchKernelGGL(qg_lin_fwd64, dim3(grid_dma), dim3(kThreads), 0, s, a);
+  else if (which == kLinFwd && lin_fwd_dma(a.n))
     hipLaunchKernelGGL(qg_lin_fwd_dma, dim3(grid_dma), dim3(kThreads), 0, s, a);
   else if (which == kLinFwd)
     hipLaunchKernelGGL(qg_lin_fwd, dim3(grid), dim3(kThreads), 0, s, a);
