@@ -1,7 +1,8 @@
 """Parity at full LLaMA-7B size in the launch configuration the benchmark times: one grouped
 plan over all 224 layers. Sampled layers (one of each shape) are checked against the oracle:
 the projected gradient R and the requantized moments in full, the back-projection and the
-stochastic rounding on sampled weight rows."""
+stochastic rounding on sampled weight rows. Step 1 starts from zero moments; step 3 runs on
+the moments two earlier steps with other gradients left (INT8 codes with real scales)."""
 import numpy as np
 import pytest
 
@@ -66,4 +67,35 @@ def test_full_7b_plan_sampled_layers(key):
                    Mq=Lt.Mq.cpu().numpy(), Ms=Lt.Ms.cpu().numpy(), Vq=Lt.Vq.cpu().numpy(),
                    Vs=Lt.Vs.cpu().numpy())
         PAR.check_step(st0, res, st, out, rows=rows)
+
+    # Steps 2 and 3 on fresh gradients, so that the moments hold INT8 codes with real group
+    # scales: step 3 is checked from the state the GPU left after step 2.
+    for t in (2, 3):
+        for k, L in enumerate(cfg.layers):
+            layers[k].G.copy_(WL.gradient_bf16_device(cfg, L, t, device=dev))
+        if t == 3:
+            for k in SAMPLED:
+                Lt = layers[k]
+                before[k] = dict(G=Lt.G.view(torch.int16).cpu().numpy().view(np.uint16),
+                                 W=Lt.Wq.cpu().numpy(), Mq=Lt.Mq.cpu().numpy(),
+                                 Ms=Lt.Ms.cpu().numpy(), Vq=Lt.Vq.cpu().numpy(),
+                                 Vs=Lt.Vs.cpu().numpy())
+        plan.step(t, WL.SR_SEED)
+    torch.cuda.synchronize()
+    for k in SAMPLED:
+        L = cfg.layers[k]
+        b = before[k]
+        assert np.abs(b["Mq"]).max() > 1 and np.abs(b["Ms"]).max() > 0
+        Pq_o, Ps_o = O.quantize_proj(Ps_float[k])
+        st = O.LayerState(L.m, L.n, r, L.layer_id, b["W"].copy(), WL.weight_scales(cfg, L),
+                          Pq_o, Ps_o, b["Mq"].copy(), b["Ms"].copy(), b["Vq"].copy(),
+                          b["Vs"].copy())
+        st0 = st.copy()
+        rows = np.sort(rng.choice(L.m, size=48, replace=False))
+        res = O.qgalore_step(st, b["G"], 3, WL.SR_SEED, rows=rows)
+        Lt = layers[k]
+        out = dict(R=Rs[k].cpu().numpy(), U=Us[k].cpu().numpy(), Wq=Lt.Wq.cpu().numpy(),
+                   Mq=Lt.Mq.cpu().numpy(), Ms=Lt.Ms.cpu().numpy(), Vq=Lt.Vq.cpu().numpy(),
+                   Vs=Lt.Vs.cpu().numpy())
+        PAR.check_step(st0, res, st, out, rows=rows, t=3)
     plan.close()

@@ -84,11 +84,51 @@ def test_an_oracle_update_that_is_not_the_rounding_of_its_n_is_rejected():
         PAR.explained_n_flips(N_o, Nb_o, N_o, Nb_bad, P, 0.25)
 
 
-def test_too_many_flips_are_rejected():
-    N_o, P = _case(r=64, n=256)             # 16384 elements: the cap allows one flip
+def _flips_at_midpoints(count, r=64, n=256):
+    N_o, P = _case(r=r, n=n)
     N_g = N_o.copy()
-    for (i, j) in ((1, 1), (2, 2)):
+    for k in range(count):
+        i, j = k % r, (7 * k) % n
         below, above = _midpoint_pair(N_o[i, j])
         N_o[i, j], N_g[i, j] = below, above
+    return N_g, N_o, P
+
+
+def test_expected_flips_follow_the_n_difference():
+    """E counts min(1, delta / u): a difference of a quarter of the bf16 spacing at every
+    element expects a quarter of the elements to flip, and that many are accepted."""
+    rng = np.random.default_rng(3)
+    N_o = O.bf16_round((rng.standard_normal((64, 256)) * 1e-3).astype(F32))
+    u = PAR._bf16_spacing(N_o)
+    shift = rng.uniform(-0.5, 0.5, N_o.shape) * u      # positions inside each bf16 cell
+    N_o = (N_o + shift).astype(F32)
+    N_g = (N_o + 0.25 * u).astype(F32)
+    E = PAR.expected_n_flips(N_g, N_o)
+    assert abs(E / N_o.size - 0.25) < 0.01
+    flips = int((O.bf16_round(N_g) != O.bf16_round(N_o)).sum())
+    assert abs(flips - E) < 5 * np.sqrt(E)
+    P = _case(r=64, n=256)[1]
+    PAR.explained_n_flips(N_g, O.bf16_round(N_g), N_o, O.bf16_round(N_o), P, 0.25)
+
+
+def test_a_few_explained_flips_are_accepted():
+    N_g, N_o, P = _flips_at_midpoints(3)
+    PAR.explained_n_flips(N_g, O.bf16_round(N_g), N_o, O.bf16_round(N_o), P, 0.25)
+
+
+def test_more_flips_than_the_n_difference_explains_are_rejected():
+    """Ten flips, each next to a midpoint, with differences of 4e-7 of N: the differences
+    expect about 1e-3 flips in all, so ten point to misplaced boundaries."""
+    N_g, N_o, P = _flips_at_midpoints(10)
+    assert PAR.expected_n_flips(N_g, N_o) < 0.01
     with pytest.raises(AssertionError, match="another bf16 value"):
         PAR.explained_n_flips(N_g, O.bf16_round(N_g), N_o, O.bf16_round(N_o), P, 0.25)
+
+
+def test_fp32_accumulation_rule():
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal((32, 64))
+    PAR.assert_fp32_accumulation(ref * (1 + 1e-6 * rng.standard_normal(ref.shape)), ref, "R")
+    low = O.bf16_round(ref.astype(F32))             # one bf16 rounding of every element
+    with pytest.raises(AssertionError, match="rms difference"):
+        PAR.assert_fp32_accumulation(low, ref, "R")
