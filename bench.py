@@ -459,27 +459,15 @@ def copy_bandwidth(torch, gib=2.0, reps=5):
     ms = e0.elapsed_time(e1) / reps
     # a read-only pass (a sum over the source) and a write-only one (a fill of the
     # destination) of the same size: the second and third kernels of known traffic that the
-    # counters' calibration is checked on
+    # counters' calibration is checked on (not timed: torch's sum makes more than one pass)
     src32 = src.view(torch.int32)
-    src32.sum()
-    torch.cuda.synchronize()
-    e0.record()
     for _ in range(reps):
         src32.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_read = e0.elapsed_time(e1) / reps
-    e0.record()
-    for _ in range(reps):
         dst.fill_(2)
-    e1.record()
     torch.cuda.synchronize()
-    ms_write = e0.elapsed_time(e1) / reps
     del src, dst, src32
     torch.cuda.empty_cache()
-    return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1),
-                read_gbs=round(n / (ms_read / 1e3) / 1e9, 1),
-                write_gbs=round(n / (ms_write / 1e3) / 1e9, 1))
+    return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1))
 
 
 def mfma_sustained(torch, B, grid=1024, iters=2000, reps=3):
@@ -754,8 +742,6 @@ def main():
                                     "kernel_ms", "optimizer_ms", "refresh_tests_per_step",
                                     "cossim_ms", "roofline")},
         "copy_gbs": copy["gbs"] if copy else None,
-        "hbm_read_gbs": copy["read_gbs"] if copy else None,
-        "hbm_write_gbs": copy["write_gbs"] if copy else None,
         "mfma_sustained": sustained,
     }
     if "library_gemm" in main_res:
