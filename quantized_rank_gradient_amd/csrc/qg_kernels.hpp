@@ -135,7 +135,8 @@ constexpr int rf_bj_block(int k) { return k >= kRfJacobiBlockSwitch ? 32 : 16; }
 // Blocks of the padded problem: ceil(k / B) rounded up to an even count.
 constexpr int rf_bj_blocks(int k, int B) { return (k + 2 * B - 1) / (2 * B) * 2; }
 // Device buffers of the block Jacobi solver for K = B * rf_bj_blocks(k, B), B = rf_bj_block(k):
-// C and V (fp64 K x K), J (fp64, K / 2B pieces of 2B x 2B), jrot (K / 2B), abs_tol (1), rot
+// C and V (fp64 K x K), J (fp64, K / 2B pieces of 2B x 2B, each the transpose of the round's
+// rotation product of one pair of blocks), jrot (K / 2B), abs_tol (1), rot
 // (max_sweeps), rank_of (k).
 struct RfBj {
   double* C;

@@ -296,183 +296,225 @@ __device__ __forceinline__ bool bj_needs(float app, float aqq, float apq, float 
   return fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
 }
 
-// Threads of the subproblem kernel for blocks of B indices: one Q row pair update of four
-// rows per thread.
+// Threads of the subproblem kernel for blocks of B indices: two 2 x 2 blocks of the
+// subproblem and four rows of a pair slot of Q per thread.
 template <int B>
 constexpr int bj_solve_threads() { return B * 2 * B / 4; }
 
-// One workgroup per pair of blocks: the 2B x 2B subproblem S of C (as fp32), one sweep of
-// 2 x 2 rotations on it, S <- R^T S R and Q <- Q R from Q = I; then Q (fp64) goes to Jm[w]
-// and whether it differs from I to jrot[w].
+// The symmetric 2 x 2 Schur rotation (Golub and Van Loan, Algorithm 8.5.1) of the pair whose
+// smaller index holds app, the larger aqq and the pair apq, in fp32, with (c, s) also in fp64
+// scaled to unit length: h = c^2 + s^2 is 1 to fp32 accuracy, and 1.5 - h / 2 is 1 / sqrt(h)
+// up to (h - 1)^2. The identity when the pair is below the rotation level.
+__device__ __forceinline__ bool bj_rotation(float app, float aqq, float apq, float tol,
+                                            float abs_tol, float& c, float& s, double& cd,
+                                            double& sd) {
+  c = 1.0f;
+  s = 0.0f;
+  cd = 1.0;
+  sd = 0.0;
+  if (!bj_needs(app, aqq, apq, tol, abs_tol)) return false;
+  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.0f * apq);
+  const float t = (tau >= 0.0f ? 1.0f : -1.0f) *
+                  __builtin_amdgcn_rcpf(fabsf(tau) + sqrtf(1.0f + tau * tau));
+  c = __builtin_amdgcn_rsqf(1.0f + t * t);
+  s = t * c;
+  const double h = (double)c * c + (double)s * s;
+  const double g = 1.5 - 0.5 * h;
+  cd = c * g;
+  sd = s * g;
+  return true;
+}
+
+// Where the indices of a 2B x 2B subproblem sit during its sweep. The B pair slots of an inner
+// round are fixed positions (2u, 2u + 1) of the stored matrices; between inner rounds the
+// entries move to the positions their indices take in the next round, so that every access
+// of the sweep is at an address fixed for the thread.
+//   FULL (all index pairs, 2B - 1 inner rounds): the round-robin ("circle") schedule with index
+//   0 fixed; slot u pairs a_u = (u == 0 ? 0 : 1 + (u - 1 + rd) mod (2B - 1)) with
+//   b_u = 1 + (2B - 2 - u + rd) mod (2B - 1).
+//   Cross (the B^2 pairs across the two blocks, B inner rounds): slot u pairs index u with
+//   B + (u + rd) mod B.
+// Either schedule returns every index to its first position after its last round.
+template <int B, bool FULL>
+struct BjSched {
+  static constexpr int S = 2 * B;
+  static constexpr int ROUNDS = FULL ? S - 1 : B;
+  // index held at position pos in the first inner round
+  __device__ static int index0(int pos) {
+    const int u = pos >> 1;
+    return (pos & 1) ? (FULL ? S - 1 - u : B + u) : u;
+  }
+  // position of index j in the first inner round
+  __device__ static int pos0(int j) {
+    return j < B ? 2 * j : (FULL ? 2 * (S - 1 - j) + 1 : 2 * (j - B) + 1);
+  }
+  // position that the entry at pos moves to for the next inner round
+  __device__ static int next(int pos) {
+    const int u = pos >> 1;
+    if (!FULL) return (pos & 1) ? 2 * ((u + B - 1) & (B - 1)) + 1 : pos;
+    if (pos & 1) return u == B - 1 ? 2 * (B - 1) : 2 * (u + 1) + 1;
+    return u <= 1 ? u : 2 * (u - 1);   // p(0) stays, p(1) -> q(0), p(u) -> p(u - 1)
+  }
+  // whether slot u's first position (2u) holds the larger index of its pair in round rd
+  __device__ static bool flipped(int u, int rd) {
+    if (!FULL) return false;
+    const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (S - 1);
+    const int b = 1 + (S - 2 - u + rd) % (S - 1);
+    return a > b;
+  }
+};
+
+// One sweep of 2 x 2 rotations on the 2B x 2B subproblem of a pair of blocks (the workgroup's
+// pair in this round of the tournament on blocks): S <- R^T S R and Q <- Q R from Q = I, S
+// held as fp32 and Q as fp64. Q^T goes to Jm[w] (row j of Jm[w] is column j of Q), whether Q
+// differs from I to jrot[w], and a rotation taken to rot[sweep].
 //
 // In the first round of an outer sweep every block is in exactly one subproblem, and the
-// sweep there covers all index pairs of the subproblem (2B - 1 inner rounds of a round-robin
-// on its 2B indices). In the other rounds it covers only the B^2 pairs across the two blocks
-// (B inner rounds: index i of the first block with index (i + t) mod B of the second), since
-// the pairs inside a block were treated in the first round: every index pair of C is thus
-// rotated once per outer sweep, as in cyclic Jacobi.
+// sweep covers all index pairs of the subproblem; in the other rounds only the pairs across
+// its two blocks, since the pairs inside a block were treated in the first round: every index
+// pair of C is thus rotated once per outer sweep, as in cyclic Jacobi.
 //
-// Only the upper triangle of S is kept (entry (i, j) at (min, max)), updated 2 x 2 block by
-// 2 x 2 block: block (u1, u2), u1 <= u2, holds rows p1, q1 of pair slot u1 and columns p2, q2
-// of slot u2, and every stored entry lies in exactly one such block. Each thread keeps the
-// same blocks, and the same pair slot of Q with four of its rows, in every inner round; the
-// pairs of each inner round come from a table. A round is the rotation parameters of the B
-// slots, a barrier, the updates (all reads issued before any write), and a barrier. A
-// subproblem with no pair over the rotation level is left as it is.
+// The subproblem is stored whole (both triangles) in position order (BjSched) in one of two
+// buffers, and so is Q^T (row = position, column = row of Q). An inner round reads only the
+// current buffers and writes only the other: each thread computes the rotations of the slots
+// it needs from the diagonal 2 x 2 blocks, rotates its two 2 x 2 blocks and its four rows of a
+// slot of Q, and writes them where their indices sit in the next round; one barrier ends the
+// round. A block is computed with the rows of its lower slot rotated first, so both copies of
+// an entry agree exactly. A subproblem with no pair over the rotation level is left as it is.
+template <int B, bool FULL>
+__device__ __forceinline__ void bj_solve_sweep(const double* Cj, int K, int lo, int hi,
+                                               float tol, float abs_tol, float* As, double* Qs,
+                                               int* need, double* out, bool& active) {
+  using Sch = BjSched<B, FULL>;
+  constexpr int S = 2 * B, NT = bj_solve_threads<B>(), PA = S + 16, H = B / 2;
+  const int t = threadIdx.x;
+  for (int e = t; e < S * S; e += NT) {
+    const int P = e / S, P2 = e % S;
+    As[P * PA + P2] = (float)gload(Cj + (int64_t)bj_index<B>(lo, hi, Sch::index0(P)) * K +
+                                   bj_index<B>(lo, hi, Sch::index0(P2)));
+    Qs[P * S + P2] = Sch::index0(P) == P2 ? 1.0 : 0.0;
+  }
+  if (t == 0) *need = 0;
+  __syncthreads();
+  {
+    int mine = 0;
+    for (int e = t; e < S * S; e += NT) {
+      const int i = e / S, j = e % S;
+      const bool considered = FULL ? i < j : (i < B && j >= B);
+      if (considered) {
+        const int pi = Sch::pos0(i), pj = Sch::pos0(j);
+        if (bj_needs(As[pi * PA + pi], As[pj * PA + pj], As[pi * PA + pj], tol, abs_tol))
+          mine = 1;
+      }
+    }
+    if (mine) *need = 1;
+  }
+  __syncthreads();
+  active = *need != 0;
+  // this thread: row slot u1, column slots u2 in {l, l + H}; rows 2l, 2l + 1, B + 2l,
+  // B + 2l + 1 of Q in slot u1
+  const int u1 = t / H, l = t % H;
+  int buf = 0;
+  for (int rd = 0; active && rd < Sch::ROUNDS; ++rd) {
+    const float* Ac = As + buf * S * PA;
+    float* An = As + (buf ^ 1) * S * PA;
+    const double* Qc = Qs + buf * S * S;
+    double* Qn = Qs + (buf ^ 1) * S * S;
+    // slot rotations: lane u of every wave computes slot u's (every lane slot u mod B), and
+    // the threads take the ones they need by cross-lane reads. Flip: the slot's first
+    // position holds the larger index of its pair; pp, pq: positions of the smaller and the
+    // larger index.
+    float c_l, s_l;
+    double cd_l, sd_l;
+    int f_l;
+    {
+      const int u = (t & 63) & (B - 1);
+      const bool f = Sch::flipped(u, rd);
+      const float2 d0 = *reinterpret_cast<const float2*>(Ac + 2 * u * PA + 2 * u);
+      const float a11 = Ac[(2 * u + 1) * PA + 2 * u + 1];
+      bj_rotation(f ? a11 : d0.x, f ? d0.x : a11, d0.y, tol, abs_tol, c_l, s_l, cd_l, sd_l);
+      f_l = f ? 1 : 0;
+    }
+    bool fl[3];
+    int pp[3], pq[3];
+    float c[3], s[3];
+    const int us[3] = {u1, l, l + H};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      fl[k] = __shfl(f_l, us[k]) != 0;
+      c[k] = __shfl(c_l, us[k]);
+      s[k] = __shfl(s_l, us[k]);
+      pp[k] = 2 * us[k] + (fl[k] ? 1 : 0);
+      pq[k] = 2 * us[k] + (fl[k] ? 0 : 1);
+    }
+    const double cd = __shfl(cd_l, u1), sd = __shfl(sd_l, u1);
+    // the two blocks (u1, u2)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int u2 = us[1 + b];
+      const float2 r0 = *reinterpret_cast<const float2*>(Ac + 2 * u1 * PA + 2 * u2);
+      const float2 r1 = *reinterpret_cast<const float2*>(Ac + (2 * u1 + 1) * PA + 2 * u2);
+      // in index order: rows (smaller, larger index of u1), columns (same for u2)
+      const bool f1 = fl[0], f2 = fl[1 + b];
+      const float2 R0 = f1 ? r1 : r0, R1 = f1 ? r0 : r1;
+      const float y00 = f2 ? R0.y : R0.x, y01 = f2 ? R0.x : R0.y;
+      const float y10 = f2 ? R1.y : R1.x, y11 = f2 ? R1.x : R1.y;
+      // the lower slot's rows are rotated first (the block transposed when u2 < u1)
+      const bool rows_low = u1 <= u2;
+      const float a = y00, bb = rows_low ? y01 : y10, cc = rows_low ? y10 : y01, d = y11;
+      const float c1 = rows_low ? c[0] : c[1 + b], s1 = rows_low ? s[0] : s[1 + b];
+      const float c2 = rows_low ? c[1 + b] : c[0], s2 = rows_low ? s[1 + b] : s[0];
+      const float ra = c1 * a - s1 * cc, rb = c1 * bb - s1 * d;
+      const float rc = s1 * a + c1 * cc, rd2 = s1 * bb + c1 * d;
+      const float n_pp = c2 * ra - s2 * rb, n_pq = s2 * ra + c2 * rb;
+      const float n_qp = u1 == u2 ? n_pq : c2 * rc - s2 * rd2, n_qq = s2 * rc + c2 * rd2;
+      // back in this block's orientation (rows u1): entries (p1, p2), (p1, q2), (q1, p2),
+      // (q1, q2)
+      const float w_pq = rows_low ? n_pq : n_qp, w_qp = rows_low ? n_qp : n_pq;
+      const int np1 = Sch::next(pp[0]) * PA, nq1 = Sch::next(pq[0]) * PA;
+      const int np2 = Sch::next(pp[1 + b]), nq2 = Sch::next(pq[1 + b]);
+      An[np1 + np2] = n_pp;
+      An[np1 + nq2] = w_pq;
+      An[nq1 + np2] = w_qp;
+      An[nq1 + nq2] = n_qq;
+    }
+    // rows of Q in slot u1: column p <- cd x - sd y, column q <- sd x + cd y
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = h * B + 2 * l;
+      const double2 x = *reinterpret_cast<const double2*>(Qc + pp[0] * S + row);
+      const double2 y = *reinterpret_cast<const double2*>(Qc + pq[0] * S + row);
+      *reinterpret_cast<double2*>(Qn + Sch::next(pp[0]) * S + row) =
+          make_double2(cd * x.x - sd * y.x, cd * x.y - sd * y.y);
+      *reinterpret_cast<double2*>(Qn + Sch::next(pq[0]) * S + row) =
+          make_double2(sd * x.x + cd * y.x, sd * x.y + cd * y.y);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  // every index is back at its first position: row j of Q^T is at position pos0(j)
+  const double* Qf = Qs + buf * S * S;
+  for (int e = t; e < S * S; e += NT) gstore(out + e, Qf[Sch::pos0(e / S) * S + e % S]);
+}
+
 template <int B>
 __global__ __launch_bounds__(bj_solve_threads<B>()) void qg_rf_bj_solve(
     const double* Cj, int K, int nb, int round, int sweep, float tol, const float* abs_tol_p,
     int* rot, double* Jm, int* jrot) {
   if (bj_converged(rot, sweep)) return;
-  constexpr int S = 2 * B, PT = S + 1, NT = bj_solve_threads<B>();
-  constexpr int kFullRounds = S - 1, kCrossRounds = B;
-  __shared__ float A[S * PT];
-  __shared__ double Q[S * PT];
-  __shared__ float4 cs[B];     // c, s (fp32), rotate flag
-  __shared__ double2 csd[B];   // c, s (fp64, unit length)
-  __shared__ uint16_t pt[kFullRounds * B];   // pairs of each inner round: p | q << 8
+  constexpr int S = 2 * B, PA = S + 16;
+  __shared__ __attribute__((aligned(16))) float As[2 * S * PA];
+  __shared__ __attribute__((aligned(16))) double Qs[2 * S * S];
   __shared__ int need;
-  const bool full = round == 0;
-  const int rounds = full ? kFullRounds : kCrossRounds;
   int lo, hi;
   bj_pair(nb, round, blockIdx.x, lo, hi);
-  for (int e = threadIdx.x; e < S * S; e += NT) {
-    const int i = e / S, j = e % S;
-    A[i * PT + j] = (float)gload(Cj + (int64_t)bj_index<B>(lo, hi, i) * K + bj_index<B>(lo, hi, j));
-    Q[i * PT + j] = i == j ? 1.0 : 0.0;
-  }
-  for (int e = threadIdx.x; e < rounds * B; e += NT) {
-    const int rd = e / B, u = e % B;
-    int p, q;
-    if (full) {   // positions u and S - 1 - u of the round-robin on S indices
-      const int a = u == 0 ? 0 : 1 + (u - 1 + rd) % (S - 1);
-      const int b = 1 + (S - 2 - u + rd) % (S - 1);
-      p = min(a, b);
-      q = max(a, b);
-    } else {
-      p = u;
-      q = B + ((u + rd) & (B - 1));
-    }
-    pt[e] = (uint16_t)(p | (q << 8));
-  }
-  if (threadIdx.x == 0) need = 0;
   const float abs_tol = gload(abs_tol_p);
-  __syncthreads();
-  {
-    int mine = 0;
-    for (int e = threadIdx.x; e < S * S; e += NT) {
-      const int i = e / S, j = e % S;
-      const bool considered = full ? i < j : (i < B && j >= B);
-      if (considered && bj_needs(A[i * PT + i], A[j * PT + j], A[i * PT + j], tol, abs_tol))
-        mine = 1;
-    }
-    if (mine) need = 1;
-  }
-  __syncthreads();
-  const bool active = need != 0;
-  // this thread's 2 x 2 blocks (slot pairs u1 <= u2, by number)
-  constexpr int kBlocks = B * (B + 1) / 2;
-  constexpr int BPT = (kBlocks + NT - 1) / NT;
-  int bu1[BPT], bu2[BPT];
-#pragma unroll
-  for (int u = 0; u < BPT; ++u) {
-    int bi = threadIdx.x + u * NT, w1 = 0;
-    if (bi >= kBlocks) {
-      bu1[u] = -1;
-      bu2[u] = -1;
-      continue;
-    }
-    while (bi >= B - w1) {
-      bi -= B - w1;
-      ++w1;
-    }
-    bu1[u] = w1;
-    bu2[u] = w1 + bi;
-  }
-  // and its slot of Q with four rows
-  constexpr int QR = 4;
-  static_assert(QR * NT == B * S, "Q rows split evenly");
-  const int qw = threadIdx.x / (S / QR);
-  const int qrow = (threadIdx.x % (S / QR)) * QR;
-  for (int rd = 0; active && rd < rounds; ++rd) {
-    const uint16_t* prd = pt + rd * B;
-    if ((int)threadIdx.x < B) {
-      const int u = threadIdx.x;
-      const int pq = prd[u];
-      const int p = pq & 0xFF, q = pq >> 8;
-      const float app = A[p * PT + p], aqq = A[q * PT + q], apq = A[p * PT + q];
-      float c = 1.0f, s = 0.0f;
-      double cd = 1.0, sd = 0.0;
-      const bool go = bj_needs(app, aqq, apq, tol, abs_tol);
-      if (go) {
-        // the symmetric 2 x 2 Schur rotation (Golub and Van Loan, Algorithm 8.5.1)
-        const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.0f * apq);
-        const float t = (tau >= 0.0f ? 1.0f : -1.0f) *
-                        __builtin_amdgcn_rcpf(fabsf(tau) + sqrtf(1.0f + tau * tau));
-        c = __builtin_amdgcn_rsqf(1.0f + t * t);
-        s = t * c;
-        // in fp64, (c, s) scaled to unit length: h = c^2 + s^2 is 1 to fp32 accuracy, and
-        // 1.5 - h / 2 is 1 / sqrt(h) up to (h - 1)^2
-        const double h = (double)c * c + (double)s * s;
-        const double g = 1.5 - 0.5 * h;
-        cd = c * g;
-        sd = s * g;
-      }
-      cs[u] = make_float4(c, s, go ? 1.0f : 0.0f, 0.0f);
-      csd[u] = make_double2(cd, sd);
-    }
-    __syncthreads();
-    // reads: rotation parameters and old entries of this thread's blocks and Q rows
-    float4 r1[BPT], r2[BPT];
-    float x[BPT][4];
-    int o[BPT][4];
-#pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-      if (bu1[u] < 0) continue;
-      const int pq1 = prd[bu1[u]], pq2 = prd[bu2[u]];
-      const int p1 = pq1 & 0xFF, q1 = pq1 >> 8, p2 = pq2 & 0xFF, q2 = pq2 >> 8;
-      o[u][0] = min(p1, p2) * PT + max(p1, p2);
-      o[u][1] = min(p1, q2) * PT + max(p1, q2);
-      o[u][2] = min(q1, p2) * PT + max(q1, p2);
-      o[u][3] = min(q1, q2) * PT + max(q1, q2);
-      r1[u] = cs[bu1[u]];
-      r2[u] = cs[bu2[u]];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[u][e] = A[o[u][e]];
-    }
-    const int qpq = prd[qw];
-    const int qp = qrow * PT + (qpq & 0xFF), qq = qrow * PT + (qpq >> 8);
-    const double2 qcs = csd[qw];
-    double qx[QR], qy[QR];
-#pragma unroll
-    for (int v = 0; v < QR; ++v) {
-      qx[v] = Q[qp + v * PT];
-      qy[v] = Q[qq + v * PT];
-    }
-    // writes: only blocks and rows touched by a rotation change
-#pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-      if (bu1[u] < 0 || (r1[u].z == 0.0f && r2[u].z == 0.0f)) continue;
-      const float c1 = r1[u].x, s1 = r1[u].y, c2 = r2[u].x, s2 = r2[u].y;
-      const float a = x[u][0], bb = x[u][1], c = x[u][2], d = x[u][3];
-      const float ra = c1 * a - s1 * c, rb = c1 * bb - s1 * d;
-      const float rc = s1 * a + c1 * c, rd2 = s1 * bb + c1 * d;
-      A[o[u][0]] = c2 * ra - s2 * rb;
-      A[o[u][1]] = s2 * ra + c2 * rb;
-      if (bu1[u] != bu2[u]) A[o[u][2]] = c2 * rc - s2 * rd2;
-      A[o[u][3]] = s2 * rc + c2 * rd2;
-    }
-    if (cs[qw].z != 0.0f) {
-#pragma unroll
-      for (int v = 0; v < QR; ++v) {
-        Q[qp + v * PT] = qcs.x * qx[v] - qcs.y * qy[v];
-        Q[qq + v * PT] = qcs.y * qx[v] + qcs.x * qy[v];
-      }
-    }
-    __syncthreads();
-  }
   double* out = Jm + (int64_t)blockIdx.x * S * S;
-  for (int e = threadIdx.x; e < S * S; e += NT) gstore(out + e, Q[(e / S) * PT + e % S]);
+  bool active;
+  if (round == 0)
+    bj_solve_sweep<B, true>(Cj, K, lo, hi, tol, abs_tol, As, Qs, &need, out, active);
+  else
+    bj_solve_sweep<B, false>(Cj, K, lo, hi, tol, abs_tol, As, Qs, &need, out, active);
   if (threadIdx.x == 0) {
     gstore(jrot + blockIdx.x, active ? 1 : 0);
     if (active) gstore(rot + sweep, 1);
@@ -541,15 +583,17 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
                                                            const double* Jm, const int* jrot) {
   if (bj_converged(rot, sweep)) return;
   constexpr int S = 2 * B, PT = S + 1;
+  // two buffers (two workgroups fit on a CU): X, and J1 then J2
   __shared__ double X[S * PT];
   __shared__ double J1[S * PT];
-  __shared__ double J2[S * PT];
+  double* J2 = J1;
   const int P = nb / 2;
   const int nC = P * (P + 1) / 2;
   int bid = blockIdx.x;
+  // Jm[w] holds J^T (row j = column j of J)
   auto load_j = [&](double* dst, int w) {
     const double* src = Jm + (int64_t)w * S * S;
-    for (int e = threadIdx.x; e < S * S; e += kThreads) dst[(e / S) * PT + e % S] = gload(src + e);
+    for (int e = threadIdx.x; e < S * S; e += kThreads) dst[(e % S) * PT + e / S] = gload(src + e);
   };
   BjMul<B> m;
   if (bid < nC) {
@@ -569,11 +613,11 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
           gload(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K + bj_index<B>(lo2, hi2, j));
     }
     load_j(J1, w1);
-    load_j(J2, w2);
     __syncthreads();
     m.template mul<true>(J1, X);   // J1^T X
     __syncthreads();
     m.put(X);
+    load_j(J2, w2);
     __syncthreads();
     m.template mul<false>(X, J2);   // (J1^T X) J2
     __syncthreads();
