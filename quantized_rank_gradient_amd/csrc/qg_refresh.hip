@@ -159,150 +159,219 @@ __global__ __launch_bounds__(kThreads) void qg_rf_sum(const float* part, int chu
 // ============================================================ Cholesky and inverse ===
 // One workgroup: W (k x k Gram matrix) + shift_rel * trace(W) / k on the diagonal = L L^T,
 // then Wt = L^-T (upper triangular, k x k row-major), so that an orthonormal basis is
-// Q = Y Wt. The matrix lives in registers: thread (ty, tx) of a 16 x 16 grid holds the
-// entries (ty + 16a, tx + 16b). Elimination step j (right-looking, no square roots inside
-// the loop): the holders of column j publish it through LDS, then every thread subtracts
-// a_ij a_lj / a_jj from its trailing entries. A pivot below a tiny floor (a rank-deficient
-// basis) is raised to it, which leaves that direction out. The inverse X = L^-1 is formed
-// the same way from the identity: step j divides row j by l_jj and subtracts l_ij times it
-// from the rows below.
-constexpr int kRfNb = (kRfMaxK + 15) / 16;   // register rows / columns per thread
+// Q = Y Wt. Blocked in 16 x 16 blocks (the matrix padded with the identity to a multiple of
+// 16, in LDS), right-looking (Golub and Van Loan, Section 4.2, block Cholesky):
+//   for each block column jb: 16 lanes of one wave, a column each in registers, factor the
+//   diagonal block (elimination without square roots inside the loop: step j subtracts
+//   a_ij a_lj / a_jj from the trailing entries, a pivot below a tiny floor, a rank-deficient
+//   basis, raised to it so that the direction is left out), scale it to L_jj and invert it
+//   (D_jb = L_jj^-1, forward substitution by columns); all threads then form the panel
+//   L_ib,jb = A_ib,jb D_jb^T and subtract L_ib,jb L_kb,jb^T from the trailing blocks.
+// The inverse X = L^-1 follows by block rows: X_ib,jb = -D_ib sum_{jb <= kb < ib} L_ib,kb
+// X_kb,jb, with X stored transposed in the upper triangle of A (the diagonal blocks D_jb^T
+// written there by the factorization), where Wt = X^T reads it in place.
+constexpr int kRfNb = (kRfMaxK + 15) / 16;   // 16 x 16 blocks per edge
+constexpr int kRfCholP = kRfNb * 16 + 1;     // LDS row pitch (odd: column reads hit distinct banks)
+// The sums T_jb of one block row of the inverse (one 16 x 17 block per column block).
+constexpr int kRfYBuf = (kRfNb - 1) * 16 * 17;
+
+// Value of v in lane `l` (uniform) of the wave.
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
 __global__ __launch_bounds__(kThreads) void qg_rf_chol_inv(const float* W, int k,
                                                            float shift_rel, float* Wt) {
-  constexpr int NB = kRfNb;
-  __shared__ float colv[kRfMaxK];
-  __shared__ float rowv[kRfMaxK];
-  __shared__ float piv[kRfMaxK];
+  constexpr int NB = kRfNb, PA = kRfCholP, KP = NB * 16;
+  __shared__ float A[KP * PA];
+  __shared__ float D[NB][16 * 17];          // D_jb = L_jj^-1, pitch 17
+  __shared__ float P[KP * 17];              // panel of the current block column
+  __shared__ float Ybuf[kRfYBuf];           // block-row sums of the inverse
   __shared__ float red[kThreads];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float R[NB][NB];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // block products: 16 blocks at a time, 16 threads each with a 4 x 4 patch (rows pr ..
+  // pr + 3, columns pc .. pc + 3)
+  const int blk = t >> 4, pr = ((t >> 2) & 3) * 4, pc = (t & 3) * 4;
+  const int nb = (k + 15) / 16;
+  const int kp = nb * 16;
   float tr_part = 0.0f;
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int i = ty + 16 * a, l = tx + 16 * b;
-      R[a][b] = (i < k && l < k) ? gload(W + i * k + l) : 0.0f;
-      if (i == l && i < k) tr_part += R[a][b];
-    }
-  red[threadIdx.x] = tr_part;
+  for (int e = t; e < kp * kp; e += kThreads) {
+    const int i = e / kp, l = e % kp;
+    const float v = (i < k && l < k) ? gload(W + i * k + l) : (i == l ? 1.0f : 0.0f);
+    A[i * PA + l] = v;
+    if (i == l && i < k) tr_part += v;
+  }
+  red[t] = tr_part;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     float tr = 0.0f;
-    for (int t = 0; t < kThreads; ++t) tr += red[t];
+    for (int q = 0; q < kThreads; ++q) tr += red[q];
     red[0] = shift_rel * tr / (float)k;
   }
   __syncthreads();
   const float shift = red[0];
   const float floor_piv = fmaxf(shift, 1e-30f);
+  for (int i = t; i < k; i += kThreads) A[i * PA + i] += shift;
+  __syncthreads();
+
+  for (int jb = 0; jb < nb; ++jb) {
+    const int b0 = jb * 16;
+    if (wave == 0 && lane < 16) {
+      // the diagonal block in registers, lane c holding its column c (both triangles: the
+      // trailing updates keep the block symmetric); pivots and columns reach the other
+      // lanes by lane reads
+      const int c = lane;
+      float a[16];
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+      for (int x = 0; x < 16; ++x) a[x] = A[(b0 + x) * PA + b0 + c];
+      float dc = 1.0f;   // this lane's (floored) pivot
+      // unscaled elimination: step j subtracts a_xj a_jc / d_j from the trailing entries
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (ty + 16 * a == tx + 16 * b) R[a][b] += shift;
-  // ---- Cholesky (unscaled): after step j, column j holds l_ij * l_jj. Steps run as
-  // j = 16 jb + jj with the register block jb a compile-time index.
-  static_for<NB>([&](auto jbc) {
-    constexpr int jb = decltype(jbc)::value;
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * jb + jj;
-      if (j >= k) break;   // uniform across the workgroup
-      if (tx == jj) {
+      for (int j = 0; j < 16; ++j) {
+        float d = lane_read(a[j], j);
+        d = d > floor_piv ? d : floor_piv;
+        if (c == j) dc = d;
+        const float inv = 1.0f / d;
+        const float ajc = a[j];
 #pragma unroll
-        for (int a = 0; a < NB; ++a) {
-          const int i = ty + 16 * a;
-          if (i >= j && i < k) colv[i] = R[a][jb];
+        for (int x = j + 1; x < 16; ++x) {
+          const float axj = lane_read(a[x], j) * inv;
+          if (c > j) a[x] = __builtin_fmaf(-axj, ajc, a[x]);
         }
       }
-      __syncthreads();
-      float d2 = colv[j];
-      d2 = d2 > floor_piv ? d2 : floor_piv;
-      if (threadIdx.x == 0) piv[j] = d2;
-      const float inv = 1.0f / d2;
-      float cl[NB];
+      // column c of L_jj: the unscaled column over sqrt(pivot), sqrt(pivot) on the diagonal
+      const float dl = sqrtf(dc);
 #pragma unroll
-      for (int b = jb; b < NB; ++b) {
-        const int l = tx + 16 * b;
-        cl[b] = (l > j && l < k) ? colv[l] : 0.0f;
+      for (int x = 0; x < 16; ++x) a[x] = x < c ? 0.0f : (x == c ? dl : a[x] / dl);
+      // D_jb = L_jj^-1, column c: forward substitution with the rows of L_jj read from
+      // their lanes; also stored transposed in the diagonal block of A (row c of D_jb^T),
+      // where the inverse below reads X^T
+      float xv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = i == c ? 1.0f : 0.0f;
+#pragma unroll
+        for (int q = 0; q < i; ++q) acc = __builtin_fmaf(-lane_read(a[i], q), xv[q], acc);
+        xv[i] = i < c ? 0.0f : acc / lane_read(a[i], i);
+        D[jb][i * 17 + c] = xv[i];
+        A[(b0 + c) * PA + b0 + i] = xv[i];
       }
-#pragma unroll
-      for (int a = jb; a < NB; ++a) {
-        const int i = ty + 16 * a;
-        const float aij = (i > j && i < k) ? colv[i] * inv : 0.0f;
-#pragma unroll
-        for (int b = jb; b <= a; ++b)
-          if (tx + 16 * b <= i) R[a][b] = __builtin_fmaf(-aij, cl[b], R[a][b]);
-      }
-      __syncthreads();
     }
-  });
-  // L = (unscaled column j) / sqrt(piv_j); held in R (lower triangle), then X = L^-1 with
-  // the identity as starting point in B
-  float B[NB][NB];
+    __syncthreads();
+    // panel: P[ib rows][c] = sum_s A[ib row][b0 + s] D_jb[c][s]  (D_jb lower: s <= c); each
+    // block by 16 threads, a 4 x 4 patch each
+    for (int ib = jb + 1 + blk; ib < nb; ib += 16) {
+      float acc[4][4] = {};
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+      for (int q = 0; q < 16; ++q) {
+        float a[4], b[4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int i = ty + 16 * a, l = tx + 16 * b;
-      float v = 0.0f;
-      if (l <= i && i < k) {
-        const float dl = sqrtf(piv[l]);
-        v = i == l ? dl : R[a][b] / dl;
+        for (int i = 0; i < 4; ++i) a[i] = A[(ib * 16 + pr + i) * PA + b0 + q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = D[jb][(pc + j) * 17 + q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
       }
-      R[a][b] = v;
-      B[a][b] = (i == l && i < k) ? 1.0f : 0.0f;
-    }
-  // ---- forward elimination on [L | I]: step j scales row j of B by 1 / l_jj and subtracts
-  // l_ij times it from the rows i > j (row j of X is zero right of the diagonal)
-  static_for<NB>([&](auto jbc) {
-    constexpr int jb = decltype(jbc)::value;
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * jb + jj;
-      if (j >= k) break;
-      if (tx == jj) {   // column j of L
 #pragma unroll
-        for (int a = jb; a < NB; ++a) {
-          const int i = ty + 16 * a;
-          if (i >= j && i < k) colv[i] = R[a][jb];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P[(ib * 16 + pr + i) * 17 + pc + j] = acc[i][j];
+    }
+    __syncthreads();
+    // the panel into A; trailing blocks (ib, kb), jb < kb <= ib: A -= L_ib,jb L_kb,jb^T
+    for (int e = t; e < (nb - jb - 1) * 256; e += kThreads) {
+      const int row = (jb + 1) * 16 + e / 16;
+      A[row * PA + b0 + (e & 15)] = P[row * 17 + (e & 15)];
+    }
+    {
+      const int nt = nb - jb - 1;   // trailing block rows
+      for (int bi = blk; bi < nt * (nt + 1) / 2; bi += 16) {
+        int ib = 0, rest = bi;   // bi -> (ib, kb), kb <= ib, row-major over the triangle
+        while (rest > ib) {
+          rest -= ib + 1;
+          ++ib;
+        }
+        const int row0 = (jb + 1 + ib) * 16 + pr, col0 = (jb + 1 + rest) * 16 + pc;
+        float acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = A[(row0 + i) * PA + col0 + j];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          float a[4], b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = P[(row0 + i) * 17 + q];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[j] = P[(col0 + j) * 17 + q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(-a[i], b[j], acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) A[(row0 + i) * PA + col0 + j] = acc[i][j];
+      }
+    }
+    __syncthreads();
+  }
+
+  // X = L^-1 by block rows; X_ib,jb (ib > jb) stored transposed at A[jb block][ib block]
+  for (int ib = 1; ib < nb; ++ib) {
+    for (int jb = blk; jb < ib; jb += 16) {
+      // T_jb = sum_{jb <= kb < ib} L_ib,kb X_kb,jb  (X_jb,jb = D_jb)
+      float acc[4][4] = {};
+      for (int kb = jb; kb < ib; ++kb) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          float av[4], bv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[i] = A[(ib * 16 + pr + i) * PA + kb * 16 + q];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[j] = A[(jb * 16 + pc + j) * PA + kb * 16 + q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
         }
       }
-      __syncthreads();
-      if (ty == jj) {   // row j of B, scaled: row j of X
-        const float rl = 1.0f / colv[j];
 #pragma unroll
-        for (int b = 0; b <= jb; ++b) {
-          const int c = tx + 16 * b;
-          const float v = B[jb][b] * rl;
-          B[jb][b] = v;
-          if (c <= j) rowv[c] = v;
-        }
-      }
-      __syncthreads();
-      float xr[NB];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int b = 0; b <= jb; ++b) {
-        const int c = tx + 16 * b;
-        xr[b] = c <= j ? rowv[c] : 0.0f;
-      }
-#pragma unroll
-      for (int a = jb; a < NB; ++a) {
-        const int i = ty + 16 * a;
-        const float lij = (i > j && i < k) ? colv[i] : 0.0f;
-#pragma unroll
-        for (int b = 0; b <= jb; ++b) B[a][b] = __builtin_fmaf(-lij, xr[b], B[a][b]);
-      }
-      __syncthreads();
+        for (int j = 0; j < 4; ++j) Ybuf[jb * 16 * 17 + (pr + i) * 17 + pc + j] = acc[i][j];
     }
-  });
-  // Wt = X^T: Wt[l][c] = X[c][l]
+    __syncthreads();
+    for (int jb = blk; jb < ib; jb += 16) {
+      // X_ib,jb = -D_ib T_jb  (D_ib lower), written transposed
+      float acc[4][4] = {};
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+      for (int q = 0; q < 16; ++q) {
+        float av[4], bv[4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int i = ty + 16 * a, l = tx + 16 * b;   // X[i][l]
-      if (i < k && l < k) gstore(Wt + l * k + i, l <= i ? B[a][b] : 0.0f);
+        for (int i = 0; i < 4; ++i) av[i] = D[ib][(pr + i) * 17 + q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = Ybuf[jb * 16 * 17 + q * 17 + pc + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(-av[i], bv[j], acc[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[(jb * 16 + pc + j) * PA + ib * 16 + pr + i] = acc[i][j];
     }
+    __syncthreads();
+  }
+  // Wt = X^T: Wt[l][c] = X[c][l] = A[l][c] for c >= l, zero below
+  for (int e = t; e < k * k; e += kThreads) {
+    const int l = e / k, c = e % k;
+    gstore(Wt + e, c >= l ? A[l * PA + c] : 0.0f);
+  }
 }
 
 // ============================================================ small fp32 products ===
