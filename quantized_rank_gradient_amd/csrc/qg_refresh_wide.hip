@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_prep(const float* C, int k,
 // and abs_tol.
 __device__ __forceinline__ bool bj_needs(float app, float aqq, float apq, float tol,
                                          float abs_tol) {
-  return fabsf(apq) > tol * sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
+  return fabsf(apq) > tol * __builtin_amdgcn_sqrtf(fabsf(app * aqq)) && fabsf(apq) > abs_tol;
 }
 
 // Threads of the subproblem kernel for blocks of B indices: two 2 x 2 blocks of the
@@ -302,7 +302,10 @@ template <int B>
 constexpr int bj_solve_threads() { return B * 2 * B / 4; }
 
 // The symmetric 2 x 2 Schur rotation (Golub and Van Loan, Algorithm 8.5.1) of the pair whose
-// smaller index holds app, the larger aqq and the pair apq, in fp32, with (c, s) also in fp64
+// smaller index holds app, the larger aqq and the pair apq, in fp32 with the hardware
+// reciprocal and square roots (the angle need not be correctly rounded: any rotation close
+// to the exact one lowers the off-diagonal norm, and (c, s) are orthonormalized below), with
+// (c, s) also in fp64
 // scaled to unit length: h = c^2 + s^2 is 1 to fp32 accuracy, and 1.5 - h / 2 is 1 / sqrt(h)
 // up to (h - 1)^2. The identity when the pair is below the rotation level.
 __device__ __forceinline__ bool bj_rotation(float app, float aqq, float apq, float tol,
@@ -315,7 +318,7 @@ __device__ __forceinline__ bool bj_rotation(float app, float aqq, float apq, flo
   if (!bj_needs(app, aqq, apq, tol, abs_tol)) return false;
   const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.0f * apq);
   const float t = (tau >= 0.0f ? 1.0f : -1.0f) *
-                  __builtin_amdgcn_rcpf(fabsf(tau) + sqrtf(1.0f + tau * tau));
+                  __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(1.0f + tau * tau));
   c = __builtin_amdgcn_rsqf(1.0f + t * t);
   s = t * c;
   const double h = (double)c * c + (double)s * s;
