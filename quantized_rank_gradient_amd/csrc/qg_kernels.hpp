@@ -110,13 +110,14 @@ enum { kSgPartial = 0, kSgSubtract = 1, kSgStore = 2 };
 // writes the product over K slab s densely at out + s*M*N; kSgSubtract: out[i*ldo + j] -=
 // product; kSgStore: out[i*ldo + j] = product. The contiguous extent of each operand (K of a
 // K-contiguous A, M of a K-major A, N of B) and every leading dimension are multiples of 4,
-// kslab a multiple of 16, and the pointers 16-byte aligned.
+// kslab a multiple of 16, and the pointers 16-byte aligned. tile: output tile edge, kSgTile
+// or 64 (tiles_m, tiles_n counted in it).
 struct SGemm {
   const float* A;
   const float* B;
   float* out;
   int64_t M, N, K, lda, ldb, ldo, kslab;
-  int tiles_m, tiles_n, split, a_kmajor, mode;
+  int tiles_m, tiles_n, split, a_kmajor, mode, tile;
 };
 hipError_t launch_rf_sgemm(const SGemm& g, hipStream_t s);
 // Qb (M x 2k bf16): hi parts of Qf (M x k fp32) in columns 0 .. k-1, lo parts in k .. 2k-1.

@@ -27,55 +27,64 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 }
 
 // ==================================================================== fp32 products ===
-// A 128 x 128 output tile per workgroup of four waves (2 x 2, each 64 x 64: 2 x 2 blocks of
-// 32 x 32). K advances in stages of 16, both operands staged in LDS K-major ([k][i], pitch
-// kSgPitch: the two half-waves of a fragment read land in opposite halves of the banks); the
-// next stage's global loads are in flight while the current stage's products run.
-constexpr int kSgBM = 128;
+// A BM x BM output tile per workgroup of four waves (2 x 2, each BM/2 x BM/2: blocks of
+// 32 x 32), BM = 128, or 64 for products too narrow to fill the chip with the larger tile.
+// K advances in stages of 16, both operands staged in LDS K-major ([k][i], pitch BM + 32:
+// the two half-waves of a fragment read land in opposite halves of the banks); the next
+// stage's global loads are in flight while the current stage's products run. Every output
+// accumulates its K terms in the same order at either tile size.
 constexpr int kSgBK = 16;
-constexpr int kSgPitch = kSgBM + 32;
-constexpr int kSgStage = 2 * kSgBK * kSgPitch;   // floats per stage (A then B)
-static_assert(kSgBM == kSgTile, "host and device tiles agree");
+template <int BM>
+struct SgCfg {
+  static constexpr int PITCH = BM + 32;
+  static constexpr int STAGE = 2 * kSgBK * PITCH;   // floats per stage (A then B)
+  static constexpr int V = BM * kSgBK / 4 / kThreads;   // float4 per thread and operand
+  static constexpr int X = BM / 64;                  // 32 x 32 blocks per wave and edge
+};
+static_assert(kSgTile == 128, "host and device tiles agree");
 
 __device__ __forceinline__ float4 ld4(const float* p, bool ok) {
   return ok ? gload(reinterpret_cast<const float4*>(p)) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// One stage of a K-major operand (rows k of length `cols`, contiguous): 16 rows x 128
-// columns, two float4 per thread.
+// One stage of a K-major operand (rows k of length `cols`, contiguous): 16 rows x BM
+// columns.
+template <int BM>
 struct SgKmaj {
+  static constexpr int CPR = BM / 4;   // float4 per row
   const float* base;
   int64_t ld, cols;
   int c0;
-  float4 v[2];
+  float4 v[SgCfg<BM>::V];
   __device__ void load(int64_t k0, int64_t k_end) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SgCfg<BM>::V; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      const int64_t kr = k0 + (q >> 5);
-      const int64_t c = c0 + 4 * (q & 31);
+      const int64_t kr = k0 + q / CPR;
+      const int64_t c = c0 + 4 * (q % CPR);
       v[u] = ld4(base + kr * ld + c, kr < k_end && c < cols);
     }
   }
   __device__ void store(float* lds) const {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SgCfg<BM>::V; ++u) {
       const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<float4*>(lds + (q >> 5) * kSgPitch + 4 * (q & 31)) = v[u];
+      *reinterpret_cast<float4*>(lds + (q / CPR) * SgCfg<BM>::PITCH + 4 * (q % CPR)) = v[u];
     }
   }
 };
 
-// One stage of a K-contiguous operand (row i holds its K values contiguously): 128 rows x 16
-// K values, two float4 per thread, transposed into the K-major LDS layout.
+// One stage of a K-contiguous operand (row i holds its K values contiguously): BM rows x 16
+// K values, transposed into the K-major LDS layout.
+template <int BM>
 struct SgKcon {
   const float* base;
   int64_t ld, rows;
   int r0;
-  float4 v[2];
+  float4 v[SgCfg<BM>::V];
   __device__ void load(int64_t k0, int64_t k_end) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SgCfg<BM>::V; ++u) {
       const int q = threadIdx.x + kThreads * u;
       const int64_t row = r0 + (q >> 2);
       const int64_t kc = k0 + 4 * (q & 3);
@@ -83,42 +92,45 @@ struct SgKcon {
     }
   }
   __device__ void store(float* lds) const {
+    constexpr int P = SgCfg<BM>::PITCH;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SgCfg<BM>::V; ++u) {
       const int q = threadIdx.x + kThreads * u;
       const int row = q >> 2, kc = 4 * (q & 3);
-      lds[(kc + 0) * kSgPitch + row] = v[u].x;
-      lds[(kc + 1) * kSgPitch + row] = v[u].y;
-      lds[(kc + 2) * kSgPitch + row] = v[u].z;
-      lds[(kc + 3) * kSgPitch + row] = v[u].w;
+      lds[(kc + 0) * P + row] = v[u].x;
+      lds[(kc + 1) * P + row] = v[u].y;
+      lds[(kc + 2) * P + row] = v[u].z;
+      lds[(kc + 3) * P + row] = v[u].w;
     }
   }
 };
 
-template <class SA>
+template <int BM, class SA>
 __device__ __forceinline__ void sgemm_tile(const SGemm& g, SA& sa, int i0, int j0, int s,
                                            float* lds) {
+  using C = SgCfg<BM>;
+  constexpr int XB = C::X, H = BM / 2;
   const int64_t k_begin = (int64_t)s * g.kslab;
   const int64_t k_end = min<int64_t>(g.K, k_begin + g.kslab);
-  SgKmaj sb{g.B, g.ldb, g.N, j0};
+  SgKmaj<BM> sb{g.B, g.ldb, g.N, j0};
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int am = (wave >> 1) * 64, bn = (wave & 1) * 64;
+  const int am = (wave >> 1) * H, bn = (wave & 1) * H;
   const int kh = lane >> 5, li = lane & 31;
-  f32x16 acc[2][2];
+  f32x16 acc[XB][XB];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < XB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < XB; ++y) acc[x][y] = f32x16{};
   if (k_begin < k_end) {
     sa.load(k_begin, k_end);
     sb.load(k_begin, k_end);
     sa.store(lds);
-    sb.store(lds + kSgBK * kSgPitch);
+    sb.store(lds + kSgBK * C::PITCH);
     __syncthreads();
     int it = 0;
     for (int64_t k0 = k_begin; k0 < k_end; k0 += kSgBK, ++it) {
-      const float* As = lds + (it & 1) * kSgStage;
-      const float* Bs = As + kSgBK * kSgPitch;
+      const float* As = lds + (it & 1) * C::STAGE;
+      const float* Bs = As + kSgBK * C::PITCH;
       const bool more = k0 + kSgBK < k_end;
       if (more) {
         sa.load(k0 + kSgBK, k_end);
@@ -126,29 +138,29 @@ __device__ __forceinline__ void sgemm_tile(const SGemm& g, SA& sa, int i0, int j
       }
 #pragma unroll
       for (int kp = 0; kp < kSgBK / 2; ++kp) {
-        const int kr = (2 * kp + kh) * kSgPitch;
-        float a[2], b[2];
+        const int kr = (2 * kp + kh) * C::PITCH;
+        float a[XB], b[XB];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) a[x] = As[kr + am + 32 * x + li];
+        for (int x = 0; x < XB; ++x) a[x] = As[kr + am + 32 * x + li];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = Bs[kr + bn + 32 * y + li];
+        for (int y = 0; y < XB; ++y) b[y] = Bs[kr + bn + 32 * y + li];
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < XB; ++x)
 #pragma unroll
-          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_f32(a[x], b[y], acc[x][y]);
+          for (int y = 0; y < XB; ++y) acc[x][y] = mfma_f32(a[x], b[y], acc[x][y]);
       }
       if (more) {
-        float* nxt = lds + ((it + 1) & 1) * kSgStage;
+        float* nxt = lds + ((it + 1) & 1) * C::STAGE;
         sa.store(nxt);
-        sb.store(nxt + kSgBK * kSgPitch);
+        sb.store(nxt + kSgBK * C::PITCH);
       }
       __syncthreads();
     }
   }
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < XB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
+    for (int y = 0; y < XB; ++y) {
       const int64_t j = j0 + bn + 32 * y + li;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -167,21 +179,29 @@ __device__ __forceinline__ void sgemm_tile(const SGemm& g, SA& sa, int i0, int j
     }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void qg_rf_sgemm(SGemm g) {
-  __shared__ __attribute__((aligned(16))) float lds[2 * kSgStage];
+template <int BM>
+__device__ __forceinline__ void sgemm_run(const SGemm& g, float* lds) {
   const int local = xcd_remap(blockIdx.x, gridDim.x);
   const int ti = local % g.tiles_m;
   const int rest = local / g.tiles_m;
   const int tj = rest % g.tiles_n;
   const int s = rest / g.tiles_n;
-  const int i0 = ti * kSgBM, j0 = tj * kSgBM;
+  const int i0 = ti * BM, j0 = tj * BM;
   if (g.a_kmajor) {
-    SgKmaj sa{g.A, g.lda, g.M, i0};
-    sgemm_tile(g, sa, i0, j0, s, lds);
+    SgKmaj<BM> sa{g.A, g.lda, g.M, i0};
+    sgemm_tile<BM>(g, sa, i0, j0, s, lds);
   } else {
-    SgKcon sa{g.A, g.lda, g.M, i0};
-    sgemm_tile(g, sa, i0, j0, s, lds);
+    SgKcon<BM> sa{g.A, g.lda, g.M, i0};
+    sgemm_tile<BM>(g, sa, i0, j0, s, lds);
   }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void qg_rf_sgemm(SGemm g) {
+  __shared__ __attribute__((aligned(16))) float lds[2 * SgCfg<128>::STAGE];
+  if (g.tile == 64)
+    sgemm_run<64>(g, lds);
+  else
+    sgemm_run<128>(g, lds);
 }
 
 // ============================================================ basis format helpers ===

@@ -799,6 +799,7 @@ constexpr int kRfSweeps = 16;            // block Jacobi sweeps at most
 struct RfGemmPlan {
   int split, tiles_m, tiles_n;
   int64_t kslab;
+  int tile = qg::kSgTile;   // fp32 products: output tile edge
 };
 // Split-K of one product with G: enough workgroups to cover the chip.
 RfGemmPlan rf_gemm_plan(int64_t M, int64_t N, int64_t K) {
@@ -814,10 +815,13 @@ RfGemmPlan rf_gemm_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 // Split-K of an fp32 product (qg::SGemm): about 512 workgroups, K slabs of 4 stages or more.
+// A product written in place (no split) takes 64 x 64 tiles when 128-edge ones would leave
+// most of the chip idle (the M x 128 updates of the block orthonormalization).
 RfGemmPlan sg_plan(int64_t M, int64_t N, int64_t K, bool split_k) {
   RfGemmPlan p;
-  p.tiles_m = (int)cdiv(M, qg::kSgTile);
-  p.tiles_n = (int)cdiv(N, qg::kSgTile);
+  if (!split_k && cdiv(M, qg::kSgTile) * cdiv(N, qg::kSgTile) < 128) p.tile = 64;
+  p.tiles_m = (int)cdiv(M, p.tile);
+  p.tiles_n = (int)cdiv(N, p.tile);
   const int64_t stages = cdiv(K, 16);
   int64_t sp = 1;
   if (split_k) {
@@ -1002,6 +1006,7 @@ extern "C" qg_status qgalore_refresh_proj(const uint16_t* G, int64_t m, int64_t 
     g.tiles_m = pl.tiles_m;
     g.tiles_n = pl.tiles_n;
     g.split = pl.split;
+    g.tile = pl.tile;
     g.a_kmajor = a_kmajor ? 1 : 0;
     const bool summed = reduce && pl.split > 1;
     g.out = summed ? spart : out;
