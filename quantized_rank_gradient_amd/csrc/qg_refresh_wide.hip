@@ -613,10 +613,32 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
   const int P = nb / 2;
   const int nC = P * (P + 1) / 2;
   int bid = blockIdx.x;
-  // Jm[w] holds J^T (row j = column j of J)
-  auto load_j = [&](double* dst, int w) {
-    const double* src = Jm + (int64_t)w * S * S;
-    for (int e = threadIdx.x; e < S * S; e += kThreads) dst[(e % S) * PT + e / S] = gload(src + e);
+  // Jm[w] holds J^T (row j = column j of J); 16-byte loads, two consecutive entries of a row
+  // of J^T each
+  constexpr int NJ = S * S / 2 / kThreads;   // double2 per thread for a 2B x 2B matrix
+  auto fetch_j = [&](double2 (&r)[NJ], int w) {
+    const double2* src = reinterpret_cast<const double2*>(Jm + (int64_t)w * S * S);
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) r[q] = gload(src + threadIdx.x + q * kThreads);
+  };
+  auto put_j = [&](double* dst, const double2 (&r)[NJ]) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int e = 2 * (threadIdx.x + q * kThreads);   // entries e, e + 1 of J^T
+      dst[(e % S) * PT + e / S] = r[q].x;
+      dst[((e + 1) % S) * PT + e / S] = r[q].y;
+    }
+  };
+  // X[i][j] = M[row(i)][col(j)], 16-byte loads (columns j, j + 1 of one block)
+  auto load_x = [&](const double* M, auto row, auto col) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int e2 = threadIdx.x + q * kThreads;
+      const int i = e2 / (S / 2), j = 2 * (e2 % (S / 2));
+      const double2 v = gload(reinterpret_cast<const double2*>(M + row(i) + col(j)));
+      X[i * PT + j] = v.x;
+      X[i * PT + j + 1] = v.y;
+    }
   };
   BjMul<B> m;
   if (bid < nC) {
@@ -630,17 +652,17 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
     int lo1, hi1, lo2, hi2;
     bj_pair(nb, round, w1, lo1, hi1);
     bj_pair(nb, round, w2, lo2, hi2);
-    for (int e = threadIdx.x; e < S * S; e += kThreads) {
-      const int i = e / S, j = e % S;
-      X[i * PT + j] =
-          gload(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K + bj_index<B>(lo2, hi2, j));
-    }
-    load_j(J1, w1);
+    double2 jr[NJ];
+    fetch_j(jr, w1);
+    load_x(Cj, [&](int i) { return (int64_t)bj_index<B>(lo1, hi1, i) * K; },
+           [&](int j) { return (int64_t)bj_index<B>(lo2, hi2, j); });
+    put_j(J1, jr);
+    fetch_j(jr, w2);   // J2 in flight during the first product
     __syncthreads();
     m.template mul<true>(J1, X);   // J1^T X
     __syncthreads();
     m.put(X);
-    load_j(J2, w2);
+    put_j(J2, jr);
     __syncthreads();
     m.template mul<false>(X, J2);   // (J1^T X) J2
     __syncthreads();
@@ -664,11 +686,11 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
     int lo, hi;
     bj_pair(nb, round, w, lo, hi);
     const int64_t r0 = (int64_t)strip * S;
-    for (int e = threadIdx.x; e < S * S; e += kThreads) {
-      const int i = e / S, j = e % S;
-      X[i * PT + j] = gload(Vj + (r0 + i) * K + bj_index<B>(lo, hi, j));
-    }
-    load_j(J1, w);
+    double2 jr[NJ];
+    fetch_j(jr, w);
+    load_x(Vj, [&](int i) { return (r0 + i) * K; },
+           [&](int j) { return (int64_t)bj_index<B>(lo, hi, j); });
+    put_j(J1, jr);
     __syncthreads();
     m.template mul<false>(X, J1);
 #pragma unroll
