@@ -411,10 +411,18 @@ __device__ __forceinline__ void bj_solve_sweep(const double* Cj, int K, int lo, 
   using Sch = BjSched<B, FULL>;
   constexpr int S = 2 * B, NT = bj_solve_threads<B>(), PA = S + 16, H = B / 2;
   const int t = threadIdx.x;
+  // entries (i, j), (i, j + 1) of the subproblem by one 16-byte load (j even: both in one
+  // block) to their positions
+  for (int e2 = t; e2 < S * S / 2; e2 += NT) {
+    const int i = e2 / (S / 2), j = 2 * (e2 % (S / 2));
+    const double2 v = gload(reinterpret_cast<const double2*>(
+        Cj + (int64_t)bj_index<B>(lo, hi, i) * K + bj_index<B>(lo, hi, j)));
+    const int pi = Sch::pos0(i) * PA;
+    As[pi + Sch::pos0(j)] = (float)v.x;
+    As[pi + Sch::pos0(j + 1)] = (float)v.y;
+  }
   for (int e = t; e < S * S; e += NT) {
     const int P = e / S, P2 = e % S;
-    As[P * PA + P2] = (float)gload(Cj + (int64_t)bj_index<B>(lo, hi, Sch::index0(P)) * K +
-                                   bj_index<B>(lo, hi, Sch::index0(P2)));
     Qs[P * S + P2] = Sch::index0(P) == P2 ? 1.0 : 0.0;
   }
   if (t == 0) *need = 0;
@@ -517,7 +525,11 @@ __device__ __forceinline__ void bj_solve_sweep(const double* Cj, int K, int lo, 
   }
   // every index is back at its first position: row j of Q^T is at position pos0(j)
   const double* Qf = Qs + buf * S * S;
-  for (int e = t; e < S * S; e += NT) gstore(out + e, Qf[Sch::pos0(e / S) * S + e % S]);
+  for (int e2 = t; e2 < S * S / 2; e2 += NT) {
+    const int e = 2 * e2;
+    gstore(reinterpret_cast<double2*>(out + e),
+           *reinterpret_cast<const double2*>(Qf + Sch::pos0(e / S) * S + e % S));
+  }
 }
 
 template <int B>
@@ -669,14 +681,20 @@ __global__ __launch_bounds__(kThreads) void qg_rf_bj_apply(double* Cj, double* V
     m.put(X);
     __syncthreads();
     const bool diag = w1 == w2;
-    for (int e = threadIdx.x; e < S * S; e += kThreads) {
-      const int i = e / S, j = e % S;
-      const double v = diag ? X[min(i, j) * PT + max(i, j)] : X[i * PT + j];
-      gstore(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K + bj_index<B>(lo2, hi2, j), v);
-      if (!diag) {   // transposed piece, element (ti, tj) of X to (tj, ti): coalesced stores
-        const int ti = e % S, tj = e / S;
-        gstore(Cj + (int64_t)bj_index<B>(lo2, hi2, tj) * K + bj_index<B>(lo1, hi1, ti),
-               X[ti * PT + tj]);
+    // 16-byte stores of entry pairs (j, j + 1), and of the transposed piece (element
+    // (ti, tj) of X to (tj, ti), pairs ti, ti + 1)
+    for (int e2 = threadIdx.x; e2 < S * S / 2; e2 += kThreads) {
+      const int i = e2 / (S / 2), j = 2 * (e2 % (S / 2));
+      const double v0 = diag ? X[min(i, j) * PT + max(i, j)] : X[i * PT + j];
+      const double v1 = diag ? X[min(i, j + 1) * PT + max(i, j + 1)] : X[i * PT + j + 1];
+      gstore(reinterpret_cast<double2*>(Cj + (int64_t)bj_index<B>(lo1, hi1, i) * K +
+                                        bj_index<B>(lo2, hi2, j)),
+             make_double2(v0, v1));
+      if (!diag) {
+        const int tj = i, ti = j;
+        gstore(reinterpret_cast<double2*>(Cj + (int64_t)bj_index<B>(lo2, hi2, tj) * K +
+                                          bj_index<B>(lo1, hi1, ti)),
+               make_double2(X[ti * PT + tj], X[(ti + 1) * PT + tj]));
       }
     }
   } else {
