@@ -152,7 +152,15 @@ __global__ __launch_bounds__(kThreads) void qg_rf_sum(const float* part, int chu
   const int e = blockIdx.x * kThreads + threadIdx.x;
   if (e >= n) return;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s = add_rn(s, gload(part + (int64_t)c * n + e));
+  int c = 0;
+  for (; c + 8 <= chunks; c += 8) {   // eight loads in flight, added in order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = gload(part + (int64_t)(c + u) * n + e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = add_rn(s, v[u]);
+  }
+  for (; c < chunks; ++c) s = add_rn(s, gload(part + (int64_t)c * n + e));
   gstore(out + e, s);
 }
 
