@@ -144,3 +144,43 @@ def test_refresh_power_iterations_help():
         P = gpu_refresh(bits, r, k, iters=q)[0].astype(np.float64)
         miss.append(1.0 - np.linalg.svd(Pw.T @ P, compute_uv=False).min())
     assert miss[0] > miss[1] > miss[2], miss
+
+
+@pytest.mark.parametrize("m,n,r,k", [
+    (512, 384, 32, 40),      # one-workgroup orthonormalization
+    (600, 400, 192, 200),    # block Gram-Schmidt and block Jacobi
+])
+def test_refresh_rank_deficient_gradient(m, n, r, k):
+    """A gradient of rank 16 < r (16 nonzero columns, exactly zero elsewhere): the sketch's
+    Gram matrices are singular and the orthonormalization raises pivots to its floor. The
+    leading 16 vectors span the oracle's, their singular values match, the others are about
+    zero, and everything is finite (the columns past the rank are not unique, so they are
+    not compared)."""
+    rk = 16
+    rng = np.random.default_rng(m + r)
+    G = np.zeros((m, n), np.float32)
+    cols = rng.choice(n, rk, replace=False)
+    G[:, cols] = rng.standard_normal((m, rk)) * np.linspace(1.0, 0.5, rk)
+    bits = O.f32_to_bf16_bits(G)
+    P, sig, Pq, Ps = gpu_refresh(bits, r, k)
+    assert np.isfinite(P).all() and np.isfinite(sig).all() and np.isfinite(Ps).all()
+    Pw, Sw = O.refresh_projection(bits, r)
+    Pg = P.astype(np.float64)
+    np.testing.assert_allclose(Pg[:, :rk].T @ Pg[:, :rk], np.eye(rk), atol=1e-4)
+    sv = np.linalg.svd(Pw[:, :rk].T @ Pg[:, :rk], compute_uv=False)
+    assert 1.0 - sv.min() < 1e-5, f"subspace: 1 - min cos = {1.0 - sv.min():.3g}"
+    np.testing.assert_allclose(sig[:rk], Sw[:rk], rtol=0, atol=1e-4 * Sw[0])
+    assert np.all(np.abs(sig[rk:]) < 1e-3 * Sw[0])
+    want_q, want_s = O.quantize_proj(P, "int4")
+    assert np.array_equal(Pq, want_q) and np.array_equal(Ps, want_s), "INT4 codes of P"
+
+
+def test_refresh_zero_gradient():
+    """G = 0: nothing to project. The library's result is finite with zero singular values
+    (its P is not compared: any orthonormal basis is an SVD of the zero matrix)."""
+    bits = np.zeros((512, 384), np.uint16)
+    P, sig, Pq, Ps = gpu_refresh(bits, 32, 40)
+    assert np.isfinite(P).all() and np.isfinite(Ps).all()
+    assert np.all(sig == 0.0)
+    want_q, want_s = O.quantize_proj(P, "int4")
+    assert np.array_equal(Pq, want_q) and np.array_equal(Ps, want_s), "INT4 codes of P"
