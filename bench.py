@@ -170,15 +170,17 @@ class Variant:
         for p in self.all_plans:
             p.enable_timing(steps)
         self.tests = 0
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
-        start.record()
-        for _ in range(steps):
+        evs[0].record()
+        for i in range(steps):
             self.step()
-        end.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end)
+        total_ms = evs[0].elapsed_time(evs[-1])
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        self.step_pct = {q: round(per[min(steps - 1, int(round(f * (steps - 1))))], 4)
+                         for q, f in (("p10", 0.1), ("median", 0.5), ("p90", 0.9))}
         acc = [0.0] * 4     # summed over the chunks of a step, averaged over the steps
         for p in self.all_plans:
             kms_p, n_p = p.kernel_times()
@@ -738,7 +740,8 @@ def main():
             "gradient_sets": main_res["gradient_sets"],
             "parallelism": "single GPU",
         },
-        **{k: main_res[k] for k in ("tflops", "dequant", "workspace_gib", "projection_gib",
+        **{k: main_res[k] for k in ("step_ms_percentiles", "tflops", "dequant",
+                                    "workspace_gib", "projection_gib",
                                     "kernel_ms", "optimizer_ms", "refresh_tests_per_step",
                                     "cossim_ms", "roofline")},
         "copy_gbs": copy["gbs"] if copy else None,
@@ -804,6 +807,7 @@ def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
         res = dict(config=vcfg.key,
                    workload=f"{vcfg.key}: {describe_layers(vcfg)}, rank {r}",
                    rank=r, steps=steps, ms_per_step=round(ms, 4),
+                   step_ms_percentiles=v.step_pct,
                    value=a["mn"] / (ms / 1e3),
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
                    gradient_sets=g_sets,
