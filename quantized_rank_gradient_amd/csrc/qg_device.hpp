@@ -204,12 +204,25 @@ __device__ __forceinline__ float recip_or_zero(float s) {
   return s == 0.0f ? 0.0f : div_rn(1.0f, s);
 }
 
-// floor(x) converted to int32 in one instruction (v_cvt_flr_i32_f32; saturates outside the
-// int32 range). Only called on finite x.
-__device__ __forceinline__ int floor_to_int(float x) {
-  int r;
-  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
+// floor(x) converted to int32, its low byte written into byte K of w in the same instruction
+// (v_cvt_flr_i32_f32 with an SDWA byte destination): the other bytes of w are kept, or for
+// K == 0 cleared, so four calls K = 0..3 build a packed word. Only called on finite x in
+// [-128, 127], where the low byte is the two's-complement code.
+template <int K>
+__device__ __forceinline__ uint32_t floor_into_byte(uint32_t w, float x) {
+  if constexpr (K == 0)
+    asm("v_cvt_flr_i32_f32_sdwa %0, %1 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD"
+        : "=v"(w) : "v"(x));
+  else if constexpr (K == 1)
+    asm("v_cvt_flr_i32_f32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+        : "+v"(w) : "v"(x));
+  else if constexpr (K == 2)
+    asm("v_cvt_flr_i32_f32_sdwa %0, %1 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+        : "+v"(w) : "v"(x));
+  else
+    asm("v_cvt_flr_i32_f32_sdwa %0, %1 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+        : "+v"(w) : "v"(x));
+  return w;
 }
 
 // Signed byte K (0..3) of w converted to float in one instruction (SDWA operand select with
@@ -230,12 +243,6 @@ __device__ __forceinline__ float sbyte_to_f32(uint32_t w) {
     asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
         : "=v"(r) : "v"(w));
   return r;
-}
-
-// The low bytes of four int32 values packed into one word (byte t from q_t).
-__device__ __forceinline__ uint32_t pack4_bytes(int q0, int q1, int q2, int q3) {
-  return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
-         __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
 }
 
 // ---------------------------------------------------------------- Philox4x32-10 ---

@@ -446,13 +446,18 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
   });
   uint32_t wout[4] = {0, 0, 0, 0};
   if (__builtin_isfinite(amax)) {
-    // clamp(floor(d), -127, 127): floor converted in one instruction, then an integer clamp
+    // clamp(floor(d), -127, 127) as floor(clamp(d, -127, 127)) (floor is monotone and the
+    // bounds are integers): a float clamp, then the floor conversion writes the code
+    // straight into its byte of the packed word
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int q[4];
+      float q[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = min(max(floor_to_int(d[4 * k + u]), -127), 127);
-      wout[k] = pack4_bytes(q[0], q[1], q[2], q[3]);
+      for (int u = 0; u < 4; ++u) q[u] = __builtin_amdgcn_fmed3f(d[4 * k + u], -127.f, 127.f);
+      uint32_t w = floor_into_byte<0>(0u, q[0]);
+      w = floor_into_byte<1>(w, q[1]);
+      w = floor_into_byte<2>(w, q[2]);
+      wout[k] = floor_into_byte<3>(w, q[3]);
     }
   } else {
     int w[16];
