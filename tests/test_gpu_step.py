@@ -235,11 +235,12 @@ def test_cossim_batch_of_mixed_row_counts():
     got = out.cpu().numpy()
     assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
 
-def test_cossim_batch_large_rank():
-    """A batch of eight pairs at rank 1024 (the cross product on 128-edge tiles with split-K),
-    with similarities from near 0 to 1."""
+@pytest.mark.parametrize("r", [1024, 968])
+def test_cossim_batch_large_rank(r):
+    """A batch of eight pairs at rank 1024, and at 968 (ragged edge tiles): the cross product
+    on 128-edge tiles with split-K; similarities from near 0 to 1."""
     B = _B()
-    r, m = 1024, 1024 + 8 * 44
+    m = r + 8 * 44
     pairs, want = [], []
     for k in range(8):
         rng = np.random.default_rng(500 + k)
