@@ -609,10 +609,22 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   c.rws = make_rsrc(L.Ws, ((numel + kGroup - 1) / kGroup) * 4);
   c.ru = make_rsrc(L.U_out, c.write_u ? numel * 4 : 0);
   const int vr = lane / LPR, vc = (lane % LPR) * 16;
-  const uint32_t j16 = (uint32_t)j0 + wn * T::WTN + vc;
+  const uint32_t jw = (uint32_t)j0 + wn * T::WTN;   // the wave's first column
+  const uint32_t j16 = jw + vc;
+  // When rows are whole scale groups apart (n % 256 == 0), the wave's WTN columns of a row
+  // lie in one group: lane l then loads the scale of the wave's row l (WTM == 64 rows) and
+  // computes its reciprocal once, and each lane takes the reciprocals of its rows from the
+  // lanes that hold them. Otherwise every lane loads and inverts the scale of each run.
+  static_assert(!VEC || T::WTM == 64, "one wave row per lane");
+  const bool row_groups = c.n % kGroup == 0 && T::WTN <= kGroup;
   uint4 wv[T::XM][NP];
   float sv[T::XM][NP];
+  float s_row = 0.0f;
   if constexpr (VEC) {
+    if (row_groups) {
+      const uint32_t i = (uint32_t)i0 + wm * T::WTM + lane;
+      s_row = bloadf(c.rws, i < c.m && jw < c.n ? ((i * c.n + jw) >> 8) * 4 : kOOB);
+    }
 #pragma unroll
     for (int x = 0; x < T::XM; ++x)
 #pragma unroll
@@ -621,7 +633,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
         const uint32_t e = i * c.n + j16;
         const bool in = i < c.m && j16 < c.n;
         wv[x][p] = bload128(c.rw, in ? e : kOOB);
-        sv[x][p] = bloadf(c.rws, in ? (e >> 8) * 4 : kOOB);
+        sv[x][p] = row_groups ? 0.0f : bloadf(c.rws, in ? (e >> 8) * 4 : kOOB);
       }
   }
 
@@ -655,6 +667,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
   if constexpr (VEC) {
+    const float inv_row = row_groups ? recip_or_zero(s_row) : 0.0f;
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
@@ -662,10 +675,13 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
       for (int p = 0; p < NP; ++p) {
         const int row = RPP * p + vr;
         const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + row;
+        // the shuffle runs on every lane (a lane whose run is off the layer only serves)
+        const float inv = row_groups ? __shfl(inv_row, 32 * x + row, 64)
+                                     : recip_or_zero(sv[x][p]);
         if (i < c.m && j16 < c.n) {
           float S[16];
           read_run16(E, row * EP + vc, S);
-          sr_block16(c, L, a, i, j16, S, recip_or_zero(sv[x][p]), wv[x][p]);
+          sr_block16(c, L, a, i, j16, S, inv, wv[x][p]);
         }
       }
       __syncthreads();
