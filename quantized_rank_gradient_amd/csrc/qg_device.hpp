@@ -22,13 +22,15 @@ struct LayerDev {
   int8_t* Vq;          // int8 r x n
   float* Vs;
   int64_t off_r;       // workspace byte offset: split x rpitch fp32 partial sums of R
-  int64_t off_n;       // workspace byte offset: bf16 r x n update N~
+  int64_t off_n;       // workspace byte offset: bf16 r x n update N~ (rows ldn apart)
   int64_t off_p;       // workspace byte offset: bf16 m x r dequantized projection P~
                        // (written at the start of every step, read by both MFMA kernels;
                        // absent when p_inline)
   float* R_out;        // optional
   float* U_out;        // optional
   int64_t m, n, r;
+  int64_t ldn;         // row pitch (elements) of N~ in the workspace: n rounded up to a
+                       // multiple of 8, so that its rows can be staged in 16-byte chunks
   int64_t rpitch;      // elements between split slabs of Rpart
   uint32_t layer_id;
   int32_t p_format;    // 0: INT4 codes, 1: INT8 codes, 2: bf16 values (Pq then holds them)

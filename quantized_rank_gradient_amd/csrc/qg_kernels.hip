@@ -132,8 +132,6 @@ __device__ __forceinline__ void adam_group(const StepArgs& a, const LayerDev& L,
   if (full) {
     gstore(reinterpret_cast<uint32_t*>(L.Mq + e0), om);
     gstore(reinterpret_cast<uint32_t*>(L.Vq + e0), ov);
-    gstore(reinterpret_cast<uint2*>(Nb + e0),
-           make_uint2(pack_bf16x2(N[0], N[1]), pack_bf16x2(N[2], N[3])));
     if (L.R_out)
       gstore(reinterpret_cast<float4*>(L.R_out + e0), make_float4(R[0], R[1], R[2], R[3]));
   } else {
@@ -141,9 +139,23 @@ __device__ __forceinline__ void adam_group(const StepArgs& a, const LayerDev& L,
       if (e0 + t < numel) {
         gstore(L.Mq + e0 + t, (int8_t)(om >> (8 * t)));
         gstore(L.Vq + e0 + t, (int8_t)(ov >> (8 * t)));
-        gstore(Nb + e0 + t, to_bf16(N[t]));
         if (L.R_out) gstore(L.R_out + e0 + t, R[t]);
       }
+  }
+  // N~ rows are ldn elements apart (n rounded up to a multiple of 8): element e of the flat
+  // r x n order sits at (e / n) * ldn + e % n
+  if (full && L.ldn == L.n) {
+    gstore(reinterpret_cast<uint2*>(Nb + e0),
+           make_uint2(pack_bf16x2(N[0], N[1]), pack_bf16x2(N[2], N[3])));
+  } else {
+    int64_t k = e0 / L.n, j = e0 - k * L.n;
+    for (int t = 0; t < 4; ++t) {
+      if (e0 + t < numel) gstore(Nb + k * L.ldn + j, to_bf16(N[t]));
+      if (++j == L.n) {
+        j = 0;
+        ++k;
+      }
+    }
   }
   if (lane == 0) {
     gstore(L.Ms + g, sm);
@@ -488,12 +500,17 @@ __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L
   const uint4 ph = philox4x32_10(make_uint4(j8 >> 3, i, a.step, L.layer_id), a.seed_lo, a.seed_hi);
   const uint32_t words[4] = {ph.x, ph.y, ph.z, ph.w};
   const uint32_t e0 = i * c.n + j8;
+  // the run's (at most 8) weights lie in at most two scale groups
+  const uint32_t g0 = e0 >> 8, g1 = (e0 + min(8u, c.n - j8) - 1) >> 8;
+  const float inv0 = recip_or_zero(bloadf(c.rws, g0 * 4));
+  float inv1 = inv0;
+  if (g1 != g0) inv1 = recip_or_zero(bloadf(c.rws, g1 * 4));
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const bool in = j8 + t < c.n;
     const uint32_t e = e0 + t;
     const float U = mul_rn(L.alpha, S[t]);
-    const float iv = recip_or_zero(bloadf(c.rws, in ? (e >> 8) * 4 : kOOB));
+    const float iv = (e >> 8) == g0 ? inv0 : inv1;
     const int w = (int)(int8_t)bload8(c.rw, in ? e : kOOB);
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
     const float d = sr_pre(w, U, iv, bits);
@@ -573,12 +590,14 @@ using BackCodes = DmaInt4C<128, 32>;
 template <class T, bool VEC, class BASE, int PM>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
                                           uint16_t* lds, uint8_t* codes) {
-  static_assert(T::DMA == VEC, "DMA layout exactly on the vector path");
+  static_assert(T::DMA, "operands staged by DMA");
   constexpr int EP = BackLds<BASE>::EP;
-  constexpr int NQ = T::WTN / 16;  // 8-column blocks per lane and 32-row chunk (element path)
   constexpr int LPR = T::WTN / 16; // vector path: lanes per row, 16 columns each
   constexpr int RPP = 64 / LPR;    //   rows per pass of a 32-row chunk
   constexpr int NP = 32 / RPP;     //   passes per chunk
+  constexpr int LPR8 = T::WTN / 8; // element path: lanes per row, 8 columns each
+  constexpr int RPP8 = 64 / LPR8;  //   rows per pass
+  constexpr int NP8 = 32 / RPP8;   //   passes per chunk
   // Tiles are numbered in bands of 4 row tiles, column-major inside a band: the tiles that
   // run together on one XCD (consecutive after the renumbering) cover about 4 row tiles x 8
   // column tiles, whose P~ rows and N~ columns fit in that XCD's L2 together.
@@ -639,30 +658,18 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
   // A = P~ (rows i, K = rank index contiguous): the INT4 codes of P dequantized on their way
   // into LDS, or the bf16 P~ (the dequant kernel's copy or the caller's bf16 P).
-  // B = N~ stored [k][j] (r x n).
+  // B = N~ stored [k][j] (r x n, rows ldn apart: 16-byte chunks for any n; a chunk that runs
+  // past column n reads row padding, which only feeds output columns that are dropped).
   const bool inl = PM == kPInline || (PM == kPMixed && L.p_inline);
   const uint16_t* Nb = reinterpret_cast<const uint16_t*>(a.ws + L.off_n);
   f32x16 acc[T::XM][T::XN];
-  auto store_a = [](auto& st, uint16_t* p) { st.template store<T::A_PITCH>(p); };
-  auto store_b = [](auto& st, uint16_t* p) { st.template store<T::B_PITCH>(p + T::A_ELEMS); };
-  if constexpr (VEC) {
-    const DmaBf16K<T::BN, T::BK> sb(Nb, L.n, L.r, L.n, j0);
-    if (PM != kPStaged && inl) {
-      const BackCodes sa(L.Pq, L.Ps, L.r, L.m, i0);
-      gemm_kloop_dma_cvt<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, codes, acc);
-    } else if (PM != kPInline) {
-      const DmaBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
-      gemm_kloop_dma<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, acc);
-    }
-  } else {
-    StageBf16K<T::BN, T::BK, false> sb(Nb, L.n, L.r, L.r, L.n, j0);
-    if (PM != kPStaged && inl) {
-      StageInt4C<T::BM, T::BK> sa(L.Pq, L.Ps, L.r, L.m, i0);
-      gemm_kloop<T, 1>(sa, sb, store_a, store_b, 0, L.r, lds, acc);
-    } else if (PM != kPInline) {
-      StageBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
-      gemm_kloop<T, 1>(sa, sb, store_a, store_b, 0, L.r, lds, acc);
-    }
+  const DmaBf16K<T::BN, T::BK> sb(Nb, L.ldn, L.r, L.n, j0);
+  if (PM != kPStaged && inl) {
+    const BackCodes sa(L.Pq, L.Ps, L.r, L.m, i0);
+    gemm_kloop_dma_cvt<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, codes, acc);
+  } else if (PM != kPInline) {
+    const DmaBf16C<T::BM, T::BK> sa(p_tilde(a, L), L.r, L.m, i0);
+    gemm_kloop_dma<T, BackLds<BASE>::NST, true>(sa, sb, 0, L.r, lds, acc);
   }
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
@@ -687,17 +694,21 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
       __syncthreads();
     }
   } else {
-    const int rr = lane >> 1, cc = (lane & 1) * (T::WTN / 2);
-    const uint32_t jb = (uint32_t)j0 + wn * T::WTN + cc;
+    // lanes along a row, 8 columns each, so that each byte access of the wave covers a few
+    // rows' contiguous runs
+    const int vr8 = lane / LPR8, vc8 = (lane % LPR8) * 8;
+    const uint32_t j8 = jw + vc8;
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
-      const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + rr;
-      if (i < c.m) {
-        for (int q = 0; q < NQ; ++q) {
+#pragma clang loop unroll(full)
+      for (int p = 0; p < NP8; ++p) {
+        const int row = RPP8 * p + vr8;
+        const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + row;
+        if (i < c.m && j8 < c.n) {
           float S[8];
-          read_run(E, rr * EP + cc + 8 * q, S);
-          sr_block8_elem(c, L, a, i, jb + 8 * q, S);
+          read_run(E, row * EP + vc8, S);
+          sr_block8_elem(c, L, a, i, j8, S);
         }
       }
       __syncthreads();
@@ -716,7 +727,7 @@ __global__ __launch_bounds__(kThreads, BackLds<T>::MINB) void qg_backproject(Ste
   if (L.n % 16 == 0)
     back_tile<DmaOf<T>, true, T, PM>(a, L, local, lds, codes);
   else
-    back_tile<T, false, T, PM>(a, L, local, lds, codes);
+    back_tile<DmaOf<T>, false, T, PM>(a, L, local, lds, codes);
 }
 
 // ================================================================ quantization of P ===

@@ -91,6 +91,9 @@ bool valid_dequant_mode(int32_t mode) {
   return mode == QG_DEQUANT_AUTO || mode == QG_DEQUANT_INLINE || mode == QG_DEQUANT_PASS;
 }
 
+// Row pitch of N~ in the workspace (elements): 16-byte aligned rows for any n.
+int64_t n_pitch(int64_t n) { return round_up(n, 8); }
+
 // Per-layer workspace: split-K partial sums of R (fp32; absent when Adam is fused into the
 // projection), the bf16 update N~ (r x n) and, for projections the MFMA kernels do not
 // dequantize themselves, the bf16 dequantized projection P~ (m x r) that both read.
@@ -104,7 +107,7 @@ WsLayout ws_layout(int64_t m, int64_t n, int64_t r, int split, int64_t base,
   w.off_r = base;
   const int64_t rbytes = fused_adam(n, split) ? 0 : (int64_t)split * w.rpitch * 4;
   w.off_n = base + round_up(rbytes, 256);
-  w.off_p = w.off_n + round_up(r * n * 2, 256);
+  w.off_p = w.off_n + round_up(r * n_pitch(n) * 2, 256);
   // a bf16 projection is staged from the caller's tensor, an inline INT4 one from its codes:
   // no dequantized copy
   const bool copy = p_format != QG_P_BF16 && !inl;
@@ -190,6 +193,7 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.m = d->m;
   L.n = d->n;
   L.r = d->r;
+  L.ldn = n_pitch(d->n);
   const bool inl = p_inline(d->p_format, d->r, d->dequant_mode);
   const WsLayout w = ws_layout(d->m, d->n, d->r, split, ws_base, d->p_format, inl);
   L.rpitch = w.rpitch;
