@@ -85,7 +85,11 @@ __device__ __forceinline__ int kmaj_slot(int k, int j) {
 // VEC (requires ld % 8 == 0): each stage reads 16-byte chunks through a buffer resource that
 // starts at the stage's first row and ends at k_end, so rows past the K range read as zero
 // without a per-lane test and the per-lane offsets stay fixed for the whole loop. Otherwise
-// elements are read one by one with full bounds tests.
+// (rows of any pitch) a chunk's 8 elements come from the five dwords at the dword-aligned
+// offset at or below it, shifted by half a dword when the chunk starts on an odd element.
+// Elements past c_end (a chunk running over its row's end) then hold the next row's values;
+// they only feed output columns that are dropped. Rows past k_end read as zero, and a chunk
+// whose five dwords would run past the source's end is read element by element.
 template <int W, int BK, bool VEC, int SETS = 1>
 struct StageBf16K {
   static constexpr int CPR = W / 8;                    // chunks per row
@@ -95,15 +99,16 @@ struct StageBf16K {
                 "tile splits evenly over the threads");
   const uint16_t* src;
   rsrc_t rs;
-  uint32_t ld, k_end, c_end;
+  uint32_t ld, k_end, c_end, nbytes;
   int c0;
   uint32_t vo[NC];   // byte offset of chunk u from the stage's first row; kOOB off the tile
   uint4 v[SETS][NC];   // SETS stages in flight (see gemm_kloop_ring)
 
   __device__ StageBf16K(const uint16_t* s, int64_t ld_, int64_t rows, int64_t k_end_,
                         int64_t c_end_, int c0_)
-      : src(s), ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_), c0(c0_) {
-    rs = make_rsrc(s, (uint32_t)(rows * ld_ * 2));
+      : src(s), ld((uint32_t)ld_), k_end((uint32_t)k_end_), c_end((uint32_t)c_end_),
+        nbytes((uint32_t)(rows * ld_ * 2)), c0(c0_) {
+    rs = make_rsrc(s, nbytes);
     const uint32_t c = c0 + 8 * (threadIdx.x % CPR);
 #pragma unroll
     for (int u = 0; u < NC; ++u)
@@ -124,13 +129,26 @@ struct StageBf16K {
         const int q = threadIdx.x + kThreads * u;
         const uint32_t k = k0 + q / CPR;
         const uint32_t c = c0 + 8 * (q % CPR);
-        uint32_t w[4] = {0, 0, 0, 0};
+        const uint32_t o = k * ld + c;            // the chunk's first element
+        const uint32_t b = (o & ~1u) * 2;         // dword-aligned byte offset at or below it
+        const bool in = k < k_end && c < c_end;
+        if (in && b + 20 > nbytes) {              // the source's last chunk: element-wise
+          uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t off = (k < k_end && c + e < c_end) ? (k * ld + c + e) * 2 : kOOB;
-          w[e >> 1] |= bload16(rs, off) << (16 * (e & 1));
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t off = c + e < c_end ? (o + e) * 2 : kOOB;
+            w[e >> 1] |= bload16(rs, off) << (16 * (e & 1));
+          }
+          v[S][u] = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          const uint4 x = bload128(rs, in ? b : kOOB);
+          const uint32_t y = bload32(rs, in ? b + 16 : kOOB);
+          const uint32_t sh = (o & 1u) * 16;
+          v[S][u] = make_uint4(__builtin_amdgcn_alignbit(x.y, x.x, sh),
+                               __builtin_amdgcn_alignbit(x.z, x.y, sh),
+                               __builtin_amdgcn_alignbit(x.w, x.z, sh),
+                               __builtin_amdgcn_alignbit(y, x.w, sh));
         }
-        v[S][u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }
