@@ -233,56 +233,6 @@ struct StageInt4K {
   }
 };
 
-// INT4 source [c][k] (row pitch ld = the K extent in codes, ld % 8 == 0, c_end rows) ->
-// K-contiguous LDS tile [c][k] in bf16 (kc_off layout), through registers. Each 8-code chunk
-// starts at a multiple of 8 in the flat index, so it lies inside one 256-element scale group;
-// chunks past the K extent or past c_end stage zeros.
-template <int W, int BK>
-struct StageInt4C {
-  static_assert(BK == 32, "K-contiguous tiles take 32-element rows");
-  static constexpr int CPR = BK / 8;
-  static constexpr int NC = W * CPR / kThreads;
-  static_assert(NC * kThreads == W * CPR, "tile splits evenly over the threads");
-  rsrc_t rq, rsc;
-  uint32_t ld, c_end;
-  int c0;
-  uint32_t w[NC];
-  float s[NC];
-
-  __device__ StageInt4C(const uint8_t* q_, const float* sc_, int64_t ld_, int64_t c_end_,
-                        int c0_)
-      : ld((uint32_t)ld_), c_end((uint32_t)c_end_), c0(c0_) {
-    const int64_t numel = c_end_ * ld_;
-    rq = make_rsrc(q_, (uint32_t)((numel + 1) / 2));
-    rsc = make_rsrc(sc_, (uint32_t)(((numel + kGroup - 1) / kGroup) * 4));
-  }
-
-  template <int S = 0>
-  __device__ __forceinline__ void load(int64_t k0_) {
-    const uint32_t k0 = (uint32_t)k0_;
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      const uint32_t row = c0 + q / CPR;
-      const uint32_t k = k0 + 8 * (q % CPR);
-      const bool in = row < c_end && k < ld;
-      const uint32_t e = row * ld + k;
-      w[u] = bload32(rq, in ? (e >> 1) : kOOB);
-      s[u] = bloadf(rsc, in ? (e >> 8) * 4 : kOOB);
-    }
-  }
-
-  template <int PITCH, int S = 0>
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-    static_assert(PITCH == 32, "K-contiguous tiles take 32-element rows");
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int q = threadIdx.x + kThreads * u;
-      *reinterpret_cast<uint4*>(lds + kc_off(q / CPR, q % CPR)) = dequant8(w[u], s[u]);
-    }
-  }
-};
-
 // INT8 source [k][c] (row pitch ld codes, ld % 8 == 0, `rows` rows) -> K-major LDS tile [k][c]
 // in bf16; like StageInt4K with one byte per code.
 template <int W, int BK>

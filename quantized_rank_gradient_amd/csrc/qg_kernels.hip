@@ -284,7 +284,8 @@ constexpr int kProjLdsBytes(int pm) {
 }
 
 // VEC: rows of G are a multiple of 8 elements: 16-byte chunks staged straight into LDS
-// (T in the DMA layout). Otherwise G is read element by element through registers.
+// (T in the DMA layout). Otherwise G goes through registers (each 8-element chunk from
+// aligned dwords, funnel-shifted to its start).
 // PM: which projection paths to compile (kPStaged, kPInline, kPMixed); a layer takes the
 // INT4 stager path when L.p_inline.
 template <class T, bool VEC, int PM>
@@ -573,9 +574,9 @@ struct BackLds {
   static constexpr int NST = SMALL ? 2 : 3;   // DMA ring buffers
   static constexpr int MINB = SMALL ? 4 : 2;  // workgroups per CU
   static constexpr int RING = NST * DmaOf<T>::STAGE * 2;   // bytes of the DMA ring
-  static constexpr int BYTES = cmax(cmax(2 * T::STAGE * 2, RING), kThreads / 64 * 32 * EP * 4);
+  static constexpr int BYTES = cmax(RING, kThreads / 64 * 32 * EP * 4);
   // with the INT4 stager's code areas after the ring (they share the array with the
-  // register-staged buffers and the epilogue, neither of which uses them)
+  // epilogue, which does not use them)
   static constexpr int bytes(int pm) {
     return pm == kPStaged ? BYTES : cmax(BYTES, RING + NST * DmaInt4C<128, 32>::AREA);
   }
@@ -583,10 +584,11 @@ struct BackLds {
 
 using BackCodes = DmaInt4C<128, 32>;
 
-// VEC: rows of W (and of N~) are a multiple of 16 elements: 16-byte weight accesses
-// (prefetched before the product) and 16-byte chunks of N~ staged straight into LDS (T in
-// the DMA layout). BASE is the tile whose LDS area the kernel declares. PM as for the
-// projection.
+// Both operands are staged straight into LDS (T in the DMA layout; N~'s rows are padded to a
+// multiple of 8 elements in the workspace). VEC: rows of W are a multiple of 16 elements, so
+// the rounding takes 16-byte weight accesses (prefetched before the product); otherwise it
+// takes byte accesses along the rows. BASE is the tile whose LDS area the kernel declares. PM
+// as for the projection.
 template <class T, bool VEC, class BASE, int PM>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
                                           uint16_t* lds, uint8_t* codes) {
