@@ -500,6 +500,32 @@ def mfma_sustained(torch, B, grid=1024, iters=2000, reps=3):
     return out
 
 
+def mfma_hold(torch, B, seconds, grid=1024, iters=2000):
+    """Runs the MFMA calibration kernel on random operands for about `seconds` (for board
+    power and clock readings beside it) and returns the rate it sustained."""
+    buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20240711)
+    ops = (torch.randn(1 << 23, generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
+    flops = B.mfma_probe(ops, buf, grid, iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    B.mfma_probe(ops, buf, grid, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    launches = max(1, int(seconds * 1e3 / e0.elapsed_time(e1)))
+    e0.record()
+    for _ in range(launches):
+        B.mfma_probe(ops, buf, grid, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    return {"mfma_probe": "random bf16 operands", "launches": launches,
+            "seconds": round(ms / 1e3, 2),
+            "tflops": round(flops * launches / (ms / 1e3) / 1e12, 1)}
+
+
 def library_gemm_ms(torch, cfg, r, reps=20):
     """torch (hipBLASLt) bf16 matmuls with the shapes of the two contractions, summed over
     the layer set: R = P^T G with P^T stored contiguous, and P N (no fused epilogues). A
@@ -611,6 +637,9 @@ def main():
     ap.add_argument("--linear", action="store_true",
                     help="instead: time the INT8-weight linear products (forward, data and "
                          "weight gradients) on the 7B layer shapes")
+    ap.add_argument("--mfma-seconds", type=float, default=0.0,
+                    help="instead: run the MFMA calibration kernel on random operands for this "
+                         "many seconds (board power and clock readings beside it)")
     ap.add_argument("--refresh-only", action="store_true",
                     help="instead: time one projection refresh per 7B shape (library vs torch)")
     ap.add_argument("--refresh-ranks", default="128",
@@ -655,7 +684,8 @@ def main():
 
     # the oracle's baseline runs first, in forked worker processes, before the GPU is touched
     cpu = None
-    if not (args.no_cpu_baseline or args.schedule or args.linear or args.refresh_only):
+    if not (args.no_cpu_baseline or args.schedule or args.linear or args.refresh_only
+            or args.mfma_seconds > 0):
         log("timing the CPU oracle ...")
         cpu = cpu_baseline()
         log(f"cpu baseline: {json.dumps(cpu)}")
@@ -694,6 +724,9 @@ def main():
 
     if args.linear:
         print(json.dumps(linear_bench(torch, B, WL, args.tokens, args.steps)), flush=True)
+        return
+    if args.mfma_seconds > 0:
+        print(json.dumps(mfma_hold(torch, B, args.mfma_seconds)), flush=True)
         return
     if args.refresh_only:
         scfg = WL.CONFIGS["schedule7b"]
