@@ -472,41 +472,29 @@ def copy_bandwidth(torch, gib=2.0, reps=5):
     return dict(bytes_per_copy=2 * n, ms=round(ms, 4), gbs=round(2 * n / (ms / 1e3) / 1e9, 1))
 
 
-def mfma_sustained(torch, B, grid=1024, iters=2000, reps=3):
+def mfma_sustained(torch, B, seconds=1.5):
     """TFLOP/s of the library's MFMA calibration kernel (bf16 32x32x16 products from register
-    operands, no memory traffic) on random operands like the step's (bf16 ~N(0, 0.05^2)) and
-    on constant ones: the rate the matrix cores sustain under the clock the load allows,
-    beside the published dense peak that the roofline fraction is taken against."""
-    out = {}
-    buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(20240711)
-    for label, ops in (("random_operands", (torch.randn(1 << 23, generator=gen, device="cuda")
-                                             * 0.05).to(torch.bfloat16)),
-                       ("constant_operands", torch.full((1 << 23,), 0.01, device="cuda",
-                                                        dtype=torch.bfloat16))):
-        flops = B.mfma_probe(ops, buf, grid, iters)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            B.mfma_probe(ops, buf, grid, iters)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        out[label] = round(flops / (ms / 1e3) / 1e12, 1)
-        del ops
-    out["unit"] = "TFLOP/s"
+    operands, no memory traffic) held for about `seconds` each on random operands like the
+    step's (bf16 ~N(0, 0.05^2)) and on constant ones: the rate the matrix cores sustain
+    under the clock the load allows, beside the published dense peak that the roofline
+    fraction is taken against."""
+    out = {"random_operands": mfma_hold(torch, B, seconds)["tflops"],
+           "constant_operands": mfma_hold(torch, B, seconds, constant=True)["tflops"],
+           "seconds_each": seconds, "unit": "TFLOP/s"}
     return out
 
 
-def mfma_hold(torch, B, seconds, grid=1024, iters=2000):
-    """Runs the MFMA calibration kernel on random operands for about `seconds` (for board
-    power and clock readings beside it) and returns the rate it sustained."""
+def mfma_hold(torch, B, seconds, grid=1024, iters=2000, constant=False):
+    """Runs the MFMA calibration kernel on random (or constant) bf16 operands for about
+    `seconds` and returns the rate it sustained; with board power and clock readings taken
+    beside it, the power-limited rate of bare matrix work."""
     buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(20240711)
-    ops = (torch.randn(1 << 23, generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
+    if constant:
+        ops = torch.full((1 << 23,), 0.01, device="cuda", dtype=torch.bfloat16)
+    else:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(20240711)
+        ops = (torch.randn(1 << 23, generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
     flops = B.mfma_probe(ops, buf, grid, iters)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -521,8 +509,8 @@ def mfma_hold(torch, B, seconds, grid=1024, iters=2000):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    return {"mfma_probe": "random bf16 operands", "launches": launches,
-            "seconds": round(ms / 1e3, 2),
+    return {"mfma_probe": "constant bf16 operands" if constant else "random bf16 operands",
+            "launches": launches, "seconds": round(ms / 1e3, 2),
             "tflops": round(flops * launches / (ms / 1e3) / 1e12, 1)}
 
 
