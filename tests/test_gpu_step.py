@@ -68,6 +68,8 @@ CASES = [
     (512, 1376, 128, "random", 2),     # down shape: n ragged, scale groups straddle rows
     (300, 200, 64, "random", 5),       # ragged everywhere, short last groups
     (2048, 5461, 64, "random", 2),     # odd n: unaligned rows take the element-wise path
+    (384, 1378, 64, "random", 2),      # n = 2 (mod 8): G rows 4-byte aligned, N~ rows padded
+    (333, 517, 40, "random", 3),       # odd m and n, rank not a multiple of 32
     (5461, 256, 32, "zero", 1),        # odd m: K tail of the projection, row tail of W
     (64, 40, 8, "random", 2),          # smallest rank
     (24, 13, 16, "random", 3),         # tiny, odd n, a single short group
