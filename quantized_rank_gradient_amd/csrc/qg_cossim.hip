@@ -433,6 +433,307 @@ __global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
                     pack_bf16x2(bf16_to_f32(a.y & 0xFFFFu) * s2, bf16_to_f32(a.y >> 16) * s2)));
 }
 
+// ------------------------------- 5: the whole chain in one workgroup (r <= 128) ---
+// For ranks up to kNsSmallMax the r x r matrices fit in LDS and the chain above costs far
+// more in launches than in products. One workgroup per pair then runs it from the block sums
+// of ||C||^2 to the result, on LDS-resident matrices, with the same products (same operand
+// ports, K order and hi/lo splitting), the same epilogue arithmetic and roundings, and the
+// same block and fold reductions, so that its result equals the multi-launch chain's.
+
+constexpr int kNsP = kNsSmallMax + 16;        // LDS row pitch (bf16): rows 8 banks apart
+constexpr int kNsMat = kNsSmallMax * kNsP;    // elements of one LDS matrix
+constexpr int kNsThreads = 512;               // 8 waves: 2 x 4 blocks of 64 x 32
+constexpr int kNsRed = 256;                   // block width of the reductions (as qg_cossim_dot)
+
+__device__ __forceinline__ int ns_wm() { return (threadIdx.x >> 6) >> 2; }
+__device__ __forceinline__ int ns_wn() { return (threadIdx.x >> 6) & 3; }
+// output row of accumulator entry v of 32-block x, and output column, for this lane
+__device__ __forceinline__ int ns_row(int x, int v) {
+  return ns_wm() * 64 + 32 * x + 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
+}
+__device__ __forceinline__ int ns_col() { return ns_wn() * 32 + (threadIdx.x & 31); }
+
+// Symmetric products (M^T M) are formed as the multi-launch chain forms them: 64 x 64 tiles
+// on and above the diagonal, each also written to its mirror position. A wave's 64 x 32
+// block lies in tile (wave row, wave column / 2).
+__device__ __forceinline__ bool ns_upper() { return ns_wm() <= (ns_wn() >> 1); }
+__device__ __forceinline__ bool ns_mirrors() { return ns_wm() < (ns_wn() >> 1); }
+
+// A-port fragment of a row-major LDS matrix read K-contiguous (8 K values of row c + lane%32).
+__device__ __forceinline__ bf16x8 ns_frag_rows(const uint16_t* M, int c, int ks) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const bf16x8*>(M + (c + (lane & 31)) * kNsP + ks + 8 * (lane >> 5));
+}
+
+// acc = products over K < kext (a multiple of 32) for this wave's 64 x 32 block: TA: M^T M
+// (both ports read M K-major); otherwise M Bop. PARTS == 2: Ml / Bl hold the bf16 low parts,
+// and each 16-K step adds hi*hi for both blocks, then hi*lo and lo*hi per block, in that
+// order (the multi-launch chain's order).
+template <bool TA, int PARTS>
+__device__ __forceinline__ void ns_mul(const uint16_t* M, const uint16_t* Ml, const uint16_t* Bo,
+                                       const uint16_t* Bl, int kext, f32x16 (&acc)[2]) {
+  const int am = ns_wm() * 64, bn = ns_wn() * 32;
+#pragma unroll
+  for (int ks = 0; ks < kNsSmallMax; ks += 16) {
+    if (ks >= kext) break;
+    bf16x8 a[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      a[x] = TA ? frag<true, kNsP>(M, am + 32 * x, ks) : ns_frag_rows(M, am + 32 * x, ks);
+    const bf16x8 b = frag<true, kNsP>(TA ? M : Bo, bn, ks);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b, ks == 0 ? f32x16{} : acc[x], 0, 0, 0);
+    if constexpr (PARTS == 2) {
+      bf16x8 al[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        al[x] = TA ? frag<true, kNsP>(Ml, am + 32 * x, ks) : ns_frag_rows(Ml, am + 32 * x, ks);
+      const bf16x8 bl = frag<true, kNsP>(TA ? Ml : Bl, bn, ks);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], bl, acc[x], 0, 0, 0);
+        acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[x], b, acc[x], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Y = beta * acc + alpha * E (E in bf16 from the LDS matrix E, skipped when alpha == 0),
+// rounded to bf16 into the LDS matrix Y; Y may be E (each lane reads and writes only its own
+// entries). Entries past r are left alone (they stay zero). SYM: a symmetric product's
+// blocks (see ns_upper).
+template <bool SYM>
+__device__ __forceinline__ void ns_put_bf16(const f32x16 (&acc)[2], int r, float alpha,
+                                            float beta, const uint16_t* E, uint16_t* Y) {
+  if (SYM && !ns_upper()) return;
+  const bool mirror = SYM && ns_mirrors();
+  const int j = ns_col();
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = ns_row(x, v);
+      if (i >= r || j >= r) continue;
+      float out = beta * acc[x][v];
+      if (alpha != 0.0f) out += alpha * bf16_to_f32(E[i * kNsP + j]);
+      Y[i * kNsP + j] = to_bf16(out);
+      if (mirror) Y[j * kNsP + i] = to_bf16(out);
+    }
+}
+
+// Sum over the block sums of 4-element dot products over the flat r x r order, as
+// qg_cossim_dot and qg_cossim_fold form it: thread t of block k takes elements
+// 4 (256 k + t) .. + 3, each block is reduced by the 256-way halving tree (all blocks at
+// once here), and the block sums are folded in double (strided, then the same tree).
+// V: LDS scratch of nblk * 256 floats; D: 256 doubles. Returns the fold on every thread.
+template <class Dot4>
+__device__ __forceinline__ double ns_blocked_dot(int n2, int nblk, Dot4 dot4, float* V, double* D) {
+  const int t = threadIdx.x;
+  for (int q = t; q < nblk * kNsRed; q += kNsThreads) {
+    const int e0 = q * 4;
+    V[q] = e0 < n2 ? dot4(e0) : 0.0f;
+  }
+  __syncthreads();
+  for (int w = kNsRed / 2; w > 0; w >>= 1) {
+    for (int q = t; q < nblk * w; q += kNsThreads) {
+      const int k = q / w, u = q - k * w;
+      V[k * kNsRed + u] += V[k * kNsRed + u + w];
+    }
+    __syncthreads();
+  }
+  if (t < kNsRed) {
+    double acc = 0.0;
+    for (int k = t; k < nblk; k += kNsRed) acc += V[k * kNsRed];
+    D[t] = acc;
+  }
+  __syncthreads();
+  for (int w = kNsRed / 2; w > 0; w >>= 1) {
+    if (t < w) D[t] += D[t + w];
+    __syncthreads();
+  }
+  const double res = D[0];
+  __syncthreads();
+  return res;
+}
+
+// grid = count (one workgroup per pair); runs after qg_cossim_gemm and qg_cossim_reduce.
+__global__ __launch_bounds__(kNsThreads, 1) void qg_ns_small(CosBatch b, float* out) {
+  __shared__ __attribute__((aligned(16))) uint16_t L[4 * kNsMat];
+  __shared__ double D[kNsRed];
+  constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
+  const int p = blockIdx.x, t = threadIdx.x;
+  const int r = b.r, n2 = r * r, nblk = b.nblk;
+  const int kext = (r + 31) / 32 * 32;
+  uint16_t* X = L;                 // X (bf16), then the high parts of the fp32 X
+  uint16_t* XL = L + kNsMat;       // low parts of the fp32 X
+  uint16_t* A = L + 2 * kNsMat;    // A = X^T X (bf16), then its high parts
+  uint16_t* Bm = L + 3 * kNsMat;   // B = b A + c A^2, then the low parts of A
+  f32x16 acc[2];
+
+  // zero padding: entries past r read as zero in every product
+  for (int q = t; q < 4 * kNsMat / 8; q += kNsThreads)
+    reinterpret_cast<uint4*>(L)[q] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  // ||C||_F^2 from the reduce kernel's block sums (qg_cossim_fold's order), X0 = bf16(C / ||C||)
+  {
+    const float* blk = pair_mat(b, p, b.off_blk);
+    if (t < kNsRed) {
+      double a0 = 0.0;
+      for (int k = t; k < nblk; k += kNsRed) a0 += blk[k];
+      D[t] = a0;
+    }
+    __syncthreads();
+    for (int w = kNsRed / 2; w > 0; w >>= 1) {
+      if (t < w) D[t] += D[t + w];
+      __syncthreads();
+    }
+    const float sq = (float)D[0];
+    __syncthreads();
+    const float inv = sq > 0.0f ? 1.0f / sqrtf(sq) : 0.0f;
+    const float* C = pair_mat(b, p, b.off_c);
+    for (int e0 = 4 * t; e0 < n2; e0 += 4 * kNsThreads) {
+      const float4 c = gload(reinterpret_cast<const float4*>(C + e0));
+      const int i = e0 / r, j = e0 - i * r;
+      *reinterpret_cast<uint2*>(X + i * kNsP + j) =
+          make_uint2(pack_bf16x2(c.x * inv, c.y * inv), pack_bf16x2(c.z * inv, c.w * inv));
+    }
+    __syncthreads();
+  }
+
+  // A = X0^T X0, then X *= s and A *= s^2 with s = ||A||_F^(-1/2)
+  if (ns_upper()) ns_mul<true, 1>(X, nullptr, nullptr, nullptr, kext, acc);
+  ns_put_bf16<true>(acc, r, 0.0f, 1.0f, nullptr, A);
+  __syncthreads();
+  {
+    float* V = reinterpret_cast<float*>(Bm);
+    const double sq = ns_blocked_dot(n2, nblk, [&](int e0) {
+      const int i = e0 / r, j = e0 - i * r;
+      const uint2 xb = *reinterpret_cast<const uint2*>(A + i * kNsP + j);
+      const float x0 = bf16_to_f32(xb.x & 0xFFFFu), x1 = bf16_to_f32(xb.x >> 16);
+      const float x2 = bf16_to_f32(xb.y & 0xFFFFu), x3 = bf16_to_f32(xb.y >> 16);
+      return x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+    }, V, D);
+    const float sqf = (float)sq;
+    const float sc = sqf > 0.0f ? 1.0f / sqrtf(sqrtf(sqf)) : 0.0f;
+    const float s2 = sc * sc;
+    for (int e0 = 4 * t; e0 < n2; e0 += 4 * kNsThreads) {
+      const int i = e0 / r, j = e0 - i * r;
+      uint2* xp = reinterpret_cast<uint2*>(X + i * kNsP + j);
+      uint2* ap = reinterpret_cast<uint2*>(A + i * kNsP + j);
+      const uint2 x = *xp, a = *ap;
+      *xp = make_uint2(pack_bf16x2(bf16_to_f32(x.x & 0xFFFFu) * sc, bf16_to_f32(x.x >> 16) * sc),
+                       pack_bf16x2(bf16_to_f32(x.y & 0xFFFFu) * sc, bf16_to_f32(x.y >> 16) * sc));
+      *ap = make_uint2(pack_bf16x2(bf16_to_f32(a.x & 0xFFFFu) * s2, bf16_to_f32(a.x >> 16) * s2),
+                       pack_bf16x2(bf16_to_f32(a.y & 0xFFFFu) * s2, bf16_to_f32(a.y >> 16) * s2));
+    }
+    // the block-sum scratch in Bm must read as zero again before B is formed there
+    for (int q = t; q < kNsMat / 8; q += kNsThreads)
+      reinterpret_cast<uint4*>(Bm)[q] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  // quintic steps: B = c A^2 + b A, X <- a X + X B
+  for (int it = 0; it < b.iters_quintic; ++it) {
+    if (it > 0) {
+      if (ns_upper()) ns_mul<true, 1>(X, nullptr, nullptr, nullptr, kext, acc);
+      ns_put_bf16<true>(acc, r, 0.0f, 1.0f, nullptr, A);
+      __syncthreads();
+    }
+    if (ns_upper()) ns_mul<true, 1>(A, nullptr, nullptr, nullptr, kext, acc);
+    ns_put_bf16<true>(acc, r, kQb, kQc, A, Bm);
+    __syncthreads();
+    ns_mul<false, 1>(X, nullptr, Bm, nullptr, kext, acc);
+    __syncthreads();                                  // every wave done reading X
+    ns_put_bf16<false>(acc, r, kQa, 1.0f, X, X);
+    __syncthreads();
+  }
+  // cubic steps with bf16 operands: X <- 1.5 X - 0.5 X A; the last one keeps X in fp32
+  float* Xg = pair_mat(b, p, b.off_x);   // this lane's fp32 X entries, read back only by it
+  for (int it = 0; it < b.iters_cubic_bf16; ++it) {
+    if (ns_upper()) ns_mul<true, 1>(X, nullptr, nullptr, nullptr, kext, acc);
+    ns_put_bf16<true>(acc, r, 0.0f, 1.0f, nullptr, A);
+    __syncthreads();
+    ns_mul<false, 1>(X, nullptr, A, nullptr, kext, acc);
+    __syncthreads();
+    if (it + 1 < b.iters_cubic_bf16) {
+      ns_put_bf16<false>(acc, r, 1.5f, -0.5f, X, X);
+    } else {
+      const int j = ns_col();
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = ns_row(x, v);
+          if (i >= r || j >= r) continue;
+          float o = -0.5f * acc[x][v];
+          o += 1.5f * bf16_to_f32(X[i * kNsP + j]);
+          gstore(Xg + i * r + j, o);
+          const uint16_t h = to_bf16(o);
+          X[i * kNsP + j] = h;
+          XL[i * kNsP + j] = to_bf16(o - bf16_to_f32(h));
+        }
+    }
+    __syncthreads();
+  }
+  // split steps: fp32 X and A as hi/lo bf16 pairs; the last X goes to LDS as flat fp32
+  float* Xf = reinterpret_cast<float*>(A);   // r * r floats over the A and Bm areas
+  for (int it = 0; it < b.iters_cubic_split; ++it) {
+    if (ns_upper()) ns_mul<true, 2>(X, XL, nullptr, nullptr, kext, acc);
+    __syncthreads();                                  // A and Bm are free
+    if (ns_upper()) {
+      const bool mirror = ns_mirrors();
+      const int j = ns_col();
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = ns_row(x, v);
+          if (i >= r || j >= r) continue;
+          const float o = 1.0f * acc[x][v];
+          const uint16_t h = to_bf16(o), l = to_bf16(o - bf16_to_f32(h));
+          A[i * kNsP + j] = h;
+          Bm[i * kNsP + j] = l;
+          if (mirror) {
+            A[j * kNsP + i] = h;
+            Bm[j * kNsP + i] = l;
+          }
+        }
+    }
+    __syncthreads();
+    ns_mul<false, 2>(X, XL, A, Bm, kext, acc);
+    __syncthreads();
+    const bool last = it + 1 == b.iters_cubic_split;
+    const int j = ns_col();
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = ns_row(x, v);
+        if (i >= r || j >= r) continue;
+        float o = -0.5f * acc[x][v];
+        o += 1.5f * gload(Xg + i * r + j);
+        if (last) {
+          Xf[i * r + j] = o;
+        } else {
+          gstore(Xg + i * r + j, o);
+          const uint16_t h = to_bf16(o);
+          X[i * kNsP + j] = h;
+          XL[i * kNsP + j] = to_bf16(o - bf16_to_f32(h));
+        }
+      }
+    __syncthreads();
+  }
+  // trace(X^T C) / r by the blocked dot and fold of qg_cossim_dot / qg_cossim_fold
+  const float* C = pair_mat(b, p, b.off_c);
+  const double tr = ns_blocked_dot(n2, nblk, [&](int e0) {
+    const float4 c = gload(reinterpret_cast<const float4*>(C + e0));
+    return Xf[e0] * c.x + Xf[e0 + 1] * c.y + Xf[e0 + 2] * c.z + Xf[e0 + 3] * c.w;
+  }, reinterpret_cast<float*>(X), D);
+  if (t == 0) out[p] = (float)(tr * (1.0f / (float)r));
+}
+
 // ------------------------------------------------------------------------ driver ---
 
 hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
@@ -445,6 +746,10 @@ hipError_t launch_cossim_batch(const CosBatch& b, float* out, hipStream_t s) {
     hipLaunchKernelGGL(qg_cossim_gemm<CosTile>, dim3(gemm_blocks), dim3(kThreads), 0, s, b);
   const int eblocks = b.count * b.nblk;
   hipLaunchKernelGGL(qg_cossim_reduce, dim3(eblocks), dim3(kThreads), 0, s, b);
+  if (b.r <= kNsSmallMax) {
+    hipLaunchKernelGGL(qg_ns_small, dim3(b.count), dim3(kNsThreads), 0, s, b, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(qg_cossim_fold, dim3(b.count), dim3(kThreads), 0, s, b, b.off_norm, 0.0f,
                      (float*)nullptr);
   hipLaunchKernelGGL(qg_cossim_init, dim3(eblocks), dim3(kThreads), 0, s, b);

@@ -15,6 +15,9 @@ constexpr int kCosTile = 64;
 // chip; smaller ranks use kCosTile.
 constexpr int kCosCTile = 128;
 constexpr int cos_ctile(int r) { return r >= 256 ? kCosCTile : kCosTile; }
+// Ranks up to this run the Newton-Schulz chain in one workgroup per pair, on LDS-resident
+// matrices (one launch instead of a launch per product).
+constexpr int kNsSmallMax = 128;
 
 struct CosPair {
   int format;          // projection storage format of both (kPInt4, kPInt8, kPBf16)

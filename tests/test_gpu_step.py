@@ -258,7 +258,8 @@ def test_cossim_batch_large_rank(r):
     assert np.all(np.abs(got - np.array(want)) <= 1e-4), (got, want)
 
 
-@pytest.mark.parametrize("m,r", [(512, 64), (4096, 128), (2048, 512), (1376, 264), (4096, 1024)])
+@pytest.mark.parametrize("m,r", [(600, 40), (512, 64), (1000, 96), (4096, 128), (2048, 512),
+                                 (1376, 264), (4096, 1024)])
 def test_cossim_matches_oracle(m, r):
     B = _B()
     rng = np.random.default_rng(m + r)
