@@ -442,22 +442,25 @@ __global__ __launch_bounds__(kThreads) void qg_ns_rescale(CosBatch b) {
 
 constexpr int kNsP = kNsSmallMax + 16;        // LDS row pitch (bf16): rows 8 banks apart
 constexpr int kNsMat = kNsSmallMax * kNsP;    // elements of one LDS matrix
-constexpr int kNsThreads = 512;               // 8 waves: 2 x 4 blocks of 64 x 32
+constexpr int kNsWM = 4, kNsWN = 4;           // waves along rows and columns
+constexpr int kNsXM = kNsSmallMax / 32 / kNsWM;  // 32-row blocks per wave
+constexpr int kNsThreads = 64 * kNsWM * kNsWN;
 constexpr int kNsRed = 256;                   // block width of the reductions (as qg_cossim_dot)
 
-__device__ __forceinline__ int ns_wm() { return (threadIdx.x >> 6) >> 2; }
-__device__ __forceinline__ int ns_wn() { return (threadIdx.x >> 6) & 3; }
+__device__ __forceinline__ int ns_wm() { return (threadIdx.x >> 6) / kNsWN; }
+__device__ __forceinline__ int ns_wn() { return (threadIdx.x >> 6) % kNsWN; }
 // output row of accumulator entry v of 32-block x, and output column, for this lane
 __device__ __forceinline__ int ns_row(int x, int v) {
-  return ns_wm() * 64 + 32 * x + 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
+  return ns_wm() * 32 * kNsXM + 32 * x + 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
 }
 __device__ __forceinline__ int ns_col() { return ns_wn() * 32 + (threadIdx.x & 31); }
 
 // Symmetric products (M^T M) are formed as the multi-launch chain forms them: 64 x 64 tiles
-// on and above the diagonal, each also written to its mirror position. A wave's 64 x 32
-// block lies in tile (wave row, wave column / 2).
-__device__ __forceinline__ bool ns_upper() { return ns_wm() <= (ns_wn() >> 1); }
-__device__ __forceinline__ bool ns_mirrors() { return ns_wm() < (ns_wn() >> 1); }
+// on and above the diagonal, each also written to its mirror position.
+__device__ __forceinline__ int ns_ti() { return ns_wm() * 32 * kNsXM / 64; }
+__device__ __forceinline__ int ns_tj() { return ns_wn() / 2; }
+__device__ __forceinline__ bool ns_upper() { return ns_ti() <= ns_tj(); }
+__device__ __forceinline__ bool ns_mirrors() { return ns_ti() < ns_tj(); }
 
 // A-port fragment of a row-major LDS matrix read K-contiguous (8 K values of row c + lane%32).
 __device__ __forceinline__ bf16x8 ns_frag_rows(const uint16_t* M, int c, int ks) {
@@ -465,33 +468,33 @@ __device__ __forceinline__ bf16x8 ns_frag_rows(const uint16_t* M, int c, int ks)
   return *reinterpret_cast<const bf16x8*>(M + (c + (lane & 31)) * kNsP + ks + 8 * (lane >> 5));
 }
 
-// acc = products over K < kext (a multiple of 32) for this wave's 64 x 32 block: TA: M^T M
+// acc = products over K < kext (a multiple of 32) for this wave's blocks: TA: M^T M
 // (both ports read M K-major); otherwise M Bop. PARTS == 2: Ml / Bl hold the bf16 low parts,
-// and each 16-K step adds hi*hi for both blocks, then hi*lo and lo*hi per block, in that
+// and each 16-K step adds hi*hi for all blocks, then hi*lo and lo*hi per block, in that
 // order (the multi-launch chain's order).
 template <bool TA, int PARTS>
 __device__ __forceinline__ void ns_mul(const uint16_t* M, const uint16_t* Ml, const uint16_t* Bo,
-                                       const uint16_t* Bl, int kext, f32x16 (&acc)[2]) {
-  const int am = ns_wm() * 64, bn = ns_wn() * 32;
-#pragma unroll
+                                       const uint16_t* Bl, int kext, f32x16 (&acc)[kNsXM]) {
+  const int am = ns_wm() * 32 * kNsXM, bn = ns_wn() * 32;
+#pragma unroll 2
   for (int ks = 0; ks < kNsSmallMax; ks += 16) {
     if (ks >= kext) break;
-    bf16x8 a[2];
+    bf16x8 a[kNsXM];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < kNsXM; ++x)
       a[x] = TA ? frag<true, kNsP>(M, am + 32 * x, ks) : ns_frag_rows(M, am + 32 * x, ks);
     const bf16x8 b = frag<true, kNsP>(TA ? M : Bo, bn, ks);
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < kNsXM; ++x)
       acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b, ks == 0 ? f32x16{} : acc[x], 0, 0, 0);
     if constexpr (PARTS == 2) {
-      bf16x8 al[2];
+      bf16x8 al[kNsXM];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < kNsXM; ++x)
         al[x] = TA ? frag<true, kNsP>(Ml, am + 32 * x, ks) : ns_frag_rows(Ml, am + 32 * x, ks);
       const bf16x8 bl = frag<true, kNsP>(TA ? Ml : Bl, bn, ks);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      for (int x = 0; x < kNsXM; ++x) {
         acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], bl, acc[x], 0, 0, 0);
         acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[x], b, acc[x], 0, 0, 0);
       }
@@ -504,13 +507,13 @@ __device__ __forceinline__ void ns_mul(const uint16_t* M, const uint16_t* Ml, co
 // entries). Entries past r are left alone (they stay zero). SYM: a symmetric product's
 // blocks (see ns_upper).
 template <bool SYM>
-__device__ __forceinline__ void ns_put_bf16(const f32x16 (&acc)[2], int r, float alpha,
+__device__ __forceinline__ void ns_put_bf16(const f32x16 (&acc)[kNsXM], int r, float alpha,
                                             float beta, const uint16_t* E, uint16_t* Y) {
   if (SYM && !ns_upper()) return;
   const bool mirror = SYM && ns_mirrors();
   const int j = ns_col();
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < kNsXM; ++x)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int i = ns_row(x, v);
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(kNsThreads, 1) void qg_ns_small(CosBatch b, float* 
   uint16_t* XL = L + kNsMat;       // low parts of the fp32 X
   uint16_t* A = L + 2 * kNsMat;    // A = X^T X (bf16), then its high parts
   uint16_t* Bm = L + 3 * kNsMat;   // B = b A + c A^2, then the low parts of A
-  f32x16 acc[2];
+  f32x16 acc[kNsXM];
 
   // zero padding: entries past r read as zero in every product
   for (int q = t; q < 4 * kNsMat / 8; q += kNsThreads)
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kNsThreads, 1) void qg_ns_small(CosBatch b, float* 
     } else {
       const int j = ns_col();
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < kNsXM; ++x)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = ns_row(x, v);
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(kNsThreads, 1) void qg_ns_small(CosBatch b, float* 
       const bool mirror = ns_mirrors();
       const int j = ns_col();
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < kNsXM; ++x)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = ns_row(x, v);
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(kNsThreads, 1) void qg_ns_small(CosBatch b, float* 
     const bool last = it + 1 == b.iters_cubic_split;
     const int j = ns_col();
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < kNsXM; ++x)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = ns_row(x, v);
