@@ -506,13 +506,29 @@ __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L
   const float inv0 = recip_or_zero(bloadf(c.rws, g0 * 4));
   float inv1 = inv0;
   if (g1 != g0) inv1 = recip_or_zero(bloadf(c.rws, g1 * 4));
+  // the run's 8 code bytes from the three dwords at the aligned offset at or below e0 (bytes
+  // past the row belong to the next one and are not used); the layer's last run, whose dwords
+  // may reach past W's end, reads byte by byte
+  uint32_t wb[2];
+  const uint32_t base = e0 & ~3u;
+  if (base + 12 <= c.m * c.n) {
+    const uint32_t w0 = bload32(c.rw, base), w1 = bload32(c.rw, base + 4);
+    const uint32_t w2 = bload32(c.rw, base + 8);
+    wb[0] = __builtin_amdgcn_alignbyte(w1, w0, e0 & 3u);
+    wb[1] = __builtin_amdgcn_alignbyte(w2, w1, e0 & 3u);
+  } else {
+    wb[0] = wb[1] = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      wb[t >> 2] |= (bload8(c.rw, j8 + t < c.n ? e0 + t : kOOB) & 0xFFu) << (8 * (t & 3));
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const bool in = j8 + t < c.n;
     const uint32_t e = e0 + t;
     const float U = mul_rn(L.alpha, S[t]);
     const float iv = (e >> 8) == g0 ? inv0 : inv1;
-    const int w = (int)(int8_t)bload8(c.rw, in ? e : kOOB);
+    const int w = (int)(int8_t)(wb[t >> 2] >> (8 * (t & 3)));
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
     const float d = sr_pre(w, U, iv, bits);
     const int nw = __builtin_isfinite(d) ? sr_code(d) : w;
