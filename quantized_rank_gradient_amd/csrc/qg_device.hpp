@@ -47,6 +47,9 @@ struct LayerDev {
   int32_t b_tiles_j;   // back-projection tiles along n
   int32_t wg_base[4];  // first workgroup of this layer in the projection / Adam /
                        // back-projection / dequant launch of a grouped step
+  int32_t fold_alpha;  // 1: U is not written and alpha = 2^k (-126 < k <= 0), so the rounding
+                       // takes S * fl(alpha / s) in place of fl(alpha S) * (1 / s): the same
+                       // value wherever alpha S is a normal number or zero
   float lr, eps, alpha;
 };
 

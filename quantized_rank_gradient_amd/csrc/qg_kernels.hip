@@ -428,7 +428,9 @@ __device__ __forceinline__ int sr_code(float d) {
 
 // Vector path (rows a multiple of 16): 16 consecutive weights (i, j16 .. j16+15), j16 a
 // multiple of 16, arrive prefetched in `wv`; they lie in one scale group (reciprocal `inv`)
-// and take two Philox blocks.
+// and take two Philox blocks. FOLD (the layer's fold_alpha): U is not written and `inv`
+// holds fl(alpha * (1/s)), so that U * (1/s) is taken as S * inv, one multiply per weight.
+template <bool FOLD>
 __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
                                            const StepArgs& a, uint32_t i, uint32_t j16,
                                            const float* S, float inv, uint4 wv) {
@@ -450,7 +452,7 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
   float amax = 0.0f;
   static_for<16>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
-    U[t] = mul_rn(L.alpha, S[t]);
+    U[t] = FOLD ? S[t] : mul_rn(L.alpha, S[t]);
     wf[t] = sbyte_to_f32<t & 3>(win[t >> 2]);
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
     const float a = mul_rn(U[t], inv);
@@ -483,7 +485,7 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
     }
   }
   bstore128(c.rw, e0, make_uint4(wout[0], wout[1], wout[2], wout[3]));
-  if (c.write_u) {
+  if (!FOLD && c.write_u) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       bstore128(c.ru, (e0 + 4 * k) * 4,
@@ -493,7 +495,8 @@ __device__ __forceinline__ void sr_block16(const SrCtx& c, const LayerDev& L,
 }
 
 // Element path for rows whose length is not a multiple of 16 (possibly straddling scale
-// groups): byte accesses and a scale lookup per element.
+// groups): byte accesses and a scale lookup per element. FOLD as for sr_block16.
+template <bool FOLD>
 __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L,
                                                const StepArgs& a, uint32_t i, uint32_t j8,
                                                const float* S) {
@@ -503,9 +506,13 @@ __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L
   const uint32_t e0 = i * c.n + j8;
   // the run's (at most 8) weights lie in at most two scale groups
   const uint32_t g0 = e0 >> 8, g1 = (e0 + min(8u, c.n - j8) - 1) >> 8;
-  const float inv0 = recip_or_zero(bloadf(c.rws, g0 * 4));
+  float inv0 = recip_or_zero(bloadf(c.rws, g0 * 4));
   float inv1 = inv0;
   if (g1 != g0) inv1 = recip_or_zero(bloadf(c.rws, g1 * 4));
+  if (FOLD) {
+    inv0 = mul_rn(L.alpha, inv0);
+    inv1 = mul_rn(L.alpha, inv1);
+  }
   // the run's 8 code bytes from the three dwords at the aligned offset at or below e0 (bytes
   // past the row belong to the next one and are not used); the layer's last run, whose dwords
   // may reach past W's end, reads byte by byte
@@ -526,14 +533,14 @@ __device__ __forceinline__ void sr_block8_elem(const SrCtx& c, const LayerDev& L
   for (int t = 0; t < 8; ++t) {
     const bool in = j8 + t < c.n;
     const uint32_t e = e0 + t;
-    const float U = mul_rn(L.alpha, S[t]);
+    const float U = FOLD ? S[t] : mul_rn(L.alpha, S[t]);
     const float iv = (e >> 8) == g0 ? inv0 : inv1;
     const int w = (int)(int8_t)(wb[t >> 2] >> (8 * (t & 3)));
     const uint32_t bits = (t & 1) ? (words[t >> 1] >> 16) : (words[t >> 1] & 0xFFFFu);
     const float d = sr_pre(w, U, iv, bits);
     const int nw = __builtin_isfinite(d) ? sr_code(d) : w;
     bstore8(c.rw, in ? e : kOOB, (uint32_t)nw);
-    if (c.write_u) bstoref(c.ru, in ? e * 4 : kOOB, U);
+    if (!FOLD && c.write_u) bstoref(c.ru, in ? e * 4 : kOOB, U);
   }
 }
 
@@ -604,8 +611,9 @@ using BackCodes = DmaInt4C<128, 32>;
 // multiple of 8 elements in the workspace). VEC: rows of W are a multiple of 16 elements, so
 // the rounding takes 16-byte weight accesses (prefetched before the product); otherwise it
 // takes byte accesses along the rows. BASE is the tile whose LDS area the kernel declares. PM
-// as for the projection.
-template <class T, bool VEC, class BASE, int PM>
+// as for the projection. FOLD: every layer of the launch has fold_alpha (alpha folded into
+// the reciprocals of the rounding, U not written).
+template <class T, bool VEC, class BASE, int PM, bool FOLD>
 __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, int local,
                                           uint16_t* lds, uint8_t* codes) {
   static_assert(T::DMA, "operands staged by DMA");
@@ -692,7 +700,8 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
   float* E = reinterpret_cast<float*>(lds) + wave * 32 * EP;
   if constexpr (VEC) {
-    const float inv_row = row_groups ? recip_or_zero(s_row) : 0.0f;
+    const float inv_row0 = row_groups ? recip_or_zero(s_row) : 0.0f;
+    const float inv_row = FOLD ? mul_rn(L.alpha, inv_row0) : inv_row0;
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
@@ -701,12 +710,17 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
         const int row = RPP * p + vr;
         const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + row;
         // the shuffle runs on every lane (a lane whose run is off the layer only serves)
-        const float inv = row_groups ? __shfl(inv_row, 32 * x + row, 64)
-                                     : recip_or_zero(sv[x][p]);
+        float inv;
+        if (row_groups) {
+          inv = __shfl(inv_row, 32 * x + row, 64);
+        } else {
+          inv = recip_or_zero(sv[x][p]);
+          if (FOLD) inv = mul_rn(L.alpha, inv);
+        }
         if (i < c.m && j16 < c.n) {
           float S[16];
           read_run16(E, row * EP + vc, S);
-          sr_block16(c, L, a, i, j16, S, inv, wv[x][p]);
+          sr_block16<FOLD>(c, L, a, i, j16, S, inv, wv[x][p]);
         }
       }
       __syncthreads();
@@ -726,7 +740,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
         if (i < c.m && j8 < c.n) {
           float S[8];
           read_run(E, row * EP + vc8, S);
-          sr_block8_elem(c, L, a, i, j8, S);
+          sr_block8_elem<FOLD>(c, L, a, i, j8, S);
         }
       }
       __syncthreads();
@@ -736,16 +750,16 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
 
 // The large tile is held to 256 registers per lane: two workgroups per CU (two waves per
 // SIMD) hide the load latency better than more registers in one. The small one to 128.
-template <class T, int PM>
+template <class T, int PM, bool FOLD>
 __global__ __launch_bounds__(kThreads, BackLds<T>::MINB) void qg_backproject(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[BackLds<T>::bytes(PM) / 2];
   uint8_t* codes = reinterpret_cast<uint8_t*>(lds) + BackLds<T>::RING;
   int local;
   const LayerDev L = fetch_layer(a, KBACK, xcd_remap(blockIdx.x, gridDim.x), local);
   if (L.n % 16 == 0)
-    back_tile<DmaOf<T>, true, T, PM>(a, L, local, lds, codes);
+    back_tile<DmaOf<T>, true, T, PM, FOLD>(a, L, local, lds, codes);
   else
-    back_tile<DmaOf<T>, false, T, PM>(a, L, local, lds, codes);
+    back_tile<DmaOf<T>, false, T, PM, FOLD>(a, L, local, lds, codes);
 }
 
 // ================================================================ quantization of P ===
@@ -819,20 +833,23 @@ hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(qg_adam, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
-template <class T>
+template <class T, bool FOLD>
 static void launch_back_t(const StepArgs& a, int grid, int pmode, hipStream_t s) {
   if (pmode == kPInline)
-    hipLaunchKernelGGL((qg_backproject<T, kPInline>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((qg_backproject<T, kPInline, FOLD>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (pmode == kPMixed)
-    hipLaunchKernelGGL((qg_backproject<T, kPMixed>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((qg_backproject<T, kPMixed, FOLD>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((qg_backproject<T, kPStaged>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((qg_backproject<T, kPStaged, FOLD>), dim3(grid), dim3(kThreads), 0, s, a);
 }
-hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, hipStream_t s) {
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, bool fold,
+                              hipStream_t s) {
   if (big)
-    launch_back_t<BackBig>(a, grid, pmode, s);
+    fold ? launch_back_t<BackBig, true>(a, grid, pmode, s)
+         : launch_back_t<BackBig, false>(a, grid, pmode, s);
   else
-    launch_back_t<BackSmall>(a, grid, pmode, s);
+    fold ? launch_back_t<BackSmall, true>(a, grid, pmode, s)
+         : launch_back_t<BackSmall, false>(a, grid, pmode, s);
   return hipGetLastError();
 }
 hipError_t launch_quantize_int4(const float* P, int64_t numel, uint8_t* Pq, float* Ps,

@@ -59,7 +59,9 @@ constexpr int kBackTileN(bool big) { return big ? 256 : 128; }
 hipError_t launch_project(const StepArgs& a, int grid, int pmode, hipStream_t s);
 hipError_t launch_dequant(const StepArgs& a, int grid, hipStream_t s);
 hipError_t launch_adam(const StepArgs& a, int grid, hipStream_t s);
-hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, hipStream_t s);
+// fold: every layer of the launch has fold_alpha set.
+hipError_t launch_backproject(const StepArgs& a, int grid, bool big, int pmode, bool fold,
+                              hipStream_t s);
 // A rank whose INT4 projection the MFMA kernels can dequantize in their stagers: each row's
 // run of a projection tile (128 rank indices) and of a back-projection stage (32) lies inside
 // one 256-element scale group.

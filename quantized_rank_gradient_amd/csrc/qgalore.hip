@@ -94,6 +94,17 @@ bool valid_dequant_mode(int32_t mode) {
 // Row pitch of N~ in the workspace (elements): 16-byte aligned rows for any n.
 int64_t n_pitch(int64_t n) { return round_up(n, 8); }
 
+// alpha = 2^k with -126 < k <= 0. Scaling by such a power of two is exact in fp32 except for
+// results in the subnormal range, so fl(fl(alpha S) * inv) = fl(S * fl(alpha inv)) whenever
+// alpha S is normal or zero and alpha inv is normal, zero or infinite; elsewhere the two differ
+// by less than 2^-21 (one rounding in the subnormal range, at most 2^-150, times an inv below
+// 2^128, plus the roundings of the two products).
+bool alpha_folds(float alpha) {
+  int e = 0;
+  const float f = std::frexp(alpha, &e);   // alpha = f 2^e, 0.5 <= f < 1
+  return f == 0.5f && e - 1 <= 0 && e - 1 > -126;
+}
+
 // Per-layer workspace: split-K partial sums of R (fp32; absent when Adam is fused into the
 // projection), the bf16 update N~ (r x n) and, for projections the MFMA kernels do not
 // dequantize themselves, the bf16 dequantized projection P~ (m x r) that both read.
@@ -213,6 +224,7 @@ LayerDev make_layer(const qg_layer_desc* d, const uint16_t* G, int8_t* W_q, cons
   L.lr = d->lr;
   L.eps = d->eps;
   L.alpha = d->alpha;
+  L.fold_alpha = (d->U_out == nullptr && alpha_folds(d->alpha)) ? 1 : 0;
   return L;
 }
 
@@ -226,7 +238,8 @@ int grid_dequant(const LayerDev& L) {
                                                  : (int)cdiv(L.m * L.r, qg::kThreads * qg::kDeqCodes);
 }
 
-qg_status launch_step(const StepArgs& a, const int grid[4], bool big, int pmode, hipStream_t s) {
+qg_status launch_step(const StepArgs& a, const int grid[4], bool big, int pmode, bool fold,
+                      hipStream_t s) {
   hipError_t e = hipSuccess;
   if (grid[3] > 0 && (e = qg::launch_dequant(a, grid[3], s)) != hipSuccess)
     return hip_fail(e, "dequant kernel launch");
@@ -234,7 +247,7 @@ qg_status launch_step(const StepArgs& a, const int grid[4], bool big, int pmode,
   if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   if (grid[1] > 0 && (e = qg::launch_adam(a, grid[1], s)) != hipSuccess)
     return hip_fail(e, "Adam kernel launch");
-  e = qg::launch_backproject(a, grid[2], big, pmode, s);
+  e = qg::launch_backproject(a, grid[2], big, pmode, fold, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   return QG_OK;
 }
@@ -284,7 +297,7 @@ extern "C" qg_status qgalore_step(const qg_layer_desc* d, const uint16_t* G, int
   const int grid[4] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one),
                        grid_dequant(a.one)};
   return launch_step(a, grid, big, a.one.p_inline ? qg::kPInline : qg::kPStaged,
-                     static_cast<hipStream_t>(d->stream));
+                     a.one.fold_alpha != 0, static_cast<hipStream_t>(d->stream));
 }
 
 // ============================================= single layer without a workspace argument ===
@@ -353,7 +366,7 @@ extern "C" qg_status qgalore_step_noalloc(const qg_layer_desc* d, const uint16_t
   const int grid[4] = {grid_project(a.one), grid_adam(a.one), grid_back(a.one),
                        grid_dequant(a.one)};
   return launch_step(a, grid, big, a.one.p_inline ? qg::kPInline : qg::kPStaged,
-                     static_cast<hipStream_t>(d->stream));
+                     a.one.fold_alpha != 0, static_cast<hipStream_t>(d->stream));
 }
 
 // ========================================================================= grouped ===
@@ -367,6 +380,7 @@ struct qg_plan {
   float beta1 = 0.f, beta2 = 0.f;
   bool big = false;
   int pmode = qg::kPStaged;   // projection paths of the MFMA launches (all staged / inline / mix)
+  bool fold = false;          // every layer has fold_alpha
   int device = 0;
   std::vector<hipEvent_t> events;   // 5 per recorded step when timing is enabled
   int timing_cap = 0;
@@ -447,6 +461,9 @@ extern "C" qg_status qgalore_plan_create(const qg_layer* layers, int32_t count, 
   int n_inline = 0;
   for (const LayerDev& L : p->layers) n_inline += L.p_inline;
   p->pmode = n_inline == 0 ? qg::kPStaged : n_inline == count ? qg::kPInline : qg::kPMixed;
+  int n_fold = 0;
+  for (const LayerDev& L : p->layers) n_fold += L.fold_alpha;
+  p->fold = n_fold == count;
   p->proj_dirty.assign((size_t)count, 1);
 
   hipError_t e = hipGetDevice(&p->device);
@@ -529,7 +546,7 @@ extern "C" qg_status qgalore_plan_step(qg_plan* p, int64_t step, uint64_t seed, 
     return hip_fail(e, "Adam kernel launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "timing event");
   a.wg_layer = p->d_map[2];
-  e = qg::launch_backproject(a, p->grid[2], p->big, p->pmode, s);
+  e = qg::launch_backproject(a, p->grid[2], p->big, p->pmode, p->fold, s);
   if (e != hipSuccess) return hip_fail(e, "back-projection kernel launch");
   if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "timing event");
   return QG_OK;

@@ -76,3 +76,54 @@ def test_int4_dequant_by_one_fma_is_the_rounded_product():
         want = (np.float32(q) * s).astype(np.float32)
         assert np.array_equal(got.view(np.uint32) & 0x7FFFFFFF, want.view(np.uint32) & 0x7FFFFFFF) \
             and np.array_equal(got, want), q
+
+
+# ---------------------------------------------------------------------------------------
+# The rounding's alpha fold. With alpha = 2^k (-126 < k <= 0) and U not written, the
+# back-projection takes U * (1/s) as S * fl(alpha * (1/s)) instead of fl(alpha * S) * (1/s).
+# Scaling by a power of two is exact outside the subnormal range, so the two agree bit for bit
+# whenever alpha * S is normal or zero and alpha * (1/s) is normal, zero or infinite; where
+# alpha * S is subnormal they differ by less than 2^-21 (one rounding of at most 2^-150, times
+# a reciprocal below 2^128, plus the final roundings of the two products).
+
+def _unfolded(S, inv, alpha):
+    with np.errstate(all="ignore"):
+        return ((alpha * S).astype(np.float32) * inv).astype(np.float32)
+
+
+def _folded(S, inv, alpha):
+    with np.errstate(all="ignore"):
+        return (S * (alpha * inv).astype(np.float32)).astype(np.float32)
+
+
+def test_alpha_fold_is_exact_outside_the_subnormal_range():
+    rng = np.random.default_rng(23)
+    n = 2_000_000
+    S = (rng.standard_normal(n) * np.exp2(rng.integers(-100, 20, n))).astype(np.float32)
+    inv = np.abs(rng.standard_normal(n) * np.exp2(rng.integers(-20, 126, n))).astype(np.float32)
+    S[:4] = [0.0, -0.0, 3.0, -5.0]
+    inv[:4] = [7.0, np.inf, 0.0, np.inf]
+    for k in (0, -1, -2, -7, -20):
+        alpha = np.float32(2.0 ** k)
+        a, b = _unfolded(S, inv, alpha), _folded(S, inv, alpha)
+        aS = np.abs(S.astype(np.float64) * float(alpha))
+        inside = (aS == 0) | (aS >= 2.0 ** -126)
+        assert inside.mean() > 0.9
+        assert _same(a, b)[inside].all(), k
+        # signed zeros agree too (they decide floor(-0) = -0 against floor(+0))
+        assert (np.signbit(a) == np.signbit(b))[inside & ~np.isnan(a)].all()
+
+
+def test_alpha_fold_differs_by_less_than_two_to_minus_21_in_the_subnormal_range():
+    rng = np.random.default_rng(29)
+    n = 1_000_000
+    alpha = np.float32(0.25)
+    # |alpha S| below 2^-126: fl(alpha S) is rounded in the subnormal range
+    S = (rng.uniform(-1, 1, n) * np.exp2(rng.integers(-150, -124, n))).astype(np.float32)
+    inv = np.exp2(rng.uniform(0, 127.9, n)).astype(np.float32)
+    a = _unfolded(S, inv, alpha).astype(np.float64)
+    b = _folded(S, inv, alpha).astype(np.float64)
+    fin = np.isfinite(a) & np.isfinite(b)
+    assert fin.all()
+    assert np.abs(a - b).max() < 2.0 ** -21
+    assert (a != b).any(), "the subnormal range does round differently"
