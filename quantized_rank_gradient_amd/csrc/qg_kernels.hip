@@ -702,6 +702,7 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
   if constexpr (VEC) {
     const float inv_row0 = row_groups ? recip_or_zero(s_row) : 0.0f;
     const float inv_row = FOLD ? mul_rn(L.alpha, inv_row0) : inv_row0;
+    const int vr4 = 4 * vr;   // ds_bpermute byte address of lane vr
 #pragma clang loop unroll(full)
     for (int x = 0; x < T::XM; ++x) {
       stage_rows<T, EP>(E, acc[x]);
@@ -709,10 +710,12 @@ __device__ __forceinline__ void back_tile(const StepArgs& a, const LayerDev& L, 
       for (int p = 0; p < NP; ++p) {
         const int row = RPP * p + vr;
         const uint32_t i = (uint32_t)i0 + wm * T::WTM + 32 * x + row;
-        // the shuffle runs on every lane (a lane whose run is off the layer only serves)
+        // the shuffle runs on every lane (a lane whose run is off the layer only serves); its
+        // byte address is the lane's own part plus a constant the instruction's offset holds
         float inv;
         if (row_groups) {
-          inv = __shfl(inv_row, 32 * x + row, 64);
+          inv = __int_as_float(__builtin_amdgcn_ds_bpermute(
+              vr4 + 4 * (32 * x + RPP * p), __float_as_int(inv_row)));
         } else {
           inv = recip_or_zero(sv[x][p]);
           if (FOLD) inv = mul_rn(L.alpha, inv);
