@@ -109,7 +109,11 @@ typedef struct {
   float lr, beta1, beta2, eps, alpha;   /* Adam (0 <= beta < 1, eps >= 0) and the update scale */
   float *M_scale, *V_scale; /* fp32[ceil(r*n/256)], read and rewritten in place */
   float *R_out;             /* optional fp32 r x n: the projected gradient R (NULL = skip) */
-  float *U_out;             /* optional fp32 m x n: the back-projected update U (NULL = skip) */
+  float *U_out;             /* optional fp32 m x n: the back-projected update U (NULL = skip).
+                             * With U skipped and alpha a power of two in [2^-125, 1], the
+                             * rounding takes U / s_W as S * fl(alpha / s_W) (S = P~ N~): the
+                             * same number wherever alpha S is normal or zero, so the W codes
+                             * match those of a call that writes U (which rounds fl(alpha S)). */
   void *workspace;          /* caller-owned device scratch, >= qgalore_workspace_bytes() */
   size_t workspace_bytes;
   void *stream;             /* hipStream_t */
