@@ -56,6 +56,34 @@ def test_noalloc_step_matches_the_workspace_step_twice():
         PAR.check_step(before, res, st, outs["noalloc"], t=t)
 
 
+@pytest.mark.gpu
+def test_noalloc_step_without_u_matches_the_workspace_step():
+    """Both entry points without U (the rounding's alpha-folded path), two calls in a row, the
+    second smaller: every output bit-identical between them."""
+    B = _B()
+    assert torch.cuda.is_available()
+    for (m, n, r, t) in [(1376, 512, 128, 2), (333, 517, 40, 3)]:
+        cfg = WL.Config("custom", 9, (WL.LayerShape(6, f"{m}x{n}", m, n),), r=r, sigma=1e-3)
+        L = cfg.layers[0]
+        st, P = PAR.host_state(cfg, L, r, "random")
+        G = WL.gradient_bf16(cfg, L, t)
+        outs = {}
+        for which in ("workspace", "noalloc"):
+            Lt = PAR.to_device(st, G, P)
+            R_out = torch.empty((r, n), dtype=torch.float32, device="cuda")
+            hp = dict(lr=1e-3, alpha=0.25)
+            if which == "workspace":
+                B.step(Lt, t, WL.SR_SEED, hp=hp, R_out=R_out)
+            else:
+                B.step_noalloc(Lt, t, WL.SR_SEED, hp=hp, R_out=R_out)
+            torch.cuda.synchronize()
+            outs[which] = {k: getattr(Lt, k).cpu().numpy() for k in ("Wq", "Mq", "Ms", "Vq", "Vs")}
+            outs[which]["R"] = R_out.cpu().numpy()
+        for k in outs["workspace"]:
+            assert np.array_equal(outs["noalloc"][k].view(np.uint8),
+                                  outs["workspace"][k].view(np.uint8)), (m, n, r, k)
+
+
 def test_noalloc_step_rejects_a_layer_beyond_its_scratch():
     """A layer whose scratch exceeds the fixed array: QG_ERR_WORKSPACE before any HIP call."""
     B = _B()
