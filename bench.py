@@ -18,6 +18,7 @@ import argparse
 import dataclasses
 import json
 import os
+import re
 import sys
 import time
 
@@ -115,6 +116,7 @@ class Variant:
         hp = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, alpha=cfg.alpha)
         nl = len(self.layers)
         w = window if 0 < window < nl else nl
+        self.window = w if w < nl else None
         self.chunks = [(a, min(nl, a + w)) for a in range(0, nl, w)]
         self.plans = []     # per gradient set: one plan per chunk of layers
         for Gs in G_sets:
@@ -279,12 +281,15 @@ def algorithmic(cfg, r, fmt="int4", inline=False):
     return dict(mn=mn, flops=flops, bytes=nbytes, ops=ops, fused_adam=fused)
 
 
-def roofline(cfg, r, kms, fmt="int4", inline=False):
+def roofline(cfg, r, kms, fmt="int4", inline=False, launches=1):
+    """kms: each kernel's time per step; launches: the launches of each kernel per step (the
+    plans of a windowed step), each doing an equal share of the set's work."""
     a = algorithmic(cfg, r, fmt, inline)
     names = KERNELS
     k = max(range(4), key=lambda i: kms[i])            # dominant kernel
     sec = kms[k] / 1e3
-    traffic = measured_traffic(cfg.key, names[k]) if fmt == "int4" else None
+    # the counter summaries hold one launch over the whole set
+    traffic = measured_traffic(cfg.key, names[k]) if fmt == "int4" and launches == 1 else None
     if k == 1 and a["fused_adam"]:
         names = list(names)
         names[1] = "qg_project (+ Adam)"
@@ -293,7 +298,8 @@ def roofline(cfg, r, kms, fmt="int4", inline=False):
     t_hbm = a["bytes"][k] / (HBM_PEAK_GBS * 1e9)
     t_mfma = a["flops"][k] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
     t_alu = a["ops"][k] / (ALU_PEAK_TOPS * 1e12)
-    common = dict(kernel=names[k], traffic=traffic, ms_per_launch=round(kms[k], 4),
+    common = dict(kernel=names[k], traffic=traffic, ms_per_launch=round(kms[k] / launches, 4),
+                  **({"launches_per_step": launches} if launches > 1 else {}),
                   lower_bound_ms={"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4),
                                   "alu": round(t_alu * 1e3, 4)})
     if t_mfma >= max(t_hbm, t_alu):
@@ -657,9 +663,10 @@ def main():
                          "between steps (only refreshed layers are dequantized again)")
     ap.add_argument("--g-sets", type=int, default=4,
                     help="gradient sets resident in HBM, used in turn by the timed steps")
-    ap.add_argument("--configs", default="single256,llama60m,llama1b",
+    ap.add_argument("--configs", default="single256,llama60m,llama1b,llama7b_r1024_window56",
                     help="the other layer sets timed and reported under 'configs' "
-                         "(comma-separated; 'none' to skip)")
+                         "(comma-separated; 'none' to skip; <set>_window<N>: that set's step "
+                         "in plans of N layers sharing one workspace)")
     ap.add_argument("--config-steps", type=int, default=20,
                     help="timed steps of each of the other layer sets")
     ap.add_argument("--no-schedule", action="store_true",
@@ -761,7 +768,7 @@ def main():
             "gradient_sets": main_res["gradient_sets"],
             "parallelism": "single GPU",
         },
-        **{k: main_res[k] for k in ("step_ms_percentiles", "tflops", "dequant",
+        **{k: main_res[k] for k in ("step_ms_percentiles", "tflops", "dequant", "window",
                                     "workspace_gib", "projection_gib",
                                     "kernel_ms", "optimizer_ms", "refresh_tests_per_step",
                                     "cossim_ms", "roofline")},
@@ -776,9 +783,12 @@ def main():
     torch.cuda.empty_cache()
     if args.configs != "none":
         for key in args.configs.split(","):
-            c = WL.CONFIGS[key]
+            # "<set>_window<N>": the set's step in plans of N layers sharing one workspace
+            m = re.fullmatch(r"(.+)_window(\d+)", key)
+            c = WL.CONFIGS[m.group(1) if m else key]
             steps = c.steps if c.steps > 1 else args.config_steps
-            subs[key] = run_layer_set(args, torch, B, WL, c, None, 2, steps, args.warmup)[0]
+            subs[key] = run_layer_set(args, torch, B, WL, c, None, args.g_sets if m else 2, steps,
+                                      args.warmup, window=int(m.group(2)) if m else None)[0]
             torch.cuda.empty_cache()
     if not args.no_schedule:
         subs["schedule7b"] = schedule_summary(torch, B, WL)
@@ -789,9 +799,10 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
+def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup, window=None):
     """Times the step on cfg's layer set (and on `secondary`, a rank variant with the same
-    shapes, sharing its gradients and weights). Returns one result per variant."""
+    shapes, sharing its gradients and weights). Returns one result per variant. window: layers
+    per plan for this run (None: --window)."""
     dev = torch.device("cuda:0")
     t0 = time.time()
     G_sets = [[WL.gradient_bf16_device(cfg, L, 1 + g, device=dev) for L in cfg.layers]
@@ -811,7 +822,8 @@ def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
     results = []
     for vcfg, r in variants:
         v = Variant(vcfg, r, G_sets, W_list, Ws_list, torch, B, WL, args.fast_setup,
-                    args.p_format, args.dequant, args.keep_proj, args.window)
+                    args.p_format, args.dequant, args.keep_proj,
+                    args.window if window is None else window)
         ms, kms, tests = v.time_steps(steps, warmup)
         cs_ms = v.time_cossim()
         a = algorithmic(vcfg, r, args.p_format)
@@ -825,22 +837,24 @@ def run_layer_set(args, torch, B, WL, cfg, secondary, g_sets, steps, warmup):
             kernel_ms["qg_dequant"] = "none (bf16 projection)"
         p_bytes = sum(int(L.Pq.numel() * L.Pq.element_size()) +
                       (int(L.Ps.numel() * 4) if L.Ps is not None else 0) for L in v.layers)
-        res = dict(config=vcfg.key,
-                   workload=f"{vcfg.key}: {describe_layers(vcfg)}, rank {r}",
+        res = dict(config=vcfg.key if window is None else f"{vcfg.key}_window{window}",
+                   workload=f"{vcfg.key}: {describe_layers(vcfg)}, rank {r}"
+                            + (f", in plans of {v.window} layers sharing one workspace"
+                               if v.window else ""),
                    rank=r, steps=steps, ms_per_step=round(ms, 4),
                    step_ms_percentiles=v.step_pct,
                    value=a["mn"] / (ms / 1e3),
                    tflops=round(4.0 * r * a["mn"] / (ms / 1e3) / 1e12, 2),
                    gradient_sets=g_sets,
                    dequant=args.dequant + ("+keep" if v.keep_proj else ""),
-                   window=len(v.chunks) > 1 and args.window or None,
+                   window=v.window,
                    workspace_gib=round(v.workspace_bytes / 2**30, 3),
                    projection_gib=round(p_bytes / 2**30, 3),
                    kernel_ms=kernel_ms,
                    optimizer_ms=round(sum(kms), 4),
                    refresh_tests_per_step=round(tests, 2),
                    cossim_ms=cs_ms,
-                   roofline=roofline(vcfg, r, kms, args.p_format, inl))
+                   roofline=roofline(vcfg, r, kms, args.p_format, inl, len(v.chunks)))
         if args.library_gemm:
             res["library_gemm"] = library_gemm_ms(torch, vcfg, r)
         log(json.dumps(res))
