@@ -2,7 +2,8 @@
 plan over all 224 layers. Sampled layers (one of each shape) are checked against the oracle:
 the projected gradient R and the requantized moments in full, the back-projection and the
 stochastic rounding on sampled weight rows. Step 1 starts from zero moments; step 3 runs on
-the moments two earlier steps with other gradients left (INT8 codes with real scales)."""
+the moments two earlier steps with other gradients left (INT8 codes with real scales). Step 1
+also runs as the benchmark launches it (no U written anywhere) and must give the same codes."""
 import numpy as np
 import pytest
 
@@ -46,10 +47,28 @@ def test_full_7b_plan_sampled_layers(key):
         Lt = layers[k]
         before[k] = dict(G=Lt.G.view(torch.int16).cpu().numpy().view(np.uint16),
                          W=Lt.Wq.cpu().numpy(), Pq=Lt.Pq.cpu().numpy(), Ps=Lt.Ps.cpu().numpy())
-    plan = B.Plan(layers, hp=dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
-                                  alpha=cfg.alpha), R_out=Rs, U_out=Us)
+    hp = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, alpha=cfg.alpha)
+    # First the benchmark's own launch: no layer writes U, so the rounding takes its
+    # alpha-folded path. The sampled layers are then reset, and the step below (which writes
+    # their U and takes the unfolded path) must give the same codes bit for bit.
+    keys = ("Wq", "Mq", "Ms", "Vq", "Vs")
+    saved = {k: {a: getattr(layers[k], a).clone() for a in keys} for k in SAMPLED}
+    plan0 = B.Plan(layers, hp=hp)
+    plan0.step(1, WL.SR_SEED)
+    torch.cuda.synchronize()
+    folded = {k: {a: getattr(layers[k], a).cpu().numpy() for a in keys} for k in SAMPLED}
+    plan0.close()
+    del plan0
+    for k in SAMPLED:
+        for a in keys:
+            getattr(layers[k], a).copy_(saved[k][a])
+    del saved
+    plan = B.Plan(layers, hp=hp, R_out=Rs, U_out=Us)
     plan.step(1, WL.SR_SEED)
     torch.cuda.synchronize()
+    for k in SAMPLED:
+        for a in keys:
+            assert np.array_equal(getattr(layers[k], a).cpu().numpy(), folded[k][a]), (k, a)
     rng = np.random.default_rng(0)
     for k in SAMPLED:
         L = cfg.layers[k]
