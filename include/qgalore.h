@@ -174,7 +174,11 @@ typedef struct qg_plan qg_plan;
 qg_status qgalore_plan_create(const qg_layer *layers, int32_t count, qg_plan **out);
 /* Device scratch a qgalore_plan_step call needs. */
 size_t qgalore_plan_workspace_bytes(const qg_plan *plan);
-/* One optimizer step over every layer of the plan, asynchronous on `stream`. */
+/* One optimizer step over every layer of the plan, asynchronous on `stream`. The workspace
+ * carries nothing from one call to the next (unless qgalore_plan_cache_proj is on), so plans
+ * stepped one after another on one stream may share one workspace of the largest size: a
+ * large layer set can step as several plans over windows of its layers, holding the
+ * step-transient update N~ and dequantized P~ of one window at a time. */
 qg_status qgalore_plan_step(qg_plan *plan, int64_t step, uint64_t seed, void *workspace,
                             size_t workspace_bytes, void *stream);
 qg_status qgalore_plan_destroy(qg_plan *plan);
