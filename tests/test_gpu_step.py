@@ -180,6 +180,39 @@ def test_plan_matches_oracle_over_mixed_layers():
     plan.close()
 
 
+def test_plans_in_turn_share_one_workspace():
+    """Two plans over windows of a layer set, stepped one after the other on one stream with
+    one workspace of the larger size (no synchronization between them): every layer matches
+    the oracle."""
+    B = _B()
+    shapes = [(512, 1376), (1376, 512), (300, 200), (512, 512)]
+    r = 64
+    cfg = WL.Config("mixed", 8, tuple(WL.LayerShape(k, "l", m, n) for k, (m, n) in enumerate(shapes)),
+                    r=r, sigma=1e-3)
+    t = 2
+    states, devs, Gs = [], [], []
+    for L in cfg.layers:
+        st, P = PAR.host_state(cfg, L, r, "random")
+        G = WL.gradient_bf16(cfg, L, t)
+        states.append(st)
+        devs.append(PAR.to_device(st, G, P))
+        Gs.append(G)
+    Rs = [torch.empty((r, L.n), dtype=torch.float32, device="cuda") for L in cfg.layers]
+    Us = [torch.empty((L.m, L.n), dtype=torch.float32, device="cuda") for L in cfg.layers]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, alpha=0.25)
+    plans = [B.Plan(devs[a:b], hp=hp, R_out=Rs[a:b], U_out=Us[a:b]) for a, b in ((0, 2), (2, 4))]
+    ws = B.alloc_workspace(max(p.workspace_bytes for p in plans))
+    for p in plans:
+        p.step(t, WL.SR_SEED, ws)
+    torch.cuda.synchronize()
+    for st, Lt, G, Ro, Uo in zip(states, devs, Gs, Rs, Us):
+        before = st.copy()
+        res = O.qgalore_step(st, G, t, WL.SR_SEED)
+        PAR.check_step(before, res, st, snapshot(Lt, Ro, Uo), t=t)
+    for p in plans:
+        p.close()
+
+
 def test_plan_kept_projections_match_fresh_dequant():
     """With dequantized projections kept between steps, three steps in which one layer's P is
     replaced (and reported) before the third give the same state, bit for bit, as a plan that
